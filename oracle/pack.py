@@ -1,0 +1,161 @@
+"""Example packing, oracle form (test infrastructure only).
+
+Follows "No Padding Please", §V (tile examples in a 2D grid, separator pixels
+between them, a binary mask), §V-A (bucket by height, fill rows greedily with
+the widest still-fitting example, tile rows with separators) and Appendix B,
+Algorithm 1 (the packing loop). The skew of §IV-A / Algorithm 1's last step is
+an implementation device for convolution-based MDLSTMs and does not change any
+cell's value, so the canvas here stays unskewed.
+
+Readings where the pages leave a step open (each listed in the design doc):
+  * bucket visiting order: tallest height first;
+  * ties between equally wide fitting examples: lowest input index;
+  * a row is closed only when nothing of the current bucket fits (as the loop
+    is printed), so a row may continue into the next, shorter bucket; its
+    height is that of its first example, and examples are top-aligned;
+  * the row still open when the loop ends is kept;
+  * one separator pixel (``sep``) between neighbours in a row and between
+    rows;
+  * canvas width = max(canvas_w_min, widest example).
+
+The padded mode is the "last-minute batch-padding" baseline of §VII-C: every
+example gets a slot of max-height x max-width, stacked vertically, the real
+pixels top-left, the rest zero padding that is computed like real cells.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import List
+
+import numpy as np
+
+BIT_L, BIT_R, BIT_U, BIT_D = 1, 2, 4, 8   # neighbour (y,x-1), (y,x+1), (y-1,x), (y+1,x) in same example
+
+
+@dataclasses.dataclass
+class Layout:
+    Hc: int
+    Wc: int
+    rects: np.ndarray        # int32 [n][4] (y0, x0, h, w) of the computed region, input order
+    real: np.ndarray         # int32 [n][4] (y0, x0, h, w) of the real pixels, input order
+    rows: List[List[int]]    # original example indices per packed row, left to right
+    eid: np.ndarray          # int32 [Hc][Wc], example id of the computed region, -1 elsewhere
+    border: np.ndarray       # uint8 [Hc][Wc], BIT_* set where that neighbour is the same example
+    mode: str
+
+
+def _check(heights, widths, canvas_w_min, sep):
+    heights = [int(v) for v in heights]
+    widths = [int(v) for v in widths]
+    if len(heights) != len(widths) or len(heights) < 1:
+        raise ValueError("need n >= 1 examples with one height and one width each")
+    if min(heights) < 1 or min(widths) < 1:
+        raise ValueError("example sizes must be positive")
+    if sep < 0 or canvas_w_min < 1:
+        raise ValueError("sep must be >= 0 and canvas_w_min >= 1")
+    return heights, widths
+
+
+def _maps(Hc, Wc, rects):
+    eid = np.full((Hc, Wc), -1, dtype=np.int32)
+    for e, (y0, x0, h, w) in enumerate(rects):
+        region = eid[y0:y0 + h, x0:x0 + w]
+        if (region != -1).any():
+            raise AssertionError("overlapping rectangles")
+        region[...] = e
+    border = np.zeros((Hc, Wc), dtype=np.uint8)
+    same = eid >= 0
+    # neighbour to the left / right / above / below belongs to the same example
+    border[:, 1:] |= np.where(same[:, 1:] & (eid[:, 1:] == eid[:, :-1]), BIT_L, 0).astype(np.uint8)
+    border[:, :-1] |= np.where(same[:, :-1] & (eid[:, :-1] == eid[:, 1:]), BIT_R, 0).astype(np.uint8)
+    border[1:, :] |= np.where(same[1:, :] & (eid[1:, :] == eid[:-1, :]), BIT_U, 0).astype(np.uint8)
+    border[:-1, :] |= np.where(same[:-1, :] & (eid[:-1, :] == eid[1:, :]), BIT_D, 0).astype(np.uint8)
+    return eid, border
+
+
+def pack_alg1(heights, widths, canvas_w_min: int, sep: int = 1) -> Layout:
+    """Shelf packing by Algorithm 1 (literal reading, see module docstring)."""
+    heights, widths = _check(heights, widths, canvas_w_min, sep)
+    n = len(heights)
+    Wc = max(int(canvas_w_min), max(widths))
+
+    # step 1 of §V-A: bucket the examples by height (tallest bucket first)
+    buckets = {}
+    for e in range(n):
+        buckets.setdefault(heights[e], []).append(e)
+
+    rows: List[List[int]] = []
+    row: List[int] = []
+    x_of = [0] * n
+    x_end = 0
+    for hgt in sorted(buckets, reverse=True):
+        bucket = list(buckets[hgt])
+        while bucket:
+            off = 0 if not row else x_end + sep
+            fitting = [e for e in bucket if off + widths[e] <= Wc]
+            if fitting:
+                # step 2: the widest still-fitting example (lowest index on ties)
+                best = max(fitting, key=lambda e: (widths[e], -e))
+                bucket.remove(best)
+                row.append(best)
+                x_of[best] = off
+                x_end = off + widths[best]
+            else:
+                # current row is full: start a new one
+                rows.append(row)
+                row = []
+                x_end = 0
+    if row:
+        rows.append(row)
+
+    # step 3: tile the rows vertically with separator rows in between
+    y_of = [0] * n
+    y = 0
+    Hc = 0
+    for k, r in enumerate(rows):
+        for e in r:
+            y_of[e] = y
+        Hc = y + heights[r[0]]
+        y = Hc + sep
+    rects = np.array([[y_of[e], x_of[e], heights[e], widths[e]] for e in range(n)], dtype=np.int32)
+    if Hc * Wc >= 2 ** 31:
+        raise OverflowError("canvas too large")
+    eid, border = _maps(Hc, Wc, rects)
+    return Layout(Hc, Wc, rects, rects.copy(), rows, eid, border, "packed")
+
+
+def pack_padded(heights, widths) -> Layout:
+    """Minimal per-batch padding: slot b at (b*Hmax, 0), Hmax x Wmax, no separator."""
+    heights, widths = _check(heights, widths, 1, 0)
+    n = len(heights)
+    Hm, Wm = max(heights), max(widths)
+    rects = np.array([[b * Hm, 0, Hm, Wm] for b in range(n)], dtype=np.int32)
+    real = np.array([[b * Hm, 0, heights[b], widths[b]] for b in range(n)], dtype=np.int32)
+    Hc, Wc = n * Hm, Wm
+    if Hc * Wc >= 2 ** 31:
+        raise OverflowError("canvas too large")
+    eid, border = _maps(Hc, Wc, rects)
+    return Layout(Hc, Wc, rects, real, [[b] for b in range(n)], eid, border, "padded")
+
+
+def pack(heights, widths, canvas_w_min: int, sep: int = 1, mode: str = "packed") -> Layout:
+    if mode == "packed":
+        return pack_alg1(heights, widths, canvas_w_min, sep)
+    if mode == "padded":
+        return pack_padded(heights, widths)
+    raise ValueError(mode)
+
+
+def waste(layout: Layout, heights, widths) -> dict:
+    """Padding figures: canvas waste, computed-cell padding fraction, zero-padding ratio."""
+    N = int(np.sum(np.asarray(heights, np.int64) * np.asarray(widths, np.int64)))
+    computed = int(np.sum(layout.rects[:, 2].astype(np.int64) * layout.rects[:, 3]))
+    return {
+        "real_pixels": N,
+        "computed_cells": computed,
+        "canvas_pixels": layout.Hc * layout.Wc,
+        "canvas_waste": 1.0 - N / (layout.Hc * layout.Wc),
+        "padded_cell_fraction": 1.0 - N / computed,
+        "zpr": (computed - N) / N,
+    }
