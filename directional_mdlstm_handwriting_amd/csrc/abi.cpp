@@ -1,0 +1,471 @@
+// abi.cpp — the extern "C" entry points of libmdlstm: argument checks, workspace
+// carving and kernel launches. Every check runs before the first launch, so a
+// failing call writes nothing; errors never cross the ABI as exceptions.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/mdlstm.h"
+#include "kernels.h"
+#include "layout.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(MDL_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+const mdl::Layout& L_of(const mdl_layout* l) { return l->L; }
+
+mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
+    const mdl::Layout& L = L_of(lay);
+    const uint8_t* b = static_cast<const uint8_t*>(d_desc);
+    mdl::Dev D;
+    D.rect = reinterpret_cast<const int32_t*>(b + L.off.rect);
+    D.real = reinterpret_cast<const int32_t*>(b + L.off.real);
+    D.flat_off = reinterpret_cast<const int64_t*>(b + L.off.flat_off);
+    D.cell_off = reinterpret_cast<const int64_t*>(b + L.off.cell_off);
+    D.units = reinterpret_cast<const int32_t*>(b + L.off.units);
+    D.eid = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(b + L.off.eid));
+    D.border = const_cast<uint8_t*>(b + L.off.border);
+    D.n = L.n;
+    D.Hc = L.Hc;
+    D.Wc = L.Wc;
+    D.T = L.computed_cells;
+    D.N = L.real_pixels;
+    D.max_depth = L.max_depth;
+    D.max_diag = L.max_diag;
+    return D;
+}
+
+int max_lds(size_t& out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    out = (size_t)v;
+    return MDL_OK;
+}
+
+int check_layer(const char* fn, const mdl_layout* layout, const void* d_desc, int32_t C, int32_t H, int32_t x_dtype) {
+    if (!layout || !d_desc) return fail(MDL_EINVAL, std::string(fn) + ": null layout or descriptor");
+    if (C < 1 || H < 1) return fail(MDL_EINVAL, std::string(fn) + ": need C >= 1 and H >= 1");
+    if (x_dtype != MDL_F32 && x_dtype != MDL_BF16) return fail(MDL_EINVAL, std::string(fn) + ": unknown dtype");
+    if (C > 1024 || H > 1024) return fail(MDL_EUNSUPPORTED, std::string(fn) + ": C or H above 1024");
+    const mdl::Layout& L = L_of(layout);
+    const int64_t P = (int64_t)L.Hc * L.Wc;
+    if (P * 4 * std::max(H, C) >= (int64_t(1) << 40)) return fail(MDL_EOVERFLOW, std::string(fn) + ": canvas too large");
+    return MDL_OK;
+}
+
+// ---- optional per-launch event timing ---------------------------------------------------------
+struct TimedLaunch {
+    std::string name;
+    hipEvent_t start, stop;
+};
+bool g_timing = false;
+std::mutex g_tmu;
+std::vector<TimedLaunch> g_tlog;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// records an event pair around one launcher call when timing is on
+class Timed {
+  public:
+    Timed(const char* name, hipStream_t st) : st_(st) {
+        if (!g_timing) return;
+        std::lock_guard<std::mutex> lk(g_tmu);
+        a_ = take_event();
+        b_ = take_event();
+        name_ = name;
+        if (a_ && b_) hipEventRecord(a_, st_);
+    }
+    ~Timed() {
+        if (!a_ || !b_) return;
+        hipEventRecord(b_, st_);
+        std::lock_guard<std::mutex> lk(g_tmu);
+        g_tlog.push_back({name_, a_, b_});
+    }
+
+  private:
+    hipStream_t st_;
+    hipEvent_t a_ = nullptr, b_ = nullptr;
+    const char* name_ = nullptr;
+};
+
+#define GUARD_BEGIN try {
+#define GUARD_END                                                      \
+    }                                                                  \
+    catch (const std::bad_alloc&) { return fail(MDL_ENOMEM, "out of host memory"); } \
+    catch (...) { return fail(MDL_EINVAL, "unexpected internal error"); }
+
+}  // namespace
+
+extern "C" {
+
+int mdl_pack(const int32_t* heights, const int32_t* widths, int32_t n, int32_t canvas_w_min, int32_t sep,
+             int32_t mode, mdl_layout** out) {
+    GUARD_BEGIN
+    if (!out) return fail(MDL_EINVAL, "mdl_pack: null output pointer");
+    *out = nullptr;
+    mdl_layout* lay = new (std::nothrow) mdl_layout;
+    if (!lay) return fail(MDL_ENOMEM, "mdl_pack: out of host memory");
+    std::string err;
+    const int rc = mdl::build_layout(heights, widths, n, canvas_w_min, sep, mode, lay->L, err);
+    if (rc != MDL_OK) {
+        delete lay;
+        return fail(rc, err);
+    }
+    *out = lay;
+    return MDL_OK;
+    GUARD_END
+}
+
+void mdl_layout_free(mdl_layout* layout) { delete layout; }
+
+int mdl_layout_info(const mdl_layout* layout, int64_t* info) {
+    if (!layout || !info) return fail(MDL_EINVAL, "mdl_layout_info: null argument");
+    const mdl::Layout& L = L_of(layout);
+    info[MDL_INFO_N] = L.n;
+    info[MDL_INFO_CANVAS_H] = L.Hc;
+    info[MDL_INFO_CANVAS_W] = L.Wc;
+    info[MDL_INFO_ROWS] = (int64_t)L.rows.size();
+    info[MDL_INFO_REAL_PIXELS] = L.real_pixels;
+    info[MDL_INFO_COMPUTED_CELLS] = L.computed_cells;
+    info[MDL_INFO_MAX_DEPTH] = L.max_depth;
+    info[MDL_INFO_MAX_DIAG] = L.max_diag;
+    info[MDL_INFO_MODE] = L.mode;
+    return MDL_OK;
+}
+
+int mdl_layout_rects(const mdl_layout* layout, int32_t* rects, int32_t* real) {
+    if (!layout) return fail(MDL_EINVAL, "mdl_layout_rects: null layout");
+    const mdl::Layout& L = L_of(layout);
+    if (rects) std::memcpy(rects, L.rect.data(), sizeof(int32_t) * 4 * L.n);
+    if (real) std::memcpy(real, L.real.data(), sizeof(int32_t) * 4 * L.n);
+    return MDL_OK;
+}
+
+int mdl_layout_rows(const mdl_layout* layout, int32_t* row_start, int32_t* row_examples) {
+    if (!layout || !row_start || !row_examples) return fail(MDL_EINVAL, "mdl_layout_rows: null argument");
+    const mdl::Layout& L = L_of(layout);
+    int32_t k = 0;
+    for (size_t r = 0; r < L.rows.size(); ++r) {
+        row_start[r] = k;
+        for (int32_t e : L.rows[r]) row_examples[k++] = e;
+    }
+    row_start[L.rows.size()] = k;
+    return MDL_OK;
+}
+
+int mdl_layout_maps(const mdl_layout* layout, int32_t* eid, uint8_t* border) {
+    if (!layout) return fail(MDL_EINVAL, "mdl_layout_maps: null layout");
+    const mdl::Layout& L = L_of(layout);
+    if (eid) std::memcpy(eid, L.eid.data(), sizeof(int32_t) * L.eid.size());
+    if (border) std::memcpy(border, L.border.data(), L.border.size());
+    return MDL_OK;
+}
+
+int mdl_layout_device_size(const mdl_layout* layout, size_t* bytes, size_t* eid_offset, size_t* border_offset) {
+    if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_layout_device_size: null argument");
+    const mdl::Layout& L = L_of(layout);
+    *bytes = L.off.total;
+    if (eid_offset) *eid_offset = L.off.eid;
+    if (border_offset) *border_offset = L.off.border;
+    return MDL_OK;
+}
+
+int mdl_layout_upload(const mdl_layout* layout, void* d_desc, size_t bytes, void* stream) {
+    GUARD_BEGIN
+    if (!layout || !d_desc) return fail(MDL_EINVAL, "mdl_layout_upload: null argument");
+    const mdl::Layout& L = L_of(layout);
+    if (bytes < L.off.total) return fail(MDL_ESIZE, "mdl_layout_upload: descriptor buffer too small");
+    if (reinterpret_cast<uintptr_t>(d_desc) % 8) return fail(MDL_EINVAL, "mdl_layout_upload: descriptor not 8-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(d_desc, L.host_desc.data(), L.host_desc.size(), hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "mdl_layout_upload: copy");
+    {
+        Timed t("build_maps", st);
+        e = mdl::launch_build_maps(make_dev(layout, d_desc), st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_layout_upload: map kernels");
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "mdl_layout_upload: synchronize");
+    return MDL_OK;
+    GUARD_END
+}
+
+int mdl_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes) {
+    if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_workspace_size: null argument");
+    if (C < 1 || H < 1) return fail(MDL_EINVAL, "mdl_workspace_size: need C >= 1 and H >= 1");
+    *bytes = mdl::ws_layout(L_of(layout).computed_cells, C, H).total;
+    return MDL_OK;
+}
+
+int mdl_scatter(const mdl_layout* layout, const void* d_desc, const void* x_flat, int32_t C, int32_t dtype,
+                void* x_canvas, void* stream) {
+    GUARD_BEGIN
+    int rc = check_layer("mdl_scatter", layout, d_desc, C, 1, dtype);
+    if (rc) return rc;
+    if (!x_flat || !x_canvas) return fail(MDL_EINVAL, "mdl_scatter: null tensor");
+    hipError_t e;
+    {
+        Timed t("scatter", static_cast<hipStream_t>(stream));
+        e = mdl::launch_scatter(make_dev(layout, d_desc), x_flat, C, dtype, x_canvas, static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_scatter");
+    return MDL_OK;
+    GUARD_END
+}
+
+int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype, int32_t C,
+                int32_t H, const float* Wx, const float* Ul, const float* Uu, const float* b, float* h_dirs, void* ws,
+                size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    int rc = check_layer("mdl_forward", layout, d_desc, C, H, x_dtype);
+    if (rc) return rc;
+    if (!x_canvas || !Wx || !Ul || !Uu || !b || !h_dirs || !ws) return fail(MDL_EINVAL, "mdl_forward: null tensor");
+    const mdl::Layout& L = L_of(layout);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, C, H);
+    if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
+    if ((int64_t)L.max_diag * H > mdl::chain_max_items())
+        return fail(MDL_EUNSUPPORTED, "mdl_forward: widest diagonal x H exceeds the wavefront kernel's items");
+    size_t lmax = 0;
+    if ((rc = max_lds(lmax))) return rc;
+    if (mdl::fwd_chain_lds(H, L.max_diag) > lmax)
+        return fail(MDL_EUNSUPPORTED, "mdl_forward: recurrent weights and diagonal state exceed LDS");
+    const mdl::Dev D = make_dev(layout, d_desc);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    float* Z = reinterpret_cast<float*>(wsb + W.zda);
+    float* stash = reinterpret_cast<float*>(wsb + W.stash);
+    hipError_t e;
+    {
+        Timed t("zero_fill", st);
+        e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_forward: zero fill");
+    {
+        Timed t("projection", st);
+        e = mdl::launch_projection(D, x_canvas, x_dtype, C, H, Wx, b, Z, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_forward: projection");
+    {
+        Timed t("fwd_wavefront", st);
+        e = mdl::launch_fwd_chain(D, H, Ul, Uu, Z, stash, h_dirs, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_forward: wavefront");
+    return MDL_OK;
+    GUARD_END
+}
+
+int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float* h_dirs, int32_t H, float* y_flat,
+                      void* stream) {
+    GUARD_BEGIN
+    int rc = check_layer("mdl_dirsum_unpack", layout, d_desc, 1, H, MDL_F32);
+    if (rc) return rc;
+    if (!h_dirs || !y_flat) return fail(MDL_EINVAL, "mdl_dirsum_unpack: null tensor");
+    hipError_t e;
+    {
+        Timed t("dirsum", static_cast<hipStream_t>(stream));
+        e = mdl::launch_dirsum(make_dev(layout, d_desc), h_dirs, H, y_flat, static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_dirsum_unpack");
+    return MDL_OK;
+    GUARD_END
+}
+
+int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype, int32_t C,
+                 int32_t H, const float* Wx, const float* Ul, const float* Uu, const float* h_dirs,
+                 const float* dy_flat, const float* dh_dirs, float* dx_flat, float* dx_canvas, float* dWx, float* dUl,
+                 float* dUu, float* db, void* ws, size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    int rc = check_layer("mdl_backward", layout, d_desc, C, H, x_dtype);
+    if (rc) return rc;
+    if (!x_canvas || !Wx || !Ul || !Uu || !h_dirs || !ws) return fail(MDL_EINVAL, "mdl_backward: null tensor");
+    if (!dWx || !dUl || !dUu || !db) return fail(MDL_EINVAL, "mdl_backward: null weight-gradient output");
+    if ((dy_flat == nullptr) == (dh_dirs == nullptr))
+        return fail(MDL_EINVAL, "mdl_backward: pass exactly one of dy_flat and dh_dirs");
+    const mdl::Layout& L = L_of(layout);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, C, H);
+    if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_backward: workspace smaller than mdl_workspace_size");
+    if ((int64_t)L.max_diag * H > mdl::chain_max_items())
+        return fail(MDL_EUNSUPPORTED, "mdl_backward: widest diagonal x H exceeds the wavefront kernel's items");
+    const int R = C + 1 + 2 * H, G = 5 * H;
+    if (!mdl::wgrad_supported(C, H))
+        return fail(MDL_EUNSUPPORTED, "mdl_backward: C and H exceed the weight-gradient kernel's register tile");
+    size_t lmax = 0;
+    if ((rc = max_lds(lmax))) return rc;
+    if (mdl::bwd_chain_lds(H, L.max_diag) > lmax)
+        return fail(MDL_EUNSUPPORTED, "mdl_backward: recurrent weights and diagonal state exceed LDS");
+    if (sizeof(float) * 32 * (size_t)(R + G) > lmax)
+        return fail(MDL_EUNSUPPORTED, "mdl_backward: weight-gradient tile exceeds LDS");
+    const mdl::Dev D = make_dev(layout, d_desc);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    float* dA = reinterpret_cast<float*>(wsb + W.zda);
+    const float* stash = reinterpret_cast<const float*>(wsb + W.stash);
+    float* part = reinterpret_cast<float*>(wsb + W.part);
+    hipError_t e;
+    {
+        Timed t("bwd_wavefront", st);
+        e = mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_backward: reverse wavefront");
+    {
+        Timed t("wgrad", st);
+        e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, part, W.nchunks, dWx, dUl, dUu, db, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight gradients");
+    if (dx_flat || dx_canvas) {
+        Timed t("dx", st);
+        e = mdl::launch_dx(D, C, H, Wx, dA, dx_flat, dx_canvas, st);
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward: input gradient");
+    }
+    return MDL_OK;
+    GUARD_END
+}
+
+static int check_conv(const char* fn, const mdl_layout* lk, const void* dk, const mdl_layout* lk1, const void* dk1,
+                      int32_t H, int32_t kh, int32_t kw, int32_t Cout) {
+    if (!lk || !dk || !lk1 || !dk1) return fail(MDL_EINVAL, std::string(fn) + ": null layout or descriptor");
+    if (H < 1 || kh < 1 || kw < 1 || Cout < 1) return fail(MDL_EINVAL, std::string(fn) + ": non-positive size");
+    const mdl::Layout& A = L_of(lk);
+    const mdl::Layout& B = L_of(lk1);
+    if (A.n != B.n) return fail(MDL_EINVAL, std::string(fn) + ": layouts hold different example counts");
+    for (int e = 0; e < A.n; ++e) {
+        const int h = A.real[4 * e + 2], w = A.real[4 * e + 3];
+        if (B.real[4 * e + 2] != (h + kh - 1) / kh || B.real[4 * e + 3] != (w + kw - 1) / kw)
+            return fail(MDL_EINVAL, std::string(fn) + ": level-(k+1) example sizes are not ceil(h/kh) x ceil(w/kw)");
+    }
+    return MDL_OK;
+}
+
+int mdl_blockconv_forward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1, const void* d_desc_k1,
+                          const float* h_dirs_k, int32_t H, int32_t kh, int32_t kw, const float* Wc, const float* bc,
+                          int32_t Cout, float* x_canvas_k1, void* stream) {
+    GUARD_BEGIN
+    int rc = check_conv("mdl_blockconv_forward", lk, d_desc_k, lk1, d_desc_k1, H, kh, kw, Cout);
+    if (rc) return rc;
+    if (!h_dirs_k || !Wc || !bc || !x_canvas_k1) return fail(MDL_EINVAL, "mdl_blockconv_forward: null tensor");
+    hipError_t e;
+    {
+        Timed t("conv_fwd", static_cast<hipStream_t>(stream));
+        e = mdl::launch_conv_fwd(make_dev(lk, d_desc_k), make_dev(lk1, d_desc_k1), h_dirs_k, H, kh, kw, Wc, bc, Cout,
+                                 x_canvas_k1, static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_blockconv_forward");
+    return MDL_OK;
+    GUARD_END
+}
+
+int mdl_blockconv_workspace_size(const mdl_layout* lk1, int32_t H, int32_t kh, int32_t kw, int32_t Cout,
+                                 size_t* bytes) {
+    if (!lk1 || !bytes) return fail(MDL_EINVAL, "mdl_blockconv_workspace_size: null argument");
+    if (H < 1 || kh < 1 || kw < 1 || Cout < 1) return fail(MDL_EINVAL, "mdl_blockconv_workspace_size: non-positive size");
+    const mdl::Layout& B = L_of(lk1);
+    mdl::Dev D{};
+    D.N = B.real_pixels;
+    const int64_t K = 4 * (int64_t)H * kh * kw;
+    *bytes = sizeof(float) * (size_t)mdl::conv_nchunks(D) * (size_t)(Cout * (K + 1));
+    return MDL_OK;
+}
+
+int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1, const void* d_desc_k1,
+                           const float* h_dirs_k, int32_t H, int32_t kh, int32_t kw, const float* Wc, int32_t Cout,
+                           const float* dx_canvas_k1, float* dh_dirs_k, float* dWc, float* dbc, void* ws,
+                           size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    int rc = check_conv("mdl_blockconv_backward", lk, d_desc_k, lk1, d_desc_k1, H, kh, kw, Cout);
+    if (rc) return rc;
+    if (!h_dirs_k || !Wc || !dx_canvas_k1 || !dh_dirs_k || !dWc || !dbc || !ws)
+        return fail(MDL_EINVAL, "mdl_blockconv_backward: null tensor");
+    size_t need = 0;
+    mdl_blockconv_workspace_size(lk1, H, kh, kw, Cout, &need);
+    if (ws_bytes < need) return fail(MDL_ESIZE, "mdl_blockconv_backward: workspace too small");
+    const int64_t K = 4 * (int64_t)H * kh * kw;
+    if (Cout * (K + 1) > 16 * 512) return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: Cout*(4*H*kh*kw+1) above 8192");
+    size_t lmax = 0;
+    if ((rc = max_lds(lmax))) return rc;
+    if (sizeof(float) * 16 * (size_t)(K + Cout) > lmax)
+        return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: weight-gradient tile exceeds LDS");
+    hipError_t e;
+    {
+        Timed t("conv_bwd", static_cast<hipStream_t>(stream));
+        e = mdl::launch_conv_bwd(make_dev(lk, d_desc_k), make_dev(lk1, d_desc_k1), h_dirs_k, H, kh, kw, Wc, Cout,
+                                 dx_canvas_k1, dh_dirs_k, dWc, dbc, static_cast<float*>(ws),
+                                 static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_blockconv_backward");
+    return MDL_OK;
+    GUARD_END
+}
+
+int mdl_timing(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing = enable != 0;
+    return MDL_OK;
+}
+
+int mdl_timing_report(int32_t max, char* names, double* total_ms, int64_t* launches, int32_t* count) {
+    GUARD_BEGIN
+    if (max < 0 || !count || (max > 0 && (!names || !total_ms || !launches)))
+        return fail(MDL_EINVAL, "mdl_timing_report: bad arguments");
+    std::lock_guard<std::mutex> lk(g_tmu);
+    std::map<std::string, std::pair<double, int64_t>> acc;
+    std::vector<std::string> order;
+    int rc = MDL_OK;
+    for (auto& t : g_tlog) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(t.stop);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+        if (e != hipSuccess && rc == MDL_OK) rc = hip_fail(e, "mdl_timing_report");
+        if (!acc.count(t.name)) order.push_back(t.name);
+        acc[t.name].first += ms;
+        acc[t.name].second += 1;
+        g_event_pool.push_back(t.start);
+        g_event_pool.push_back(t.stop);
+    }
+    g_tlog.clear();
+    int k = 0;
+    for (const auto& nm : order) {
+        if (k >= max) break;
+        std::memset(names + 32 * k, 0, 32);
+        std::strncpy(names + 32 * k, nm.c_str(), 31);
+        total_ms[k] = acc[nm].first;
+        launches[k] = acc[nm].second;
+        ++k;
+    }
+    *count = k;
+    return rc;
+    GUARD_END
+}
+
+const char* mdl_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// k_layout.hip — canvas maps, scatter onto the canvas, direction sum + un-packing.
+//
+// "No Padding Please", §V: the binary mask marks example pixels (here with the
+// example id) so that state from padding or separator predecessors is
+// blocked; §V-A: un-packing cuts each example's activations out of the canvas
+// by its original index and size. All of these are HBM-bound copies: one
+// thread per output element, consecutive threads on consecutive addresses.
+#include "kernels.h"
+
+namespace mdl {
+
+namespace {
+
+constexpr int TPB = 256;
+
+inline unsigned grid_for(int64_t n, int tpb = TPB, int64_t cap = 1 << 20) {
+    int64_t g = (n + tpb - 1) / tpb;
+    if (g < 1) g = 1;
+    return (unsigned)(g < cap ? g : cap);
+}
+
+__global__ void k_fill_eid(int32_t* __restrict__ eid, int64_t P) {
+    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x)
+        eid[p] = -1;
+}
+
+// blockIdx.y = example; paints its computed region
+__global__ void k_paint_eid(Dev D) {
+    const int e = blockIdx.y;
+    const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
+    const int64_t cells = (int64_t)h * w;
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < cells; q += (int64_t)gridDim.x * blockDim.x) {
+        const int ly = (int)(q / w), lx = (int)(q % w);
+        D.eid[(int64_t)(y0 + ly) * D.Wc + x0 + lx] = e;
+    }
+}
+
+__global__ void k_border(Dev D) {
+    const int64_t P = (int64_t)D.Hc * D.Wc;
+    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x) {
+        const int y = (int)(p / D.Wc), x = (int)(p % D.Wc);
+        const int e = D.eid[p];
+        uint8_t bits = 0;
+        if (e >= 0) {
+            if (x > 0 && D.eid[p - 1] == e) bits |= 1;
+            if (x + 1 < D.Wc && D.eid[p + 1] == e) bits |= 2;
+            if (y > 0 && D.eid[p - D.Wc] == e) bits |= 4;
+            if (y + 1 < D.Hc && D.eid[p + D.Wc] == e) bits |= 8;
+        }
+        D.border[p] = bits;
+    }
+}
+
+// One thread per canvas element (pixel, channel): copy from the example's flat
+// tensor inside its real rectangle, zero elsewhere.
+template <typename T>
+__global__ void k_scatter(Dev D, const T* __restrict__ xf, int C, T* __restrict__ xc) {
+    const int64_t E = (int64_t)D.Hc * D.Wc * C;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < E; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = i / C;
+        const int c = (int)(i % C);
+        const int e = D.eid[p];
+        T v = T(0);
+        if (e >= 0) {
+            const int y = (int)(p / D.Wc), x = (int)(p % D.Wc);
+            const int ry = y - D.real[4 * e], rx = x - D.real[4 * e + 1];
+            const int rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+            if (ry < rh && rx < rw) v = xf[(D.flat_off[e] + (int64_t)ry * rw + rx) * C + c];
+        }
+        xc[i] = v;
+    }
+}
+
+// blockIdx.y = example: y_flat[e][r][c][k] = sum_d h_dirs[d][y0+r][x0+c][k], d = 0..3 in order
+__global__ void k_dirsum(Dev D, const float* __restrict__ hd, int H, float* __restrict__ y) {
+    const int e = blockIdx.y;
+    const int y0 = D.real[4 * e], x0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+    const int64_t cnt = (int64_t)rh * rw * H;
+    const int64_t plane = (int64_t)D.Hc * D.Wc * H;
+    float* out = y + D.flat_off[e] * H;
+    for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < cnt; q += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t pix = q / H;
+        const int k = (int)(q % H);
+        const int ly = (int)(pix / rw), lx = (int)(pix % rw);
+        const int64_t src = ((int64_t)(y0 + ly) * D.Wc + x0 + lx) * H + k;
+        float s = hd[src];
+        s += hd[src + plane];
+        s += hd[src + 2 * plane];
+        s += hd[src + 3 * plane];
+        out[q] = s;
+    }
+}
+
+// zero `planes` planes of [Hc*Wc][K] floats at every pixel outside all computed regions
+__global__ void k_zero_outside(Dev D, float* __restrict__ buf, int K, int planes) {
+    const int64_t P = (int64_t)D.Hc * D.Wc;
+    const int64_t E = P * K;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < E; i += (int64_t)gridDim.x * blockDim.x) {
+        if (D.eid[i / K] >= 0) continue;
+        for (int pl = 0; pl < planes; ++pl) buf[pl * E + i] = 0.f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_zero_outside(const Dev& D, float* buf, int K, int planes, hipStream_t st) {
+    const int64_t E = (int64_t)D.Hc * D.Wc * K;
+    hipLaunchKernelGGL(k_zero_outside, dim3(grid_for(E)), dim3(TPB), 0, st, D, buf, K, planes);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_maps(const Dev& D, hipStream_t st) {
+    const int64_t P = (int64_t)D.Hc * D.Wc;
+    hipLaunchKernelGGL(k_fill_eid, dim3(grid_for(P)), dim3(TPB), 0, st, D.eid, P);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_paint_eid, dim3(64, D.n), dim3(TPB), 0, st, D);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_border, dim3(grid_for(P)), dim3(TPB), 0, st, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter(const Dev& D, const void* x_flat, int C, int dtype, void* x_canvas, hipStream_t st) {
+    const int64_t E = (int64_t)D.Hc * D.Wc * C;
+    if (dtype == 0)
+        hipLaunchKernelGGL(k_scatter<float>, dim3(grid_for(E)), dim3(TPB), 0, st, D,
+                           (const float*)x_flat, C, (float*)x_canvas);
+    else
+        hipLaunchKernelGGL(k_scatter<uint16_t>, dim3(grid_for(E)), dim3(TPB), 0, st, D,
+                           (const uint16_t*)x_flat, C, (uint16_t*)x_canvas);
+    return hipGetLastError();
+}
+
+hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st) {
+    hipLaunchKernelGGL(k_dirsum, dim3(64, D.n), dim3(TPB), 0, st, D, h_dirs, H, y_flat);
+    return hipGetLastError();
+}
+
+}  // namespace mdl

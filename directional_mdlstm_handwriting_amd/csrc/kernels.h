@@ -1,0 +1,108 @@
+// kernels.h — device view of a layout and the launchers of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "layout.h"
+
+namespace mdl {
+
+// Pointers into an uploaded descriptor plus the sizes the kernels need.
+struct Dev {
+    const int32_t* rect;      // [n][4] computed region (y0, x0, h, w)
+    const int32_t* real;      // [n][4] real pixels
+    const int64_t* flat_off;  // [n+1]
+    const int64_t* cell_off;  // [n+1]
+    const int32_t* units;     // [4n]
+    int32_t* eid;             // [Hc*Wc]
+    uint8_t* border;          // [Hc*Wc]
+    int n, Hc, Wc;
+    int64_t T;                // computed cells per direction
+    int64_t N;                // real pixels
+    int max_depth, max_diag;
+};
+
+// Canvas position of the direction-local cell (a, b) of an example whose
+// computed region is (y0, x0, h, w), for direction d (bit 1: rows scanned
+// bottom-up, bit 0: columns scanned right-to-left).
+struct Flip {
+    int y0, x0, h, w;
+    bool fy, fx;
+    MDL_HD int y(int a) const { return y0 + (fy ? h - 1 - a : a); }
+    MDL_HD int x(int b) const { return x0 + (fx ? w - 1 - b : b); }
+};
+
+// Decode a cell's position in an example's diagonal-major order: index q ->
+// (diagonal s, row a). Inverse of dg_start(s) + a - dg_lo(s).
+MDL_HD inline void dg_decode(int h, int w, int64_t q, int& s, int& a) {
+    const int A = h < w ? h : w, B = h < w ? w : h;
+    const int64_t t1 = (int64_t)A * (A + 1) / 2;
+    const int64_t t2 = t1 + (int64_t)(B - A) * A;
+    if (q < t1) {
+        int v = (int)((sqrt(8.0 * (double)q + 1.0) - 1.0) * 0.5);
+        while ((int64_t)v * (v + 1) / 2 > q) --v;
+        while ((int64_t)(v + 1) * (v + 2) / 2 <= q) ++v;
+        s = v;
+    } else if (q < t2) {
+        s = A + (int)((q - t1) / A);
+    } else {
+        const int64_t r = (int64_t)h * w - 1 - q;  // position counted from the last cell
+        int v = (int)((sqrt(8.0 * (double)r + 1.0) - 1.0) * 0.5);
+        while ((int64_t)v * (v + 1) / 2 > r) --v;
+        while ((int64_t)(v + 1) * (v + 2) / 2 <= r) ++v;
+        s = h + w - 2 - v;
+    }
+    a = dg_lo(h, w, s) + (int)(q - dg_start(h, w, s));
+}
+
+// Largest e with off[e] <= g (off has n+1 ascending entries, off[0] = 0).
+MDL_HD inline int find_example(const int64_t* off, int n, int64_t g) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Workspace carving for one MDLSTM layer (all offsets 256-byte aligned).
+struct WsLayout {
+    size_t stash = 0;   // float [4][T][6H]: gates i, f_l, f_u, o, g and memory state c of every cell
+    size_t zda = 0;     // float [4][T][5H]: projection x.Wx+b (forward), gate gradients dA (backward)
+    size_t part = 0;    // float [4][nchunks][(C+1+2H)*5H]: weight-gradient partial sums
+    size_t total = 0;
+    int64_t nchunks = 0;
+};
+constexpr int WGRAD_CHUNK = 1024;  // cells per weight-gradient partial sum
+WsLayout ws_layout(int64_t T, int C, int H);
+
+// launchers: return hipSuccess or the launch error
+hipError_t launch_build_maps(const Dev& D, hipStream_t st);
+hipError_t launch_zero_outside(const Dev& D, float* buf, int K, int planes, hipStream_t st);
+hipError_t launch_scatter(const Dev& D, const void* x_flat, int C, int dtype, void* x_canvas, hipStream_t st);
+hipError_t launch_projection(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
+                             const float* b, float* Z, hipStream_t st);
+size_t fwd_chain_lds(int H, int Lmax);
+size_t bwd_chain_lds(int H, int Lmax);
+int chain_max_items();
+hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z,
+                            float* stash, float* h_dirs, hipStream_t st);
+hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st);
+hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
+                            const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
+bool wgrad_supported(int C, int H);
+hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
+                        const float* dA, float* part, int64_t nchunks, float* dWx, float* dUl, float* dUu,
+                        float* db, hipStream_t st);
+hipError_t launch_dx(const Dev& D, int C, int H, const float* Wx, const float* dA, float* dx_flat,
+                     float* dx_canvas, hipStream_t st);
+hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
+                           const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st);
+int64_t conv_nchunks(const Dev& Dk1);
+hipError_t launch_conv_bwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
+                           const float* Wc, int Cout, const float* dx_k1, float* dh_k, float* dWc,
+                           float* dbc, float* part, hipStream_t st);
+
+}  // namespace mdl

@@ -1,0 +1,259 @@
+/*
+ * mdlstm.h — C ABI of libmdlstm: example-packed 4-direction 2D MDLSTM on MI355X (gfx950).
+ *
+ * The method is that of "No Padding Please: Efficient Neural Handwriting
+ * Recognition": variable-size images are tiled onto one 2D canvas with
+ * separator pixels and a mask instead of being padded and stacked (§V), and a
+ * 4-directional 2D MDLSTM layer (§III) runs over that canvas; the block-strided
+ * convolution between MDLSTM levels works on chunked example lists (§V-B).
+ *
+ * Conventions for every entry point below
+ *  - Plain C types only. Device pointers are HIP device memory owned by the
+ *    caller; the library never allocates or frees device memory. Host pointers
+ *    are marked "host".
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Device
+ *    work is enqueued asynchronously on it; nothing synchronizes unless stated.
+ *  - Return value: MDL_OK or a negative MDL_E* code; on failure nothing has been
+ *    launched or written and mdl_last_error() holds a message (thread-local,
+ *    valid until the next call on that thread). The library never prints and
+ *    never aborts. A device fault inside a kernel surfaces at the caller's next
+ *    synchronization, as for any HIP work.
+ *  - Outputs are overwritten, never accumulated into.
+ *  - Results are deterministic: the same inputs on the same stream give
+ *    bit-identical outputs (fixed reduction orders, no floating-point atomics).
+ *
+ * Canvas conventions
+ *  - The canvas is Hc x Wc pixels, row-major. Channel-last tensors on it are
+ *    [Hc][Wc][K]; per-direction tensors are [4][Hc][Wc][H] (direction-major).
+ *  - Directions: 0 scans from the top-left, 1 from the top-right, 2 from the
+ *    bottom-left, 3 from the bottom-right. For direction (sy, sx) in
+ *    {(+1,+1), (+1,-1), (-1,+1), (-1,-1)} the predecessors of (y, x) are
+ *    "left" (y, x - sx) and "up" (y - sy, x) ("as defined by the scanning
+ *    direction", §IV-A).
+ *  - Per-example ("flat") tensors are the examples' [h][w][K] blocks
+ *    concatenated in input order.
+ *  - Gate axis of width 5H, in blocks of H: (i, f_left, f_up, o, g).
+ *    Wx[4][C][5H], Ul[4][H][5H], Uu[4][H][5H], b[4][5H], all float32.
+ */
+#ifndef MDLSTM_H
+#define MDLSTM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MDL_OK            0
+#define MDL_EINVAL       (-1) /* bad argument (null pointer, non-positive size, bad enum) */
+#define MDL_ENOMEM       (-2) /* host allocation failed */
+#define MDL_EOVERFLOW    (-3) /* canvas or buffer size exceeds the 32-bit index range */
+#define MDL_ESIZE        (-4) /* caller buffer (workspace, descriptor) too small */
+#define MDL_EHIP         (-5) /* HIP runtime or launch error */
+#define MDL_EUNSUPPORTED (-6) /* size combination this build does not handle (e.g. LDS limit) */
+
+/* packing modes */
+#define MDL_PACK_ALG1   0 /* shelf packing, Appendix B Algorithm 1 */
+#define MDL_PACK_PADDED 1 /* minimal per-batch padding ("batch-padding", §VII-C) */
+
+/* element types of pixel tensors */
+#define MDL_F32  0
+#define MDL_BF16 1
+
+/* indices into the int64 array filled by mdl_layout_info */
+#define MDL_INFO_N              0 /* examples */
+#define MDL_INFO_CANVAS_H       1
+#define MDL_INFO_CANVAS_W       2
+#define MDL_INFO_ROWS           3 /* packed rows (padded mode: n) */
+#define MDL_INFO_REAL_PIXELS    4 /* sum of h*w */
+#define MDL_INFO_COMPUTED_CELLS 5 /* cells the MDLSTM computes per direction (padded mode: n*Hmax*Wmax) */
+#define MDL_INFO_MAX_DEPTH      6 /* max over examples of h+w-1: dependent steps per pass */
+#define MDL_INFO_MAX_DIAG       7 /* max over examples of min(h,w): widest anti-diagonal */
+#define MDL_INFO_MODE           8
+#define MDL_INFO_COUNT          9
+
+typedef struct mdl_layout mdl_layout; /* host object, immutable once built */
+
+/*
+ * mdl_pack — place n examples of sizes heights[e] x widths[e] (host arrays) on a
+ * canvas. Host-only, integer, allocates only the returned layout.
+ *
+ * MDL_PACK_ALG1 (§V, §V-A, Appendix B Algorithm 1): canvas width
+ * Wc = max(canvas_w_min, max width); examples are bucketed by height and the
+ * buckets visited tallest first; rows are filled with the widest example of the
+ * current bucket that still fits (ties: lowest index), `sep` separator pixels
+ * between neighbours; a row is closed only when nothing of the current bucket
+ * fits, so it may continue into the next, shorter bucket; rows are stacked
+ * with `sep` separator rows between them, examples top-aligned. The skew of
+ * Algorithm 1's last step is not applied (it changes no cell's value).
+ * MDL_PACK_PADDED (§VII-C, batch padding): slot e at (e*Hmax, 0) of size
+ * Hmax x Wmax, the real pixels top-left; every slot cell is computed.
+ *
+ * Errors: MDL_EINVAL for n < 1, null pointers, a size < 1, sep < 0,
+ * canvas_w_min < 1 or an unknown mode; MDL_EOVERFLOW if Hc*Wc >= 2^31;
+ * MDL_ENOMEM. On success *out owns the layout (free with mdl_layout_free).
+ */
+int mdl_pack(const int32_t* heights, const int32_t* widths, int32_t n, int32_t canvas_w_min,
+             int32_t sep, int32_t mode, mdl_layout** out);
+
+/* Frees a layout from mdl_pack (NULL is ignored). */
+void mdl_layout_free(mdl_layout* layout);
+
+/* Fills info[MDL_INFO_COUNT] (host) with the layout's sizes. */
+int mdl_layout_info(const mdl_layout* layout, int64_t* info);
+
+/*
+ * Host copies of the rectangles, input order, as [n][4] = (y0, x0, h, w):
+ * `rects` the computed region of each example, `real` its real pixels (equal
+ * in MDL_PACK_ALG1 mode). Either pointer may be NULL.
+ */
+int mdl_layout_rects(const mdl_layout* layout, int32_t* rects, int32_t* real);
+
+/*
+ * Original example indices per packed row (Algorithm 1's result): row r holds
+ * row_examples[row_start[r] .. row_start[r+1]-1], left to right.
+ * row_start has info[MDL_INFO_ROWS]+1 entries, row_examples n.
+ */
+int mdl_layout_rows(const mdl_layout* layout, int32_t* row_start, int32_t* row_examples);
+
+/*
+ * Host per-pixel maps (§V: the binary mask, here with the example id): eid[Hc*Wc]
+ * = example covering the pixel's computed region or -1; border[Hc*Wc] bit 0/1/2/3
+ * set when the neighbour (y,x-1)/(y,x+1)/(y-1,x)/(y+1,x) belongs to the same
+ * example. A predecessor whose bit is clear reads as zero hidden and memory state.
+ */
+int mdl_layout_maps(const mdl_layout* layout, int32_t* eid, uint8_t* border);
+
+/*
+ * Size of the device descriptor of a layout (rects, offsets, unit schedule and
+ * the device eid/border maps), and the byte offsets of the eid (int32) and
+ * border (uint8) maps inside it.
+ */
+int mdl_layout_device_size(const mdl_layout* layout, size_t* bytes, size_t* eid_offset,
+                           size_t* border_offset);
+
+/*
+ * Copies the layout's descriptor into d_desc (device, >= the size above) and
+ * builds the eid/border maps there with a kernel. Synchronizes `stream` before
+ * returning, so the layout may be freed afterwards. MDL_ESIZE if bytes is too small.
+ */
+int mdl_layout_upload(const mdl_layout* layout, void* d_desc, size_t bytes, void* stream);
+
+/*
+ * Workspace bytes mdl_forward/mdl_backward need for a layer with C input channels
+ * and H hidden units per direction on this layout: the forward stash (gates and
+ * memory state of every computed cell), the projection / gate-gradient buffer
+ * and the weight-gradient partial sums. The same workspace must be passed,
+ * unmodified, from mdl_forward to the mdl_backward that follows it.
+ */
+int mdl_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes);
+
+/*
+ * Scatter: x_flat (device, flat [h][w][C] per example, dtype MDL_F32 or
+ * MDL_BF16) -> x_canvas (device, [Hc][Wc][C], same dtype), zero outside the real
+ * pixels (separators, unused canvas, padding). Bit-exact copy.
+ */
+int mdl_scatter(const mdl_layout* layout, const void* d_desc, const void* x_flat, int32_t C,
+                int32_t dtype, void* x_canvas, void* stream);
+
+/*
+ * Forward of one 4-direction MDLSTM layer over the canvas.
+ * Input projection x.Wx + b of every computed cell and direction as one GEMM
+ * (§IV-B: the five input matrices computed together; RETURNN §4.2: the
+ * non-recurrent part as one matrix product for the whole batch), then the
+ * recurrence as an anti-diagonal wavefront (§I; RETURNN §4.2: all positions of
+ * a diagonal at once, four directions at once), each example on its own local
+ * diagonals:
+ *   a = x.Wx[d] + b[d] + h_left.Ul[d] + h_up.Uu[d]
+ *   i, f_l, f_u, o = sigmoid(.), g = tanh(.)
+ *   c = f_l*c_left + f_u*c_up + i*g,  h = o*tanh(c)
+ * with predecessors outside the example read as zero (§V mask).
+ * x_canvas [Hc][Wc][C] (x_dtype), h_dirs out [4][Hc][Wc][H] float32 (zero
+ * outside the computed region). ws: >= mdl_workspace_size bytes.
+ * MDL_EUNSUPPORTED when H or the widest diagonal exceed the kernel's LDS budget.
+ */
+int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
+                int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu,
+                const float* b, float* h_dirs, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Direction sum and un-packing (§III four directions combined; §V-A
+ * un-packing by original index and size, separators dropped):
+ * y_flat[e][r][c][k] = sum_{d=0..3} h_dirs[d][y0+r][x0+c][k] over each real pixel,
+ * summed in the order d = 0,1,2,3.
+ */
+int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float* h_dirs,
+                      int32_t H, float* y_flat, void* stream);
+
+/*
+ * 2D BPTT backward of the mdl_forward that filled `ws` (RETURNN §4.2: the
+ * recurrent part back-propagated over the diagonals in reverse, then the
+ * weight and input gradients as matrix products).
+ * Upstream gradient: exactly one of
+ *   dy_flat  (flat [h][w][H], gradient of the direction-summed output; every
+ *            direction receives it), or
+ *   dh_dirs  ([4][Hc][Wc][H], gradient of each direction's output).
+ * Outputs (each may be NULL except the weight gradients):
+ *   dx_flat [h][w][C] float32 per example, dx_canvas [Hc][Wc][C] float32 (zero
+ *   outside the real pixels); dWx, dUl, dUu, db shaped like Wx, Ul, Uu, b.
+ * Weight gradients are fixed-order blocked sums over all computed cells.
+ */
+int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
+                 int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu,
+                 const float* h_dirs, const float* dy_flat, const float* dh_dirs, float* dx_flat,
+                 float* dx_canvas, float* dWx, float* dUl, float* dUu, float* db, void* ws,
+                 size_t ws_bytes, void* stream);
+
+/*
+ * Block-strided convolution between MDLSTM levels (§V-B), kernel kh x kw with
+ * stride kh x kw, as one gather-GEMM over all blocks of all examples:
+ *   x_k1[e][r][c][o] = bc[o] + sum_{d,k,i,j} Wc[o][d][k][i][j] * h_k[d][2r+i][4c+j][k]
+ * (for kh=2, kw=4), where out-of-range input rows/cols read as zero. The
+ * level-k layout `lk` gives where example e's level-k outputs are; the
+ * level-(k+1) layout `lk1` must hold e with size ceil(h/kh) x ceil(w/kw) and
+ * receives x_canvas_k1 [Hc'][Wc'][Cout] float32 (zero outside real pixels).
+ * h_dirs_k [4][Hc][Wc][H]; Wc [Cout][4][H][kh][kw]; bc [Cout].
+ */
+int mdl_blockconv_forward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1,
+                          const void* d_desc_k1, const float* h_dirs_k, int32_t H, int32_t kh,
+                          int32_t kw, const float* Wc, const float* bc, int32_t Cout,
+                          float* x_canvas_k1, void* stream);
+
+/* Workspace bytes for mdl_blockconv_backward (weight-gradient partial sums). */
+int mdl_blockconv_workspace_size(const mdl_layout* lk1, int32_t H, int32_t kh, int32_t kw,
+                                 int32_t Cout, size_t* bytes);
+
+/*
+ * Backward of mdl_blockconv_forward: dx_canvas_k1 [Hc'][Wc'][Cout] -> dh_dirs_k
+ * [4][Hc][Wc][H] (zero outside the level-k real pixels), dWc, dbc (fixed-order sums).
+ */
+int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1,
+                           const void* d_desc_k1, const float* h_dirs_k, int32_t H, int32_t kh,
+                           int32_t kw, const float* Wc, int32_t Cout, const float* dx_canvas_k1,
+                           float* dh_dirs_k, float* dWc, float* dbc, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Kernel timing (measurement support). mdl_timing(1) makes every later launch
+ * record a HIP event pair on its stream around each kernel group (names:
+ * "build_maps", "scatter", "zero_fill", "projection", "fwd_wavefront", "dirsum",
+ * "bwd_wavefront", "wgrad", "dx", "conv_fwd", "conv_bwd"); mdl_timing(0) stops
+ * recording. mdl_timing_report synchronizes the recorded events and writes, for
+ * up to `max` kernel groups, the name (NUL-terminated, 32 bytes per entry in
+ * `names`), the summed milliseconds and the launch count; *count receives the
+ * number of groups; the records are then cleared. Process-wide, not meant for
+ * concurrent use from several threads.
+ */
+int mdl_timing(int32_t enable);
+int mdl_timing_report(int32_t max, char* names, double* total_ms, int64_t* launches, int32_t* count);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* mdl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MDLSTM_H */

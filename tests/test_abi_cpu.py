@@ -1,0 +1,144 @@
+"""Host-side tests of libmdlstm (no GPU needed).
+
+* the library loads and exports every entry point that include/mdlstm.h declares;
+* mdl_pack (host C++) equals the oracle packer bit for bit: Hc, Wc, rectangles,
+  rows, eid and border maps, on seeded and adversarial size lists;
+* argument errors return the documented codes with a message.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _ensure_built():
+    lib = os.path.join(ROOT, "directional_mdlstm_handwriting_amd", "libmdlstm.so")
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+_ensure_built()
+
+import directional_mdlstm_handwriting_amd as M  # noqa: E402
+from oracle import pack as opack  # noqa: E402
+from workloads import make_sizes_only  # noqa: E402
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "mdlstm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mdl_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 15
+    lib = ctypes.CDLL(M.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(M.EXPORTED) == names
+
+
+def _compare(h, w, cw, sep, mode="packed"):
+    lay = M.mdl_pack(h, w, cw, sep, M.MDL_PACK_PADDED if mode == "padded" else M.MDL_PACK_ALG1)
+    ref = opack.pack(h, w, cw, sep, mode)
+    assert (lay.Hc, lay.Wc) == (ref.Hc, ref.Wc)
+    rects, real = M.mdl_layout_rects(lay)
+    assert np.array_equal(rects, ref.rects)
+    assert np.array_equal(real, ref.real)
+    assert M.mdl_layout_rows(lay) == ref.rows
+    eid, border = M.mdl_layout_maps(lay)
+    assert np.array_equal(eid, ref.eid)
+    assert np.array_equal(border, ref.border)
+    N = int(np.sum(np.asarray(h, np.int64) * np.asarray(w, np.int64)))
+    assert lay.info["real_pixels"] == N
+    assert lay.info["computed_cells"] == int(np.sum(ref.rects[:, 2].astype(np.int64) * ref.rects[:, 3]))
+    assert lay.info["max_depth"] == int(np.max(ref.rects[:, 2] + ref.rects[:, 3] - 1))
+    assert lay.info["max_diag"] == int(np.max(np.minimum(ref.rects[:, 2], ref.rects[:, 3])))
+
+
+@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("kind,cw", [("tiny", 8), ("word", 1024), ("line", 2048)])
+def test_packer_matches_oracle(kind, cw, seed):
+    h, w = make_sizes_only(kind, seed)
+    _compare(h, w, cw, 1)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_packer_matches_oracle_adversarial(seed):
+    rng = np.random.default_rng(500 + seed)
+    n = int(rng.integers(1, 129))
+    h = rng.integers(1, 7, n)
+    w = rng.integers(1, 20, n)
+    for sep in (0, 1, 3):
+        _compare(h, w, int(rng.integers(1, 25)), sep)
+
+
+def test_packer_edge_cases():
+    _compare([5], [7], 3, 1)
+    _compare([2, 3, 2], [9, 9, 9], 9, 1)
+    _compare([4] * 4, [5, 2, 5, 3], 10, 1)
+    _compare([1] * 5, [1] * 5, 1, 0)
+    _compare([40] * 128, [200] * 128, 1024, 1)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_padded_matches_oracle(seed):
+    h, w = make_sizes_only("word", seed)
+    _compare(h, w, 1, 0, "padded")
+
+
+def test_word_stack_levels_pack():
+    h, w = make_sizes_only("word", 0, 128)
+    _compare(h, w, 1024, 1)
+    h2, w2 = -(-h // 2), -(-w // 4)
+    _compare(h2, w2, 256, 1)
+    _compare(-(-h2 // 2), -(-w2 // 4), 64, 1)
+
+
+def test_error_codes():
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_pack([], [], 8, 1)
+    assert e.value.code == M.MDL_EINVAL
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_pack([3, 0], [2, 2], 8, 1)
+    assert e.value.code == M.MDL_EINVAL and "size" in M.mdl_last_error()
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_pack([3], [3], 8, -1)
+    assert e.value.code == M.MDL_EINVAL
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_pack([3], [3], 8, 1, mode=7)
+    assert e.value.code == M.MDL_EINVAL
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_pack([2 ** 16], [2 ** 15], 1, 1)
+    assert e.value.code == M.MDL_EOVERFLOW
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_pack([2 ** 16, 2 ** 16], [2 ** 14, 2 ** 14], 1, 0, mode=M.MDL_PACK_PADDED)
+    assert e.value.code == M.MDL_EOVERFLOW
+    lib = M.library()
+    assert lib.mdl_layout_info(None, None) == M.MDL_EINVAL
+    lay = M.mdl_pack([3, 4], [5, 6], 8, 1)
+    b = ctypes.c_size_t()
+    assert lib.mdl_workspace_size(lay.handle, 0, 4, ctypes.byref(b)) == M.MDL_EINVAL
+    # device entry points validate before touching the device
+    assert lib.mdl_forward(lay.handle, None, None, 0, 1, 4, None, None, None, None, None, None, 0, None) == M.MDL_EINVAL
+    assert lib.mdl_backward(lay.handle, 1, 1, 0, 1, 4, 1, 1, 1, 1, 1, 1, None, None, 1, 1, 1, 1, 1, 1, None) \
+        == M.MDL_EINVAL   # both dy_flat and dh_dirs given
+    assert "exactly one" in M.mdl_last_error()
+    assert lib.mdl_scatter(lay.handle, 1, 1, 1, 5, 1, None) == M.MDL_EINVAL
+    ws = M.mdl_workspace_size(lay, 4, 16)
+    assert lib.mdl_forward(lay.handle, 1, 1, 0, 4, 16, 1, 1, 1, 1, 1, 1, ws - 1, None) == M.MDL_ESIZE
+
+
+def test_workspace_grows_with_size():
+    lay = M.mdl_pack([10, 12], [30, 20], 64, 1)
+    a = M.mdl_workspace_size(lay, 4, 16)
+    b = M.mdl_workspace_size(lay, 4, 32)
+    T = lay.info["computed_cells"]
+    assert b > a >= 4 * T * (6 * 16 + 5 * 16) * 4
