@@ -18,6 +18,12 @@ from typing import Optional
 
 import numpy as np
 
+# torch is imported before the library is loaded: its HIP runtime then is the one
+# libamdhip64 dependency the library binds to, so the device pointers and stream
+# handles torch hands over belong to the same runtime instance as the library's
+# own HIP calls (a second runtime loaded first finds no device it can use).
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmdlstm.so")
 

@@ -39,6 +39,7 @@ mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     D.flat_off = reinterpret_cast<const int64_t*>(b + L.off.flat_off);
     D.cell_off = reinterpret_cast<const int64_t*>(b + L.off.cell_off);
     D.units = reinterpret_cast<const int32_t*>(b + L.off.units);
+    D.chunks = reinterpret_cast<const int32_t*>(b + L.off.chunks);
     D.eid = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(b + L.off.eid));
     D.border = const_cast<uint8_t*>(b + L.off.border);
     D.n = L.n;
@@ -48,6 +49,7 @@ mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     D.N = L.real_pixels;
     D.max_depth = L.max_depth;
     D.max_diag = L.max_diag;
+    D.nchunks = L.nchunks;
     return D;
 }
 
@@ -223,7 +225,7 @@ int mdl_layout_upload(const mdl_layout* layout, void* d_desc, size_t bytes, void
 int mdl_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes) {
     if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_workspace_size: null argument");
     if (C < 1 || H < 1) return fail(MDL_EINVAL, "mdl_workspace_size: need C >= 1 and H >= 1");
-    *bytes = mdl::ws_layout(L_of(layout).computed_cells, C, H).total;
+    *bytes = mdl::ws_layout(L_of(layout).computed_cells, L_of(layout).nchunks, C, H).total;
     return MDL_OK;
 }
 
@@ -251,14 +253,17 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     if (rc) return rc;
     if (!x_canvas || !Wx || !Ul || !Uu || !b || !h_dirs || !ws) return fail(MDL_EINVAL, "mdl_forward: null tensor");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nchunks, C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
-    if ((int64_t)L.max_diag * H > mdl::chain_max_items())
+    if (!mdl::chain_uses_mfma(H, L.max_diag) && (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_forward: widest diagonal x H exceeds the wavefront kernel's items");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
     if (mdl::fwd_chain_lds(H, L.max_diag) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_forward: recurrent weights and diagonal state exceed LDS");
+    // the kernels address these tensors with 32-bit byte offsets
+    if (4 * L.computed_cells * 6 * H * 4 >= (int64_t(1) << 31) || 4LL * L.Hc * L.Wc * H * 4 >= (int64_t(1) << 31))
+        return fail(MDL_EUNSUPPORTED, "mdl_forward: per-layer tensors above 2 GiB");
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -312,19 +317,21 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     if ((dy_flat == nullptr) == (dh_dirs == nullptr))
         return fail(MDL_EINVAL, "mdl_backward: pass exactly one of dy_flat and dh_dirs");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nchunks, C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_backward: workspace smaller than mdl_workspace_size");
-    if ((int64_t)L.max_diag * H > mdl::chain_max_items())
+    if (!mdl::chain_uses_mfma(H, L.max_diag) && (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_backward: widest diagonal x H exceeds the wavefront kernel's items");
-    const int R = C + 1 + 2 * H, G = 5 * H;
     if (!mdl::wgrad_supported(C, H))
         return fail(MDL_EUNSUPPORTED, "mdl_backward: C and H exceed the weight-gradient kernel's register tile");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
     if (mdl::bwd_chain_lds(H, L.max_diag) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward: recurrent weights and diagonal state exceed LDS");
-    if (sizeof(float) * 32 * (size_t)(R + G) > lmax)
+    if (mdl::wgrad_lds_bytes(C, H) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward: weight-gradient tile exceeds LDS");
+    // the kernels address these tensors with 32-bit byte offsets
+    if (4 * L.computed_cells * 6 * H * 4 >= (int64_t(1) << 31) || 4LL * L.Hc * L.Wc * H * 4 >= (int64_t(1) << 31))
+        return fail(MDL_EUNSUPPORTED, "mdl_backward: per-layer tensors above 2 GiB");
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -337,16 +344,17 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
         e = mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward: reverse wavefront");
+    if (dx_canvas) {
+        Timed t("zero_fill", st);
+        e = mdl::launch_zero_outside(D, dx_canvas, C, 1, st);
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward: zero fill");
+    }
     {
         Timed t("wgrad", st);
-        e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, part, W.nchunks, dWx, dUl, dUu, db, st);
+        e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dWx, dUl, dUu, db, dx_flat, dx_canvas,
+                              st);
     }
-    if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight gradients");
-    if (dx_flat || dx_canvas) {
-        Timed t("dx", st);
-        e = mdl::launch_dx(D, C, H, Wx, dA, dx_flat, dx_canvas, st);
-        if (e != hipSuccess) return hip_fail(e, "mdl_backward: input gradient");
-    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight and input gradients");
     return MDL_OK;
     GUARD_END
 }

@@ -24,7 +24,21 @@ namespace {
 constexpr int CHAIN_THREADS = 256;
 constexpr int MAXI = 8;  // (cell, hidden) items per thread and step
 
-__device__ inline float sigm(float z) { return 1.0f / (1.0f + expf(-z)); }
+// Gate nonlinearities on the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32,
+// about 1 ulp each). sigmoid(z) = 1 / (1 + e^-z); tanh(x) = (1 - e^-2|x|) / (1 + e^-2|x|)
+// with the sign of x, and for |x| < 1/8 its odd Taylor polynomial to x^9, so that
+// tanh keeps its relative accuracy near 0 instead of losing it to cancellation.
+__device__ inline float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ inline float sigm(float z) { return frcp(1.0f + fexp(-z)); }
+__device__ inline float ftanh(float x) {
+    const float ax = fabsf(x);
+    const float e = fexp(-2.0f * ax);
+    const float big = (1.0f - e) * frcp(1.0f + e);
+    const float x2 = x * x;
+    const float small = ax * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f + x2 * (62.0f / 2835.0f)))));
+    return copysignf(ax < 0.125f ? small : big, x);
+}
 
 // Forward. Z [4][T][5H], stash out [4][T][6H] = (i, f_l, f_u, o, g, c) per cell,
 // h_dirs out [4][Hc][Wc][H].
@@ -126,9 +140,9 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
                     cu = cp[(a - 1 - lop) * H + k];
                 }
                 const float ig = sigm(acc0), fl = sigm(acc1), fu = sigm(acc2), og = sigm(acc3);
-                const float gg = tanhf(acc4);
+                const float gg = ftanh(acc4);
                 const float c = fl * cl + fu * cu + ig * gg;
-                const float hv = og * tanhf(c);
+                const float hv = og * ftanh(c);
                 hn[j * H + k] = hv;
                 cn[j * H + k] = c;
                 Hd[((int64_t)F.y(a) * D.Wc + F.x(b)) * H + k] = hv;
@@ -232,7 +246,7 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
                     for (int n = 0; n < G; ++n) dh += dv[n] * ut[n * H2];
                     dcin += dcur[jd * H + k];
                 }
-                const float tc = tanhf(c);
+                const float tc = ftanh(c);
                 const float dov = dh * tc;
                 const float dc = dcin + dh * og * (1.f - tc * tc);
                 const float d0 = dc * gg * ig * (1.f - ig);
@@ -252,21 +266,377 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
     }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Matrix-core variants. The recurrent contraction of one step is dense: for the
+// cells of a diagonal, [h_left | h_up] (2H) times [Ul; Uu] (2H x 5H) in the
+// forward, [da_right | da_down] (10H) times [Ul^T; Uu^T] (10H x H) in the
+// backward. Each wave owns one block of 16 hidden units (kb) and keeps that
+// block's weight columns as v_mfma_f32_16x16x4_f32 B fragments in registers
+// for the whole pass; the A fragments (16 cells x 4 inputs) come from the LDS
+// copy of the previous diagonal, with a zero row standing in for predecessors
+// outside the example. Gate columns are taken per gate type for the lane's
+// hidden unit, so after the MFMAs each lane holds all five pre-activations of
+// its 4 (cell, hidden unit) pairs and finishes the cell update in registers.
+// The projection x.Wx+b seeds the accumulators; next-step operands are
+// prefetched from HBM while the current step computes.
+// ---------------------------------------------------------------------------------------------
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// All global traffic of the step loops goes through raw buffer loads/stores on
+// per-unit buffer descriptors. A lane without a valid (cell, hidden unit) uses
+// an offset past the descriptor's range: its load returns 0 and its store is
+// dropped by the hardware. So every lane issues the same memory instructions
+// in every step, with no branches around them, and the compiler can wait for a
+// prefetch with vmcnt(N) while the step's stores stay in flight (loads and
+// stores share one in-order counter on this architecture) instead of draining
+// every store before each step.
+constexpr uint32_t kBufCfg = 0x00020000;   // dword 3 of a raw 32-bit buffer descriptor (gfx9 family)
+constexpr int kOOB = 0x40000000;            // byte offset past every per-unit range used here (1 GiB)
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufCfg);
+}
+__device__ inline float bld(__amdgpu_buffer_rsrc_t r, int off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void bst(float v, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+template <int H>
+__global__ __launch_bounds__(256) void k_fwd_mfma(Dev D, int, int Lmax, const float* __restrict__ Ul,
+                                                  const float* __restrict__ Uu, const float* __restrict__ Z,
+                                                  float* __restrict__ stash, float* __restrict__ hdirs) {
+    constexpr int KS = (2 * H + 3) / 4;        // k-steps over [h_left; h_up]
+    constexpr int KB = H <= 16 ? 1 : H <= 32 ? 2 : 4;  // blocks of 16 hidden units
+    const int u = D.units[blockIdx.x];
+    const int e = u >> 2, d = u & 3;
+    const Flip F{D.rect[4 * e], D.rect[4 * e + 1], D.rect[4 * e + 2], D.rect[4 * e + 3], (d & 2) != 0, (d & 1) != 0};
+    const int h = F.h, w = F.w;
+    constexpr int G = 5 * H;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kb = wave % KB, mt = wave / KB;   // one block of 16 hidden units, one M-tile of 16 cells
+    const int kk = kb * 16 + (lane & 15);      // hidden unit of this lane's output column
+    const bool kok = kk < H;
+    const int krow = lane >> 4;                // input offset within a k-step of the A and B operands
+    const int orow = mt * 16 + 4 * (lane >> 4);  // first of this lane's 4 output cells on a diagonal
+
+    float Bw[5][KS];                            // [Ul; Uu][4ks + krow][g*H + kk]
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int kr = 4 * ks + krow;
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            float v = 0.f;
+            if (kok && kr < 2 * H)
+                v = kr < H ? Ul[((int64_t)d * H + kr) * G + g * H + kk] : Uu[((int64_t)d * H + kr - H) * G + g * H + kk];
+            Bw[g][ks] = v;
+        }
+    }
+    extern __shared__ float lds[];
+    const int ZR = 16 * ((Lmax + 15) / 16);    // zero row; rows [0, ZR) hold a diagonal
+    const int LR = ZR + 1;
+    float* hb = lds;                            // [2][LR][H]
+    float* cb = hb + 2 * LR * H;                // [2][LR][H]
+    for (int i = threadIdx.x; i < 4 * LR * H; i += blockDim.x) lds[i] = 0.f;
+    const int64_t base = (int64_t)d * D.T + D.cell_off[e];
+    const int64_t cells = (int64_t)h * w;
+    const __amdgpu_buffer_rsrc_t rZ = rsrc(Z + base * G, cells * G * 4);
+    const __amdgpu_buffer_rsrc_t rS = rsrc(stash + base * 6 * H, cells * 6 * H * 4);
+    const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4);
+    const int S = h + w - 1;
+
+    auto load_z = [&](int s, float (&z)[5][4]) {
+        const int L = s < S ? dg_len(h, w, s) : 0;
+        const int st = s < S ? (int)dg_start(h, w, s) : 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jo = orow + r;
+            const bool ok = jo < L && kok;
+            const int off = ok ? ((st + jo) * G + kk) * 4 : kOOB;
+#pragma unroll
+            for (int g = 0; g < 5; ++g) z[g][r] = bld(rZ, off + g * H * 4);
+        }
+    };
+    auto step = [&](int s, float (&zc)[5][4], float (&zn)[5][4]) {
+        const int L = dg_len(h, w, s), lo = dg_lo(h, w, s);
+        const int st = (int)dg_start(h, w, s);
+        const int lop = dg_lo(h, w, s - 1);
+        load_z(s + 1, zn);                      // prefetch; consumed one step later
+        const float* hp = hb + ((s + 1) & 1) * LR * H;
+        const float* cp = cb + ((s + 1) & 1) * LR * H;
+        float* hn = hb + (s & 1) * LR * H;
+        float* cn = cb + (s & 1) * LR * H;
+        f32x4 acc[5];
+#pragma unroll
+        for (int g = 0; g < 5; ++g) acc[g] = f32x4{zc[g][0], zc[g][1], zc[g][2], zc[g][3]};
+        if (mt * 16 < L) {                      // uniform over the wave; no global memory inside
+            const int ja = mt * 16 + (lane & 15);
+            const int aA = lo + ja, bA = s - aA;
+            const int rl = (ja < L && bA > 0) ? aA - lop : ZR;
+            const int ru = (ja < L && aA > 0) ? aA - 1 - lop : ZR;
+            // A operand addresses first (the zero row stands in for a missing predecessor), then one
+            // unconditional LDS read per k-step, all issued ahead of the MFMA chain
+            float av[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int kr = 4 * ks + krow;
+                const int idx = kr < H ? rl * H + kr : (kr < 2 * H ? ru * H + kr - H : ZR * H);
+                av[ks] = hp[idx];
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int g = 0; g < 5; ++g) acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], Bw[g][ks], acc[g], 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jo = orow + r;
+            const bool ok = jo < L && kok;
+            const int a = lo + jo, b = s - a;
+            const int kc = kok ? kk : 0;
+            const float cl = cp[((ok && b > 0) ? a - lop : ZR) * H + kc];
+            const float cu = cp[((ok && a > 0) ? a - 1 - lop : ZR) * H + kc];
+            const float ig = sigm(acc[0][r]), fl = sigm(acc[1][r]), fu = sigm(acc[2][r]), og = sigm(acc[3][r]);
+            const float gg = ftanh(acc[4][r]);
+            const float c = fl * cl + fu * cu + ig * gg;
+            const float hv = og * ftanh(c);
+            if (ok) {
+                hn[jo * H + kk] = hv;
+                cn[jo * H + kk] = c;
+            }
+            bst(hv, rH, ok ? (int)(((int64_t)F.y(a) * D.Wc + F.x(b)) * H + kk) * 4 : kOOB);
+            const int so = ok ? ((st + jo) * 6 * H + kk) * 4 : kOOB;
+            bst(ig, rS, so);
+            bst(fl, rS, so + H * 4);
+            bst(fu, rS, so + 2 * H * 4);
+            bst(og, rS, so + 3 * H * 4);
+            bst(gg, rS, so + 4 * H * 4);
+            bst(c, rS, so + 5 * H * 4);
+        }
+        __syncthreads();
+    };
+    float zA[5][4], zB[5][4];
+    load_z(0, zA);
+    __syncthreads();
+    int s = 0;
+    for (; s + 1 < S; s += 2) {
+        step(s, zA, zB);
+        step(s + 1, zB, zA);
+    }
+    if (s < S) step(s, zA, zB);
+}
+
+template <int H>
+__global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const float* __restrict__ Ul,
+                                                  const float* __restrict__ Uu, const float* __restrict__ stash,
+                                                  const float* __restrict__ dy_flat,
+                                                  const float* __restrict__ dh_dirs, float* __restrict__ dA) {
+    constexpr int G = 5 * H;
+    constexpr int KS = (2 * G + 3) / 4;        // k-steps over [da_right; da_down]
+    constexpr int KB = H <= 16 ? 1 : H <= 32 ? 2 : 4;
+    const int u = D.units[blockIdx.x];
+    const int e = u >> 2, d = u & 3;
+    const Flip F{D.rect[4 * e], D.rect[4 * e + 1], D.rect[4 * e + 2], D.rect[4 * e + 3], (d & 2) != 0, (d & 1) != 0};
+    const int h = F.h, w = F.w;
+    const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kb = wave % KB, mt = wave / KB;
+    const int kk = kb * 16 + (lane & 15);
+    const bool kok = kk < H;
+    const int krow = lane >> 4;
+    const int orow = mt * 16 + 4 * (lane >> 4);
+
+    float Bw[KS];                               // [Ul^T; Uu^T][4ks + krow][kk]
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int n = 4 * ks + krow;
+        float v = 0.f;
+        if (kok && n < 2 * G)
+            v = n < G ? Ul[((int64_t)d * H + kk) * G + n] : Uu[((int64_t)d * H + kk) * G + n - G];
+        Bw[ks] = v;
+    }
+    extern __shared__ float lds[];
+    const int ZR = 16 * ((Lmax + 15) / 16);
+    const int LR = ZR + 1;
+    float* dab = lds;                           // [2][LR][G]   gate gradients of the later diagonal
+    float* dcl = dab + 2 * LR * G;              // [2][LR][H]   dc * f_l
+    float* dcu = dcl + 2 * LR * H;              // [2][LR][H]   dc * f_u
+    for (int i = threadIdx.x; i < 2 * LR * G + 4 * LR * H; i += blockDim.x) lds[i] = 0.f;
+    const int64_t base = (int64_t)d * D.T + D.cell_off[e];
+    const int64_t cells = (int64_t)h * w;
+    const __amdgpu_buffer_rsrc_t rS = rsrc(stash + base * 6 * H, cells * 6 * H * 4);
+    const __amdgpu_buffer_rsrc_t rA = rsrc(dA + base * G, cells * G * 4);
+    // upstream gradient: per-direction canvas tensor, or the flat gradient of the direction sum
+    const bool per_dir = dh_dirs != nullptr;
+    const __amdgpu_buffer_rsrc_t rU =
+        per_dir ? rsrc(dh_dirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4)
+                : rsrc(dy_flat + D.flat_off[e] * H, (int64_t)rh * rw * H * 4);
+    const int S = h + w - 1;
+
+    // per output cell: i, f_l, f_u, o, g, c, c_left, c_up, upstream dh
+    auto load_v = [&](int s, float (&v)[9][4]) {
+        const bool in = s >= 0;
+        const int L = in ? dg_len(h, w, s) : 0, lo = in ? dg_lo(h, w, s) : 0;
+        const int st = in ? (int)dg_start(h, w, s) : 0;
+        const int lop = s > 0 ? dg_lo(h, w, s - 1) : 0;
+        const int stp = s > 0 ? (int)dg_start(h, w, s - 1) : 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jo = orow + r;
+            const bool ok = jo < L && kok;
+            const int a = lo + jo, b = s - a;
+            const int so = ok ? ((st + jo) * 6 * H + kk) * 4 : kOOB;
+#pragma unroll
+            for (int g = 0; g < 6; ++g) v[g][r] = bld(rS, so + g * H * 4);
+            v[6][r] = bld(rS, (ok && b > 0) ? ((stp + a - lop) * 6 * H + 5 * H + kk) * 4 : kOOB);
+            v[7][r] = bld(rS, (ok && a > 0) ? ((stp + a - 1 - lop) * 6 * H + 5 * H + kk) * 4 : kOOB);
+            const int y = F.y(a), x = F.x(b);
+            const int ly = y - ry0, lx = x - rx0;
+            int uo = kOOB;
+            if (ok && per_dir) uo = (int)(((int64_t)y * D.Wc + x) * H + kk) * 4;
+            if (ok && !per_dir && ly < rh && lx < rw) uo = ((ly * rw + lx) * H + kk) * 4;
+            v[8][r] = bld(rU, uo);
+        }
+    };
+    auto step = [&](int s, float (&vc)[9][4], float (&vn)[9][4]) {
+        const int L = dg_len(h, w, s), lo = dg_lo(h, w, s);
+        const int st = (int)dg_start(h, w, s);
+        const int lon = dg_lo(h, w, s + 1);
+        load_v(s - 1, vn);                      // prefetch; consumed one step later
+        const float* dar = dab + ((s + 1) & 1) * LR * G;
+        const float* dclr = dcl + ((s + 1) & 1) * LR * H;
+        const float* dcur = dcu + ((s + 1) & 1) * LR * H;
+        float* daw = dab + (s & 1) * LR * G;
+        float* dclw = dcl + (s & 1) * LR * H;
+        float* dcuw = dcu + (s & 1) * LR * H;
+        f32x4 acc = f32x4{vc[8][0], vc[8][1], vc[8][2], vc[8][3]};
+        if (mt * 16 < L) {                      // uniform over the wave; no global memory inside
+            const int ja = mt * 16 + (lane & 15);
+            const int aA = lo + ja, bA = s - aA;
+            const int jr = (ja < L && bA + 1 < w) ? aA - lon : ZR;       // right successor (a, b+1)
+            const int jd = (ja < L && aA + 1 < h) ? aA + 1 - lon : ZR;   // lower successor (a+1, b)
+            // A operand addresses first (zero row for a missing successor), one unconditional LDS read
+            // per k-step issued ahead of the MFMAs; two accumulators halve the dependent chain
+            float av[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int n = 4 * ks + krow;
+                const int idx = n < G ? jr * G + n : (n < 2 * G ? jd * G + n - G : ZR * G);
+                av[ks] = dar[idx];
+            }
+            f32x4 acc2 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks & 1) acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], Bw[ks], acc2, 0, 0, 0);
+                else acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], Bw[ks], acc, 0, 0, 0);
+            }
+            acc += acc2;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int jo = orow + r;
+            const bool ok = jo < L && kok;
+            const int a = lo + jo, b = s - a;
+            const float dh = acc[r];
+            const int kc = kok ? kk : 0;
+            const float dcin = dclr[((ok && b + 1 < w) ? a - lon : ZR) * H + kc] +
+                               dcur[((ok && a + 1 < h) ? a + 1 - lon : ZR) * H + kc];
+            const float ig = vc[0][r], fl = vc[1][r], fu = vc[2][r], og = vc[3][r];
+            const float gg = vc[4][r], c = vc[5][r], cl = vc[6][r], cu = vc[7][r];
+            const float tc = ftanh(c);
+            const float dov = dh * tc;
+            const float dc = dcin + dh * og * (1.f - tc * tc);
+            const float d0 = dc * gg * ig * (1.f - ig);
+            const float d1 = dc * cl * fl * (1.f - fl);
+            const float d2 = dc * cu * fu * (1.f - fu);
+            const float d3 = dov * og * (1.f - og);
+            const float d4 = dc * ig * (1.f - gg * gg);
+            if (ok) {
+                float* dw = daw + jo * G + kk;
+                dw[0] = d0; dw[H] = d1; dw[2 * H] = d2; dw[3 * H] = d3; dw[4 * H] = d4;
+                dclw[jo * H + kk] = dc * fl;
+                dcuw[jo * H + kk] = dc * fu;
+            }
+            const int ao = ok ? ((st + jo) * G + kk) * 4 : kOOB;
+            bst(d0, rA, ao);
+            bst(d1, rA, ao + H * 4);
+            bst(d2, rA, ao + 2 * H * 4);
+            bst(d3, rA, ao + 3 * H * 4);
+            bst(d4, rA, ao + 4 * H * 4);
+        }
+        __syncthreads();
+    };
+    float vA[9][4], vB[9][4];
+    load_v(S - 1, vA);
+    __syncthreads();
+    int s = S - 1;
+    for (; s - 1 >= 0; s -= 2) {
+        step(s, vA, vB);
+        step(s - 1, vB, vA);
+    }
+    if (s >= 0) step(s, vA, vB);
+}
+
+typedef void (*FwdKernel)(Dev, int, int, const float*, const float*, const float*, float*, float*);
+typedef void (*BwdKernel)(Dev, int, int, const float*, const float*, const float*, const float*, const float*, float*);
+
+// instantiated hidden sizes: the workloads' 2, 4, 10, 16, 32 and 50
+struct MfmaEntry {
+    int H;
+    FwdKernel fwd;
+    BwdKernel bwd;
+    int KB;
+};
+const MfmaEntry kMfma[] = {
+    {2, k_fwd_mfma<2>, k_bwd_mfma<2>, 1},
+    {4, k_fwd_mfma<4>, k_bwd_mfma<4>, 1},
+    {10, k_fwd_mfma<10>, k_bwd_mfma<10>, 1},
+    {16, k_fwd_mfma<16>, k_bwd_mfma<16>, 1},
+    {32, k_fwd_mfma<32>, k_bwd_mfma<32>, 2},
+    {50, k_fwd_mfma<50>, k_bwd_mfma<50>, 4},
+};
+
+// one M-tile of 16 cells per wave: 4/KB tiles cover the widest diagonal
+const MfmaEntry* mfma_entry(int H, int Lmax) {
+    for (const auto& m : kMfma)
+        if (m.H == H) return (Lmax + 15) / 16 <= 4 / m.KB ? &m : nullptr;
+    return nullptr;
+}
+
+int lds_rows(int Lmax) { return 16 * ((Lmax + 15) / 16) + 1; }
+size_t fwd_mfma_lds(int H, int Lmax) { return sizeof(float) * (size_t)4 * lds_rows(Lmax) * H; }
+size_t bwd_mfma_lds(int H, int Lmax) {
+    return sizeof(float) * ((size_t)2 * lds_rows(Lmax) * 5 * H + (size_t)4 * lds_rows(Lmax) * H);
+}
+
 }  // namespace
 
 int chain_max_items() { return MAXI * CHAIN_THREADS; }
 
+
 size_t fwd_chain_lds(int H, int Lmax) {
+    if (mfma_entry(H, Lmax)) return fwd_mfma_lds(H, Lmax);
     return sizeof(float) * ((size_t)2 * H * 5 * H + (size_t)4 * Lmax * H);
 }
 
 size_t bwd_chain_lds(int H, int Lmax) {
+    if (mfma_entry(H, Lmax)) return bwd_mfma_lds(H, Lmax);
     return sizeof(float) * ((size_t)2 * H * 5 * H + (size_t)2 * Lmax * 5 * H + (size_t)4 * Lmax * H);
 }
+
+bool chain_uses_mfma(int H, int Lmax) { return mfma_entry(H, Lmax) != nullptr; }
 
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
                             float* h_dirs, hipStream_t st) {
     const int Lmax = D.max_diag;
+    if (const MfmaEntry* m = mfma_entry(H, Lmax)) {
+        hipLaunchKernelGGL(m->fwd, dim3(4 * D.n), dim3(256), fwd_mfma_lds(H, Lmax), st, D, H, Lmax, Ul, Uu, Z, stash,
+                           h_dirs);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_fwd_chain, dim3(4 * D.n), dim3(CHAIN_THREADS), fwd_chain_lds(H, Lmax), st, D, H, Lmax, Ul,
                        Uu, Z, stash, h_dirs);
     return hipGetLastError();
@@ -275,6 +645,11 @@ hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* U
 hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                             const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st) {
     const int Lmax = D.max_diag;
+    if (const MfmaEntry* m = mfma_entry(H, Lmax)) {
+        hipLaunchKernelGGL(m->bwd, dim3(4 * D.n), dim3(256), bwd_mfma_lds(H, Lmax), st, D, H, Lmax, Ul, Uu, stash,
+                           dy_flat, dh_dirs, dA);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_bwd_chain, dim3(4 * D.n), dim3(CHAIN_THREADS), bwd_chain_lds(H, Lmax), st, D, H, Lmax, Ul,
                        Uu, stash, dy_flat, dh_dirs, dA);
     return hipGetLastError();

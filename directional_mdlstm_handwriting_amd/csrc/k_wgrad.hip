@@ -2,142 +2,362 @@
 //
 // RETURNN §4.2: after the recurrent part is back-propagated through time, the
 // gradients with respect to the weights and the inputs are matrix products
-// over the whole batch. For direction d, with A-row r(p) = [x(p), 1, h_left(p),
-// h_up(p)] (predecessors outside the example read as zero) and gate gradient
-// da(p):
-//     [dWx; db; dUl; dUu][d] = sum over computed cells p of r(p)^T da(p)
-//     dx(p) = sum_d da_d(p) Wx[d]^T
-// The sum over cells is a fixed-order two-stage reduction: chunks of
-// WGRAD_CHUNK consecutive stash cells give partial sums (stage 1), which are
-// added chunk by chunk in order (stage 2). No atomics, so results are
-// bit-reproducible.
+// over the whole batch. For direction d, with the A-row of a computed cell p
+//     r(p) = [x(p), 1, h_left(p), h_up(p)]      (C + 1 + 2H values; a predecessor
+//                                              outside the example reads as zero)
+// and its gate gradient da_d(p) (5H values):
+//     [dWx; db; dUl; dUu][d] = sum over computed cells p of r(p)^T da_d(p)
+//     dx(p)                  = sum over d of da_d(p) Wx[d]^T
+// One workgroup takes one chunk of rows of one example (the layout's chunk
+// table) for all four directions: it stages tiles of TP cells of A-rows and
+// gate gradients in LDS, accumulates r^T da on the matrix cores
+// (v_mfma_f32_16x16x4_f32, K = cells, fp32 products and sums; wave d owns
+// direction d's output tiles, up to 32 per pass over the chunk), and computes
+// dx of the same cells from the staged gate gradients. Chunk partial sums are then added in
+// chunk order by a second kernel, so the result is bit-reproducible.
 #include "kernels.h"
 
 namespace mdl {
 
-WsLayout ws_layout(int64_t T, int C, int H) {
+WsLayout ws_layout(int64_t T, int64_t nchunks, int C, int H) {
     auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
     WsLayout w;
     const int G = 5 * H;
     const int R = C + 1 + 2 * H;
-    w.nchunks = (T + WGRAD_CHUNK - 1) / WGRAD_CHUNK;
+    w.nchunks = nchunks;
     size_t p = 0;
     w.stash = p; p = al(p + sizeof(float) * 4 * (size_t)T * 6 * H);
     w.zda = p;   p = al(p + sizeof(float) * 4 * (size_t)T * G);
-    w.part = p;  p = al(p + sizeof(float) * 4 * (size_t)w.nchunks * R * G);
+    w.part = p;  p = al(p + sizeof(float) * 4 * (size_t)nchunks * R * G);
     w.total = p;
     return w;
 }
 
 namespace {
 
-constexpr int WG_THREADS = 1024;
-constexpr int MAXE = 32;   // output entries per thread
-constexpr int TILE = 32;   // cells staged in LDS at a time
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int ACC_TILES = 16;   // 16x16 output tiles one wave owns per pass
+constexpr int STAGE_H = 4096;   // staged predecessor-h values per tile (all directions)
+constexpr int STAGE_D = 10240;  // staged gate-gradient values per tile (all directions)
 
-template <typename XT> __device__ inline float to_f32(XT v);
-template <> __device__ inline float to_f32<float>(float v) { return v; }
-template <> __device__ inline float to_f32<uint16_t>(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+constexpr uint32_t kBufCfg = 0x00020000;  // dword 3 of a raw 32-bit buffer descriptor (gfx9 family)
+constexpr int kOOB = 0x7ffffff0;           // byte offset past every range: loads return 0
 
-// grid (nchunks, 4): partial sums of r(p)^T da(p) over one chunk of direction d's cells
-template <typename XT>
-__global__ __launch_bounds__(WG_THREADS) void k_wgrad_partial(Dev D, const XT* __restrict__ xc, int C, int H,
-                                                              const float* __restrict__ hdirs,
-                                                              const float* __restrict__ dA,
-                                                              float* __restrict__ part, int64_t nchunks) {
-    const int d = blockIdx.y;
-    const int64_t g0 = (int64_t)blockIdx.x * WGRAD_CHUNK;
-    const int64_t g1 = g0 + WGRAD_CHUNK < D.T ? g0 + WGRAD_CHUNK : D.T;
-    const int G = 5 * H, R = C + 1 + 2 * H, E = R * G;
-    const bool fy = (d & 2) != 0, fx = (d & 1) != 0;
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufCfg);
+}
+__device__ inline float bld(__amdgpu_buffer_rsrc_t r, int off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// n / d for n < 2^16, d < 2^16, with m = 2^32 / d + 1
+__host__ __device__ inline uint32_t magic(uint32_t d) { return (uint32_t)(0xffffffffu / d) + 1u; }
+__device__ inline int fdiv(int n, uint32_t m) { return (int)__umulhi((uint32_t)n, m); }
+
+struct WgradShape {
+    int C, H, G, R, MT, NT, Q, P, TP;  // Q N-tiles per pass, P passes over the chunk, TP cells per tile
+    int nh, nd, nx;                  // staged elements per tile: predecessor h, gate gradients, x
+    uint32_t m_hd, m_h2, m_gd, m_g, m_x;
+    int wx_lds;                      // Wx copied to LDS
+    int sp;                          // threads per dx output
+};
+
+__host__ __device__ inline size_t wgrad_lds_floats(const WgradShape& s) {
+    return (size_t)s.nx + s.nh + s.nd + 4 * (size_t)s.TP * s.C + 1;
+}
+
+inline WgradShape wgrad_shape(int C, int H) {
+    WgradShape s;
+    s.C = C;
+    s.H = H;
+    s.G = 5 * H;
+    s.R = C + 1 + 2 * H;
+    s.MT = (s.R + 15) / 16;
+    s.NT = (s.G + 15) / 16;
+    s.Q = ACC_TILES / s.MT < 1 ? 1 : ACC_TILES / s.MT;   // N-tiles per pass (all M-tiles each pass)
+    if (s.Q > s.NT) s.Q = s.NT;
+    s.P = (s.NT + s.Q - 1) / s.Q;
+    s.TP = 32;
+    while (s.TP > 4 && (4 * s.TP * 2 * H > STAGE_H || 4 * s.TP * s.G > STAGE_D)) s.TP /= 2;
+    s.nh = 4 * s.TP * 2 * H;
+    s.nd = 4 * s.TP * s.G;
+    s.nx = s.TP * (C + 1);
+    s.m_hd = magic(s.TP * 2 * H);
+    s.m_h2 = magic(2 * H);
+    s.m_gd = magic(s.TP * s.G);
+    s.m_g = magic(s.G);
+    s.m_x = magic(C + 1);
+    s.wx_lds = 0;
+    s.sp = 1;
+    return s;
+}
+
+// position of region-local cell (ly, lx) of an h x w region in direction d's diagonal-major order
+__device__ inline int stash_index(int h, int w, int ly, int lx, int d) {
+    const int a = (d & 2) ? h - 1 - ly : ly;
+    const int b = (d & 1) ? w - 1 - lx : lx;
+    const int s = a + b;
+    return (int)dg_start(h, w, s) + (a - dg_lo(h, w, s));
+}
+
+// CT/HT > 0: channel count and hidden size fixed at compile time (loops unroll, divisions fold);
+// 0: taken from the shape at run time.
+template <bool BF16, int CT, int HT>
+__global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restrict__ xc, WgradShape S,
+                                                    const float* __restrict__ hdirs, const float* __restrict__ dA,
+                                                    const float* __restrict__ Wx, float* __restrict__ part,
+                                                    float* __restrict__ dx_flat, float* __restrict__ dx_canvas) {
+    constexpr int MAXH = STAGE_H / 256, MAXD = STAGE_D / 256, MAXX = 2;
+    const int C = CT > 0 ? CT : S.C, H = HT > 0 ? HT : S.H;
+    const int G = 5 * H, R = C + 1 + 2 * H, H2 = 2 * H;
+    const int MT = (R + 15) / 16, NT = (G + 15) / 16;
+    const int TP = S.TP;
+    const int ch = blockIdx.x;
+    const int e = D.chunks[3 * ch], r0 = D.chunks[3 * ch + 1], r1 = D.chunks[3 * ch + 2];
+    const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
+    const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wd = tid >> 6;      // wave wd: direction wd
+    const int l16 = lane & 15, krow = lane >> 4;
     extern __shared__ float lds[];
-    float* arow = lds;                 // [TILE][R]
-    float* drow = arow + TILE * R;     // [TILE][G]
-    __shared__ int64_t cpix[TILE];     // canvas pixel of the cell
-    __shared__ int cflag[TILE];        // bit 0: left predecessor valid, bit 1: upper, bit 2: cell exists
-    const float* hd = hdirs + (int64_t)d * D.Hc * D.Wc * H;
-    const float* dAd = dA + (int64_t)d * D.T * G;
-    const int tid = threadIdx.x, nthr = blockDim.x;
-    // thread -> one gate column and a contiguous run of A-rows of the output block
-    const int tpc = nthr / G;                      // threads per column (>= 1)
-    const int col = tid % G, grp = tid / G;
-    const int rpt = (R + tpc - 1) / tpc;           // rows per thread (<= MAXE, checked by the host)
-    const int r0 = grp * rpt;
-    const bool active = grp < tpc && r0 < R;
-    const int nrow = active ? (R - r0 < rpt ? R - r0 : rpt) : 0;
-    float acc[MAXE];
+    float* xs = lds;                               // [TP][C+1]  x and the constant 1
+    float* hs = xs + S.nx;                         // [4][TP][2H] h_left, h_up
+    float* dab = hs + S.nh;                        // [4][TP][G]  gate gradients
+    float* dxs = dab + S.nd;                       // [4][TP][C]  per-direction dx
+    float* zero = dxs + 4 * TP * C;                // one 0.0f
+    __shared__ int t_pix[32], t_flat[32], t_cst[4][32], t_flags[32];
+    if (tid == 0) zero[0] = 0.f;
+    // dx B fragments: Wx[d][c][n] as B[n = 4ks + krow][c = l16]; kept in registers for the whole chunk
+    // when the shape is fixed at compile time with C <= 16, else loaded per use
+    constexpr bool PRE = CT > 0 && CT <= 16 && HT > 0;
+    constexpr int KX = HT > 0 ? (5 * HT + 3) / 4 : 64;
+    float bwx[PRE ? KX : 1];
+    if (PRE) {
 #pragma unroll
-    for (int i = 0; i < MAXE; ++i) acc[i] = 0.f;
-
-    for (int64_t t0 = g0; t0 < g1; t0 += TILE) {
-        if (tid < TILE) {
-            const int64_t g = t0 + tid;
-            int flag = 0;
-            int64_t pix = 0;
-            if (g < g1) {
-                const int e = find_example(D.cell_off, D.n, g);
-                const int h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
-                int s, a;
-                dg_decode(h, w, g - D.cell_off[e], s, a);
-                const int b = s - a;
-                const Flip F{D.rect[4 * e], D.rect[4 * e + 1], h, w, fy, fx};
-                pix = (int64_t)F.y(a) * D.Wc + F.x(b);
-                flag = 4 | (b > 0 ? 1 : 0) | (a > 0 ? 2 : 0);
-            }
-            cpix[tid] = pix;
-            cflag[tid] = flag;
+        for (int ks = 0; ks < (PRE ? KX : 1); ++ks) {
+            const int n = 4 * ks + krow;
+            bwx[ks] = (l16 < C && n < G) ? Wx[((int64_t)wd * C + l16) * G + n] : 0.f;
         }
-        __syncthreads();
-        const int sxs = fx ? -1 : 1;             // column step of the scan
-        const int64_t sys = fy ? -D.Wc : D.Wc;   // row step of the scan, in pixels
-        for (int idx = tid; idx < TILE * R; idx += nthr) {
-            const int c = idx / R, r = idx - (idx / R) * R;
-            const int f = cflag[c];
-            float v = 0.f;
-            if (f & 4) {
-                const int64_t p = cpix[c];
-                if (r < C) v = to_f32<XT>(xc[p * C + r]);
-                else if (r == C) v = 1.f;
-                else if (r < C + 1 + H) { if (f & 1) v = hd[(p - sxs) * H + (r - C - 1)]; }
-                else { if (f & 2) v = hd[(p - sys) * H + (r - C - 1 - H)]; }
-            }
-            arow[idx] = v;
-        }
-        for (int idx = tid; idx < TILE * G; idx += nthr) {
-            const int c = idx / G;
-            const int64_t g = t0 + c;
-            drow[idx] = g < g1 ? dAd[g * G + (idx - c * G)] : 0.f;
-        }
-        __syncthreads();
-        if (active) {
-            for (int c = 0; c < TILE; ++c) {
-                const float dv = drow[c * G + col];
-                const float* ar = arow + c * R + r0;
-#pragma unroll
-                for (int i = 0; i < MAXE; ++i)
-                    if (i < nrow) acc[i] += ar[i] * dv;
-            }
-        }
-        __syncthreads();
     }
-    float* out = part + ((int64_t)d * nchunks + blockIdx.x) * E;
-    if (active) {
+    const int plane = D.Hc * D.Wc * H;
+    const float* xf = static_cast<const float*>(xc);
+    const uint16_t* xb = static_cast<const uint16_t*>(xc);
+    const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs, 4 * (int64_t)plane * 4);
+    const __amdgpu_buffer_rsrc_t rA = rsrc(dA, 4 * D.T * G * 4);
+    const int ncell = (r1 - r0) * w;
+    const int cell0 = (int)D.cell_off[e];
+
+    // passes over the chunk: all MT M-tiles times NQ N-tiles at a time
+    constexpr int MTC = HT > 0 ? (CT + 1 + 2 * HT + 15) / 16 : 16;                 // M-tile bound
+    constexpr int NQC = HT > 0 ? (ACC_TILES / MTC < (5 * HT + 15) / 16 ? ACC_TILES / MTC : (5 * HT + 15) / 16)
+                               : ACC_TILES;                                        // N-tiles per pass bound
+    const int NQ = S.Q;
+    for (int pass = 0; pass < S.P; ++pass) {
+        const int nbase = pass * NQ;
+        f32x4 acc[MTC * NQC > ACC_TILES ? ACC_TILES : MTC * NQC];
 #pragma unroll
-        for (int i = 0; i < MAXE; ++i)
-            if (i < nrow) out[(int64_t)(r0 + i) * G + col] = acc[i];
+        for (int t = 0; t < (MTC * NQC > ACC_TILES ? ACC_TILES : MTC * NQC); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t0 = 0; t0 < ncell; t0 += TP) {
+            // cell table of the tile
+            if (tid < TP) {
+                const int q = t0 + tid;
+                int pix = -1, flat = -1, flags = 0;
+                int cst[4] = {-1, -1, -1, -1};
+                if (q < ncell) {
+                    const int ly = r0 + q / w, lx = q - (q / w) * w;
+                    pix = (y0 + ly) * D.Wc + x0 + lx;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        cst[d] = stash_index(h, w, ly, lx, d);
+                        const bool lok = (d & 1) ? lx < w - 1 : lx > 0;   // left predecessor (y, x - sx)
+                        const bool uok = (d & 2) ? ly < h - 1 : ly > 0;   // upper predecessor (y - sy, x)
+                        flags |= (lok ? 1 : 0) << (2 * d) | (uok ? 2 : 0) << (2 * d);
+                    }
+                    const int qy = y0 + ly - ry0, qx = x0 + lx - rx0;
+                    if (qy < rh && qx < rw) flat = (int)(D.flat_off[e] + qy * rw + qx);
+                }
+                t_pix[tid] = pix;
+                t_flat[tid] = flat;
+                t_flags[tid] = flags;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) t_cst[d][tid] = cst[d];
+            }
+            __syncthreads();
+            // issue every load of the tile, then write LDS
+            float vh[MAXH], vd[MAXD], vx[MAXX];
+#pragma unroll
+            for (int i = 0; i < MAXH; ++i) {
+                const int idx = tid + i * 256;
+                int off = kOOB;
+                if (idx < S.nh) {
+                    const int d = idx / (TP * H2);
+                    const int rem = idx - d * TP * H2;
+                    const int c = rem / H2, k = rem - c * H2;
+                    const int pix = t_pix[c], fl = t_flags[c] >> (2 * d);
+                    const int src = k < H ? ((fl & 1) ? pix + ((d & 1) ? 1 : -1) : -1)
+                                          : ((fl & 2) ? pix + ((d & 2) ? D.Wc : -D.Wc) : -1);
+                    if (pix >= 0 && src >= 0) off = (d * plane + src * H + (k < H ? k : k - H)) * 4;
+                }
+                vh[i] = bld(rH, off);
+            }
+#pragma unroll
+            for (int i = 0; i < MAXD; ++i) {
+                const int idx = tid + i * 256;
+                int off = kOOB;
+                if (idx < S.nd) {
+                    const int d = idx / (TP * G);
+                    const int rem = idx - d * TP * G;
+                    const int c = rem / G, n = rem - c * G;
+                    const int cs = t_cst[d][c];
+                    if (cs >= 0) off = ((d * (int)D.T + cell0 + cs) * G + n) * 4;
+                }
+                vd[i] = bld(rA, off);
+            }
+#pragma unroll
+            for (int i = 0; i < MAXX; ++i) {
+                const int idx = tid + i * 256;
+                float v = 0.f;
+                if (idx < S.nx) {
+                    const int c = idx / (C + 1), r = idx - c * (C + 1);
+                    const int pix = t_pix[c];
+                    if (r == C) v = pix >= 0 ? 1.f : 0.f;
+                    else if (pix >= 0)
+                        v = BF16 ? __uint_as_float(((uint32_t)xb[(int64_t)pix * C + r]) << 16) : xf[(int64_t)pix * C + r];
+                }
+                vx[i] = v;
+            }
+#pragma unroll
+            for (int i = 0; i < MAXH; ++i)
+                if (tid + i * 256 < S.nh) hs[tid + i * 256] = vh[i];
+#pragma unroll
+            for (int i = 0; i < MAXD; ++i)
+                if (tid + i * 256 < S.nd) dab[tid + i * 256] = vd[i];
+#pragma unroll
+            for (int i = 0; i < MAXX; ++i)
+                if (tid + i * 256 < S.nx) xs[tid + i * 256] = vx[i];
+            __syncthreads();
+            // r^T da on the matrix cores: A = r^T (rows R, K = cells), B = da (K = cells, cols G).
+            // Per k-step each M-tile's A fragment and each N-tile's B fragment is read once.
+            for (int ks = 0; ks < TP; ks += 4) {
+                const int c = ks + krow;
+                auto a_off = [&](int mt) {
+                    const int r = mt * 16 + l16;
+                    return r <= C ? (int)(xs - lds) + c * (C + 1) + r
+                                  : (r < R ? (int)(hs - lds) + (wd * TP + c) * H2 + (r - C - 1) : (int)(zero - lds));
+                };
+                auto b_off = [&](int j) {
+                    const int n = (nbase + j) * 16 + l16;
+                    return (n < G && j < NQ) ? (int)(dab - lds) + (wd * TP + c) * G + n : (int)(zero - lds);
+                };
+                if constexpr (HT > 0) {
+                    float af[MTC], bf[NQC];
+#pragma unroll
+                    for (int mt = 0; mt < MTC; ++mt) af[mt] = mt < MT ? lds[a_off(mt)] : 0.f;
+#pragma unroll
+                    for (int j = 0; j < NQC; ++j) bf[j] = lds[b_off(j)];
+#pragma unroll
+                    for (int mt = 0; mt < MTC; ++mt)
+#pragma unroll
+                        for (int j = 0; j < NQC; ++j)
+                            if (mt < MT && j < NQ)
+                                acc[mt * NQC + j] =
+                                    __builtin_amdgcn_mfma_f32_16x16x4f32(af[mt], bf[j], acc[mt * NQC + j], 0, 0, 0);
+                } else {
+                    // shape known only at run time: accumulator t holds M-tile t / NQ, N-tile t % NQ
+#pragma unroll
+                    for (int t = 0; t < ACC_TILES; ++t) {
+                        const int mt = t / NQ, j = t - mt * NQ;
+                        if (mt < MT)
+                            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(lds[a_off(mt)], lds[b_off(j)], acc[t], 0, 0, 0);
+                    }
+                }
+            }
+            if (pass == 0) {
+                // dx_d = da_d Wx[d]^T for the tile's cells on the matrix cores (A = da_d: cells x G,
+                // B = Wx[d]^T: G x C), per 16-cell M-tile; the four directions are then summed in order
+                for (int m0 = 0; m0 < TP; m0 += 16) {
+                    const bool cv = m0 + l16 < TP;       // A row = cell m0 + l16 of this tile
+                    const float* arow = dab + (wd * TP + (cv ? m0 + l16 : 0)) * G;
+                    for (int c0 = 0; c0 < C; c0 += 16) {
+                        f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
+                        const int cc = c0 + l16;
+#pragma unroll
+                        for (int ks = 0; ks < KX; ++ks) {
+                            const int n = 4 * ks + krow;
+                            if (4 * ks < G) {
+                                const float bv = PRE ? bwx[PRE ? ks : 0]
+                                                     : ((cc < C && n < G) ? Wx[((int64_t)wd * C + cc) * G + n] : 0.f);
+                                dacc = __builtin_amdgcn_mfma_f32_16x16x4f32((cv && n < G) ? arow[n] : 0.f, bv, dacc, 0, 0, 0);
+                            }
+                        }
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int cell = m0 + 4 * krow + r;
+                            if (cc < C && cell < TP) dxs[(wd * TP + cell) * C + cc] = dacc[r];
+                        }
+                    }
+                }
+                __syncthreads();
+                for (int o = tid; o < TP * C; o += 256) {
+                    const int c = o / C, chn = o - (o / C) * C;
+                    if (t_pix[c] < 0) continue;
+                    const float v = ((dxs[(0 * TP + c) * C + chn] + dxs[(1 * TP + c) * C + chn]) +
+                                     dxs[(2 * TP + c) * C + chn]) + dxs[(3 * TP + c) * C + chn];
+                    if (dx_flat && t_flat[c] >= 0) dx_flat[(int64_t)t_flat[c] * C + chn] = v;
+                    if (dx_canvas) dx_canvas[(int64_t)t_pix[c] * C + chn] = t_flat[c] >= 0 ? v : 0.f;
+                }
+            }
+            __syncthreads();
+        }
+        // partial sums of this chunk: part[chunk][d][R][G]
+        float* out = part + ((int64_t)ch * 4 + wd) * R * G;
+        auto store_tile = [&](int mt, int j, const f32x4& a) {
+            const int col = (nbase + j) * 16 + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = mt * 16 + 4 * krow + r;
+                if (row < R && col < G) out[(int64_t)row * G + col] = a[r];
+            }
+        };
+        if constexpr (HT > 0) {
+#pragma unroll
+            for (int mt = 0; mt < MTC; ++mt)
+#pragma unroll
+                for (int j = 0; j < NQC; ++j)
+                    if (mt < MT && j < NQ) store_tile(mt, j, acc[mt * NQC + j]);
+        } else {
+#pragma unroll
+            for (int t = 0; t < ACC_TILES; ++t) {
+                const int mt = t / NQ, j = t - mt * NQ;
+                if (mt < MT) store_tile(mt, j, acc[t]);
+            }
+        }
     }
 }
 
-// one thread per (direction, entry): chunks added in order, then routed to dWx / db / dUl / dUu
-__global__ void k_wgrad_reduce(const float* __restrict__ part, int64_t nchunks, int C, int H, float* __restrict__ dWx,
+}  // namespace
+
+namespace {
+
+// one thread per (direction, entry): chunk partials added in a fixed order, then
+// routed to dWx / db / dUl / dUu
+__global__ void k_wgrad_reduce(const float* __restrict__ part, int nchunks, int C, int H, float* __restrict__ dWx,
                                float* __restrict__ dUl, float* __restrict__ dUu, float* __restrict__ db) {
     const int G = 5 * H, R = C + 1 + 2 * H, E = R * G;
     const int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (id >= 4 * (int64_t)E) return;
     const int d = (int)(id / E), ent = (int)(id % E);
-    const float* p = part + (int64_t)d * nchunks * E + ent;
-    float s = 0.f;
-    for (int64_t c = 0; c < nchunks; ++c) s += p[c * E];
+    const float* p = part + (int64_t)d * E + ent;
+    const int64_t stride = 4 * (int64_t)E;
+    float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 8 <= nchunks; c += 8)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) s8[j] += p[(int64_t)(c + j) * stride];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (c + j < nchunks) s8[j] += p[(int64_t)(c + j) * stride];
+    const float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
     const int r = ent / G, n = ent % G;
     if (r < C) dWx[((int64_t)d * C + r) * G + n] = s;
     else if (r == C) db[(int64_t)d * G + n] = s;
@@ -145,78 +365,40 @@ __global__ void k_wgrad_reduce(const float* __restrict__ part, int64_t nchunks, 
     else dUu[((int64_t)d * H + (r - C - 1 - H)) * G + n] = s;
 }
 
-// one thread per canvas element (pixel, channel): dx inside real pixels, zero elsewhere
-__global__ void k_dx(Dev D, int C, int H, const float* __restrict__ Wx, const float* __restrict__ dA,
-                     float* __restrict__ dx_flat, float* __restrict__ dx_canvas) {
-    const int G = 5 * H;
-    const int64_t E = (int64_t)D.Hc * D.Wc * C;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < E; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t p = i / C;
-        const int ch = (int)(i % C);
-        const int e = D.eid[p];
-        float v = 0.f;
-        bool real = false;
-        int64_t fidx = 0;
-        if (e >= 0) {
-            const int y = (int)(p / D.Wc), x = (int)(p % D.Wc);
-            const int ry = y - D.real[4 * e], rx = x - D.real[4 * e + 1];
-            const int rw = D.real[4 * e + 3];
-            if (ry < D.real[4 * e + 2] && rx < rw) {
-                real = true;
-                fidx = (D.flat_off[e] + (int64_t)ry * rw + rx) * C + ch;
-                const int h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
-                const int ly = y - D.rect[4 * e], lx = x - D.rect[4 * e + 1];
-                for (int d = 0; d < 4; ++d) {
-                    const int a = (d & 2) ? h - 1 - ly : ly;
-                    const int b = (d & 1) ? w - 1 - lx : lx;
-                    const int s = a + b;
-                    const int64_t cell = (int64_t)d * D.T + D.cell_off[e] + dg_start(h, w, s) + (a - dg_lo(h, w, s));
-                    const float* da = dA + cell * G;
-                    const float* wr = Wx + ((int64_t)d * C + ch) * G;
-                    for (int n = 0; n < G; ++n) v += da[n] * wr[n];
-                }
-            }
-        }
-        if (dx_canvas) dx_canvas[i] = v;
-        if (dx_flat && real) dx_flat[fidx] = v;
-    }
-}
-
 }  // namespace
 
 bool wgrad_supported(int C, int H) {
-    const int G = 5 * H, R = C + 1 + 2 * H;
-    if (G > WG_THREADS) return false;
-    const int tpc = WG_THREADS / G;
-    return (R + tpc - 1) / tpc <= MAXE;
+    const WgradShape s = wgrad_shape(C, H);
+    return s.TP * (C + 1) <= 512 && 4 * s.TP * 2 * H <= STAGE_H && 4 * s.TP * s.G <= STAGE_D && s.P <= 64 &&
+           s.TP >= 4 && 5 * H <= 256 && s.MT * s.Q <= ACC_TILES;
 }
+
+size_t wgrad_lds_bytes(int C, int H) { return sizeof(float) * wgrad_lds_floats(wgrad_shape(C, H)); }
 
 hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
-                        const float* dA, float* part, int64_t nchunks, float* dWx, float* dUl, float* dUu, float* db,
-                        hipStream_t st) {
-    const int R = C + 1 + 2 * H, G = 5 * H;
-    const size_t lds = sizeof(float) * (size_t)TILE * (R + G);
-    const dim3 grid((unsigned)nchunks, 4);
-    if (dtype == 0)
-        hipLaunchKernelGGL(k_wgrad_partial<float>, grid, dim3(WG_THREADS), lds, st, D, (const float*)x_canvas, C, H,
-                           h_dirs, dA, part, nchunks);
-    else
-        hipLaunchKernelGGL(k_wgrad_partial<uint16_t>, grid, dim3(WG_THREADS), lds, st, D, (const uint16_t*)x_canvas,
-                           C, H, h_dirs, dA, part, nchunks);
+                        const float* dA, const float* Wx, float* part, float* dWx, float* dUl, float* dUu, float* db,
+                        float* dx_flat, float* dx_canvas, hipStream_t st) {
+    const WgradShape s = wgrad_shape(C, H);
+    const size_t lds = sizeof(float) * wgrad_lds_floats(s);
+    const dim3 grid((unsigned)D.nchunks), block(256);
+#define MDL_WG(B, CT, HT) hipLaunchKernelGGL((k_wgrad_mfma<B, CT, HT>), grid, block, lds, st, D, x_canvas, s, h_dirs, \
+                                             dA, Wx, part, dx_flat, dx_canvas)
+    const bool bf = dtype != 0;
+    if (!bf && C == 4 && H == 16) MDL_WG(false, 4, 16);
+    else if (!bf && C == 1 && H == 4) MDL_WG(false, 1, 4);
+    else if (bf && C == 4 && H == 32) MDL_WG(true, 4, 32);
+    else if (!bf && C == 4 && H == 32) MDL_WG(false, 4, 32);
+    else if (!bf && C == 4 && H == 2) MDL_WG(false, 4, 2);
+    else if (!bf && C == 6 && H == 10) MDL_WG(false, 6, 10);
+    else if (!bf && C == 20 && H == 50) MDL_WG(false, 20, 50);
+    else if (bf) MDL_WG(true, 0, 0);
+    else MDL_WG(false, 0, 0);
+#undef MDL_WG
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t tot = 4 * (int64_t)R * G;
-    hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, part, nchunks, C, H, dWx,
-                       dUl, dUu, db);
-    return hipGetLastError();
-}
-
-hipError_t launch_dx(const Dev& D, int C, int H, const float* Wx, const float* dA, float* dx_flat, float* dx_canvas,
-                     hipStream_t st) {
-    const int64_t E = (int64_t)D.Hc * D.Wc * C;
-    int64_t g = (E + 255) / 256;
-    if (g > (1 << 20)) g = 1 << 20;
-    hipLaunchKernelGGL(k_dx, dim3((unsigned)g), dim3(256), 0, st, D, C, H, Wx, dA, dx_flat, dx_canvas);
+    const int64_t tot = 4 * (int64_t)s.R * s.G;
+    hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, part, D.nchunks, C, H,
+                       dWx, dUl, dUu, db);
     return hipGetLastError();
 }
 

@@ -16,12 +16,14 @@ struct Dev {
     const int64_t* flat_off;  // [n+1]
     const int64_t* cell_off;  // [n+1]
     const int32_t* units;     // [4n]
+    const int32_t* chunks;    // [nchunks][3]
     int32_t* eid;             // [Hc*Wc]
     uint8_t* border;          // [Hc*Wc]
     int n, Hc, Wc;
     int64_t T;                // computed cells per direction
     int64_t N;                // real pixels
     int max_depth, max_diag;
+    int nchunks;
 };
 
 // Canvas position of the direction-local cell (a, b) of an example whose
@@ -71,12 +73,11 @@ MDL_HD inline int find_example(const int64_t* off, int n, int64_t g) {
 struct WsLayout {
     size_t stash = 0;   // float [4][T][6H]: gates i, f_l, f_u, o, g and memory state c of every cell
     size_t zda = 0;     // float [4][T][5H]: projection x.Wx+b (forward), gate gradients dA (backward)
-    size_t part = 0;    // float [4][nchunks][(C+1+2H)*5H]: weight-gradient partial sums
+    size_t part = 0;    // float [nchunks][4][(C+1+2H)*5H]: weight-gradient partial sums
     size_t total = 0;
     int64_t nchunks = 0;
 };
-constexpr int WGRAD_CHUNK = 1024;  // cells per weight-gradient partial sum
-WsLayout ws_layout(int64_t T, int C, int H);
+WsLayout ws_layout(int64_t T, int64_t nchunks, int C, int H);
 
 // launchers: return hipSuccess or the launch error
 hipError_t launch_build_maps(const Dev& D, hipStream_t st);
@@ -87,17 +88,17 @@ hipError_t launch_projection(const Dev& D, const void* x_canvas, int dtype, int 
 size_t fwd_chain_lds(int H, int Lmax);
 size_t bwd_chain_lds(int H, int Lmax);
 int chain_max_items();
+bool chain_uses_mfma(int H, int Lmax);
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z,
                             float* stash, float* h_dirs, hipStream_t st);
 hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st);
 hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                             const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
 bool wgrad_supported(int C, int H);
+size_t wgrad_lds_bytes(int C, int H);
 hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
-                        const float* dA, float* part, int64_t nchunks, float* dWx, float* dUl, float* dUu,
-                        float* db, hipStream_t st);
-hipError_t launch_dx(const Dev& D, int C, int H, const float* Wx, const float* dA, float* dx_flat,
-                     float* dx_canvas, hipStream_t st);
+                        const float* dA, const float* Wx, float* part, float* dWx, float* dUl, float* dUu, float* db,
+                        float* dx_flat, float* dx_canvas, hipStream_t st);
 hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st);
 int64_t conv_nchunks(const Dev& Dk1);

@@ -39,12 +39,15 @@ MDL_HD inline int64_t dg_start(int h, int w, int s) {
     return (int64_t)h * w - t * (t + 1) / 2;
 }
 
+constexpr int kChunkCells = 512;
+
 struct DescOffsets {
     size_t rect = 0;      // int32 [n][4] computed region (y0, x0, h, w)
     size_t real = 0;      // int32 [n][4] real pixels
     size_t flat_off = 0;  // int64 [n+1] prefix of real pixels (flat per-example tensors)
     size_t cell_off = 0;  // int64 [n+1] prefix of computed cells (per-direction stash)
     size_t units = 0;     // int32 [4n] (example*4 + direction), most cells first
+    size_t chunks = 0;    // int32 [nchunks][3] (example, first row, end row) of the reduction chunks
     size_t eid = 0;       // int32 [Hc*Wc]
     size_t border = 0;    // uint8 [Hc*Wc]
     size_t total = 0;
@@ -61,6 +64,10 @@ struct Layout {
     std::vector<uint8_t> border;
     int64_t real_pixels = 0, computed_cells = 0;
     int32_t max_depth = 0, max_diag = 0;
+    // Row ranges of the computed regions, about kChunkCells cells each and never
+    // crossing an example: the fixed blocks of the weight-gradient sums.
+    std::vector<int32_t> chunks;
+    int32_t nchunks = 0;
     DescOffsets off;
     std::vector<uint8_t> host_desc;  // descriptor bytes up to off.eid (the maps are built on device)
 };

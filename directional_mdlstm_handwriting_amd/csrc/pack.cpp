@@ -70,6 +70,17 @@ void finish(Layout& L) {
         return ca > cb;
     });
     paint_maps(L);
+    L.chunks.clear();
+    for (int e = 0; e < n; ++e) {
+        const int h = L.rect[4 * e + 2], w = L.rect[4 * e + 3];
+        const int rows = std::max(1, kChunkCells / w);
+        for (int r0 = 0; r0 < h; r0 += rows) {
+            L.chunks.push_back(e);
+            L.chunks.push_back(r0);
+            L.chunks.push_back(std::min(h, r0 + rows));
+        }
+    }
+    L.nchunks = (int32_t)(L.chunks.size() / 3);
 
     DescOffsets& o = L.off;
     size_t p = 0;
@@ -78,6 +89,7 @@ void finish(Layout& L) {
     o.flat_off = p; p = align256(p + sizeof(int64_t) * (n + 1));
     o.cell_off = p; p = align256(p + sizeof(int64_t) * (n + 1));
     o.units = p;    p = align256(p + sizeof(int32_t) * 4 * n);
+    o.chunks = p;   p = align256(p + sizeof(int32_t) * L.chunks.size());
     o.eid = p;      p = align256(p + sizeof(int32_t) * (size_t)L.Hc * L.Wc);
     o.border = p;   p = align256(p + (size_t)L.Hc * L.Wc);
     o.total = p;
@@ -87,6 +99,7 @@ void finish(Layout& L) {
     std::memcpy(&L.host_desc[o.flat_off], L.flat_off.data(), sizeof(int64_t) * (n + 1));
     std::memcpy(&L.host_desc[o.cell_off], L.cell_off.data(), sizeof(int64_t) * (n + 1));
     std::memcpy(&L.host_desc[o.units], L.units.data(), sizeof(int32_t) * 4 * n);
+    std::memcpy(&L.host_desc[o.chunks], L.chunks.data(), sizeof(int32_t) * L.chunks.size());
 }
 
 }  // namespace

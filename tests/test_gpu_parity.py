@@ -55,12 +55,21 @@ def assert_close(name, got, ref, tol, abs_sum=None):
                              f"gpu {got[i]!r} ref {ref[i]!r}")
 
 
+def poison(lay):
+    """NaN in every workspace and output buffer, so that an element a kernel fails to write cannot pass."""
+    lay.ws.view(torch.float32).fill_(float("nan"))
+    lay.h_dirs.fill_(float("nan"))
+    lay.y.fill_(float("nan"))
+    lay.x_canvas.fill_(float("nan"))
+
+
 def run_layer(heights, widths, xs, P, mode="packed", canvas_w_min=None, sep=1, x_dtype="f32", dys=None,
               want_canvas_dx=False):
     cw = canvas_w_min or max(int(max(widths)), 8)
     print(f"[gpu] layer n={len(heights)} mode={mode} C={P.C} H={P.H} dtype={x_dtype}", flush=True)
     dl = DeviceLayout(heights, widths, cw, sep, mode, DEV)
     lay = PackedLayer(dl, P.C, P.H, x_dtype)
+    poison(lay)
     Pd = DeviceParams.from_host(P, DEV)
     lay.scatter(flat_input(xs, x_dtype, DEV))
     lay.forward(Pd)
@@ -68,7 +77,7 @@ def run_layer(heights, widths, xs, P, mode="packed", canvas_w_min=None, sep=1, x
     out = {"layer": lay, "dl": dl}
     if dys is not None:
         dy = torch.as_tensor(np.concatenate([d.reshape(-1) for d in dys]).astype(np.float32), device=DEV)
-        g = LayerGrads.like(Pd)
+        g = LayerGrads(*(torch.full_like(t, float("nan")) for t in (Pd.Wx, Pd.Ul, Pd.Uu, Pd.b)))
         dx = torch.full((int(sum(np.asarray(x).size for x in xs)),), float("nan"), device=DEV)
         dxc = torch.full((dl.info["canvas_h"], dl.info["canvas_w"], P.C), float("nan"), device=DEV) \
             if want_canvas_dx else None
@@ -249,6 +258,12 @@ def test_stack_small():
     xs = random_images(64, heights, widths, C)
     print("[gpu] stack small", flush=True)
     st = PackedStack(heights, widths, C, Hs, couts, [64, 16, 8], device=DEV)
+    for lay in st.levels:
+        poison(lay)
+    for t in st.dx_canvas + st.dh_dirs:
+        t.fill_(float("nan"))
+    for wsb, _ in st.conv_ws:
+        wsb.view(torch.float32).fill_(float("nan"))
     params = [DeviceParams.from_host(P, DEV) for P in layers]
     cdev = [(torch.as_tensor(c.W, device=DEV), torch.as_tensor(c.b, device=DEV)) for c in convs]
     y = st.forward(flat_input(xs, "f32", DEV), params, cdev)
@@ -256,8 +271,8 @@ def test_stack_small():
     assert_close("stack y", _np(y), np.concatenate([a.reshape(-1) for a in ys_ref]), F32_TOL)
     dys = [np.random.default_rng(7).standard_normal(a.shape).astype(np.float32) for a in ys_ref]
     dy = torch.as_tensor(np.concatenate([d.reshape(-1) for d in dys]), device=DEV)
-    lg = [LayerGrads.like(p) for p in params]
-    cg = [(torch.empty_like(W), torch.empty_like(b)) for W, b in cdev]
+    lg = [LayerGrads(*(torch.full_like(t, float("nan")) for t in (p.Wx, p.Ul, p.Uu, p.b))) for p in params]
+    cg = [(torch.full_like(W, float("nan")), torch.full_like(b, float("nan"))) for W, b in cdev]
     dx = torch.empty(int(sum(x.size for x in xs)), device=DEV)
     st.backward(params, cdev, dy, lg, cg, dx_flat=dx)
     torch.cuda.synchronize()
