@@ -44,18 +44,109 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=24, help="examples in the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="after the run, copy MIB MiB on the device (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
 
 
-def layer_flops(rects, H):
-    """Recurrent matmul flops of one pass (forward or backward) over all units: 10 H^2 per valid predecessor."""
-    tot = 0
-    for (_, _, h, w) in rects:
-        h, w = int(h), int(w)
-        # every direction of an h x w example has h*(w-1) left and (h-1)*w upper predecessor links
-        tot += 4 * (h * (w - 1) + (h - 1) * w)
-    return tot * 10 * H * H
+def link_count(rects):
+    """Predecessor links of all four directions: an h x w region has h(w-1) left and (h-1)w upper links."""
+    return sum(4 * (int(h) * (int(w) - 1) + (int(h) - 1) * int(w)) for (_, _, h, w) in rects)
+
+
+def kernel_model(info, rects, C, H, x_bytes, nchunks=None):
+    """Algorithmic HBM bytes and flops of one launch of each kernel group (one layer, one step).
+
+    T = computed cells per direction, N = real pixels; every tensor is counted
+    once at its storage size, so re-reads show up as traffic above these bytes.
+    The recurrent flops count 10 H^2 per predecessor link (a 5H x H matrix-vector
+    product), both in the forward and in the backward pass.
+    """
+    T = info["computed_cells"]
+    N = info["real_pixels"]
+    P = info["canvas_h"] * info["canvas_w"]
+    G = 5 * H
+    R = C + 1 + 2 * H
+    rec = 10 * H * H * link_count(rects)
+    f = 4  # bytes per float
+    return {
+        # x (canvas) in, Z = x Wx + b for four directions out
+        "projection": (T * C * x_bytes + 4 * T * G * f, 4 * T * 2 * C * G),
+        # Z in; stash (i, f_l, f_u, o, g, c) and h out
+        "fwd_wavefront": (4 * T * (G + 6 * H + H) * f, rec),
+        # four h planes in, y out
+        "dirsum": (N * 5 * H * f, 3 * N * H),
+        # stash and dy in, dA (5H gate pre-activation gradients) out
+        "bwd_wavefront": (4 * T * (6 * H + G) * f + N * H * f, rec),
+        # dA and h in (each h once), x in, dx out; r^T dA and dA Wx^T on the matrix cores
+        "wgrad": (4 * T * (G + H) * f + T * C * x_bytes + N * C * f + 4 * R * G * f,
+                  4 * T * 2 * R * G + 4 * T * 2 * G * C),
+        # flat x in, canvas x out
+        "scatter": (N * C * x_bytes + P * C * x_bytes, 0),
+        # h planes outside the examples zeroed
+        "zero_fill": (4 * (P - T) * H * f, 0),
+    }
+
+
+def roofline(kernel, avg_ms, model):
+    """Fractions of HBM and fp32 matrix-core peaks; the bound is the larger fraction."""
+    nbytes, flops = model[kernel]
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    tfs = flops / (avg_ms * 1e-3) / 1e12
+    fh = gbs / MI355X["hbm_GBps"]
+    fm = tfs / MI355X["fp32_mfma_TFLOPs"]
+    if fm > fh:
+        r = {"bound": "mfma", "achieved": round(tfs, 4), "peak": MI355X["fp32_mfma_TFLOPs"], "unit": "TFLOP/s",
+             "frac": round(fm, 6)}
+    else:
+        r = {"bound": "hbm", "achieved": round(gbs, 2), "peak": MI355X["hbm_GBps"], "unit": "GB/s",
+             "frac": round(fh, 6)}
+    r.update({"kernel": kernel, "avg_launch_ms": round(avg_ms, 5), "algorithmic_bytes": int(nbytes),
+              "algorithmic_flops": int(flops), "hbm_frac": round(fh, 6), "mfma_frac": round(fm, 6)})
+    return r
+
+
+KERNEL_SOURCES = {
+    "projection": "k_proj.hip", "fwd_wavefront": "k_chain.hip", "bwd_wavefront": "k_chain.hip",
+    "wgrad": "k_wgrad.hip", "dirsum": "k_layout.hip", "scatter": "k_layout.hip", "zero_fill": "k_layout.hip",
+}
+
+
+def source_digest(kernel):
+    import hashlib
+    path = os.path.join(ROOT, "directional_mdlstm_handwriting_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy
+    kernel of known size), or None when there is none or the kernel's source has changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest(kernel) or "traffic_bytes_per_launch" not in kv:
+        return None
+    return int(float(kv["traffic_bytes_per_launch"]))
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of a known size, for scaling the HBM byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copy calibration: 3 copies of {mib} MiB", file=sys.stderr, flush=True)
 
 
 class Runner:
@@ -105,36 +196,39 @@ class Runner:
         return ms, {k: v[0] / v[1] for k, v in per_kernel.items()}
 
 
-def cpu_baseline(wl, n_sample):
-    """The oracle (float64 NumPy, single BLAS thread) on the first n_sample examples, fwd+bwd."""
+def cpu_baseline(wl, min_seconds):
+    """The oracle (float64 NumPy, one BLAS thread) on the whole batch: pack + forward + backward, repeated
+    until at least min_seconds have passed; the rate is real cell-direction updates per second."""
     from threadpoolctl import threadpool_limits
     from oracle import mdlstm as omd, pack as opack
     from workloads import cotangent
-    idx = list(range(min(n_sample, wl.n)))
-    h, w = wl.heights[idx], wl.widths[idx]
-    xs = [wl.xs[i] for i in idx]
+    h, w = wl.heights, wl.widths
     dys = cotangent(wl.seed, h, w, wl.H)
+    passes = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        lay = opack.pack_alg1(h, w, wl.canvas_w_min[0], wl.sep)
-        ys, cache = omd.layer_forward(lay, xs, wl.layers[0])
-        omd.layer_backward(lay, wl.layers[0], cache, dys=dys)
-        t = time.perf_counter() - t0
+        while True:
+            lay = opack.pack_alg1(h, w, wl.canvas_w_min[0], wl.sep)
+            ys, cache = omd.layer_forward(lay, wl.xs, wl.layers[0])
+            omd.layer_backward(lay, wl.layers[0], cache, dys=dys)
+            passes += 1
+            t = time.perf_counter() - t0
+            if t >= min_seconds:
+                break
     N = int(np.sum(h.astype(np.int64) * w))
-    return {"value": 4 * N / t, "unit": "cell-direction updates/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {len(idx)} of {wl.n} {wl.name} images (seed {wl.seed}), {N} pixels, "
-                      f"pack + forward + backward in float64 NumPy, one thread, {t:.1f} s"}
+    return {"value": 4 * N * passes / t, "unit": "cell-direction updates/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {wl.n} {wl.name} images (seed {wl.seed}, {N} pixels), {passes} passes of pack + "
+                      f"forward + backward in float64 NumPy on one thread, {t:.1f} s"}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the path shards over examples, see DESIGN.md)", file=sys.stderr)
+              f"(the examples of a batch would be split across GPUs, one process each)", file=sys.stderr)
         sys.exit(2)
     import torch
     from workloads import make_workload
-    from oracle import pack as opack
 
     device = "cuda:0"
     torch.cuda.set_device(0)
@@ -156,21 +250,14 @@ def main():
         reps.append(time.perf_counter() - t0)
     pack_us = float(np.median(reps) * 1e6)
 
-    # roofline of the dominant kernel group
+    # roofline of the dominant kernel group, from the library's HIP-event times on the bench stream
     rects, _ = M.mdl_layout_rects(packed.dl.layout)
     H, C = wl.H, wl.C
-    flops_pass = layer_flops(rects, H)
+    model = kernel_model(info, rects, C, H, 2 if wl.x_dtype == "bf16" else 4)
     dom = max(kern, key=kern.get)
-    dom_ms = kern[dom]
-    if dom in ("fwd_wavefront", "bwd_wavefront"):
-        achieved = flops_pass / (dom_ms * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "alu", "achieved": round(achieved, 4),
-                "peak": MI355X["fp32_vector_TFLOPs"], "unit": "TFLOP/s",
-                "frac": round(achieved / MI355X["fp32_vector_TFLOPs"], 6), "traffic": None,
-                "algorithmic_flops_per_launch": flops_pass, "avg_launch_ms": round(dom_ms, 5)}
-    else:
-        roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": MI355X["hbm_GBps"], "unit": "GB/s",
-                "frac": None, "traffic": None, "avg_launch_ms": round(dom_ms, 5)}
+    roof = roofline(dom, kern[dom], model)
+    roof["traffic"] = measured_traffic(dom, wl.name)
+    per_kernel = {k: roofline(k, v, model) for k, v in kern.items() if k in model}
 
     out = {
         "metric": "MDLSTM cell-direction updates/sec (fwd+bwd) on packed canvas; % of roofline",
@@ -191,29 +278,32 @@ def main():
                    "max_depth": info["max_depth"], "parallelism": "single GPU"},
         "roofline": roof,
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
+        "kernels_roofline": {k: {"bound": r["bound"], "frac": r["frac"], "hbm_frac": r["hbm_frac"],
+                                 "mfma_frac": r["mfma_frac"]} for k, r in per_kernel.items()},
         "pack_host_us": round(pack_us, 2),
     }
-    ow = opack.waste(opack.pack_alg1(wl.heights, wl.widths, wl.canvas_w_min[0], wl.sep), wl.heights, wl.widths)
-    out["config"]["canvas_waste"] = round(ow["canvas_waste"], 4)
+    out["config"]["canvas_waste"] = round(1.0 - N / (info["canvas_h"] * info["canvas_w"]), 4)
 
     if not args.no_padded and wl.name != "tiny":
         padded = Runner(wl, "padded", device, stream)
         pms, pk = padded.time(max(5, args.steps // 2), 2)
-        pw = opack.waste(opack.pack_padded(wl.heights, wl.widths), wl.heights, wl.widths)
+        pinfo = padded.dl.info
         out["packed_vs_padded"] = {
             "ms_per_step_packed": ms, "ms_per_step_padded": pms, "speedup": pms / ms,
-            "padded_cell_fraction": round(pw["padded_cell_fraction"], 4), "zpr": round(pw["zpr"], 4),
-            "computed_cells_padded": pw["computed_cells"], "padded_kernels_ms": {k: round(v, 5) for k, v in pk.items()},
+            "padded_cell_fraction": round(1.0 - N / pinfo["computed_cells"], 4),
+            "computed_cells_padded": pinfo["computed_cells"], "padded_kernels_ms": {k: round(v, 5) for k, v in pk.items()},
             "pages_context": "6.6x for IAM words: whole-model training epochs, 2x GTX 1080, batch 20 padded vs "
                              "200 packed (No Padding Please, Table IV)",
         }
         del padded
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+    if args.copy_calib:
+        copy_calibration(args.copy_calib)
 
 
 if __name__ == "__main__":

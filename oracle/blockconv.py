@@ -7,7 +7,7 @@ batch axis, runs one convolution over the stack, and de-chunking puts each
 example's outputs back together from the original sizes; the result equals
 the per-example convolution.
 
-Readings (listed in the design doc): the kernel is (rows 2, cols 4); its input is
+Readings where the pages are silent: the kernel is (rows 2, cols 4); its input is
 the four directions' hidden outputs stacked as 4H channels (channel d*H + k),
 so no direction sum happens between levels; partial blocks at the bottom and
 right edge are zero padded (output size ceil(h/2) x ceil(w/4)); no activation

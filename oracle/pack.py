@@ -7,7 +7,7 @@ Algorithm 1 (the packing loop). The skew of §IV-A / Algorithm 1's last step is
 an implementation device for convolution-based MDLSTMs and does not change any
 cell's value, so the canvas here stays unskewed.
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
   * bucket visiting order: tallest height first;
   * ties between equally wide fitting examples: lowest input index;
   * a row is closed only when nothing of the current bucket fits (as the loop
