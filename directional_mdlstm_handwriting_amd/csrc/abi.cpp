@@ -255,7 +255,8 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     const mdl::Layout& L = L_of(layout);
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nchunks, C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
-    if (!mdl::chain_uses_mfma(H, L.max_diag) && (int64_t)L.max_diag * H > mdl::chain_max_items())
+    if (!mdl::fwd16_supported(H, L.max_diag) && !mdl::chain_uses_mfma(H, L.max_diag) &&
+        (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_forward: widest diagonal x H exceeds the wavefront kernel's items");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;

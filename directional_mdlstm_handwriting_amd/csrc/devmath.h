@@ -1,0 +1,61 @@
+// devmath.h — device helpers shared by the wavefront and gradient kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace mdl {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer loads/stores on a per-unit buffer descriptor. A lane with nothing
+// to load or store passes an offset past the descriptor's range: the hardware
+// returns 0 for the load and drops the store. Every lane then issues the same
+// memory instructions with no branch around them, so the compiler can wait
+// for one prefetch with vmcnt(N) while earlier stores stay in flight (loads
+// and stores share one in-order counter on this architecture).
+constexpr uint32_t kBufCfg = 0x00020000;  // dword 3 of a raw 32-bit buffer descriptor (gfx9 family)
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufCfg);
+}
+__device__ inline float bld(__amdgpu_buffer_rsrc_t r, int off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void bst(float v, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+// Gate nonlinearities on the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32,
+// about 1 ulp each). sigmoid(z) = 1 / (1 + e^-z); tanh(x) = (1 - e^-2|x|) / (1 + e^-2|x|)
+// with the sign of x, and for |x| < 1/8 its odd Taylor polynomial to x^9, so that
+// tanh keeps its relative accuracy near 0 instead of losing it to cancellation.
+__device__ inline float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ inline float sigm(float z) { return frcp(1.0f + fexp(-z)); }
+__device__ inline float ftanh(float x) {
+    const float ax = fabsf(x);
+    const float e = fexp(-2.0f * ax);
+    const float big = (1.0f - e) * frcp(1.0f + e);
+    const float x2 = x * x;
+    const float small = ax * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f + x2 * (62.0f / 2835.0f)))));
+    return copysignf(ax < 0.125f ? small : big, x);
+}
+
+// tanh(x) = 2 sigmoid(2x) - 1: four instructions; absolute error about 1e-7 near 0
+// (the subtraction cancels there), relative error about 1 ulp for |x| > 1/2.
+__device__ inline float ftanh2(float x) { return __builtin_fmaf(2.0f, frcp(1.0f + fexp(-2.0f * x)), -1.0f); }
+
+// fp32 value -> f16 pair (hi, lo) with hi + lo equal to v to about 2^-22 relative,
+// for |v| < 65504 and |v| above the f16 normal range's floor.
+__device__ inline void split16(float v, _Float16& hi, _Float16& lo) {
+    hi = (_Float16)v;
+    lo = (_Float16)(v - (float)hi);
+}
+
+}  // namespace mdl

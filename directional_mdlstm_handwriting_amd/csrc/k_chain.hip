@@ -16,6 +16,7 @@
 // Global traffic per step is one contiguous run of the diagonal-major stash
 // (prefetched a step ahead in the forward) plus the h output on the canvas.
 #include "kernels.h"
+#include "devmath.h"
 
 namespace mdl {
 
@@ -24,24 +25,7 @@ namespace {
 constexpr int CHAIN_THREADS = 256;
 constexpr int MAXI = 8;  // (cell, hidden) items per thread and step
 
-// Gate nonlinearities on the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32,
-// about 1 ulp each). sigmoid(z) = 1 / (1 + e^-z); tanh(x) = (1 - e^-2|x|) / (1 + e^-2|x|)
-// with the sign of x, and for |x| < 1/8 its odd Taylor polynomial to x^9, so that
-// tanh keeps its relative accuracy near 0 instead of losing it to cancellation.
-__device__ inline float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
-__device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ inline float sigm(float z) { return frcp(1.0f + fexp(-z)); }
-__device__ inline float ftanh(float x) {
-    const float ax = fabsf(x);
-    const float e = fexp(-2.0f * ax);
-    const float big = (1.0f - e) * frcp(1.0f + e);
-    const float x2 = x * x;
-    const float small = ax * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f + x2 * (62.0f / 2835.0f)))));
-    return copysignf(ax < 0.125f ? small : big, x);
-}
-
-// Forward. Z [4][T][5H], stash out [4][T][6H] = (i, f_l, f_u, o, g, c) per cell,
-// h_dirs out [4][Hc][Wc][H].
+// Forward. Z in (Z4, Z1), gate stash out (S4, S2), h_dirs out [4][Hc][Wc][H].
 __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int Lmax, const float* __restrict__ Ul,
                                                              const float* __restrict__ Uu,
                                                              const float* __restrict__ Z, float* __restrict__ stash,
@@ -60,8 +44,10 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
         U[H * G + i] = Uu[(int64_t)d * H * G + i];
     }
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
-    const float* Zd = Z + base * G;
-    float* Sd = stash + base * 6 * H;
+    const float* Z4d = Z + base * 4 * H;
+    const float* Z1d = Z + z1_offset(D.T, H) + base * H;
+    float* S4d = stash + base * 4 * H;
+    float* S2d = stash + z1_offset(D.T, H) + base * 2 * H;
     float* Hd = hdirs + (int64_t)d * D.Hc * D.Wc * H;
     const int S = h + w - 1;
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -75,7 +61,8 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
             if (item < L * H) {
                 const int j = item / H, k = item - (item / H) * H;
 #pragma unroll
-                for (int g = 0; g < 5; ++g) zc[i][g] = Zd[(int64_t)j * G + g * H + k];
+                for (int g = 0; g < 4; ++g) zc[i][g] = Z4d[((int64_t)j * H + k) * 4 + g];
+                zc[i][4] = Z1d[(int64_t)j * H + k];
             }
         }
     }
@@ -95,7 +82,8 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
                 if (item < Ln * H) {
                     const int j = item / H, k = item - (item / H) * H;
 #pragma unroll
-                    for (int g = 0; g < 5; ++g) zn[i][g] = Zd[(stn + j) * G + g * H + k];
+                    for (int g = 0; g < 4; ++g) zn[i][g] = Z4d[((stn + j) * H + k) * 4 + g];
+                    zn[i][4] = Z1d[(stn + j) * H + k];
                 }
             }
         }
@@ -146,13 +134,14 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
                 hn[j * H + k] = hv;
                 cn[j * H + k] = c;
                 Hd[((int64_t)F.y(a) * D.Wc + F.x(b)) * H + k] = hv;
-                float* rec = Sd + (st + j) * 6 * H + k;
-                rec[0] = ig;
-                rec[H] = fl;
-                rec[2 * H] = fu;
-                rec[3 * H] = og;
-                rec[4 * H] = gg;
-                rec[5 * H] = c;
+                float* r4 = S4d + ((st + j) * H + k) * 4;
+                r4[0] = ig;
+                r4[1] = fl;
+                r4[2] = fu;
+                r4[3] = og;
+                float* r2 = S2d + ((st + j) * H + k) * 2;
+                r2[0] = gg;
+                r2[1] = c;
             }
         }
         __syncthreads();
@@ -192,7 +181,8 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
     }
     __syncthreads();
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
-    const float* Sd = stash + base * 6 * H;
+    const float* S4d = stash + base * 4 * H;
+    const float* S2d = stash + z1_offset(D.T, H) + base * 2 * H;
     float* dAd = dA + base * G;
     const float* dyb = dy_flat ? dy_flat + D.flat_off[e] * H : nullptr;
     const float* dhd = dh_dirs ? dh_dirs + (int64_t)d * D.Hc * D.Wc * H : nullptr;
@@ -219,11 +209,11 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
                 const int a = lo + j, b = s - a;
                 const int y = F.y(a), x = F.x(b);
                 // forward values of this cell and its predecessors' memory states
-                const float* rec = Sd + (st + j) * 6 * H + k;
-                const float ig = rec[0], fl = rec[H], fu = rec[2 * H], og = rec[3 * H], gg = rec[4 * H];
-                const float c = rec[5 * H];
-                const float cl = b > 0 ? Sd[(stp + a - lop) * 6 * H + 5 * H + k] : 0.f;
-                const float cu = a > 0 ? Sd[(stp + a - 1 - lop) * 6 * H + 5 * H + k] : 0.f;
+                const float* r4 = S4d + ((st + j) * H + k) * 4;
+                const float ig = r4[0], fl = r4[1], fu = r4[2], og = r4[3];
+                const float gg = S2d[((st + j) * H + k) * 2], c = S2d[((st + j) * H + k) * 2 + 1];
+                const float cl = b > 0 ? S2d[((stp + a - lop) * H + k) * 2 + 1] : 0.f;
+                const float cu = a > 0 ? S2d[((stp + a - 1 - lop) * H + k) * 2 + 1] : 0.f;
                 float dh = 0.f;
                 if (dhd) {
                     dh = dhd[((int64_t)y * D.Wc + x) * H + k];
@@ -282,152 +272,9 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
 // prefetched from HBM while the current step computes.
 // ---------------------------------------------------------------------------------------------
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// All global traffic of the step loops goes through raw buffer loads/stores on
-// per-unit buffer descriptors. A lane without a valid (cell, hidden unit) uses
-// an offset past the descriptor's range: its load returns 0 and its store is
-// dropped by the hardware. So every lane issues the same memory instructions
-// in every step, with no branches around them, and the compiler can wait for a
-// prefetch with vmcnt(N) while the step's stores stay in flight (loads and
-// stores share one in-order counter on this architecture) instead of draining
-// every store before each step.
-constexpr uint32_t kBufCfg = 0x00020000;   // dword 3 of a raw 32-bit buffer descriptor (gfx9 family)
-constexpr int kOOB = 0x40000000;            // byte offset past every per-unit range used here (1 GiB)
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufCfg);
-}
-__device__ inline float bld(__amdgpu_buffer_rsrc_t r, int off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ inline void bst(float v, __amdgpu_buffer_rsrc_t r, int off) {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
-}
-
-template <int H>
-__global__ __launch_bounds__(256) void k_fwd_mfma(Dev D, int, int Lmax, const float* __restrict__ Ul,
-                                                  const float* __restrict__ Uu, const float* __restrict__ Z,
-                                                  float* __restrict__ stash, float* __restrict__ hdirs) {
-    constexpr int KS = (2 * H + 3) / 4;        // k-steps over [h_left; h_up]
-    constexpr int KB = H <= 16 ? 1 : H <= 32 ? 2 : 4;  // blocks of 16 hidden units
-    const int u = D.units[blockIdx.x];
-    const int e = u >> 2, d = u & 3;
-    const Flip F{D.rect[4 * e], D.rect[4 * e + 1], D.rect[4 * e + 2], D.rect[4 * e + 3], (d & 2) != 0, (d & 1) != 0};
-    const int h = F.h, w = F.w;
-    constexpr int G = 5 * H;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kb = wave % KB, mt = wave / KB;   // one block of 16 hidden units, one M-tile of 16 cells
-    const int kk = kb * 16 + (lane & 15);      // hidden unit of this lane's output column
-    const bool kok = kk < H;
-    const int krow = lane >> 4;                // input offset within a k-step of the A and B operands
-    const int orow = mt * 16 + 4 * (lane >> 4);  // first of this lane's 4 output cells on a diagonal
-
-    float Bw[5][KS];                            // [Ul; Uu][4ks + krow][g*H + kk]
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int kr = 4 * ks + krow;
-#pragma unroll
-        for (int g = 0; g < 5; ++g) {
-            float v = 0.f;
-            if (kok && kr < 2 * H)
-                v = kr < H ? Ul[((int64_t)d * H + kr) * G + g * H + kk] : Uu[((int64_t)d * H + kr - H) * G + g * H + kk];
-            Bw[g][ks] = v;
-        }
-    }
-    extern __shared__ float lds[];
-    const int ZR = 16 * ((Lmax + 15) / 16);    // zero row; rows [0, ZR) hold a diagonal
-    const int LR = ZR + 1;
-    float* hb = lds;                            // [2][LR][H]
-    float* cb = hb + 2 * LR * H;                // [2][LR][H]
-    for (int i = threadIdx.x; i < 4 * LR * H; i += blockDim.x) lds[i] = 0.f;
-    const int64_t base = (int64_t)d * D.T + D.cell_off[e];
-    const int64_t cells = (int64_t)h * w;
-    const __amdgpu_buffer_rsrc_t rZ = rsrc(Z + base * G, cells * G * 4);
-    const __amdgpu_buffer_rsrc_t rS = rsrc(stash + base * 6 * H, cells * 6 * H * 4);
-    const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4);
-    const int S = h + w - 1;
-
-    auto load_z = [&](int s, float (&z)[5][4]) {
-        const int L = s < S ? dg_len(h, w, s) : 0;
-        const int st = s < S ? (int)dg_start(h, w, s) : 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int jo = orow + r;
-            const bool ok = jo < L && kok;
-            const int off = ok ? ((st + jo) * G + kk) * 4 : kOOB;
-#pragma unroll
-            for (int g = 0; g < 5; ++g) z[g][r] = bld(rZ, off + g * H * 4);
-        }
-    };
-    auto step = [&](int s, float (&zc)[5][4], float (&zn)[5][4]) {
-        const int L = dg_len(h, w, s), lo = dg_lo(h, w, s);
-        const int st = (int)dg_start(h, w, s);
-        const int lop = dg_lo(h, w, s - 1);
-        load_z(s + 1, zn);                      // prefetch; consumed one step later
-        const float* hp = hb + ((s + 1) & 1) * LR * H;
-        const float* cp = cb + ((s + 1) & 1) * LR * H;
-        float* hn = hb + (s & 1) * LR * H;
-        float* cn = cb + (s & 1) * LR * H;
-        f32x4 acc[5];
-#pragma unroll
-        for (int g = 0; g < 5; ++g) acc[g] = f32x4{zc[g][0], zc[g][1], zc[g][2], zc[g][3]};
-        if (mt * 16 < L) {                      // uniform over the wave; no global memory inside
-            const int ja = mt * 16 + (lane & 15);
-            const int aA = lo + ja, bA = s - aA;
-            const int rl = (ja < L && bA > 0) ? aA - lop : ZR;
-            const int ru = (ja < L && aA > 0) ? aA - 1 - lop : ZR;
-            // A operand addresses first (the zero row stands in for a missing predecessor), then one
-            // unconditional LDS read per k-step, all issued ahead of the MFMA chain
-            float av[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int kr = 4 * ks + krow;
-                const int idx = kr < H ? rl * H + kr : (kr < 2 * H ? ru * H + kr - H : ZR * H);
-                av[ks] = hp[idx];
-            }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-                for (int g = 0; g < 5; ++g) acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[ks], Bw[g][ks], acc[g], 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int jo = orow + r;
-            const bool ok = jo < L && kok;
-            const int a = lo + jo, b = s - a;
-            const int kc = kok ? kk : 0;
-            const float cl = cp[((ok && b > 0) ? a - lop : ZR) * H + kc];
-            const float cu = cp[((ok && a > 0) ? a - 1 - lop : ZR) * H + kc];
-            const float ig = sigm(acc[0][r]), fl = sigm(acc[1][r]), fu = sigm(acc[2][r]), og = sigm(acc[3][r]);
-            const float gg = ftanh(acc[4][r]);
-            const float c = fl * cl + fu * cu + ig * gg;
-            const float hv = og * ftanh(c);
-            if (ok) {
-                hn[jo * H + kk] = hv;
-                cn[jo * H + kk] = c;
-            }
-            bst(hv, rH, ok ? (int)(((int64_t)F.y(a) * D.Wc + F.x(b)) * H + kk) * 4 : kOOB);
-            const int so = ok ? ((st + jo) * 6 * H + kk) * 4 : kOOB;
-            bst(ig, rS, so);
-            bst(fl, rS, so + H * 4);
-            bst(fu, rS, so + 2 * H * 4);
-            bst(og, rS, so + 3 * H * 4);
-            bst(gg, rS, so + 4 * H * 4);
-            bst(c, rS, so + 5 * H * 4);
-        }
-        __syncthreads();
-    };
-    float zA[5][4], zB[5][4];
-    load_z(0, zA);
-    __syncthreads();
-    int s = 0;
-    for (; s + 1 < S; s += 2) {
-        step(s, zA, zB);
-        step(s + 1, zB, zA);
-    }
-    if (s < S) step(s, zA, zB);
-}
+// All global traffic of the step loops goes through raw buffer loads/stores
+// (devmath.h); kOOB is an offset past every per-unit range used here (1 GiB).
+constexpr int kOOB = 0x40000000;
 
 template <int H>
 __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const float* __restrict__ Ul,
@@ -467,7 +314,8 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
     for (int i = threadIdx.x; i < 2 * LR * G + 4 * LR * H; i += blockDim.x) lds[i] = 0.f;
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
     const int64_t cells = (int64_t)h * w;
-    const __amdgpu_buffer_rsrc_t rS = rsrc(stash + base * 6 * H, cells * 6 * H * 4);
+    const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 4 * H * 4);
+    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + z1_offset(D.T, H) + base * 2 * H, cells * 2 * H * 4);
     const __amdgpu_buffer_rsrc_t rA = rsrc(dA + base * G, cells * G * 4);
     // upstream gradient: per-direction canvas tensor, or the flat gradient of the direction sum
     const bool per_dir = dh_dirs != nullptr;
@@ -488,11 +336,14 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
             const int jo = orow + r;
             const bool ok = jo < L && kok;
             const int a = lo + jo, b = s - a;
-            const int so = ok ? ((st + jo) * 6 * H + kk) * 4 : kOOB;
+            const int ei = (st + jo) * H + kk;  // (cell, hidden unit) element of the stash
+            const int so4 = ok ? ei * 16 : kOOB, so2 = ok ? ei * 8 : kOOB;
 #pragma unroll
-            for (int g = 0; g < 6; ++g) v[g][r] = bld(rS, so + g * H * 4);
-            v[6][r] = bld(rS, (ok && b > 0) ? ((stp + a - lop) * 6 * H + 5 * H + kk) * 4 : kOOB);
-            v[7][r] = bld(rS, (ok && a > 0) ? ((stp + a - 1 - lop) * 6 * H + 5 * H + kk) * 4 : kOOB);
+            for (int g = 0; g < 4; ++g) v[g][r] = bld(rS4, so4 + g * 4);
+            v[4][r] = bld(rS2, so2);
+            v[5][r] = bld(rS2, so2 + 4);
+            v[6][r] = bld(rS2, (ok && b > 0) ? (((stp + a - lop) * H + kk) * 2 + 1) * 4 : kOOB);
+            v[7][r] = bld(rS2, (ok && a > 0) ? (((stp + a - 1 - lop) * H + kk) * 2 + 1) * 4 : kOOB);
             const int y = F.y(a), x = F.x(b);
             const int ly = y - ry0, lx = x - rx0;
             int uo = kOOB;
@@ -580,23 +431,17 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
     if (s >= 0) step(s, vA, vB);
 }
 
-typedef void (*FwdKernel)(Dev, int, int, const float*, const float*, const float*, float*, float*);
 typedef void (*BwdKernel)(Dev, int, int, const float*, const float*, const float*, const float*, const float*, float*);
 
 // instantiated hidden sizes: the workloads' 2, 4, 10, 16, 32 and 50
 struct MfmaEntry {
     int H;
-    FwdKernel fwd;
     BwdKernel bwd;
     int KB;
 };
 const MfmaEntry kMfma[] = {
-    {2, k_fwd_mfma<2>, k_bwd_mfma<2>, 1},
-    {4, k_fwd_mfma<4>, k_bwd_mfma<4>, 1},
-    {10, k_fwd_mfma<10>, k_bwd_mfma<10>, 1},
-    {16, k_fwd_mfma<16>, k_bwd_mfma<16>, 1},
-    {32, k_fwd_mfma<32>, k_bwd_mfma<32>, 2},
-    {50, k_fwd_mfma<50>, k_bwd_mfma<50>, 4},
+    {2, k_bwd_mfma<2>, 1},  {4, k_bwd_mfma<4>, 1},   {10, k_bwd_mfma<10>, 1},
+    {16, k_bwd_mfma<16>, 1}, {32, k_bwd_mfma<32>, 2}, {50, k_bwd_mfma<50>, 4},
 };
 
 // one M-tile of 16 cells per wave: 4/KB tiles cover the widest diagonal
@@ -607,7 +452,6 @@ const MfmaEntry* mfma_entry(int H, int Lmax) {
 }
 
 int lds_rows(int Lmax) { return 16 * ((Lmax + 15) / 16) + 1; }
-size_t fwd_mfma_lds(int H, int Lmax) { return sizeof(float) * (size_t)4 * lds_rows(Lmax) * H; }
 size_t bwd_mfma_lds(int H, int Lmax) {
     return sizeof(float) * ((size_t)2 * lds_rows(Lmax) * 5 * H + (size_t)4 * lds_rows(Lmax) * H);
 }
@@ -618,7 +462,7 @@ int chain_max_items() { return MAXI * CHAIN_THREADS; }
 
 
 size_t fwd_chain_lds(int H, int Lmax) {
-    if (mfma_entry(H, Lmax)) return fwd_mfma_lds(H, Lmax);
+    if (fwd16_supported(H, Lmax)) return fwd16_lds(H, Lmax);
     return sizeof(float) * ((size_t)2 * H * 5 * H + (size_t)4 * Lmax * H);
 }
 
@@ -632,11 +476,7 @@ bool chain_uses_mfma(int H, int Lmax) { return mfma_entry(H, Lmax) != nullptr; }
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
                             float* h_dirs, hipStream_t st) {
     const int Lmax = D.max_diag;
-    if (const MfmaEntry* m = mfma_entry(H, Lmax)) {
-        hipLaunchKernelGGL(m->fwd, dim3(4 * D.n), dim3(256), fwd_mfma_lds(H, Lmax), st, D, H, Lmax, Ul, Uu, Z, stash,
-                           h_dirs);
-        return hipGetLastError();
-    }
+    if (fwd16_supported(H, Lmax)) return launch_fwd16(D, H, Ul, Uu, Z, stash, h_dirs, st);
     hipLaunchKernelGGL(k_fwd_chain, dim3(4 * D.n), dim3(CHAIN_THREADS), fwd_chain_lds(H, Lmax), st, D, H, Lmax, Ul,
                        Uu, Z, stash, h_dirs);
     return hipGetLastError();

@@ -1,0 +1,345 @@
+// k_fwd16.hip — forward wavefront with the recurrent product on the f16 matrix cores.
+//
+// Same schedule as the other wavefront kernels ("No Padding Please" §IV-A and
+// RETURNN §4.2: all cells of a local anti-diagonal are independent; one
+// workgroup per (example, direction) unit walks its diagonals in order), but
+// the recurrent product
+//     a(cell) = Z(cell) + [h_left, h_up](cell) . [Ul; Uu]
+// runs on v_mfma_f32_16x16x32_f16, which moves 8x the multiply-adds per
+// cycle of the fp32 matrix instruction. Both operands are split into f16
+// pairs, x = hi + lo, and the product keeps the three terms
+// hi.hi + hi.lo + lo.hi (the dropped lo.lo term is below 2^-21 of the
+// product), accumulated in fp32: fp32-class accuracy at 3 f16 instructions per
+// 32-wide K block instead of 8 fp32 ones. f16 has a narrow exponent range, so
+// h (|h| < 1) is scaled by 2^14 and each weight column by its own power of
+// two (its largest magnitude lands in [2^14, 2^15)); the accumulator is scaled
+// back exactly before Z is added.
+//
+// Work split: NB * CG waves; wave = (16-wide block kb of hidden units, cell
+// group cg). Cells of the diagonal are dealt round-robin to the CG cell
+// groups, and inside a wave cell i sits in MFMA row 4*(i%4) + i/4, so that a
+// lane's four accumulator rows hold cells q, q+4, q+8, q+12 (q = lane/16): a
+// wave whose group has m cells on the widest diagonal needs NR = ceil(m/4)
+// accumulator rows. NR is fixed per launch, so every step is one straight
+// instruction sequence: the compiler then knows how many memory operations
+// are in flight and waits for a prefetch with vmcnt(N) instead of draining
+// every store (loads and stores retire in order on this architecture). The
+// projection Z is prefetched three diagonals ahead into four register sets.
+// The previous diagonal's h (as scaled f16 hi/lo) and c sit in LDS ping-pong
+// buffers with a zero row standing in for a missing predecessor.
+#include "kernels.h"
+#include "devmath.h"
+
+#include <type_traits>
+
+namespace mdl {
+
+namespace {
+
+constexpr int kOOB = 0x40000000;    // byte offset past every per-unit range used here (1 GiB)
+constexpr float kHScale = 16384.f;  // 2^14: h in (-1, 1) -> f16 range
+constexpr int kZD = 3;              // diagonals of Z prefetch ahead
+
+template <int H>
+struct F16Shape {
+    static constexpr int NB = (H + 15) / 16;       // blocks of 16 hidden units
+    static constexpr int HP = (H + 7) / 8 * 8;     // h_left / h_up segment in the K dimension
+    static constexpr int KB = (2 * HP + 31) / 32;  // K blocks of 32
+    static_assert(NB <= 4, "hidden size above 64");
+};
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+template <int H, int CG, int NR>
+__global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, const float* __restrict__ Ul,
+                                                                     const float* __restrict__ Uu,
+                                                                     const float* __restrict__ Z,
+                                                                     float* __restrict__ stash,
+                                                                     float* __restrict__ hdirs) {
+    using Sh = F16Shape<H>;
+    constexpr int HP = Sh::HP, KB = Sh::KB;
+    constexpr int G = 5 * H;
+    const int u = D.units[blockIdx.x];
+    const int e = u >> 2, d = u & 3;
+    const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kb = wave / CG, cg = wave % CG;
+    const int q = lane >> 4, col = lane & 15;
+    const int kk = kb * 16 + col;  // this lane's hidden unit (output column)
+    const bool kok = kk < H;
+    const int kc = kok ? kk : 0;
+
+    // B operand: lane holds rows 32t + 8q .. +7 of column g*H + kk of [Ul; Uu] (Ul row k at K index k,
+    // Uu row k at HP + k, zeros elsewhere), scaled per column by 2^E and split into f16 hi + lo.
+    f16x8 Bh[5][KB], Bl[5][KB];
+    float us[5];  // 2^-(E + 14): undoes both scalings
+#pragma unroll
+    for (int g = 0; g < 5; ++g) {
+        float v[KB][8];
+        float m = 0.f;
+#pragma unroll
+        for (int t = 0; t < KB; ++t)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int k = 32 * t + 8 * q + i;
+                float x = 0.f;
+                if (kok) {
+                    if (k < H) x = Ul[((int64_t)d * H + k) * G + g * H + kk];
+                    else if (k >= HP && k - HP < H) x = Uu[((int64_t)d * H + (k - HP)) * G + g * H + kk];
+                }
+                v[t][i] = x;
+                m = fmaxf(m, fabsf(x));
+            }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        int E = 0;
+        if (m > 0.f) {
+            E = 14 - ((int)((__float_as_uint(m) >> 23) & 255) - 127);
+            E = E < -100 ? -100 : (E > 100 ? 100 : E);
+        }
+        us[g] = ldexpf(1.0f, -(E + 14));
+#pragma unroll
+        for (int t = 0; t < KB; ++t)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                _Float16 hi, lo;
+                split16(ldexpf(v[t][i], E), hi, lo);
+                Bh[g][t][i] = hi;
+                Bl[g][t][i] = lo;
+            }
+    }
+
+    // LDS, two buffers (previous / current diagonal) of NRW rows each: h * 2^14 as f16 hi and lo (row
+    // stride RS halves), then c (row stride CS floats). Diagonal position j is kept in row P(j) (below);
+    // row ZR is zeros, row XR absorbs the writes of lanes without a cell.
+    constexpr int RS = 2 * HP + 8, CS = H + 4;
+    constexpr int NRW = 16 * CG + 2, ZR = 16 * CG, XR = 16 * CG + 1;
+    constexpr int HBUF = NRW * RS * 2, CBUF = NRW * CS * 4;  // bytes of one h / c buffer
+    extern __shared__ __align__(16) unsigned char smem[];
+    {
+        uint32_t* z32 = reinterpret_cast<uint32_t*>(smem);
+        for (int i = threadIdx.x; i < (HBUF + CBUF) / 2; i += blockDim.x) z32[i] = 0u;
+    }
+    const int64_t base = (int64_t)d * D.T + D.cell_off[e];
+    const int64_t cells = (int64_t)h * w;
+    const int64_t o1 = z1_offset(D.T, H);
+    const __amdgpu_buffer_rsrc_t rZ4 = rsrc(Z + base * 4 * H, cells * 16 * H);
+    const __amdgpu_buffer_rsrc_t rZ1 = rsrc(Z + o1 + base * H, cells * 4 * H);
+    const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 16 * H);
+    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 2 * H, cells * 8 * H);
+    const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4);
+    const int S = h + w - 1;
+
+    // Cell j of a diagonal belongs to cell group j % CG and is cell i = j / CG of that group's wave,
+    // computed in MFMA row 4(i%4) + i/4. Its LDS row P(j) = 16(j % CG) + 4(i%4) + i/4: the 16 lanes that
+    // gather one K block of the A operand then read 16 consecutive rows, and the odd row stride (in
+    // 16-byte units) puts them on distinct banks. Positions outside [0, 16 CG) map to the zero row.
+    auto P = [&](int j) {
+        if (j < 0 || j >= 16 * CG) return ZR;
+        const int i = j / CG;
+        return 16 * (j % CG) + 4 * (i & 3) + (i >> 2);
+    };
+
+    // Every address of the step loop is a per-lane constant plus a per-step scalar. Cell (a, b) of the
+    // unit (b = s - a on diagonal s) sits at canvas (Y0 + SY a, X0 + SX b), so its h byte offset is
+    // HB + a DA + s DS + 4 kk; a = lo + j for position j on the diagonal. On diagonal s the left
+    // predecessor of position j is position j + dl of diagonal s - 1 and the upper one j + dl - 1, with
+    // dl = 0 while s < w and 1 after.
+    const int SY = (d & 2) ? -1 : 1, SX = (d & 1) ? -1 : 1;
+    const int Y0 = (d & 2) ? y0 + h - 1 : y0, X0 = (d & 1) ? x0 + w - 1 : x0;
+    const int H4 = 4 * H;
+    const int DA = SY * D.Wc * H4 - SX * H4, DS = SX * H4;
+    const int HB = (Y0 * D.Wc + X0) * H4;
+    int jo[NR], vh[NR], ve[NR];  // per accumulator row r: diagonal position, h offset, stash element
+    int owc[NR], owh[NR];        // LDS byte offsets of the row's own c and h entries (within a buffer)
+    int opc[NR][3];              // LDS byte offsets of c at positions jo - 1, jo, jo + 1
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        jo[r] = (4 * r + q) * CG + cg;
+        vh[r] = jo[r] * DA + 4 * kk;
+        ve[r] = jo[r] * H + kk;
+        const int pw = 16 * cg + 4 * q + r;  // P(jo[r])
+        owc[r] = pw * CS * 4 + 4 * kc;
+        owh[r] = pw * RS * 2 + 2 * kc;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) opc[r][m] = P(jo[r] + m - 1) * CS * 4 + 4 * kc;
+    }
+    const int oxc = XR * CS * 4 + 4 * kc, oxh = XR * RS * 2 + 2 * kc, ozc = ZR * CS * 4 + 4 * kc;
+    const int ja = (4 * (col & 3) + (col >> 2)) * CG + cg;  // diagonal position of this lane's A row
+    int oah[3];  // LDS byte offsets of the h rows at positions ja - 1, ja, ja + 1
+#pragma unroll
+    for (int m = 0; m < 3; ++m) oah[m] = P(ja + m - 1) * RS * 2;
+    const int oza = ZR * RS * 2;
+
+    auto diag_len = [&](int s) {
+        const int lo = s > w - 1 ? s - (w - 1) : 0;
+        const int hi = s < h - 1 ? s : h - 1;
+        return s < S ? hi - lo + 1 : 0;
+    };
+
+    // Z of diagonal s1 (first cell st1) into one register set; lanes without a cell load nothing
+    auto load_z = [&](int s1, int st1, f32x4 (&z4)[NR], float (&zg)[NR]) {
+        const int L1 = diag_len(s1);
+        const int pe = st1 * H;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const bool ok = jo[r] < L1 && kok;
+            const int el = pe + ve[r];
+            z4[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rZ4, ok ? el * 16 : kOOB, 0, 0));
+            zg[r] = bld(rZ1, ok ? el * 4 : kOOB);
+        }
+    };
+
+    f32x4 z4s[4][NR];
+    float zgs[4][NR];
+    int st = 0;   // stash index of the first cell of diagonal s
+    int stz = 0;  // ... of diagonal s + kZD
+#pragma unroll
+    for (int i = 0; i < kZD; ++i) {
+        load_z(i, stz, z4s[i], zgs[i]);
+        stz += diag_len(i);
+    }
+    // wait for the first sets here, once: the loop then starts with nothing in flight, the same state
+    // for every diagonal, and the compiler's per-step waits only cover the kZD-step-old prefetch
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+
+    // diagonal s at position POS = s mod 4 of the unrolled loop: buffer s & 1 is written and 1 - (s & 1)
+    // read; Z set POS is consumed and set (POS + kZD) mod 4 refilled for diagonal s + kZD
+    auto step = [&](int s, auto POSc) {
+        constexpr int POS = decltype(POSc)::value;
+        constexpr int CB = POS & 1;
+        const int L = diag_len(s);
+        load_z(s + kZD, stz, z4s[(POS + kZD) & 3], zgs[(POS + kZD) & 3]);
+        stz += diag_len(s + kZD);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
+        const bool dl = s >= w;
+        const int lo = dl ? s - (w - 1) : 0;
+        const int Ml = L < s - lo ? L : s - lo;  // position j has a left predecessor iff j < Ml
+        const int Tu = dl ? 0 : 1;                // ... and an upper one iff Tu <= j < L
+        const unsigned char* hsp = smem + (1 - CB) * HBUF;
+        const unsigned char* csp = smem + 2 * HBUF + (1 - CB) * CBUF;
+        const int al = dl ? oah[2] : oah[1], au = dl ? oah[1] : oah[0];
+        const int rl = ja < Ml ? al : oza;
+        const int ru = (ja >= Tu && ja < L) ? au : oza;
+        f16x8 Ah[KB], Al[KB];
+#pragma unroll
+        for (int t = 0; t < KB; ++t) {
+            const int k0 = 32 * t + 8 * q;
+            const int row = k0 < HP ? rl : (k0 < 2 * HP ? ru : oza);
+            const int off = 2 * (k0 < HP ? k0 : (k0 < 2 * HP ? k0 - HP : 0));
+            const unsigned char* p = hsp + row + off;
+            Ah[t] = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p, 16));
+            Al[t] = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p + 2 * HP, 16));
+        }
+        float cl[NR], cu[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int ol = dl ? opc[r][2] : opc[r][1], ou = dl ? opc[r][1] : opc[r][0];
+            cl[r] = *reinterpret_cast<const float*>(csp + (jo[r] < Ml ? ol : ozc));
+            cu[r] = *reinterpret_cast<const float*>(csp + ((jo[r] >= Tu && jo[r] < L) ? ou : ozc));
+        }
+        f32x4 acc[5];
+#pragma unroll
+        for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < KB; ++t)
+#pragma unroll
+            for (int g = 0; g < 5; ++g) {
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[t], Bh[g][t], acc[g], 0, 0, 0);
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[t], Bl[g][t], acc[g], 0, 0, 0);
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al[t], Bh[g][t], acc[g], 0, 0, 0);
+            }
+        const f32x4(&zc4)[NR] = z4s[POS];
+        const float(&zcg)[NR] = zgs[POS];
+        const int ph = HB + lo * DA + s * DS;  // h offset of diagonal position 0, minus 4 kk
+        const int pe = st * H;                 // stash element of diagonal position 0
+        unsigned char* cw = smem + 2 * HBUF + CB * CBUF;
+        unsigned char* hw = smem + CB * HBUF;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const bool ok = jo[r] < L && kok;
+            const float ig = sigm(__builtin_fmaf(acc[0][r], us[0], zc4[r][0]));
+            const float fl = sigm(__builtin_fmaf(acc[1][r], us[1], zc4[r][1]));
+            const float fu = sigm(__builtin_fmaf(acc[2][r], us[2], zc4[r][2]));
+            const float og = sigm(__builtin_fmaf(acc[3][r], us[3], zc4[r][3]));
+            const float gg = ftanh2(__builtin_fmaf(acc[4][r], us[4], zcg[r]));
+            const float c = __builtin_fmaf(fl, cl[r], __builtin_fmaf(fu, cu[r], ig * gg));
+            const float hv = og * ftanh2(c);
+            *reinterpret_cast<float*>(cw + (ok ? owc[r] : oxc)) = c;
+            _Float16 hh, hl;
+            split16(hv * kHScale, hh, hl);
+            _Float16* hp = reinterpret_cast<_Float16*>(hw + (ok ? owh[r] : oxh));
+            hp[0] = hh;
+            hp[HP] = hl;
+            bst(hv, rH, ok ? ph + vh[r] : kOOB);
+            const int el = pe + ve[r];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{ig, fl, fu, og}), rS4,
+                                                   ok ? el * 16 : kOOB, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{gg, c}), rS2, ok ? el * 8 : kOOB,
+                                                  0, 0);
+        }
+        st += L;
+        __syncthreads();
+    };
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+        step(s, IC<0>{});
+        step(s + 1, IC<1>{});
+        step(s + 2, IC<2>{});
+        step(s + 3, IC<3>{});
+    }
+    if (s < S) step(s, IC<0>{});
+    if (s + 1 < S) step(s + 1, IC<1>{});
+    if (s + 2 < S) step(s + 2, IC<2>{});
+}
+
+typedef void (*Fwd16Kernel)(Dev, const float*, const float*, const float*, float*, float*);
+
+// instantiated hidden sizes (the workloads' 2, 4, 10, 16, 32 and 50), each with its cell-group count CG
+// and accumulator rows NR = 1..4; the widest diagonal must fit 16 CG cells
+struct F16Entry {
+    int H, CG, NB, HP;
+    Fwd16Kernel fwd[4];
+};
+#define MDL_F16(h, cg)                                                                           \
+    {h, cg, F16Shape<h>::NB, F16Shape<h>::HP,                                                    \
+     {k_fwd16<h, cg, 1>, k_fwd16<h, cg, 2>, k_fwd16<h, cg, 3>, k_fwd16<h, cg, 4>}}
+// two waves per SIMD (8 waves) where the registers allow it, else one
+const F16Entry kF16[] = {MDL_F16(2, 8),  MDL_F16(4, 8),  MDL_F16(10, 8),
+                         MDL_F16(16, 8), MDL_F16(32, 4), MDL_F16(50, 1)};
+#undef MDL_F16
+
+const F16Entry* f16_entry(int H, int Lmax) {
+    for (const auto& m : kF16)
+        if (m.H == H) return (Lmax + m.CG - 1) / m.CG <= 16 ? &m : nullptr;
+    return nullptr;
+}
+
+size_t f16_lds(const F16Entry& m) {
+    const size_t nrw = 16 * (size_t)m.CG + 2;
+    return 2 * nrw * (2 * m.HP + 8) * 2 + 2 * nrw * (m.H + 4) * 4;
+}
+
+}  // namespace
+
+bool fwd16_supported(int H, int Lmax) { return f16_entry(H, Lmax) != nullptr; }
+
+size_t fwd16_lds(int H, int Lmax) {
+    const F16Entry* m = f16_entry(H, Lmax);
+    return m ? f16_lds(*m) : 0;
+}
+
+hipError_t launch_fwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
+                        float* h_dirs, hipStream_t st) {
+    const F16Entry* m = f16_entry(H, D.max_diag);
+    if (!m) return hipErrorInvalidValue;
+    const int cells = (D.max_diag + m->CG - 1) / m->CG;  // widest diagonal's cells per group, <= 16
+    const int nr = (cells + 3) / 4;
+    hipLaunchKernelGGL(m->fwd[nr - 1], dim3(4 * D.n), dim3(64 * m->NB * m->CG), f16_lds(*m), st, D, Ul, Uu, Z,
+                       stash, h_dirs);
+    return hipGetLastError();
+}
+
+}  // namespace mdl

@@ -8,8 +8,9 @@
 //     Z[d][cell][n] = sum_c x[cell][c] * Wx[d][c][n] + b[d][n],
 // on the matrix cores (v_mfma_f32_16x16x4_f32: A 16 cells x 4 channels,
 // B 4 channels x 16 gate columns, fp32 products and accumulation). The cell's
-// row of Z is written at its position in each direction's diagonal-major
-// stash, so the wavefront kernel reads each anti-diagonal contiguously.
+// pre-activations are written at its position in each direction's
+// diagonal-major order (layouts Z4 / Z1), so the wavefront kernel reads each
+// anti-diagonal contiguously.
 // With C <= 20 input channels the kernel is bound by writing Z (5H floats per
 // cell and direction), not by the matrix cores.
 #include "kernels.h"
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(256) void k_proj(Dev D, const XT* __restrict__ xc, 
     if (cell0 >= D.T) return;  // whole wave leaves together
     const int G = 5 * H;
     const int NT = 4 * G;
+    float* Z1 = Z + z1_offset(D.T, H);
 
     // A operand: lane supplies x[cell0 + (lane % 16)][4*ks + lane / 16]
     const int64_t ca = cell0 + (lane & 15);
@@ -74,6 +76,7 @@ __global__ __launch_bounds__(256) void k_proj(Dev D, const XT* __restrict__ xc, 
         const bool nok = n < NT;
         const int d = nok ? n / G : 0;
         const int gcol = nok ? n - d * G : 0;
+        const int g = gcol / H, k = gcol - g * H;  // gate, hidden unit
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int ks = 0; ks < ksteps; ++ks) {
             const int k = 4 * ks + (lane >> 4);
@@ -87,7 +90,10 @@ __global__ __launch_bounds__(256) void k_proj(Dev D, const XT* __restrict__ xc, 
             for (int r = 0; r < 4; ++r) {
                 // select without dynamic register indexing
                 const int64_t t = d == 0 ? dst[r][0] : d == 1 ? dst[r][1] : d == 2 ? dst[r][2] : dst[r][3];
-                if (t >= 0) Z[t * G + gcol] = acc[r] + bb;
+                if (t >= 0) {
+                    if (g < 4) Z[(t * H + k) * 4 + g] = acc[r] + bb;
+                    else Z1[t * H + k] = acc[r] + bb;
+                }
             }
         }
     }

@@ -16,6 +16,7 @@
 // dx of the same cells from the staged gate gradients. Chunk partial sums are then added in
 // chunk order by a second kernel, so the result is bit-reproducible.
 #include "kernels.h"
+#include "devmath.h"
 
 namespace mdl {
 
@@ -35,20 +36,11 @@ WsLayout ws_layout(int64_t T, int64_t nchunks, int C, int H) {
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int ACC_TILES = 16;   // 16x16 output tiles one wave owns per pass
 constexpr int STAGE_H = 4096;   // staged predecessor-h values per tile (all directions)
 constexpr int STAGE_D = 10240;  // staged gate-gradient values per tile (all directions)
 
-constexpr uint32_t kBufCfg = 0x00020000;  // dword 3 of a raw 32-bit buffer descriptor (gfx9 family)
-constexpr int kOOB = 0x7ffffff0;           // byte offset past every range: loads return 0
-
-__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kBufCfg);
-}
-__device__ inline float bld(__amdgpu_buffer_rsrc_t r, int off) {
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
+constexpr int kOOB = 0x7ffffff0;  // byte offset past every buffer range: loads return 0
 
 // n / d for n < 2^16, d < 2^16, with m = 2^32 / d + 1
 __host__ __device__ inline uint32_t magic(uint32_t d) { return (uint32_t)(0xffffffffu / d) + 1u; }

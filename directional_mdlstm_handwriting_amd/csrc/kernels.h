@@ -70,6 +70,18 @@ MDL_HD inline int find_example(const int64_t* off, int n, int64_t g) {
 }
 
 // Workspace carving for one MDLSTM layer (all offsets 256-byte aligned).
+// Projection and gate-stash layouts. For direction d, computed cell t (each
+// example's cells in diagonal-major order, examples one after another) and
+// hidden unit k, with T computed cells per direction:
+//   Z4[((d*T + t)*H + k)*4 + g]  pre-activation x.Wx + b of gate g = i, f_l, f_u, o
+//   Z1[(d*T + t)*H + k]          pre-activation of the cell input g
+//   S4[((d*T + t)*H + k)*4 + g]  gate values i, f_l, f_u, o
+//   S2[((d*T + t)*H + k)*2 + m]  m = 0: g, m = 1: the memory state c
+// A lane owning (cell, k) reads or writes its four sigmoid gates with one
+// 16-byte access. Z1 follows Z4 in the workspace's projection region, S2
+// follows S4 in its stash region.
+MDL_HD inline int64_t z1_offset(int64_t T, int H) { return 4 * T * 4 * (int64_t)H; }
+
 struct WsLayout {
     size_t stash = 0;   // float [4][T][6H]: gates i, f_l, f_u, o, g and memory state c of every cell
     size_t zda = 0;     // float [4][T][5H]: projection x.Wx+b (forward), gate gradients dA (backward)
@@ -89,6 +101,11 @@ size_t fwd_chain_lds(int H, int Lmax);
 size_t bwd_chain_lds(int H, int Lmax);
 int chain_max_items();
 bool chain_uses_mfma(int H, int Lmax);
+// forward wavefront on the f16 matrix cores (split operands, fp32-class accuracy)
+bool fwd16_supported(int H, int Lmax);
+size_t fwd16_lds(int H, int Lmax);
+hipError_t launch_fwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
+                        float* h_dirs, hipStream_t st);
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z,
                             float* stash, float* h_dirs, hipStream_t st);
 hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st);
