@@ -255,12 +255,12 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     const mdl::Layout& L = L_of(layout);
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nchunks, C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
-    if (!mdl::fwd16_supported(H, L.max_diag) && !mdl::chain_uses_mfma(H, L.max_diag) &&
-        (int64_t)L.max_diag * H > mdl::chain_max_items())
+    const bool fused = mdl::fwd16_supported(H, C, x_dtype, L.max_diag);
+    if (!fused && (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_forward: widest diagonal x H exceeds the wavefront kernel's items");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
-    if (mdl::fwd_chain_lds(H, L.max_diag) > lmax)
+    if ((fused ? mdl::fwd16_lds(H, C, x_dtype, L.max_diag) : mdl::fwd_chain_lds(H, L.max_diag)) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_forward: recurrent weights and diagonal state exceed LDS");
     // the kernels address these tensors with 32-bit byte offsets
     if (4 * L.computed_cells * 6 * H * 4 >= (int64_t(1) << 31) || 4LL * L.Hc * L.Wc * H * 4 >= (int64_t(1) << 31))
@@ -276,12 +276,15 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
         e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_forward: zero fill");
-    {
-        Timed t("projection", st);
-        e = mdl::launch_projection(D, x_canvas, x_dtype, C, H, Wx, b, Z, st);
-    }
-    if (e != hipSuccess) return hip_fail(e, "mdl_forward: projection");
-    {
+    if (fused) {
+        Timed t("fwd_wavefront", st);
+        e = mdl::launch_fwd16(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, stash, h_dirs, st);
+    } else {
+        {
+            Timed t("projection", st);
+            e = mdl::launch_projection(D, x_canvas, x_dtype, C, H, Wx, b, Z, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, "mdl_forward: projection");
         Timed t("fwd_wavefront", st);
         e = mdl::launch_fwd_chain(D, H, Ul, Uu, Z, stash, h_dirs, st);
     }
@@ -320,7 +323,8 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     const mdl::Layout& L = L_of(layout);
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nchunks, C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_backward: workspace smaller than mdl_workspace_size");
-    if (!mdl::chain_uses_mfma(H, L.max_diag) && (int64_t)L.max_diag * H > mdl::chain_max_items())
+    if (!mdl::bwd16_supported(H, L.max_diag) && !mdl::chain_uses_mfma(H, L.max_diag) &&
+        (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_backward: widest diagonal x H exceeds the wavefront kernel's items");
     if (!mdl::wgrad_supported(C, H))
         return fail(MDL_EUNSUPPORTED, "mdl_backward: C and H exceed the weight-gradient kernel's register tile");

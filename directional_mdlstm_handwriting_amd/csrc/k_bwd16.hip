@@ -1,0 +1,407 @@
+// k_bwd16.hip — reverse wavefront (2D BPTT) with the recurrent product on the f16 matrix cores.
+//
+// The backward pass visits each unit's diagonals in reverse ("Single Stream
+// Parallelization of Generalized LSTM-Like RNNs on a GPU": back-propagation in
+// reverse order of the forward dependencies; RETURNN §4.2 for the 2D case).
+// For cell (a, b) on diagonal s, with da the gradient of its five gate
+// pre-activations and its successors R = (a, b+1), D = (a+1, b) on s+1:
+//     dh     = dy(a, b) + da(R) . Ul^T + da(D) . Uu^T
+//     dc_in  = dc(R) f_l(R) + dc(D) f_u(D)
+//     tc = tanh c;  dc = dc_in + dh o (1 - tc^2)
+//     da = [dc g i(1-i), dc c_l f_l(1-f_l), dc c_u f_u(1-f_u), dh tc o(1-o), dc i (1-g^2)]
+// The product runs on v_mfma_f32_16x16x32_f16 with both operands split into
+// f16 hi + lo pairs (three partial products summed in fp32). Gate gradients
+// have no bound, so each (cell, 16-wide block of hidden units) row of da is
+// scaled by the power of two that brings its largest magnitude into
+// [2^14, 2^15) before it is split; the exponent sits in LDS beside it and the
+// accumulator of that row and block is scaled back exactly. The K dimension
+// orders da by (hidden unit, gate) with the five gates padded to eight, so a
+// lane stores its split gate gradients with two 16-byte LDS writes.
+//
+// Work split, LDS row permutation, fixed accumulator row count, 4-step
+// unrolling and the three-diagonal prefetch (here of the forward's gate
+// stash, the predecessors' c and the upstream gradient) are those of the
+// forward kernel; see k_fwd16.hip.
+#include "kernels.h"
+#include "devmath.h"
+
+#include <type_traits>
+
+namespace mdl {
+
+namespace {
+
+constexpr int kOOB = 0x40000000;  // byte offset past every per-unit range used here (1 GiB)
+constexpr int kPD = 3;            // diagonals of prefetch ahead
+
+template <int H>
+struct B16Shape {
+    static constexpr int NB = (H + 15) / 16;  // blocks of 16 hidden units
+    static constexpr int KA = 128;            // K extent of one successor's da per block: 16 units x 8 slots
+    static constexpr int KT = KA / 32;        // K blocks of 32 per (successor, block)
+    static_assert(NB <= 2, "hidden size above 32");
+};
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// exact power-of-two scale 2^E that brings m (> 0) into [2^14, 2^15); 0 for m = 0
+__device__ inline int scale_exp(uint32_t mbits) {
+    if (mbits == 0) return 0;
+    int E = 14 - ((int)((mbits >> 23) & 255) - 127);
+    return E < -100 ? -100 : (E > 100 ? 100 : E);
+}
+
+// largest value of x over the 16 lanes of each row of the wave (DPP within rows)
+__device__ inline uint32_t row16_max(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false));  // row_ror:4
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false));  // row_ror:8
+    return x;
+}
+
+template <int H, int CG, int NR>
+__global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, const float* __restrict__ Ul,
+                                                                     const float* __restrict__ Uu,
+                                                                     const float* __restrict__ stash,
+                                                                     const float* __restrict__ dy_flat,
+                                                                     const float* __restrict__ dh_dirs,
+                                                                     float* __restrict__ dA) {
+    using Sh = B16Shape<H>;
+    constexpr int NB = Sh::NB, KA = Sh::KA, KT = Sh::KT;
+    constexpr int G = 5 * H;
+    const int u = D.units[blockIdx.x];
+    const int e = u >> 2, d = u & 3;
+    const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
+    const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kb = wave / CG, cg = wave % CG;
+    const int q = lane >> 4, col = lane & 15;
+    const int kk = kb * 16 + col;  // this lane's hidden unit (output column, and produced da's unit)
+    const bool kok = kk < H;
+    const int kc = kok ? kk : 0;
+
+    // B operand for output block kb: [Ul^T; Uu^T] rows in the (unit, gate) K order. For successor m
+    // (0: right, uses Ul; 1: down, uses Uu), input block bi and K block t, the lane holds K rows
+    // 32t + 8q + i = 8 (4t + q) + i of that block: unit k' = 16 bi + 4t + q, gate i (zero for i >= 5).
+    // Scaled per output column by 2^E and split into f16 hi + lo.
+    f16x8 Bh[2][NB][KT], Bl[2][NB][KT];
+    float ecol;  // the column's scale exponent, negated
+    {
+        float v[2][NB][KT][8];
+        float m = 0.f;
+#pragma unroll
+        for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int kp = 16 * bi + 4 * t + q;
+                        float x = 0.f;
+                        if (kok && kp < H && i < 5) {
+                            const float* U = sm ? Uu : Ul;
+                            x = U[((int64_t)d * H + kk) * G + i * H + kp];
+                        }
+                        v[sm][bi][t][i] = x;
+                        m = fmaxf(m, fabsf(x));
+                    }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        const int E = scale_exp(__float_as_uint(m));
+        ecol = (float)(-E);
+#pragma unroll
+        for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+                for (int t = 0; t < KT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        _Float16 hi, lo;
+                        split16(ldexpf(v[sm][bi][t][i], E), hi, lo);
+                        Bh[sm][bi][t][i] = hi;
+                        Bl[sm][bi][t][i] = lo;
+                    }
+    }
+    const int ec = (int)ecol;
+
+    // LDS, two buffers (later / current diagonal) of NRW rows: the split, scaled da as f16
+    // [hi | lo][block][unit][8] (row stride RA halves), the scale exponents [block] (ints), and
+    // dc*f_l, dc*f_u (row stride CS floats). Rows: P(position), zero row ZR, discard row XR.
+    constexpr int RA = 2 * NB * KA + 8, CS = H + 4;
+    constexpr int NRW = 16 * CG + 2, ZR = 16 * CG, XR = 16 * CG + 1;
+    constexpr int ABUF = NRW * RA * 2, EBUF = NRW * NB * 4, CBUF = NRW * CS * 4;
+    constexpr int OFF_E = 2 * ABUF, OFF_CL = OFF_E + 2 * EBUF, OFF_CU = OFF_CL + 2 * CBUF;
+    constexpr int LDS_BYTES = OFF_CU + 2 * CBUF;
+    extern __shared__ __align__(16) unsigned char smem[];
+    {
+        uint32_t* z32 = reinterpret_cast<uint32_t*>(smem);
+        for (int i = threadIdx.x; i < LDS_BYTES / 4; i += blockDim.x) z32[i] = 0u;
+    }
+    const int64_t base = (int64_t)d * D.T + D.cell_off[e];
+    const int64_t cells = (int64_t)h * w;
+    const int64_t o1 = z1_offset(D.T, H);
+    const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 16 * H);
+    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 2 * H, cells * 8 * H);
+    const __amdgpu_buffer_rsrc_t rA4 = rsrc(dA + base * 4 * H, cells * 16 * H);
+    const __amdgpu_buffer_rsrc_t rA1 = rsrc(dA + o1 + base * H, cells * 4 * H);
+    const bool per_dir = dh_dirs != nullptr;
+    const __amdgpu_buffer_rsrc_t rU =
+        per_dir ? rsrc(dh_dirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4)
+                : rsrc(dy_flat + D.flat_off[e] * H, (int64_t)rh * rw * H * 4);
+    const int S = h + w - 1;
+
+    auto P = [&](int j) {
+        if (j < 0 || j >= 16 * CG) return ZR;
+        const int i = j / CG;
+        return 16 * (j % CG) + 4 * (i & 3) + (i >> 2);
+    };
+
+    // Cell (a, b) sits at canvas (Y0 + SY a, X0 + SX b). The upstream gradient's byte offset is
+    // UB + a UA + s US + 4 kk (b = s - a): on the canvas plane for a per-direction gradient, else in
+    // the example's flat real-pixel block, where the cell must also lie in the real region.
+    const int SY = (d & 2) ? -1 : 1, SX = (d & 1) ? -1 : 1;
+    const int Y0 = (d & 2) ? y0 + h - 1 : y0, X0 = (d & 1) ? x0 + w - 1 : x0;
+    const int H4 = 4 * H;
+    const int rowlen = per_dir ? D.Wc : rw;
+    const int UY = per_dir ? Y0 : Y0 - ry0, UX = per_dir ? X0 : X0 - rx0;
+    const int UA = SY * rowlen * H4 - SX * H4, US = SX * H4;
+    const int UB = (UY * rowlen + UX) * H4;
+    // real region in unit coordinates: a in [ar0, ar1), b in [br0, br1)
+    const int ar0 = (d & 2) ? h - (ry0 - y0) - rh : ry0 - y0, ar1 = ar0 + rh;
+    const int br0 = (d & 1) ? w - (rx0 - x0) - rw : rx0 - x0, br1 = br0 + rw;
+
+    int jo[NR], vu[NR], ve[NR];  // per accumulator row r: diagonal position, upstream offset, stash element
+    int owa[NR], owe[NR], owc[NR];  // own LDS row (da, exponent, dc*f) byte offsets within a buffer
+    int oe[NR][3], occ[NR][3];      // LDS byte offsets at positions jo - 1, jo, jo + 1: exponent row, c row
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        jo[r] = (4 * r + q) * CG + cg;
+        vu[r] = jo[r] * UA + 4 * kk;
+        ve[r] = jo[r] * H + kk;
+        const int pw = 16 * cg + 4 * q + r;  // P(jo[r])
+        owa[r] = pw * RA * 2 + (kb * KA + 8 * col) * 2;
+        owe[r] = (pw * NB + kb) * 4;
+        owc[r] = pw * CS * 4 + 4 * kc;
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+            const int pr = P(jo[r] + m - 1);
+            oe[r][m] = pr * NB * 4;
+            occ[r][m] = pr * CS * 4 + 4 * kc;
+        }
+    }
+    const int oxa = XR * RA * 2 + (kb * KA + 8 * col) * 2, oxe = (XR * NB + kb) * 4, oxc = XR * CS * 4 + 4 * kc;
+    const int ozc = ZR * CS * 4 + 4 * kc, oze = ZR * NB * 4;
+    const int ja = (4 * (col & 3) + (col >> 2)) * CG + cg;  // diagonal position of this lane's A row
+    int oa[3];  // LDS byte offsets of the da rows at positions ja - 1, ja, ja + 1
+#pragma unroll
+    for (int m = 0; m < 3; ++m) oa[m] = P(ja + m - 1) * RA * 2;
+    const int oza = ZR * RA * 2;
+
+    auto diag_len = [&](int s) {
+        if (s < 0 || s >= S) return 0;
+        const int lo = s > w - 1 ? s - (w - 1) : 0;
+        const int hi = s < h - 1 ? s : h - 1;
+        return hi - lo + 1;
+    };
+    auto diag_lo = [&](int s) { return s > w - 1 ? s - (w - 1) : 0; };
+
+    // forward values of one diagonal's cells: i, f_l, f_u, o | g, c | c_left | c_up | upstream dh
+    struct Fw {
+        f32x4 g4[NR];
+        f32x2 g2[NR];
+        float cl[NR], cu[NR], dy[NR];
+    };
+    // s1: diagonal, st1: stash index of its first cell
+    auto load_f = [&](int s1, int st1, Fw& f) {
+        const int L1 = diag_len(s1);
+        const int lo1 = diag_lo(s1 < 0 ? 0 : s1);
+        const bool dl = s1 >= w;
+        const int Ml = L1 < s1 - lo1 ? L1 : s1 - lo1;  // left predecessor iff j < Ml
+        const int Tu = dl ? 0 : 1;                       // upper predecessor iff Tu <= j
+        const int stp = st1 - diag_len(s1 - 1);         // first cell of diagonal s1 - 1
+        const int pe = st1 * H, pl = (stp + (dl ? 1 : 0)) * H, pu = pl - H;
+        const int pu0 = UB + lo1 * UA + s1 * US;
+        // real-region bounds as position ranges: a = lo1 + j in [ar0, ar1), b = s1 - lo1 - j in [br0, br1)
+        const int jr0 = max(ar0 - lo1, s1 - lo1 - br1 + 1), jr1 = min(ar1 - lo1, s1 - lo1 - br0 + 1);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const bool ok = (jo[r] < L1) & kok;
+            const int el = pe + ve[r];
+            f.g4[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, ok ? el * 16 : kOOB, 0, 0));
+            f.g2[r] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rS2, ok ? el * 8 : kOOB, 0, 0));
+            // predicates combined without short-circuit evaluation: plain selects, no branches
+            const bool vl = ok & (jo[r] < Ml), vu_ = ok & (jo[r] >= Tu);
+            const bool vy = ok & (per_dir | ((jo[r] >= jr0) & (jo[r] < jr1)));
+            f.cl[r] = bld(rS2, vl ? (pl + ve[r]) * 8 + 4 : kOOB);
+            f.cu[r] = bld(rS2, vu_ ? (pu + ve[r]) * 8 + 4 : kOOB);
+            f.dy[r] = bld(rU, vy ? pu0 + vu[r] : kOOB);
+        }
+    };
+
+    Fw fs[4];
+    // stash index of the first cell of diagonal s and of the prefetch diagonal s - kPD
+    int st = (int)cells - 1;  // diagonal S - 1 is the single last cell
+    int stz = st;
+#pragma unroll
+    for (int i = 0; i < kPD; ++i) {
+        load_f(S - 1 - i, stz, fs[i]);
+        stz -= diag_len(S - 2 - i);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loop starts with nothing in flight
+    __syncthreads();
+
+    // diagonal s at position POS of the unrolled loop (POS = (S - 1 - s) mod 4): buffer POS & 1 is
+    // written, 1 - (POS & 1) holds diagonal s + 1; prefetch set POS is consumed, (POS + kPD) & 3 refilled
+    auto step = [&](int s, auto POSc) {
+        constexpr int POS = decltype(POSc)::value;
+        constexpr int CB = POS & 1;
+        const int L = diag_len(s), L1 = diag_len(s + 1);
+        load_f(s - kPD, stz, fs[(POS + kPD) & 3]);
+        stz -= diag_len(s - kPD - 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
+        const Fw& f = fs[POS];
+        const int dn = s >= w - 1 ? 1 : 0;  // successors of position j: right j - dn, down j + 1 - dn
+        const unsigned char* ap = smem + (1 - CB) * ABUF;
+        const unsigned char* ep = smem + OFF_E + (1 - CB) * EBUF;
+        const unsigned char* clp = smem + OFF_CL + (1 - CB) * CBUF;
+        const unsigned char* cup = smem + OFF_CU + (1 - CB) * CBUF;
+        // A operand rows of this lane's cell: right and down successors (zero row when absent)
+        const int rr = ja >= dn ? (dn ? oa[0] : oa[1]) : oza;
+        const int rd = (ja + 1 - dn < L1) ? (dn ? oa[1] : oa[2]) : oza;
+        f32x4 acc[2][NB];
+#pragma unroll
+        for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi) acc[sm][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+                for (int t = 0; t < KT; ++t) {
+                    const unsigned char* p = ap + (sm ? rd : rr) + (bi * KA + 32 * t + 8 * q) * 2;
+                    const f16x8 ah = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p, 16));
+                    const f16x8 al = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p + NB * KA * 2, 16));
+                    acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[sm][bi][t], acc[sm][bi], 0, 0, 0);
+                    acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[sm][bi][t], acc[sm][bi], 0, 0, 0);
+                    acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[sm][bi][t], acc[sm][bi], 0, 0, 0);
+                }
+        const int pe = st * H;
+        unsigned char* aw = smem + CB * ABUF;
+        unsigned char* ew = smem + OFF_E + CB * EBUF;
+        unsigned char* clw = smem + OFF_CL + CB * CBUF;
+        unsigned char* cuw = smem + OFF_CU + CB * CBUF;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const bool ok = jo[r] < L && kok;
+            const bool hr = jo[r] >= dn, hd = jo[r] + 1 - dn < L1;  // successors present
+            const int mr = dn ? 0 : 1, md = dn ? 1 : 2;             // their position slots
+            float dh = f.dy[r];
+#pragma unroll
+            for (int bi = 0; bi < NB; ++bi) {
+                const int er = *reinterpret_cast<const int*>(ep + (hr ? oe[r][mr] : oze) + 4 * bi);
+                const int ed = *reinterpret_cast<const int*>(ep + (hd ? oe[r][md] : oze) + 4 * bi);
+                dh += ldexpf(acc[0][bi][r], ec - er) + ldexpf(acc[1][bi][r], ec - ed);
+            }
+            const float dcin = *reinterpret_cast<const float*>(clp + (hr ? occ[r][mr] : ozc)) +
+                               *reinterpret_cast<const float*>(cup + (hd ? occ[r][md] : ozc));
+            const float ig = f.g4[r][0], fl = f.g4[r][1], fu = f.g4[r][2], og = f.g4[r][3];
+            const float gg = f.g2[r][0], c = f.g2[r][1];
+            const float tc = ftanh2(c);
+            const float dov = dh * tc;
+            const float dc = __builtin_fmaf(dh * og, 1.f - tc * tc, dcin);
+            const float d0 = dc * gg * ig * (1.f - ig);
+            const float d1 = dc * f.cl[r] * fl * (1.f - fl);
+            const float d2 = dc * f.cu[r] * fu * (1.f - fu);
+            const float d3 = dov * og * (1.f - og);
+            const float d4 = dc * ig * (1.f - gg * gg);
+            // scale of this (cell, block): the largest |da| over the 16 units of the block
+            uint32_t mb = max(max(__float_as_uint(fabsf(d0)), __float_as_uint(fabsf(d1))),
+                              max(max(__float_as_uint(fabsf(d2)), __float_as_uint(fabsf(d3))),
+                                  __float_as_uint(fabsf(d4))));
+            mb = row16_max(ok ? mb : 0u);
+            const int E = scale_exp(mb);
+            const float s0 = ldexpf(d0, E), s1 = ldexpf(d1, E), s2 = ldexpf(d2, E), s3 = ldexpf(d3, E),
+                        s4 = ldexpf(d4, E);
+            _Float16 h0, l0, h1, l1, h2, l2, h3, l3, h4, l4;
+            split16(s0, h0, l0);
+            split16(s1, h1, l1);
+            split16(s2, h2, l2);
+            split16(s3, h3, l3);
+            split16(s4, h4, l4);
+            const f16x8 hv = {h0, h1, h2, h3, h4, (_Float16)0, (_Float16)0, (_Float16)0};
+            const f16x8 lv = {l0, l1, l2, l3, l4, (_Float16)0, (_Float16)0, (_Float16)0};
+            unsigned char* pa = aw + (ok ? owa[r] : oxa);
+            *reinterpret_cast<f16x8*>(__builtin_assume_aligned(pa, 16)) = hv;
+            *reinterpret_cast<f16x8*>(__builtin_assume_aligned(pa + NB * KA * 2, 16)) = lv;
+            *reinterpret_cast<int*>(ew + (ok ? owe[r] : oxe)) = E;
+            *reinterpret_cast<float*>(clw + (ok ? owc[r] : oxc)) = dc * fl;
+            *reinterpret_cast<float*>(cuw + (ok ? owc[r] : oxc)) = dc * fu;
+            const int el = pe + ve[r];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{d0, d1, d2, d3}), rA4,
+                                                   ok ? el * 16 : kOOB, 0, 0);
+            bst(d4, rA1, ok ? el * 4 : kOOB);
+        }
+        st -= diag_len(s - 1);
+        __syncthreads();
+    };
+    int s = S - 1;
+    for (; s - 3 >= 0; s -= 4) {
+        step(s, IC<0>{});
+        step(s - 1, IC<1>{});
+        step(s - 2, IC<2>{});
+        step(s - 3, IC<3>{});
+    }
+    if (s >= 0) step(s, IC<0>{});
+    if (s - 1 >= 0) step(s - 1, IC<1>{});
+    if (s - 2 >= 0) step(s - 2, IC<2>{});
+}
+
+typedef void (*Bwd16Kernel)(Dev, const float*, const float*, const float*, const float*, const float*, float*);
+
+struct B16Entry {
+    int H, CG, NB;
+    Bwd16Kernel bwd[4];
+};
+#define MDL_B16(h, cg) \
+    {h, cg, B16Shape<h>::NB, {k_bwd16<h, cg, 1>, k_bwd16<h, cg, 2>, k_bwd16<h, cg, 3>, k_bwd16<h, cg, 4>}}
+const B16Entry kB16[] = {MDL_B16(2, 4), MDL_B16(4, 4), MDL_B16(10, 4), MDL_B16(16, 4), MDL_B16(32, 2)};
+#undef MDL_B16
+
+const B16Entry* b16_entry(int H, int Lmax) {
+    for (const auto& m : kB16)
+        if (m.H == H) return (Lmax + m.CG - 1) / m.CG <= 16 ? &m : nullptr;
+    return nullptr;
+}
+
+size_t b16_lds(const B16Entry& m) {
+    const size_t nrw = 16 * (size_t)m.CG + 2;
+    const size_t ra = 2 * (size_t)m.NB * 128 + 8, cs = (size_t)m.H + 4;
+    return 2 * nrw * ra * 2 + 2 * nrw * m.NB * 4 + 4 * nrw * cs * 4;
+}
+
+}  // namespace
+
+bool bwd16_supported(int H, int Lmax) { return b16_entry(H, Lmax) != nullptr; }
+
+size_t bwd16_lds(int H, int Lmax) {
+    const B16Entry* m = b16_entry(H, Lmax);
+    return m ? b16_lds(*m) : 0;
+}
+
+hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
+                        const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st) {
+    const B16Entry* m = b16_entry(H, D.max_diag);
+    if (!m) return hipErrorInvalidValue;
+    const int cells = (D.max_diag + m->CG - 1) / m->CG;
+    const int nr = (cells + 3) / 4;
+    hipLaunchKernelGGL(m->bwd[nr - 1], dim3(4 * D.n), dim3(64 * m->NB * m->CG), b16_lds(*m), st, D, Ul, Uu, stash,
+                       dy_flat, dh_dirs, dA);
+    return hipGetLastError();
+}
+
+}  // namespace mdl

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
 }
 
 // Backward over the diagonals in reverse. Upstream gradient from dy_flat (same
-// for every direction) or dh_dirs [4][Hc][Wc][H]. dA out [4][T][5H].
+// for every direction) or dh_dirs [4][Hc][Wc][H]. dA out (dA4, dA1).
 __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int Lmax, const float* __restrict__ Ul,
                                                              const float* __restrict__ Uu,
                                                              const float* __restrict__ stash,
@@ -183,7 +183,8 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
     const float* S4d = stash + base * 4 * H;
     const float* S2d = stash + z1_offset(D.T, H) + base * 2 * H;
-    float* dAd = dA + base * G;
+    float* dA4d = dA + base * 4 * H;
+    float* dA1d = dA + z1_offset(D.T, H) + base * H;
     const float* dyb = dy_flat ? dy_flat + D.flat_off[e] * H : nullptr;
     const float* dhd = dh_dirs ? dh_dirs + (int64_t)d * D.Hc * D.Wc * H : nullptr;
     const int S = h + w - 1;
@@ -248,8 +249,9 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
                 dw[0] = d0; dw[H] = d1; dw[2 * H] = d2; dw[3 * H] = d3; dw[4 * H] = d4;
                 dclw[j * H + k] = dc * fl;
                 dcuw[j * H + k] = dc * fu;
-                float* dg = dAd + (st + j) * G + k;
-                dg[0] = d0; dg[H] = d1; dg[2 * H] = d2; dg[3 * H] = d3; dg[4 * H] = d4;
+                float* dg = dA4d + ((st + j) * H + k) * 4;
+                dg[0] = d0; dg[1] = d1; dg[2] = d2; dg[3] = d3;
+                dA1d[(st + j) * H + k] = d4;
             }
         }
         __syncthreads();
@@ -316,7 +318,8 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
     const int64_t cells = (int64_t)h * w;
     const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 4 * H * 4);
     const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + z1_offset(D.T, H) + base * 2 * H, cells * 2 * H * 4);
-    const __amdgpu_buffer_rsrc_t rA = rsrc(dA + base * G, cells * G * 4);
+    const __amdgpu_buffer_rsrc_t rA4 = rsrc(dA + base * 4 * H, cells * 16 * H);
+    const __amdgpu_buffer_rsrc_t rA1 = rsrc(dA + z1_offset(D.T, H) + base * H, cells * 4 * H);
     // upstream gradient: per-direction canvas tensor, or the flat gradient of the direction sum
     const bool per_dir = dh_dirs != nullptr;
     const __amdgpu_buffer_rsrc_t rU =
@@ -411,12 +414,13 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
                 dclw[jo * H + kk] = dc * fl;
                 dcuw[jo * H + kk] = dc * fu;
             }
-            const int ao = ok ? ((st + jo) * G + kk) * 4 : kOOB;
-            bst(d0, rA, ao);
-            bst(d1, rA, ao + H * 4);
-            bst(d2, rA, ao + 2 * H * 4);
-            bst(d3, rA, ao + 3 * H * 4);
-            bst(d4, rA, ao + 4 * H * 4);
+            const int ea = (st + jo) * H + kk;
+            const int a4 = ok ? ea * 16 : kOOB, a1 = ok ? ea * 4 : kOOB;
+            bst(d0, rA4, a4);
+            bst(d1, rA4, a4 + 4);
+            bst(d2, rA4, a4 + 8);
+            bst(d3, rA4, a4 + 12);
+            bst(d4, rA1, a1);
         }
         __syncthreads();
     };
@@ -462,11 +466,11 @@ int chain_max_items() { return MAXI * CHAIN_THREADS; }
 
 
 size_t fwd_chain_lds(int H, int Lmax) {
-    if (fwd16_supported(H, Lmax)) return fwd16_lds(H, Lmax);
     return sizeof(float) * ((size_t)2 * H * 5 * H + (size_t)4 * Lmax * H);
 }
 
 size_t bwd_chain_lds(int H, int Lmax) {
+    if (bwd16_supported(H, Lmax)) return bwd16_lds(H, Lmax);
     if (mfma_entry(H, Lmax)) return bwd_mfma_lds(H, Lmax);
     return sizeof(float) * ((size_t)2 * H * 5 * H + (size_t)2 * Lmax * 5 * H + (size_t)4 * Lmax * H);
 }
@@ -476,7 +480,6 @@ bool chain_uses_mfma(int H, int Lmax) { return mfma_entry(H, Lmax) != nullptr; }
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
                             float* h_dirs, hipStream_t st) {
     const int Lmax = D.max_diag;
-    if (fwd16_supported(H, Lmax)) return launch_fwd16(D, H, Ul, Uu, Z, stash, h_dirs, st);
     hipLaunchKernelGGL(k_fwd_chain, dim3(4 * D.n), dim3(CHAIN_THREADS), fwd_chain_lds(H, Lmax), st, D, H, Lmax, Ul,
                        Uu, Z, stash, h_dirs);
     return hipGetLastError();
@@ -485,6 +488,7 @@ hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* U
 hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                             const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st) {
     const int Lmax = D.max_diag;
+    if (bwd16_supported(H, Lmax)) return launch_bwd16(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     if (const MfmaEntry* m = mfma_entry(H, Lmax)) {
         hipLaunchKernelGGL(m->bwd, dim3(4 * D.n), dim3(256), bwd_mfma_lds(H, Lmax), st, D, H, Lmax, Ul, Uu, stash,
                            dy_flat, dh_dirs, dA);

@@ -13,7 +13,13 @@
 // 32-wide K block instead of 8 fp32 ones. f16 has a narrow exponent range, so
 // h (|h| < 1) is scaled by 2^14 and each weight column by its own power of
 // two (its largest magnitude lands in [2^14, 2^15)); the accumulator is scaled
-// back exactly before Z is added.
+// back exactly before x.Wx + b is added.
+//
+// The input projection x.Wx + b ("No Padding Please" §IV-B: the input-only
+// part of the gates is one 1x1 convolution) is computed in the same step on
+// the fp32 matrix cores (v_mfma_f32_16x16x4_f32, K = 4 channels per
+// instruction, the bias seeding the accumulator), from the canvas pixels of
+// the diagonal's cells: no projection tensor is written or read.
 //
 // Work split: NB * CG waves; wave = (16-wide block kb of hidden units, cell
 // group cg). Cells of the diagonal are dealt round-robin to the CG cell
@@ -24,7 +30,7 @@
 // instruction sequence: the compiler then knows how many memory operations
 // are in flight and waits for a prefetch with vmcnt(N) instead of draining
 // every store (loads and stores retire in order on this architecture). The
-// projection Z is prefetched three diagonals ahead into four register sets.
+// input pixels are prefetched three diagonals ahead into four register sets.
 // The previous diagonal's h (as scaled f16 hi/lo) and c sit in LDS ping-pong
 // buffers with a zero row standing in for a missing predecessor.
 #include "kernels.h"
@@ -38,7 +44,7 @@ namespace {
 
 constexpr int kOOB = 0x40000000;    // byte offset past every per-unit range used here (1 GiB)
 constexpr float kHScale = 16384.f;  // 2^14: h in (-1, 1) -> f16 range
-constexpr int kZD = 3;              // diagonals of Z prefetch ahead
+constexpr int kZD = 3;              // diagonals of input prefetch ahead
 
 template <int H>
 struct F16Shape {
@@ -51,10 +57,13 @@ struct F16Shape {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int H, int CG, int NR>
-__global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, const float* __restrict__ Ul,
+// KX: K steps of 4 input channels; BF16: canvas pixels stored as bf16
+template <int H, int CG, int NR, int KX, bool BF16>
+__global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, const void* __restrict__ xc, int C,
+                                                                     const float* __restrict__ Wx,
+                                                                     const float* __restrict__ bias,
+                                                                     const float* __restrict__ Ul,
                                                                      const float* __restrict__ Uu,
-                                                                     const float* __restrict__ Z,
                                                                      float* __restrict__ stash,
                                                                      float* __restrict__ hdirs) {
     using Sh = F16Shape<H>;
@@ -110,6 +119,18 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             }
     }
 
+    // input projection: B = Wx[d][4 ks + q][g*H + kk] for K step ks; the bias seeds the accumulators
+    float Bx[5][KX], bz[5];
+#pragma unroll
+    for (int g = 0; g < 5; ++g) {
+        bz[g] = kok ? bias[(int64_t)d * G + g * H + kk] : 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KX; ++ks) {
+            const int c = 4 * ks + q;
+            Bx[g][ks] = (kok && c < C) ? Wx[((int64_t)d * C + c) * G + g * H + kk] : 0.f;
+        }
+    }
+
     // LDS, two buffers (previous / current diagonal) of NRW rows each: h * 2^14 as f16 hi and lo (row
     // stride RS halves), then c (row stride CS floats). Diagonal position j is kept in row P(j) (below);
     // row ZR is zeros, row XR absorbs the writes of lanes without a cell.
@@ -124,8 +145,8 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
     const int64_t cells = (int64_t)h * w;
     const int64_t o1 = z1_offset(D.T, H);
-    const __amdgpu_buffer_rsrc_t rZ4 = rsrc(Z + base * 4 * H, cells * 16 * H);
-    const __amdgpu_buffer_rsrc_t rZ1 = rsrc(Z + o1 + base * H, cells * 4 * H);
+    constexpr int XB = BF16 ? 2 : 4;  // bytes per input value
+    const __amdgpu_buffer_rsrc_t rX = rsrc(xc, (int64_t)D.Hc * D.Wc * C * XB);
     const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 16 * H);
     const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 2 * H, cells * 8 * H);
     const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4);
@@ -167,6 +188,16 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     }
     const int oxc = XR * CS * 4 + 4 * kc, oxh = XR * RS * 2 + 2 * kc, ozc = ZR * CS * 4 + 4 * kc;
     const int ja = (4 * (col & 3) + (col >> 2)) * CG + cg;  // diagonal position of this lane's A row
+    // canvas input of the A row's cell: byte offset XBASE + a XA + s XS + vx[ks] (channel 4 ks + q)
+    const int XA = (SY * D.Wc * C - SX * C) * XB, XS = SX * C * XB;
+    const int XBASE = (Y0 * D.Wc + X0) * C * XB;
+    int vx[KX];
+    bool cx[KX];
+#pragma unroll
+    for (int ks = 0; ks < KX; ++ks) {
+        vx[ks] = ja * XA + (4 * ks + q) * XB;
+        cx[ks] = 4 * ks + q < C;
+    }
     int oah[3];  // LDS byte offsets of the h rows at positions ja - 1, ja, ja + 1
 #pragma unroll
     for (int m = 0; m < 3; ++m) oah[m] = P(ja + m - 1) * RS * 2;
@@ -178,41 +209,38 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
         return s < S ? hi - lo + 1 : 0;
     };
 
-    // Z of diagonal s1 (first cell st1) into one register set; lanes without a cell load nothing
-    auto load_z = [&](int s1, int st1, f32x4 (&z4)[NR], float (&zg)[NR]) {
+    // input pixels of this lane's A-row cell on diagonal s1, one value per K step (0 where absent)
+    auto load_x = [&](int s1, float (&xv)[KX]) {
         const int L1 = diag_len(s1);
-        const int pe = st1 * H;
+        const int lo1 = s1 > w - 1 ? s1 - (w - 1) : 0;
+        const int px = XBASE + lo1 * XA + s1 * XS;
+        const bool va = ja < L1;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const bool ok = jo[r] < L1 && kok;
-            const int el = pe + ve[r];
-            z4[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rZ4, ok ? el * 16 : kOOB, 0, 0));
-            zg[r] = bld(rZ1, ok ? el * 4 : kOOB);
+        for (int ks = 0; ks < KX; ++ks) {
+            const int off = (va & cx[ks]) ? px + vx[ks] : kOOB;
+            if constexpr (BF16)
+                xv[ks] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rX, off, 0, 0) << 16);
+            else
+                xv[ks] = bld(rX, off);
         }
     };
 
-    f32x4 z4s[4][NR];
-    float zgs[4][NR];
-    int st = 0;   // stash index of the first cell of diagonal s
-    int stz = 0;  // ... of diagonal s + kZD
+    float xs[4][KX];
+    int st = 0;  // stash index of the first cell of diagonal s
 #pragma unroll
-    for (int i = 0; i < kZD; ++i) {
-        load_z(i, stz, z4s[i], zgs[i]);
-        stz += diag_len(i);
-    }
+    for (int i = 0; i < kZD; ++i) load_x(i, xs[i]);
     // wait for the first sets here, once: the loop then starts with nothing in flight, the same state
     // for every diagonal, and the compiler's per-step waits only cover the kZD-step-old prefetch
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
     // diagonal s at position POS = s mod 4 of the unrolled loop: buffer s & 1 is written and 1 - (s & 1)
-    // read; Z set POS is consumed and set (POS + kZD) mod 4 refilled for diagonal s + kZD
+    // read; input set POS is consumed and set (POS + kZD) mod 4 refilled for diagonal s + kZD
     auto step = [&](int s, auto POSc) {
         constexpr int POS = decltype(POSc)::value;
         constexpr int CB = POS & 1;
         const int L = diag_len(s);
-        load_z(s + kZD, stz, z4s[(POS + kZD) & 3], zgs[(POS + kZD) & 3]);
-        stz += diag_len(s + kZD);
+        load_x(s + kZD, xs[(POS + kZD) & 3]);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
         const bool dl = s >= w;
         const int lo = dl ? s - (w - 1) : 0;
@@ -240,9 +268,17 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             cl[r] = *reinterpret_cast<const float*>(csp + (jo[r] < Ml ? ol : ozc));
             cu[r] = *reinterpret_cast<const float*>(csp + ((jo[r] >= Tu && jo[r] < L) ? ou : ozc));
         }
-        f32x4 acc[5];
+        f32x4 acc[5], accx[5];
 #pragma unroll
-        for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int g = 0; g < 5; ++g) {
+            acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accx[g] = f32x4{bz[g], bz[g], bz[g], bz[g]};
+        }
+#pragma unroll
+        for (int ks = 0; ks < KX; ++ks)
+#pragma unroll
+            for (int g = 0; g < 5; ++g)
+                accx[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[POS][ks], Bx[g][ks], accx[g], 0, 0, 0);
 #pragma unroll
         for (int t = 0; t < KB; ++t)
 #pragma unroll
@@ -251,8 +287,6 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
                 acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[t], Bl[g][t], acc[g], 0, 0, 0);
                 acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al[t], Bh[g][t], acc[g], 0, 0, 0);
             }
-        const f32x4(&zc4)[NR] = z4s[POS];
-        const float(&zcg)[NR] = zgs[POS];
         const int ph = HB + lo * DA + s * DS;  // h offset of diagonal position 0, minus 4 kk
         const int pe = st * H;                 // stash element of diagonal position 0
         unsigned char* cw = smem + 2 * HBUF + CB * CBUF;
@@ -260,11 +294,11 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const bool ok = jo[r] < L && kok;
-            const float ig = sigm(__builtin_fmaf(acc[0][r], us[0], zc4[r][0]));
-            const float fl = sigm(__builtin_fmaf(acc[1][r], us[1], zc4[r][1]));
-            const float fu = sigm(__builtin_fmaf(acc[2][r], us[2], zc4[r][2]));
-            const float og = sigm(__builtin_fmaf(acc[3][r], us[3], zc4[r][3]));
-            const float gg = ftanh2(__builtin_fmaf(acc[4][r], us[4], zcg[r]));
+            const float ig = sigm(__builtin_fmaf(acc[0][r], us[0], accx[0][r]));
+            const float fl = sigm(__builtin_fmaf(acc[1][r], us[1], accx[1][r]));
+            const float fu = sigm(__builtin_fmaf(acc[2][r], us[2], accx[2][r]));
+            const float og = sigm(__builtin_fmaf(acc[3][r], us[3], accx[3][r]));
+            const float gg = ftanh2(__builtin_fmaf(acc[4][r], us[4], accx[4][r]));
             const float c = __builtin_fmaf(fl, cl[r], __builtin_fmaf(fu, cu[r], ig * gg));
             const float hv = og * ftanh2(c);
             *reinterpret_cast<float*>(cw + (ok ? owc[r] : oxc)) = c;
@@ -295,25 +329,30 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     if (s + 2 < S) step(s + 2, IC<2>{});
 }
 
-typedef void (*Fwd16Kernel)(Dev, const float*, const float*, const float*, float*, float*);
+typedef void (*Fwd16Kernel)(Dev, const void*, int, const float*, const float*, const float*, const float*, float*,
+                            float*);
 
-// instantiated hidden sizes (the workloads' 2, 4, 10, 16, 32 and 50), each with its cell-group count CG
-// and accumulator rows NR = 1..4; the widest diagonal must fit 16 CG cells
+// instantiated (hidden size, input K steps, bf16 input) combinations of the workloads, each with its
+// cell-group count CG (two waves per SIMD where the registers allow it) and accumulator rows NR = 1..4;
+// the widest diagonal must fit 16 CG cells
 struct F16Entry {
-    int H, CG, NB, HP;
+    int H, KX;
+    bool bf16;
+    int CG, NB, HP;
     Fwd16Kernel fwd[4];
 };
-#define MDL_F16(h, cg)                                                                           \
-    {h, cg, F16Shape<h>::NB, F16Shape<h>::HP,                                                    \
-     {k_fwd16<h, cg, 1>, k_fwd16<h, cg, 2>, k_fwd16<h, cg, 3>, k_fwd16<h, cg, 4>}}
-// two waves per SIMD (8 waves) where the registers allow it, else one
-const F16Entry kF16[] = {MDL_F16(2, 8),  MDL_F16(4, 8),  MDL_F16(10, 8),
-                         MDL_F16(16, 8), MDL_F16(32, 4), MDL_F16(50, 1)};
+#define MDL_F16(h, kx, bf, cg)                                                                                \
+    {h, kx, bf, cg, F16Shape<h>::NB, F16Shape<h>::HP,                                                         \
+     {k_fwd16<h, cg, 1, kx, bf>, k_fwd16<h, cg, 2, kx, bf>, k_fwd16<h, cg, 3, kx, bf>, k_fwd16<h, cg, 4, kx, bf>}}
+const F16Entry kF16[] = {MDL_F16(2, 1, false, 8),  MDL_F16(4, 1, false, 8),  MDL_F16(10, 2, false, 8),
+                         MDL_F16(16, 1, false, 8), MDL_F16(16, 1, true, 8),  MDL_F16(32, 1, false, 4),
+                         MDL_F16(32, 1, true, 4),  MDL_F16(50, 5, false, 1)};
 #undef MDL_F16
 
-const F16Entry* f16_entry(int H, int Lmax) {
+const F16Entry* f16_entry(int H, int C, int dtype, int Lmax) {
+    const int kx = (C + 3) / 4;
     for (const auto& m : kF16)
-        if (m.H == H) return (Lmax + m.CG - 1) / m.CG <= 16 ? &m : nullptr;
+        if (m.H == H && m.KX == kx && m.bf16 == (dtype != 0)) return (Lmax + m.CG - 1) / m.CG <= 16 ? &m : nullptr;
     return nullptr;
 }
 
@@ -324,21 +363,22 @@ size_t f16_lds(const F16Entry& m) {
 
 }  // namespace
 
-bool fwd16_supported(int H, int Lmax) { return f16_entry(H, Lmax) != nullptr; }
+bool fwd16_supported(int H, int C, int dtype, int Lmax) { return f16_entry(H, C, dtype, Lmax) != nullptr; }
 
-size_t fwd16_lds(int H, int Lmax) {
-    const F16Entry* m = f16_entry(H, Lmax);
+size_t fwd16_lds(int H, int C, int dtype, int Lmax) {
+    const F16Entry* m = f16_entry(H, C, dtype, Lmax);
     return m ? f16_lds(*m) : 0;
 }
 
-hipError_t launch_fwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
-                        float* h_dirs, hipStream_t st) {
-    const F16Entry* m = f16_entry(H, D.max_diag);
+hipError_t launch_fwd16(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
+                        const float* b, const float* Ul, const float* Uu, float* stash, float* h_dirs,
+                        hipStream_t st) {
+    const F16Entry* m = f16_entry(H, C, dtype, D.max_diag);
     if (!m) return hipErrorInvalidValue;
     const int cells = (D.max_diag + m->CG - 1) / m->CG;  // widest diagonal's cells per group, <= 16
     const int nr = (cells + 3) / 4;
-    hipLaunchKernelGGL(m->fwd[nr - 1], dim3(4 * D.n), dim3(64 * m->NB * m->CG), f16_lds(*m), st, D, Ul, Uu, Z,
-                       stash, h_dirs);
+    hipLaunchKernelGGL(m->fwd[nr - 1], dim3(4 * D.n), dim3(64 * m->NB * m->CG), f16_lds(*m), st, D, x_canvas, C, Wx,
+                       b, Ul, Uu, stash, h_dirs);
     return hipGetLastError();
 }
 

@@ -201,7 +201,11 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
                     const int rem = idx - d * TP * G;
                     const int c = rem / G, n = rem - c * G;
                     const int cs = t_cst[d][c];
-                    if (cs >= 0) off = ((d * (int)D.T + cell0 + cs) * G + n) * 4;
+                    if (cs >= 0) {
+                        const int g = n / H, k = n - g * H;  // gate, hidden unit
+                        const int el = (d * (int)D.T + cell0 + cs) * H + k;
+                        off = g < 4 ? el * 16 + g * 4 : (int)(z1_offset(D.T, H) * 4) + el * 4;
+                    }
                 }
                 vd[i] = bld(rA, off);
             }

@@ -77,6 +77,7 @@ MDL_HD inline int find_example(const int64_t* off, int n, int64_t g) {
 //   Z1[(d*T + t)*H + k]          pre-activation of the cell input g
 //   S4[((d*T + t)*H + k)*4 + g]  gate values i, f_l, f_u, o
 //   S2[((d*T + t)*H + k)*2 + m]  m = 0: g, m = 1: the memory state c
+//   dA4, dA1: the gate pre-activation gradients in the layout of Z4 / Z1
 // A lane owning (cell, k) reads or writes its four sigmoid gates with one
 // 16-byte access. Z1 follows Z4 in the workspace's projection region, S2
 // follows S4 in its stash region.
@@ -101,11 +102,18 @@ size_t fwd_chain_lds(int H, int Lmax);
 size_t bwd_chain_lds(int H, int Lmax);
 int chain_max_items();
 bool chain_uses_mfma(int H, int Lmax);
-// forward wavefront on the f16 matrix cores (split operands, fp32-class accuracy)
-bool fwd16_supported(int H, int Lmax);
-size_t fwd16_lds(int H, int Lmax);
-hipError_t launch_fwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
-                        float* h_dirs, hipStream_t st);
+// forward wavefront with the input projection fused, recurrent product on the f16 matrix cores
+// (split operands, fp32-class accuracy); supported for the instantiated (H, C, dtype) combinations
+bool fwd16_supported(int H, int C, int dtype, int Lmax);
+size_t fwd16_lds(int H, int C, int dtype, int Lmax);
+hipError_t launch_fwd16(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
+                        const float* b, const float* Ul, const float* Uu, float* stash, float* h_dirs,
+                        hipStream_t st);
+// reverse wavefront on the f16 matrix cores (split, power-of-two scaled operands)
+bool bwd16_supported(int H, int Lmax);
+size_t bwd16_lds(int H, int Lmax);
+hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
+                        const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z,
                             float* stash, float* h_dirs, hipStream_t st);
 hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st);
