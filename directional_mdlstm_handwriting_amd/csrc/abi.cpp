@@ -326,13 +326,14 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     if (!mdl::bwd16_supported(H, L.max_diag) && !mdl::chain_uses_mfma(H, L.max_diag) &&
         (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_backward: widest diagonal x H exceeds the wavefront kernel's items");
-    if (!mdl::wgrad_supported(C, H))
+    const bool wg2 = mdl::wgrad2_supported(C, H, x_dtype);
+    if (!wg2 && !mdl::wgrad_supported(C, H))
         return fail(MDL_EUNSUPPORTED, "mdl_backward: C and H exceed the weight-gradient kernel's register tile");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
     if (mdl::bwd_chain_lds(H, L.max_diag) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward: recurrent weights and diagonal state exceed LDS");
-    if (mdl::wgrad_lds_bytes(C, H) > lmax)
+    if ((wg2 ? mdl::wgrad2_lds_bytes(C, H, x_dtype) : mdl::wgrad_lds_bytes(C, H)) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward: weight-gradient tile exceeds LDS");
     // the kernels address these tensors with 32-bit byte offsets
     if (4 * L.computed_cells * 6 * H * 4 >= (int64_t(1) << 31) || 4LL * L.Hc * L.Wc * H * 4 >= (int64_t(1) << 31))

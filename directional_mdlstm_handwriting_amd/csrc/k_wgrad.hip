@@ -375,6 +375,14 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
                         const float* dA, const float* Wx, float* part, float* dWx, float* dUl, float* dUu, float* db,
                         float* dx_flat, float* dx_canvas, hipStream_t st) {
     const WgradShape s = wgrad_shape(C, H);
+    const int64_t tot = 4 * (int64_t)s.R * s.G;
+    if (wgrad2_supported(C, H, dtype)) {
+        hipError_t err = launch_wgrad2(D, x_canvas, dtype, C, H, h_dirs, dA, Wx, part, dx_flat, dx_canvas, st);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, part, D.nchunks, C,
+                           H, dWx, dUl, dUu, db);
+        return hipGetLastError();
+    }
     const size_t lds = sizeof(float) * wgrad_lds_floats(s);
     const dim3 grid((unsigned)D.nchunks), block(256);
 #define MDL_WG(B, CT, HT) hipLaunchKernelGGL((k_wgrad_mfma<B, CT, HT>), grid, block, lds, st, D, x_canvas, s, h_dirs, \
@@ -392,7 +400,6 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
 #undef MDL_WG
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t tot = 4 * (int64_t)s.R * s.G;
     hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, part, D.nchunks, C, H,
                        dWx, dUl, dUu, db);
     return hipGetLastError();

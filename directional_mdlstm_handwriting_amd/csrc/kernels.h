@@ -119,6 +119,12 @@ hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* U
 hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st);
 hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                             const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
+// software-pipelined weight-gradient kernel for the instantiated (C, H, dtype) shapes
+bool wgrad2_supported(int C, int H, int dtype);
+size_t wgrad2_lds_bytes(int C, int H, int dtype);
+hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
+                         const float* dA, const float* Wx, float* part, float* dx_flat, float* dx_canvas,
+                         hipStream_t st);
 bool wgrad_supported(int C, int H);
 size_t wgrad_lds_bytes(int C, int H);
 hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
