@@ -3,9 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload word] [--no-cpu-baseline]
 
 A step is one pass of the whole device path over one batch whose inputs are
-already in HBM: scatter the examples onto the packed canvas, input projection,
-forward wavefront, direction sum + un-packing, reverse wavefront, weight and
-input gradients. The metric counts real cell-direction updates only:
+already in HBM: scatter the examples onto the packed canvas, forward wavefront
+(with the input projection), direction sum + un-packing, reverse wavefront,
+weight and input gradients. The metric counts real cell-direction updates only:
 4 * sum(h*w) / step time (forward + backward). Prints one JSON line.
 
 Also reported: per-kernel-group times from HIP events recorded by the library
@@ -71,21 +71,22 @@ def kernel_model(info, rects, C, H, x_bytes, nchunks=None):
     rec = 10 * H * H * link_count(rects)
     f = 4  # bytes per float
     return {
-        # x (canvas) in, Z = x Wx + b for four directions out
-        "projection": (T * C * x_bytes + 4 * T * G * f, 4 * T * 2 * C * G),
-        # Z in; stash (i, f_l, f_u, o, g, c) and h out
-        "fwd_wavefront": (4 * T * (G + 6 * H + H) * f, rec),
+        # x (canvas pixels) in for each direction; gate stash (i, f_l, f_u, o, g, c) and h out; the input
+        # projection x Wx + b is computed in the same kernel
+        "fwd_wavefront": (4 * T * (C * x_bytes + 7 * H * f), rec + 4 * T * 2 * C * G),
         # four h planes in, y out
         "dirsum": (N * 5 * H * f, 3 * N * H),
-        # stash and dy in, dA (5H gate pre-activation gradients) out
-        "bwd_wavefront": (4 * T * (6 * H + G) * f + N * H * f, rec),
-        # dA and h in (each h once), x in, dx out; r^T dA and dA Wx^T on the matrix cores
-        "wgrad": (4 * T * (G + H) * f + T * C * x_bytes + N * C * f + 4 * R * G * f,
+        # gate stash and dy in (dy once per direction), dA (5H gate pre-activation gradients) out
+        "bwd_wavefront": (4 * T * (6 * H + G) * f + 4 * N * H * f, rec),
+        # dA and h in (each h once), x in, dx out, chunk partials out; r^T dA and dA Wx^T on the matrix cores
+        "wgrad": (4 * T * (G + H) * f + 4 * T * C * x_bytes + N * C * f + 4 * R * G * f,
                   4 * T * 2 * R * G + 4 * T * 2 * G * C),
         # flat x in, canvas x out
         "scatter": (N * C * x_bytes + P * C * x_bytes, 0),
         # h planes outside the examples zeroed
         "zero_fill": (4 * (P - T) * H * f, 0),
+        # shapes without the fused forward: x in, Z = x Wx + b for four directions out
+        "projection": (T * C * x_bytes + 4 * T * G * f, 4 * T * 2 * C * G),
     }
 
 

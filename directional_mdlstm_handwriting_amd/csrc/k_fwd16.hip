@@ -333,7 +333,7 @@ typedef void (*Fwd16Kernel)(Dev, const void*, int, const float*, const float*, c
                             float*);
 
 // instantiated (hidden size, input K steps, bf16 input) combinations of the workloads, each with its
-// cell-group count CG (two waves per SIMD where the registers allow it) and accumulator rows NR = 1..4;
+// cell-group count CG (measured per shape: extra waves repeat the matrix-core work) and accumulator rows NR;
 // the widest diagonal must fit 16 CG cells
 struct F16Entry {
     int H, KX;
@@ -345,7 +345,7 @@ struct F16Entry {
     {h, kx, bf, cg, F16Shape<h>::NB, F16Shape<h>::HP,                                                         \
      {k_fwd16<h, cg, 1, kx, bf>, k_fwd16<h, cg, 2, kx, bf>, k_fwd16<h, cg, 3, kx, bf>, k_fwd16<h, cg, 4, kx, bf>}}
 const F16Entry kF16[] = {MDL_F16(2, 1, false, 8),  MDL_F16(4, 1, false, 8),  MDL_F16(10, 2, false, 8),
-                         MDL_F16(16, 1, false, 8), MDL_F16(16, 1, true, 8),  MDL_F16(32, 1, false, 4),
+                         MDL_F16(16, 1, false, 4), MDL_F16(16, 1, true, 4),  MDL_F16(32, 1, false, 4),
                          MDL_F16(32, 1, true, 4),  MDL_F16(50, 5, false, 1)};
 #undef MDL_F16
 
