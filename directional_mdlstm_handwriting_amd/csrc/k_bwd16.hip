@@ -9,19 +9,29 @@
 //     dc_in  = dc(R) f_l(R) + dc(D) f_u(D)
 //     tc = tanh c;  dc = dc_in + dh o (1 - tc^2)
 //     da = [dc g i(1-i), dc c_l f_l(1-f_l), dc c_u f_u(1-f_u), dh tc o(1-o), dc i (1-g^2)]
-// The product runs on v_mfma_f32_16x16x32_f16 with both operands split into
-// f16 hi + lo pairs (three partial products summed in fp32). Gate gradients
-// have no bound, so each (cell, 16-wide block of hidden units) row of da is
-// scaled by the power of two that brings its largest magnitude into
-// [2^14, 2^15) before it is split; the exponent sits in LDS beside it and the
-// accumulator of that row and block is scaled back exactly. The K dimension
-// orders da by (hidden unit, gate) with the five gates padded to eight, so a
-// lane stores its split gate gradients with two 16-byte LDS writes.
 //
-// Work split, LDS row permutation, fixed accumulator row count, 4-step
-// unrolling and the three-diagonal prefetch (here of the forward's gate
-// stash, the predecessors' c and the upstream gradient) are those of the
-// forward kernel; see k_fwd16.hip.
+// Each diagonal is done in two phases separated by a barrier.
+//  1. Four matrix waves (one per SIMD) form the recurrent part of dh on
+//     v_mfma_f32_16x16x32_f16 and leave it in LDS. Both operands are split
+//     into f16 hi + lo pairs (three partial products summed in fp32). Gate
+//     gradients have no bound, so each (cell, 16-wide block of hidden units)
+//     row of da was scaled by the power of two that brings its largest
+//     magnitude into [2^14, 2^15) before it was split; its exponent sits in
+//     LDS beside it and the product is scaled back exactly. The K dimension
+//     orders da by (hidden unit, gate), the five gates padded to eight.
+//  2. All eight waves do the elementwise part, each thread owning fixed
+//     (diagonal position, hidden unit) elements: dc, da, the scale of its
+//     row (a maximum over the 16 lanes of a DPP row), the split into the LDS
+//     A rows of the next phase 1, and the store of da for the weight
+//     gradients. A single wave issues a VALU instruction only every few
+//     cycles, so spreading this part over all eight waves (two per SIMD)
+//     instead of the four matrix waves shortens the dependent chain.
+// Rows of the LDS A operand are permuted so the 16 lanes gathering one K
+// block read 16 consecutive rows on distinct banks. The forward's gate stash,
+// the predecessors' c and the upstream gradient of each element are
+// prefetched three diagonals ahead; the loop is unrolled by four so every
+// step is straight code and the compiler's vmcnt waits cover only the
+// prefetch they need (loads and stores retire in order on this hardware).
 #include "kernels.h"
 #include "devmath.h"
 
@@ -33,10 +43,14 @@ namespace {
 
 constexpr int kOOB = 0x40000000;  // byte offset past every per-unit range used here (1 GiB)
 constexpr int kPD = 3;            // diagonals of prefetch ahead
+constexpr int kThreads = 512;     // 8 waves: phase 2 on all of them
+constexpr int kMatWaves = 4;      // phase 1 on the first four
 
 template <int H>
 struct B16Shape {
     static constexpr int NB = (H + 15) / 16;  // blocks of 16 hidden units
+    static constexpr int HE = 16 * NB;        // hidden units padded to whole DPP rows
+    static constexpr int CG = kMatWaves / NB; // cell groups of the matrix waves
     static constexpr int KA = 128;            // K extent of one successor's da per block: 16 units x 8 slots
     static constexpr int KT = KA / 32;        // K blocks of 32 per (successor, block)
     static_assert(NB <= 2, "hidden size above 32");
@@ -61,33 +75,33 @@ __device__ inline uint32_t row16_max(uint32_t x) {
     return x;
 }
 
-template <int H, int CG, int NR>
-__global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, const float* __restrict__ Ul,
-                                                                     const float* __restrict__ Uu,
-                                                                     const float* __restrict__ stash,
-                                                                     const float* __restrict__ dy_flat,
-                                                                     const float* __restrict__ dh_dirs,
-                                                                     float* __restrict__ dA) {
+// NE: elements per thread in phase 2 (cells x padded units of the widest diagonal over 512 threads)
+template <int H, int NE>
+__global__ __launch_bounds__(kThreads) void k_bwd16(Dev D, const float* __restrict__ Ul, const float* __restrict__ Uu,
+                                                    const float* __restrict__ stash,
+                                                    const float* __restrict__ dy_flat,
+                                                    const float* __restrict__ dh_dirs, float* __restrict__ dA) {
     using Sh = B16Shape<H>;
-    constexpr int NB = Sh::NB, KA = Sh::KA, KT = Sh::KT;
+    constexpr int NB = Sh::NB, HE = Sh::HE, CG = Sh::CG, KA = Sh::KA, KT = Sh::KT;
     constexpr int G = 5 * H;
     const int u = D.units[blockIdx.x];
     const int e = u >> 2, d = u & 3;
     const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
     const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kb = wave / CG, cg = wave % CG;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const bool mat = wave < kMatWaves;
+    // phase 1 role of a matrix wave: output block kb, cell group cg; lane (q, col)
+    const int kb = (wave % kMatWaves) / CG, cg = (wave % kMatWaves) % CG;
     const int q = lane >> 4, col = lane & 15;
-    const int kk = kb * 16 + col;  // this lane's hidden unit (output column, and produced da's unit)
-    const bool kok = kk < H;
-    const int kc = kok ? kk : 0;
+    const int kk = kb * 16 + col;
 
-    // B operand for output block kb: [Ul^T; Uu^T] rows in the (unit, gate) K order. For successor m
+    // B operand of output block kb: [Ul^T; Uu^T] rows in the (unit, gate) K order. For successor sm
     // (0: right, uses Ul; 1: down, uses Uu), input block bi and K block t, the lane holds K rows
     // 32t + 8q + i = 8 (4t + q) + i of that block: unit k' = 16 bi + 4t + q, gate i (zero for i >= 5).
     // Scaled per output column by 2^E and split into f16 hi + lo.
     f16x8 Bh[2][NB][KT], Bl[2][NB][KT];
-    float ecol;  // the column's scale exponent, negated
+    int ec;  // the column's scale exponent, negated
     {
         float v[2][NB][KT][8];
         float m = 0.f;
@@ -101,7 +115,7 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
                     for (int i = 0; i < 8; ++i) {
                         const int kp = 16 * bi + 4 * t + q;
                         float x = 0.f;
-                        if (kok && kp < H && i < 5) {
+                        if (mat && kk < H && kp < H && i < 5) {
                             const float* U = sm ? Uu : Ul;
                             x = U[((int64_t)d * H + kk) * G + i * H + kp];
                         }
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         const int E = scale_exp(__float_as_uint(m));
-        ecol = (float)(-E);
+        ec = -E;
 #pragma unroll
         for (int sm = 0; sm < 2; ++sm)
 #pragma unroll
@@ -126,20 +140,21 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
                         Bl[sm][bi][t][i] = lo;
                     }
     }
-    const int ec = (int)ecol;
 
     // LDS, two buffers (later / current diagonal) of NRW rows: the split, scaled da as f16
-    // [hi | lo][block][unit][8] (row stride RA halves), the scale exponents [block] (ints), and
-    // dc*f_l, dc*f_u (row stride CS floats). Rows: P(position), zero row ZR, discard row XR.
-    constexpr int RA = 2 * NB * KA + 8, CS = H + 4;
+    // [hi | lo][block][unit][8] (row stride RA halves), the scale exponents [block] (ints), dc*f_l and
+    // dc*f_u (row stride CS floats); one buffer of the phase-1 result dh [NRW][HE]. Diagonal position j
+    // lives in row P(j) (below); ZR is a zero row, XR absorbs the writes of idle threads.
+    constexpr int RA = 2 * NB * KA + 8, CS = HE + 4;
     constexpr int NRW = 16 * CG + 2, ZR = 16 * CG, XR = 16 * CG + 1;
     constexpr int ABUF = NRW * RA * 2, EBUF = NRW * NB * 4, CBUF = NRW * CS * 4;
     constexpr int OFF_E = 2 * ABUF, OFF_CL = OFF_E + 2 * EBUF, OFF_CU = OFF_CL + 2 * CBUF;
-    constexpr int LDS_BYTES = OFF_CU + 2 * CBUF;
+    constexpr int OFF_DH = OFF_CU + 2 * CBUF;
+    constexpr int LDS_BYTES = OFF_DH + NRW * HE * 4;
     extern __shared__ __align__(16) unsigned char smem[];
     {
         uint32_t* z32 = reinterpret_cast<uint32_t*>(smem);
-        for (int i = threadIdx.x; i < LDS_BYTES / 4; i += blockDim.x) z32[i] = 0u;
+        for (int i = tid; i < LDS_BYTES / 4; i += kThreads) z32[i] = 0u;
     }
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
     const int64_t cells = (int64_t)h * w;
@@ -154,14 +169,34 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
                 : rsrc(dy_flat + D.flat_off[e] * H, (int64_t)rh * rw * H * 4);
     const int S = h + w - 1;
 
+    // Cell j of a diagonal belongs to cell group j % CG and is cell i = j / CG of that group's matrix wave,
+    // computed in MFMA row 4(i%4) + i/4; its LDS row P(j) = 16(j % CG) + 4(i%4) + i/4 makes the 16 lanes
+    // that gather one K block read 16 consecutive rows. Positions outside [0, 16 CG) map to the zero row.
     auto P = [&](int j) {
         if (j < 0 || j >= 16 * CG) return ZR;
         const int i = j / CG;
         return 16 * (j % CG) + 4 * (i & 3) + (i >> 2);
     };
 
+    // ---- phase 1 constants (matrix waves) ----
+    int jo[4], owd[4], oe[4][3];  // rows r: position, dh result offset, exponent rows at jo - 1, jo, jo + 1
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        jo[r] = (4 * r + q) * CG + cg;
+        owd[r] = OFF_DH + ((16 * cg + 4 * q + r) * HE + kk) * 4;  // P(jo[r])
+#pragma unroll
+        for (int m = 0; m < 3; ++m) oe[r][m] = P(jo[r] + m - 1) * NB * 4;
+    }
+    const int oze = ZR * NB * 4;
+    const int ja = (4 * (col & 3) + (col >> 2)) * CG + cg;  // diagonal position of this lane's A row
+    int oa[3];  // LDS byte offsets of the da rows at positions ja - 1, ja, ja + 1
+#pragma unroll
+    for (int m = 0; m < 3; ++m) oa[m] = P(ja + m - 1) * RA * 2;
+    const int oza = ZR * RA * 2;
+
+    // ---- phase 2 constants: element n of this thread is (position pj, unit pk) ----
     // Cell (a, b) sits at canvas (Y0 + SY a, X0 + SX b). The upstream gradient's byte offset is
-    // UB + a UA + s US + 4 kk (b = s - a): on the canvas plane for a per-direction gradient, else in
+    // UB + a UA + s US + 4 k (b = s - a): on the canvas plane for a per-direction gradient, else in
     // the example's flat real-pixel block, where the cell must also lie in the real region.
     const int SY = (d & 2) ? -1 : 1, SX = (d & 1) ? -1 : 1;
     const int Y0 = (d & 2) ? y0 + h - 1 : y0, X0 = (d & 1) ? x0 + w - 1 : x0;
@@ -173,33 +208,31 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
     // real region in unit coordinates: a in [ar0, ar1), b in [br0, br1)
     const int ar0 = (d & 2) ? h - (ry0 - y0) - rh : ry0 - y0, ar1 = ar0 + rh;
     const int br0 = (d & 1) ? w - (rx0 - x0) - rw : rx0 - x0, br1 = br0 + rw;
-
-    int jo[NR], vu[NR], ve[NR];  // per accumulator row r: diagonal position, upstream offset, stash element
-    int owa[NR], owe[NR], owc[NR];  // own LDS row (da, exponent, dc*f) byte offsets within a buffer
-    int oe[NR][3], occ[NR][3];      // LDS byte offsets at positions jo - 1, jo, jo + 1: exponent row, c row
+    int pj[NE], vu[NE], ve[NE];
+    bool pk_ok[NE];
+    int rdh[NE], wa[NE], we[NE], wc[NE];  // own LDS offsets (within a buffer)
+    int oc[NE][3];                         // c-row offsets at positions pj - 1, pj, pj + 1
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        jo[r] = (4 * r + q) * CG + cg;
-        vu[r] = jo[r] * UA + 4 * kk;
-        ve[r] = jo[r] * H + kk;
-        const int pw = 16 * cg + 4 * q + r;  // P(jo[r])
-        owa[r] = pw * RA * 2 + (kb * KA + 8 * col) * 2;
-        owe[r] = (pw * NB + kb) * 4;
-        owc[r] = pw * CS * 4 + 4 * kc;
+    for (int n = 0; n < NE; ++n) {
+        const int el = tid + kThreads * n;
+        pj[n] = el / HE;
+        const int pk = el - pj[n] * HE, pb = pk / 16, pc = pk - 16 * pb;
+        pk_ok[n] = pk < H;
+        const int pkc = pk < H ? pk : 0;
+        vu[n] = pj[n] * UA + 4 * pkc;
+        ve[n] = pj[n] * H + pkc;
+        const int pr = P(pj[n]);
+        rdh[n] = OFF_DH + (pr * HE + pk) * 4;
+        wa[n] = pr * RA * 2 + (pb * KA + 8 * pc) * 2;
+        we[n] = (pr * NB + pb) * 4;
+        wc[n] = pr * CS * 4 + 4 * pk;
 #pragma unroll
-        for (int m = 0; m < 3; ++m) {
-            const int pr = P(jo[r] + m - 1);
-            oe[r][m] = pr * NB * 4;
-            occ[r][m] = pr * CS * 4 + 4 * kc;
-        }
+        for (int m = 0; m < 3; ++m) oc[n][m] = P(pj[n] + m - 1) * CS * 4 + 4 * pk;
     }
-    const int oxa = XR * RA * 2 + (kb * KA + 8 * col) * 2, oxe = (XR * NB + kb) * 4, oxc = XR * CS * 4 + 4 * kc;
-    const int ozc = ZR * CS * 4 + 4 * kc, oze = ZR * NB * 4;
-    const int ja = (4 * (col & 3) + (col >> 2)) * CG + cg;  // diagonal position of this lane's A row
-    int oa[3];  // LDS byte offsets of the da rows at positions ja - 1, ja, ja + 1
-#pragma unroll
-    for (int m = 0; m < 3; ++m) oa[m] = P(ja + m - 1) * RA * 2;
-    const int oza = ZR * RA * 2;
+    // writes of elements without a cell go to the discard row, reads of absent successors to the zero row
+    const int pk0 = tid % HE, pb0 = pk0 / 16, pc0 = pk0 - 16 * pb0;
+    const int xa = XR * RA * 2 + (pb0 * KA + 8 * pc0) * 2, xe = (XR * NB + pb0) * 4, xc = XR * CS * 4 + 4 * pk0;
+    const int zc = ZR * CS * 4 + 4 * pk0;
 
     auto diag_len = [&](int s) {
         if (s < 0 || s >= S) return 0;
@@ -209,11 +242,11 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
     };
     auto diag_lo = [&](int s) { return s > w - 1 ? s - (w - 1) : 0; };
 
-    // forward values of one diagonal's cells: i, f_l, f_u, o | g, c | c_left | c_up | upstream dh
+    // forward values of this thread's elements on one diagonal: i, f_l, f_u, o | g, c | c_left | c_up | dy
     struct Fw {
-        f32x4 g4[NR];
-        f32x2 g2[NR];
-        float cl[NR], cu[NR], dy[NR];
+        f32x4 g4[NE];
+        f32x2 g2[NE];
+        float cl[NE], cu[NE], dy[NE];
     };
     // s1: diagonal, st1: stash index of its first cell
     auto load_f = [&](int s1, int st1, Fw& f) {
@@ -228,17 +261,17 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
         // real-region bounds as position ranges: a = lo1 + j in [ar0, ar1), b = s1 - lo1 - j in [br0, br1)
         const int jr0 = max(ar0 - lo1, s1 - lo1 - br1 + 1), jr1 = min(ar1 - lo1, s1 - lo1 - br0 + 1);
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const bool ok = (jo[r] < L1) & kok;
-            const int el = pe + ve[r];
-            f.g4[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, ok ? el * 16 : kOOB, 0, 0));
-            f.g2[r] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rS2, ok ? el * 8 : kOOB, 0, 0));
+        for (int n = 0; n < NE; ++n) {
             // predicates combined without short-circuit evaluation: plain selects, no branches
-            const bool vl = ok & (jo[r] < Ml), vu_ = ok & (jo[r] >= Tu);
-            const bool vy = ok & (per_dir | ((jo[r] >= jr0) & (jo[r] < jr1)));
-            f.cl[r] = bld(rS2, vl ? (pl + ve[r]) * 8 + 4 : kOOB);
-            f.cu[r] = bld(rS2, vu_ ? (pu + ve[r]) * 8 + 4 : kOOB);
-            f.dy[r] = bld(rU, vy ? pu0 + vu[r] : kOOB);
+            const bool ok = (pj[n] < L1) & pk_ok[n];
+            const int el = pe + ve[n];
+            f.g4[n] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, ok ? el * 16 : kOOB, 0, 0));
+            f.g2[n] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rS2, ok ? el * 8 : kOOB, 0, 0));
+            const bool vl = ok & (pj[n] < Ml), vu_ = ok & (pj[n] >= Tu);
+            const bool vy = ok & (per_dir | ((pj[n] >= jr0) & (pj[n] < jr1)));
+            f.cl[n] = bld(rS2, vl ? (pl + ve[n]) * 8 + 4 : kOOB);
+            f.cu[n] = bld(rS2, vu_ ? (pu + ve[n]) * 8 + 4 : kOOB);
+            f.dy[n] = bld(rU, vy ? pu0 + vu[n] : kOOB);
         }
     };
 
@@ -263,60 +296,74 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
         load_f(s - kPD, stz, fs[(POS + kPD) & 3]);
         stz -= diag_len(s - kPD - 1);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
-        const Fw& f = fs[POS];
         const int dn = s >= w - 1 ? 1 : 0;  // successors of position j: right j - dn, down j + 1 - dn
         const unsigned char* ap = smem + (1 - CB) * ABUF;
         const unsigned char* ep = smem + OFF_E + (1 - CB) * EBUF;
+        // ---- phase 1: recurrent part of dh, matrix waves only (no global memory inside) ----
+        if (mat) {
+            const int rr = ja >= dn ? (dn ? oa[0] : oa[1]) : oza;
+            const int rd = (ja + 1 - dn < L1) ? (dn ? oa[1] : oa[2]) : oza;
+            f32x4 acc[2][NB];
+#pragma unroll
+            for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+                for (int bi = 0; bi < NB; ++bi) acc[sm][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sm = 0; sm < 2; ++sm)
+#pragma unroll
+                for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+                    for (int t = 0; t < KT; ++t) {
+                        const unsigned char* p = ap + (sm ? rd : rr) + (bi * KA + 32 * t + 8 * q) * 2;
+                        const f16x8 ah = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p, 16));
+                        const f16x8 al = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p + NB * KA * 2, 16));
+                        acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[sm][bi][t], acc[sm][bi], 0, 0, 0);
+                        acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[sm][bi][t], acc[sm][bi], 0, 0, 0);
+                        acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[sm][bi][t], acc[sm][bi], 0, 0, 0);
+                    }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool hr = jo[r] >= dn, hd = jo[r] + 1 - dn < L1;  // successors present
+                // their exponent rows (positions jo - dn and jo + 1 - dn), or the zero row
+                const int oer = hr ? (dn ? oe[r][0] : oe[r][1]) : oze;
+                const int oed = hd ? (dn ? oe[r][1] : oe[r][2]) : oze;
+                float dh = 0.f;
+#pragma unroll
+                for (int bi = 0; bi < NB; ++bi) {
+                    const int er = *reinterpret_cast<const int*>(ep + oer + 4 * bi);
+                    const int ed = *reinterpret_cast<const int*>(ep + oed + 4 * bi);
+                    dh += ldexpf(acc[0][bi][r], ec - er) + ldexpf(acc[1][bi][r], ec - ed);
+                }
+                *reinterpret_cast<float*>(smem + owd[r]) = dh;
+            }
+        }
+        __syncthreads();
+        // ---- phase 2: elementwise, all threads ----
+        const Fw& f = fs[POS];
         const unsigned char* clp = smem + OFF_CL + (1 - CB) * CBUF;
         const unsigned char* cup = smem + OFF_CU + (1 - CB) * CBUF;
-        // A operand rows of this lane's cell: right and down successors (zero row when absent)
-        const int rr = ja >= dn ? (dn ? oa[0] : oa[1]) : oza;
-        const int rd = (ja + 1 - dn < L1) ? (dn ? oa[1] : oa[2]) : oza;
-        f32x4 acc[2][NB];
-#pragma unroll
-        for (int sm = 0; sm < 2; ++sm)
-#pragma unroll
-            for (int bi = 0; bi < NB; ++bi) acc[sm][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int sm = 0; sm < 2; ++sm)
-#pragma unroll
-            for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-                for (int t = 0; t < KT; ++t) {
-                    const unsigned char* p = ap + (sm ? rd : rr) + (bi * KA + 32 * t + 8 * q) * 2;
-                    const f16x8 ah = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p, 16));
-                    const f16x8 al = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p + NB * KA * 2, 16));
-                    acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[sm][bi][t], acc[sm][bi], 0, 0, 0);
-                    acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[sm][bi][t], acc[sm][bi], 0, 0, 0);
-                    acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[sm][bi][t], acc[sm][bi], 0, 0, 0);
-                }
-        const int pe = st * H;
         unsigned char* aw = smem + CB * ABUF;
         unsigned char* ew = smem + OFF_E + CB * EBUF;
         unsigned char* clw = smem + OFF_CL + CB * CBUF;
         unsigned char* cuw = smem + OFF_CU + CB * CBUF;
+        const int pe = st * H;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const bool ok = jo[r] < L && kok;
-            const bool hr = jo[r] >= dn, hd = jo[r] + 1 - dn < L1;  // successors present
-            const int mr = dn ? 0 : 1, md = dn ? 1 : 2;             // their position slots
-            float dh = f.dy[r];
-#pragma unroll
-            for (int bi = 0; bi < NB; ++bi) {
-                const int er = *reinterpret_cast<const int*>(ep + (hr ? oe[r][mr] : oze) + 4 * bi);
-                const int ed = *reinterpret_cast<const int*>(ep + (hd ? oe[r][md] : oze) + 4 * bi);
-                dh += ldexpf(acc[0][bi][r], ec - er) + ldexpf(acc[1][bi][r], ec - ed);
-            }
-            const float dcin = *reinterpret_cast<const float*>(clp + (hr ? occ[r][mr] : ozc)) +
-                               *reinterpret_cast<const float*>(cup + (hd ? occ[r][md] : ozc));
-            const float ig = f.g4[r][0], fl = f.g4[r][1], fu = f.g4[r][2], og = f.g4[r][3];
-            const float gg = f.g2[r][0], c = f.g2[r][1];
+        for (int n = 0; n < NE; ++n) {
+            const int j = pj[n];
+            const bool ok = (j < L) & pk_ok[n];
+            const bool hr = j >= dn, hd = j + 1 - dn < L1;
+            const int ocr = hr ? (dn ? oc[n][0] : oc[n][1]) : zc;  // right successor's c row, or zero row
+            const int ocd = hd ? (dn ? oc[n][1] : oc[n][2]) : zc;  // lower successor's
+            const float dh = *reinterpret_cast<const float*>(smem + rdh[n]) + f.dy[n];
+            const float dcin = *reinterpret_cast<const float*>(clp + ocr) + *reinterpret_cast<const float*>(cup + ocd);
+            const float ig = f.g4[n][0], fl = f.g4[n][1], fu = f.g4[n][2], og = f.g4[n][3];
+            const float gg = f.g2[n][0], c = f.g2[n][1];
             const float tc = ftanh2(c);
             const float dov = dh * tc;
             const float dc = __builtin_fmaf(dh * og, 1.f - tc * tc, dcin);
             const float d0 = dc * gg * ig * (1.f - ig);
-            const float d1 = dc * f.cl[r] * fl * (1.f - fl);
-            const float d2 = dc * f.cu[r] * fu * (1.f - fu);
+            const float d1 = dc * f.cl[n] * fl * (1.f - fl);
+            const float d2 = dc * f.cu[n] * fu * (1.f - fu);
             const float d3 = dov * og * (1.f - og);
             const float d4 = dc * ig * (1.f - gg * gg);
             // scale of this (cell, block): the largest |da| over the 16 units of the block
@@ -325,23 +372,21 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
                                   __float_as_uint(fabsf(d4))));
             mb = row16_max(ok ? mb : 0u);
             const int E = scale_exp(mb);
-            const float s0 = ldexpf(d0, E), s1 = ldexpf(d1, E), s2 = ldexpf(d2, E), s3 = ldexpf(d3, E),
-                        s4 = ldexpf(d4, E);
             _Float16 h0, l0, h1, l1, h2, l2, h3, l3, h4, l4;
-            split16(s0, h0, l0);
-            split16(s1, h1, l1);
-            split16(s2, h2, l2);
-            split16(s3, h3, l3);
-            split16(s4, h4, l4);
+            split16(ldexpf(d0, E), h0, l0);
+            split16(ldexpf(d1, E), h1, l1);
+            split16(ldexpf(d2, E), h2, l2);
+            split16(ldexpf(d3, E), h3, l3);
+            split16(ldexpf(d4, E), h4, l4);
             const f16x8 hv = {h0, h1, h2, h3, h4, (_Float16)0, (_Float16)0, (_Float16)0};
             const f16x8 lv = {l0, l1, l2, l3, l4, (_Float16)0, (_Float16)0, (_Float16)0};
-            unsigned char* pa = aw + (ok ? owa[r] : oxa);
+            unsigned char* pa = aw + (ok ? wa[n] : xa);
             *reinterpret_cast<f16x8*>(__builtin_assume_aligned(pa, 16)) = hv;
             *reinterpret_cast<f16x8*>(__builtin_assume_aligned(pa + NB * KA * 2, 16)) = lv;
-            *reinterpret_cast<int*>(ew + (ok ? owe[r] : oxe)) = E;
-            *reinterpret_cast<float*>(clw + (ok ? owc[r] : oxc)) = dc * fl;
-            *reinterpret_cast<float*>(cuw + (ok ? owc[r] : oxc)) = dc * fu;
-            const int el = pe + ve[r];
+            *reinterpret_cast<int*>(ew + (ok ? we[n] : xe)) = E;
+            *reinterpret_cast<float*>(clw + (ok ? wc[n] : xc)) = dc * fl;
+            *reinterpret_cast<float*>(cuw + (ok ? wc[n] : xc)) = dc * fu;
+            const int el = pe + ve[n];
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{d0, d1, d2, d3}), rA4,
                                                    ok ? el * 16 : kOOB, 0, 0);
             bst(d4, rA1, ok ? el * 4 : kOOB);
@@ -363,25 +408,26 @@ __global__ __launch_bounds__(64 * B16Shape<H>::NB * CG) void k_bwd16(Dev D, cons
 
 typedef void (*Bwd16Kernel)(Dev, const float*, const float*, const float*, const float*, const float*, float*);
 
+// hidden sizes of the workloads; NE = 1 or 2 elements per thread
 struct B16Entry {
-    int H, CG, NB;
-    Bwd16Kernel bwd[4];
+    int H, NB, CG;
+    Bwd16Kernel bwd[2];
 };
-#define MDL_B16(h, cg) \
-    {h, cg, B16Shape<h>::NB, {k_bwd16<h, cg, 1>, k_bwd16<h, cg, 2>, k_bwd16<h, cg, 3>, k_bwd16<h, cg, 4>}}
-const B16Entry kB16[] = {MDL_B16(2, 4), MDL_B16(4, 4), MDL_B16(10, 4), MDL_B16(16, 4), MDL_B16(32, 2)};
+#define MDL_B16(h) {h, B16Shape<h>::NB, B16Shape<h>::CG, {k_bwd16<h, 1>, k_bwd16<h, 2>}}
+const B16Entry kB16[] = {MDL_B16(2), MDL_B16(4), MDL_B16(10), MDL_B16(16), MDL_B16(32)};
 #undef MDL_B16
 
+// the widest diagonal must fit the matrix waves' tiles (16 CG cells) and two phase-2 elements per thread
 const B16Entry* b16_entry(int H, int Lmax) {
     for (const auto& m : kB16)
-        if (m.H == H) return (Lmax + m.CG - 1) / m.CG <= 16 ? &m : nullptr;
+        if (m.H == H) return (Lmax <= 16 * m.CG && Lmax * 16 * m.NB <= 2 * kThreads) ? &m : nullptr;
     return nullptr;
 }
 
 size_t b16_lds(const B16Entry& m) {
-    const size_t nrw = 16 * (size_t)m.CG + 2;
-    const size_t ra = 2 * (size_t)m.NB * 128 + 8, cs = (size_t)m.H + 4;
-    return 2 * nrw * ra * 2 + 2 * nrw * m.NB * 4 + 4 * nrw * cs * 4;
+    const size_t nrw = 16 * (size_t)m.CG + 2, he = 16 * (size_t)m.NB;
+    const size_t ra = 2 * (size_t)m.NB * 128 + 8, cs = he + 4;
+    return 2 * nrw * ra * 2 + 2 * nrw * m.NB * 4 + 4 * nrw * cs * 4 + nrw * he * 4;
 }
 
 }  // namespace
@@ -397,10 +443,10 @@ hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, c
                         const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st) {
     const B16Entry* m = b16_entry(H, D.max_diag);
     if (!m) return hipErrorInvalidValue;
-    const int cells = (D.max_diag + m->CG - 1) / m->CG;
-    const int nr = (cells + 3) / 4;
-    hipLaunchKernelGGL(m->bwd[nr - 1], dim3(4 * D.n), dim3(64 * m->NB * m->CG), b16_lds(*m), st, D, Ul, Uu, stash,
-                       dy_flat, dh_dirs, dA);
+    const int elems = D.max_diag * 16 * m->NB;  // phase-2 elements of the widest diagonal
+    const int ne = (elems + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(m->bwd[ne - 1], dim3(4 * D.n), dim3(kThreads), b16_lds(*m), st, D, Ul, Uu, stash, dy_flat,
+                       dh_dirs, dA);
     return hipGetLastError();
 }
 
