@@ -108,17 +108,23 @@ def roofline(kernel, avg_ms, model):
     return r
 
 
+# Every source file a kernel group is compiled from; a counter summary holds for the digest of all of them.
+_COMMON = ("devmath.h", "kernels.h")
 KERNEL_SOURCES = {
-    "projection": "k_proj.hip", "fwd_wavefront": "k_chain.hip", "bwd_wavefront": "k_chain.hip",
-    "wgrad": "k_wgrad.hip", "dirsum": "k_layout.hip", "scatter": "k_layout.hip", "zero_fill": "k_layout.hip",
+    "projection": ("k_proj.hip",), "fwd_wavefront": ("k_fwd16.hip", "k_chain.hip") + _COMMON,
+    "bwd_wavefront": ("k_bwd16.hip", "k_chain.hip") + _COMMON, "wgrad": ("k_wgrad2.hip", "k_wgrad.hip") + _COMMON,
+    "dirsum": ("k_layout.hip",), "scatter": ("k_layout.hip",), "zero_fill": ("k_layout.hip",),
+    "conv_fwd": ("k_conv.hip",), "conv_bwd_data": ("k_conv.hip",), "conv_wgrad": ("k_conv.hip",),
 }
 
 
 def source_digest(kernel):
     import hashlib
-    path = os.path.join(ROOT, "directional_mdlstm_handwriting_amd", "csrc", KERNEL_SOURCES[kernel])
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "directional_mdlstm_handwriting_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
