@@ -135,10 +135,14 @@ class Layout:
     def handle(self):
         return self._h
 
-    def __del__(self):
-        if getattr(self, "_h", None) is not None and self._h.value:
+    def free(self):
+        # _lib is None during interpreter shutdown, when the process releases everything anyway
+        if getattr(self, "_h", None) is not None and self._h.value and _lib is not None:
             _lib.mdl_layout_free(self._h)
-            self._h = None
+        self._h = None
+
+    def __del__(self):
+        self.free()
 
     n = property(lambda s: s.info["n"])
     Hc = property(lambda s: s.info["canvas_h"])
@@ -151,6 +155,16 @@ def mdl_pack(heights, widths, canvas_w_min: int, sep: int = 1, mode: int = MDL_P
     out = ctypes.c_void_p()
     _check(_lib.mdl_pack(h.ctypes.data, w.ctypes.data, len(h), canvas_w_min, sep, mode, ctypes.byref(out)))
     return Layout(out.value)
+
+
+def mdl_layout_free(layout: Layout):
+    layout.free()
+
+
+def mdl_layout_info(layout: Layout) -> dict:
+    info = np.zeros(len(INFO_KEYS), dtype=np.int64)
+    _check(_lib.mdl_layout_info(layout.handle, info.ctypes.data))
+    return {k: int(v) for k, v in zip(INFO_KEYS, info)}
 
 
 def mdl_layout_rects(layout: Layout):

@@ -245,6 +245,27 @@ int mdl_scatter(const mdl_layout* layout, const void* d_desc, const void* x_flat
     GUARD_END
 }
 
+// The kernels address device tensors through buffer descriptors with 32-bit byte ranges and offsets.
+// The wavefront kernels take one direction's h plane and the canvas input each as one range and send a
+// masked lane 2^30 bytes past its start; the gate stash is addressed one example at a time. The
+// weight-gradient kernel of the instantiated shapes takes one direction's h plane and gate gradients per
+// range; the general one takes all four h planes and the whole gate-gradient tensor each as one range.
+static int check_extent(const char* fn, const mdl::Layout& L, int C, int H, int x_dtype, bool backward,
+                        bool general_wgrad) {
+    const int64_t plane = (int64_t)L.Hc * L.Wc * H * 4;
+    const int64_t xbytes = (int64_t)L.Hc * L.Wc * C * (x_dtype == MDL_BF16 ? 2 : 4);
+    const int64_t dabytes = L.computed_cells * 5 * (int64_t)H * 4;  // one direction
+    const int64_t lim = (int64_t(1) << 31) - 16;
+    if (plane > (int64_t(1) << 30) || xbytes > (int64_t(1) << 30))
+        return fail(MDL_EUNSUPPORTED, std::string(fn) + ": one direction's h plane or the canvas input above 1 GiB");
+    if (backward && dabytes >= lim)
+        return fail(MDL_EUNSUPPORTED, std::string(fn) + ": one direction's gate gradients above 2 GiB");
+    if (backward && general_wgrad && (4 * plane >= lim || 4 * dabytes >= lim))
+        return fail(MDL_EUNSUPPORTED, std::string(fn) + ": the four h planes or the gate gradients above 2 GiB "
+                                                        "for this (C, H)");
+    return MDL_OK;
+}
+
 int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype, int32_t C,
                 int32_t H, const float* Wx, const float* Ul, const float* Uu, const float* b, float* h_dirs, void* ws,
                 size_t ws_bytes, void* stream) {
@@ -255,6 +276,7 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     const mdl::Layout& L = L_of(layout);
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nchunks, C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
+    if ((rc = check_extent("mdl_forward", L, C, H, x_dtype, false, false))) return rc;
     const bool fused = mdl::fwd16_supported(H, C, x_dtype, L.max_diag);
     if (!fused && (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_forward: widest diagonal x H exceeds the wavefront kernel's items");
@@ -262,9 +284,6 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     if ((rc = max_lds(lmax))) return rc;
     if ((fused ? mdl::fwd16_lds(H, C, x_dtype, L.max_diag) : mdl::fwd_chain_lds(H, L.max_diag)) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_forward: recurrent weights and diagonal state exceed LDS");
-    // the kernels address these tensors with 32-bit byte offsets
-    if (4 * L.computed_cells * 6 * H * 4 >= (int64_t(1) << 31) || 4LL * L.Hc * L.Wc * H * 4 >= (int64_t(1) << 31))
-        return fail(MDL_EUNSUPPORTED, "mdl_forward: per-layer tensors above 2 GiB");
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -327,6 +346,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
         (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_backward: widest diagonal x H exceeds the wavefront kernel's items");
     const bool wg2 = mdl::wgrad2_supported(C, H, x_dtype);
+    if ((rc = check_extent("mdl_backward", L, C, H, x_dtype, true, !wg2))) return rc;
     if (!wg2 && !mdl::wgrad_supported(C, H))
         return fail(MDL_EUNSUPPORTED, "mdl_backward: C and H exceed the weight-gradient kernel's register tile");
     size_t lmax = 0;
@@ -335,9 +355,6 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
         return fail(MDL_EUNSUPPORTED, "mdl_backward: recurrent weights and diagonal state exceed LDS");
     if ((wg2 ? mdl::wgrad2_lds_bytes(C, H, x_dtype) : mdl::wgrad_lds_bytes(C, H)) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward: weight-gradient tile exceeds LDS");
-    // the kernels address these tensors with 32-bit byte offsets
-    if (4 * L.computed_cells * 6 * H * 4 >= (int64_t(1) << 31) || 4LL * L.Hc * L.Wc * H * 4 >= (int64_t(1) << 31))
-        return fail(MDL_EUNSUPPORTED, "mdl_backward: per-layer tensors above 2 GiB");
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);

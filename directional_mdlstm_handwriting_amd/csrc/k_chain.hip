@@ -443,9 +443,9 @@ struct MfmaEntry {
     BwdKernel bwd;
     int KB;
 };
+// the f16 reverse wavefront covers the smaller hidden sizes over the same diagonal widths
 const MfmaEntry kMfma[] = {
-    {2, k_bwd_mfma<2>, 1},  {4, k_bwd_mfma<4>, 1},   {10, k_bwd_mfma<10>, 1},
-    {16, k_bwd_mfma<16>, 1}, {32, k_bwd_mfma<32>, 2}, {50, k_bwd_mfma<50>, 4},
+    {50, k_bwd_mfma<50>, 4},
 };
 
 // one M-tile of 16 cells per wave: 4/KB tiles cover the widest diagonal

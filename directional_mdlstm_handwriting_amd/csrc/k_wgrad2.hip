@@ -94,7 +94,7 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
     const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
     const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave descriptors
     const int d = wave / WPD, sub = wave % WPD;  // direction, share of its N tiles
     const int td = tid - d * NTH;                // thread index within the direction
     const int i16 = lane & 15, q = lane >> 4;
@@ -145,9 +145,10 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
         }
     };
 
-    const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs, 4 * plane * 4);
-    const __amdgpu_buffer_rsrc_t rA4 = rsrc(dA, (int64_t)D.T * 4 * 16 * H);
-    const __amdgpu_buffer_rsrc_t rA1 = rsrc(dA + z1_offset(D.T, H), (int64_t)D.T * 4 * 4 * H);
+    // this wave's direction: its h plane and its gate gradients, each one 32-bit range
+    const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs + d * plane, plane * 4);
+    const __amdgpu_buffer_rsrc_t rA4 = rsrc(dA + (int64_t)d * D.T * 4 * H, (int64_t)D.T * 16 * H);
+    const __amdgpu_buffer_rsrc_t rA1 = rsrc(dA + z1_offset(D.T, H) + (int64_t)d * D.T * H, (int64_t)D.T * 4 * H);
     const __amdgpu_buffer_rsrc_t rX = rsrc(xc, (int64_t)D.Hc * D.Wc * C * XB);
 
     // staged values of one tile for this thread's direction
@@ -169,7 +170,7 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
                 const int p = pix[c], fl = flg[c] >> (2 * d);
                 const int src = up ? ((fl & 2) ? p + ((d & 2) ? D.Wc : -D.Wc) : -1)
                                    : ((fl & 1) ? p + ((d & 1) ? 1 : -1) : -1);
-                if (p >= 0 && src >= 0) off = (int)((d * plane + (int64_t)src * H) * 4) + kv * VH * 4;
+                if (p >= 0 && src >= 0) off = (src * H + kv * VH) * 4;
             }
             vh[i] = vload<VH>(rH, off);
         }
@@ -179,7 +180,7 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
             int off = kOOBw;
             if (idx < TP * H) {
                 const int c = idx / H, k = idx - c * H;
-                if (cst[c] >= 0) off = ((d * (int)D.T + cell0 + cst[c]) * H + k) * 16;
+                if (cst[c] >= 0) off = ((cell0 + cst[c]) * H + k) * 16;
             }
             vd4[i] = vload<4>(rA4, off);
         }
@@ -189,7 +190,7 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
             int off = kOOBw;
             if (idx < TP * H / VH) {
                 const int c = idx / (H / VH), kv = idx - c * (H / VH);
-                if (cst[c] >= 0) off = ((d * (int)D.T + cell0 + cst[c]) * H + kv * VH) * 4;
+                if (cst[c] >= 0) off = ((cell0 + cst[c]) * H + kv * VH) * 4;
             }
             vd1[i] = vload<VH>(rA1, off);
         }

@@ -160,19 +160,22 @@ int mdl_scatter(const mdl_layout* layout, const void* d_desc, const void* x_flat
 
 /*
  * Forward of one 4-direction MDLSTM layer over the canvas.
- * Input projection x.Wx + b of every computed cell and direction as one GEMM
- * (§IV-B: the five input matrices computed together; RETURNN §4.2: the
- * non-recurrent part as one matrix product for the whole batch), then the
- * recurrence as an anti-diagonal wavefront (§I; RETURNN §4.2: all positions of
- * a diagonal at once, four directions at once), each example on its own local
- * diagonals:
+ * Input projection x.Wx + b of every computed cell and direction (§IV-B: the
+ * five input matrices computed together; RETURNN §4.2: the non-recurrent part
+ * as one matrix product), formed on the matrix cores inside the wavefront step
+ * for the hidden sizes and channel counts the library instantiates and as one
+ * GEMM before it otherwise, and the recurrence as an anti-diagonal wavefront
+ * (§I; RETURNN §4.2: all positions of a diagonal at once, four directions at
+ * once), each example on its own local diagonals:
  *   a = x.Wx[d] + b[d] + h_left.Ul[d] + h_up.Uu[d]
  *   i, f_l, f_u, o = sigmoid(.), g = tanh(.)
  *   c = f_l*c_left + f_u*c_up + i*g,  h = o*tanh(c)
  * with predecessors outside the example read as zero (§V mask).
  * x_canvas [Hc][Wc][C] (x_dtype), h_dirs out [4][Hc][Wc][H] float32 (zero
  * outside the computed region). ws: >= mdl_workspace_size bytes.
- * MDL_EUNSUPPORTED when H or the widest diagonal exceed the kernel's LDS budget.
+ * MDL_EUNSUPPORTED when H or the widest diagonal exceed the kernel's LDS budget,
+ * or when one direction's h plane (Hc*Wc*H floats) or the canvas input
+ * exceeds 1 GiB (buffer ranges are 32-bit).
  */
 int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
                 int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu,
@@ -199,6 +202,11 @@ int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float*
  *   dx_flat [h][w][C] float32 per example, dx_canvas [Hc][Wc][C] float32 (zero
  *   outside the real pixels); dWx, dUl, dUu, db shaped like Wx, Ul, Uu, b.
  * Weight gradients are fixed-order blocked sums over all computed cells.
+ * MDL_EUNSUPPORTED under the same size limits as mdl_forward, when one
+ * direction's gate gradients (T*5H floats, T = computed cells) reach 2 GiB,
+ * when C and H exceed the weight-gradient kernel's register tile, and, for
+ * (C, H) without a compiled weight-gradient shape, when all four h planes or
+ * all four directions' gate gradients together reach 2 GiB.
  */
 int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
                  int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu,

@@ -43,6 +43,9 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(M.EXPORTED) == names
+    # the binding offers a function of the same name for every entry point
+    for n in names:
+        assert callable(getattr(M, n, None)), n
 
 
 def _compare(h, w, cw, sep, mode="packed"):
@@ -58,6 +61,7 @@ def _compare(h, w, cw, sep, mode="packed"):
     assert np.array_equal(border, ref.border)
     N = int(np.sum(np.asarray(h, np.int64) * np.asarray(w, np.int64)))
     assert lay.info["real_pixels"] == N
+    assert M.mdl_layout_info(lay) == lay.info
     assert lay.info["computed_cells"] == int(np.sum(ref.rects[:, 2].astype(np.int64) * ref.rects[:, 3]))
     assert lay.info["max_depth"] == int(np.max(ref.rects[:, 2] + ref.rects[:, 3] - 1))
     assert lay.info["max_diag"] == int(np.max(np.minimum(ref.rects[:, 2], ref.rects[:, 3])))
@@ -134,6 +138,23 @@ def test_error_codes():
     assert lib.mdl_scatter(lay.handle, 1, 1, 1, 5, 1, None) == M.MDL_EINVAL
     ws = M.mdl_workspace_size(lay, 4, 16)
     assert lib.mdl_forward(lay.handle, 1, 1, 0, 4, 16, 1, 1, 1, 1, 1, 1, ws - 1, None) == M.MDL_ESIZE
+    # buffer ranges are 32-bit: one h plane of 3000 x 3000 x 32 floats (1.07 GiB) is refused before any launch
+    big = M.mdl_pack([3000], [3000], 8, 1)
+    wsb = M.mdl_workspace_size(big, 4, 32)
+    assert lib.mdl_forward(big.handle, 1, 1, 0, 4, 32, 1, 1, 1, 1, 1, 1, ctypes.c_size_t(wsb), None) \
+        == M.MDL_EUNSUPPORTED
+    assert "1 GiB" in M.mdl_last_error()
+    assert lib.mdl_backward(big.handle, 1, 1, 0, 4, 32, 1, 1, 1, 1, 1, None, None, None, 1, 1, 1, 1, 1,
+                            ctypes.c_size_t(wsb), None) == M.MDL_EUNSUPPORTED
+    # the line workload's layer (stash above 2 GiB, each descriptor range below it) passes the size checks
+    from workloads import make_workload
+    wl = make_workload("line", 0)
+    ll = M.mdl_pack(wl.heights, wl.widths, wl.canvas_w_min[0], wl.sep)
+    wsl = M.mdl_workspace_size(ll, 4, 32)
+    assert wsl > 2 ** 31
+    rc = lib.mdl_forward(ll.handle, 1, 1, 1, 4, 32, 1, 1, 1, 1, 1, 1, ctypes.c_size_t(wsl), None)
+    # with no GPU here the first device query fails (MDL_EHIP); with one the call would go on to launch
+    assert rc not in (M.MDL_EUNSUPPORTED, M.MDL_ESIZE, M.MDL_EINVAL), M.mdl_last_error()
 
 
 def test_workspace_grows_with_size():

@@ -169,6 +169,10 @@ RAGGED = [
     ([7, 3, 11, 5, 6, 2, 9], [13, 27, 4, 16, 6, 31, 2], 6, 10),
     ([5, 3, 4, 2], [9, 7, 3, 6], 20, 50),
     ([6, 9, 4], [12, 7, 15], 4, 2),
+    # shapes outside the matrix-core instantiations: a diagonal wider than their tiles (H = 16, 70 cells),
+    # and a hidden size with none (H = 8, C = 3); these run the general fp32 kernels
+    ([70, 12, 3], [80, 30, 5], 4, 16),
+    ([5, 9, 13, 1], [11, 6, 2, 7], 3, 8),
 ]
 
 
