@@ -335,30 +335,41 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
 
 namespace {
 
-// one thread per (direction, entry): chunk partials added in a fixed order, then
-// routed to dWx / db / dUl / dUu
-__global__ void k_wgrad_reduce(const float* __restrict__ part, int nchunks, int C, int H, float* __restrict__ dWx,
-                               float* __restrict__ dUl, float* __restrict__ dUu, float* __restrict__ db) {
+// Chunk partials summed in a fixed order, then routed to dWx / db / dUl / dUu. A workgroup takes 64
+// consecutive (direction, entry) slots (coalesced reads of each chunk's partial row) and 8 slices of the
+// chunks: slice j adds chunks j, j + 8, j + 16, ... in order, and the 8 slice sums are added in slice
+// order through LDS. The order depends only on the chunk count, so reruns are bit-identical.
+constexpr int RED_X = 64, RED_Y = 8;
+__global__ __launch_bounds__(RED_X* RED_Y) void k_wgrad_reduce(const float* __restrict__ part, int nchunks, int C,
+                                                               int H, float* __restrict__ dWx,
+                                                               float* __restrict__ dUl, float* __restrict__ dUu,
+                                                               float* __restrict__ db) {
     const int G = 5 * H, R = C + 1 + 2 * H, E = R * G;
-    const int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (id >= 4 * (int64_t)E) return;
-    const int d = (int)(id / E), ent = (int)(id % E);
-    const float* p = part + (int64_t)d * E + ent;
+    const int tx = threadIdx.x % RED_X, ty = threadIdx.x / RED_X;
+    const int64_t id = blockIdx.x * (int64_t)RED_X + tx;
+    const bool ok = id < 4 * (int64_t)E;
     const int64_t stride = 4 * (int64_t)E;
-    float s8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int c = 0;
-    for (; c + 8 <= nchunks; c += 8)
+    float s = 0.f;
+    if (ok) {
+        const float* p = part + id;
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+        int c = ty, j = 0;
+        for (; c < nchunks; c += RED_Y, j = (j + 1) & 3) s4[j] += p[(int64_t)c * stride];
+        s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    }
+    __shared__ float red[RED_Y][RED_X];
+    red[ty][tx] = s;
+    __syncthreads();
+    if (ty != 0 || !ok) return;
+    float t = red[0][tx];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) s8[j] += p[(int64_t)(c + j) * stride];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (c + j < nchunks) s8[j] += p[(int64_t)(c + j) * stride];
-    const float s = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
+    for (int y = 1; y < RED_Y; ++y) t += red[y][tx];
+    const int d = (int)(id / E), ent = (int)(id % E);
     const int r = ent / G, n = ent % G;
-    if (r < C) dWx[((int64_t)d * C + r) * G + n] = s;
-    else if (r == C) db[(int64_t)d * G + n] = s;
-    else if (r < C + 1 + H) dUl[((int64_t)d * H + (r - C - 1)) * G + n] = s;
-    else dUu[((int64_t)d * H + (r - C - 1 - H)) * G + n] = s;
+    if (r < C) dWx[((int64_t)d * C + r) * G + n] = t;
+    else if (r == C) db[(int64_t)d * G + n] = t;
+    else if (r < C + 1 + H) dUl[((int64_t)d * H + (r - C - 1)) * G + n] = t;
+    else dUu[((int64_t)d * H + (r - C - 1 - H)) * G + n] = t;
 }
 
 }  // namespace
@@ -379,8 +390,8 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
     if (wgrad2_supported(C, H, dtype)) {
         hipError_t err = launch_wgrad2(D, x_canvas, dtype, C, H, h_dirs, dA, Wx, part, dx_flat, dx_canvas, st);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, part, D.nchunks, C,
-                           H, dWx, dUl, dUu, db);
+        hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st,
+                           part, D.nchunks, C, H, dWx, dUl, dUu, db);
         return hipGetLastError();
     }
     const size_t lds = sizeof(float) * wgrad_lds_floats(s);
@@ -400,8 +411,8 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
 #undef MDL_WG
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st, part, D.nchunks, C, H,
-                       dWx, dUl, dUu, db);
+    hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st, part,
+                       D.nchunks, C, H, dWx, dUl, dUu, db);
     return hipGetLastError();
 }
 

@@ -10,13 +10,17 @@
 // tiles of TP cells. The global loads of tile t+1 (16-byte loads of the
 // predecessors' h and of the gate gradients in their [cell][k][4] layout)
 // are issued before tile t is computed from LDS, so their latency hides
-// behind the matrix-core work; the chunk's cell table (pixel, flat index,
-// stash index per direction, predecessor flags) is built one tile ahead.
+// behind the matrix-core work. Each thread stages a fixed share of one cell
+// of each tile and works out that cell's pixel, predecessors and stash
+// position itself, so the loads wait on no shared table.
 // r^T da runs on v_mfma_f32_16x16x4_f32 (fp32 products and sums, K = 4
 // cells per instruction); each wave owns all M tiles of its direction and a
-// share of its N tiles. dx runs on the same instruction (A = da, B = Wx^T in
-// registers), and the four directions' dx are added in a fixed order. LDS row
-// strides are chosen so the fragment reads of a wave hit distinct banks.
+// share of its N tiles. dx runs on v_mfma_f32_4x4x1f32, whose 16 independent
+// 4 x 4 blocks fit the few input channels without padding (the 16 x 16
+// instruction would waste three quarters of its columns at C = 4): every wave
+// takes a share of the gate-gradient columns of all four directions, the
+// directions are added across lanes, and the waves' shares in a fixed order.
+// LDS row strides are chosen so the fragment reads of a wave hit distinct banks.
 // Chunk partials are reduced in chunk order by k_wgrad_reduce (k_wgrad.hip).
 #include "kernels.h"
 #include "devmath.h"
@@ -26,25 +30,31 @@ namespace mdl {
 namespace {
 
 constexpr int kOOBw = 0x7ffffff0;  // byte offset past every buffer range: loads return 0
-constexpr int TP = 32;             // cells per tile (8 K steps)
 
 template <int C, int H>
 struct WgShape {
     static constexpr int G = 5 * H, R = C + 1 + 2 * H;
+    static constexpr int TP = H >= 32 ? 16 : 32;          // cells per tile: the staged loads of the next tile fit
     static constexpr int MT = (R + 15) / 16, NT = (G + 15) / 16;
-    static constexpr int WPD = (MT * NT + 15) / 16;       // waves per direction: at most 16 tiles per wave
+    static constexpr int WPD = (MT * NT + 31) / 32;       // waves per direction: at most 32 tiles per wave
     static constexpr int NTW = (NT + WPD - 1) / WPD;      // N tiles per wave (bound)
     static constexpr int RP = MT % 2 ? 16 * MT : 16 * MT + 16;  // r row stride: 16 (mod 32) floats
     static constexpr int DS = G + 1 + ((4 - G % 4) % 4);  // da row stride: 1 (mod 4), > G (column G stays 0)
     static constexpr int VH = H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1);    // h / dA1 load width
     static constexpr int NTH = 64 * WPD;                  // threads per direction
-    static constexpr int NHL = (TP * 2 * H / VH + NTH - 1) / NTH;   // h loads per thread
-    static constexpr int ND4 = (TP * H + NTH - 1) / NTH;            // dA4 loads per thread (16 bytes)
-    static constexpr int ND1 = (TP * H / VH + NTH - 1) / NTH;       // dA1 loads per thread
-    static constexpr int NXL = (TP * C + NTH - 1) / NTH;            // x loads per thread
-    static constexpr int KX = (G + 3) / 4;                // K steps of the dx product
+    static constexpr int TPC = NTH / TP;                  // threads per cell of a tile in the loads
+    static constexpr int NVH = 2 * H / VH, NV1 = H / VH;  // h and dA1 vectors of a cell
+    static constexpr int NHL = (NVH + TPC - 1) / TPC;     // h loads per thread
+    static constexpr int ND4 = (H + TPC - 1) / TPC;       // dA4 loads per thread (16 bytes)
+    static constexpr int ND1 = (NV1 + TPC - 1) / TPC;     // dA1 loads per thread
+    static constexpr int NXL = (C + TPC - 1) / TPC;       // x loads per thread
+    static constexpr int NWV = 4 * WPD;                   // waves of the workgroup
+    static constexpr int NPW = (G + NWV - 1) / NWV;       // da columns of the dx product per wave
+    static constexpr int NC4 = (C + 3) / 4;               // groups of 4 input channels
     static_assert(C <= 16, "dx product assumes at most 16 input channels");
     static_assert(DS % 4 == 1 && DS > G, "da row stride");
+    static_assert(NWV * NPW <= DS, "dx column shares stay inside a da row");
+    static_assert(NTH % TP == 0 && (TPC & (TPC - 1)) == 0, "whole power-of-two thread groups per cell");
 };
 
 template <int N>
@@ -85,8 +95,9 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
                                                                       float* __restrict__ dx_flat,
                                                                       float* __restrict__ dx_canvas) {
     using S = WgShape<C, H>;
-    constexpr int G = S::G, R = S::R, MT = S::MT, NT = S::NT, WPD = S::WPD, NTW = S::NTW;
-    constexpr int RP = S::RP, DS = S::DS, VH = S::VH, NTH = S::NTH, KX = S::KX;
+    constexpr int G = S::G, R = S::R, MT = S::MT, NT = S::NT, WPD = S::WPD, NTW = S::NTW, TP = S::TP;
+    constexpr int RP = S::RP, DS = S::DS, VH = S::VH, NTH = S::NTH, NWV = S::NWV, NPW = S::NPW, NC4 = S::NC4;
+    constexpr int TPC = S::TPC, NVH = S::NVH, NV1 = S::NV1, NHL = S::NHL, ND4 = S::ND4, ND1 = S::ND1, NXL = S::NXL;
     constexpr int XB = BF16 ? 2 : 4;
     typedef typename VecOf<VH>::T HV;
     const int ch = blockIdx.x;
@@ -102,48 +113,25 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
     const int ncell = (r1 - r0) * w;
     const int ntiles = (ncell + TP - 1) / TP;
     const int cell0 = (int)D.cell_off[e];
+    const int flat0 = (int)D.flat_off[e];  // read once: a global load inside the loop would wait on the stores
     const int64_t plane = (int64_t)D.Hc * D.Wc * H;
 
     // LDS: r rows [4][TP][RP], gate gradients [4][TP][DS] (units k: gates 0..3 at 4k + g, gate 4 at 4H + k),
-    // per-direction dx [4][TP][C], cell tables [3][TP] of pix, flat, flags and the four stash positions
+    // dx shares of the waves [NWV][TP][C], and two slots of the tile's cell table (pixel, flat index) for
+    // the dx store
     extern __shared__ __align__(16) unsigned char smem[];
     float* rs = reinterpret_cast<float*>(smem);
     float* das = rs + 4 * TP * RP;
     float* dxs = das + 4 * TP * DS;
-    int* tpix = reinterpret_cast<int*>(dxs + 4 * TP * C);
-    int* tflat = tpix + 3 * TP;
-    int* tflag = tflat + 3 * TP;
-    int* tcst = tflag + 3 * TP;  // [3][4][TP]
-    constexpr int NWORDS = 4 * TP * RP + 4 * TP * DS + 4 * TP * C + 3 * TP * 7;
+    int* tpix = reinterpret_cast<int*>(dxs + NWV * TP * C);  // [2][TP]
+    int* tflat = tpix + 2 * TP;                              // [2][TP]
+    constexpr int NWORDS = 4 * TP * RP + 4 * TP * DS + NWV * TP * C + 4 * TP;
     for (int i = tid; i < NWORDS; i += blockDim.x) reinterpret_cast<uint32_t*>(smem)[i] = 0u;
     __syncthreads();
     for (int i = tid; i < 4 * TP; i += blockDim.x) rs[i * RP + C] = 1.f;  // the bias row of r
 
-    auto build_table = [&](int t, int slot) {
-        if (tid < TP) {
-            const int qc = t * TP + tid;
-            int pix = -1, flat = -1, flags = 0;
-            int cst[4] = {-1, -1, -1, -1};
-            if (qc < ncell) {
-                const int ly = r0 + qc / w, lx = qc - (qc / w) * w;
-                pix = (y0 + ly) * D.Wc + x0 + lx;
-#pragma unroll
-                for (int dd = 0; dd < 4; ++dd) {
-                    cst[dd] = stash_pos(h, w, ly, lx, dd);
-                    const bool lok = (dd & 1) ? lx < w - 1 : lx > 0;  // left predecessor (y, x - sx)
-                    const bool uok = (dd & 2) ? ly < h - 1 : ly > 0;  // upper predecessor (y - sy, x)
-                    flags |= (lok ? 1 : 0) << (2 * dd) | (uok ? 2 : 0) << (2 * dd);
-                }
-                const int qy = y0 + ly - ry0, qx = x0 + lx - rx0;
-                if (qy < rh && qx < rw) flat = (int)(D.flat_off[e] + qy * rw + qx);
-            }
-            tpix[slot * TP + tid] = pix;
-            tflat[slot * TP + tid] = flat;
-            tflag[slot * TP + tid] = flags;
-#pragma unroll
-            for (int dd = 0; dd < 4; ++dd) tcst[(slot * 4 + dd) * TP + tid] = cst[dd];
-        }
-    };
+    // loads: thread td of a direction stages cell lc = td / TPC of each tile, vectors pt, pt + TPC, ...
+    const int lc = td / TPC, pt = td % TPC;
 
     // this wave's direction: its h plane and its gate gradients, each one 32-bit range
     const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs + d * plane, plane * 4);
@@ -152,98 +140,83 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
     const __amdgpu_buffer_rsrc_t rX = rsrc(xc, (int64_t)D.Hc * D.Wc * C * XB);
 
     // staged values of one tile for this thread's direction
-    HV vh[S::NHL];
-    f32x4 vd4[S::ND4];
-    HV vd1[S::ND1];
-    float vx[S::NXL];
-    auto issue_loads = [&](int slot) {
-        const int* pix = tpix + slot * TP;
-        const int* flg = tflag + slot * TP;
-        const int* cst = tcst + (slot * 4 + d) * TP;
-#pragma unroll
-        for (int i = 0; i < S::NHL; ++i) {
-            const int idx = td + i * NTH;  // (cell, part, vector) of [TP][2][H / VH]
-            int off = kOOBw;
-            if (idx < TP * 2 * H / VH) {
-                const int c = idx / (2 * H / VH), rem = idx - c * (2 * H / VH);
-                const int up = rem / (H / VH), kv = rem - up * (H / VH);
-                const int p = pix[c], fl = flg[c] >> (2 * d);
-                const int src = up ? ((fl & 2) ? p + ((d & 2) ? D.Wc : -D.Wc) : -1)
-                                   : ((fl & 1) ? p + ((d & 1) ? 1 : -1) : -1);
-                if (p >= 0 && src >= 0) off = (src * H + kv * VH) * 4;
-            }
-            vh[i] = vload<VH>(rH, off);
+    HV vh[NHL];
+    f32x4 vd4[ND4];
+    HV vd1[ND1];
+    float vx[NXL];
+    auto issue_loads = [&](int t, int slot) {
+        // this thread's cell: canvas pixel, predecessors in direction d, position in d's stash order
+        const int qc = t * TP + lc;
+        const bool ok = qc < ncell;
+        const int ly = r0 + qc / w, lx = qc - (qc / w) * w;
+        const int pix = ok ? (y0 + ly) * D.Wc + x0 + lx : -1;
+        const bool lok = ok & ((d & 1) ? lx < w - 1 : lx > 0);  // left predecessor (y, x - sx)
+        const bool uok = ok & ((d & 2) ? ly < h - 1 : ly > 0);  // upper predecessor (y - sy, x)
+        const int srcl = pix + ((d & 1) ? 1 : -1), srcu = pix + ((d & 2) ? D.Wc : -D.Wc);
+        const int cst = ok ? stash_pos(h, w, ly, lx, d) : 0;
+        if (d == 0 && pt == 0) {  // the dx store's table
+            const int qy = y0 + ly - ry0, qx = x0 + lx - rx0;
+            tpix[slot * TP + lc] = pix;
+            tflat[slot * TP + lc] = (ok & (qy < rh) & (qx < rw)) ? flat0 + qy * rw + qx : -1;
         }
 #pragma unroll
-        for (int i = 0; i < S::ND4; ++i) {
-            const int idx = td + i * NTH;  // (cell, unit)
-            int off = kOOBw;
-            if (idx < TP * H) {
-                const int c = idx / H, k = idx - c * H;
-                if (cst[c] >= 0) off = ((cell0 + cst[c]) * H + k) * 16;
-            }
-            vd4[i] = vload<4>(rA4, off);
+        for (int i = 0; i < NHL; ++i) {
+            const int v = pt + i * TPC;  // vector of [2][H / VH]: left then upper predecessor
+            const bool up = v >= NV1;
+            const int kv = up ? v - NV1 : v;
+            const bool pok = (v < NVH) & (up ? uok : lok);
+            vh[i] = vload<VH>(rH, pok ? ((up ? srcu : srcl) * H + kv * VH) * 4 : kOOBw);
         }
 #pragma unroll
-        for (int i = 0; i < S::ND1; ++i) {
-            const int idx = td + i * NTH;  // (cell, vector of units)
-            int off = kOOBw;
-            if (idx < TP * H / VH) {
-                const int c = idx / (H / VH), kv = idx - c * (H / VH);
-                if (cst[c] >= 0) off = ((cell0 + cst[c]) * H + kv * VH) * 4;
-            }
-            vd1[i] = vload<VH>(rA1, off);
+        for (int i = 0; i < ND4; ++i) {
+            const int k = pt + i * TPC;
+            vd4[i] = vload<4>(rA4, ((k < H) & ok) ? ((cell0 + cst) * H + k) * 16 : kOOBw);
         }
 #pragma unroll
-        for (int i = 0; i < S::NXL; ++i) {
-            const int idx = td + i * NTH;  // (cell, channel)
-            int off = kOOBw;
-            if (idx < TP * C) {
-                const int c = idx / C, k = idx - c * C;
-                if (pix[c] >= 0) off = (pix[c] * C + k) * XB;
-            }
+        for (int i = 0; i < ND1; ++i) {
+            const int kv = pt + i * TPC;
+            vd1[i] = vload<VH>(rA1, ((kv < NV1) & ok) ? ((cell0 + cst) * H + kv * VH) * 4 : kOOBw);
+        }
+#pragma unroll
+        for (int i = 0; i < NXL; ++i) {
+            const int k = pt + i * TPC;
+            const int off = ((k < C) & ok) ? (pix * C + k) * XB : kOOBw;
             if constexpr (BF16) vx[i] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rX, off, 0, 0) << 16);
             else vx[i] = bld(rX, off);
         }
     };
     auto write_lds = [&]() {
-        float* rsd = rs + d * TP * RP;
-        float* dad = das + d * TP * DS;
+        float* rsd = rs + (d * TP + lc) * RP;
+        float* dad = das + (d * TP + lc) * DS;
 #pragma unroll
-        for (int i = 0; i < S::NHL; ++i) {
-            const int idx = td + i * NTH;
-            if (idx < TP * 2 * H / VH) {
-                const int c = idx / (2 * H / VH), rem = idx - c * (2 * H / VH);
-                const int up = rem / (H / VH), kv = rem - up * (H / VH);
+        for (int i = 0; i < NHL; ++i) {
+            const int v = pt + i * TPC;
+            if (v < NVH) {
+                const int up = v >= NV1 ? 1 : 0, kv = v - up * NV1;
 #pragma unroll
-                for (int j = 0; j < VH; ++j) rsd[c * RP + C + 1 + up * H + kv * VH + j] = vget<VH>(vh[i], j);
+                for (int j = 0; j < VH; ++j) rsd[C + 1 + up * H + kv * VH + j] = vget<VH>(vh[i], j);
             }
         }
 #pragma unroll
-        for (int i = 0; i < S::ND4; ++i) {
-            const int idx = td + i * NTH;
-            if (idx < TP * H) {
-                const int c = idx / H, k = idx - c * H;
+        for (int i = 0; i < ND4; ++i) {
+            const int k = pt + i * TPC;
+            if (k < H) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) dad[c * DS + 4 * k + g] = vd4[i][g];
+                for (int g = 0; g < 4; ++g) dad[4 * k + g] = vd4[i][g];
             }
         }
 #pragma unroll
-        for (int i = 0; i < S::ND1; ++i) {
-            const int idx = td + i * NTH;
-            if (idx < TP * H / VH) {
-                const int c = idx / (H / VH), kv = idx - c * (H / VH);
+        for (int i = 0; i < ND1; ++i) {
+            const int kv = pt + i * TPC;
+            if (kv < NV1) {
 #pragma unroll
-                for (int j = 0; j < VH; ++j) dad[c * DS + 4 * H + kv * VH + j] = vget<VH>(vd1[i], j);
+                for (int j = 0; j < VH; ++j) dad[4 * H + kv * VH + j] = vget<VH>(vd1[i], j);
             }
         }
 #pragma unroll
-        for (int i = 0; i < S::NXL; ++i) {
-            const int idx = td + i * NTH;
-            if (idx < TP * C) {
-                const int c = idx / C, k = idx - c * C;
-                rsd[c * RP + k] = vx[i];
-            }
+        for (int i = 0; i < NXL; ++i) {
+            const int k = pt + i * TPC;
+            if (k < C) rsd[k] = vx[i];
         }
     };
 
@@ -255,18 +228,23 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
         const int g = n / H, k = n - g * H;
         bo[j] = (nt0 + j < NT && n < G) ? (g < 4 ? 4 * k + g : 4 * H + k) : G;  // column G of a row is zero
     }
-    // dx: B = Wx[d]^T, rows n = 4 ks + q, column c = i16; kept in registers when one wave serves the
-    // direction, read from the (cached) weights otherwise
-    constexpr bool BREG = WPD == 1;
-    float bwx[BREG ? KX : 1];
-    auto wx_b = [&](int ks) {
-        const int n = 4 * ks + q;
-        return (i16 < C && n < G) ? Wx[((int64_t)d * C + i16) * G + n] : 0.f;
-    };
-    if constexpr (BREG) {
+    // dx = sum over d of da_d Wx_d^T on v_mfma_f32_4x4x1f32 (16 blocks of 4 x 4 x 1): block b = lane / 4
+    // holds cell group b % 4 (4 cells) of direction b / 4 against 4 input channels, so every lane does
+    // useful work with C <= 4 and the direction sum is two cross-lane additions. Each wave takes NPW
+    // consecutive columns of the da rows (same for all four directions); its Wx_d values, permuted to that
+    // column order (column 4k + g holds gate g < 4 of unit k, column 4H + k gate 4), stay in registers.
+    const int xd = lane >> 4, xi = lane & 3, xcell = lane & 15;  // block direction; row / channel in block; cell
+    const int col0 = wave * NPW;
+    float wxr[NC4][NPW];
 #pragma unroll
-        for (int ks = 0; ks < KX; ++ks) bwx[ks] = wx_b(ks);
-    }
+    for (int g4 = 0; g4 < NC4; ++g4)
+#pragma unroll
+        for (int sc = 0; sc < NPW; ++sc) {
+            const int col = col0 + sc, ch = 4 * g4 + xi;
+            const int n = col < 4 * H ? (col & 3) * H + (col >> 2) : col;
+            wxr[g4][sc] = (col < G && ch < C) ? Wx[((int64_t)xd * C + ch) * G + n] : 0.f;
+        }
+    const bool want_dx = dx_flat != nullptr || dx_canvas != nullptr;
 
     f32x4 acc[MT][NTW];
 #pragma unroll
@@ -274,15 +252,12 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    build_table(0, 0);
-    __syncthreads();
-    issue_loads(0);
+    issue_loads(0, 0);
     for (int t = 0; t < ntiles; ++t) {
-        const int slot = t % 3;
+        const int slot = t & 1;
         write_lds();
-        if (t + 1 < ntiles) build_table(t + 1, (t + 1) % 3);
         __syncthreads();
-        if (t + 1 < ntiles) issue_loads((t + 1) % 3);
+        if (t + 1 < ntiles) issue_loads(t + 1, (t + 1) & 1);
         const float* rsd = rs + d * TP * RP;
         const float* dad = das + d * TP * DS;
 #pragma unroll
@@ -299,20 +274,34 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
                 for (int j = 0; j < NTW; ++j)
                     if (nt0 + j < NT) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[m], bf[j], acc[m][j], 0, 0, 0);
         }
-        // dx of this direction for the tile's cells: 16-cell M tiles shared out over the direction's waves
-        for (int m2 = sub; m2 < TP / 16; m2 += WPD) {
-            const float* arow = dad + (16 * m2 + i16) * DS;
-            f32x4 dacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        // this wave's share of dx for the tile's cells, 16 cells at a time
+        if (want_dx) {
 #pragma unroll
-            for (int ks = 0; ks < KX; ++ks) {
-                const int n = 4 * ks + q;
-                const int g = n / H, k = n - g * H;
-                const float av = n < G ? arow[g < 4 ? 4 * k + g : 4 * H + k] : 0.f;
-                dacc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, BREG ? bwx[BREG ? ks : 0] : wx_b(ks), dacc, 0, 0, 0);
+            for (int m2 = 0; m2 < TP / 16; ++m2) {
+                const float* arow = das + (xd * TP + 16 * m2 + xcell) * DS + col0;
+                f32x4 dacc[NC4];
+#pragma unroll
+                for (int g4 = 0; g4 < NC4; ++g4) dacc[g4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sc = 0; sc < NPW; ++sc) {
+                    const float av = arow[sc];  // columns G .. DS-1 of a row are zero
+#pragma unroll
+                    for (int g4 = 0; g4 < NC4; ++g4)
+                        dacc[g4] = __builtin_amdgcn_mfma_f32_4x4x1f32(av, wxr[g4][sc], dacc[g4], 0, 0, 0);
+                }
+#pragma unroll
+                for (int g4 = 0; g4 < NC4; ++g4)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        // lanes l, l^16, l^32, l^48 hold the four directions of one (cell, channel);
+                        // every lane ends with the same sum (fp addition commutes)
+                        float v = dacc[g4][r];
+                        v += __shfl_xor(v, 16);
+                        v += __shfl_xor(v, 32);
+                        const int ch = 4 * g4 + xi;
+                        if (lane < 16 && ch < C) dxs[(wave * TP + 16 * m2 + 4 * (xcell >> 2) + r) * C + ch] = v;
+                    }
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (i16 < C) dxs[(d * TP + 16 * m2 + 4 * q + r) * C + i16] = dacc[r];
         }
         __syncthreads();
         {
@@ -321,8 +310,9 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
             for (int o = tid; o < TP * C; o += blockDim.x) {
                 const int c = o / C, chn = o - c * C;
                 if (pix[c] < 0) continue;
-                const float v = ((dxs[(0 * TP + c) * C + chn] + dxs[(1 * TP + c) * C + chn]) +
-                                 dxs[(2 * TP + c) * C + chn]) + dxs[(3 * TP + c) * C + chn];
+                float v = dxs[c * C + chn];
+#pragma unroll
+                for (int wv = 1; wv < NWV; ++wv) v += dxs[(wv * TP + c) * C + chn];  // waves in order
                 if (dx_flat && flat[c] >= 0) dx_flat[(int64_t)flat[c] * C + chn] = v;
                 if (dx_canvas) dx_canvas[(int64_t)pix[c] * C + chn] = flat[c] >= 0 ? v : 0.f;
             }
@@ -346,7 +336,8 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
 template <bool BF16, int C, int H>
 size_t wg2_lds() {
     using S = WgShape<C, H>;
-    return 4 * ((size_t)4 * TP * S::RP + (size_t)4 * TP * S::DS + (size_t)4 * TP * C + (size_t)3 * TP * 7);
+    constexpr size_t TP = S::TP;
+    return 4 * (4 * TP * S::RP + 4 * TP * S::DS + (size_t)S::NWV * TP * C + 4 * TP);
 }
 
 typedef void (*Wg2Kernel)(Dev, const void*, const float*, const float*, const float*, float*, float*, float*);
