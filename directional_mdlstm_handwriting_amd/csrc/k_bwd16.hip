@@ -43,7 +43,6 @@ namespace {
 
 constexpr int kOOB = 0x40000000;  // byte offset past every per-unit range used here (1 GiB)
 constexpr int kPD = 3;            // diagonals of prefetch ahead
-constexpr int kThreads = 512;     // 8 waves: phase 2 on all of them
 constexpr int kMatWaves = 4;      // phase 1 on the first four
 
 template <int H>
@@ -75,9 +74,9 @@ __device__ inline uint32_t row16_max(uint32_t x) {
     return x;
 }
 
-// NE: elements per thread in phase 2 (cells x padded units of the widest diagonal over 512 threads)
-template <int H, int NE>
-__global__ __launch_bounds__(kThreads) void k_bwd16(Dev D, const float* __restrict__ Ul, const float* __restrict__ Uu,
+// NE: elements per thread in phase 2, NT threads: NE NT covers the cells x padded units of the widest diagonal
+template <int H, int NE, int NT>
+__global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ Ul, const float* __restrict__ Uu,
                                                     const float* __restrict__ stash,
                                                     const float* __restrict__ dy_flat,
                                                     const float* __restrict__ dh_dirs, float* __restrict__ dA) {
@@ -154,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd16(Dev D, const float* __restri
     extern __shared__ __align__(16) unsigned char smem[];
     {
         uint32_t* z32 = reinterpret_cast<uint32_t*>(smem);
-        for (int i = tid; i < LDS_BYTES / 4; i += kThreads) z32[i] = 0u;
+        for (int i = tid; i < LDS_BYTES / 4; i += NT) z32[i] = 0u;
     }
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
     const int64_t cells = (int64_t)h * w;
@@ -179,15 +178,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd16(Dev D, const float* __restri
     };
 
     // ---- phase 1 constants (matrix waves) ----
-    int jo[4], owd[4], oe[4][3];  // rows r: position, dh result offset, exponent rows at jo - 1, jo, jo + 1
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        jo[r] = (4 * r + q) * CG + cg;
-        owd[r] = OFF_DH + ((16 * cg + 4 * q + r) * HE + kk) * 4;  // P(jo[r])
-#pragma unroll
-        for (int m = 0; m < 3; ++m) oe[r][m] = P(jo[r] + m - 1) * NB * 4;
-    }
-    const int oze = ZR * NB * 4;
+    // rows r: position jo = (4 r + q) CG + cg, dh result offset owd
+    const int owd = OFF_DH + ((16 * cg + 4 * q) * HE + kk) * 4;  // P(jo[0]); row r adds r HE floats
     const int ja = (4 * (col & 3) + (col >> 2)) * CG + cg;  // diagonal position of this lane's A row
     int oa[3];  // LDS byte offsets of the da rows at positions ja - 1, ja, ja + 1
 #pragma unroll
@@ -214,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd16(Dev D, const float* __restri
     int oc[NE][3];                         // c-row offsets at positions pj - 1, pj, pj + 1
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
-        const int el = tid + kThreads * n;
+        const int el = tid + NT * n;
         pj[n] = el / HE;
         const int pk = el - pj[n] * HE, pb = pk / 16, pc = pk - 16 * pb;
         pk_ok[n] = pk < H;
@@ -323,10 +315,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd16(Dev D, const float* __restri
                     }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool hr = jo[r] >= dn, hd = jo[r] + 1 - dn < L1;  // successors present
-                // their exponent rows (positions jo - dn and jo + 1 - dn), or the zero row
-                const int oer = hr ? (dn ? oe[r][0] : oe[r][1]) : oze;
-                const int oed = hd ? (dn ? oe[r][1] : oe[r][2]) : oze;
+                // exponent rows of the successors (positions jo - dn and jo + 1 - dn; the zero row when absent)
+                const int jr = (4 * r + q) * CG + cg - dn;
+                const int oer = P(jr) * NB * 4;
+                const int oed = (jr + 1 < L1 ? P(jr + 1) : ZR) * NB * 4;
                 float dh = 0.f;
 #pragma unroll
                 for (int bi = 0; bi < NB; ++bi) {
@@ -334,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd16(Dev D, const float* __restri
                     const int ed = *reinterpret_cast<const int*>(ep + oed + 4 * bi);
                     dh += ldexpf(acc[0][bi][r], ec - er) + ldexpf(acc[1][bi][r], ec - ed);
                 }
-                *reinterpret_cast<float*>(smem + owd[r]) = dh;
+                *reinterpret_cast<float*>(smem + owd + r * HE * 4) = dh;
             }
         }
         __syncthreads();
@@ -408,19 +400,36 @@ __global__ __launch_bounds__(kThreads) void k_bwd16(Dev D, const float* __restri
 
 typedef void (*Bwd16Kernel)(Dev, const float*, const float*, const float*, const float*, const float*, float*);
 
-// hidden sizes of the workloads; NE = 1 or 2 elements per thread
+// hidden sizes of the workloads, each with its (elements per thread, threads) shapes in order of preference:
+// one element per thread while the widest diagonal fits the workgroup (shorter chains in phase 2), else two
+struct B16Shape2 {
+    int NE, NT;
+    Bwd16Kernel k;
+};
 struct B16Entry {
     int H, NB, CG;
-    Bwd16Kernel bwd[2];
+    B16Shape2 shapes[4];
 };
-#define MDL_B16(h) {h, B16Shape<h>::NB, B16Shape<h>::CG, {k_bwd16<h, 1>, k_bwd16<h, 2>}}
-const B16Entry kB16[] = {MDL_B16(2), MDL_B16(4), MDL_B16(10), MDL_B16(16), MDL_B16(32)};
+#define MDL_B16S(h, ne, nt) {ne, nt, k_bwd16<h, ne, nt>}
+#define MDL_B16(h)                                                                                          \
+    {h, B16Shape<h>::NB, B16Shape<h>::CG,                                                                   \
+     {MDL_B16S(h, 1, 512), MDL_B16S(h, 1, 640), MDL_B16S(h, 1, 768), MDL_B16S(h, 2, 512)}}
+const B16Entry kB16[] = {MDL_B16(2), MDL_B16(4), MDL_B16(10), MDL_B16(16),
+                         {32, B16Shape<32>::NB, B16Shape<32>::CG,
+                          {MDL_B16S(32, 1, 512), MDL_B16S(32, 2, 512), {0, 0, nullptr}, {0, 0, nullptr}}}};
 #undef MDL_B16
+#undef MDL_B16S
 
-// the widest diagonal must fit the matrix waves' tiles (16 CG cells) and two phase-2 elements per thread
+// the widest diagonal must fit the matrix waves' tiles (16 CG cells) and one of the phase-2 shapes
+const B16Shape2* b16_shape(const B16Entry& m, int Lmax) {
+    const int elems = Lmax * 16 * m.NB;
+    for (const auto& sh : m.shapes)
+        if (sh.k && elems <= sh.NE * sh.NT) return &sh;
+    return nullptr;
+}
 const B16Entry* b16_entry(int H, int Lmax) {
     for (const auto& m : kB16)
-        if (m.H == H) return (Lmax <= 16 * m.CG && Lmax * 16 * m.NB <= 2 * kThreads) ? &m : nullptr;
+        if (m.H == H) return (Lmax <= 16 * m.CG && b16_shape(m, Lmax)) ? &m : nullptr;
     return nullptr;
 }
 
@@ -443,10 +452,8 @@ hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, c
                         const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st) {
     const B16Entry* m = b16_entry(H, D.max_diag);
     if (!m) return hipErrorInvalidValue;
-    const int elems = D.max_diag * 16 * m->NB;  // phase-2 elements of the widest diagonal
-    const int ne = (elems + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(m->bwd[ne - 1], dim3(4 * D.n), dim3(kThreads), b16_lds(*m), st, D, Ul, Uu, stash, dy_flat,
-                       dh_dirs, dA);
+    const B16Shape2* sh = b16_shape(*m, D.max_diag);
+    hipLaunchKernelGGL(sh->k, dim3(4 * D.n), dim3(sh->NT), b16_lds(*m), st, D, Ul, Uu, stash, dy_flat, dh_dirs, dA);
     return hipGetLastError();
 }
 
