@@ -142,14 +142,16 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
 
     // LDS, two buffers (later / current diagonal) of NRW rows: the split, scaled da as f16
     // [hi | lo][block][unit][8] (row stride RA halves), the scale exponents [block] (ints), dc*f_l and
-    // dc*f_u (row stride CS floats); one buffer of the phase-1 result dh [NRW][HE]. Diagonal position j
-    // lives in row P(j) (below); ZR is a zero row, XR absorbs the writes of idle threads.
+    // dc*f_u (row stride CS floats); one buffer of the phase-1 result dh [NRW][HE] and one of the memory
+    // states c of the predecessor diagonal (row stride CS). Diagonal position j lives in row P(j) (below);
+    // ZR is a zero row, XR absorbs the writes of idle threads.
     constexpr int RA = 2 * NB * KA + 8, CS = HE + 4;
     constexpr int NRW = 16 * CG + 2, ZR = 16 * CG, XR = 16 * CG + 1;
     constexpr int ABUF = NRW * RA * 2, EBUF = NRW * NB * 4, CBUF = NRW * CS * 4;
     constexpr int OFF_E = 2 * ABUF, OFF_CL = OFF_E + 2 * EBUF, OFF_CU = OFF_CL + 2 * CBUF;
     constexpr int OFF_DH = OFF_CU + 2 * CBUF;
-    constexpr int LDS_BYTES = OFF_DH + NRW * HE * 4;
+    constexpr int OFF_CP = OFF_DH + NRW * HE * 4;
+    constexpr int LDS_BYTES = OFF_CP + CBUF;
     extern __shared__ __align__(16) unsigned char smem[];
     {
         uint32_t* z32 = reinterpret_cast<uint32_t*>(smem);
@@ -234,21 +236,17 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
     };
     auto diag_lo = [&](int s) { return s > w - 1 ? s - (w - 1) : 0; };
 
-    // forward values of this thread's elements on one diagonal: i, f_l, f_u, o | g, c | c_left | c_up | dy
+    // forward values of this thread's elements on one diagonal: i, f_l, f_u, o | g, c | dy
     struct Fw {
         f32x4 g4[NE];
         f32x2 g2[NE];
-        float cl[NE], cu[NE], dy[NE];
+        float dy[NE];
     };
     // s1: diagonal, st1: stash index of its first cell
     auto load_f = [&](int s1, int st1, Fw& f) {
         const int L1 = diag_len(s1);
         const int lo1 = diag_lo(s1 < 0 ? 0 : s1);
-        const bool dl = s1 >= w;
-        const int Ml = L1 < s1 - lo1 ? L1 : s1 - lo1;  // left predecessor iff j < Ml
-        const int Tu = dl ? 0 : 1;                       // upper predecessor iff Tu <= j
-        const int stp = st1 - diag_len(s1 - 1);         // first cell of diagonal s1 - 1
-        const int pe = st1 * H, pl = (stp + (dl ? 1 : 0)) * H, pu = pl - H;
+        const int pe = st1 * H;
         const int pu0 = UB + lo1 * UA + s1 * US;
         // real-region bounds as position ranges: a = lo1 + j in [ar0, ar1), b = s1 - lo1 - j in [br0, br1)
         const int jr0 = max(ar0 - lo1, s1 - lo1 - br1 + 1), jr1 = min(ar1 - lo1, s1 - lo1 - br0 + 1);
@@ -259,10 +257,7 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
             const int el = pe + ve[n];
             f.g4[n] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, ok ? el * 16 : kOOB, 0, 0));
             f.g2[n] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rS2, ok ? el * 8 : kOOB, 0, 0));
-            const bool vl = ok & (pj[n] < Ml), vu_ = ok & (pj[n] >= Tu);
             const bool vy = ok & (per_dir | ((pj[n] >= jr0) & (pj[n] < jr1)));
-            f.cl[n] = bld(rS2, vl ? (pl + ve[n]) * 8 + 4 : kOOB);
-            f.cu[n] = bld(rS2, vu_ ? (pu + ve[n]) * 8 + 4 : kOOB);
             f.dy[n] = bld(rU, vy ? pu0 + vu[n] : kOOB);
         }
     };
@@ -329,6 +324,9 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
                 *reinterpret_cast<float*>(smem + owd + r * HE * 4) = dh;
             }
         }
+        // memory states of diagonal s - 1 (prefetched with it) for this diagonal's predecessor terms
+#pragma unroll
+        for (int n = 0; n < NE; ++n) *reinterpret_cast<float*>(smem + OFF_CP + wc[n]) = fs[(POS + 1) & 3].g2[n][1];
         __syncthreads();
         // ---- phase 2: elementwise, all threads ----
         const Fw& f = fs[POS];
@@ -339,11 +337,17 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
         unsigned char* clw = smem + OFF_CL + CB * CBUF;
         unsigned char* cuw = smem + OFF_CU + CB * CBUF;
         const int pe = st * H;
+        // predecessors of position j on diagonal s - 1: left j + dl iff j < Ml, up j + dl - 1 iff j >= 1 - dl
+        const int dl = s >= w ? 1 : 0;
+        const int lo = diag_lo(s);
+        const int Ml = L < s - lo ? L : s - lo;
 #pragma unroll
         for (int n = 0; n < NE; ++n) {
             const int j = pj[n];
             const bool ok = (j < L) & pk_ok[n];
             const bool hr = j >= dn, hd = j + 1 - dn < L1;
+            const float cl = *reinterpret_cast<const float*>(smem + OFF_CP + (j < Ml ? (dl ? oc[n][2] : oc[n][1]) : zc));
+            const float cu = *reinterpret_cast<const float*>(smem + OFF_CP + (j + dl >= 1 ? (dl ? oc[n][1] : oc[n][0]) : zc));
             const int ocr = hr ? (dn ? oc[n][0] : oc[n][1]) : zc;  // right successor's c row, or zero row
             const int ocd = hd ? (dn ? oc[n][1] : oc[n][2]) : zc;  // lower successor's
             const float dh = *reinterpret_cast<const float*>(smem + rdh[n]) + f.dy[n];
@@ -354,8 +358,8 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
             const float dov = dh * tc;
             const float dc = __builtin_fmaf(dh * og, 1.f - tc * tc, dcin);
             const float d0 = dc * gg * ig * (1.f - ig);
-            const float d1 = dc * f.cl[n] * fl * (1.f - fl);
-            const float d2 = dc * f.cu[n] * fu * (1.f - fu);
+            const float d1 = dc * cl * fl * (1.f - fl);
+            const float d2 = dc * cu * fu * (1.f - fu);
             const float d3 = dov * og * (1.f - og);
             const float d4 = dc * ig * (1.f - gg * gg);
             // scale of this (cell, block): the largest |da| over the 16 units of the block
@@ -436,7 +440,7 @@ const B16Entry* b16_entry(int H, int Lmax) {
 size_t b16_lds(const B16Entry& m) {
     const size_t nrw = 16 * (size_t)m.CG + 2, he = 16 * (size_t)m.NB;
     const size_t ra = 2 * (size_t)m.NB * 128 + 8, cs = he + 4;
-    return 2 * nrw * ra * 2 + 2 * nrw * m.NB * 4 + 4 * nrw * cs * 4 + nrw * he * 4;
+    return 2 * nrw * ra * 2 + 2 * nrw * m.NB * 4 + 5 * nrw * cs * 4 + nrw * he * 4;
 }
 
 }  // namespace
