@@ -11,27 +11,29 @@
 //     da = [dc g i(1-i), dc c_l f_l(1-f_l), dc c_u f_u(1-f_u), dh tc o(1-o), dc i (1-g^2)]
 //
 // Each diagonal is done in two phases separated by a barrier.
-//  1. Four matrix waves (one per SIMD) form the recurrent part of dh on
-//     v_mfma_f32_16x16x32_f16 and leave it in LDS. Both operands are split
-//     into f16 hi + lo pairs (three partial products summed in fp32). Gate
-//     gradients have no bound, so each (cell, 16-wide block of hidden units)
-//     row of da was scaled by the power of two that brings its largest
-//     magnitude into [2^14, 2^15) before it was split; its exponent sits in
-//     LDS beside it and the product is scaled back exactly. The K dimension
-//     orders da by (hidden unit, gate), the five gates padded to eight.
-//  2. All eight waves do the elementwise part, each thread owning fixed
+//  1. Four matrix waves (one per SIMD) take the gate gradients da of the later diagonal s + 1, already in
+//     LDS, and form for each of its cells m the products X(m) = da(m) Ul^T and Y(m) = da(m) Uu^T on
+//     v_mfma_f32_16x16x32_f16: the parts of dh that m sends to its left and upper predecessors. Then
+//     dh(a, b) = dy(a, b) + X(R) + Y(D), and each row of da is read once. Both operands are split
+//     into f16 hi + lo pairs (three partial products summed in fp32). Gate gradients have no bound, so
+//     each (cell, 16-wide block of hidden units) row of da was scaled by the power of two that brings its
+//     largest magnitude into [2^14, 2^15) before it was split; its exponent sits in LDS beside it and the
+//     product is scaled back exactly. The K dimension orders da by (hidden unit, gate), the five gates
+//     padded to eight.
+//  2. All waves do the elementwise part, each thread owning fixed
 //     (diagonal position, hidden unit) elements: dc, da, the scale of its
 //     row (a maximum over the 16 lanes of a DPP row), the split into the LDS
 //     A rows of the next phase 1, and the store of da for the weight
 //     gradients. A single wave issues a VALU instruction only every few
-//     cycles, so spreading this part over all eight waves (two per SIMD)
-//     instead of the four matrix waves shortens the dependent chain.
+//     cycles, so the workgroup is sized to give each thread of the widest
+//     diagonal one element (two where the registers do not allow it).
 // Rows of the LDS A operand are permuted so the 16 lanes gathering one K
-// block read 16 consecutive rows on distinct banks. The forward's gate stash,
-// the predecessors' c and the upstream gradient of each element are
-// prefetched three diagonals ahead; the loop is unrolled by four so every
-// step is straight code and the compiler's vmcnt waits cover only the
-// prefetch they need (loads and stores retire in order on this hardware).
+// block read 16 consecutive rows on distinct banks. The forward's gate stash
+// and the upstream gradient of each element are prefetched three diagonals
+// ahead; the memory states c of the predecessor diagonal come from its own
+// prefetch through LDS. The loop is unrolled by four so every step is
+// straight code and the compiler's vmcnt waits cover only the prefetch they
+// need (loads and stores retire in order on this hardware).
 #include "kernels.h"
 #include "devmath.h"
 
@@ -93,64 +95,64 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
     // phase 1 role of a matrix wave: output block kb, cell group cg; lane (q, col)
     const int kb = (wave % kMatWaves) / CG, cg = (wave % kMatWaves) % CG;
     const int q = lane >> 4, col = lane & 15;
-    const int kk = kb * 16 + col;
 
-    // B operand of output block kb: [Ul^T; Uu^T] rows in the (unit, gate) K order. For successor sm
-    // (0: right, uses Ul; 1: down, uses Uu), input block bi and K block t, the lane holds K rows
-    // 32t + 8q + i = 8 (4t + q) + i of that block: unit k' = 16 bi + 4t + q, gate i (zero for i >= 5).
+    // Phase 1 forms, for every cell m of the later diagonal s + 1, X(m) = da(m) Ul^T and Y(m) = da(m) Uu^T:
+    // the parts of dh that cell m sends to its left and upper predecessors. A wave computes two output
+    // column blocks ("pairs") for its 16 cells: with one block of hidden units, X and Y of that block;
+    // with two, blocks 0 and 1 of X (kb = 0) or of Y (kb = 1).
+    // B operand of pair p: U^T rows in the (unit, gate) K order; for input block bi and K block t the lane
+    // holds K rows 32t + 8q + i = 8 (4t + q) + i: unit k' = 16 bi + 4t + q, gate i (zero for i >= 5).
     // Scaled per output column by 2^E and split into f16 hi + lo.
+    auto pair_y = [&](int p) { return NB == 1 ? p : kb; };               // pair computes Y (uses Uu)
+    auto pair_col = [&](int p) { return 16 * (NB == 1 ? 0 : p) + col; };  // output hidden unit
     f16x8 Bh[2][NB][KT], Bl[2][NB][KT];
-    int ec;  // the column's scale exponent, negated
-    {
-        float v[2][NB][KT][8];
+    int ec[2];  // the columns' scale exponents, negated
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+        float v[NB][KT][8];
         float m = 0.f;
+        const float* U = pair_y(pp) ? Uu : Ul;
+        const int kc = pair_col(pp);
 #pragma unroll
-        for (int sm = 0; sm < 2; ++sm)
+        for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-            for (int bi = 0; bi < NB; ++bi)
+            for (int t = 0; t < KT; ++t)
 #pragma unroll
-                for (int t = 0; t < KT; ++t)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int kp = 16 * bi + 4 * t + q;
-                        float x = 0.f;
-                        if (mat && kk < H && kp < H && i < 5) {
-                            const float* U = sm ? Uu : Ul;
-                            x = U[((int64_t)d * H + kk) * G + i * H + kp];
-                        }
-                        v[sm][bi][t][i] = x;
-                        m = fmaxf(m, fabsf(x));
-                    }
+                for (int i = 0; i < 8; ++i) {
+                    const int kp = 16 * bi + 4 * t + q;
+                    float x = 0.f;
+                    if (mat && kc < H && kp < H && i < 5) x = U[((int64_t)d * H + kc) * G + i * H + kp];
+                    v[bi][t][i] = x;
+                    m = fmaxf(m, fabsf(x));
+                }
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
         const int E = scale_exp(__float_as_uint(m));
-        ec = -E;
+        ec[pp] = -E;
 #pragma unroll
-        for (int sm = 0; sm < 2; ++sm)
+        for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-            for (int bi = 0; bi < NB; ++bi)
+            for (int t = 0; t < KT; ++t)
 #pragma unroll
-                for (int t = 0; t < KT; ++t)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        _Float16 hi, lo;
-                        split16(ldexpf(v[sm][bi][t][i], E), hi, lo);
-                        Bh[sm][bi][t][i] = hi;
-                        Bl[sm][bi][t][i] = lo;
-                    }
+                for (int i = 0; i < 8; ++i) {
+                    _Float16 hi, lo;
+                    split16(ldexpf(v[bi][t][i], E), hi, lo);
+                    Bh[pp][bi][t][i] = hi;
+                    Bl[pp][bi][t][i] = lo;
+                }
     }
 
     // LDS, two buffers (later / current diagonal) of NRW rows: the split, scaled da as f16
     // [hi | lo][block][unit][8] (row stride RA halves), the scale exponents [block] (ints), dc*f_l and
-    // dc*f_u (row stride CS floats); one buffer of the phase-1 result dh [NRW][HE] and one of the memory
-    // states c of the predecessor diagonal (row stride CS). Diagonal position j lives in row P(j) (below);
-    // ZR is a zero row, XR absorbs the writes of idle threads.
+    // dc*f_u (row stride CS floats); one buffer each of the phase-1 results X and Y of the later diagonal
+    // and of the memory states c of the predecessor diagonal (row stride CS). Diagonal position j lives
+    // in row P(j) (below); ZR is a zero row, XR absorbs the writes of idle threads.
     constexpr int RA = 2 * NB * KA + 8, CS = HE + 4;
     constexpr int NRW = 16 * CG + 2, ZR = 16 * CG, XR = 16 * CG + 1;
     constexpr int ABUF = NRW * RA * 2, EBUF = NRW * NB * 4, CBUF = NRW * CS * 4;
     constexpr int OFF_E = 2 * ABUF, OFF_CL = OFF_E + 2 * EBUF, OFF_CU = OFF_CL + 2 * CBUF;
-    constexpr int OFF_DH = OFF_CU + 2 * CBUF;
-    constexpr int OFF_CP = OFF_DH + NRW * HE * 4;
+    constexpr int OFF_X = OFF_CU + 2 * CBUF, OFF_Y = OFF_X + CBUF;
+    constexpr int OFF_CP = OFF_Y + CBUF;
     constexpr int LDS_BYTES = OFF_CP + CBUF;
     extern __shared__ __align__(16) unsigned char smem[];
     {
@@ -180,13 +182,11 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
     };
 
     // ---- phase 1 constants (matrix waves) ----
-    // rows r: position jo = (4 r + q) CG + cg, dh result offset owd
-    const int owd = OFF_DH + ((16 * cg + 4 * q) * HE + kk) * 4;  // P(jo[0]); row r adds r HE floats
-    const int ja = (4 * (col & 3) + (col >> 2)) * CG + cg;  // diagonal position of this lane's A row
-    int oa[3];  // LDS byte offsets of the da rows at positions ja - 1, ja, ja + 1
-#pragma unroll
-    for (int m = 0; m < 3; ++m) oa[m] = P(ja + m - 1) * RA * 2;
-    const int oza = ZR * RA * 2;
+    // The lane's A row is its own cell ja = (4 (col & 3) + (col >> 2)) CG + cg of the later diagonal; its
+    // output rows r are the cells (4r + q) CG + cg, at LDS rows 16 cg + 4q + r, whose scale exponents the
+    // product carries.
+    const int oa1 = P((4 * (col & 3) + (col >> 2)) * CG + cg) * RA * 2;
+    const int orow = 16 * cg + 4 * q;  // LDS row of output row r: orow + r
 
     // ---- phase 2 constants: element n of this thread is (position pj, unit pk) ----
     // Cell (a, b) sits at canvas (Y0 + SY a, X0 + SX b). The upstream gradient's byte offset is
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
     const int br0 = (d & 1) ? w - (rx0 - x0) - rw : rx0 - x0, br1 = br0 + rw;
     int pj[NE], vu[NE], ve[NE];
     bool pk_ok[NE];
-    int rdh[NE], wa[NE], we[NE], wc[NE];  // own LDS offsets (within a buffer)
+    int wa[NE], we[NE], wc[NE];  // own LDS offsets (within a buffer)
     int oc[NE][3];                         // c-row offsets at positions pj - 1, pj, pj + 1
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
@@ -216,7 +216,6 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
         vu[n] = pj[n] * UA + 4 * pkc;
         ve[n] = pj[n] * H + pkc;
         const int pr = P(pj[n]);
-        rdh[n] = OFF_DH + (pr * HE + pk) * 4;
         wa[n] = pr * RA * 2 + (pb * KA + 8 * pc) * 2;
         we[n] = (pr * NB + pb) * 4;
         wc[n] = pr * CS * 4 + 4 * pk;
@@ -286,43 +285,48 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
         const int dn = s >= w - 1 ? 1 : 0;  // successors of position j: right j - dn, down j + 1 - dn
         const unsigned char* ap = smem + (1 - CB) * ABUF;
         const unsigned char* ep = smem + OFF_E + (1 - CB) * EBUF;
-        // ---- phase 1: recurrent part of dh, matrix waves only (no global memory inside) ----
+        // ---- phase 1: X and Y of the later diagonal, matrix waves only (no global memory inside) ----
         if (mat) {
-            const int rr = ja >= dn ? (dn ? oa[0] : oa[1]) : oza;
-            const int rd = (ja + 1 - dn < L1) ? (dn ? oa[1] : oa[2]) : oza;
+            // scale exponents of the output rows: read before the products where registers allow
+            int er[4][NB];
+            auto read_er = [&]() {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int bi = 0; bi < NB; ++bi)
+                        er[r][bi] = *reinterpret_cast<const int*>(ep + ((orow + r) * NB + bi) * 4);
+            };
+            if constexpr (NB == 1) read_er();
             f32x4 acc[2][NB];
 #pragma unroll
-            for (int sm = 0; sm < 2; ++sm)
+            for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-                for (int bi = 0; bi < NB; ++bi) acc[sm][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int bi = 0; bi < NB; ++bi) acc[pp][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int sm = 0; sm < 2; ++sm)
+            for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
-                for (int bi = 0; bi < NB; ++bi)
+                for (int t = 0; t < KT; ++t) {
+                    const unsigned char* p = ap + oa1 + (bi * KA + 32 * t + 8 * q) * 2;
+                    const f16x8 ah = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p, 16));
+                    const f16x8 al = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p + NB * KA * 2, 16));
 #pragma unroll
-                    for (int t = 0; t < KT; ++t) {
-                        const unsigned char* p = ap + (sm ? rd : rr) + (bi * KA + 32 * t + 8 * q) * 2;
-                        const f16x8 ah = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p, 16));
-                        const f16x8 al = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p + NB * KA * 2, 16));
-                        acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[sm][bi][t], acc[sm][bi], 0, 0, 0);
-                        acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[sm][bi][t], acc[sm][bi], 0, 0, 0);
-                        acc[sm][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[sm][bi][t], acc[sm][bi], 0, 0, 0);
+                    for (int pp = 0; pp < 2; ++pp) {
+                        acc[pp][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[pp][bi][t], acc[pp][bi], 0, 0, 0);
+                        acc[pp][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[pp][bi][t], acc[pp][bi], 0, 0, 0);
+                        acc[pp][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[pp][bi][t], acc[pp][bi], 0, 0, 0);
                     }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // exponent rows of the successors (positions jo - dn and jo + 1 - dn; the zero row when absent)
-                const int jr = (4 * r + q) * CG + cg - dn;
-                const int oer = P(jr) * NB * 4;
-                const int oed = (jr + 1 < L1 ? P(jr + 1) : ZR) * NB * 4;
-                float dh = 0.f;
-#pragma unroll
-                for (int bi = 0; bi < NB; ++bi) {
-                    const int er = *reinterpret_cast<const int*>(ep + oer + 4 * bi);
-                    const int ed = *reinterpret_cast<const int*>(ep + oed + 4 * bi);
-                    dh += ldexpf(acc[0][bi][r], ec - er) + ldexpf(acc[1][bi][r], ec - ed);
                 }
-                *reinterpret_cast<float*>(smem + owd + r * HE * 4) = dh;
-            }
+            if constexpr (NB != 1) read_er();
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int bi = 0; bi < NB; ++bi) v += ldexpf(acc[pp][bi][r], ec[pp] - er[r][bi]);
+                    *reinterpret_cast<float*>(smem + (pair_y(pp) ? OFF_Y : OFF_X) +
+                                              ((orow + r) * CS + pair_col(pp)) * 4) = v;
+                }
         }
         // memory states of diagonal s - 1 (prefetched with it) for this diagonal's predecessor terms
 #pragma unroll
@@ -350,7 +354,9 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
             const float cu = *reinterpret_cast<const float*>(smem + OFF_CP + (j + dl >= 1 ? (dl ? oc[n][1] : oc[n][0]) : zc));
             const int ocr = hr ? (dn ? oc[n][0] : oc[n][1]) : zc;  // right successor's c row, or zero row
             const int ocd = hd ? (dn ? oc[n][1] : oc[n][2]) : zc;  // lower successor's
-            const float dh = *reinterpret_cast<const float*>(smem + rdh[n]) + f.dy[n];
+            // dh: X of the right successor and Y of the lower one (zero rows when absent), plus dy
+            const float dh = (*reinterpret_cast<const float*>(smem + OFF_X + ocr) +
+                              *reinterpret_cast<const float*>(smem + OFF_Y + ocd)) + f.dy[n];
             const float dcin = *reinterpret_cast<const float*>(clp + ocr) + *reinterpret_cast<const float*>(cup + ocd);
             const float ig = f.g4[n][0], fl = f.g4[n][1], fu = f.g4[n][2], og = f.g4[n][3];
             const float gg = f.g2[n][0], c = f.g2[n][1];
@@ -440,7 +446,7 @@ const B16Entry* b16_entry(int H, int Lmax) {
 size_t b16_lds(const B16Entry& m) {
     const size_t nrw = 16 * (size_t)m.CG + 2, he = 16 * (size_t)m.NB;
     const size_t ra = 2 * (size_t)m.NB * 128 + 8, cs = he + 4;
-    return 2 * nrw * ra * 2 + 2 * nrw * m.NB * 4 + 5 * nrw * cs * 4 + nrw * he * 4;
+    return 2 * nrw * ra * 2 + 2 * nrw * m.NB * 4 + 7 * nrw * cs * 4;
 }
 
 }  // namespace
