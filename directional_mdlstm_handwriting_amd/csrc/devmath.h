@@ -47,10 +47,6 @@ __device__ inline float ftanh(float x) {
     return copysignf(ax < 0.125f ? small : big, x);
 }
 
-// tanh(x) = 2 sigmoid(2x) - 1: four instructions; absolute error about 1e-7 near 0
-// (the subtraction cancels there), relative error about 1 ulp for |x| > 1/2.
-__device__ inline float ftanh2(float x) { return __builtin_fmaf(2.0f, frcp(1.0f + fexp(-2.0f * x)), -1.0f); }
-
 // fp32 value -> f16 pair (hi, lo) with hi + lo equal to v to about 2^-22 relative,
 // for |v| < 65504 and |v| above the f16 normal range's floor.
 __device__ inline void split16(float v, _Float16& hi, _Float16& lo) {

@@ -360,7 +360,7 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
             const float dcin = *reinterpret_cast<const float*>(clp + ocr) + *reinterpret_cast<const float*>(cup + ocd);
             const float ig = f.g4[n][0], fl = f.g4[n][1], fu = f.g4[n][2], og = f.g4[n][3];
             const float gg = f.g2[n][0], c = f.g2[n][1];
-            const float tc = ftanh2(c);
+            const float tc = ftanh(c);
             const float dov = dh * tc;
             const float dc = __builtin_fmaf(dh * og, 1.f - tc * tc, dcin);
             const float d0 = dc * gg * ig * (1.f - ig);

@@ -45,6 +45,14 @@ namespace {
 constexpr int kOOB = 0x40000000;    // byte offset past every per-unit range used here (1 GiB)
 constexpr float kHScale = 16384.f;  // 2^14: h in (-1, 1) -> f16 range
 constexpr int kZD = 3;              // diagonals of input prefetch ahead
+// The sigmoid gates take their argument in base-2 exponent form, sigmoid(a) = 1 / (1 + 2^(-a log2 e)): the
+// factor -log2 e of gates i, f_l, f_u, o is folded into the weight scales and the bias, so their
+// accumulators already hold the exponents. The cell input g = tanh(a) keeps its plain argument: tanh goes
+// through ftanh, whose error is relative also near 0 (a small g or c would otherwise carry an absolute
+// error of about 1e-7 into every gradient that multiplies it).
+constexpr float kL2E = 1.44269504088896341f;
+__host__ __device__ constexpr float gate_fold(int g) { return g < 4 ? -kL2E : 1.0f; }
+__device__ inline float sig_e2(float t) { return frcp(1.0f + __builtin_amdgcn_exp2f(t)); }
 
 template <int H>
 struct F16Shape {
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     // B operand: lane holds rows 32t + 8q .. +7 of column g*H + kk of [Ul; Uu] (Ul row k at K index k,
     // Uu row k at HP + k, zeros elsewhere), scaled per column by 2^E and split into f16 hi + lo.
     f16x8 Bh[5][KB], Bl[5][KB];
-    float us[5];  // 2^-(E + 14): undoes both scalings
+    float us[5];  // 2^-(E + 14) times the gate's fold: undoes both scalings
 #pragma unroll
     for (int g = 0; g < 5; ++g) {
         float v[KB][8];
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             E = 14 - ((int)((__float_as_uint(m) >> 23) & 255) - 127);
             E = E < -100 ? -100 : (E > 100 ? 100 : E);
         }
-        us[g] = ldexpf(1.0f, -(E + 14));
+        us[g] = ldexpf(1.0f, -(E + 14)) * gate_fold(g);  // undoes both scalings, times the gate's fold
 #pragma unroll
         for (int t = 0; t < KB; ++t)
 #pragma unroll
@@ -123,11 +131,11 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     float Bx[5][KX], bz[5];
 #pragma unroll
     for (int g = 0; g < 5; ++g) {
-        bz[g] = kok ? bias[(int64_t)d * G + g * H + kk] : 0.f;
+        bz[g] = kok ? bias[(int64_t)d * G + g * H + kk] * gate_fold(g) : 0.f;
 #pragma unroll
         for (int ks = 0; ks < KX; ++ks) {
             const int c = 4 * ks + q;
-            Bx[g][ks] = (kok && c < C) ? Wx[((int64_t)d * C + c) * G + g * H + kk] : 0.f;
+            Bx[g][ks] = (kok && c < C) ? Wx[((int64_t)d * C + c) * G + g * H + kk] * gate_fold(g) : 0.f;
         }
     }
 
@@ -294,13 +302,13 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const bool ok = jo[r] < L && kok;
-            const float ig = sigm(__builtin_fmaf(acc[0][r], us[0], accx[0][r]));
-            const float fl = sigm(__builtin_fmaf(acc[1][r], us[1], accx[1][r]));
-            const float fu = sigm(__builtin_fmaf(acc[2][r], us[2], accx[2][r]));
-            const float og = sigm(__builtin_fmaf(acc[3][r], us[3], accx[3][r]));
-            const float gg = ftanh2(__builtin_fmaf(acc[4][r], us[4], accx[4][r]));
+            const float ig = sig_e2(__builtin_fmaf(acc[0][r], us[0], accx[0][r]));
+            const float fl = sig_e2(__builtin_fmaf(acc[1][r], us[1], accx[1][r]));
+            const float fu = sig_e2(__builtin_fmaf(acc[2][r], us[2], accx[2][r]));
+            const float og = sig_e2(__builtin_fmaf(acc[3][r], us[3], accx[3][r]));
+            const float gg = ftanh(__builtin_fmaf(acc[4][r], us[4], accx[4][r]));
             const float c = __builtin_fmaf(fl, cl[r], __builtin_fmaf(fu, cu[r], ig * gg));
-            const float hv = og * ftanh2(c);
+            const float hv = og * ftanh(c);
             *reinterpret_cast<float*>(cw + (ok ? owc[r] : oxc)) = c;
             _Float16 hh, hl;
             split16(hv * kHScale, hh, hl);

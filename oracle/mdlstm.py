@@ -222,16 +222,8 @@ def diagonals(rects, d):
     return out
 
 
-def forward_vec(xc, rects, P, with_scale=False):
-    """Same as forward_canvas_brute, one local diagonal at a time.
-
-    With ``with_scale`` also returns ``cab`` [4][Hc][Wc][H]: the memory-state
-    recurrence evaluated on absolute values of its terms,
-    cab = f_l*cab_left + f_u*cab_up + |i*g|, i.e. the sum of the magnitudes of
-    everything that was added up into c. A rounding error of relative size u in
-    the evaluation of c is bounded by about (number of steps) * u * cab, so cab
-    is the scale against which a floating-point evaluation of c (and of
-    h = o*tanh(c)) can be judged where c itself comes out of cancellation."""
+def forward_vec(xc, rects, P):
+    """Same as forward_canvas_brute, one local diagonal at a time."""
     Wx, Ul, Uu, b = _p64(P)
     xc = np.asarray(xc, np.float64)
     Hc, Wc, _ = xc.shape
@@ -239,7 +231,6 @@ def forward_vec(xc, rects, P, with_scale=False):
     hd = np.zeros((4, Hc, Wc, H))
     cd = np.zeros((4, Hc, Wc, H))
     gd = np.zeros((4, Hc, Wc, 5 * H))
-    cab = np.zeros((4, Hc, Wc, H)) if with_scale else None
     for d in range(4):
         sy, sx = DIRS[d]
         for (Y, X, VL, VU) in diagonals(rects, d):
@@ -252,53 +243,21 @@ def forward_vec(xc, rects, P, with_scale=False):
             cu[VU] = cd[d, Y[VU] - sy, X[VU]]
             h, c, g = _cell(xc[Y, X], hl, cl, hu, cu, Wx[d], Ul[d], Uu[d], b[d], H)
             hd[d, Y, X], cd[d, Y, X], gd[d, Y, X] = h, c, g
-            if with_scale:
-                al = np.zeros((m, H)); au = np.zeros((m, H))
-                al[VL] = cab[d, Y[VL], X[VL] - sx]
-                au[VU] = cab[d, Y[VU] - sy, X[VU]]
-                cab[d, Y, X] = g[:, H:2 * H] * al + g[:, 2 * H:3 * H] * au + np.abs(g[:, 0:H] * g[:, 4 * H:5 * H])
-    if with_scale:
-        return hd, cd, gd, cab
     return hd, cd, gd
 
 
-def h_scale(cd, gd, cab):
-    """Magnitude scale of h = o*tanh(c): |h| + o*(1 - tanh(c)^2)*cab (first-order error propagation)."""
-    H = cd.shape[-1]
-    o = gd[..., 3 * H:4 * H]
-    return np.abs(o * np.tanh(cd)) + o * (1.0 - np.tanh(cd) ** 2) * cab
-
-
-def backward_vec(xc, rects, P, hd, cd, gd, dhd, with_abs=False, cab=None, dhd_abs=None):
-    """Same as backward_canvas_brute, one local diagonal at a time, in reverse.
-
-    With ``with_abs`` the same recurrence is also evaluated on magnitudes: every
-    quantity q is paired with a scale S(q) >= |q| that sums the absolute values
-    of the terms q is built from (dh from |dy| and |da|.|U|, dc from the
-    successors' S(dc)*f and S(dh)*o*(1-tanh^2 c), da from S(dc) and the gates,
-    with the forward memory-state scale ``cab`` standing in for |c| of the
-    predecessors). Returned: for every weight-gradient entry and every pixel's
-    dx, the sum of S(term) over the terms that make it up - the scale that the
-    rounding error of a floating-point evaluation is proportional to."""
+def backward_vec(xc, rects, P, hd, cd, gd, dhd):
+    """Same as backward_canvas_brute, one local diagonal at a time, in reverse."""
     Wx, Ul, Uu, b = _p64(P)
     xc = np.asarray(xc, np.float64)
     Hc, Wc, C = xc.shape
     H = Ul.shape[1]
     dxc = np.zeros((Hc, Wc, C))
     dWx, dUl, dUu, db = (np.zeros_like(a) for a in (Wx, Ul, Uu, b))
-    if with_abs:
-        aWx, aUl, aUu, ab = (np.zeros_like(a) for a in (Wx, Ul, Uu, b))
-        adx = np.zeros((Hc, Wc, C))
-        if cab is None:
-            cab = np.abs(cd)
-        aU = (np.abs(Ul), np.abs(Uu))
     for d in range(4):
         sy, sx = DIRS[d]
         dh_acc = np.array(dhd[d], np.float64)
         dc_acc = np.zeros((Hc, Wc, H))
-        if with_abs:
-            sh_acc = np.abs(np.array(dhd[d] if dhd_abs is None else dhd_abs[d], np.float64))
-            sc_acc = np.zeros((Hc, Wc, H))
         for (Y, X, VL, VU) in reversed(diagonals(rects, d)):
             m = len(Y)
             hl = np.zeros((m, H)); cl = np.zeros((m, H))
@@ -320,30 +279,6 @@ def backward_vec(xc, rects, P, hd, cd, gd, dhd, with_abs=False, cab=None, dhd_ab
             dUu[d] += hu.T @ da
             db[d] += da.sum(axis=0)
             dxc[Y, X] += da @ Wx[d].T
-            if with_abs:
-                i, _, _, o, g = (gates[:, k * H:(k + 1) * H] for k in range(5))
-                tc = np.tanh(cd[d, Y, X])
-                al = np.zeros((m, H)); au = np.zeros((m, H))
-                al[VL] = cab[d, Y[VL], X[VL] - sx]
-                au[VU] = cab[d, Y[VU] - sy, X[VU]]
-                sdh = sh_acc[Y, X]
-                sdc = sc_acc[Y, X] + sdh * o * (1.0 - tc * tc)
-                sda = np.concatenate([sdc * np.abs(g) * i * (1.0 - i),
-                                      sdc * al * fl * (1.0 - fl),
-                                      sdc * au * fu * (1.0 - fu),
-                                      sdh * np.abs(tc) * o * (1.0 - o),
-                                      sdc * i * (1.0 - g * g)], axis=-1)
-                sh_acc[Y[VL], X[VL] - sx] += sda[VL] @ aU[0][d].T
-                sc_acc[Y[VL], X[VL] - sx] += sdc[VL] * fl[VL]
-                sh_acc[Y[VU] - sy, X[VU]] += sda[VU] @ aU[1][d].T
-                sc_acc[Y[VU] - sy, X[VU]] += sdc[VU] * fu[VU]
-                aWx[d] += np.abs(xv).T @ sda
-                aUl[d] += np.abs(hl).T @ sda
-                aUu[d] += np.abs(hu).T @ sda
-                ab[d] += sda.sum(axis=0)
-                adx[Y, X] += sda @ np.abs(Wx[d]).T
-    if with_abs:
-        return dxc, dWx, dUl, dUu, db, (aWx, aUl, aUu, ab, adx)
     return dxc, dWx, dUl, dUu, db
 
 
@@ -351,44 +286,32 @@ def backward_vec(xc, rects, P, hd, cd, gd, dhd, with_abs=False, cab=None, dhd_ab
 # whole layer on a packed canvas: per-example inputs in, per-example outputs out
 # ----------------------------------------------------------------------------------------------
 
-def layer_forward(layout, xs: Sequence[np.ndarray], P, brute=False, with_scale=False):
+def layer_forward(layout, xs: Sequence[np.ndarray], P, brute=False):
     """Scatter -> 4-direction forward -> (direction sum, un-pack).
 
-    Returns (ys, cache) with ys[e] [h][w][H]. With ``with_scale`` the cache also
-    holds the memory-state scale (see forward_vec)."""
+    Returns (ys, cache) with ys[e] [h][w][H]."""
     from .canvas import scatter, dirsum_unpack
     xc = scatter(layout, xs)
     if brute:
         hd, cd, gd = forward_canvas_brute(xc, layout.eid, layout.border, P)
-        cab = None
-    elif with_scale:
-        hd, cd, gd, cab = forward_vec(xc, layout.rects, P, with_scale=True)
     else:
         hd, cd, gd = forward_vec(xc, layout.rects, P)
-        cab = None
-    cache = (xc, hd, cd, gd) if cab is None else (xc, hd, cd, gd, cab)
-    return dirsum_unpack(layout, hd), cache
+    return dirsum_unpack(layout, hd), (xc, hd, cd, gd)
 
 
-def layer_backward(layout, P, cache, dys: Sequence[np.ndarray] = None, dhd=None, brute=False,
-                   with_abs=False):
+def layer_backward(layout, P, cache, dys: Sequence[np.ndarray] = None, dhd=None, brute=False):
     """Backward of layer_forward for per-example output gradients ``dys`` (each
     direction receives the same gradient through the direction sum), or for a
     per-direction canvas gradient ``dhd`` [4][Hc][Wc][H].
 
-    Returns (dxs, dWx, dUl, dUu, db[, (scales of dWx, dUl, dUu, db, per-example dx)])."""
+    Returns (dxs, dWx, dUl, dUu, db)."""
     from .canvas import scatter, unpack
-    xc, hd, cd, gd = cache[:4]
-    cab = cache[4] if len(cache) > 4 else None
+    xc, hd, cd, gd = cache
     if dhd is None:
         dyc = scatter(layout, dys)
         dhd = np.broadcast_to(dyc, (4,) + dyc.shape)
     if brute:
         res = backward_canvas_brute(xc, layout.eid, layout.border, P, hd, cd, gd, dhd)
     else:
-        res = backward_vec(xc, layout.rects, P, hd, cd, gd, dhd, with_abs=with_abs, cab=cab)
-    dxs = unpack(layout, res[0])
-    if with_abs:
-        a = res[5]
-        return (dxs,) + tuple(res[1:5]) + ((a[0], a[1], a[2], a[3], unpack(layout, a[4])),)
-    return (dxs,) + tuple(res[1:])
+        res = backward_vec(xc, layout.rects, P, hd, cd, gd, dhd)
+    return (unpack(layout, res[0]),) + tuple(res[1:])

@@ -7,14 +7,15 @@ the oracle computes a sample of them one by one, each alone. The upstream
 gradient is nonzero only on the sampled examples. Then every other example's
 input gradient is exactly zero, and the weight gradients are sums over the
 sampled examples only, which the oracle fixes as well. The sample always holds
-the deepest example (most dependent diagonals) and the smallest one.
+the deepest example (most dependent diagonals) and the smallest one. The
+tolerance and its conditioning fallback are those of test_gpu_parity.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from test_gpu_parity import BF16_TOL, DEV, F32_TOL, _np, assert_close, oracle_layer, poison, run_layer
+from test_gpu_parity import BF16_TOL, DEV, F32_TOL, _np, assert_close, oracle_layer, oracle_stack, poison, run_layer
 from workloads import cotangent, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -22,7 +23,6 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import directional_mdlstm_handwriting_amd as M
     from directional_mdlstm_handwriting_amd.layer import DeviceParams, LayerGrads, PackedStack, flat_input
-from oracle import stack as ostack
 
 
 def sample(heights, widths, n_random, seed):
@@ -52,25 +52,27 @@ def test_layer_full_size_sampled(name, n_random):
     y, dx = _np(g["layer"].y), _np(g["dx"])
     yo, xo = offsets(wl.heights, wl.widths, H), offsets(wl.heights, wl.widths, C)
     dW = [0.0] * 4
-    aW = [0.0] * 4
+    sens = []
     for e in idx:
         h, w = int(wl.heights[e]), int(wl.widths[e])
         o = oracle_layer([h], [w], [wl.xs[e]], P, dys=[dys[e]])
+        sn = o["sens"]
+        sens.append(sn)
         y0, x0 = int(real[e][0]), int(real[e][1])
         assert_close(f"h_dirs[{e}]", _np(g["layer"].h_dirs[:, y0:y0 + h, x0:x0 + w, :]), o["hd"][:, :h, :w, :], F32_TOL,
-                     abs_sum=o["hs"][:, :h, :w, :])
-        assert_close(f"y[{e}]", y[yo[e]:yo[e + 1]], o["ys"][0], F32_TOL, abs_sum=o["ys_scale"][0])
+                     sens=lambda sn=sn, h=h, w=w: sn()["hd"][:, :h, :w, :])
+        assert_close(f"y[{e}]", y[yo[e]:yo[e + 1]], o["ys"][0], F32_TOL, sens=lambda sn=sn: sn()["ys"][0])
         if wl.x_dtype == "bf16":  # the bf16-input bound as well (the fp32 one above is stricter)
             assert_close(f"y[{e}] (bf16 bound)", y[yo[e]:yo[e + 1]], o["ys"][0], BF16_TOL)
-        assert_close(f"dx[{e}]", dx[xo[e]:xo[e + 1]], o["dxs"][0], F32_TOL, abs_sum=o["dxs_scale"][0])
+        assert_close(f"dx[{e}]", dx[xo[e]:xo[e + 1]], o["dxs"][0], F32_TOL, sens=lambda sn=sn: sn()["dxs"][0])
         dW = [a + b for a, b in zip(dW, o["dW"])]
-        aW = [a + b for a, b in zip(aW, o["absW"])]
     others = np.ones(dx.size, bool)
     for e in idx:
         others[xo[e]:xo[e + 1]] = False
     assert np.all(dx[others] == 0.0), "input gradient of an example with zero upstream gradient"
-    for nm, got, ref, a in zip(("dWx", "dUl", "dUu", "db"), (g["g"].dWx, g["g"].dUl, g["g"].dUu, g["g"].db), dW, aW):
-        assert_close(nm, _np(got), ref, F32_TOL, abs_sum=a)
+    for k, (nm, got, ref) in enumerate(zip(("dWx", "dUl", "dUu", "db"), (g["g"].dWx, g["g"].dUl, g["g"].dUu, g["g"].db),
+                                            dW)):
+        assert_close(nm, _np(got), ref, F32_TOL, sens=lambda k=k: sum(sn()["dW"][k] for sn in sens))
 
 
 def test_stack_full_size_sampled():
@@ -109,22 +111,26 @@ def test_stack_full_size_sampled():
     yo, xo = offsets(hL, wL, HL), offsets(wl.heights, wl.widths, wl.C)
     lg_ref = [[0.0] * 4 for _ in Hs]
     cg_ref = [[0.0] * 2 for _ in wl.convs]
+    sens = []
     for e in idx:
         h, w = int(wl.heights[e]), int(wl.widths[e])
-        ys_ref, caches = ostack.stack_forward([h], [w], [wl.xs[e]], wl.layers, wl.convs, wl.canvas_w_min)
-        assert_close(f"stack y[{e}]", y[yo[e]:yo[e + 1]], ys_ref[0], F32_TOL)
-        dxs_ref, lgr, cgr = ostack.stack_backward(wl.layers, wl.convs, caches, [dys[e]])
-        assert_close(f"stack dx[{e}]", dx[xo[e]:xo[e + 1]], dxs_ref[0], F32_TOL)
-        lg_ref = [[a + b for a, b in zip(acc, r)] for acc, r in zip(lg_ref, lgr)]
-        cg_ref = [[a + b for a, b in zip(acc, r)] for acc, r in zip(cg_ref, cgr)]
+        o = oracle_stack([h], [w], [wl.xs[e]], wl.layers, wl.convs, wl.canvas_w_min, [dys[e]])
+        sn = o["sens"]
+        sens.append(sn)
+        assert_close(f"stack y[{e}]", y[yo[e]:yo[e + 1]], o["ys"][0], F32_TOL, sens=lambda sn=sn: sn()["ys"][0])
+        assert_close(f"stack dx[{e}]", dx[xo[e]:xo[e + 1]], o["dxs"][0], F32_TOL, sens=lambda sn=sn: sn()["dxs"][0])
+        lg_ref = [[a + b for a, b in zip(acc, r)] for acc, r in zip(lg_ref, o["lg"])]
+        cg_ref = [[a + b for a, b in zip(acc, r)] for acc, r in zip(cg_ref, o["cg"])]
     others = np.ones(dx.size, bool)
     for e in idx:
         others[xo[e]:xo[e + 1]] = False
     assert np.all(dx[others] == 0.0), "input gradient of an example with zero upstream gradient"
     for lvl in range(len(Hs)):
-        for nm, got, ref in zip(("dWx", "dUl", "dUu", "db"),
-                                (lg[lvl].dWx, lg[lvl].dUl, lg[lvl].dUu, lg[lvl].db), lg_ref[lvl]):
-            assert_close(f"L{lvl} {nm}", _np(got), ref, F32_TOL)
+        for k, (nm, got, ref) in enumerate(zip(("dWx", "dUl", "dUu", "db"),
+                                               (lg[lvl].dWx, lg[lvl].dUl, lg[lvl].dUu, lg[lvl].db), lg_ref[lvl])):
+            assert_close(f"L{lvl} {nm}", _np(got), ref, F32_TOL,
+                         sens=lambda lvl=lvl, k=k: sum(sn()["lg"][lvl][k] for sn in sens))
     for j in range(len(wl.convs)):
-        assert_close(f"conv{j} dW", _np(cg[j][0]), cg_ref[j][0], F32_TOL)
-        assert_close(f"conv{j} db", _np(cg[j][1]), cg_ref[j][1], F32_TOL)
+        for k, nm in enumerate(("dW", "db")):
+            assert_close(f"conv{j} {nm}", _np(cg[j][k]), cg_ref[j][k], F32_TOL,
+                         sens=lambda j=j, k=k: sum(sn()["cg"][j][k] for sn in sens))

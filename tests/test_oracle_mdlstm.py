@@ -370,35 +370,3 @@ def test_padded_mode_is_zero_padded_images():
         xp[:h, :w] = x
         ref = _alone(xp, P).sum(axis=0)[:h, :w]
         np.testing.assert_allclose(ys[e], ref, rtol=1e-12, atol=1e-14)
-
-
-def test_abs_sums_bound_the_gradients():
-    wl, lay = _tiny(0)
-    P = wl.layers[0]
-    ys, cache = mdlstm.layer_forward(lay, wl.xs, P, with_scale=True)
-    dys = cotangent(0, wl.heights, wl.widths, wl.H)
-    res = mdlstm.layer_backward(lay, P, cache, dys=dys, with_abs=True)
-    for g, a in zip(res[1:5], res[5][:4]):
-        assert np.all(np.abs(g) <= a * (1 + 1e-12) + 1e-300)
-    for dx, a in zip(res[0], res[5][4]):
-        assert np.all(np.abs(dx) <= a * (1 + 1e-12) + 1e-300)
-    # the scale of each dx is at least the scale of the same gradient with one direction only
-    assert all(np.all(a > 0) for a in res[5][4])
-
-
-def test_memory_state_scale():
-    """cab >= |c| always; cab == c when every term added into c is positive."""
-    wl, lay = _tiny(1)
-    P = wl.layers[0]
-    xc = canvas.scatter(lay, wl.xs)
-    hd, cd, gd, cab = mdlstm.forward_vec(xc, lay.rects, P, with_scale=True)
-    assert np.all(cab >= np.abs(cd) * (1 - 1e-12))
-    hs = mdlstm.h_scale(cd, gd, cab)
-    assert np.all(hs >= np.abs(hd) * (1 - 1e-12))
-    H = wl.H
-    b = np.array(P.b, np.float64)
-    b[:, 4 * H:] = 1.0                       # g = tanh(x.Wx + 1) > 0 with Wx >= 0, x >= 0
-    Q = LayerParams(np.abs(np.asarray(P.Wx, np.float64)), np.zeros_like(P.Ul), np.zeros_like(P.Uu), b)
-    hd, cd, gd, cab = mdlstm.forward_vec(xc, lay.rects, Q, with_scale=True)
-    np.testing.assert_allclose(cab, cd, rtol=1e-13, atol=0)
-    assert np.all(cd[:, lay.eid >= 0] > 0)
