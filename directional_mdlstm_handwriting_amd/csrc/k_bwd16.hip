@@ -68,13 +68,19 @@ __device__ inline int scale_exp(uint32_t mbits) {
 }
 
 // largest value of x over the 16 lanes of each row of the wave (DPP within rows)
+// (0 is the identity of the maximum, so each lane move can fold into the max instruction)
 __device__ inline uint32_t row16_max(uint32_t x) {
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false));  // row_ror:4
-    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false));  // row_ror:8
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, true));  // row_ror:4
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, true));  // row_ror:8
     return x;
 }
+
+// f16 pair of a scaled value v (|v| < 2^15): hi is v with its low 13 mantissa bits cleared, which f16
+// holds exactly (11 significant bits; below the f16 normal range the rounding is under 2^-25), and
+// lo = v - hi rounded to f16, so hi + lo is v to about 2^-21 of |v|
+__device__ inline float hi_part(float v) { return __uint_as_float(__float_as_uint(v) & 0xFFFFE000u); }
 
 // NE: elements per thread in phase 2, NT threads: NE NT covers the cells x padded units of the widest diagonal
 template <int H, int NE, int NT>
@@ -368,20 +374,18 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
             const float d2 = dc * cu * fu * (1.f - fu);
             const float d3 = dov * og * (1.f - og);
             const float d4 = dc * ig * (1.f - gg * gg);
-            // scale of this (cell, block): the largest |da| over the 16 units of the block
-            uint32_t mb = max(max(__float_as_uint(fabsf(d0)), __float_as_uint(fabsf(d1))),
-                              max(max(__float_as_uint(fabsf(d2)), __float_as_uint(fabsf(d3))),
-                                  __float_as_uint(fabsf(d4))));
-            mb = row16_max(ok ? mb : 0u);
+            // scale of this (cell, block): the largest |da| over the 16 units of the block (non-negative
+            // floats order like their bit patterns)
+            const float am = fmaxf(fmaxf(fabsf(d0), fabsf(d1)), fmaxf(fmaxf(fabsf(d2), fabsf(d3)), fabsf(d4)));
+            const uint32_t mb = row16_max(ok ? __float_as_uint(am) : 0u);
             const int E = scale_exp(mb);
-            _Float16 h0, l0, h1, l1, h2, l2, h3, l3, h4, l4;
-            split16(ldexpf(d0, E), h0, l0);
-            split16(ldexpf(d1, E), h1, l1);
-            split16(ldexpf(d2, E), h2, l2);
-            split16(ldexpf(d3, E), h3, l3);
-            split16(ldexpf(d4, E), h4, l4);
-            const f16x8 hv = {h0, h1, h2, h3, h4, (_Float16)0, (_Float16)0, (_Float16)0};
-            const f16x8 lv = {l0, l1, l2, l3, l4, (_Float16)0, (_Float16)0, (_Float16)0};
+            const float s0 = ldexpf(d0, E), s1 = ldexpf(d1, E), s2 = ldexpf(d2, E), s3 = ldexpf(d3, E),
+                        s4 = ldexpf(d4, E);
+            const float t0 = hi_part(s0), t1 = hi_part(s1), t2 = hi_part(s2), t3 = hi_part(s3), t4 = hi_part(s4);
+            const f16x8 hv = {(_Float16)t0, (_Float16)t1, (_Float16)t2, (_Float16)t3, (_Float16)t4,
+                              (_Float16)0, (_Float16)0, (_Float16)0};
+            const f16x8 lv = {(_Float16)(s0 - t0), (_Float16)(s1 - t1), (_Float16)(s2 - t2), (_Float16)(s3 - t3),
+                              (_Float16)(s4 - t4), (_Float16)0, (_Float16)0, (_Float16)0};
             unsigned char* pa = aw + (ok ? wa[n] : xa);
             *reinterpret_cast<f16x8*>(__builtin_assume_aligned(pa, 16)) = hv;
             *reinterpret_cast<f16x8*>(__builtin_assume_aligned(pa + NB * KA * 2, 16)) = lv;
