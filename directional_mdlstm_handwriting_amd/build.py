@@ -27,6 +27,10 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
+# Per-source additions. The forward wavefront keeps its matrix-core accumulators in ordinary vector
+# registers: in the accumulation registers every gate value would cost one extra move before its
+# nonlinearity, on the kernel's critical path. (Elsewhere that register form makes the larger shapes spill.)
+EXTRA = {"k_fwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def sources():
@@ -40,7 +44,7 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, *COMMON, *DEVICE, "-x", "hip", "-c", src, "-o", obj]
+        cmd = [HIPCC, *COMMON, *DEVICE, *EXTRA.get(os.path.basename(src), []), "-x", "hip", "-c", src, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-x", "c++", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

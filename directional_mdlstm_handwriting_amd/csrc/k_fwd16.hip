@@ -189,12 +189,14 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
         vh[r] = jo[r] * DA + 4 * kk;
         ve[r] = jo[r] * H + kk;
         const int pw = 16 * cg + 4 * q + r;  // P(jo[r])
-        owc[r] = pw * CS * 4 + 4 * kc;
-        owh[r] = pw * RS * 2 + 2 * kc;
+        // a lane without a hidden unit writes the discard row; a row of a position beyond the diagonal takes
+        // whatever its lane computes, since no later step reads positions past its predecessor's length
+        owc[r] = kok ? pw * CS * 4 + 4 * kc : XR * CS * 4 + 4 * kc;
+        owh[r] = kok ? pw * RS * 2 + 2 * kc : XR * RS * 2 + 2 * kc;
 #pragma unroll
         for (int m = 0; m < 3; ++m) opc[r][m] = P(jo[r] + m - 1) * CS * 4 + 4 * kc;
     }
-    const int oxc = XR * CS * 4 + 4 * kc, oxh = XR * RS * 2 + 2 * kc, ozc = ZR * CS * 4 + 4 * kc;
+    const int ozc = ZR * CS * 4 + 4 * kc;
     const int ja = (4 * (col & 3) + (col >> 2)) * CG + cg;  // diagonal position of this lane's A row
     // canvas input of the A row's cell: byte offset XBASE + a XA + s XS + vx[ks] (channel 4 ks + q)
     const int XA = (SY * D.Wc * C - SX * C) * XB, XS = SX * C * XB;
@@ -309,10 +311,10 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             const float gg = ftanh(__builtin_fmaf(acc[4][r], us[4], accx[4][r]));
             const float c = __builtin_fmaf(fl, cl[r], __builtin_fmaf(fu, cu[r], ig * gg));
             const float hv = og * ftanh(c);
-            *reinterpret_cast<float*>(cw + (ok ? owc[r] : oxc)) = c;
+            *reinterpret_cast<float*>(cw + owc[r]) = c;
             _Float16 hh, hl;
             split16(hv * kHScale, hh, hl);
-            _Float16* hp = reinterpret_cast<_Float16*>(hw + (ok ? owh[r] : oxh));
+            _Float16* hp = reinterpret_cast<_Float16*>(hw + owh[r]);
             hp[0] = hh;
             hp[HP] = hl;
             bst(hv, rH, ok ? ph + vh[r] : kOOB);
