@@ -11,7 +11,9 @@ weight and input gradients. The metric counts real cell-direction updates only:
 Also reported: per-kernel-group times from HIP events recorded by the library
 on the bench stream over the timed steps; the roofline of the dominant kernel;
 the host packer's time; the same images laid out as a minimal-padding stack
-(batch padding) and timed the same way; and the CPU oracle on a bounded sample.
+(batch padding) and timed the same way; the other image batch of the pages'
+comparison (line-like next to word-like, and the reverse), packed, for context;
+and the CPU oracle on a bounded sample.
 """
 
 from __future__ import annotations
@@ -44,6 +46,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the line-like (or word-like) companion run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB on the device (counter calibration under rocprofv3 --pmc)")
@@ -303,6 +306,26 @@ def main():
                              "200 packed (No Padding Please, Table IV)",
         }
         del padded
+
+    # the other image batch of the pages' comparison, timed the same way (packed), for context
+    other = {"word": "line", "line": "word"}.get(wl.name)
+    if other and not args.no_other:
+        wo = make_workload(other, args.seed)
+        No = int(np.sum(wo.heights.astype(np.int64) * wo.widths))
+        ro = Runner(wo, "packed", device, stream)
+        oms, ok = ro.time(max(5, args.steps // 2), 2)
+        oi = ro.dl.info
+        orects, _ = M.mdl_layout_rects(ro.dl.layout)
+        omodel = kernel_model(oi, orects, wo.C, wo.H, 2 if wo.x_dtype == "bf16" else 4)
+        out["other_workload"] = {
+            "workload": f"{wo.name}: {wo.n} images, C={wo.C}, H={wo.H}, seed {wo.seed}, canvas "
+                        f"{oi['canvas_h']}x{oi['canvas_w']}, x {wo.x_dtype}",
+            "value": 4 * No / (oms * 1e-3), "unit": "cell-direction updates/s", "ms_per_step": oms,
+            "max_depth": oi["max_depth"], "kernels_ms": {k: round(v, 5) for k, v in ok.items()},
+            "kernels_roofline": {k: {"bound": r["bound"], "frac": r["frac"]}
+                                 for k, r in ((k, roofline(k, v, omodel)) for k, v in ok.items() if k in omodel)},
+        }
+        del ro
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
