@@ -32,19 +32,20 @@ __device__ inline void bst(float v, __amdgpu_buffer_rsrc_t r, int off) {
 }
 
 // Gate nonlinearities on the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32,
-// about 1 ulp each). sigmoid(z) = 1 / (1 + e^-z); tanh(x) = (1 - e^-2|x|) / (1 + e^-2|x|)
-// with the sign of x, and for |x| < 1/8 its odd Taylor polynomial to x^9, so that
-// tanh keeps its relative accuracy near 0 instead of losing it to cancellation.
+// about 1 ulp each). sigmoid(z) = 1 / (1 + e^-z). tanh(x) = 2 / (1 + e^-2x) - 1 for
+// |x| >= 1/8 (absolute error about 1e-7, relative below 1e-6 there; finite for any x),
+// and below 1/8 its odd Taylor polynomial to x^7 (truncation below 2e-9 relative), so
+// that tanh keeps its relative accuracy near 0 instead of losing it to cancellation.
+// Both branches are computed and one is selected: no divergence.
 __device__ inline float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 __device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ inline float sigm(float z) { return frcp(1.0f + fexp(-z)); }
 __device__ inline float ftanh(float x) {
-    const float ax = fabsf(x);
-    const float e = fexp(-2.0f * ax);
-    const float big = (1.0f - e) * frcp(1.0f + e);
+    const float big = __builtin_fmaf(2.0f, frcp(1.0f + fexp(-2.0f * x)), -1.0f);
     const float x2 = x * x;
-    const float small = ax * (1.0f + x2 * (-1.0f / 3.0f + x2 * (2.0f / 15.0f + x2 * (-17.0f / 315.0f + x2 * (62.0f / 2835.0f)))));
-    return copysignf(ax < 0.125f ? small : big, x);
+    const float p = __builtin_fmaf(x2, __builtin_fmaf(x2, -17.0f / 315.0f, 2.0f / 15.0f), -1.0f / 3.0f);
+    const float small = __builtin_fmaf(x * x2, p, x);
+    return fabsf(x) < 0.125f ? small : big;
 }
 
 // fp32 value -> f16 pair (hi, lo) with hi + lo equal to v to about 2^-22 relative,
