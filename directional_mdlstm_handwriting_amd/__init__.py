@@ -66,6 +66,7 @@ _SIGS = [
     ("mdl_blockconv_backward", _I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ,
                                       _P]),
     ("mdl_timing", _I32, [_I32]),
+    ("mdl_timing_only", _I32, [ctypes.c_char_p]),
     ("mdl_timing_report", _I32, [_I32, _P, _P, _P, ctypes.POINTER(_I32)]),
     ("mdl_last_error", ctypes.c_char_p, []),
 ]
@@ -247,6 +248,10 @@ def mdl_blockconv_backward(lk: Layout, d_desc_k, lk1: Layout, d_desc_k1, h_dirs_
 
 def mdl_timing(enable: bool):
     _check(_lib.mdl_timing(1 if enable else 0))
+
+
+def mdl_timing_only(group=None):
+    _check(_lib.mdl_timing_only(group.encode() if group else None))
 
 
 def mdl_timing_report(max_groups: int = 32):

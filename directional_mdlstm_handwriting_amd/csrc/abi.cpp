@@ -15,6 +15,10 @@
 #include "kernels.h"
 #include "layout.h"
 
+namespace mdl {
+thread_local LaunchClock* t_launch_clock = nullptr;
+}  // namespace mdl
+
 namespace {
 
 thread_local std::string g_err;
@@ -78,9 +82,10 @@ int check_layer(const char* fn, const mdl_layout* layout, const void* d_desc, in
 // ---- optional per-launch event timing ---------------------------------------------------------
 struct TimedLaunch {
     std::string name;
-    hipEvent_t start, stop;
+    std::vector<hipEvent_t> ev;  // start, stop of each dispatch of the group, in launch order
 };
 bool g_timing = false;
+std::string g_timing_only;  // empty: every group
 std::mutex g_tmu;
 std::vector<TimedLaunch> g_tlog;
 std::vector<hipEvent_t> g_event_pool;
@@ -96,28 +101,43 @@ hipEvent_t take_event() {
     return e;
 }
 
-// records an event pair around one launcher call when timing is on
-class Timed {
+// While timing is on, installs itself as the thread's launch clock for one launcher call: each dispatch
+// gets a start/stop event pair recorded by the dispatch itself, and the group's time runs from the first
+// dispatch's start to the last one's stop.
+class Timed : public mdl::LaunchClock {
   public:
-    Timed(const char* name, hipStream_t st) : st_(st) {
-        if (!g_timing) return;
-        std::lock_guard<std::mutex> lk(g_tmu);
-        a_ = take_event();
-        b_ = take_event();
-        name_ = name;
-        if (a_ && b_) hipEventRecord(a_, st_);
+    explicit Timed(const char* name) : name_(name) {
+        if (!g_timing || (!g_timing_only.empty() && g_timing_only != name)) return;
+        prev_ = mdl::t_launch_clock;
+        mdl::t_launch_clock = this;
+        on_ = true;
     }
-    ~Timed() {
-        if (!a_ || !b_) return;
-        hipEventRecord(b_, st_);
+    ~Timed() override {
+        if (!on_) return;
+        mdl::t_launch_clock = prev_;
+        if (ev_.empty()) return;
         std::lock_guard<std::mutex> lk(g_tmu);
-        g_tlog.push_back({name_, a_, b_});
+        g_tlog.push_back({name_, std::move(ev_)});
+    }
+    void events(hipEvent_t* start, hipEvent_t* stop) override {
+        std::lock_guard<std::mutex> lk(g_tmu);
+        hipEvent_t a = take_event(), b = take_event();
+        if (!a || !b) {
+            if (a) g_event_pool.push_back(a);
+            if (b) g_event_pool.push_back(b);
+            return;
+        }
+        ev_.push_back(a);
+        ev_.push_back(b);
+        *start = a;
+        *stop = b;
     }
 
   private:
-    hipStream_t st_;
-    hipEvent_t a_ = nullptr, b_ = nullptr;
-    const char* name_ = nullptr;
+    const char* name_;
+    bool on_ = false;
+    mdl::LaunchClock* prev_ = nullptr;
+    std::vector<hipEvent_t> ev_;
 };
 
 #define GUARD_BEGIN try {
@@ -212,7 +232,7 @@ int mdl_layout_upload(const mdl_layout* layout, void* d_desc, size_t bytes, void
     hipError_t e = hipMemcpyAsync(d_desc, L.host_desc.data(), L.host_desc.size(), hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "mdl_layout_upload: copy");
     {
-        Timed t("build_maps", st);
+        Timed t("build_maps");
         e = mdl::launch_build_maps(make_dev(layout, d_desc), st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_layout_upload: map kernels");
@@ -237,7 +257,7 @@ int mdl_scatter(const mdl_layout* layout, const void* d_desc, const void* x_flat
     if (!x_flat || !x_canvas) return fail(MDL_EINVAL, "mdl_scatter: null tensor");
     hipError_t e;
     {
-        Timed t("scatter", static_cast<hipStream_t>(stream));
+        Timed t("scatter");
         e = mdl::launch_scatter(make_dev(layout, d_desc), x_flat, C, dtype, x_canvas, static_cast<hipStream_t>(stream));
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_scatter");
@@ -291,20 +311,20 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     float* stash = reinterpret_cast<float*>(wsb + W.stash);
     hipError_t e;
     {
-        Timed t("zero_fill", st);
+        Timed t("zero_fill");
         e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_forward: zero fill");
     if (fused) {
-        Timed t("fwd_wavefront", st);
+        Timed t("fwd_wavefront");
         e = mdl::launch_fwd16(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, stash, h_dirs, st);
     } else {
         {
-            Timed t("projection", st);
+            Timed t("projection");
             e = mdl::launch_projection(D, x_canvas, x_dtype, C, H, Wx, b, Z, st);
         }
         if (e != hipSuccess) return hip_fail(e, "mdl_forward: projection");
-        Timed t("fwd_wavefront", st);
+        Timed t("fwd_wavefront");
         e = mdl::launch_fwd_chain(D, H, Ul, Uu, Z, stash, h_dirs, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_forward: wavefront");
@@ -320,7 +340,7 @@ int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float*
     if (!h_dirs || !y_flat) return fail(MDL_EINVAL, "mdl_dirsum_unpack: null tensor");
     hipError_t e;
     {
-        Timed t("dirsum", static_cast<hipStream_t>(stream));
+        Timed t("dirsum");
         e = mdl::launch_dirsum(make_dev(layout, d_desc), h_dirs, H, y_flat, static_cast<hipStream_t>(stream));
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_dirsum_unpack");
@@ -363,17 +383,17 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     float* part = reinterpret_cast<float*>(wsb + W.part);
     hipError_t e;
     {
-        Timed t("bwd_wavefront", st);
+        Timed t("bwd_wavefront");
         e = mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward: reverse wavefront");
     if (dx_canvas) {
-        Timed t("zero_fill", st);
+        Timed t("zero_fill");
         e = mdl::launch_zero_outside(D, dx_canvas, C, 1, st);
         if (e != hipSuccess) return hip_fail(e, "mdl_backward: zero fill");
     }
     {
-        Timed t("wgrad", st);
+        Timed t("wgrad");
         e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dWx, dUl, dUu, db, dx_flat, dx_canvas,
                               st);
     }
@@ -406,7 +426,7 @@ int mdl_blockconv_forward(const mdl_layout* lk, const void* d_desc_k, const mdl_
     if (!h_dirs_k || !Wc || !bc || !x_canvas_k1) return fail(MDL_EINVAL, "mdl_blockconv_forward: null tensor");
     hipError_t e;
     {
-        Timed t("conv_fwd", static_cast<hipStream_t>(stream));
+        Timed t("conv_fwd");
         e = mdl::launch_conv_fwd(make_dev(lk, d_desc_k), make_dev(lk1, d_desc_k1), h_dirs_k, H, kh, kw, Wc, bc, Cout,
                                  x_canvas_k1, static_cast<hipStream_t>(stream));
     }
@@ -447,7 +467,7 @@ int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl
         return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: weight-gradient tile exceeds LDS");
     hipError_t e;
     {
-        Timed t("conv_bwd", static_cast<hipStream_t>(stream));
+        Timed t("conv_bwd");
         e = mdl::launch_conv_bwd(make_dev(lk, d_desc_k), make_dev(lk1, d_desc_k1), h_dirs_k, H, kh, kw, Wc, Cout,
                                  dx_canvas_k1, dh_dirs_k, dWc, dbc, static_cast<float*>(ws),
                                  static_cast<hipStream_t>(stream));
@@ -463,6 +483,13 @@ int mdl_timing(int32_t enable) {
     return MDL_OK;
 }
 
+int mdl_timing_only(const char* group) {
+    if (group && std::strlen(group) >= 32) return fail(MDL_EINVAL, "mdl_timing_only: group name too long");
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing_only = group ? group : "";
+    return MDL_OK;
+}
+
 int mdl_timing_report(int32_t max, char* names, double* total_ms, int64_t* launches, int32_t* count) {
     GUARD_BEGIN
     if (max < 0 || !count || (max > 0 && (!names || !total_ms || !launches)))
@@ -473,14 +500,13 @@ int mdl_timing_report(int32_t max, char* names, double* total_ms, int64_t* launc
     int rc = MDL_OK;
     for (auto& t : g_tlog) {
         float ms = 0.f;
-        hipError_t e = hipEventSynchronize(t.stop);
-        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.start, t.stop);
+        hipError_t e = hipEventSynchronize(t.ev.back());
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.ev.front(), t.ev.back());
         if (e != hipSuccess && rc == MDL_OK) rc = hip_fail(e, "mdl_timing_report");
         if (!acc.count(t.name)) order.push_back(t.name);
         acc[t.name].first += ms;
         acc[t.name].second += 1;
-        g_event_pool.push_back(t.start);
-        g_event_pool.push_back(t.stop);
+        for (hipEvent_t ev : t.ev) g_event_pool.push_back(ev);
     }
     g_tlog.clear();
     int k = 0;

@@ -467,7 +467,7 @@ hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, c
     const B16Entry* m = b16_entry(H, D.max_diag);
     if (!m) return hipErrorInvalidValue;
     const B16Shape2* sh = b16_shape(*m, D.max_diag);
-    hipLaunchKernelGGL(sh->k, dim3(4 * D.n), dim3(sh->NT), b16_lds(*m), st, D, Ul, Uu, stash, dy_flat, dh_dirs, dA);
+    launch(sh->k, dim3(4 * D.n), dim3(sh->NT), b16_lds(*m), st, D, Ul, Uu, stash, dy_flat, dh_dirs, dA);
     return hipGetLastError();
 }
 

@@ -480,8 +480,8 @@ bool chain_uses_mfma(int H, int Lmax) { return mfma_entry(H, Lmax) != nullptr; }
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
                             float* h_dirs, hipStream_t st) {
     const int Lmax = D.max_diag;
-    hipLaunchKernelGGL(k_fwd_chain, dim3(4 * D.n), dim3(CHAIN_THREADS), fwd_chain_lds(H, Lmax), st, D, H, Lmax, Ul,
-                       Uu, Z, stash, h_dirs);
+    launch(k_fwd_chain, dim3(4 * D.n), dim3(CHAIN_THREADS), fwd_chain_lds(H, Lmax), st, D, H, Lmax, Ul,
+           Uu, Z, stash, h_dirs);
     return hipGetLastError();
 }
 
@@ -490,12 +490,12 @@ hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* U
     const int Lmax = D.max_diag;
     if (bwd16_supported(H, Lmax)) return launch_bwd16(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     if (const MfmaEntry* m = mfma_entry(H, Lmax)) {
-        hipLaunchKernelGGL(m->bwd, dim3(4 * D.n), dim3(256), bwd_mfma_lds(H, Lmax), st, D, H, Lmax, Ul, Uu, stash,
-                           dy_flat, dh_dirs, dA);
+        launch(m->bwd, dim3(4 * D.n), dim3(256), bwd_mfma_lds(H, Lmax), st, D, H, Lmax, Ul, Uu, stash,
+               dy_flat, dh_dirs, dA);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_bwd_chain, dim3(4 * D.n), dim3(CHAIN_THREADS), bwd_chain_lds(H, Lmax), st, D, H, Lmax, Ul,
-                       Uu, stash, dy_flat, dh_dirs, dA);
+    launch(k_bwd_chain, dim3(4 * D.n), dim3(CHAIN_THREADS), bwd_chain_lds(H, Lmax), st, D, H, Lmax, Ul,
+           Uu, stash, dy_flat, dh_dirs, dA);
     return hipGetLastError();
 }
 

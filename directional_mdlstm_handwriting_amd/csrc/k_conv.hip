@@ -170,8 +170,8 @@ int64_t conv_nchunks(const Dev& Dk1) { return (Dk1.N + CONV_CHUNK - 1) / CONV_CH
 hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st) {
     const int64_t E = (int64_t)Dk1.Hc * Dk1.Wc * Cout;
-    hipLaunchKernelGGL(k_conv_fwd, dim3(grid_for(E)), dim3(256), 0, st, Dk, Dk1, h_dirs_k, H, kh, kw, Wc, bc, Cout,
-                       x_k1);
+    launch(k_conv_fwd, dim3(grid_for(E)), dim3(256), 0, st, Dk, Dk1, h_dirs_k, H, kh, kw, Wc, bc, Cout,
+           x_k1);
     return hipGetLastError();
 }
 
@@ -179,19 +179,19 @@ hipError_t launch_conv_bwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k,
                            const float* Wc, int Cout, const float* dx_k1, float* dh_k, float* dWc, float* dbc,
                            float* part, hipStream_t st) {
     const int64_t E = 4 * (int64_t)Dk.Hc * Dk.Wc * H;
-    hipLaunchKernelGGL(k_conv_bwd_data, dim3(grid_for(E)), dim3(256), 0, st, Dk, Dk1, H, kh, kw, Wc, Cout, dx_k1,
-                       dh_k);
+    launch(k_conv_bwd_data, dim3(grid_for(E)), dim3(256), 0, st, Dk, Dk1, H, kh, kw, Wc, Cout, dx_k1,
+           dh_k);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int K = 4 * H * kh * kw;
     const int64_t nch = conv_nchunks(Dk1);
     const size_t lds = sizeof(float) * (size_t)CW_TILE * (K + Cout);
-    hipLaunchKernelGGL(k_conv_wpartial, dim3((unsigned)nch), dim3(CW_THREADS), lds, st, Dk, Dk1, h_dirs_k, H, kh, kw,
-                       Cout, dx_k1, part);
+    launch(k_conv_wpartial, dim3((unsigned)nch), dim3(CW_THREADS), lds, st, Dk, Dk1, h_dirs_k, H, kh, kw,
+           Cout, dx_k1, part);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int Ew = Cout * (K + 1);
-    hipLaunchKernelGGL(k_conv_wreduce, dim3((Ew + 255) / 256), dim3(256), 0, st, part, nch, K, Cout, dWc, dbc);
+    launch(k_conv_wreduce, dim3((Ew + 255) / 256), dim3(256), 0, st, part, nch, K, Cout, dWc, dbc);
     return hipGetLastError();
 }
 

@@ -387,8 +387,8 @@ hipError_t launch_fwd16(const Dev& D, const void* x_canvas, int dtype, int C, in
     if (!m) return hipErrorInvalidValue;
     const int cells = (D.max_diag + m->CG - 1) / m->CG;  // widest diagonal's cells per group, <= 16
     const int nr = (cells + 3) / 4;
-    hipLaunchKernelGGL(m->fwd[nr - 1], dim3(4 * D.n), dim3(64 * m->NB * m->CG), f16_lds(*m), st, D, x_canvas, C, Wx,
-                       b, Ul, Uu, stash, h_dirs);
+    launch(m->fwd[nr - 1], dim3(4 * D.n), dim3(64 * m->NB * m->CG), f16_lds(*m), st, D, x_canvas, C, Wx,
+           b, Ul, Uu, stash, h_dirs);
     return hipGetLastError();
 }
 

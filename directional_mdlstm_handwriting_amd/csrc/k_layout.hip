@@ -105,35 +105,35 @@ __global__ void k_zero_outside(Dev D, float* __restrict__ buf, int K, int planes
 
 hipError_t launch_zero_outside(const Dev& D, float* buf, int K, int planes, hipStream_t st) {
     const int64_t E = (int64_t)D.Hc * D.Wc * K;
-    hipLaunchKernelGGL(k_zero_outside, dim3(grid_for(E)), dim3(TPB), 0, st, D, buf, K, planes);
+    launch(k_zero_outside, dim3(grid_for(E)), dim3(TPB), 0, st, D, buf, K, planes);
     return hipGetLastError();
 }
 
 hipError_t launch_build_maps(const Dev& D, hipStream_t st) {
     const int64_t P = (int64_t)D.Hc * D.Wc;
-    hipLaunchKernelGGL(k_fill_eid, dim3(grid_for(P)), dim3(TPB), 0, st, D.eid, P);
+    launch(k_fill_eid, dim3(grid_for(P)), dim3(TPB), 0, st, D.eid, P);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_paint_eid, dim3(64, D.n), dim3(TPB), 0, st, D);
+    launch(k_paint_eid, dim3(64, D.n), dim3(TPB), 0, st, D);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_border, dim3(grid_for(P)), dim3(TPB), 0, st, D);
+    launch(k_border, dim3(grid_for(P)), dim3(TPB), 0, st, D);
     return hipGetLastError();
 }
 
 hipError_t launch_scatter(const Dev& D, const void* x_flat, int C, int dtype, void* x_canvas, hipStream_t st) {
     const int64_t E = (int64_t)D.Hc * D.Wc * C;
     if (dtype == 0)
-        hipLaunchKernelGGL(k_scatter<float>, dim3(grid_for(E)), dim3(TPB), 0, st, D,
-                           (const float*)x_flat, C, (float*)x_canvas);
+        launch(k_scatter<float>, dim3(grid_for(E)), dim3(TPB), 0, st, D,
+               (const float*)x_flat, C, (float*)x_canvas);
     else
-        hipLaunchKernelGGL(k_scatter<uint16_t>, dim3(grid_for(E)), dim3(TPB), 0, st, D,
-                           (const uint16_t*)x_flat, C, (uint16_t*)x_canvas);
+        launch(k_scatter<uint16_t>, dim3(grid_for(E)), dim3(TPB), 0, st, D,
+               (const uint16_t*)x_flat, C, (uint16_t*)x_canvas);
     return hipGetLastError();
 }
 
 hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st) {
-    hipLaunchKernelGGL(k_dirsum, dim3(64, D.n), dim3(TPB), 0, st, D, h_dirs, H, y_flat);
+    launch(k_dirsum, dim3(64, D.n), dim3(TPB), 0, st, D, h_dirs, H, y_flat);
     return hipGetLastError();
 }
 

@@ -106,10 +106,10 @@ hipError_t launch_projection(const Dev& D, const void* x_canvas, int dtype, int 
     const int64_t waves = (D.T + 15) / 16;
     const unsigned blocks = (unsigned)((waves + 3) / 4);
     if (dtype == 0)
-        hipLaunchKernelGGL(k_proj<float>, dim3(blocks), dim3(256), 0, st, D, (const float*)x_canvas, C, H, Wx, b, Z);
+        launch(k_proj<float>, dim3(blocks), dim3(256), 0, st, D, (const float*)x_canvas, C, H, Wx, b, Z);
     else
-        hipLaunchKernelGGL(k_proj<uint16_t>, dim3(blocks), dim3(256), 0, st, D, (const uint16_t*)x_canvas, C, H,
-                           Wx, b, Z);
+        launch(k_proj<uint16_t>, dim3(blocks), dim3(256), 0, st, D, (const uint16_t*)x_canvas, C, H,
+               Wx, b, Z);
     return hipGetLastError();
 }
 

@@ -390,14 +390,14 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
     if (wgrad2_supported(C, H, dtype)) {
         hipError_t err = launch_wgrad2(D, x_canvas, dtype, C, H, h_dirs, dA, Wx, part, dx_flat, dx_canvas, st);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st,
-                           part, D.nchunks, C, H, dWx, dUl, dUu, db);
+        launch(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st,
+               part, D.nchunks, C, H, dWx, dUl, dUu, db);
         return hipGetLastError();
     }
     const size_t lds = sizeof(float) * wgrad_lds_floats(s);
     const dim3 grid((unsigned)D.nchunks), block(256);
-#define MDL_WG(B, CT, HT) hipLaunchKernelGGL((k_wgrad_mfma<B, CT, HT>), grid, block, lds, st, D, x_canvas, s, h_dirs, \
-                                             dA, Wx, part, dx_flat, dx_canvas)
+#define MDL_WG(B, CT, HT) launch((k_wgrad_mfma<B, CT, HT>), grid, block, lds, st, D, x_canvas, s, h_dirs, \
+                                 dA, Wx, part, dx_flat, dx_canvas)
     const bool bf = dtype != 0;
     if (!bf && C == 4 && H == 16) MDL_WG(false, 4, 16);
     else if (!bf && C == 1 && H == 4) MDL_WG(false, 1, 4);
@@ -411,8 +411,8 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
 #undef MDL_WG
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st, part,
-                       D.nchunks, C, H, dWx, dUl, dUu, db);
+    launch(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st, part,
+           D.nchunks, C, H, dWx, dUl, dUu, db);
     return hipGetLastError();
 }
 

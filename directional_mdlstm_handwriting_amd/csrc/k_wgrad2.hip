@@ -373,8 +373,8 @@ hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, i
                          hipStream_t st) {
     const Wg2Entry* m = wg2_entry(C, H, dtype != 0);
     if (!m) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(m->k, dim3((unsigned)D.nchunks), dim3(m->threads), m->lds, st, D, x_canvas, h_dirs, dA, Wx,
-                       part, dx_flat, dx_canvas);
+    launch(m->k, dim3((unsigned)D.nchunks), dim3(m->threads), m->lds, st, D, x_canvas, h_dirs, dA, Wx,
+           part, dx_flat, dx_canvas);
     return hipGetLastError();
 }
 

@@ -4,10 +4,41 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <tuple>
+#include <utility>
 
 #include "layout.h"
 
 namespace mdl {
+
+// Launch timing. While a clock is installed on the calling thread, every
+// launch below hands the dispatch a pair of events that record its own start
+// and end (hipExtLaunchKernel), so timing inserts no marker packets between
+// kernels and the elapsed time is the kernel's alone.
+struct LaunchClock {
+    virtual ~LaunchClock() = default;
+    virtual void events(hipEvent_t* start, hipEvent_t* stop) = 0;
+};
+extern thread_local LaunchClock* t_launch_clock;
+
+// Launches `kernel` with its arguments converted to the kernel's own
+// parameter types; the launch status is left for hipGetLastError.
+template <typename... P, typename... A>
+inline void launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t st, A&&... args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> vals(static_cast<P>(std::forward<A>(args))...);
+    std::apply(
+        [&](auto&... v) {
+            void* argv[] = {static_cast<void*>(&v)...};
+            hipEvent_t a = nullptr, b = nullptr;
+            if (t_launch_clock) t_launch_clock->events(&a, &b);
+            if (a && b)
+                (void)hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, st, a, b, 0);
+            else
+                (void)hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, st);
+        },
+        vals);
+}
 
 // Pointers into an uploaded descriptor plus the sizes the kernels need.
 struct Dev {

@@ -245,16 +245,23 @@ int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl
 
 /*
  * Kernel timing (measurement support). mdl_timing(1) makes every later launch
- * record a HIP event pair on its stream around each kernel group (names:
- * "build_maps", "scatter", "zero_fill", "projection", "fwd_wavefront", "dirsum",
- * "bwd_wavefront", "wgrad", "dx", "conv_fwd", "conv_bwd"); mdl_timing(0) stops
- * recording. mdl_timing_report synchronizes the recorded events and writes, for
- * up to `max` kernel groups, the name (NUL-terminated, 32 bytes per entry in
- * `names`), the summed milliseconds and the launch count; *count receives the
- * number of groups; the records are then cleared. Process-wide, not meant for
- * concurrent use from several threads.
+ * of a kernel group (names: "build_maps", "scatter", "zero_fill", "projection",
+ * "fwd_wavefront", "dirsum", "bwd_wavefront", "wgrad", "conv_fwd", "conv_bwd")
+ * hand each of its dispatches a HIP event pair that the dispatch itself
+ * records (hipExtLaunchKernel): the group's time runs from its first
+ * dispatch's start to its last one's end, with no marker packets between
+ * kernels. mdl_timing(0) stops recording. mdl_timing_only(name) limits the
+ * recording to one group (NULL or "" restores all groups); every recorded
+ * dispatch still costs the stream a few microseconds, so a throughput
+ * measurement times only the group it needs. mdl_timing_report synchronizes
+ * the recorded events and writes, for up to `max` kernel groups, the name
+ * (NUL-terminated, 32 bytes per entry in `names`), the summed milliseconds and
+ * the launch count; *count receives the number of groups; the records are then
+ * cleared. Process-wide, not meant for concurrent use from several threads.
+ * Errors: MDL_EINVAL for bad arguments or a name of 32 bytes or more.
  */
 int mdl_timing(int32_t enable);
+int mdl_timing_only(const char* group);
 int mdl_timing_report(int32_t max, char* names, double* total_ms, int64_t* launches, int32_t* count);
 
 /* Message of the last failed call on this thread ("" if none). */
