@@ -43,7 +43,8 @@ mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     D.flat_off = reinterpret_cast<const int64_t*>(b + L.off.flat_off);
     D.cell_off = reinterpret_cast<const int64_t*>(b + L.off.cell_off);
     D.units = reinterpret_cast<const int32_t*>(b + L.off.units);
-    D.chunks = reinterpret_cast<const int32_t*>(b + L.off.chunks);
+    D.segs = reinterpret_cast<const int32_t*>(b + L.off.segs);
+    D.groups = reinterpret_cast<const int32_t*>(b + L.off.groups);
     D.eid = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(b + L.off.eid));
     D.border = const_cast<uint8_t*>(b + L.off.border);
     D.n = L.n;
@@ -53,7 +54,8 @@ mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     D.N = L.real_pixels;
     D.max_depth = L.max_depth;
     D.max_diag = L.max_diag;
-    D.nchunks = L.nchunks;
+    D.nsegs = L.nsegs;
+    D.ngroups = L.ngroups;
     return D;
 }
 
@@ -245,7 +247,7 @@ int mdl_layout_upload(const mdl_layout* layout, void* d_desc, size_t bytes, void
 int mdl_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes) {
     if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_workspace_size: null argument");
     if (C < 1 || H < 1) return fail(MDL_EINVAL, "mdl_workspace_size: need C >= 1 and H >= 1");
-    *bytes = mdl::ws_layout(L_of(layout).computed_cells, L_of(layout).nchunks, C, H).total;
+    *bytes = mdl::ws_layout(L_of(layout).computed_cells, L_of(layout).nparts(), C, H).total;
     return MDL_OK;
 }
 
@@ -294,7 +296,7 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     if (rc) return rc;
     if (!x_canvas || !Wx || !Ul || !Uu || !b || !h_dirs || !ws) return fail(MDL_EINVAL, "mdl_forward: null tensor");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nchunks, C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
     if ((rc = check_extent("mdl_forward", L, C, H, x_dtype, false, false))) return rc;
     const bool fused = mdl::fwd16_supported(H, C, x_dtype, L.max_diag);
@@ -360,7 +362,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     if ((dy_flat == nullptr) == (dh_dirs == nullptr))
         return fail(MDL_EINVAL, "mdl_backward: pass exactly one of dy_flat and dh_dirs");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nchunks, C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_backward: workspace smaller than mdl_workspace_size");
     if (!mdl::bwd16_supported(H, L.max_diag) && !mdl::chain_uses_mfma(H, L.max_diag) &&
         (int64_t)L.max_diag * H > mdl::chain_max_items())

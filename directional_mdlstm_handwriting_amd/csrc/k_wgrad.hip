@@ -8,28 +8,29 @@
 // and its gate gradient da_d(p) (5H values):
 //     [dWx; db; dUl; dUu][d] = sum over computed cells p of r(p)^T da_d(p)
 //     dx(p)                  = sum over d of da_d(p) Wx[d]^T
-// One workgroup takes one chunk of rows of one example (the layout's chunk
-// table) for all four directions: it stages tiles of TP cells of A-rows and
-// gate gradients in LDS, accumulates r^T da on the matrix cores
-// (v_mfma_f32_16x16x4_f32, K = cells, fp32 products and sums; wave d owns
-// direction d's output tiles, up to 32 per pass over the chunk), and computes
-// dx of the same cells from the staged gate gradients. Chunk partial sums are then added in
-// chunk order by a second kernel, so the result is bit-reproducible.
+// One workgroup takes one segment of the layout's weight-gradient split (a
+// range of cells of one example) for all four directions: it stages tiles of
+// TP cells of A-rows and gate gradients in LDS, accumulates r^T da on the
+// matrix cores (v_mfma_f32_16x16x4_f32, K = cells, fp32 products and sums;
+// wave d owns direction d's output tiles, up to 32 per pass over the segment),
+// and computes dx of the same cells from the staged gate gradients. Segment
+// partial sums are then added in segment order by a second kernel, so the
+// result is bit-reproducible.
 #include "kernels.h"
 #include "devmath.h"
 
 namespace mdl {
 
-WsLayout ws_layout(int64_t T, int64_t nchunks, int C, int H) {
+WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H) {
     auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
     WsLayout w;
     const int G = 5 * H;
     const int R = C + 1 + 2 * H;
-    w.nchunks = nchunks;
+    w.nparts = nparts;
     size_t p = 0;
     w.stash = p; p = al(p + sizeof(float) * 4 * (size_t)T * 6 * H);
     w.zda = p;   p = al(p + sizeof(float) * 4 * (size_t)T * G);
-    w.part = p;  p = al(p + sizeof(float) * 4 * (size_t)nchunks * R * G);
+    w.part = p;  p = al(p + sizeof(float) * 4 * (size_t)nparts * R * G);
     w.total = p;
     return w;
 }
@@ -47,7 +48,7 @@ __host__ __device__ inline uint32_t magic(uint32_t d) { return (uint32_t)(0xffff
 __device__ inline int fdiv(int n, uint32_t m) { return (int)__umulhi((uint32_t)n, m); }
 
 struct WgradShape {
-    int C, H, G, R, MT, NT, Q, P, TP;  // Q N-tiles per pass, P passes over the chunk, TP cells per tile
+    int C, H, G, R, MT, NT, Q, P, TP;  // Q N-tiles per pass, P passes over the segment, TP cells per tile
     int nh, nd, nx;                  // staged elements per tile: predecessor h, gate gradients, x
     uint32_t m_hd, m_h2, m_gd, m_g, m_x;
     int wx_lds;                      // Wx copied to LDS
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
     const int MT = (R + 15) / 16, NT = (G + 15) / 16;
     const int TP = S.TP;
     const int ch = blockIdx.x;
-    const int e = D.chunks[3 * ch], r0 = D.chunks[3 * ch + 1], r1 = D.chunks[3 * ch + 2];
+    const int e = D.segs[3 * ch], c0 = D.segs[3 * ch + 1], c1 = D.segs[3 * ch + 2];
     const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
     const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
     const int tid = threadIdx.x;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
     float* zero = dxs + 4 * TP * C;                // one 0.0f
     __shared__ int t_pix[32], t_flat[32], t_cst[4][32], t_flags[32];
     if (tid == 0) zero[0] = 0.f;
-    // dx B fragments: Wx[d][c][n] as B[n = 4ks + krow][c = l16]; kept in registers for the whole chunk
+    // dx B fragments: Wx[d][c][n] as B[n = 4ks + krow][c = l16]; kept in registers for the whole segment
     // when the shape is fixed at compile time with C <= 16, else loaded per use
     constexpr bool PRE = CT > 0 && CT <= 16 && HT > 0;
     constexpr int KX = HT > 0 ? (5 * HT + 3) / 4 : 64;
@@ -136,10 +137,10 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
     const uint16_t* xb = static_cast<const uint16_t*>(xc);
     const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs, 4 * (int64_t)plane * 4);
     const __amdgpu_buffer_rsrc_t rA = rsrc(dA, 4 * D.T * G * 4);
-    const int ncell = (r1 - r0) * w;
+    const int ncell = c1 - c0;
     const int cell0 = (int)D.cell_off[e];
 
-    // passes over the chunk: all MT M-tiles times NQ N-tiles at a time
+    // passes over the segment: all MT M-tiles times NQ N-tiles at a time
     constexpr int MTC = HT > 0 ? (CT + 1 + 2 * HT + 15) / 16 : 16;                 // M-tile bound
     constexpr int NQC = HT > 0 ? (ACC_TILES / MTC < (5 * HT + 15) / 16 ? ACC_TILES / MTC : (5 * HT + 15) / 16)
                                : ACC_TILES;                                        // N-tiles per pass bound
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
                 int pix = -1, flat = -1, flags = 0;
                 int cst[4] = {-1, -1, -1, -1};
                 if (q < ncell) {
-                    const int ly = r0 + q / w, lx = q - (q / w) * w;
+                    const int ly = (c0 + q) / w, lx = c0 + q - ly * w;
                     pix = (y0 + ly) * D.Wc + x0 + lx;
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
             }
             __syncthreads();
         }
-        // partial sums of this chunk: part[chunk][d][R][G]
+        // partial sums of this segment: part[segment][d][R][G]
         float* out = part + ((int64_t)ch * 4 + wd) * R * G;
         auto store_tile = [&](int mt, int j, const f32x4& a) {
             const int col = (nbase + j) * 16 + l16;
@@ -335,12 +336,12 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
 
 namespace {
 
-// Chunk partials summed in a fixed order, then routed to dWx / db / dUl / dUu. A workgroup takes 64
-// consecutive (direction, entry) slots (coalesced reads of each chunk's partial row) and 8 slices of the
-// chunks: slice j adds chunks j, j + 8, j + 16, ... in order, and the 8 slice sums are added in slice
-// order through LDS. The order depends only on the chunk count, so reruns are bit-identical.
+// Partial blocks summed in a fixed order, then routed to dWx / db / dUl / dUu. A workgroup takes 64
+// consecutive (direction, entry) slots (coalesced reads of each block's partial row) and 8 slices of the
+// blocks: slice j adds blocks j, j + 8, j + 16, ... in order, and the 8 slice sums are added in slice
+// order through LDS. The order depends only on the block count, so reruns are bit-identical.
 constexpr int RED_X = 64, RED_Y = 8;
-__global__ __launch_bounds__(RED_X* RED_Y) void k_wgrad_reduce(const float* __restrict__ part, int nchunks, int C,
+__global__ __launch_bounds__(RED_X* RED_Y) void k_wgrad_reduce(const float* __restrict__ part, int nparts, int C,
                                                                int H, float* __restrict__ dWx,
                                                                float* __restrict__ dUl, float* __restrict__ dUu,
                                                                float* __restrict__ db) {
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(RED_X* RED_Y) void k_wgrad_reduce(const float* __re
         const float* p = part + id;
         float s4[4] = {0.f, 0.f, 0.f, 0.f};
         int c = ty, j = 0;
-        for (; c < nchunks; c += RED_Y, j = (j + 1) & 3) s4[j] += p[(int64_t)c * stride];
+        for (; c < nparts; c += RED_Y, j = (j + 1) & 3) s4[j] += p[(int64_t)c * stride];
         s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
     __shared__ float red[RED_Y][RED_X];
@@ -391,11 +392,11 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
         hipError_t err = launch_wgrad2(D, x_canvas, dtype, C, H, h_dirs, dA, Wx, part, dx_flat, dx_canvas, st);
         if (err != hipSuccess) return err;
         launch(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st,
-               part, D.nchunks, C, H, dWx, dUl, dUu, db);
+               part, D.ngroups, C, H, dWx, dUl, dUu, db);
         return hipGetLastError();
     }
     const size_t lds = sizeof(float) * wgrad_lds_floats(s);
-    const dim3 grid((unsigned)D.nchunks), block(256);
+    const dim3 grid((unsigned)D.nsegs), block(256);
 #define MDL_WG(B, CT, HT) launch((k_wgrad_mfma<B, CT, HT>), grid, block, lds, st, D, x_canvas, s, h_dirs, \
                                  dA, Wx, part, dx_flat, dx_canvas)
     const bool bf = dtype != 0;
@@ -412,7 +413,7 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     launch(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st, part,
-           D.nchunks, C, H, dWx, dUl, dUu, db);
+           D.nsegs, C, H, dWx, dUl, dUu, db);
     return hipGetLastError();
 }
 

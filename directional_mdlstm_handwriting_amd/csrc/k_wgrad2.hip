@@ -5,9 +5,10 @@
 // over the whole batch):
 //     [dWx; db; dUl; dUu][d] = sum over computed cells p of r(p)^T da_d(p),
 //     r(p) = [x(p), 1, h_left(p), h_up(p)],       dx(p) = sum over d of da_d(p) Wx[d]^T,
-// for shapes fixed at compile time. One workgroup takes one row chunk of an
-// example for all four directions, WPD waves per direction, and walks it in
-// tiles of TP cells. The global loads of tile t+1 (16-byte loads of the
+// for shapes fixed at compile time. One workgroup takes one group of the
+// layout's weight-gradient split (a few cell ranges of about the same total
+// size for every workgroup, so all compute units finish together) for all
+// four directions, WPD waves per direction, and walks it in tiles of TP cells. The global loads of tile t+1 (16-byte loads of the
 // predecessors' h and of the gate gradients in their [cell][k][4] layout)
 // are issued before tile t is computed from LDS, so their latency hides
 // behind the matrix-core work. Each thread stages a fixed share of one cell
@@ -21,7 +22,7 @@
 // takes a share of the gate-gradient columns of all four directions, the
 // directions are added across lanes, and the waves' shares in a fixed order.
 // LDS row strides are chosen so the fragment reads of a wave hit distinct banks.
-// Chunk partials are reduced in chunk order by k_wgrad_reduce (k_wgrad.hip).
+// The workgroups' partials are reduced in workgroup order by k_wgrad_reduce (k_wgrad.hip).
 #include "kernels.h"
 #include "devmath.h"
 
@@ -100,21 +101,32 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
     constexpr int TPC = S::TPC, NVH = S::NVH, NV1 = S::NV1, NHL = S::NHL, ND4 = S::ND4, ND1 = S::ND1, NXL = S::NXL;
     constexpr int XB = BF16 ? 2 : 4;
     typedef typename VecOf<VH>::T HV;
-    const int ch = blockIdx.x;
-    const int e = D.chunks[3 * ch], r0 = D.chunks[3 * ch + 1], r1 = D.chunks[3 * ch + 2];
-    const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
-    const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+    const int grp = blockIdx.x;
+    const int sg0 = D.groups[grp], nsg = D.groups[grp + 1] - sg0;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave descriptors
     const int d = wave / WPD, sub = wave % WPD;  // direction, share of its N tiles
     const int td = tid - d * NTH;                // thread index within the direction
     const int i16 = lane & 15, q = lane >> 4;
     const int nt0 = sub * NTW;
-    const int ncell = (r1 - r0) * w;
-    const int ntiles = (ncell + TP - 1) / TP;
-    const int cell0 = (int)D.cell_off[e];
-    const int flat0 = (int)D.flat_off[e];  // read once: a global load inside the loop would wait on the stores
     const int64_t plane = (int64_t)D.Hc * D.Wc * H;
+
+    // this workgroup's segments, read once into LDS (a global load inside the loop would wait on the
+    // stores): region y0, x0, h, w; real pixels y0, x0, h, w; stash and flat offsets; cell range
+    __shared__ int sgt[kGroupSegs][12];
+    if (tid < nsg) {
+        const int sg = sg0 + tid, e = D.segs[3 * sg];
+        int* o = sgt[tid];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[i] = D.rect[4 * e + i];
+            o[4 + i] = D.real[4 * e + i];
+        }
+        o[8] = (int)D.cell_off[e];
+        o[9] = (int)D.flat_off[e];
+        o[10] = D.segs[3 * sg + 1];
+        o[11] = D.segs[3 * sg + 2];
+    }
 
     // LDS: r rows [4][TP][RP], gate gradients [4][TP][DS] (units k: gates 0..3 at 4k + g, gate 4 at 4H + k),
     // dx shares of the waves [NWV][TP][C], and two slots of the tile's cell table (pixel, flat index) for
@@ -129,6 +141,8 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
     for (int i = tid; i < NWORDS; i += blockDim.x) reinterpret_cast<uint32_t*>(smem)[i] = 0u;
     __syncthreads();
     for (int i = tid; i < 4 * TP; i += blockDim.x) rs[i * RP + C] = 1.f;  // the bias row of r
+    int ntiles = 0;
+    for (int sg = 0; sg < nsg; ++sg) ntiles += (sgt[sg][11] - sgt[sg][10] + TP - 1) / TP;
 
     // loads: thread td of a direction stages cell lc = td / TPC of each tile, vectors pt, pt + TPC, ...
     const int lc = td / TPC, pt = td % TPC;
@@ -144,20 +158,24 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
     f32x4 vd4[ND4];
     HV vd1[ND1];
     float vx[NXL];
-    auto issue_loads = [&](int t, int slot) {
-        // this thread's cell: canvas pixel, predecessors in direction d, position in d's stash order
-        const int qc = t * TP + lc;
-        const bool ok = qc < ncell;
-        const int ly = r0 + qc / w, lx = qc - (qc / w) * w;
+    auto issue_loads = [&](int sg, int lt, int slot) {
+        // this thread's cell (tile lt of segment sg): canvas pixel, predecessors in direction d, position
+        // in d's stash order
+        const int* S = sgt[sg];
+        const int y0 = S[0], x0 = S[1], h = S[2], w = S[3];
+        const int cell0 = S[8];
+        const int qc = S[10] + lt * TP + lc;
+        const bool ok = qc < S[11];
+        const int ly = qc / w, lx = qc - ly * w;
         const int pix = ok ? (y0 + ly) * D.Wc + x0 + lx : -1;
         const bool lok = ok & ((d & 1) ? lx < w - 1 : lx > 0);  // left predecessor (y, x - sx)
         const bool uok = ok & ((d & 2) ? ly < h - 1 : ly > 0);  // upper predecessor (y - sy, x)
         const int srcl = pix + ((d & 1) ? 1 : -1), srcu = pix + ((d & 2) ? D.Wc : -D.Wc);
         const int cst = ok ? stash_pos(h, w, ly, lx, d) : 0;
         if (d == 0 && pt == 0) {  // the dx store's table
-            const int qy = y0 + ly - ry0, qx = x0 + lx - rx0;
+            const int qy = y0 + ly - S[4], qx = x0 + lx - S[5];
             tpix[slot * TP + lc] = pix;
-            tflat[slot * TP + lc] = (ok & (qy < rh) & (qx < rw)) ? flat0 + qy * rw + qx : -1;
+            tflat[slot * TP + lc] = (ok & (qy < S[6]) & (qx < S[7])) ? S[9] + qy * S[7] + qx : -1;
         }
 #pragma unroll
         for (int i = 0; i < NHL; ++i) {
@@ -252,12 +270,18 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue_loads(0, 0);
+    int sg = 0, lt = 0;  // the tile being computed: segment, tile within it
+    issue_loads(0, 0, 0);
     for (int t = 0; t < ntiles; ++t) {
         const int slot = t & 1;
+        int sgn = sg, ltn = lt + 1;  // the next tile
+        if (ltn * TP >= sgt[sg][11] - sgt[sg][10]) {
+            ++sgn;
+            ltn = 0;
+        }
         write_lds();
         __syncthreads();
-        if (t + 1 < ntiles) issue_loads(t + 1, (t + 1) & 1);
+        if (t + 1 < ntiles) issue_loads(sgn, ltn, (t + 1) & 1);
         const float* rsd = rs + d * TP * RP;
         const float* dad = das + d * TP * DS;
 #pragma unroll
@@ -317,9 +341,11 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
                 if (dx_canvas) dx_canvas[(int64_t)pix[c] * C + chn] = flat[c] >= 0 ? v : 0.f;
             }
         }
+        sg = sgn;
+        lt = ltn;
     }
-    // partial sums of this chunk: part[chunk][d][R][G]
-    float* out = part + ((int64_t)ch * 4 + d) * R * G;
+    // partial sums of this workgroup: part[group][d][R][G]
+    float* out = part + ((int64_t)grp * 4 + d) * R * G;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -373,7 +399,7 @@ hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, i
                          hipStream_t st) {
     const Wg2Entry* m = wg2_entry(C, H, dtype != 0);
     if (!m) return hipErrorInvalidValue;
-    launch(m->k, dim3((unsigned)D.nchunks), dim3(m->threads), m->lds, st, D, x_canvas, h_dirs, dA, Wx,
+    launch(m->k, dim3((unsigned)D.ngroups), dim3(m->threads), m->lds, st, D, x_canvas, h_dirs, dA, Wx,
            part, dx_flat, dx_canvas);
     return hipGetLastError();
 }

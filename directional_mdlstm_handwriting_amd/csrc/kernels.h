@@ -47,14 +47,15 @@ struct Dev {
     const int64_t* flat_off;  // [n+1]
     const int64_t* cell_off;  // [n+1]
     const int32_t* units;     // [4n]
-    const int32_t* chunks;    // [nchunks][3]
+    const int32_t* segs;      // [nsegs][3] (example, first cell, end cell)
+    const int32_t* groups;    // [ngroups+1] first segment of each weight-gradient workgroup
     int32_t* eid;             // [Hc*Wc]
     uint8_t* border;          // [Hc*Wc]
     int n, Hc, Wc;
     int64_t T;                // computed cells per direction
     int64_t N;                // real pixels
     int max_depth, max_diag;
-    int nchunks;
+    int nsegs, ngroups;
 };
 
 // Canvas position of the direction-local cell (a, b) of an example whose
@@ -117,11 +118,11 @@ MDL_HD inline int64_t z1_offset(int64_t T, int H) { return 4 * T * 4 * (int64_t)
 struct WsLayout {
     size_t stash = 0;   // float [4][T][6H]: gates i, f_l, f_u, o, g and memory state c of every cell
     size_t zda = 0;     // float [4][T][5H]: projection x.Wx+b (forward), gate gradients dA (backward)
-    size_t part = 0;    // float [nchunks][4][(C+1+2H)*5H]: weight-gradient partial sums
+    size_t part = 0;    // float [nparts][4][(C+1+2H)*5H]: weight-gradient partial sums
     size_t total = 0;
-    int64_t nchunks = 0;
+    int64_t nparts = 0;
 };
-WsLayout ws_layout(int64_t T, int64_t nchunks, int C, int H);
+WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H);
 
 // launchers: return hipSuccess or the launch error
 hipError_t launch_build_maps(const Dev& D, hipStream_t st);

@@ -39,7 +39,11 @@ MDL_HD inline int64_t dg_start(int h, int w, int s) {
     return (int64_t)h * w - t * (t + 1) / 2;
 }
 
-constexpr int kChunkCells = 512;
+// Weight-gradient work split (see Layout::segs): at most kGroups workgroups (two per compute unit of a
+// 256-CU device), at least about kGroupMinCells cells each, at most kGroupSegs segments each.
+constexpr int kGroups = 512;
+constexpr int kGroupMinCells = 256;
+constexpr int kGroupSegs = 16;
 
 struct DescOffsets {
     size_t rect = 0;      // int32 [n][4] computed region (y0, x0, h, w)
@@ -47,7 +51,8 @@ struct DescOffsets {
     size_t flat_off = 0;  // int64 [n+1] prefix of real pixels (flat per-example tensors)
     size_t cell_off = 0;  // int64 [n+1] prefix of computed cells (per-direction stash)
     size_t units = 0;     // int32 [4n] (example*4 + direction), most cells first
-    size_t chunks = 0;    // int32 [nchunks][3] (example, first row, end row) of the reduction chunks
+    size_t segs = 0;      // int32 [nsegs][3] (example, first cell, end cell) of the weight-gradient split
+    size_t groups = 0;    // int32 [ngroups+1] first segment of each weight-gradient workgroup
     size_t eid = 0;       // int32 [Hc*Wc]
     size_t border = 0;    // uint8 [Hc*Wc]
     size_t total = 0;
@@ -64,10 +69,15 @@ struct Layout {
     std::vector<uint8_t> border;
     int64_t real_pixels = 0, computed_cells = 0;
     int32_t max_depth = 0, max_diag = 0;
-    // Row ranges of the computed regions, about kChunkCells cells each and never
-    // crossing an example: the fixed blocks of the weight-gradient sums.
-    std::vector<int32_t> chunks;
-    int32_t nchunks = 0;
+    // Weight-gradient split: the computed cells of all examples (example order, row-major within
+    // one) cut into ranges of nearly equal size, one per workgroup; a range's pieces inside one
+    // example are its segments (cells [first, end) of the region). groups[g] .. groups[g+1] are
+    // workgroup g's segments. The partial sums are per workgroup and per segment (for kernels that
+    // take one segment per workgroup), so nparts() = max(nsegs, ngroups) partial blocks.
+    std::vector<int32_t> segs;
+    std::vector<int32_t> groups;
+    int32_t nsegs = 0, ngroups = 0;
+    int64_t nparts() const { return nsegs > ngroups ? nsegs : ngroups; }
     DescOffsets off;
     std::vector<uint8_t> host_desc;  // descriptor bytes up to off.eid (the maps are built on device)
 };

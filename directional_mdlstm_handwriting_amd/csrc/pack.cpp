@@ -44,6 +44,40 @@ void paint_maps(Layout& L) {
         }
 }
 
+// Cuts the computed cells of all examples (example order, row-major inside each region) into at most
+// kGroups ranges of nearly equal size, with boundaries on multiples of 32 cells of the sequence; each
+// range's pieces inside one example are its segments. A range that would hold more than kGroupSegs
+// segments is closed early and its rest goes on in a new group. Depends only on the layout, so the
+// weight-gradient sums are blocked the same way on every run.
+void split_wgrad(Layout& L) {
+    L.segs.clear();
+    L.groups.assign(1, 0);
+    const int64_t T = L.computed_cells;
+    const int64_t G = std::max<int64_t>(1, std::min<int64_t>(kGroups, (T + kGroupMinCells - 1) / kGroupMinCells));
+    int e = 0;
+    int64_t pos = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        const int64_t end = g + 1 == G ? T : std::min(T, (T * (g + 1) / G + 31) / 32 * 32);
+        int in_group = 0;
+        while (pos < end) {
+            while (L.cell_off[e + 1] <= pos) ++e;
+            const int64_t stop = std::min(end, L.cell_off[e + 1]);
+            if (in_group == kGroupSegs) {
+                L.groups.push_back((int32_t)(L.segs.size() / 3));
+                in_group = 0;
+            }
+            L.segs.push_back(e);
+            L.segs.push_back((int32_t)(pos - L.cell_off[e]));
+            L.segs.push_back((int32_t)(stop - L.cell_off[e]));
+            ++in_group;
+            pos = stop;
+        }
+        if (in_group > 0) L.groups.push_back((int32_t)(L.segs.size() / 3));
+    }
+    L.nsegs = (int32_t)(L.segs.size() / 3);
+    L.ngroups = (int32_t)L.groups.size() - 1;
+}
+
 void finish(Layout& L) {
     const int n = L.n;
     L.flat_off.assign(n + 1, 0);
@@ -70,17 +104,7 @@ void finish(Layout& L) {
         return ca > cb;
     });
     paint_maps(L);
-    L.chunks.clear();
-    for (int e = 0; e < n; ++e) {
-        const int h = L.rect[4 * e + 2], w = L.rect[4 * e + 3];
-        const int rows = std::max(1, kChunkCells / w);
-        for (int r0 = 0; r0 < h; r0 += rows) {
-            L.chunks.push_back(e);
-            L.chunks.push_back(r0);
-            L.chunks.push_back(std::min(h, r0 + rows));
-        }
-    }
-    L.nchunks = (int32_t)(L.chunks.size() / 3);
+    split_wgrad(L);
 
     DescOffsets& o = L.off;
     size_t p = 0;
@@ -89,7 +113,8 @@ void finish(Layout& L) {
     o.flat_off = p; p = align256(p + sizeof(int64_t) * (n + 1));
     o.cell_off = p; p = align256(p + sizeof(int64_t) * (n + 1));
     o.units = p;    p = align256(p + sizeof(int32_t) * 4 * n);
-    o.chunks = p;   p = align256(p + sizeof(int32_t) * L.chunks.size());
+    o.segs = p;     p = align256(p + sizeof(int32_t) * L.segs.size());
+    o.groups = p;   p = align256(p + sizeof(int32_t) * L.groups.size());
     o.eid = p;      p = align256(p + sizeof(int32_t) * (size_t)L.Hc * L.Wc);
     o.border = p;   p = align256(p + (size_t)L.Hc * L.Wc);
     o.total = p;
@@ -99,7 +124,8 @@ void finish(Layout& L) {
     std::memcpy(&L.host_desc[o.flat_off], L.flat_off.data(), sizeof(int64_t) * (n + 1));
     std::memcpy(&L.host_desc[o.cell_off], L.cell_off.data(), sizeof(int64_t) * (n + 1));
     std::memcpy(&L.host_desc[o.units], L.units.data(), sizeof(int32_t) * 4 * n);
-    std::memcpy(&L.host_desc[o.chunks], L.chunks.data(), sizeof(int32_t) * L.chunks.size());
+    std::memcpy(&L.host_desc[o.segs], L.segs.data(), sizeof(int32_t) * L.segs.size());
+    std::memcpy(&L.host_desc[o.groups], L.groups.data(), sizeof(int32_t) * L.groups.size());
 }
 
 }  // namespace
