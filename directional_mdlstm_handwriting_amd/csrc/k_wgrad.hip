@@ -337,10 +337,12 @@ __global__ __launch_bounds__(256) void k_wgrad_mfma(Dev D, const void* __restric
 namespace {
 
 // Partial blocks summed in a fixed order, then routed to dWx / db / dUl / dUu. A workgroup takes 64
-// consecutive (direction, entry) slots (coalesced reads of each block's partial row) and 8 slices of the
-// blocks: slice j adds blocks j, j + 8, j + 16, ... in order, and the 8 slice sums are added in slice
-// order through LDS. The order depends only on the block count, so reruns are bit-identical.
-constexpr int RED_X = 64, RED_Y = 8;
+// consecutive (direction, entry) slots (coalesced reads of each block's partial row) and 16 slices of the
+// blocks: slice j adds blocks j, j + 16, j + 32, ... into four accumulators in turn, and the 16 slice sums
+// are added in slice order through LDS. The loads of 16 blocks are issued before they are added, so each
+// thread keeps 16 reads in flight. The order depends only on the block count, so reruns are
+// bit-identical.
+constexpr int RED_X = 64, RED_Y = 16, RED_U = 16;
 __global__ __launch_bounds__(RED_X* RED_Y) void k_wgrad_reduce(const float* __restrict__ part, int nparts, int C,
                                                                int H, float* __restrict__ dWx,
                                                                float* __restrict__ dUl, float* __restrict__ dUu,
@@ -355,6 +357,13 @@ __global__ __launch_bounds__(RED_X* RED_Y) void k_wgrad_reduce(const float* __re
         const float* p = part + id;
         float s4[4] = {0.f, 0.f, 0.f, 0.f};
         int c = ty, j = 0;
+        for (; c + (RED_U - 1) * RED_Y < nparts; c += RED_U * RED_Y) {  // RED_U % 4 == 0: j is unchanged
+            float v[RED_U];
+#pragma unroll
+            for (int u = 0; u < RED_U; ++u) v[u] = p[(int64_t)(c + u * RED_Y) * stride];
+#pragma unroll
+            for (int u = 0; u < RED_U; ++u) s4[u & 3] += v[u];
+        }
         for (; c < nparts; c += RED_Y, j = (j + 1) & 3) s4[j] += p[(int64_t)c * stride];
         s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
