@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true")
     ap.add_argument("--no-other", action="store_true", help="skip the line-like (or word-like) companion run")
+    ap.add_argument("--no-stack", action="store_true", help="skip the three-level stack companion run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB on the device (counter calibration under rocprofv3 --pmc)")
@@ -224,6 +225,57 @@ class Runner:
         return ms, dom, kd[dom], kern
 
 
+class StackRunner:
+    """The three-level stack (MDLSTM -> 2x4 block conv -> MDLSTM -> block conv -> MDLSTM, each level re-packed),
+    forward and backward over one batch, timed like Runner."""
+
+    def __init__(self, wl, device, stream):
+        import torch
+        from directional_mdlstm_handwriting_amd.layer import DeviceParams, LayerGrads, PackedStack, flat_input
+        Hs = [P.H for P in wl.layers]
+        couts = [c.b.shape[0] for c in wl.convs]
+        self.st = PackedStack(wl.heights, wl.widths, wl.C, Hs, couts, wl.canvas_w_min, sep=wl.sep, device=device)
+        self.params = [DeviceParams.from_host(P, device) for P in wl.layers]
+        self.convs = [(torch.as_tensor(c.W, device=device), torch.as_tensor(c.b, device=device)) for c in wl.convs]
+        self.lg = [LayerGrads.like(p) for p in self.params]
+        self.cg = [(torch.empty_like(W), torch.empty_like(b)) for W, b in self.convs]
+        self.x = flat_input(wl.xs, "f32", device)
+        last = self.st.levels[-1]
+        self.dy = torch.as_tensor(np.random.default_rng(wl.seed + 101).standard_normal(last.y.numel()).astype(np.float32),
+                                  device=device)
+        self.dx = torch.empty(int(sum(x.size for x in wl.xs)), device=device)
+        self.stream = stream
+
+    def step(self):
+        self.st.forward(self.x, self.params, self.convs, self.stream)
+        self.st.backward(self.params, self.convs, self.dy, self.lg, self.cg, dx_flat=self.dx, stream=self.stream)
+
+    def time(self, steps, warmup):
+        """ms per step with no events inside the timed region, and the breakdown pass's ms per step of each
+        kernel group (summed over the levels)."""
+        import torch
+        import directional_mdlstm_handwriting_amd as M
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        M.mdl_timing_report()
+        M.mdl_timing_only(None)
+        M.mdl_timing(True)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        M.mdl_timing(False)
+        per_kernel = {k: v[0] / steps for k, v in M.mdl_timing_report().items()}
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        stop.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps, per_kernel
+
+
 def cpu_baseline(wl, min_seconds):
     """The oracle (float64 NumPy, one BLAS thread) on the whole batch: pack + forward + backward, repeated
     until at least min_seconds have passed; the rate is real cell-direction updates per second."""
@@ -264,8 +316,10 @@ def main():
     wl = make_workload(args.workload, args.seed)
     N = int(np.sum(wl.heights.astype(np.int64) * wl.widths))
 
+    torch.cuda.reset_peak_memory_stats()
     packed = Runner(wl, "packed", device, stream)
     ms, dom, dom_ms, kern = packed.time(args.steps, args.warmup)
+    peak_packed = torch.cuda.max_memory_allocated()
     info = packed.dl.info
     value = 4 * N / (ms * 1e-3)
 
@@ -313,13 +367,22 @@ def main():
     out["config"]["canvas_waste"] = round(1.0 - N / (info["canvas_h"] * info["canvas_w"]), 4)
 
     if not args.no_padded and wl.name != "tiny":
+        del packed
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
         padded = Runner(wl, "padded", device, stream)
         pms, _, _, pk = padded.time(max(5, args.steps // 2), 2)
+        peak_padded = torch.cuda.max_memory_allocated()
         pinfo = padded.dl.info
         out["packed_vs_padded"] = {
             "ms_per_step_packed": ms, "ms_per_step_padded": pms, "speedup": pms / ms,
             "padded_cell_fraction": round(1.0 - N / pinfo["computed_cells"], 4),
-            "computed_cells_padded": pinfo["computed_cells"], "padded_kernels_ms": {k: round(v, 5) for k, v in pk.items()},
+            # padded zeros relative to the real pixels (the ZPR measure of the speech-batching page)
+            "zpr": round((pinfo["computed_cells"] - N) / N, 4),
+            "computed_cells_padded": pinfo["computed_cells"],
+            "computed_cell_direction_updates_per_s_padded": 4 * pinfo["computed_cells"] / (pms * 1e-3),
+            "peak_device_bytes_packed": int(peak_packed), "peak_device_bytes_padded": int(peak_padded),
+            "padded_kernels_ms": {k: round(v, 5) for k, v in pk.items()},
             "pages_context": "6.6x for IAM words: whole-model training epochs, 2x GTX 1080, batch 20 padded vs "
                              "200 packed (No Padding Please, Table IV)",
         }
@@ -344,6 +407,26 @@ def main():
                                  for k, r in ((k, roofline(k, v, omodel)) for k, v in ok.items() if k in omodel)},
         }
         del ro
+
+    # the three-level stack of the pages' model (128 word-like images), timed the same way, for context
+    if wl.name == "word" and not args.no_stack:
+        ws_ = make_workload("stack", args.seed)
+        sr = StackRunner(ws_, device, stream)
+        sms, sk = sr.time(max(5, args.steps // 2), 2)
+        lv = []
+        for lay, P in zip(sr.st.levels, ws_.layers):
+            li = lay.dl.info
+            lv.append({"canvas": f"{li['canvas_h']}x{li['canvas_w']}", "real_pixels": li["real_pixels"],
+                       "C": P.C, "H": P.H, "max_depth": li["max_depth"]})
+        Ns = sum(v["real_pixels"] for v in lv)
+        out["stack_workload"] = {
+            "workload": f"stack: {ws_.n} word-like images, MDLSTM H={[P.H for P in ws_.layers]} with 2x4 block "
+                        f"convs to {[c.b.shape[0] for c in ws_.convs]} channels, seed {ws_.seed}",
+            "value": 4 * Ns / (sms * 1e-3), "unit": "cell-direction updates/s (all three levels)",
+            "ms_per_step": sms, "levels": lv,
+            "kernels_ms_per_step": {k: round(v, 5) for k, v in sk.items()},
+        }
+        del sr
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -270,10 +270,8 @@ int mdl_scatter(const mdl_layout* layout, const void* d_desc, const void* x_flat
 // The kernels address device tensors through buffer descriptors with 32-bit byte ranges and offsets.
 // The wavefront kernels take one direction's h plane and the canvas input each as one range and send a
 // masked lane 2^30 bytes past its start; the gate stash is addressed one example at a time. The
-// weight-gradient kernel of the instantiated shapes takes one direction's h plane and gate gradients per
-// range; the general one takes all four h planes and the whole gate-gradient tensor each as one range.
-static int check_extent(const char* fn, const mdl::Layout& L, int C, int H, int x_dtype, bool backward,
-                        bool general_wgrad) {
+// software-pipelined weight-gradient kernel takes one direction's h plane and gate gradients per range.
+static int check_extent(const char* fn, const mdl::Layout& L, int C, int H, int x_dtype, bool backward) {
     const int64_t plane = (int64_t)L.Hc * L.Wc * H * 4;
     const int64_t xbytes = (int64_t)L.Hc * L.Wc * C * (x_dtype == MDL_BF16 ? 2 : 4);
     const int64_t dabytes = L.computed_cells * 5 * (int64_t)H * 4;  // one direction
@@ -282,9 +280,6 @@ static int check_extent(const char* fn, const mdl::Layout& L, int C, int H, int 
         return fail(MDL_EUNSUPPORTED, std::string(fn) + ": one direction's h plane or the canvas input above 1 GiB");
     if (backward && dabytes >= lim)
         return fail(MDL_EUNSUPPORTED, std::string(fn) + ": one direction's gate gradients above 2 GiB");
-    if (backward && general_wgrad && (4 * plane >= lim || 4 * dabytes >= lim))
-        return fail(MDL_EUNSUPPORTED, std::string(fn) + ": the four h planes or the gate gradients above 2 GiB "
-                                                        "for this (C, H)");
     return MDL_OK;
 }
 
@@ -298,7 +293,7 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     const mdl::Layout& L = L_of(layout);
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
-    if ((rc = check_extent("mdl_forward", L, C, H, x_dtype, false, false))) return rc;
+    if ((rc = check_extent("mdl_forward", L, C, H, x_dtype, false))) return rc;
     const bool fused = mdl::fwd16_supported(H, C, x_dtype, L.max_diag);
     if (!fused && (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_forward: widest diagonal x H exceeds the wavefront kernel's items");
@@ -368,9 +363,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
         (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_backward: widest diagonal x H exceeds the wavefront kernel's items");
     const bool wg2 = mdl::wgrad2_supported(C, H, x_dtype);
-    if ((rc = check_extent("mdl_backward", L, C, H, x_dtype, true, !wg2))) return rc;
-    if (!wg2 && !mdl::wgrad_supported(C, H))
-        return fail(MDL_EUNSUPPORTED, "mdl_backward: C and H exceed the weight-gradient kernel's register tile");
+    if ((rc = check_extent("mdl_backward", L, C, H, x_dtype, true))) return rc;
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
     if (mdl::bwd_chain_lds(H, L.max_diag) > lmax)
@@ -426,6 +419,10 @@ int mdl_blockconv_forward(const mdl_layout* lk, const void* d_desc_k, const mdl_
     int rc = check_conv("mdl_blockconv_forward", lk, d_desc_k, lk1, d_desc_k1, H, kh, kw, Cout);
     if (rc) return rc;
     if (!h_dirs_k || !Wc || !bc || !x_canvas_k1) return fail(MDL_EINVAL, "mdl_blockconv_forward: null tensor");
+    size_t lmax = 0;
+    if ((rc = max_lds(lmax))) return rc;
+    if (mdl::conv_fwd_lds(H, kh, kw, Cout) > lmax)
+        return fail(MDL_EUNSUPPORTED, "mdl_blockconv_forward: weights and block tile exceed LDS");
     hipError_t e;
     {
         Timed t("conv_fwd");
@@ -444,6 +441,8 @@ int mdl_blockconv_workspace_size(const mdl_layout* lk1, int32_t H, int32_t kh, i
     const mdl::Layout& B = L_of(lk1);
     mdl::Dev D{};
     D.N = B.real_pixels;
+    D.Hc = B.Hc;
+    D.Wc = B.Wc;
     const int64_t K = 4 * (int64_t)H * kh * kw;
     *bytes = sizeof(float) * (size_t)mdl::conv_nchunks(D) * (size_t)(Cout * (K + 1));
     return MDL_OK;
@@ -465,7 +464,7 @@ int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl
     if (Cout * (K + 1) > 16 * 512) return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: Cout*(4*H*kh*kw+1) above 8192");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
-    if (sizeof(float) * 16 * (size_t)(K + Cout) > lmax)
+    if (mdl::conv_wgrad_lds(H, kh, kw, Cout) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: weight-gradient tile exceeds LDS");
     hipError_t e;
     {

@@ -4,56 +4,100 @@
 // output pixel reads its own kh x kw block; tensor-list chunking stacks all
 // blocks of all examples and runs one convolution over them, and de-chunking
 // puts each example's outputs back by its size. Here the chunks never leave
-// the canvases: each output pixel of the level-(k+1) canvas gathers its block
-// from the level-k canvas (all four directions' hidden outputs as 4H
-// channels), one output channel per thread; the backward scatters the output
-// gradient back through the same blocks. Weight gradients are fixed-order
-// chunked sums over the output pixels. These kernels move little data and are
-// HBM/latency bound.
+// the canvases: output pixels of the level-(k+1) canvas are taken in tiles of
+// CW_TILE, each tile's blocks (all four directions' hidden outputs of the
+// level-k canvas, 4H channels) are gathered into LDS once, and the products
+// run from there:
+//   forward   x1[p][o] = bc[o] + sum_f Wc[o][f] blk[p][f]     (Wc staged in LDS as well)
+//   dW, db    partial sums over the tiles of a chunk of output pixels, per
+//             workgroup, then added in chunk order (fixed order, no atomics)
+// with f = ((d H + k) kh + i) kw + j, the layout of Wc's trailing axes, and
+// block elements outside the level-k example read as zero (partial blocks at
+// the bottom and right edge are zero-padded). The data gradient scatters the
+// output gradient back through the same blocks, one thread per element of dh.
 #include "kernels.h"
 
 namespace mdl {
 
 namespace {
 
-constexpr int CONV_CHUNK = 1024;  // output pixels per weight-gradient partial sum
 constexpr int CW_THREADS = 512;
-constexpr int CW_MAXE = 16;
-constexpr int CW_TILE = 16;
+constexpr int CW_MAXE = 16;   // weight-gradient entries per thread: Cout (K + 1) <= CW_MAXE CW_THREADS
+constexpr int CW_TILE = 16;   // output pixels per staged tile
+constexpr int CW_GROUPS = 512;  // at most this many weight-gradient workgroups (chunks)
 
-// one thread per (level-(k+1) canvas pixel, output channel)
-__global__ void k_conv_fwd(Dev Dk, Dev Dk1, const float* __restrict__ hk, int H, int kh, int kw,
-                           const float* __restrict__ Wc, const float* __restrict__ bc, int Cout,
-                           float* __restrict__ x1) {
-    const int64_t E = (int64_t)Dk1.Hc * Dk1.Wc * Cout;
+// Where output pixel p1 of the level-(k+1) canvas takes its block: the block's first level-k pixel
+// (row-major index on the level-k canvas), the rows and columns of the block inside the level-k example
+// (0 rows for a pixel outside every example's real region, whose block is all zero).
+struct BlockSrc {
+    int base, nrow, ncol;
+};
+
+__device__ inline BlockSrc block_src(const Dev& Dk, const Dev& Dk1, int64_t p1, int kh, int kw) {
+    BlockSrc b{0, 0, 0};
+    const int e = Dk1.eid[p1];
+    if (e < 0) return b;
+    const int r = (int)(p1 / Dk1.Wc) - Dk1.real[4 * e];
+    const int c = (int)(p1 % Dk1.Wc) - Dk1.real[4 * e + 1];
+    if (r >= Dk1.real[4 * e + 2] || c >= Dk1.real[4 * e + 3]) return b;
+    const int yy = kh * r, xx = kw * c;
+    b.base = (Dk.real[4 * e] + yy) * Dk.Wc + Dk.real[4 * e + 1] + xx;
+    b.nrow = min(kh, Dk.real[4 * e + 2] - yy);
+    b.ncol = min(kw, Dk.real[4 * e + 3] - xx);
+    return b;
+}
+
+// Gathers the blocks of output pixels [p0, p0 + CW_TILE) into blk[CW_TILE][K] (zero past P1), using the
+// per-pixel sources `src` the caller filled. Consecutive threads take consecutive f.
+__device__ inline void gather_tile(const Dev& Dk, const float* __restrict__ hk, int H, int kh, int kw, int K,
+                                   const BlockSrc* src, float* blk) {
     const int64_t plane = (int64_t)Dk.Hc * Dk.Wc * H;
-    for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < E; t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t p1 = t / Cout;
-        const int o = (int)(t % Cout);
-        const int e = Dk1.eid[p1];
+    for (int idx = threadIdx.x; idx < CW_TILE * K; idx += blockDim.x) {
+        const int tt = idx / K, f = idx - tt * K;
+        const int j = f % kw, i = (f / kw) % kh, k = (f / (kw * kh)) % H, d = f / (kw * kh * H);
+        const BlockSrc s = src[tt];
         float v = 0.f;
-        if (e >= 0) {
-            const int r = (int)(p1 / Dk1.Wc) - Dk1.real[4 * e];
-            const int c = (int)(p1 % Dk1.Wc) - Dk1.real[4 * e + 1];
-            if (r < Dk1.real[4 * e + 2] && c < Dk1.real[4 * e + 3]) {
-                const int y0 = Dk.real[4 * e], x0 = Dk.real[4 * e + 1], h = Dk.real[4 * e + 2], w = Dk.real[4 * e + 3];
-                v = bc[o];
-                for (int d = 0; d < 4; ++d)
-                    for (int k = 0; k < H; ++k) {
-                        const float* wr = Wc + (((int64_t)o * 4 + d) * H + k) * kh * kw;
-                        for (int i = 0; i < kh; ++i) {
-                            const int yy = kh * r + i;
-                            if (yy >= h) break;
-                            for (int j = 0; j < kw; ++j) {
-                                const int xx = kw * c + j;
-                                if (xx >= w) break;
-                                v += wr[i * kw + j] * hk[d * plane + ((int64_t)(y0 + yy) * Dk.Wc + x0 + xx) * H + k];
-                            }
-                        }
-                    }
-            }
+        if (i < s.nrow && j < s.ncol) v = hk[d * plane + (int64_t)(s.base + i * Dk.Wc + j) * H + k];
+        blk[idx] = v;
+    }
+}
+
+// Forward: workgroups stride over tiles of CW_TILE canvas pixels of level k+1; Wc [Cout][K] sits in LDS
+// for the whole workgroup. Every canvas pixel is written (zero outside the real pixels).
+__global__ __launch_bounds__(256) void k_conv_fwd(Dev Dk, Dev Dk1, const float* __restrict__ hk, int H, int kh,
+                                                  int kw, const float* __restrict__ Wc,
+                                                  const float* __restrict__ bc, int Cout, float* __restrict__ x1) {
+    const int K = 4 * H * kh * kw;
+    extern __shared__ float lds[];
+    float* w = lds;                         // [Cout][K]
+    float* blk = w + Cout * K;              // [CW_TILE][K]
+    BlockSrc* src = reinterpret_cast<BlockSrc*>(blk + CW_TILE * K);  // [CW_TILE]
+    for (int i = threadIdx.x; i < Cout * K; i += blockDim.x) w[i] = Wc[i];
+    const int64_t P1 = (int64_t)Dk1.Hc * Dk1.Wc;
+    const int64_t ntiles = (P1 + CW_TILE - 1) / CW_TILE;
+    for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int64_t p0 = tile * CW_TILE;
+        __syncthreads();  // the previous tile's reads of blk and src are done
+        if (threadIdx.x < CW_TILE) {
+            const int64_t p1 = p0 + threadIdx.x;
+            src[threadIdx.x] = p1 < P1 ? block_src(Dk, Dk1, p1, kh, kw) : BlockSrc{0, 0, 0};
         }
-        x1[t] = v;
+        __syncthreads();
+        gather_tile(Dk, hk, H, kh, kw, K, src, blk);
+        __syncthreads();
+        for (int o2 = threadIdx.x; o2 < CW_TILE * Cout; o2 += blockDim.x) {
+            const int tt = o2 / Cout, o = o2 - tt * Cout;
+            const int64_t p1 = p0 + tt;
+            if (p1 >= P1) continue;
+            float v = 0.f;
+            if (src[tt].nrow > 0) {
+                v = bc[o];
+                const float* br = blk + tt * K;
+                const float* wr = w + o * K;
+                for (int f = 0; f < K; ++f) v += wr[f] * br[f];
+            }
+            x1[p1 * Cout + o] = v;
+        }
     }
 }
 
@@ -84,43 +128,42 @@ __global__ void k_conv_bwd_data(Dev Dk, Dev Dk1, int H, int kh, int kw, const fl
     }
 }
 
-// grid nchunks: partial sums of dWc (and dbc) over CONV_CHUNK consecutive real output pixels
+// Output pixels per weight-gradient chunk: whole tiles, at most CW_GROUPS chunks over the level-(k+1)
+// canvas.
+inline int64_t conv_chunk(const Dev& Dk1) {
+    const int64_t P1 = (int64_t)Dk1.Hc * Dk1.Wc;
+    const int64_t per = (P1 + CW_GROUPS - 1) / CW_GROUPS;
+    return (per + CW_TILE - 1) / CW_TILE * CW_TILE;
+}
+
+// grid nchunks: partial sums of dWc (and dbc) over one chunk of level-(k+1) canvas pixels (pixels outside
+// the real pixels carry a zero gradient and an all-zero block)
 __global__ __launch_bounds__(CW_THREADS) void k_conv_wpartial(Dev Dk, Dev Dk1, const float* __restrict__ hk, int H,
                                                               int kh, int kw, int Cout, const float* __restrict__ dx1,
-                                                              float* __restrict__ part) {
+                                                              int64_t chunk, float* __restrict__ part) {
     const int K = 4 * H * kh * kw;
     const int E = Cout * (K + 1);
-    const int64_t q0 = (int64_t)blockIdx.x * CONV_CHUNK;
-    const int64_t q1 = q0 + CONV_CHUNK < Dk1.N ? q0 + CONV_CHUNK : Dk1.N;
-    const int64_t plane = (int64_t)Dk.Hc * Dk.Wc * H;
+    const int64_t P1 = (int64_t)Dk1.Hc * Dk1.Wc;
+    const int64_t q0 = (int64_t)blockIdx.x * chunk;
+    const int64_t q1 = q0 + chunk < P1 ? q0 + chunk : P1;
     extern __shared__ float lds[];
     float* blk = lds;                   // [CW_TILE][K]
     float* gx = blk + CW_TILE * K;      // [CW_TILE][Cout]
+    BlockSrc* src = reinterpret_cast<BlockSrc*>(gx + CW_TILE * Cout);  // [CW_TILE]
     const int tid = threadIdx.x, nthr = blockDim.x;
     float acc[CW_MAXE];
 #pragma unroll
     for (int i = 0; i < CW_MAXE; ++i) acc[i] = 0.f;
     for (int64_t t0 = q0; t0 < q1; t0 += CW_TILE) {
-        for (int idx = tid; idx < CW_TILE * (K + Cout); idx += nthr) {
-            const int tt = idx / (K + Cout), f = idx - tt * (K + Cout);
-            const int64_t q = t0 + tt;
-            float v = 0.f;
-            if (q < q1) {
-                const int e = find_example(Dk1.flat_off, Dk1.n, q);
-                const int w1 = Dk1.real[4 * e + 3];
-                const int64_t qq = q - Dk1.flat_off[e];
-                const int r = (int)(qq / w1), c = (int)(qq % w1);
-                if (f < K) {
-                    const int j = f % kw, i = (f / kw) % kh, k = (f / (kw * kh)) % H, d = f / (kw * kh * H);
-                    const int yy = kh * r + i, xx = kw * c + j;
-                    if (yy < Dk.real[4 * e + 2] && xx < Dk.real[4 * e + 3])
-                        v = hk[d * plane + ((int64_t)(Dk.real[4 * e] + yy) * Dk.Wc + Dk.real[4 * e + 1] + xx) * H + k];
-                } else {
-                    const int64_t p1 = (int64_t)(Dk1.real[4 * e] + r) * Dk1.Wc + Dk1.real[4 * e + 1] + c;
-                    v = dx1[p1 * Cout + (f - K)];
-                }
-            }
-            if (f < K) blk[tt * K + f] = v; else gx[tt * Cout + (f - K)] = v;
+        if (tid < CW_TILE) {
+            const int64_t p1 = t0 + tid;
+            src[tid] = p1 < q1 ? block_src(Dk, Dk1, p1, kh, kw) : BlockSrc{0, 0, 0};
+        }
+        __syncthreads();
+        gather_tile(Dk, hk, H, kh, kw, K, src, blk);
+        for (int idx = tid; idx < CW_TILE * Cout; idx += nthr) {
+            const int tt = idx / Cout;
+            gx[idx] = src[tt].nrow > 0 ? dx1[(t0 + tt) * Cout + (idx - tt * Cout)] : 0.f;
         }
         __syncthreads();
 #pragma unroll
@@ -165,13 +208,28 @@ inline unsigned grid_for(int64_t n) {
 
 }  // namespace
 
-int64_t conv_nchunks(const Dev& Dk1) { return (Dk1.N + CONV_CHUNK - 1) / CONV_CHUNK; }
+int64_t conv_nchunks(const Dev& Dk1) {
+    const int64_t P1 = (int64_t)Dk1.Hc * Dk1.Wc;
+    const int64_t c = conv_chunk(Dk1);
+    return (P1 + c - 1) / c;
+}
+
+size_t conv_fwd_lds(int H, int kh, int kw, int Cout) {
+    const size_t K = 4 * (size_t)H * kh * kw;
+    return sizeof(float) * ((size_t)Cout * K + CW_TILE * K) + sizeof(BlockSrc) * CW_TILE;
+}
+
+size_t conv_wgrad_lds(int H, int kh, int kw, int Cout) {
+    const size_t K = 4 * (size_t)H * kh * kw;
+    return sizeof(float) * (CW_TILE * K + CW_TILE * (size_t)Cout) + sizeof(BlockSrc) * CW_TILE;
+}
 
 hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st) {
-    const int64_t E = (int64_t)Dk1.Hc * Dk1.Wc * Cout;
-    launch(k_conv_fwd, dim3(grid_for(E)), dim3(256), 0, st, Dk, Dk1, h_dirs_k, H, kh, kw, Wc, bc, Cout,
-           x_k1);
+    const int64_t ntiles = ((int64_t)Dk1.Hc * Dk1.Wc + CW_TILE - 1) / CW_TILE;
+    const unsigned grid = (unsigned)(ntiles < 1024 ? ntiles : 1024);
+    launch(k_conv_fwd, dim3(grid), dim3(256), conv_fwd_lds(H, kh, kw, Cout), st, Dk, Dk1, h_dirs_k, H, kh, kw, Wc,
+           bc, Cout, x_k1);
     return hipGetLastError();
 }
 
@@ -185,9 +243,8 @@ hipError_t launch_conv_bwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k,
     if (err != hipSuccess) return err;
     const int K = 4 * H * kh * kw;
     const int64_t nch = conv_nchunks(Dk1);
-    const size_t lds = sizeof(float) * (size_t)CW_TILE * (K + Cout);
-    launch(k_conv_wpartial, dim3((unsigned)nch), dim3(CW_THREADS), lds, st, Dk, Dk1, h_dirs_k, H, kh, kw,
-           Cout, dx_k1, part);
+    launch(k_conv_wpartial, dim3((unsigned)nch), dim3(CW_THREADS), conv_wgrad_lds(H, kh, kw, Cout), st, Dk, Dk1,
+           h_dirs_k, H, kh, kw, Cout, dx_k1, conv_chunk(Dk1), part);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int Ew = Cout * (K + 1);

@@ -157,7 +157,6 @@ size_t wgrad2_lds_bytes(int C, int H, int dtype);
 hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
                          const float* dA, const float* Wx, float* part, float* dx_flat, float* dx_canvas,
                          hipStream_t st);
-bool wgrad_supported(int C, int H);
 size_t wgrad_lds_bytes(int C, int H);
 hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
                         const float* dA, const float* Wx, float* part, float* dWx, float* dUl, float* dUu, float* db,
@@ -165,6 +164,8 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
 hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st);
 int64_t conv_nchunks(const Dev& Dk1);
+size_t conv_fwd_lds(int H, int kh, int kw, int Cout);
+size_t conv_wgrad_lds(int H, int kh, int kw, int Cout);
 hipError_t launch_conv_bwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, int Cout, const float* dx_k1, float* dh_k, float* dWc,
                            float* dbc, float* part, hipStream_t st);

@@ -202,11 +202,8 @@ int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float*
  *   dx_flat [h][w][C] float32 per example, dx_canvas [Hc][Wc][C] float32 (zero
  *   outside the real pixels); dWx, dUl, dUu, db shaped like Wx, Ul, Uu, b.
  * Weight gradients are fixed-order blocked sums over all computed cells.
- * MDL_EUNSUPPORTED under the same size limits as mdl_forward, when one
- * direction's gate gradients (T*5H floats, T = computed cells) reach 2 GiB,
- * when C and H exceed the weight-gradient kernel's register tile, and, for
- * (C, H) without a compiled weight-gradient shape, when all four h planes or
- * all four directions' gate gradients together reach 2 GiB.
+ * MDL_EUNSUPPORTED under the same size limits as mdl_forward and when one
+ * direction's gate gradients (T*5H floats, T = computed cells) reach 2 GiB.
  */
 int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
                  int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu,
@@ -223,6 +220,8 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
  * level-(k+1) layout `lk1` must hold e with size ceil(h/kh) x ceil(w/kw) and
  * receives x_canvas_k1 [Hc'][Wc'][Cout] float32 (zero outside real pixels).
  * h_dirs_k [4][Hc][Wc][H]; Wc [Cout][4][H][kh][kw]; bc [Cout].
+ * MDL_EUNSUPPORTED when Wc plus one tile of 16 blocks (floats: (Cout + 16) *
+ * 4*H*kh*kw) exceeds a workgroup's LDS.
  */
 int mdl_blockconv_forward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1,
                           const void* d_desc_k1, const float* h_dirs_k, int32_t H, int32_t kh,
@@ -235,7 +234,10 @@ int mdl_blockconv_workspace_size(const mdl_layout* lk1, int32_t H, int32_t kh, i
 
 /*
  * Backward of mdl_blockconv_forward: dx_canvas_k1 [Hc'][Wc'][Cout] -> dh_dirs_k
- * [4][Hc][Wc][H] (zero outside the level-k real pixels), dWc, dbc (fixed-order sums).
+ * [4][Hc][Wc][H] (zero outside the level-k real pixels), dWc, dbc (fixed-order
+ * sums: partial sums over chunks of level-(k+1) canvas pixels, added in chunk
+ * order). MDL_EUNSUPPORTED when Cout*(4*H*kh*kw+1) exceeds 8192 or one tile of
+ * 16 blocks and their output gradients exceeds a workgroup's LDS.
  */
 int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1,
                            const void* d_desc_k1, const float* h_dirs_k, int32_t H, int32_t kh,
