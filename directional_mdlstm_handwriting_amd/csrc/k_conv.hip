@@ -47,9 +47,9 @@ __device__ inline BlockSrc block_src(const Dev& Dk, const Dev& Dk1, int64_t p1, 
     return b;
 }
 
-// Gathers the blocks of output pixels [p0, p0 + CW_TILE) into blk[CW_TILE][K] (zero past P1), using the
-// per-pixel sources `src` the caller filled. Consecutive threads take consecutive f.
-__device__ inline void gather_tile(const Dev& Dk, const float* __restrict__ hk, int H, int kh, int kw, int K,
+// Gathers the blocks of output pixels [p0, p0 + CW_TILE) into blk[CW_TILE][KS] (row stride KS >= K; zero
+// past P1), using the per-pixel sources `src` the caller filled. Consecutive threads take consecutive f.
+__device__ inline void gather_tile(const Dev& Dk, const float* __restrict__ hk, int H, int kh, int kw, int K, int KS,
                                    const BlockSrc* src, float* blk) {
     const int64_t plane = (int64_t)Dk.Hc * Dk.Wc * H;
     for (int idx = threadIdx.x; idx < CW_TILE * K; idx += blockDim.x) {
@@ -58,7 +58,7 @@ __device__ inline void gather_tile(const Dev& Dk, const float* __restrict__ hk, 
         const BlockSrc s = src[tt];
         float v = 0.f;
         if (i < s.nrow && j < s.ncol) v = hk[d * plane + (int64_t)(s.base + i * Dk.Wc + j) * H + k];
-        blk[idx] = v;
+        blk[tt * KS + f] = v;
     }
 }
 
@@ -68,11 +68,12 @@ __global__ __launch_bounds__(256) void k_conv_fwd(Dev Dk, Dev Dk1, const float* 
                                                   int kw, const float* __restrict__ Wc,
                                                   const float* __restrict__ bc, int Cout, float* __restrict__ x1) {
     const int K = 4 * H * kh * kw;
+    const int KS = K | 1;  // odd row stride: the lanes of a wave read different rows on different banks
     extern __shared__ float lds[];
-    float* w = lds;                         // [Cout][K]
-    float* blk = w + Cout * K;              // [CW_TILE][K]
-    BlockSrc* src = reinterpret_cast<BlockSrc*>(blk + CW_TILE * K);  // [CW_TILE]
-    for (int i = threadIdx.x; i < Cout * K; i += blockDim.x) w[i] = Wc[i];
+    float* w = lds;                         // [Cout][KS]
+    float* blk = w + Cout * KS;             // [CW_TILE][KS]
+    BlockSrc* src = reinterpret_cast<BlockSrc*>(blk + CW_TILE * KS);  // [CW_TILE]
+    for (int i = threadIdx.x; i < Cout * K; i += blockDim.x) w[(i / K) * KS + i % K] = Wc[i];
     const int64_t P1 = (int64_t)Dk1.Hc * Dk1.Wc;
     const int64_t ntiles = (P1 + CW_TILE - 1) / CW_TILE;
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void k_conv_fwd(Dev Dk, Dev Dk1, const float* 
             src[threadIdx.x] = p1 < P1 ? block_src(Dk, Dk1, p1, kh, kw) : BlockSrc{0, 0, 0};
         }
         __syncthreads();
-        gather_tile(Dk, hk, H, kh, kw, K, src, blk);
+        gather_tile(Dk, hk, H, kh, kw, K, KS, src, blk);
         __syncthreads();
         for (int o2 = threadIdx.x; o2 < CW_TILE * Cout; o2 += blockDim.x) {
             const int tt = o2 / Cout, o = o2 - tt * Cout;
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(256) void k_conv_fwd(Dev Dk, Dev Dk1, const float* 
             float v = 0.f;
             if (src[tt].nrow > 0) {
                 v = bc[o];
-                const float* br = blk + tt * K;
-                const float* wr = w + o * K;
+                const float* br = blk + tt * KS;
+                const float* wr = w + o * KS;
                 for (int f = 0; f < K; ++f) v += wr[f] * br[f];
             }
             x1[p1 * Cout + o] = v;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(CW_THREADS) void k_conv_wpartial(Dev Dk, Dev Dk1, c
             src[tid] = p1 < q1 ? block_src(Dk, Dk1, p1, kh, kw) : BlockSrc{0, 0, 0};
         }
         __syncthreads();
-        gather_tile(Dk, hk, H, kh, kw, K, src, blk);
+        gather_tile(Dk, hk, H, kh, kw, K, K, src, blk);
         for (int idx = tid; idx < CW_TILE * Cout; idx += nthr) {
             const int tt = idx / Cout;
             gx[idx] = src[tt].nrow > 0 ? dx1[(t0 + tt) * Cout + (idx - tt * Cout)] : 0.f;
@@ -189,15 +190,28 @@ __global__ __launch_bounds__(CW_THREADS) void k_conv_wpartial(Dev Dk, Dev Dk1, c
     }
 }
 
-__global__ void k_conv_wreduce(const float* __restrict__ part, int64_t nchunks, int K, int Cout,
-                               float* __restrict__ dWc, float* __restrict__ dbc) {
+// dWc and dbc: the chunk partials summed in a fixed order. A workgroup takes 64 consecutive entries and 16
+// slices of the chunks (slice j adds chunks j, j + 16, ... in order); the slice sums are then added in
+// slice order.
+constexpr int CR_X = 64, CR_Y = 16;
+__global__ __launch_bounds__(CR_X* CR_Y) void k_conv_wreduce(const float* __restrict__ part, int64_t nchunks, int K,
+                                                             int Cout, float* __restrict__ dWc,
+                                                             float* __restrict__ dbc) {
     const int E = Cout * (K + 1);
-    const int id = blockIdx.x * blockDim.x + threadIdx.x;
-    if (id >= E) return;
+    const int tx = threadIdx.x % CR_X, ty = threadIdx.x / CR_X;
+    const int id = blockIdx.x * CR_X + tx;
     float s = 0.f;
-    for (int64_t c = 0; c < nchunks; ++c) s += part[c * E + id];
+    if (id < E)
+        for (int64_t c = ty; c < nchunks; c += CR_Y) s += part[c * E + id];
+    __shared__ float red[CR_Y][CR_X];
+    red[ty][tx] = s;
+    __syncthreads();
+    if (ty != 0 || id >= E) return;
+    float t = red[0][tx];
+#pragma unroll
+    for (int y = 1; y < CR_Y; ++y) t += red[y][tx];
     const int o = id / (K + 1), f = id % (K + 1);
-    if (f < K) dWc[(int64_t)o * K + f] = s; else dbc[o] = s;
+    if (f < K) dWc[(int64_t)o * K + f] = t; else dbc[o] = t;
 }
 
 inline unsigned grid_for(int64_t n) {
@@ -215,8 +229,8 @@ int64_t conv_nchunks(const Dev& Dk1) {
 }
 
 size_t conv_fwd_lds(int H, int kh, int kw, int Cout) {
-    const size_t K = 4 * (size_t)H * kh * kw;
-    return sizeof(float) * ((size_t)Cout * K + CW_TILE * K) + sizeof(BlockSrc) * CW_TILE;
+    const size_t KS = (4 * (size_t)H * kh * kw) | 1;
+    return sizeof(float) * ((size_t)Cout * KS + CW_TILE * KS) + sizeof(BlockSrc) * CW_TILE;
 }
 
 size_t conv_wgrad_lds(int H, int kh, int kw, int Cout) {
@@ -248,7 +262,7 @@ hipError_t launch_conv_bwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k,
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int Ew = Cout * (K + 1);
-    launch(k_conv_wreduce, dim3((Ew + 255) / 256), dim3(256), 0, st, part, nch, K, Cout, dWc, dbc);
+    launch(k_conv_wreduce, dim3((Ew + CR_X - 1) / CR_X), dim3(CR_X * CR_Y), 0, st, part, nch, K, Cout, dWc, dbc);
     return hipGetLastError();
 }
 

@@ -14,9 +14,10 @@
 // (segment, direction, 64 x 64 output tile) gathers r and da of 16 cells at a
 // time into LDS and accumulates on v_mfma_f32_16x16x4_f32 (fp32 products and
 // sums), so even a layer of few cells and many hidden units spreads over many
-// workgroups. dx takes one thread per (canvas pixel, input channel) of the
-// computed regions. Segment partial sums are then added in segment order by
-// k_wgrad_reduce, so the result is bit-reproducible.
+// workgroups. dx is a product of the same kind (canvas pixels x channels, K =
+// the four directions' gate gradients) on the matrix cores. Segment
+// partial sums are then added in segment order by k_wgrad_reduce, so the
+// result is bit-reproducible.
 #include "kernels.h"
 #include "devmath.h"
 
@@ -138,39 +139,66 @@ __global__ __launch_bounds__(256) void k_wgrad_tile(Dev D, const void* __restric
             }
 }
 
-// dx(p)[c] = sum over d (in order 0..3) of da_d(p) . Wx[d][c][:], one thread per (canvas pixel, channel);
-// written for computed cells: dx_flat at the real pixels, dx_canvas at every computed cell (zero outside
-// the real pixels)
+// dx(p)[c] = sum over d (in order 0..3) of da_d(p) . Wx[d][c][:], written for computed cells: dx_flat at
+// the real pixels, dx_canvas at every computed cell (zero outside the real pixels). A workgroup takes 16
+// canvas pixels (one MFMA row tile), wave d direction d: v_mfma_f32_16x16x4_f32 with A = the pixels' gate
+// gradients (K: first the 4H values (unit, gate < 4) in their stored order, then the H values of gate 4)
+// and B = Wx[d] in the same K order, 16 channels at a time; the four directions are added through LDS.
+constexpr int DX_PIX = 16;
 __global__ __launch_bounds__(256) void k_dx_cells(Dev D, int C, int H, const float* __restrict__ dA,
                                                   const float* __restrict__ Wx, float* __restrict__ dx_flat,
                                                   float* __restrict__ dx_canvas) {
     const int G = 5 * H;
-    const int64_t E = (int64_t)D.Hc * D.Wc * C;
-    for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < E; o += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t pix = o / C;
-        const int ch = (int)(o - pix * C);
-        const int e = D.eid[pix];
-        if (e < 0) continue;
-        const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
-        const int ly = (int)(pix / D.Wc) - y0, lx = (int)(pix % D.Wc) - x0;
-        float v = 0.f;
-        for (int d = 0; d < 4; ++d) {
-            const int64_t t = D.cell_off[e] + stash_index(h, w, ly, lx, d);
-            const float* a4 = dA + ((int64_t)d * D.T + t) * 4 * H;
-            const float* a1 = dA + z1_offset(D.T, H) + ((int64_t)d * D.T + t) * H;
-            const float* wx = Wx + ((int64_t)d * C + ch) * G;
-            float s = 0.f;
-            for (int k = 0; k < H; ++k) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) s += a4[4 * k + g] * wx[g * H + k];
-                s += a1[k] * wx[4 * H + k];
-            }
-            v = d == 0 ? s : v + s;
+    const int lane = threadIdx.x & 63, d = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i16 = lane & 15, q = lane >> 4;
+    const int64_t P = (int64_t)D.Hc * D.Wc;
+    const int64_t p0 = (int64_t)blockIdx.x * DX_PIX;
+    // this lane's A row: pixel p0 + i16
+    const int64_t pa = p0 + i16;
+    const int ea = pa < P ? D.eid[pa] : -1;
+    const float* a4 = dA;  // [4H] of the pixel's cell in direction d
+    const float* a1 = dA;  // [H]
+    if (ea >= 0) {
+        const int y0 = D.rect[4 * ea], x0 = D.rect[4 * ea + 1], h = D.rect[4 * ea + 2], w = D.rect[4 * ea + 3];
+        const int ly = (int)(pa / D.Wc) - y0, lx = (int)(pa % D.Wc) - x0;
+        const int64_t t = (int64_t)d * D.T + D.cell_off[ea] + stash_index(h, w, ly, lx, d);
+        a4 = dA + t * 4 * H;
+        a1 = dA + z1_offset(D.T, H) + t * H;
+    }
+    __shared__ float red[4][DX_PIX][17];
+    for (int cb = 0; cb < C; cb += 16) {
+        const int c = cb + i16;  // this lane's B column
+        const bool cok = c < C;
+        const float* wr = Wx + ((int64_t)d * C + (cok ? c : 0)) * G;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < H; ++ks) {  // K index 4 ks + q: unit ks, gate q
+            const float av = ea >= 0 ? a4[4 * ks + q] : 0.f;
+            const float bv = cok ? wr[q * H + ks] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
         }
-        const int qy = y0 + ly - D.real[4 * e], qx = x0 + lx - D.real[4 * e + 1];
-        const bool real = qy < D.real[4 * e + 2] && qx < D.real[4 * e + 3];
-        if (dx_flat && real) dx_flat[(D.flat_off[e] + (int64_t)qy * D.real[4 * e + 3] + qx) * C + ch] = v;
-        if (dx_canvas) dx_canvas[o] = real ? v : 0.f;
+        for (int ks = 0; 4 * ks < H; ++ks) {  // gate 4 of unit 4 ks + q
+            const int k = 4 * ks + q;
+            const float av = (ea >= 0 && k < H) ? a1[k] : 0.f;
+            const float bv = (cok && k < H) ? wr[4 * H + k] : 0.f;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+        }
+        __syncthreads();  // the previous block's sums have been read
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[d][4 * q + r][i16] = acc[r];  // pixel row 4q + r, channel column i16
+        __syncthreads();
+        const int pr = threadIdx.x >> 4, cc = threadIdx.x & 15;
+        const int64_t pix = p0 + pr;
+        if (pr < DX_PIX && pix < P && cb + cc < C) {
+            const int e = D.eid[pix];
+            if (e >= 0) {
+                const float v = ((red[0][pr][cc] + red[1][pr][cc]) + red[2][pr][cc]) + red[3][pr][cc];
+                const int qy = (int)(pix / D.Wc) - D.real[4 * e], qx = (int)(pix % D.Wc) - D.real[4 * e + 1];
+                const bool real = qy < D.real[4 * e + 2] && qx < D.real[4 * e + 3];
+                if (dx_flat && real)
+                    dx_flat[(D.flat_off[e] + (int64_t)qy * D.real[4 * e + 3] + qx) * C + cb + cc] = v;
+                if (dx_canvas) dx_canvas[pix * C + cb + cc] = real ? v : 0.f;
+            }
+        }
     }
 }
 
@@ -245,10 +273,9 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         if (dx_flat || dx_canvas) {
-            const int64_t E = (int64_t)D.Hc * D.Wc * C;
-            const int64_t g = (E + 255) / 256;
-            launch(k_dx_cells, dim3((unsigned)(g < 65536 ? g : 65536)), dim3(256), 0, st, D, C, H, dA, Wx, dx_flat,
-                   dx_canvas);
+            const int64_t P = (int64_t)D.Hc * D.Wc;
+            launch(k_dx_cells, dim3((unsigned)((P + DX_PIX - 1) / DX_PIX)), dim3(256), 0, st, D, C, H, dA, Wx,
+                   dx_flat, dx_canvas);
             err = hipGetLastError();
             if (err != hipSuccess) return err;
         }
