@@ -294,13 +294,17 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
     if ((rc = check_extent("mdl_forward", L, C, H, x_dtype, false))) return rc;
-    const bool fused = mdl::fwd16_supported(H, C, x_dtype, L.max_diag);
-    if (!fused && (int64_t)L.max_diag * H > mdl::chain_max_items())
+    // small hidden sizes: vector-ALU wavefront; instantiated matrix-core shapes: f16 wavefront; both with
+    // the projection fused. Otherwise the projection as its own GEMM and the general fp32 wavefront.
+    const bool small = mdl::small_fwd_supported(H, C, x_dtype, L.max_diag);
+    const bool fused = !small && mdl::fwd16_supported(H, C, x_dtype, L.max_diag);
+    if (!small && !fused && (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_forward: widest diagonal x H exceeds the wavefront kernel's items");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
-    if ((fused ? mdl::fwd16_lds(H, C, x_dtype, L.max_diag) : mdl::fwd_chain_lds(H, L.max_diag)) > lmax)
-        return fail(MDL_EUNSUPPORTED, "mdl_forward: recurrent weights and diagonal state exceed LDS");
+    const size_t need = small ? mdl::small_fwd_lds(H, L.max_diag)
+                              : (fused ? mdl::fwd16_lds(H, C, x_dtype, L.max_diag) : mdl::fwd_chain_lds(H, L.max_diag));
+    if (need > lmax) return fail(MDL_EUNSUPPORTED, "mdl_forward: recurrent weights and diagonal state exceed LDS");
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -312,7 +316,10 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
         e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_forward: zero fill");
-    if (fused) {
+    if (small) {
+        Timed t("fwd_wavefront");
+        e = mdl::launch_fwd_small(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, stash, h_dirs, st);
+    } else if (fused) {
         Timed t("fwd_wavefront");
         e = mdl::launch_fwd16(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, stash, h_dirs, st);
     } else {
@@ -359,7 +366,8 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     const mdl::Layout& L = L_of(layout);
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_backward: workspace smaller than mdl_workspace_size");
-    if (!mdl::bwd16_supported(H, L.max_diag) && !mdl::chain_uses_mfma(H, L.max_diag) &&
+    if (!mdl::small_bwd_supported(H, L.max_diag) && !mdl::bwd16_supported(H, L.max_diag) &&
+        !mdl::chain_uses_mfma(H, L.max_diag) &&
         (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_backward: widest diagonal x H exceeds the wavefront kernel's items");
     const bool wg2 = mdl::wgrad2_supported(C, H, x_dtype);

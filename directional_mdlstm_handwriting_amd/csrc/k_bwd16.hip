@@ -428,7 +428,7 @@ struct B16Entry {
 #define MDL_B16(h)                                                                                          \
     {h, B16Shape<h>::NB, B16Shape<h>::CG,                                                                   \
      {MDL_B16S(h, 1, 512), MDL_B16S(h, 1, 640), MDL_B16S(h, 1, 768), MDL_B16S(h, 2, 512)}}
-const B16Entry kB16[] = {MDL_B16(2), MDL_B16(4), MDL_B16(10), MDL_B16(16),
+const B16Entry kB16[] = {MDL_B16(16),
                          {32, B16Shape<32>::NB, B16Shape<32>::CG,
                           {MDL_B16S(32, 1, 512), MDL_B16S(32, 2, 512), {0, 0, nullptr}, {0, 0, nullptr}}}};
 #undef MDL_B16

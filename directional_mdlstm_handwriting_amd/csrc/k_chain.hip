@@ -443,7 +443,7 @@ struct MfmaEntry {
     BwdKernel bwd;
     int KB;
 };
-// the f16 reverse wavefront covers the smaller hidden sizes over the same diagonal widths
+// hidden sizes with a vector-ALU or f16 reverse wavefront take those over the diagonal widths they cover
 const MfmaEntry kMfma[] = {
     {50, k_bwd_mfma<50>, 4},
 };
@@ -470,6 +470,7 @@ size_t fwd_chain_lds(int H, int Lmax) {
 }
 
 size_t bwd_chain_lds(int H, int Lmax) {
+    if (small_bwd_supported(H, Lmax)) return small_bwd_lds(H, Lmax);
     if (bwd16_supported(H, Lmax)) return bwd16_lds(H, Lmax);
     if (mfma_entry(H, Lmax)) return bwd_mfma_lds(H, Lmax);
     return sizeof(float) * ((size_t)2 * H * 5 * H + (size_t)2 * Lmax * 5 * H + (size_t)4 * Lmax * H);
@@ -488,6 +489,7 @@ hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* U
 hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                             const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st) {
     const int Lmax = D.max_diag;
+    if (small_bwd_supported(H, Lmax)) return launch_bwd_small(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     if (bwd16_supported(H, Lmax)) return launch_bwd16(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     if (const MfmaEntry* m = mfma_entry(H, Lmax)) {
         launch(m->bwd, dim3(4 * D.n), dim3(256), bwd_mfma_lds(H, Lmax), st, D, H, Lmax, Ul, Uu, stash,

@@ -354,8 +354,7 @@ struct F16Entry {
 #define MDL_F16(h, kx, bf, cg)                                                                                \
     {h, kx, bf, cg, F16Shape<h>::NB, F16Shape<h>::HP,                                                         \
      {k_fwd16<h, cg, 1, kx, bf>, k_fwd16<h, cg, 2, kx, bf>, k_fwd16<h, cg, 3, kx, bf>, k_fwd16<h, cg, 4, kx, bf>}}
-const F16Entry kF16[] = {MDL_F16(2, 1, false, 8),  MDL_F16(4, 1, false, 8),  MDL_F16(10, 2, false, 8),
-                         MDL_F16(16, 1, false, 4), MDL_F16(16, 1, true, 4),  MDL_F16(32, 1, false, 4),
+const F16Entry kF16[] = {MDL_F16(16, 1, false, 4), MDL_F16(16, 1, true, 4), MDL_F16(32, 1, false, 4),
                          MDL_F16(32, 1, true, 4),  MDL_F16(50, 5, false, 1)};
 #undef MDL_F16
 

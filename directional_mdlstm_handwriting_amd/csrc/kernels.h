@@ -146,6 +146,16 @@ bool bwd16_supported(int H, int Lmax);
 size_t bwd16_lds(int H, int Lmax);
 hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                         const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
+// wavefront kernels for small hidden sizes (H <= 10) on the vector ALUs, fp32, input projection fused
+bool small_fwd_supported(int H, int C, int dtype, int Lmax);
+bool small_bwd_supported(int H, int Lmax);
+size_t small_fwd_lds(int H, int Lmax);
+size_t small_bwd_lds(int H, int Lmax);
+hipError_t launch_fwd_small(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
+                            const float* b, const float* Ul, const float* Uu, float* stash, float* h_dirs,
+                            hipStream_t st);
+hipError_t launch_bwd_small(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
+                            const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z,
                             float* stash, float* h_dirs, hipStream_t st);
 hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st);

@@ -249,6 +249,13 @@ RAGGED = [
     # and a hidden size with none (H = 8, C = 3); these run the general fp32 kernels
     ([70, 12, 3], [80, 30, 5], 4, 16),
     ([5, 9, 13, 1], [11, 6, 2, 7], 3, 8),
+    # the vector-ALU kernels of small hidden sizes: H = 2 over a 100-cell diagonal, H = 10 over 25 and 26
+    # cells (partial last waves) and over 51 (their widest); 52 cells exceed them and take the general kernels
+    ([100, 1, 37], [150, 60, 2], 4, 2),
+    ([25, 30, 4], [40, 25, 9], 6, 10),
+    ([26, 2], [30, 26], 6, 10),
+    ([51, 3], [60, 5], 6, 10),
+    ([52, 3], [60, 5], 6, 10),
 ]
 
 
