@@ -16,6 +16,14 @@ largest error is within K_COND times the oracle's own largest response to such
 a one-ulp perturbation of all inputs and weights (the oracle run again on
 perturbed inputs, with a fixed seed). Every such use is printed. A wrong index
 or term gives errors of the order of the outputs themselves and fails either way.
+
+K_COND = 8. The one-ulp response covers one rounding of every input, while an
+fp32 evaluation also rounds every intermediate value of every cell. Measured on
+sixteen random word-like batches (the eight of test_random_word_like_batches and
+eight more drawn the same way), on tensors with elements outside the elementwise
+bound: a plain fp32 evaluation of these formulas (the library's general
+kernels) reaches 3.5 times the response, the matrix-core kernels 2.2 times.
+K_COND = 8 admits both with a margin of about 2.
 """
 
 import numpy as np
@@ -35,7 +43,7 @@ DEV = "cuda:0"
 F32_TOL = (1e-5, 1e-4)
 BF16_TOL = (1e-3, 2e-2)
 U32 = 2.0 ** -24  # fp32 unit roundoff: size of the input perturbation
-K_COND = 2.0      # allowed ratio of the largest error to the largest one-ulp perturbation response
+K_COND = 8.0      # allowed ratio of the largest error to the largest one-ulp perturbation response
 
 
 def _np(t):
@@ -257,6 +265,22 @@ RAGGED = [
     ([51, 3], [60, 5], 6, 10),
     ([52, 3], [60, 5], 6, 10),
 ]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_word_like_batches(seed):
+    """Random word-like batches (two to four images, h in [12, 40], w = clip(rint(h lognormal(1, 0.5)), 8,
+    200), C = 4, H = 16) on a 1024-wide canvas: the headline layer's kernels on chains of 30 to 240 steps."""
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(2, 5))
+    h = [int(v) for v in rng.integers(12, 41, n)]
+    w = [int(min(200, max(8, round(hh * rng.lognormal(1.0, 0.5))))) for hh in h]
+    P = random_layer(1100 + seed, 4, 16)
+    xs = random_images(1200 + seed, h, w, 4)
+    dys = cotangent(1300 + seed, h, w, 16)
+    g = run_layer(h, w, xs, P, canvas_w_min=1024, dys=dys)
+    o = oracle_layer(h, w, xs, P, canvas_w_min=1024, dys=dys)
+    check_layer(g, o)
 
 
 @pytest.mark.parametrize("case", range(len(RAGGED)))
