@@ -472,8 +472,8 @@ int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl
     if (Cout * (K + 1) > 16 * 512) return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: Cout*(4*H*kh*kw+1) above 8192");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
-    if (mdl::conv_wgrad_lds(H, kh, kw, Cout) > lmax)
-        return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: weight-gradient tile exceeds LDS");
+    if (mdl::conv_wgrad_lds(H, kh, kw, Cout) > lmax || mdl::conv_data_lds(H, kh, kw, Cout) > lmax)
+        return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: weight-gradient tile or weights exceed LDS");
     hipError_t e;
     {
         Timed t("conv_bwd");

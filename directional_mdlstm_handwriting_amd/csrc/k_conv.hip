@@ -14,7 +14,8 @@
 // with f = ((d H + k) kh + i) kw + j, the layout of Wc's trailing axes, and
 // block elements outside the level-k example read as zero (partial blocks at
 // the bottom and right edge are zero-padded). The data gradient scatters the
-// output gradient back through the same blocks, one thread per element of dh.
+// output gradient back through the same blocks, one thread per element of dh
+// (Wc staged in LDS).
 #include "kernels.h"
 
 namespace mdl {
@@ -102,9 +103,16 @@ __global__ __launch_bounds__(256) void k_conv_fwd(Dev Dk, Dev Dk1, const float* 
     }
 }
 
-// one thread per element of dh_k [4][Hc][Wc][H]
-__global__ void k_conv_bwd_data(Dev Dk, Dev Dk1, int H, int kh, int kw, const float* __restrict__ Wc, int Cout,
-                                const float* __restrict__ dx1, float* __restrict__ dhk) {
+// Data gradient: one thread per element of dh_k [4][Hc][Wc][H], workgroups striding over them; Wc sits in
+// LDS transposed to [f][Cout] (row stride Cout | 1), so a thread's Cout weights are consecutive.
+__global__ __launch_bounds__(256) void k_conv_bwd_data(Dev Dk, Dev Dk1, int H, int kh, int kw,
+                                                       const float* __restrict__ Wc, int Cout,
+                                                       const float* __restrict__ dx1, float* __restrict__ dhk) {
+    const int K = 4 * H * kh * kw;
+    const int CS = Cout | 1;
+    extern __shared__ float wt[];  // [K][CS]
+    for (int i = threadIdx.x; i < Cout * K; i += blockDim.x) wt[(i % K) * CS + i / K] = Wc[i];
+    __syncthreads();
     const int64_t P = (int64_t)Dk.Hc * Dk.Wc;
     const int64_t E = 4 * P * H;
     for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < E; t += (int64_t)gridDim.x * blockDim.x) {
@@ -121,8 +129,8 @@ __global__ void k_conv_bwd_data(Dev Dk, Dev Dk1, int H, int kh, int kw, const fl
                 const int r = ly / kh, i = ly - r * kh, c = lx / kw, j = lx - c * kw;
                 const int64_t p1 = (int64_t)(Dk1.real[4 * e] + r) * Dk1.Wc + Dk1.real[4 * e + 1] + c;
                 const float* g = dx1 + p1 * Cout;
-                for (int o = 0; o < Cout; ++o)
-                    v += g[o] * Wc[((((int64_t)o * 4 + d) * H + k) * kh + i) * kw + j];
+                const float* wr = wt + (((d * H + k) * kh + i) * kw + j) * CS;
+                for (int o = 0; o < Cout; ++o) v += g[o] * wr[o];
             }
         }
         dhk[t] = v;
@@ -233,6 +241,10 @@ size_t conv_fwd_lds(int H, int kh, int kw, int Cout) {
     return sizeof(float) * ((size_t)Cout * KS + CW_TILE * KS) + sizeof(BlockSrc) * CW_TILE;
 }
 
+size_t conv_data_lds(int H, int kh, int kw, int Cout) {
+    return sizeof(float) * 4 * (size_t)H * kh * kw * (size_t)(Cout | 1);
+}
+
 size_t conv_wgrad_lds(int H, int kh, int kw, int Cout) {
     const size_t K = 4 * (size_t)H * kh * kw;
     return sizeof(float) * (CW_TILE * K + CW_TILE * (size_t)Cout) + sizeof(BlockSrc) * CW_TILE;
@@ -251,8 +263,9 @@ hipError_t launch_conv_bwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k,
                            const float* Wc, int Cout, const float* dx_k1, float* dh_k, float* dWc, float* dbc,
                            float* part, hipStream_t st) {
     const int64_t E = 4 * (int64_t)Dk.Hc * Dk.Wc * H;
-    launch(k_conv_bwd_data, dim3(grid_for(E)), dim3(256), 0, st, Dk, Dk1, H, kh, kw, Wc, Cout, dx_k1,
-           dh_k);
+    const unsigned gd = grid_for(E) < 2048 ? grid_for(E) : 2048;  // each workgroup stages Wc once
+    launch(k_conv_bwd_data, dim3(gd), dim3(256), conv_data_lds(H, kh, kw, Cout), st, Dk, Dk1, H, kh, kw, Wc, Cout,
+           dx_k1, dh_k);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int K = 4 * H * kh * kw;

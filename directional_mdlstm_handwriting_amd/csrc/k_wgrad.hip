@@ -207,16 +207,17 @@ __global__ __launch_bounds__(256) void k_dx_cells(Dev D, int C, int H, const flo
 namespace {
 
 // Partial blocks summed in a fixed order, then routed to dWx / db / dUl / dUu. A workgroup takes 64
-// consecutive (direction, entry) slots (coalesced reads of each block's partial row) and 16 slices of the
-// blocks: slice j adds blocks j, j + 16, j + 32, ... into four accumulators in turn, and the 16 slice sums
-// are added in slice order through LDS. The loads of 16 blocks are issued before they are added, so each
-// thread keeps 16 reads in flight. The order depends only on the block count, so reruns are
-// bit-identical.
-constexpr int RED_X = 64, RED_Y = 16, RED_U = 16;
-__global__ __launch_bounds__(RED_X* RED_Y) void k_wgrad_reduce(const float* __restrict__ part, int nparts, int C,
-                                                               int H, float* __restrict__ dWx,
-                                                               float* __restrict__ dUl, float* __restrict__ dUu,
-                                                               float* __restrict__ db) {
+// consecutive (direction, entry) slots (coalesced reads of each block's partial row) and RY slices of the
+// blocks: slice j adds blocks j, j + RY, j + 2 RY, ... into four accumulators in turn, and the RY slice sums
+// are added in slice order through LDS. The loads of 16 blocks are issued before they are added (a missing
+// block reads as zero), so each thread keeps 16 reads in flight. RY is 16 for many blocks and 4 for few
+// (at most 64), so that a few blocks still fill the loads of one round. The order depends only on the
+// block count, so reruns are bit-identical.
+constexpr int RED_X = 64, RED_U = 16;
+template <int RY>
+__global__ __launch_bounds__(RED_X* RY) void k_wgrad_reduce(const float* __restrict__ part, int nparts, int C, int H,
+                                                            float* __restrict__ dWx, float* __restrict__ dUl,
+                                                            float* __restrict__ dUu, float* __restrict__ db) {
     const int G = 5 * H, R = C + 1 + 2 * H, E = R * G;
     const int tx = threadIdx.x % RED_X, ty = threadIdx.x / RED_X;
     const int64_t id = blockIdx.x * (int64_t)RED_X + tx;
@@ -226,24 +227,22 @@ __global__ __launch_bounds__(RED_X* RED_Y) void k_wgrad_reduce(const float* __re
     if (ok) {
         const float* p = part + id;
         float s4[4] = {0.f, 0.f, 0.f, 0.f};
-        int c = ty, j = 0;
-        for (; c + (RED_U - 1) * RED_Y < nparts; c += RED_U * RED_Y) {  // RED_U % 4 == 0: j is unchanged
+        for (int c = ty; c < nparts; c += RED_U * RY) {
             float v[RED_U];
 #pragma unroll
-            for (int u = 0; u < RED_U; ++u) v[u] = p[(int64_t)(c + u * RED_Y) * stride];
+            for (int u = 0; u < RED_U; ++u) v[u] = c + u * RY < nparts ? p[(int64_t)(c + u * RY) * stride] : 0.f;
 #pragma unroll
             for (int u = 0; u < RED_U; ++u) s4[u & 3] += v[u];
         }
-        for (; c < nparts; c += RED_Y, j = (j + 1) & 3) s4[j] += p[(int64_t)c * stride];
         s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
     }
-    __shared__ float red[RED_Y][RED_X];
+    __shared__ float red[RY][RED_X];
     red[ty][tx] = s;
     __syncthreads();
     if (ty != 0 || !ok) return;
     float t = red[0][tx];
 #pragma unroll
-    for (int y = 1; y < RED_Y; ++y) t += red[y][tx];
+    for (int y = 1; y < RY; ++y) t += red[y][tx];
     const int d = (int)(id / E), ent = (int)(id % E);
     const int r = ent / G, n = ent % G;
     if (r < C) dWx[((int64_t)d * C + r) * G + n] = t;
@@ -281,8 +280,11 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
         }
         nparts = D.nsegs;
     }
-    launch(k_wgrad_reduce, dim3((unsigned)((tot + RED_X - 1) / RED_X)), dim3(RED_X * RED_Y), 0, st, part,
-           (int)nparts, C, H, dWx, dUl, dUu, db);
+    const dim3 rgrid((unsigned)((tot + RED_X - 1) / RED_X));
+    if (nparts > 64)
+        launch(k_wgrad_reduce<16>, rgrid, dim3(RED_X * 16), 0, st, part, (int)nparts, C, H, dWx, dUl, dUu, db);
+    else
+        launch(k_wgrad_reduce<4>, rgrid, dim3(RED_X * 4), 0, st, part, (int)nparts, C, H, dWx, dUl, dUu, db);
     return hipGetLastError();
 }
 

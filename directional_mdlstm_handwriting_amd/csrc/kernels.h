@@ -176,6 +176,7 @@ hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k,
 int64_t conv_nchunks(const Dev& Dk1);
 size_t conv_fwd_lds(int H, int kh, int kw, int Cout);
 size_t conv_wgrad_lds(int H, int kh, int kw, int Cout);
+size_t conv_data_lds(int H, int kh, int kw, int Cout);
 hipError_t launch_conv_bwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, int Cout, const float* dx_k1, float* dh_k, float* dWc,
                            float* dbc, float* part, hipStream_t st);

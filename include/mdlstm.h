@@ -236,8 +236,8 @@ int mdl_blockconv_workspace_size(const mdl_layout* lk1, int32_t H, int32_t kh, i
  * Backward of mdl_blockconv_forward: dx_canvas_k1 [Hc'][Wc'][Cout] -> dh_dirs_k
  * [4][Hc][Wc][H] (zero outside the level-k real pixels), dWc, dbc (fixed-order
  * sums: partial sums over chunks of level-(k+1) canvas pixels, added in chunk
- * order). MDL_EUNSUPPORTED when Cout*(4*H*kh*kw+1) exceeds 8192 or one tile of
- * 16 blocks and their output gradients exceeds a workgroup's LDS.
+ * order). MDL_EUNSUPPORTED when Cout*(4*H*kh*kw+1) exceeds 8192, or when one
+ * tile of 16 blocks and their output gradients, or Wc, exceeds a workgroup's LDS.
  */
 int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1,
                            const void* d_desc_k1, const float* h_dirs_k, int32_t H, int32_t kh,
