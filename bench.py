@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true")
+    ap.add_argument("--no-literal", action="store_true", help="skip the exact-height / skewed-canvas comparison")
     ap.add_argument("--no-other", action="store_true", help="skip the line-like (or word-like) companion run")
     ap.add_argument("--no-stack", action="store_true", help="skip the three-level stack companion run")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
@@ -388,6 +389,28 @@ def main():
                              "200 packed (No Padding Please, Table IV)",
         }
         del padded
+
+    # the pages' own layout for the same images: exact-height rows, whole canvas skewed for column-parallel
+    # steps; its canvas, skew padding and dependent-step count next to this schedule's, and this schedule
+    # timed on the exact-height canvas
+    if not args.no_literal and wl.name != "tiny":
+        def skewed(li):
+            Hc, Wc = li["canvas_h"], li["canvas_w"]
+            cells = Hc * (Wc + Hc - 1)
+            return {"canvas": f"{Hc}x{Wc}", "canvas_waste": round(1.0 - N / (Hc * Wc), 4),
+                    "skewed_cells": cells, "skewed_padding_fraction": round(1.0 - N / cells, 4),
+                    "global_depth": Hc + Wc - 1, "cells_per_column": Hc}
+        torch.cuda.empty_cache()
+        ex = Runner(wl, "exact", device, stream)
+        ems, _, _, ek = ex.time(max(5, args.steps // 2), 2)
+        ei = ex.dl.info
+        out["paper_literal_layout"] = {
+            "alg1_rows": skewed(info), "exact_height_rows": skewed(ei),
+            "local_depth": info["max_depth"], "widest_local_diagonal": info["max_diag"],
+            "ms_per_step_alg1": ms, "ms_per_step_exact_height": ems,
+            "exact_height_kernels_ms": {k: round(v, 5) for k, v in ek.items()},
+        }
+        del ex
 
     # the other image batch of the pages' comparison, timed the same way (packed), for context
     other = {"word": "line", "line": "word"}.get(wl.name)

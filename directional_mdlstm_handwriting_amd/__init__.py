@@ -37,6 +37,7 @@ MDL_EUNSUPPORTED = -6
 
 MDL_PACK_ALG1 = 0
 MDL_PACK_PADDED = 1
+MDL_PACK_EXACT = 2
 MDL_F32 = 0
 MDL_BF16 = 1
 

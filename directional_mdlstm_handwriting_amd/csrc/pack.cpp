@@ -8,6 +8,8 @@
 // row may run on into the next, shorter bucket. Rows are then stacked with
 // separator rows in between, examples top-aligned, and the row still open at
 // the end is kept. Canvas width = max(canvas_w_min, widest example).
+// The exact-height mode (§V: one height per packed row, which the input-skewing
+// trick of §IV-A needs) also closes the row when its bucket is used up.
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -134,7 +136,10 @@ int build_layout(const int32_t* heights, const int32_t* widths, int32_t n, int32
                  int32_t sep, int32_t mode, Layout& L, std::string& err) {
     if (!heights || !widths) { err = "mdl_pack: null size array"; return MDL_EINVAL; }
     if (n < 1) { err = "mdl_pack: need n >= 1 examples"; return MDL_EINVAL; }
-    if (mode != MDL_PACK_ALG1 && mode != MDL_PACK_PADDED) { err = "mdl_pack: unknown mode"; return MDL_EINVAL; }
+    if (mode != MDL_PACK_ALG1 && mode != MDL_PACK_PADDED && mode != MDL_PACK_EXACT) {
+        err = "mdl_pack: unknown mode";
+        return MDL_EINVAL;
+    }
     if (sep < 0 || canvas_w_min < 1) { err = "mdl_pack: need sep >= 0 and canvas_w_min >= 1"; return MDL_EINVAL; }
     int32_t hmax = 0, wmax = 0;
     for (int e = 0; e < n; ++e) {
@@ -198,6 +203,11 @@ int build_layout(const int32_t* heights, const int32_t* widths, int32_t n, int32
                 row.clear();
                 x_end = 0;
             }
+        }
+        if (mode == MDL_PACK_EXACT && !row.empty()) {  // exact-height rows end with their bucket
+            L.rows.push_back(row);
+            row.clear();
+            x_end = 0;
         }
     }
     if (!row.empty()) L.rows.push_back(row);

@@ -16,8 +16,8 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MDL_BF16, MDL_F32, MDL_PACK_ALG1, MDL_PACK_PADDED, Layout, mdl_backward, mdl_blockconv_backward,
-               mdl_blockconv_forward, mdl_blockconv_workspace_size, mdl_dirsum_unpack, mdl_forward,
+from . import (MDL_BF16, MDL_F32, MDL_PACK_ALG1, MDL_PACK_EXACT, MDL_PACK_PADDED, Layout, mdl_backward,
+               mdl_blockconv_backward, mdl_blockconv_forward, mdl_blockconv_workspace_size, mdl_dirsum_unpack, mdl_forward,
                mdl_layout_device_size, mdl_layout_upload, mdl_pack, mdl_scatter, mdl_workspace_size)
 
 
@@ -52,7 +52,10 @@ class DeviceLayout:
 
     def __init__(self, heights, widths, canvas_w_min: int, sep: int = 1, mode: str = "packed",
                  device: str = "cuda", stream=None):
-        m = MDL_PACK_PADDED if mode == "padded" else MDL_PACK_ALG1
+        modes = {"packed": MDL_PACK_ALG1, "padded": MDL_PACK_PADDED, "exact": MDL_PACK_EXACT}
+        if mode not in modes:
+            raise ValueError(f"unknown packing mode {mode!r}; one of {sorted(modes)}")
+        m = modes[mode]
         self.layout: Layout = mdl_pack(heights, widths, canvas_w_min, sep, m)
         self.device = device
         nbytes, self.eid_off, self.border_off = mdl_layout_device_size(self.layout)

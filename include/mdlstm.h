@@ -57,6 +57,7 @@ extern "C" {
 /* packing modes */
 #define MDL_PACK_ALG1   0 /* shelf packing, Appendix B Algorithm 1 */
 #define MDL_PACK_PADDED 1 /* minimal per-batch padding ("batch-padding", §VII-C) */
+#define MDL_PACK_EXACT  2 /* shelf packing with exact-height rows (§V, §V-A prose) */
 
 /* element types of pixel tensors */
 #define MDL_F32  0
@@ -90,6 +91,11 @@ typedef struct mdl_layout mdl_layout; /* host object, immutable once built */
  * Algorithm 1's last step is not applied (it changes no cell's value).
  * MDL_PACK_PADDED (§VII-C, batch padding): slot e at (e*Hmax, 0) of size
  * Hmax x Wmax, the real pixels top-left; every slot cell is computed.
+ * MDL_PACK_EXACT (§V: the examples of one packed row share one height, as the
+ * input-skewing trick of §IV-A requires; §V-A step 2 fills rows inside each
+ * height bucket): as MDL_PACK_ALG1, but a row is also closed when its bucket
+ * is used up, so no row mixes heights. The kernels compute the same cells
+ * (the real pixels) in every packed mode; only the canvas differs.
  *
  * Errors: MDL_EINVAL for n < 1, null pointers, a size < 1, sep < 0,
  * canvas_w_min < 1 or an unknown mode; MDL_EOVERFLOW if Hc*Wc >= 2^31;
@@ -107,7 +113,7 @@ int mdl_layout_info(const mdl_layout* layout, int64_t* info);
 /*
  * Host copies of the rectangles, input order, as [n][4] = (y0, x0, h, w):
  * `rects` the computed region of each example, `real` its real pixels (equal
- * in MDL_PACK_ALG1 mode). Either pointer may be NULL.
+ * in the two shelf modes). Either pointer may be NULL.
  */
 int mdl_layout_rects(const mdl_layout* layout, int32_t* rects, int32_t* real);
 

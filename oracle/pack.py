@@ -21,6 +21,19 @@ Readings where the pages leave a step open:
 The padded mode is the "last-minute batch-padding" baseline of §VII-C: every
 example gets a slot of max-height x max-width, stacked vertically, the real
 pixels top-left, the rest zero padding that is computed like real cells.
+
+The exact-height mode is the other reading of the same section: §V requires
+that the examples of one packed row share one height (so that the rows can be
+skewed and un-skewed for the column-parallel computation of §IV-A), and step 2
+of §V-A fills rows inside each height bucket. Here a row is therefore also
+closed when its bucket runs out; everything else (bucket order, greedy choice,
+ties, separators) is as in the Algorithm 1 reading. ``skew`` / ``unskew`` and
+``skew_stats`` give the input-skewing trick of §IV-A (Figure 3; Algorithm 1's
+last step applies it to the whole packed tensor and mask): image row i is
+shifted right by i pixels, so that column k of the skewed grid holds exactly
+the cells on the canvas's global anti-diagonal y + x = k and depends only on
+column k - 1. A pass over the skewed canvas then takes Hc + Wc - 1 dependent
+column steps and computes every cell of the Hc x (Wc + Hc - 1) grid.
 """
 
 from __future__ import annotations
@@ -76,6 +89,15 @@ def _maps(Hc, Wc, rects):
 
 def pack_alg1(heights, widths, canvas_w_min: int, sep: int = 1) -> Layout:
     """Shelf packing by Algorithm 1 (literal reading, see module docstring)."""
+    return _shelf(heights, widths, canvas_w_min, sep, exact=False)
+
+
+def pack_exact(heights, widths, canvas_w_min: int, sep: int = 1) -> Layout:
+    """Shelf packing with exact-height rows (§V, §V-A prose reading): a row also closes when its bucket empties."""
+    return _shelf(heights, widths, canvas_w_min, sep, exact=True)
+
+
+def _shelf(heights, widths, canvas_w_min: int, sep: int, exact: bool) -> Layout:
     heights, widths = _check(heights, widths, canvas_w_min, sep)
     n = len(heights)
     Wc = max(int(canvas_w_min), max(widths))
@@ -106,6 +128,11 @@ def pack_alg1(heights, widths, canvas_w_min: int, sep: int = 1) -> Layout:
                 rows.append(row)
                 row = []
                 x_end = 0
+        if exact and row:
+            # exact-height rows: the bucket is used up, so is its row
+            rows.append(row)
+            row = []
+            x_end = 0
     if row:
         rows.append(row)
 
@@ -122,7 +149,7 @@ def pack_alg1(heights, widths, canvas_w_min: int, sep: int = 1) -> Layout:
     if Hc * Wc >= 2 ** 31:
         raise OverflowError("canvas too large")
     eid, border = _maps(Hc, Wc, rects)
-    return Layout(Hc, Wc, rects, rects.copy(), rows, eid, border, "packed")
+    return Layout(Hc, Wc, rects, rects.copy(), rows, eid, border, "exact" if exact else "packed")
 
 
 def pack_padded(heights, widths) -> Layout:
@@ -144,6 +171,8 @@ def pack(heights, widths, canvas_w_min: int, sep: int = 1, mode: str = "packed")
         return pack_alg1(heights, widths, canvas_w_min, sep)
     if mode == "padded":
         return pack_padded(heights, widths)
+    if mode == "exact":
+        return pack_exact(heights, widths, canvas_w_min, sep)
     raise ValueError(mode)
 
 
@@ -158,4 +187,44 @@ def waste(layout: Layout, heights, widths) -> dict:
         "canvas_waste": 1.0 - N / (layout.Hc * layout.Wc),
         "padded_cell_fraction": 1.0 - N / computed,
         "zpr": (computed - N) / N,
+    }
+
+
+def skew(canvas: np.ndarray) -> np.ndarray:
+    """Input-skewing trick (§IV-A, Figure 3): row i of an Hc x Wc (x ...) canvas moves right by i pixels into
+    an Hc x (Wc + Hc - 1) grid of zeros."""
+    Hc, Wc = canvas.shape[0], canvas.shape[1]
+    out = np.zeros((Hc, Wc + Hc - 1) + canvas.shape[2:], dtype=canvas.dtype)
+    for i in range(Hc):
+        out[i, i:i + Wc] = canvas[i]
+    return out
+
+
+def unskew(skewed: np.ndarray, Wc: int) -> np.ndarray:
+    """Inverse of ``skew``: row i is read back from columns i .. i + Wc - 1."""
+    Hc = skewed.shape[0]
+    out = np.zeros((Hc, Wc) + skewed.shape[2:], dtype=skewed.dtype)
+    for i in range(Hc):
+        out[i] = skewed[i, i:i + Wc]
+    return out
+
+
+def skew_stats(layout: Layout, heights, widths) -> dict:
+    """Work and depth of one direction's pass over the skewed canvas (§IV-A) next to the per-example local
+    diagonals: the skewed grid's cells are all computed (the mask zeroes the invalid ones), one column per
+    dependent step."""
+    h = np.asarray(heights, np.int64)
+    w = np.asarray(widths, np.int64)
+    N = int(np.sum(h * w))
+    Hc, Wc = layout.Hc, layout.Wc
+    cells = Hc * (Wc + Hc - 1)
+    return {
+        "canvas": [Hc, Wc],
+        "canvas_waste": 1.0 - N / (Hc * Wc),
+        "skewed_cells": cells,
+        "skewed_padding_fraction": 1.0 - N / cells,
+        "global_depth": Hc + Wc - 1,
+        "local_depth": int(np.max(h + w - 1)),
+        "cells_per_column": Hc,
+        "widest_local_diagonal": int(np.max(np.minimum(h, w))),
     }

@@ -49,7 +49,8 @@ def test_exports_every_declared_symbol():
 
 
 def _compare(h, w, cw, sep, mode="packed"):
-    lay = M.mdl_pack(h, w, cw, sep, M.MDL_PACK_PADDED if mode == "padded" else M.MDL_PACK_ALG1)
+    lay = M.mdl_pack(h, w, cw, sep, {"packed": M.MDL_PACK_ALG1, "padded": M.MDL_PACK_PADDED,
+                                     "exact": M.MDL_PACK_EXACT}[mode])
     ref = opack.pack(h, w, cw, sep, mode)
     assert (lay.Hc, lay.Wc) == (ref.Hc, ref.Wc)
     rects, real = M.mdl_layout_rects(lay)
@@ -90,6 +91,24 @@ def test_packer_edge_cases():
     _compare([4] * 4, [5, 2, 5, 3], 10, 1)
     _compare([1] * 5, [1] * 5, 1, 0)
     _compare([40] * 128, [200] * 128, 1024, 1)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("kind,cw", [("tiny", 8), ("word", 1024), ("line", 2048)])
+def test_exact_height_matches_oracle(kind, cw, seed):
+    h, w = make_sizes_only(kind, seed)
+    _compare(h, w, cw, 1, "exact")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_exact_height_matches_oracle_adversarial(seed):
+    rng = np.random.default_rng(700 + seed)
+    n = int(rng.integers(1, 129))
+    h = rng.integers(1, 7, n)
+    w = rng.integers(1, 20, n)
+    for sep in (0, 1, 3):
+        _compare(h, w, int(rng.integers(1, 25)), sep, "exact")
+    _compare([3, 2], [2, 3], 10, 1, "exact")
 
 
 @pytest.mark.parametrize("seed", range(3))

@@ -199,7 +199,8 @@ def check_layer(g, o, tol=F32_TOL):
 
 # ----------------------------------------------------------------------------------------- layout
 
-@pytest.mark.parametrize("name,mode", [("tiny", "packed"), ("word", "packed"), ("word", "padded"), ("line", "packed")])
+@pytest.mark.parametrize("name,mode", [("tiny", "packed"), ("word", "packed"), ("word", "padded"), ("word", "exact"),
+                                       ("line", "packed")])
 def test_device_maps_bit_exact(name, mode):
     wl = make_workload(name, 0)
     cw = wl.canvas_w_min[0]
@@ -306,6 +307,21 @@ def test_padded_mode_subset():
     dys = cotangent(9, h, w, wl.H)
     g = run_layer(h, w, xs, P, mode="padded", dys=dys)
     o = oracle_layer(h, w, xs, P, mode="padded", dys=dys)
+    check_layer(g, o)
+
+
+def test_exact_height_mode_subset():
+    """The exact-height packing (one height per packed row) moves examples to other canvas positions; each
+    example's outputs and the weight gradients stay those of the oracle."""
+    wl = make_workload("word", 3)
+    idx = [1, 4, 8, 15, 22, 31, 47]
+    h, w = wl.heights[idx], wl.widths[idx]
+    xs = [wl.xs[i] for i in idx]
+    P = wl.layers[0]
+    dys = cotangent(11, h, w, wl.H)
+    g = run_layer(h, w, xs, P, mode="exact", canvas_w_min=256, dys=dys)
+    o = oracle_layer(h, w, xs, P, mode="exact", canvas_w_min=256, dys=dys)
+    assert len(o["lay"].rows) > 1
     check_layer(g, o)
 
 
