@@ -228,12 +228,16 @@ class Runner:
 
 
 class StackRunner:
-    """The three-level stack (MDLSTM -> 2x4 block conv -> MDLSTM -> block conv -> MDLSTM, each level re-packed),
-    forward and backward over one batch, timed like Runner."""
+    """The three-level stack (MDLSTM -> 2x4 block conv -> MDLSTM -> block conv -> MDLSTM, each level re-packed)
+    and the model head (height collapse, shared fully-connected layer to 80 classes, CTC loss on synthetic
+    labels): forward, loss and backward over one batch, timed like Runner."""
 
     def __init__(self, wl, device, stream):
         import torch
-        from directional_mdlstm_handwriting_amd.layer import DeviceParams, LayerGrads, PackedStack, flat_input
+        import directional_mdlstm_handwriting_amd as M
+        from directional_mdlstm_handwriting_amd.layer import (CTCHead, DeviceParams, LayerGrads, PackedStack,
+                                                              flat_input)
+        from workloads import ctc_labels, head_params
         Hs = [P.H for P in wl.layers]
         couts = [c.b.shape[0] for c in wl.convs]
         self.st = PackedStack(wl.heights, wl.widths, wl.C, Hs, couts, wl.canvas_w_min, sep=wl.sep, device=device)
@@ -243,14 +247,21 @@ class StackRunner:
         self.cg = [(torch.empty_like(W), torch.empty_like(b)) for W, b in self.convs]
         self.x = flat_input(wl.xs, "f32", device)
         last = self.st.levels[-1]
-        self.dy = torch.as_tensor(np.random.default_rng(wl.seed + 101).standard_normal(last.y.numel()).astype(np.float32),
-                                  device=device)
+        _, real = M.mdl_layout_rects(last.dl.layout)
+        frames = real[:, 3]
+        Wfc, bfc = head_params(wl.seed, last.H)
+        self.head = CTCHead(last.dl, last.H, Wfc.shape[1], ctc_labels(wl.seed, frames))
+        self.Wfc, self.bfc = torch.as_tensor(Wfc, device=device), torch.as_tensor(bfc, device=device)
+        self.dWfc, self.dbfc = torch.empty_like(self.Wfc), torch.empty_like(self.bfc)
+        self.frames = int(frames.sum())
         self.dx = torch.empty(int(sum(x.size for x in wl.xs)), device=device)
         self.stream = stream
 
     def step(self):
-        self.st.forward(self.x, self.params, self.convs, self.stream)
-        self.st.backward(self.params, self.convs, self.dy, self.lg, self.cg, dx_flat=self.dx, stream=self.stream)
+        y = self.st.forward(self.x, self.params, self.convs, self.stream)
+        self.head.run(y, self.Wfc, self.bfc, self.dWfc, self.dbfc, stream=self.stream)
+        self.st.backward(self.params, self.convs, self.head.dy, self.lg, self.cg, dx_flat=self.dx,
+                         stream=self.stream)
 
     def time(self, steps, warmup):
         """ms per step with no events inside the timed region, and the breakdown pass's ms per step of each
@@ -443,9 +454,12 @@ def main():
             lv.append({"canvas": f"{li['canvas_h']}x{li['canvas_w']}", "real_pixels": li["real_pixels"],
                        "C": P.C, "H": P.H, "max_depth": li["max_depth"]})
         Ns = sum(v["real_pixels"] for v in lv)
+        loss = sr.head.loss.float().cpu().numpy()
         out["stack_workload"] = {
             "workload": f"stack: {ws_.n} word-like images, MDLSTM H={[P.H for P in ws_.layers]} with 2x4 block "
-                        f"convs to {[c.b.shape[0] for c in ws_.convs]} channels, seed {ws_.seed}",
+                        f"convs to {[c.b.shape[0] for c in ws_.convs]} channels, shared fully-connected head to "
+                        f"{sr.head.K} classes and CTC loss on synthetic labels, seed {ws_.seed}",
+            "ctc_frames": sr.frames, "ctc_loss_mean": float(loss.mean()),
             "value": 4 * Ns / (sms * 1e-3), "unit": "cell-direction updates/s (all three levels)",
             "ms_per_step": sms, "levels": lv,
             "kernels_ms_per_step": {k: round(v, 5) for k, v in sk.items()},

@@ -66,6 +66,9 @@ _SIGS = [
     ("mdl_blockconv_workspace_size", _I32, [_P, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     ("mdl_blockconv_backward", _I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ,
                                       _P]),
+    ("mdl_ctc_workspace_size", _I32, [_P, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    ("mdl_ctc_head", _I32, [_P, _P, _P, _I32, _P, _P, _I32, _P, _P, ctypes.c_int64, _I32, _P, _P, _P, _P, _P,
+                            _SZ, _P]),
     ("mdl_timing", _I32, [_I32]),
     ("mdl_timing_only", _I32, [ctypes.c_char_p]),
     ("mdl_timing_report", _I32, [_I32, _P, _P, _P, ctypes.POINTER(_I32)]),
@@ -232,6 +235,19 @@ def mdl_blockconv_forward(lk: Layout, d_desc_k, lk1: Layout, d_desc_k1, h_dirs_k
                           Cout: int, x_canvas_k1, stream=None):
     _check(_lib.mdl_blockconv_forward(lk.handle, _ptr(d_desc_k), lk1.handle, _ptr(d_desc_k1), _ptr(h_dirs_k), H, kh,
                                       kw, _ptr(Wc), _ptr(bc), Cout, _ptr(x_canvas_k1), _stream(stream)))
+
+
+def mdl_ctc_workspace_size(layout: Layout, H: int, K: int, max_label: int) -> int:
+    b = _SZ()
+    _check(_lib.mdl_ctc_workspace_size(layout.handle, H, K, max_label, ctypes.byref(b)))
+    return b.value
+
+
+def mdl_ctc_head(layout: Layout, d_desc, y_flat, H: int, Wfc, bfc, K: int, labels, label_off, n_labels: int,
+                 max_label: int, loss, dy_flat, dWfc, dbfc, ws, ws_bytes: int, stream=None):
+    _check(_lib.mdl_ctc_head(layout.handle, _ptr(d_desc), _ptr(y_flat), H, _ptr(Wfc), _ptr(bfc), K, _ptr(labels),
+                             _ptr(label_off), n_labels, max_label, _ptr(loss), _ptr(dy_flat), _ptr(dWfc),
+                             _ptr(dbfc), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def mdl_blockconv_workspace_size(lk1: Layout, H: int, kh: int, kw: int, Cout: int) -> int:

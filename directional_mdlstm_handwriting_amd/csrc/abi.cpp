@@ -486,6 +486,67 @@ int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl
     GUARD_END
 }
 
+static int ctc_tmax(const mdl::Layout& L) {
+    int t = 0;
+    for (int e = 0; e < L.n; ++e) t = std::max(t, L.real[4 * e + 3]);
+    return t;
+}
+
+static int check_ctc(const char* fn, const mdl_layout* layout, int32_t H, int32_t K, int32_t max_label) {
+    if (!layout) return fail(MDL_EINVAL, std::string(fn) + ": null layout");
+    if (H < 1 || K < 2 || max_label < 0)
+        return fail(MDL_EINVAL, std::string(fn) + ": need H >= 1, K >= 2 and max_label >= 0");
+    if (H > 1024 || K > 4096 || max_label > 65535)
+        return fail(MDL_EUNSUPPORTED, std::string(fn) + ": H above 1024, K above 4096 or max_label above 65535");
+    const int64_t T = ctc_tmax(L_of(layout));
+    const int64_t S = 2 * (int64_t)max_label + 1;
+    if (T * std::max<int64_t>(std::max<int64_t>(H, K), S) >= (int64_t(1) << 31))
+        return fail(MDL_EOVERFLOW, std::string(fn) + ": frames times classes, hidden units or label states reach 2^31");
+    return MDL_OK;
+}
+
+int mdl_ctc_workspace_size(const mdl_layout* layout, int32_t H, int32_t K, int32_t max_label, size_t* bytes) {
+    GUARD_BEGIN
+    if (!bytes) return fail(MDL_EINVAL, "mdl_ctc_workspace_size: null argument");
+    int rc = check_ctc("mdl_ctc_workspace_size", layout, H, K, max_label);
+    if (rc) return rc;
+    const mdl::Layout& L = L_of(layout);
+    *bytes = sizeof(float) * (size_t)mdl::ctc_ws(L.n, ctc_tmax(L), H, K, max_label).total;
+    return MDL_OK;
+    GUARD_END
+}
+
+int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_flat, int32_t H, const float* Wfc,
+                 const float* bfc, int32_t K, const int32_t* labels, const int32_t* label_off, int64_t n_labels,
+                 int32_t max_label, float* loss, float* dy_flat, float* dWfc, float* dbfc, void* ws,
+                 size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    int rc = check_ctc("mdl_ctc_head", layout, H, K, max_label);
+    if (rc) return rc;
+    if (!d_desc || !y_flat || !Wfc || !bfc || !label_off || !loss || !ws)
+        return fail(MDL_EINVAL, "mdl_ctc_head: null tensor");
+    if (n_labels < 0 || (n_labels > 0 && !labels)) return fail(MDL_EINVAL, "mdl_ctc_head: bad label array");
+    if ((dWfc == nullptr) != (dbfc == nullptr))
+        return fail(MDL_EINVAL, "mdl_ctc_head: give both dWfc and dbfc, or neither");
+    const mdl::Layout& L = L_of(layout);
+    const int Tmax = ctc_tmax(L);
+    const size_t need = sizeof(float) * (size_t)mdl::ctc_ws(L.n, Tmax, H, K, max_label).total;
+    if (ws_bytes < need) return fail(MDL_ESIZE, "mdl_ctc_head: workspace smaller than mdl_ctc_workspace_size");
+    size_t lds = 0;
+    rc = max_lds(lds);
+    if (rc) return rc;
+    hipError_t e;
+    {
+        Timed t("ctc_head");
+        e = mdl::launch_ctc_head(make_dev(layout, d_desc), y_flat, H, Wfc, bfc, K, labels, label_off, n_labels,
+                                 max_label, Tmax, static_cast<float*>(ws), loss, dy_flat, dWfc, dbfc, lds,
+                                 static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_ctc_head");
+    return MDL_OK;
+    GUARD_END
+}
+
 int mdl_timing(int32_t enable) {
     std::lock_guard<std::mutex> lk(g_tmu);
     g_timing = enable != 0;

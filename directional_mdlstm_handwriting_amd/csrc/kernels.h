@@ -181,4 +181,43 @@ hipError_t launch_conv_bwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k,
                            const float* Wc, int Cout, const float* dx_k1, float* dh_k, float* dWc,
                            float* dbc, float* part, hipStream_t st);
 
+// model head (height collapse, shared fully-connected layer, CTC loss); workspace sizes in floats
+struct CtcWs {
+    int64_t smax = 0;   // states of the longest blank-padded label, 2 Umax + 1
+    int64_t slot = 0;   // per-example slot (a multiple of 4 floats): the arrays of ctc_offsets
+    int64_t part = 0;   // offset of the per-example weight-gradient partials
+    int64_t total = 0;
+};
+// offsets (floats, each a multiple of 4) of one example's arrays after w0 leading floats: Y [Tmax][H],
+// log-probabilities and dz [Tmax][K] (float), log alpha and log beta [Tmax][smax] (double), then the
+// blank-padded label (smax ints) where the arrays sit in LDS
+struct CtcOff {
+    int64_t y, ly, dz, la, lb, lp;
+};
+MDL_HD inline int64_t ctc_al4(int64_t v) { return (v + 3) & ~int64_t(3); }
+MDL_HD inline CtcOff ctc_offsets(int64_t w0, int Tmax, int H, int K, int64_t smax) {
+    CtcOff o;
+    o.y = ctc_al4(w0);
+    o.ly = ctc_al4(o.y + (int64_t)Tmax * H);
+    o.dz = ctc_al4(o.ly + (int64_t)Tmax * K);
+    o.la = ctc_al4(o.dz + (int64_t)Tmax * K);
+    o.lb = o.la + 2 * (int64_t)Tmax * smax;
+    o.lp = ctc_al4(o.lb + 2 * (int64_t)Tmax * smax);
+    return o;
+}
+MDL_HD inline CtcWs ctc_ws(int n, int Tmax, int H, int K, int Umax) {
+    CtcWs w;
+    w.smax = 2 * (int64_t)Umax + 1;
+    w.slot = ctc_offsets(0, Tmax, H, K, w.smax).lp;
+    w.part = (int64_t)n * w.slot;
+    w.total = w.part + (int64_t)n * ((int64_t)H + 1) * K;
+    return w;
+}
+// LDS bytes of the head kernel's in-LDS form; the launcher takes it when it fits lds_limit
+size_t ctc_lds_bytes(int Tmax, int H, int K, int Umax);
+hipError_t launch_ctc_head(const Dev& D, const float* y_flat, int H, const float* Wfc, const float* bfc, int K,
+                           const int32_t* labels, const int32_t* label_off, int64_t nlab, int Umax, int Tmax,
+                           float* ws, float* loss, float* dy_flat, float* dW, float* db, size_t lds_limit,
+                           hipStream_t st);
+
 }  // namespace mdl

@@ -5,7 +5,9 @@ kernel. ``PackedLayer`` holds one layout's descriptor and a layer's workspace
 and runs scatter -> forward -> direction sum/un-pack, and the backward.
 ``PackedStack`` chains three levels with block-strided convolutions, each
 level re-packed from the previous level's output sizes ("No Padding Please",
-§V-A: packing happens just before each MDLSTM layer).
+§V-A: packing happens just before each MDLSTM layer). ``CTCHead`` runs the
+model head (height collapse, shared fully-connected layer, CTC loss) on the
+last level's output.
 """
 
 from __future__ import annotations
@@ -18,7 +20,8 @@ import torch
 
 from . import (MDL_BF16, MDL_F32, MDL_PACK_ALG1, MDL_PACK_EXACT, MDL_PACK_PADDED, Layout, mdl_backward,
                mdl_blockconv_backward, mdl_blockconv_forward, mdl_blockconv_workspace_size, mdl_dirsum_unpack, mdl_forward,
-               mdl_layout_device_size, mdl_layout_upload, mdl_pack, mdl_scatter, mdl_workspace_size)
+               mdl_layout_device_size, mdl_layout_upload, mdl_pack, mdl_scatter, mdl_workspace_size,
+               mdl_ctc_head, mdl_ctc_workspace_size)
 
 
 def _dev(a, device, dtype=torch.float32):
@@ -190,3 +193,37 @@ class PackedStack:
                 mdl_blockconv_backward(prev.dl.layout, prev.dl.desc, lay.dl.layout, lay.dl.desc, prev.h_dirs, prev.H,
                                        self.kh, self.kw, W, self.couts[lvl - 1], self.dx_canvas[lvl - 1],
                                        self.dh_dirs[lvl - 1], dW, db, wsb, nb, stream)
+
+
+class CTCHead:
+    """The model head on a layout's direction-summed output: rows summed into frames, one fully-connected layer
+    to K classes (0 = blank), CTC loss per example and the gradients of their sum (mdl_ctc_head). Labels are
+    fixed at construction: one sequence of classes 1..K-1 per example of the layout, in input order."""
+
+    def __init__(self, dl: DeviceLayout, H: int, K: int, labels: Sequence[Sequence[int]],
+                 max_label: Optional[int] = None):
+        n = dl.info["n"]
+        if len(labels) != n:
+            raise ValueError(f"need one label per example ({n}), got {len(labels)}")
+        self.dl, self.K, self.H = dl, K, H
+        flat = np.array([c for lab in labels for c in lab], dtype=np.int32)
+        off = np.zeros(n + 1, dtype=np.int32)
+        off[1:] = np.cumsum([len(lab) for lab in labels])
+        self.max_label = int(max(len(lab) for lab in labels)) if max_label is None else int(max_label)
+        dev = dl.device
+        self.n_labels = int(flat.size)
+        self.labels = torch.as_tensor(flat if flat.size else np.zeros(1, np.int32), device=dev)
+        self.label_off = torch.as_tensor(off, device=dev)
+        self.ws_bytes = mdl_ctc_workspace_size(dl.layout, H, K, self.max_label)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.loss = torch.empty(n, dtype=torch.float32, device=dev)
+        self.dy = torch.empty(dl.info["real_pixels"] * H, dtype=torch.float32, device=dev)
+
+    def run(self, y_flat: torch.Tensor, Wfc: torch.Tensor, bfc: torch.Tensor, dWfc: Optional[torch.Tensor] = None,
+            dbfc: Optional[torch.Tensor] = None, want_dy: bool = True, stream=None):
+        """Loss per example into self.loss, the gradient of the summed loss with respect to y_flat into self.dy
+        (if want_dy), dWfc / dbfc if given."""
+        mdl_ctc_head(self.dl.layout, self.dl.desc, y_flat, self.H, Wfc, bfc, self.K, self.labels, self.label_off,
+                     self.n_labels, self.max_label, self.loss, self.dy if want_dy else None, dWfc, dbfc, self.ws,
+                     self.ws_bytes, stream)
+        return self.loss

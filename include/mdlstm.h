@@ -252,9 +252,43 @@ int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl
                            void* stream);
 
 /*
+ * Model head after the last MDLSTM level ("No Padding Please" §II / Figure 1:
+ * one fully-connected layer shared across the four directions, trained with
+ * CTC, the pages' reference [13]). For each example e of the layout, with
+ * y_e = y_flat's [h][w][H] block (the direction sum, as mdl_dirsum_unpack
+ * writes it):
+ *   frames     Y[t][j] = sum over rows r of y_e[r][t][j], t < w (height collapse)
+ *   logits     z[t][k] = sum_j Y[t][j] Wfc[j][k] + bfc[k], k < K, class 0 = blank
+ *   loss[e]    = -ln p(l_e | z), the CTC probability of label l_e under the
+ *                per-frame softmax of z (forward-backward recursion in log space)
+ * and the gradients of sum_e loss[e]: dy_flat (every row of a frame receives
+ * that frame's dz.Wfc^T), dWfc [H][K], dbfc [K].
+ * Labels (device, int32): example e's label is labels[label_off[e] ..
+ * label_off[e+1]-1], classes 1..K-1; label_off has n+1 entries; n_labels is
+ * the length of `labels`; max_label bounds every label's length and sizes the
+ * workspace. An example whose label cannot be aligned to its w frames gets
+ * loss +inf and no gradient; one whose offsets leave [0, n_labels], decrease,
+ * or whose label is longer than max_label or holds a class outside 1..K-1
+ * gets loss NaN and no gradient (these are found on the device).
+ * dy_flat may be NULL; dWfc and dbfc are both given or both NULL. dWfc / dbfc
+ * are fixed-order sums (per-example partials added in example order).
+ * ws: >= mdl_ctc_workspace_size bytes, device, contents not kept.
+ * Errors: MDL_EINVAL for null tensors or H < 1, K < 2, max_label < 0;
+ * MDL_EUNSUPPORTED for H > 1024, K > 4096 or max_label > 65535; MDL_EOVERFLOW
+ * when the widest example's frames times max(H, K, 2 max_label + 1) reach 2^31;
+ * MDL_ESIZE for a short workspace.
+ */
+int mdl_ctc_workspace_size(const mdl_layout* layout, int32_t H, int32_t K, int32_t max_label, size_t* bytes);
+int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_flat, int32_t H,
+                 const float* Wfc, const float* bfc, int32_t K, const int32_t* labels,
+                 const int32_t* label_off, int64_t n_labels, int32_t max_label, float* loss,
+                 float* dy_flat, float* dWfc, float* dbfc, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Kernel timing (measurement support). mdl_timing(1) makes every later launch
  * of a kernel group (names: "build_maps", "scatter", "zero_fill", "projection",
- * "fwd_wavefront", "dirsum", "bwd_wavefront", "wgrad", "conv_fwd", "conv_bwd")
+ * "fwd_wavefront", "dirsum", "bwd_wavefront", "wgrad", "conv_fwd", "conv_bwd",
+ * "ctc_head")
  * hand each of its dispatches a HIP event pair that the dispatch itself
  * records (hipExtLaunchKernel): the group's time runs from its first
  * dispatch's start to its last one's end, with no marker packets between

@@ -182,3 +182,30 @@ def test_workspace_grows_with_size():
     b = M.mdl_workspace_size(lay, 4, 32)
     T = lay.info["computed_cells"]
     assert b > a >= 4 * T * (6 * 16 + 5 * 16) * 4
+
+
+def test_ctc_head_error_codes():
+    lib = M.library()
+    lay = M.mdl_pack([3, 4], [5, 6], 8, 1)
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_ctc_workspace_size(lay, 4, 1, 3)
+    assert e.value.code == M.MDL_EINVAL
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_ctc_workspace_size(lay, 2000, 10, 3)
+    assert e.value.code == M.MDL_EUNSUPPORTED
+    with pytest.raises(M.MdlError) as e:
+        M.mdl_ctc_workspace_size(lay, 4, 10, -1)
+    assert e.value.code == M.MDL_EINVAL
+    # slot per example: Tmax (H + 2K) floats (rounded up to even), then Tmax (2 Umax + 1) doubles twice;
+    # then (H + 1) K partial sums per example
+    ws = M.mdl_ctc_workspace_size(lay, 4, 10, 3)
+    assert ws == 4 * (2 * (6 * (4 + 20) + 4 * 6 * 7) + 2 * 5 * 10)
+    # device entry point: validation before any launch
+    assert lib.mdl_ctc_head(lay.handle, 1, 1, 4, 1, 1, 10, 1, 1, 4, 3, 1, None, 1, None, 1, ws, None) == M.MDL_EINVAL
+    assert "dWfc and dbfc" in M.mdl_last_error()
+    assert lib.mdl_ctc_head(lay.handle, 1, 1, 4, 1, 1, 10, 1, None, 4, 3, 1, None, None, None, 1, ws,
+                            None) == M.MDL_EINVAL
+    assert lib.mdl_ctc_head(lay.handle, 1, 1, 4, 1, 1, 10, None, 1, 4, 3, 1, None, None, None, 1, ws,
+                            None) == M.MDL_EINVAL
+    assert lib.mdl_ctc_head(lay.handle, 1, 1, 4, 1, 1, 10, 1, 1, 4, 3, 1, None, None, None, 1, ws - 4,
+                            None) == M.MDL_ESIZE

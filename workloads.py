@@ -213,3 +213,25 @@ def cotangent(seed: int, heights, widths, H: int) -> List[np.ndarray]:
     rng = np.random.default_rng(seed + 7919)
     return [rng.standard_normal((int(h), int(w), H)).astype(np.float32)
             for h, w in zip(heights, widths)]
+
+
+CTC_CLASSES = 80  # 79 symbols and the CTC blank: the size of the IAM character set the pages train on
+
+
+def head_params(seed: int, H: int, K: int = CTC_CLASSES):
+    """Seeded N(0, 0.1) float32 weights [H][K] and bias [K] of the model head's fully-connected layer."""
+    rng = np.random.default_rng(seed + 104729)
+    W = rng.normal(0.0, 0.1, (H, K)).astype(np.float32)
+    b = rng.normal(0.0, 0.1, K).astype(np.float32)
+    return W, b
+
+
+def ctc_labels(seed: int, frames, K: int = CTC_CLASSES) -> List[List[int]]:
+    """One synthetic label per example with T = frames[e] frames: length U ~ U{1..(T+1)//2} (so every label,
+    repeats included, can be aligned), classes ~ U{1..K-1}."""
+    rng = np.random.default_rng(seed + 130363)
+    out = []
+    for T in frames:
+        U = int(rng.integers(1, (int(T) + 1) // 2 + 1))
+        out.append([int(c) for c in rng.integers(1, K, U)])
+    return out
