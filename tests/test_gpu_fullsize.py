@@ -1,4 +1,5 @@
-"""Full-size parity: the word, line and stack workloads at their real sizes, checked on sampled examples.
+"""Full-size parity: the word, line and stack workloads at their real sizes, checked on sampled examples
+(the word batch also on its exact-height-rows canvas).
 
 The layer runs over the whole packed canvas with the layout, shapes and
 launches the bench times. Examples on a packed canvas are independent (the
@@ -39,14 +40,14 @@ def offsets(heights, widths, K):
     return np.concatenate([[0], np.cumsum(sizes)])
 
 
-@pytest.mark.parametrize("name,n_random", [("word", 4), ("line", 0)])
-def test_layer_full_size_sampled(name, n_random):
+@pytest.mark.parametrize("name,n_random,mode", [("word", 4, "packed"), ("word", 2, "exact"), ("line", 0, "packed")])
+def test_layer_full_size_sampled(name, n_random, mode):
     wl = make_workload(name, 0)
     P, H, C = wl.layers[0], wl.H, wl.C
     idx = sample(wl.heights, wl.widths, n_random, 17)
-    print(f"[gpu] full-size {name}: {wl.n} images, sampled {idx}", flush=True)
+    print(f"[gpu] full-size {name} ({mode}): {wl.n} images, sampled {idx}", flush=True)
     dys = [d if e in idx else np.zeros_like(d) for e, d in enumerate(cotangent(11, wl.heights, wl.widths, H))]
-    g = run_layer(wl.heights, wl.widths, wl.xs, P, canvas_w_min=wl.canvas_w_min[0], sep=wl.sep,
+    g = run_layer(wl.heights, wl.widths, wl.xs, P, mode=mode, canvas_w_min=wl.canvas_w_min[0], sep=wl.sep,
                   x_dtype=wl.x_dtype, dys=dys)
     _, real = M.mdl_layout_rects(g["dl"].layout)
     y, dx = _np(g["layer"].y), _np(g["dx"])
