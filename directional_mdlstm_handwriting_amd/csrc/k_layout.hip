@@ -6,6 +6,7 @@
 // by its original index and size. All of these are HBM-bound copies: one
 // thread per output element, consecutive threads on consecutive addresses.
 #include "kernels.h"
+#include "devmath.h"
 
 namespace mdl {
 
@@ -71,6 +72,58 @@ __global__ void k_scatter(Dev D, const T* __restrict__ xf, int C, T* __restrict_
     }
 }
 
+// Whole-pixel forms of the copies above, for the common shapes: one thread per canvas pixel (scatter, a pixel's
+// C channels as one 8- or 16-byte vector V) or per 16-byte group of a pixel's values (zero fill, direction sum),
+// canvas rows on blockIdx.y (a grid-stride loop past 65535 rows), 32-bit index arithmetic inside a row or an
+// example. Same results as the element forms, bit for bit.
+template <typename V>
+__global__ void k_scatter_px(Dev D, const V* __restrict__ xf, V* __restrict__ xc) {
+    const int x = blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= D.Wc) return;
+    for (int y = blockIdx.y; y < D.Hc; y += gridDim.y) {
+        const int64_t p = (int64_t)y * D.Wc + x;
+        const int e = D.eid[p];
+        V v = {};
+        if (e >= 0) {
+            const int ry = y - D.real[4 * e], rx = x - D.real[4 * e + 1];
+            const int rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+            if (ry < rh && rx < rw) v = xf[D.flat_off[e] + (int64_t)ry * rw + rx];
+        }
+        xc[p] = v;
+    }
+}
+
+// K4 = K / 4 float4 groups per pixel; plane4 = Hc * Wc * K4
+__global__ void k_zero_outside4(Dev D, f32x4* __restrict__ buf, int K4, int planes, int64_t plane4) {
+    const int q = blockIdx.x * blockDim.x + threadIdx.x;  // float4 group within the canvas row
+    if (q >= D.Wc * K4) return;
+    const int x = q / K4;
+    for (int y = blockIdx.y; y < D.Hc; y += gridDim.y) {
+        if (D.eid[(int64_t)y * D.Wc + x] >= 0) continue;
+        const int64_t i = (int64_t)y * D.Wc * K4 + q;
+        for (int pl = 0; pl < planes; ++pl) buf[pl * plane4 + i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+}
+
+// blockIdx.y = example; H4 = H / 4
+__global__ void k_dirsum4(Dev D, const f32x4* __restrict__ hd, int H4, f32x4* __restrict__ y) {
+    const int e = blockIdx.y;
+    const int y0 = D.real[4 * e], x0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+    const int cnt = rh * rw * H4;
+    const int64_t plane = (int64_t)D.Hc * D.Wc * H4;
+    f32x4* out = y + D.flat_off[e] * H4;
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
+        const int pix = q / H4, k = q - pix * H4;
+        const int ly = pix / rw, lx = pix - ly * rw;
+        const int64_t src = ((int64_t)(y0 + ly) * D.Wc + x0 + lx) * H4 + k;
+        f32x4 s = hd[src];
+        s += hd[src + plane];
+        s += hd[src + 2 * plane];
+        s += hd[src + 3 * plane];
+        out[q] = s;
+    }
+}
+
 // blockIdx.y = example: y_flat[e][r][c][k] = sum_d h_dirs[d][y0+r][x0+c][k], d = 0..3 in order
 __global__ void k_dirsum(Dev D, const float* __restrict__ hd, int H, float* __restrict__ y) {
     const int e = blockIdx.y;
@@ -103,9 +156,20 @@ __global__ void k_zero_outside(Dev D, float* __restrict__ buf, int K, int planes
 
 }  // namespace
 
+namespace {
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+unsigned rows_grid(int Hc) { return (unsigned)(Hc < 65535 ? Hc : 65535); }
+}  // namespace
+
 hipError_t launch_zero_outside(const Dev& D, float* buf, int K, int planes, hipStream_t st) {
     const int64_t E = (int64_t)D.Hc * D.Wc * K;
-    launch(k_zero_outside, dim3(grid_for(E)), dim3(TPB), 0, st, D, buf, K, planes);
+    if (K % 4 == 0 && aligned(buf, 16) && (int64_t)D.Wc * (K / 4) < (int64_t(1) << 31)) {
+        const int K4 = K / 4;
+        launch(k_zero_outside4, dim3((unsigned)(((int64_t)D.Wc * K4 + TPB - 1) / TPB), rows_grid(D.Hc)), dim3(TPB), 0,
+               st, D, reinterpret_cast<f32x4*>(buf), K4, planes, E / 4);
+    } else {
+        launch(k_zero_outside, dim3(grid_for(E)), dim3(TPB), 0, st, D, buf, K, planes);
+    }
     return hipGetLastError();
 }
 
@@ -123,7 +187,13 @@ hipError_t launch_build_maps(const Dev& D, hipStream_t st) {
 
 hipError_t launch_scatter(const Dev& D, const void* x_flat, int C, int dtype, void* x_canvas, hipStream_t st) {
     const int64_t E = (int64_t)D.Hc * D.Wc * C;
-    if (dtype == 0)
+    const int pixel_bytes = C * (dtype == 0 ? 4 : 2);
+    const dim3 pgrid((unsigned)((D.Wc + TPB - 1) / TPB), rows_grid(D.Hc));
+    if (pixel_bytes == 16 && aligned(x_flat, 16) && aligned(x_canvas, 16))
+        launch(k_scatter_px<u32x4>, pgrid, dim3(TPB), 0, st, D, (const u32x4*)x_flat, (u32x4*)x_canvas);
+    else if (pixel_bytes == 8 && aligned(x_flat, 8) && aligned(x_canvas, 8))
+        launch(k_scatter_px<u32x2>, pgrid, dim3(TPB), 0, st, D, (const u32x2*)x_flat, (u32x2*)x_canvas);
+    else if (dtype == 0)
         launch(k_scatter<float>, dim3(grid_for(E)), dim3(TPB), 0, st, D,
                (const float*)x_flat, C, (float*)x_canvas);
     else
@@ -133,7 +203,11 @@ hipError_t launch_scatter(const Dev& D, const void* x_flat, int C, int dtype, vo
 }
 
 hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st) {
-    launch(k_dirsum, dim3(64, D.n), dim3(TPB), 0, st, D, h_dirs, H, y_flat);
+    if (H % 4 == 0 && aligned(h_dirs, 16) && aligned(y_flat, 16) && D.N * (H / 4) < (int64_t(1) << 31))
+        launch(k_dirsum4, dim3(64, D.n), dim3(TPB), 0, st, D, reinterpret_cast<const f32x4*>(h_dirs), H / 4,
+               reinterpret_cast<f32x4*>(y_flat));
+    else
+        launch(k_dirsum, dim3(64, D.n), dim3(TPB), 0, st, D, h_dirs, H, y_flat);
     return hipGetLastError();
 }
 
