@@ -40,8 +40,11 @@ __device__ inline void bst(float v, __amdgpu_buffer_rsrc_t r, int off) {
 __device__ inline float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
 __device__ inline float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ inline float sigm(float z) { return frcp(1.0f + fexp(-z)); }
+// e^-2x as 2^(x (-2 log2 e)): -2 times the float log2 e is exact, and scaling by a power of two commutes with
+// rounding, so this is bit for bit exp2((-2x) log2 e) at one multiply fewer.
+constexpr float kM2L2E = -2.0f * 1.44269504088896341f;
 __device__ inline float ftanh(float x) {
-    const float big = __builtin_fmaf(2.0f, frcp(1.0f + fexp(-2.0f * x)), -1.0f);
+    const float big = __builtin_fmaf(2.0f, frcp(1.0f + __builtin_amdgcn_exp2f(x * kM2L2E)), -1.0f);
     const float x2 = x * x;
     const float p = __builtin_fmaf(x2, __builtin_fmaf(x2, -17.0f / 315.0f, 2.0f / 15.0f), -1.0f / 3.0f);
     const float small = __builtin_fmaf(x * x2, p, x);
