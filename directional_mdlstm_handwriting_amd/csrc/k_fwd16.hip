@@ -244,6 +244,22 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
+    // input projection x.Wx + b of one diagonal's A-row cells on the fp32 matrix cores, the bias seeding the
+    // accumulators. It does not depend on the recurrence, so each step forms the next diagonal's projection
+    // after its own gate arithmetic, while the matrix cores are otherwise idle: the step's dependent matrix
+    // phase then holds only the recurrent product.
+    f32x4 accx[5];
+    auto project = [&](const float (&xv)[KX]) {
+#pragma unroll
+        for (int g = 0; g < 5; ++g) accx[g] = f32x4{bz[g], bz[g], bz[g], bz[g]};
+#pragma unroll
+        for (int ks = 0; ks < KX; ++ks)
+#pragma unroll
+            for (int g = 0; g < 5; ++g)
+                accx[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv[ks], Bx[g][ks], accx[g], 0, 0, 0);
+    };
+    project(xs[0]);
+
     // diagonal s at position POS = s mod 4 of the unrolled loop: buffer s & 1 is written and 1 - (s & 1)
     // read; input set POS is consumed and set (POS + kZD) mod 4 refilled for diagonal s + kZD
     auto step = [&](int s, auto POSc) {
@@ -278,17 +294,9 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             cl[r] = *reinterpret_cast<const float*>(csp + (jo[r] < Ml ? ol : ozc));
             cu[r] = *reinterpret_cast<const float*>(csp + ((jo[r] >= Tu && jo[r] < L) ? ou : ozc));
         }
-        f32x4 acc[5], accx[5];
+        f32x4 acc[5];
 #pragma unroll
-        for (int g = 0; g < 5; ++g) {
-            acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accx[g] = f32x4{bz[g], bz[g], bz[g], bz[g]};
-        }
-#pragma unroll
-        for (int ks = 0; ks < KX; ++ks)
-#pragma unroll
-            for (int g = 0; g < 5; ++g)
-                accx[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[POS][ks], Bx[g][ks], accx[g], 0, 0, 0);
+        for (int g = 0; g < 5; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < KB; ++t)
 #pragma unroll
@@ -324,6 +332,7 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{gg, c}), rS2, ok ? el * 8 : kOOB,
                                                   0, 0);
         }
+        project(xs[(POS + 1) & 3]);  // diagonal s + 1 (prefetched two steps ago)
         st += L;
         __syncthreads();
     };
