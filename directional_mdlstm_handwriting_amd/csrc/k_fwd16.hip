@@ -261,13 +261,12 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     project(xs[0]);
 
     // diagonal s at position POS = s mod 4 of the unrolled loop: buffer s & 1 is written and 1 - (s & 1)
-    // read; input set POS is consumed and set (POS + kZD) mod 4 refilled for diagonal s + kZD
+    // read; at the end of the step input set (POS + 1) mod 4 feeds the projection of diagonal s + 1 and set
+    // (POS + kZD) mod 4, whose diagonal s - 1 is done with, is refilled for diagonal s + kZD
     auto step = [&](int s, auto POSc) {
         constexpr int POS = decltype(POSc)::value;
         constexpr int CB = POS & 1;
         const int L = diag_len(s);
-        load_x(s + kZD, xs[(POS + kZD) & 3]);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
         const bool dl = s >= w;
         const int lo = dl ? s - (w - 1) : 0;
         const int Ml = L < s - lo ? L : s - lo;  // position j has a left predecessor iff j < Ml
@@ -333,6 +332,9 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
                                                   0, 0);
         }
         project(xs[(POS + 1) & 3]);  // diagonal s + 1 (prefetched two steps ago)
+        // refill the set just consumed with diagonal s + kZD; issued here, its address arithmetic stays off
+        // the dependent path between the barrier and the recurrent product
+        load_x(s + kZD, xs[(POS + kZD) & 3]);
         st += L;
         __syncthreads();
     };
