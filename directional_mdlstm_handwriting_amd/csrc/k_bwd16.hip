@@ -285,12 +285,12 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
         constexpr int POS = decltype(POSc)::value;
         constexpr int CB = POS & 1;
         const int L = diag_len(s), L1 = diag_len(s + 1);
-        // the prefetch: at the top of the step, except in the matrix waves of one-block shapes, which issue it
-        // inside phase 1 so that its address arithmetic overlaps their LDS reads and products
-        constexpr bool late = NB == 1;
+        // the prefetch: at the top of the step, except in the matrix waves, which issue it inside phase 1 so
+        // that its address arithmetic overlaps their LDS reads and products (every wave issues the same memory
+        // operations per step)
         const int stz_now = stz;
         stz -= diag_len(s - kPD - 1);
-        if (!(late && mat)) load_f(s - kPD, stz_now, fs[(POS + kPD) & 3]);
+        if (!mat) load_f(s - kPD, stz_now, fs[(POS + kPD) & 3]);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
         const int dn = s >= w - 1 ? 1 : 0;  // successors of position j: right j - dn, down j + 1 - dn
         const unsigned char* ap = smem + (1 - CB) * ABUF;
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
                         er[r][bi] = *reinterpret_cast<const int*>(ep + ((orow + r) * NB + bi) * 4);
             };
             if constexpr (NB == 1) read_er();
-            if constexpr (late) load_f(s - kPD, stz_now, fs[(POS + kPD) & 3]);
+            load_f(s - kPD, stz_now, fs[(POS + kPD) & 3]);
             f32x4 acc[2][NB];
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
