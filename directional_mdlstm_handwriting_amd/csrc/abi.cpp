@@ -310,8 +310,8 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     uint8_t* wsb = static_cast<uint8_t*>(ws);
     float* Z = reinterpret_cast<float*>(wsb + W.zda);
     float* stash = reinterpret_cast<float*>(wsb + W.stash);
-    hipError_t e;
-    {
+    hipError_t e = hipSuccess;
+    if (!fused) {  // the f16 forward clears h outside the computed regions itself, in its smallest units' tail
         Timed t("zero_fill");
         e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
     }

@@ -348,6 +348,22 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     if (s < S) step(s, IC<0>{});
     if (s + 1 < S) step(s + 1, IC<1>{});
     if (s + 2 < S) step(s + 2, IC<2>{});
+
+    // h outside every computed region reads zero: the second half of the launch order (the smallest units,
+    // done first) clears it, one band of canvas rows per workgroup, while the larger units still run
+    const int half = (int)gridDim.x / 2, zb = (int)blockIdx.x - half, nz = (int)gridDim.x - half;
+    if (zb >= 0) {
+        const int64_t r0 = (int64_t)D.Hc * zb / nz, r1 = (int64_t)D.Hc * (zb + 1) / nz;
+        const int64_t plane = (int64_t)D.Hc * D.Wc * H;
+        const int64_t n = (r1 - r0) * D.Wc * H;
+        float* base = hdirs + r0 * D.Wc * H;
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const int64_t px = i / H;  // H is a compile-time constant here
+            if (D.eid[r0 * D.Wc + px] >= 0) continue;
+#pragma unroll
+            for (int d4 = 0; d4 < 4; ++d4) base[d4 * plane + i] = 0.f;
+        }
+    }
 }
 
 typedef void (*Fwd16Kernel)(Dev, const void*, int, const float*, const float*, const float*, const float*, float*,
