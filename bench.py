@@ -66,13 +66,14 @@ def link_count(rects):
     return sum(4 * (int(h) * (int(w) - 1) + (int(h) - 1) * int(w)) for (_, _, h, w) in rects)
 
 
-def kernel_model(info, rects, C, H, x_bytes, nchunks=None):
+def kernel_model(info, rects, C, H, x_bytes, nchunks=None, fwd_zero=False):
     """Algorithmic HBM bytes and flops of one launch of each kernel group (one layer, one step).
 
     T = computed cells per direction, N = real pixels; every tensor is counted
     once at its storage size, so re-reads show up as traffic above these bytes.
     The recurrent flops count 10 H^2 per predecessor link (a 5H x H matrix-vector
-    product), both in the forward and in the backward pass.
+    product), both in the forward and in the backward pass. fwd_zero: the forward
+    wavefront also zeroes h outside the computed regions (no zero-fill launch).
     """
     T = info["computed_cells"]
     N = info["real_pixels"]
@@ -84,7 +85,8 @@ def kernel_model(info, rects, C, H, x_bytes, nchunks=None):
     return {
         # x (canvas pixels) in for each direction; gate stash (i, f_l, f_u, o, g, c) and h out; the input
         # projection x Wx + b is computed in the same kernel
-        "fwd_wavefront": (4 * T * (C * x_bytes + 7 * H * f), rec + 4 * T * 2 * C * G),
+        "fwd_wavefront": (4 * T * (C * x_bytes + 7 * H * f) + (4 * (P - T) * H * f if fwd_zero else 0),
+                          rec + 4 * T * 2 * C * G),
         # four h planes in, y out
         "dirsum": (N * 5 * H * f, 3 * N * H),
         # gate stash and dy in (dy once per direction), dA (5H gate pre-activation gradients) out
@@ -348,7 +350,7 @@ def main():
     # roofline of the dominant kernel group, from HIP events its dispatches recorded in the timed region
     rects, _ = M.mdl_layout_rects(packed.dl.layout)
     H, C = wl.H, wl.C
-    model = kernel_model(info, rects, C, H, 2 if wl.x_dtype == "bf16" else 4)
+    model = kernel_model(info, rects, C, H, 2 if wl.x_dtype == "bf16" else 4, fwd_zero="zero_fill" not in kern)
     roof = roofline(dom, dom_ms, model)
     roof["traffic"] = measured_traffic(dom, wl.name)
     per_kernel = {k: roofline(k, v, model) for k, v in kern.items() if k in model}
@@ -432,7 +434,7 @@ def main():
         oms, _, _, ok = ro.time(max(5, args.steps // 2), 2)
         oi = ro.dl.info
         orects, _ = M.mdl_layout_rects(ro.dl.layout)
-        omodel = kernel_model(oi, orects, wo.C, wo.H, 2 if wo.x_dtype == "bf16" else 4)
+        omodel = kernel_model(oi, orects, wo.C, wo.H, 2 if wo.x_dtype == "bf16" else 4, fwd_zero="zero_fill" not in ok)
         out["other_workload"] = {
             "workload": f"{wo.name}: {wo.n} images, C={wo.C}, H={wo.H}, seed {wo.seed}, canvas "
                         f"{oi['canvas_h']}x{oi['canvas_w']}, x {wo.x_dtype}",

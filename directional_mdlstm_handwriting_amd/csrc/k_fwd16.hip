@@ -351,17 +351,19 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
 
     // h outside every computed region reads zero: the second half of the launch order (the smallest units,
     // done first) clears it, one band of canvas rows per workgroup, while the larger units still run
+    // (a layout whose computed regions fill the canvas, as the padded stack does, has nothing to clear)
     const int half = (int)gridDim.x / 2, zb = (int)blockIdx.x - half, nz = (int)gridDim.x - half;
-    if (zb >= 0) {
-        const int64_t r0 = (int64_t)D.Hc * zb / nz, r1 = (int64_t)D.Hc * (zb + 1) / nz;
-        const int64_t plane = (int64_t)D.Hc * D.Wc * H;
-        const int64_t n = (r1 - r0) * D.Wc * H;
-        float* base = hdirs + r0 * D.Wc * H;
-        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-            const int64_t px = i / H;  // H is a compile-time constant here
-            if (D.eid[r0 * D.Wc + px] >= 0) continue;
+    const int64_t npx = (int64_t)D.Hc * D.Wc;
+    if (zb >= 0 && D.T < npx) {
+        const int64_t p0 = (int64_t)D.Hc * zb / nz * D.Wc, p1 = (int64_t)D.Hc * (zb + 1) / nz * D.Wc;
+        const int64_t plane = npx * H;
+        for (int64_t p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
+            if (D.eid[p] >= 0) continue;
+            float* q = hdirs + p * H;
 #pragma unroll
-            for (int d4 = 0; d4 < 4; ++d4) base[d4 * plane + i] = 0.f;
+            for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+                for (int k = 0; k < H; ++k) q[d4 * plane + k] = 0.f;
         }
     }
 }
