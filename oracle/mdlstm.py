@@ -42,7 +42,12 @@ Forms
 * ``forward_vec`` / ``backward_vec``: the same arithmetic, all cells of one
   local anti-diagonal of every example at once (the diagonal parallelism of
   §I / RETURNN §4.2); checked against the brute forms.
-All arithmetic in float64.
+All arithmetic in float64. The per-diagonal forms also take a numeric context
+(``num``): the floating-point type of every array and the elementary functions
+(exponential, tanh, division). The default is float64 with NumPy's functions;
+a float32 context evaluates the same formulas in single precision, which the
+tests use to measure how far valid fp32 evaluations scatter around the exact
+result and the CPU timing uses as the float32 form.
 """
 
 from __future__ import annotations
@@ -56,13 +61,32 @@ from .pack import BIT_D, BIT_L, BIT_R, BIT_U
 DIRS = ((+1, +1), (+1, -1), (-1, +1), (-1, -1))
 
 
-def _p64(P):
-    return (np.asarray(P.Wx, np.float64), np.asarray(P.Ul, np.float64),
-            np.asarray(P.Uu, np.float64), np.asarray(P.b, np.float64))
+class Num:
+    """Numeric context of the per-diagonal forms: array type and elementary functions."""
+
+    def __init__(self, dtype=np.float64):
+        self.dtype = np.dtype(dtype)
+
+    def exp(self, z):
+        return np.exp(z)
+
+    def tanh(self, z):
+        return np.tanh(z)
+
+    def div(self, a, b):
+        return a / b
 
 
-def sigmoid(z):
-    return 1.0 / (1.0 + np.exp(-z))
+F64 = Num(np.float64)
+
+
+def _p64(P, dtype=np.float64):
+    return (np.asarray(P.Wx, dtype), np.asarray(P.Ul, dtype),
+            np.asarray(P.Uu, dtype), np.asarray(P.b, dtype))
+
+
+def sigmoid(z, num=F64):
+    return num.div(1.0, 1.0 + num.exp(-z))
 
 
 def _pred_bits(d):
@@ -70,21 +94,21 @@ def _pred_bits(d):
     return (BIT_L if sx > 0 else BIT_R), (BIT_U if sy > 0 else BIT_D)
 
 
-def _cell(xv, hl, cl, hu, cu, Wx, Ul, Uu, b, H):
+def _cell(xv, hl, cl, hu, cu, Wx, Ul, Uu, b, H, num=F64):
     a = xv @ Wx + b + hl @ Ul + hu @ Uu
-    i = sigmoid(a[..., 0:H])
-    fl = sigmoid(a[..., H:2 * H])
-    fu = sigmoid(a[..., 2 * H:3 * H])
-    o = sigmoid(a[..., 3 * H:4 * H])
-    g = np.tanh(a[..., 4 * H:5 * H])
+    i = sigmoid(a[..., 0:H], num)
+    fl = sigmoid(a[..., H:2 * H], num)
+    fu = sigmoid(a[..., 2 * H:3 * H], num)
+    o = sigmoid(a[..., 3 * H:4 * H], num)
+    g = num.tanh(a[..., 4 * H:5 * H])
     c = fl * cl + fu * cu + i * g
-    h = o * np.tanh(c)
+    h = o * num.tanh(c)
     return h, c, np.concatenate([i, fl, fu, o, g], axis=-1)
 
 
-def _cell_grad(dh, dc_in, gates, c, cl, cu, H):
+def _cell_grad(dh, dc_in, gates, c, cl, cu, H, num=F64):
     i, fl, fu, o, g = (gates[..., k * H:(k + 1) * H] for k in range(5))
-    tc = np.tanh(c)
+    tc = num.tanh(c)
     do = dh * tc
     dc = dc_in + dh * o * (1.0 - tc * tc)
     da = np.concatenate([dc * g * i * (1.0 - i),
@@ -222,52 +246,54 @@ def diagonals(rects, d):
     return out
 
 
-def forward_vec(xc, rects, P):
+def forward_vec(xc, rects, P, num=F64):
     """Same as forward_canvas_brute, one local diagonal at a time."""
-    Wx, Ul, Uu, b = _p64(P)
-    xc = np.asarray(xc, np.float64)
+    ft = num.dtype
+    Wx, Ul, Uu, b = _p64(P, ft)
+    xc = np.asarray(xc, ft)
     Hc, Wc, _ = xc.shape
     H = Ul.shape[1]
-    hd = np.zeros((4, Hc, Wc, H))
-    cd = np.zeros((4, Hc, Wc, H))
-    gd = np.zeros((4, Hc, Wc, 5 * H))
+    hd = np.zeros((4, Hc, Wc, H), ft)
+    cd = np.zeros((4, Hc, Wc, H), ft)
+    gd = np.zeros((4, Hc, Wc, 5 * H), ft)
     for d in range(4):
         sy, sx = DIRS[d]
         for (Y, X, VL, VU) in diagonals(rects, d):
             m = len(Y)
-            hl = np.zeros((m, H)); cl = np.zeros((m, H))
-            hu = np.zeros((m, H)); cu = np.zeros((m, H))
+            hl = np.zeros((m, H), ft); cl = np.zeros((m, H), ft)
+            hu = np.zeros((m, H), ft); cu = np.zeros((m, H), ft)
             hl[VL] = hd[d, Y[VL], X[VL] - sx]
             cl[VL] = cd[d, Y[VL], X[VL] - sx]
             hu[VU] = hd[d, Y[VU] - sy, X[VU]]
             cu[VU] = cd[d, Y[VU] - sy, X[VU]]
-            h, c, g = _cell(xc[Y, X], hl, cl, hu, cu, Wx[d], Ul[d], Uu[d], b[d], H)
+            h, c, g = _cell(xc[Y, X], hl, cl, hu, cu, Wx[d], Ul[d], Uu[d], b[d], H, num)
             hd[d, Y, X], cd[d, Y, X], gd[d, Y, X] = h, c, g
     return hd, cd, gd
 
 
-def backward_vec(xc, rects, P, hd, cd, gd, dhd):
+def backward_vec(xc, rects, P, hd, cd, gd, dhd, num=F64):
     """Same as backward_canvas_brute, one local diagonal at a time, in reverse."""
-    Wx, Ul, Uu, b = _p64(P)
-    xc = np.asarray(xc, np.float64)
+    ft = num.dtype
+    Wx, Ul, Uu, b = _p64(P, ft)
+    xc = np.asarray(xc, ft)
     Hc, Wc, C = xc.shape
     H = Ul.shape[1]
-    dxc = np.zeros((Hc, Wc, C))
+    dxc = np.zeros((Hc, Wc, C), ft)
     dWx, dUl, dUu, db = (np.zeros_like(a) for a in (Wx, Ul, Uu, b))
     for d in range(4):
         sy, sx = DIRS[d]
-        dh_acc = np.array(dhd[d], np.float64)
-        dc_acc = np.zeros((Hc, Wc, H))
+        dh_acc = np.array(dhd[d], ft)
+        dc_acc = np.zeros((Hc, Wc, H), ft)
         for (Y, X, VL, VU) in reversed(diagonals(rects, d)):
             m = len(Y)
-            hl = np.zeros((m, H)); cl = np.zeros((m, H))
-            hu = np.zeros((m, H)); cu = np.zeros((m, H))
+            hl = np.zeros((m, H), ft); cl = np.zeros((m, H), ft)
+            hu = np.zeros((m, H), ft); cu = np.zeros((m, H), ft)
             hl[VL] = hd[d, Y[VL], X[VL] - sx]
             cl[VL] = cd[d, Y[VL], X[VL] - sx]
             hu[VU] = hd[d, Y[VU] - sy, X[VU]]
             cu[VU] = cd[d, Y[VU] - sy, X[VU]]
             gates = gd[d, Y, X]
-            da, dc, fl, fu = _cell_grad(dh_acc[Y, X], dc_acc[Y, X], gates, cd[d, Y, X], cl, cu, H)
+            da, dc, fl, fu = _cell_grad(dh_acc[Y, X], dc_acc[Y, X], gates, cd[d, Y, X], cl, cu, H, num)
             # the left predecessors of distinct cells are distinct, likewise the upper ones
             dh_acc[Y[VL], X[VL] - sx] += da[VL] @ Ul[d].T
             dc_acc[Y[VL], X[VL] - sx] += dc[VL] * fl[VL]
@@ -286,20 +312,20 @@ def backward_vec(xc, rects, P, hd, cd, gd, dhd):
 # whole layer on a packed canvas: per-example inputs in, per-example outputs out
 # ----------------------------------------------------------------------------------------------
 
-def layer_forward(layout, xs: Sequence[np.ndarray], P, brute=False):
+def layer_forward(layout, xs: Sequence[np.ndarray], P, brute=False, num=F64):
     """Scatter -> 4-direction forward -> (direction sum, un-pack).
 
-    Returns (ys, cache) with ys[e] [h][w][H]."""
+    Returns (ys, cache) with ys[e] [h][w][H]. ``num`` applies to the per-diagonal form."""
     from .canvas import scatter, dirsum_unpack
     xc = scatter(layout, xs)
     if brute:
         hd, cd, gd = forward_canvas_brute(xc, layout.eid, layout.border, P)
     else:
-        hd, cd, gd = forward_vec(xc, layout.rects, P)
+        hd, cd, gd = forward_vec(xc, layout.rects, P, num)
     return dirsum_unpack(layout, hd), (xc, hd, cd, gd)
 
 
-def layer_backward(layout, P, cache, dys: Sequence[np.ndarray] = None, dhd=None, brute=False):
+def layer_backward(layout, P, cache, dys: Sequence[np.ndarray] = None, dhd=None, brute=False, num=F64):
     """Backward of layer_forward for per-example output gradients ``dys`` (each
     direction receives the same gradient through the direction sum), or for a
     per-direction canvas gradient ``dhd`` [4][Hc][Wc][H].
@@ -313,5 +339,5 @@ def layer_backward(layout, P, cache, dys: Sequence[np.ndarray] = None, dhd=None,
     if brute:
         res = backward_canvas_brute(xc, layout.eid, layout.border, P, hd, cd, gd, dhd)
     else:
-        res = backward_vec(xc, layout.rects, P, hd, cd, gd, dhd)
+        res = backward_vec(xc, layout.rects, P, hd, cd, gd, dhd, num)
     return (unpack(layout, res[0]),) + tuple(res[1:])
