@@ -6,11 +6,22 @@
 // the recurrent product
 //     a(cell) = Z(cell) + [h_left, h_up](cell) . [Ul; Uu]
 // runs on v_mfma_f32_16x16x32_f16, which moves 8x the multiply-adds per
-// cycle of the fp32 matrix instruction. Both operands are split into f16
-// pairs, x = hi + lo, and the product keeps the three terms
-// hi.hi + hi.lo + lo.hi (the dropped lo.lo term is below 2^-21 of the
-// product), accumulated in fp32: fp32-class accuracy at 3 f16 instructions per
-// 32-wide K block instead of 8 fp32 ones. f16 has a narrow exponent range, so
+// cycle of the fp32 matrix instruction. h is split into an f16 pair
+// h = hi + lo (about 22 bits), the weights into three f16 pieces
+// U = hi + lo + r (r, the rounding residue of the pair, makes the weights
+// exact to about 2^-33), and the product keeps the four terms
+// h_hi.r + h_lo.U_hi + h_hi.U_lo + h_hi.U_hi, accumulated in fp32 in that
+// order (smallest first), at 4 f16 instructions per 32-wide K block instead of
+// 8 fp32 ones. Dropping r (a pair holds U only to about 2^-22 of each weight)
+// perturbs every weight by a fixed amount in every cell, an error that the
+// long chains of the recurrence accumulate coherently: on long word-like
+// chains that alone put the outputs and gradients about twice as far from
+// the exact result as plain fp32 evaluations are (measured against the
+// float64 oracle with a float32 emulation of this arithmetic). The terms
+// dropped now (h_lo times U_lo and r) are below 2^-21 of a product and vary
+// from cell to cell, as fp32 rounding does. At H = 50 the residue's registers
+// would spill, so that shape (short chains only: the third level of the stack)
+// keeps the pair. f16 has a narrow exponent range, so
 // h (|h| < 1) is scaled by 2^14 and each weight column by its own power of
 // two (its largest magnitude lands in [2^14, 2^15)); the accumulator is scaled
 // back exactly before x.Wx + b is added.
@@ -59,6 +70,7 @@ struct F16Shape {
     static constexpr int NB = (H + 15) / 16;       // blocks of 16 hidden units
     static constexpr int HP = (H + 7) / 8 * 8;     // h_left / h_up segment in the K dimension
     static constexpr int KB = (2 * HP + 31) / 32;  // K blocks of 32
+    static constexpr bool R3 = NB <= 2;            // weights as three f16 pieces (registers allow it)
     static_assert(NB <= 4, "hidden size above 64");
 };
 
@@ -76,6 +88,7 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
                                                                      float* __restrict__ hdirs) {
     using Sh = F16Shape<H>;
     constexpr int HP = Sh::HP, KB = Sh::KB;
+    constexpr bool R3 = Sh::R3;
     constexpr int G = 5 * H;
     const int u = D.units[blockIdx.x];
     const int e = u >> 2, d = u & 3;
@@ -88,8 +101,8 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     const int kc = kok ? kk : 0;
 
     // B operand: lane holds rows 32t + 8q .. +7 of column g*H + kk of [Ul; Uu] (Ul row k at K index k,
-    // Uu row k at HP + k, zeros elsewhere), scaled per column by 2^E and split into f16 hi + lo.
-    f16x8 Bh[5][KB], Bl[5][KB];
+    // Uu row k at HP + k, zeros elsewhere), scaled per column by 2^E and split into f16 hi + lo + r.
+    f16x8 Bh[5][KB], Bl[5][KB], Br[5][R3 ? KB : 1];
     float us[5];  // 2^-(E + 14) times the gate's fold: undoes both scalings
 #pragma unroll
     for (int g = 0; g < 5; ++g) {
@@ -120,10 +133,13 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
         for (int t = 0; t < KB; ++t)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
+                const float vs = ldexpf(v[t][i], E);
                 _Float16 hi, lo;
-                split16(ldexpf(v[t][i], E), hi, lo);
+                split16(vs, hi, lo);
                 Bh[g][t][i] = hi;
                 Bl[g][t][i] = lo;
+                // vs - hi and then - lo are exact in fp32 (each operand holds the leading bits of the other)
+                if constexpr (R3) Br[g][t][i] = (_Float16)((vs - (float)hi) - (float)lo);
             }
     }
 
@@ -300,9 +316,10 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
         for (int t = 0; t < KB; ++t)
 #pragma unroll
             for (int g = 0; g < 5; ++g) {
-                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[t], Bh[g][t], acc[g], 0, 0, 0);
-                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[t], Bl[g][t], acc[g], 0, 0, 0);
+                if constexpr (R3) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[t], Br[g][t], acc[g], 0, 0, 0);
                 acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al[t], Bh[g][t], acc[g], 0, 0, 0);
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[t], Bl[g][t], acc[g], 0, 0, 0);
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[t], Bh[g][t], acc[g], 0, 0, 0);
             }
         const int ph = HB + lo * DA + s * DS;  // h offset of diagonal position 0, minus 4 kk
         const int pe = st * H;                 // stash element of diagonal position 0

@@ -1,4 +1,4 @@
-// pack.cpp — the example packer ("No Padding Please", §V, §V-A, Appendix B Algorithm 1)
+// pack.cpp — the example packer ("No Padding Please", §V, §V-A, §IX-B (packing algorithm details, Algorithm 1))
 // and the padded-stack baseline (§VII-C), as integer host code.
 //
 // Shelf packing: examples are bucketed by height and the buckets visited from

@@ -55,7 +55,7 @@ extern "C" {
 #define MDL_EUNSUPPORTED (-6) /* size combination this build does not handle (e.g. LDS limit) */
 
 /* packing modes */
-#define MDL_PACK_ALG1   0 /* shelf packing, Appendix B Algorithm 1 */
+#define MDL_PACK_ALG1   0 /* shelf packing, §IX-B (packing algorithm details, Algorithm 1) */
 #define MDL_PACK_PADDED 1 /* minimal per-batch padding ("batch-padding", §VII-C) */
 #define MDL_PACK_EXACT  2 /* shelf packing with exact-height rows (§V, §V-A prose) */
 
@@ -81,7 +81,7 @@ typedef struct mdl_layout mdl_layout; /* host object, immutable once built */
  * mdl_pack — place n examples of sizes heights[e] x widths[e] (host arrays) on a
  * canvas. Host-only, integer, allocates only the returned layout.
  *
- * MDL_PACK_ALG1 (§V, §V-A, Appendix B Algorithm 1): canvas width
+ * MDL_PACK_ALG1 (§V, §V-A, §IX-B (packing algorithm details, Algorithm 1)): canvas width
  * Wc = max(canvas_w_min, max width); examples are bucketed by height and the
  * buckets visited tallest first; rows are filled with the widest example of the
  * current bucket that still fits (ties: lowest index), `sep` separator pixels

@@ -9,7 +9,7 @@ only module both sides use is ``workloads`` (seeded inputs, no arithmetic of
 the method).
 
 Modules:
-  pack       example packing (Appendix B, Algorithm 1) and the padded stack
+  pack       example packing (§IX-B (packing algorithm details, Algorithm 1)) and the padded stack
   canvas     scatter onto the canvas, direction sum and un-packing (§V-A)
   mdlstm     the cell, forward and 2D BPTT, per-cell and per-diagonal forms
   blockconv  block-strided convolution with tensor-list chunking (§V-B)

@@ -2,8 +2,8 @@
 
 Follows "No Padding Please", §V (tile examples in a 2D grid, separator pixels
 between them, a binary mask), §V-A (bucket by height, fill rows greedily with
-the widest still-fitting example, tile rows with separators) and Appendix B,
-Algorithm 1 (the packing loop). The skew of §IV-A / Algorithm 1's last step is
+the widest still-fitting example, tile rows with separators) and §IX-B
+(packing algorithm details, Algorithm 1: the packing loop). The skew of §IV-A / Algorithm 1's last step is
 an implementation device for convolution-based MDLSTMs and does not change any
 cell's value, so the canvas here stays unskewed.
 

@@ -9,26 +9,33 @@ relative resolution as outputs of order one.
 
 Long diagonals make the recurrence ill-conditioned: the exact result for the
 given fp32 inputs moves by up to about 1e-3 of its largest magnitude when every
-input is changed by one fp32 unit in the last place, so no fp32 evaluation can
-meet an elementwise bound there (measured: a plain fp32 evaluation misses it as
-well). A tensor that misses the elementwise bound therefore passes only if its
-largest error is within K_COND times the oracle's own largest response to such
-a one-ulp perturbation of all inputs and weights (the oracle run again on
-perturbed inputs, with a fixed seed). Every such use is printed. A wrong index
-or term gives errors of the order of the outputs themselves and fails either way.
+input is changed by one fp32 unit in the last place. There a valid fp32
+evaluation does not meet the elementwise bound as a rule: the oracle's own
+formulas evaluated in float32 with faithfully rounded exp, tanh and division
+miss it by up to hundreds of elements (test_tolerance_cpu). A tensor that misses
+it therefore passes only if its largest error is within K_COND times the
+oracle's own largest response to a one-ulp perturbation of all inputs and
+weights (the oracle run again on perturbed inputs, with a fixed seed). Every
+such use is recorded: a ConditioningWarning, and a list at the end of the run.
+A wrong index or term gives errors of the order of the outputs themselves and
+fails either way.
 
-K_COND = 8. The one-ulp response covers one rounding of every input, while an
-fp32 evaluation also rounds every intermediate value of every cell. Measured on
-sixteen random word-like batches (the eight of test_random_word_like_batches and
-eight more drawn the same way), on tensors with elements outside the elementwise
-bound: a plain fp32 evaluation of these formulas (the library's general
-kernels) reaches 3.5 times the response, the matrix-core kernels 2.2 times.
-K_COND = 8 admits both with a margin of about 2.
+K_COND = 2. Where those float32 evaluations miss the elementwise bound (the
+long-chain cases: a word-like batch with a 29 x 144 example, the line batch's
+32 x 1024 example), their largest error is 0.25 to 0.92 times the response
+(1.16 at most over 16 draws): K_COND = 2 admits them all with a margin of
+about 1.7 over the worst draw. It is derived from them, on the CPU, not from
+the kernels.
 """
+
+import os
+import warnings
 
 import numpy as np
 import pytest
 import torch
+
+import parity_log
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +50,7 @@ DEV = "cuda:0"
 F32_TOL = (1e-5, 1e-4)
 BF16_TOL = (1e-3, 2e-2)
 U32 = 2.0 ** -24  # fp32 unit roundoff: size of the input perturbation
-K_COND = 8.0      # allowed ratio of the largest error to the largest one-ulp perturbation response
+K_COND = 2.0      # allowed ratio of the largest error to the largest one-ulp perturbation response
 
 
 def _np(t):
@@ -87,12 +94,15 @@ def assert_close(name, got, ref, tol, sens=None):
     sv = np.asarray(sens() if callable(sens) else sens, np.float64).reshape(-1)
     assert sv.shape == ref.shape, (name, sv.shape, ref.shape)
     e_inf, s_inf = float(err.max()), float(np.abs(sv).max())
-    print(f"[conditioning] {name}: {int(bad.sum())} of {bad.size} elements outside the elementwise bound; "
-          f"largest error {e_inf:.3g}, largest one-ulp response {s_inf:.3g} (ratio {e_inf / max(s_inf, 1e-300):.3g})",
-          flush=True)
+    ratio = e_inf / max(s_inf, 1e-300)
+    msg = (f"{name}: {int(bad.sum())} of {bad.size} elements outside the elementwise bound; largest error "
+           f"{e_inf:.3g}, largest one-ulp response {s_inf:.3g} (ratio {ratio:.3g})")
     if e_inf > K_COND * s_inf + atol * scale:
         raise AssertionError(f"{name}: largest error {e_inf:.3g} above {K_COND} x the one-ulp response {s_inf:.3g}; "
                              f"{int(bad.sum())} of {bad.size} outside the elementwise bound; {where}")
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    parity_log.USES.append(f"{test} {msg}")
+    warnings.warn(parity_log.ConditioningWarning(msg))
 
 
 def poison(lay):

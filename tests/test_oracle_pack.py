@@ -1,4 +1,4 @@
-"""Pins of the oracle packer ("No Padding Please", §V, §V-A, Appendix B Algorithm 1) and of the
+"""Pins of the oracle packer ("No Padding Please", §V, §V-A, §IX-B (packing algorithm details, Algorithm 1)) and of the
 input-skewing trick (§IV-A, Figure 3).
 
 The packer is checked against (a) hand-worked runs of the loop, (b) an
