@@ -1,12 +1,16 @@
 """Throughput of the packed 4-direction MDLSTM layer, forward + backward, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload word] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload line] [--no-cpu-baseline]
 
 A step is one pass of the whole device path over one batch whose inputs are
 already in HBM: scatter the examples onto the packed canvas, forward wavefront
 (with the input projection), direction sum + un-packing, reverse wavefront,
 weight and input gradients. The metric counts real cell-direction updates only:
-4 * sum(h*w) / step time (forward + backward). Prints one JSON line.
+4 * sum(h*w) / step time (forward + backward). Prints one JSON line. The
+headline batch is the line-like one (32 images of 32 x 256..1024, H = 32), the
+largest of the workloads; the word-like batch (packed, as a minimal-padding
+stack, and on exact-height rows) and the three-level stack are reported beside
+it.
 
 Timing: after the warmup, a breakdown pass of K steps times every kernel
 group with HIP events that each dispatch records itself (the library's timing
@@ -15,11 +19,11 @@ that group's dispatches only, since each timed dispatch costs the stream a few
 microseconds.
 
 Also reported: the per-kernel-group times of the breakdown pass; the roofline
-of the dominant kernel (its launch time from the timed region);
-the host packer's time; the same images laid out as a minimal-padding stack
-(batch padding) and timed the same way; the other image batch of the pages'
-comparison (line-like next to word-like, and the reverse), packed, for context;
-and the CPU oracle on a bounded sample.
+of the dominant kernel (its launch time from the timed region) against the
+algorithmic flops and minimum bytes of each kernel; the host packer's time;
+the word-like images packed, as a minimal-padding stack and on exact-height
+rows; the stack; and the CPU oracle (float32, one process per host core) on
+the headline batch.
 """
 
 from __future__ import annotations
@@ -40,6 +44,7 @@ MI355X = {
     "fp32_vector_TFLOPs": 157.3,  # 256 CU x 2.4 GHz x 256 fp32 flop/clk/CU
     "fp32_mfma_TFLOPs": 157.3,
     "bf16_mfma_TFLOPs": 2500.0,
+    "f16_mfma_TFLOPs": 2500.0,
 }
 
 
@@ -48,14 +53,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="word", choices=["word", "line", "tiny"])
+    ap.add_argument("--workload", default="line", choices=["line", "word", "tiny"])
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-padded", action="store_true")
     ap.add_argument("--no-literal", action="store_true", help="skip the exact-height / skewed-canvas comparison")
-    ap.add_argument("--no-other", action="store_true", help="skip the line-like (or word-like) companion run")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the word-like companion runs (packed, as a padded stack, on exact-height rows)")
     ap.add_argument("--no-stack", action="store_true", help="skip the three-level stack companion run")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU time of the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the CPU oracle baseline")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB on the device (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -67,13 +73,14 @@ def link_count(rects):
 
 
 def kernel_model(info, rects, C, H, x_bytes, nchunks=None, fwd_zero=False):
-    """Algorithmic HBM bytes and flops of one launch of each kernel group (one layer, one step).
+    """Design bytes and algorithmic flops of one launch of each kernel group (one layer, one step).
 
-    T = computed cells per direction, N = real pixels; every tensor is counted
-    once at its storage size, so re-reads show up as traffic above these bytes.
-    The recurrent flops count 10 H^2 per predecessor link (a 5H x H matrix-vector
-    product), both in the forward and in the backward pass. fwd_zero: the forward
-    wavefront also zeroes h outside the computed regions (no zero-fill launch).
+    T = computed cells per direction, N = real pixels; every tensor of this
+    design (gate stash, gate gradients) is counted once at its storage size, so
+    re-reads show up as counter traffic above these bytes. The recurrent flops
+    count 10 H^2 per predecessor link (a 5H x H matrix-vector product), both in
+    the forward and in the backward pass. fwd_zero: the forward wavefront also
+    zeroes h outside the computed regions (no zero-fill launch).
     """
     T = info["computed_cells"]
     N = info["real_pixels"]
@@ -103,21 +110,44 @@ def kernel_model(info, rects, C, H, x_bytes, nchunks=None, fwd_zero=False):
     }
 
 
-def roofline(kernel, avg_ms, model):
-    """Fractions of HBM and fp32 matrix-core peaks; the bound is the larger fraction."""
+def min_bytes(N, C, H, x_bytes):
+    """The minimum HBM bytes of one forward + backward step over N real pixels (all four directions), split by
+    kernel group: x read by the forward and by the weight gradients, one (h, c) pair per cell-direction written
+    by the forward and read back by the reverse wavefront, dy read, y and dx written. Their sum is
+    N (2 C x_bytes + 4 C + 72 H); gate stashes, gate gradients and re-reads are the design's, not counted."""
+    f = 4
+    return {"fwd_wavefront": N * (C * x_bytes + 4 * 2 * H * f), "dirsum": N * H * f,
+            "bwd_wavefront": N * (H * f + 4 * 2 * H * f), "wgrad": N * (C * x_bytes + C * f),
+            "scatter": 0, "zero_fill": 0, "projection": 0}
+
+
+# f16 matrix-core products issued per fp32 product of the recurrence: h and da as f16 pairs, the forward's weights
+# as three pieces (hidden sizes up to 32), the backward's as a pair
+F16_PIECES = {"fwd_wavefront": lambda H: 4 if H <= 32 else 3, "bwd_wavefront": lambda H: 3}
+
+
+def roofline(kernel, avg_ms, model, bmin, H=None):
+    """Fractions of the fp32 peak (algorithmic flops) and of HBM (minimum bytes of the step that belong to this
+    kernel); the bound is the larger fraction. The design's own bytes and their HBM fraction are kept beside."""
     nbytes, flops = model[kernel]
-    gbs = nbytes / (avg_ms * 1e-3) / 1e9
-    tfs = flops / (avg_ms * 1e-3) / 1e12
-    fh = gbs / MI355X["hbm_GBps"]
+    mb = bmin.get(kernel, 0)
+    t = avg_ms * 1e-3
+    tfs = flops / t / 1e12
     fm = tfs / MI355X["fp32_mfma_TFLOPs"]
-    if fm > fh:
+    fh = mb / t / 1e9 / MI355X["hbm_GBps"]
+    if fm >= fh:
         r = {"bound": "mfma", "achieved": round(tfs, 4), "peak": MI355X["fp32_mfma_TFLOPs"], "unit": "TFLOP/s",
              "frac": round(fm, 6)}
     else:
-        r = {"bound": "hbm", "achieved": round(gbs, 2), "peak": MI355X["hbm_GBps"], "unit": "GB/s",
+        r = {"bound": "hbm", "achieved": round(mb / t / 1e9, 2), "peak": MI355X["hbm_GBps"], "unit": "GB/s",
              "frac": round(fh, 6)}
-    r.update({"kernel": kernel, "avg_launch_ms": round(avg_ms, 5), "algorithmic_bytes": int(nbytes),
-              "algorithmic_flops": int(flops), "hbm_frac": round(fh, 6), "mfma_frac": round(fm, 6)})
+    r.update({"kernel": kernel, "avg_launch_ms": round(avg_ms, 5), "algorithmic_flops": int(flops),
+              "fp32_frac": round(fm, 6), "min_bytes": int(mb), "min_bytes_hbm_frac": round(fh, 6),
+              "design_bytes": int(nbytes), "design_bytes_hbm_frac": round(nbytes / t / 1e9 / MI355X["hbm_GBps"], 6)})
+    if H is not None and kernel in F16_PIECES:
+        k = F16_PIECES[kernel](H)
+        r["f16_products_per_fp32_product"] = k
+        r["f16_issue_frac"] = round(flops * k / t / 1e12 / MI355X["f16_mfma_TFLOPs"], 6)
     return r
 
 
@@ -291,29 +321,96 @@ class StackRunner:
         return start.elapsed_time(stop) / steps, per_kernel
 
 
-def cpu_baseline(wl, min_seconds):
-    """The oracle (float64 NumPy, one BLAS thread) on the whole batch: pack + forward + backward, repeated
-    until at least min_seconds have passed; the rate is real cell-direction updates per second."""
-    from threadpoolctl import threadpool_limits
+_CPU_WL = {}
+
+
+def _cpu_init(name, seed):
+    """Worker start-up: one BLAS thread, the workload drawn once."""
+    from workloads import make_workload
+    _CPU_WL["wl"] = make_workload(name, seed)
+
+
+def _cpu_part(idx):
+    """The oracle, float32, on the examples `idx` of the worker's workload (packed on their own canvas: examples
+    are independent on the canvas, so this is the batch's work split by example): pack + forward + backward."""
+    import numpy as np
     from oracle import mdlstm as omd, pack as opack
     from workloads import cotangent
-    h, w = wl.heights, wl.widths
+    wl = _CPU_WL["wl"]
+    h, w = wl.heights[idx], wl.widths[idx]
+    xs = [wl.xs[i] for i in idx]
     dys = cotangent(wl.seed, h, w, wl.H)
-    passes = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            lay = opack.pack_alg1(h, w, wl.canvas_w_min[0], wl.sep)
-            ys, cache = omd.layer_forward(lay, wl.xs, wl.layers[0])
-            omd.layer_backward(lay, wl.layers[0], cache, dys=dys)
-            passes += 1
-            t = time.perf_counter() - t0
-            if t >= min_seconds:
-                break
-    N = int(np.sum(h.astype(np.int64) * w))
-    return {"value": 4 * N * passes / t, "unit": "cell-direction updates/s", "cores": 1, "kind": "oracle",
+    num = omd.Num(np.float32)
+    lay = opack.pack_alg1(h, w, wl.canvas_w_min[0], wl.sep)
+    ys, cache = omd.layer_forward(lay, xs, wl.layers[0], num=num)
+    omd.layer_backward(lay, wl.layers[0], cache, dys=dys, num=num)
+    return len(idx)
+
+
+def cpu_baseline(wl, min_seconds):
+    """The oracle (its per-diagonal form, float32 arrays) on the whole batch, split over one worker process per
+    host core: examples dealt by the greedy largest-cost-into-least-loaded rule (cost h w (h + w)), each worker
+    single-threaded. Passes of pack + forward + backward are repeated until min_seconds of wall time have
+    passed; the rate is real cell-direction updates per second."""
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        cores = min(cores, int(os.environ["OMP_NUM_THREADS"]))
+    cores = max(1, min(cores, wl.n))
+    cost = [int(h) * int(w) * (int(h) + int(w)) for h, w in zip(wl.heights, wl.widths)]
+    bins = [[] for _ in range(cores)]
+    load = [0] * cores
+    for e in sorted(range(wl.n), key=lambda e: -cost[e]):
+        k = int(np.argmin(load))
+        bins[k].append(e)
+        load[k] += cost[e]
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(cores, initializer=_cpu_init, initargs=(wl.name, wl.seed)) as pool:
+            pool.map(_cpu_part, [[bins[k][0]] for k in range(cores)])  # start-up and imports, untimed
+            passes = 0
+            t0 = time.perf_counter()
+            while True:
+                pool.map(_cpu_part, bins, chunksize=1)
+                passes += 1
+                t = time.perf_counter() - t0
+                if t >= min_seconds:
+                    break
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    N = int(np.sum(wl.heights.astype(np.int64) * wl.widths))
+    return {"value": 4 * N * passes / t, "unit": "cell-direction updates/s", "cores": cores, "kind": "oracle",
             "sample": f"all {wl.n} {wl.name} images (seed {wl.seed}, {N} pixels), {passes} passes of pack + "
-                      f"forward + backward in float64 NumPy on one thread, {t:.1f} s"}
+                      f"forward + backward of the oracle's per-diagonal form in float32, split by example over "
+                      f"{cores} single-threaded worker processes, {t:.1f} s"}
+
+
+def step_roofline(model, bmin, ms):
+    """Whole-step fractions: all algorithmic flops against the fp32 peak, all minimum bytes against HBM."""
+    flops = sum(f for _, f in model.values())
+    mb = sum(bmin.values())
+    t = ms * 1e-3
+    return {"algorithmic_flops": int(flops), "fp32_frac": round(flops / t / 1e12 / MI355X["fp32_mfma_TFLOPs"], 6),
+            "min_bytes": int(mb), "min_bytes_hbm_frac": round(mb / t / 1e9 / MI355X["hbm_GBps"], 6)}
+
+
+def layer_report(runner, wl, ms, kern):
+    """Per-kernel rooflines of one layer's step, and the model the fractions come from."""
+    import directional_mdlstm_handwriting_amd as M
+    info = runner.dl.info
+    rects, _ = M.mdl_layout_rects(runner.dl.layout)
+    xb = 2 if wl.x_dtype == "bf16" else 4
+    model = kernel_model(info, rects, wl.C, wl.H, xb, fwd_zero="zero_fill" not in kern)
+    bmin = min_bytes(info["real_pixels"], wl.C, wl.H, xb)
+    per = {k: roofline(k, v, model, bmin, wl.H) for k, v in kern.items() if k in model}
+    return model, bmin, per
 
 
 def main():
@@ -322,24 +419,30 @@ def main():
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the examples of a batch would be split across GPUs, one process each)", file=sys.stderr)
         sys.exit(2)
-    import torch
     from workloads import make_workload
-
-    device = "cuda:0"
-    torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
     wl = make_workload(args.workload, args.seed)
     N = int(np.sum(wl.heights.astype(np.int64) * wl.widths))
 
+    # the CPU oracle first, before this process touches the GPU (its workers are fresh processes)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    import torch
+    import directional_mdlstm_handwriting_amd as M
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    print(f"bench: {wl.name} packed", file=sys.stderr, flush=True)
     torch.cuda.reset_peak_memory_stats()
     packed = Runner(wl, "packed", device, stream)
     ms, dom, dom_ms, kern = packed.time(args.steps, args.warmup)
-    peak_packed = torch.cuda.max_memory_allocated()
     info = packed.dl.info
     value = 4 * N / (ms * 1e-3)
 
     # host packer alone (median of repeats)
-    import directional_mdlstm_handwriting_amd as M
     reps = []
     for _ in range(20):
         t0 = time.perf_counter()
@@ -348,13 +451,13 @@ def main():
     pack_us = float(np.median(reps) * 1e6)
 
     # roofline of the dominant kernel group, from HIP events its dispatches recorded in the timed region
-    rects, _ = M.mdl_layout_rects(packed.dl.layout)
-    H, C = wl.H, wl.C
-    model = kernel_model(info, rects, C, H, 2 if wl.x_dtype == "bf16" else 4, fwd_zero="zero_fill" not in kern)
-    roof = roofline(dom, dom_ms, model)
+    model, bmin, per_kernel = layer_report(packed, wl, ms, kern)
+    roof = roofline(dom, dom_ms, model, bmin, wl.H)
     roof["traffic"] = measured_traffic(dom, wl.name)
-    per_kernel = {k: roofline(k, v, model) for k, v in kern.items() if k in model}
-
+    roof["dependent_steps"] = info["max_depth"]
+    roof["us_per_dependent_step"] = round(dom_ms * 1e3 / info["max_depth"], 4)
+    H, C = wl.H, wl.C
+    bf16 = wl.x_dtype == "bf16"
     out = {
         "metric": "MDLSTM cell-direction updates/sec (fwd+bwd) on packed canvas; % of roofline",
         "value": value,
@@ -366,87 +469,108 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16-in/f32" if wl.x_dtype == "bf16" else "f32",
+        "dtype": ("bf16 input, " if bf16 else "") + "f32 (recurrent products on f16 matrix cores, operands "
+                 "split into f16 pieces, fp32 accumulation)",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.n} images, C={C}, H={H}, seed {wl.seed}, canvas "
                                f"{info['canvas_h']}x{info['canvas_w']}",
                    "real_pixels": N, "computed_cells": info["computed_cells"],
                    "max_depth": info["max_depth"], "parallelism": "single GPU"},
         "roofline": roof,
+        "step_roofline": step_roofline(model, bmin, ms),
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
         "kernels_ms_source": "breakdown pass before the timed region, events on every dispatch",
-        "kernels_roofline": {k: {"bound": r["bound"], "frac": r["frac"], "hbm_frac": r["hbm_frac"],
-                                 "mfma_frac": r["mfma_frac"]} for k, r in per_kernel.items()},
+        "kernels_roofline": {k: {kk: r[kk] for kk in ("bound", "frac", "fp32_frac", "min_bytes_hbm_frac",
+                                                       "design_bytes_hbm_frac")}
+                             for k, r in per_kernel.items()},
         "pack_host_us": round(pack_us, 2),
     }
     out["config"]["canvas_waste"] = round(1.0 - N / (info["canvas_h"] * info["canvas_w"]), 4)
+    del packed
+    torch.cuda.empty_cache()
 
-    if not args.no_padded and wl.name != "tiny":
-        del packed
-        torch.cuda.empty_cache()
+    # the word-like batch: packed, as a minimal-padding stack, and on exact-height rows (the pages' own layout)
+    ww = wl if wl.name == "word" else make_workload("word", args.seed)
+    Nw = int(np.sum(ww.heights.astype(np.int64) * ww.widths))
+    if wl.name == "tiny":
+        ww = None
+    if ww is not None and ww is wl:
+        # the headline is the word batch itself
+        wms, wk, wi = ms, kern, info
+        peak_packed = torch.cuda.max_memory_allocated()
+    elif ww is not None and not args.no_other:
+        print("bench: word packed", file=sys.stderr, flush=True)
         torch.cuda.reset_peak_memory_stats()
-        padded = Runner(wl, "padded", device, stream)
-        pms, _, _, pk = padded.time(max(5, args.steps // 2), 2)
-        peak_padded = torch.cuda.max_memory_allocated()
-        pinfo = padded.dl.info
-        out["packed_vs_padded"] = {
-            "ms_per_step_packed": ms, "ms_per_step_padded": pms, "speedup": pms / ms,
-            "padded_cell_fraction": round(1.0 - N / pinfo["computed_cells"], 4),
-            # padded zeros relative to the real pixels (the ZPR measure of the speech-batching page)
-            "zpr": round((pinfo["computed_cells"] - N) / N, 4),
-            "computed_cells_padded": pinfo["computed_cells"],
-            "computed_cell_direction_updates_per_s_padded": 4 * pinfo["computed_cells"] / (pms * 1e-3),
-            "peak_device_bytes_packed": int(peak_packed), "peak_device_bytes_padded": int(peak_padded),
-            "padded_kernels_ms": {k: round(v, 5) for k, v in pk.items()},
-            "pages_context": "6.6x for IAM words: whole-model training epochs, 2x GTX 1080, batch 20 padded vs "
-                             "200 packed (No Padding Please, Table IV)",
+        rw = Runner(ww, "packed", device, stream)
+        wms, _, _, wk = rw.time(args.steps, 2)
+        peak_packed = torch.cuda.max_memory_allocated()
+        wi = rw.dl.info
+        wmodel, wbmin, wper = layer_report(rw, ww, wms, wk)
+        out["word_workload"] = {
+            "workload": f"word: {ww.n} images, C={ww.C}, H={ww.H}, seed {ww.seed}, canvas "
+                        f"{wi['canvas_h']}x{wi['canvas_w']}",
+            "value": 4 * Nw / (wms * 1e-3), "unit": "cell-direction updates/s", "ms_per_step": wms,
+            "max_depth": wi["max_depth"], "kernels_ms": {k: round(v, 5) for k, v in wk.items()},
+            "kernels_roofline": {k: {kk: r[kk] for kk in ("bound", "frac", "fp32_frac", "min_bytes_hbm_frac")}
+                                 for k, r in wper.items()},
+            "step_roofline": step_roofline(wmodel, wbmin, wms),
         }
-        del padded
-
-    # the pages' own layout for the same images: exact-height rows, whole canvas skewed for column-parallel
-    # steps; its canvas, skew padding and dependent-step count next to this schedule's, and this schedule
-    # timed on the exact-height canvas
-    if not args.no_literal and wl.name != "tiny":
-        def skewed(li):
-            Hc, Wc = li["canvas_h"], li["canvas_w"]
-            cells = Hc * (Wc + Hc - 1)
-            return {"canvas": f"{Hc}x{Wc}", "canvas_waste": round(1.0 - N / (Hc * Wc), 4),
-                    "skewed_cells": cells, "skewed_padding_fraction": round(1.0 - N / cells, 4),
-                    "global_depth": Hc + Wc - 1, "cells_per_column": Hc}
+        del rw
         torch.cuda.empty_cache()
-        ex = Runner(wl, "exact", device, stream)
-        ems, _, _, ek = ex.time(max(5, args.steps // 2), 2)
-        ei = ex.dl.info
-        out["paper_literal_layout"] = {
-            "alg1_rows": skewed(info), "exact_height_rows": skewed(ei),
-            "local_depth": info["max_depth"], "widest_local_diagonal": info["max_diag"],
-            "ms_per_step_alg1": ms, "ms_per_step_exact_height": ems,
-            "exact_height_kernels_ms": {k: round(v, 5) for k, v in ek.items()},
-        }
-        del ex
+    else:
+        ww = None
+    if ww is not None:
+        if not args.no_padded:
+            print("bench: word padded", file=sys.stderr, flush=True)
+            torch.cuda.reset_peak_memory_stats()
+            padded = Runner(ww, "padded", device, stream)
+            pms, _, _, pk = padded.time(max(5, args.steps // 2), 2)
+            peak_padded = torch.cuda.max_memory_allocated()
+            pinfo = padded.dl.info
+            out["packed_vs_padded"] = {
+                "workload": "the word-like batch above",
+                "ms_per_step_packed": wms, "ms_per_step_padded": pms, "speedup": pms / wms,
+                "padded_cell_fraction": round(1.0 - Nw / pinfo["computed_cells"], 4),
+                # padded zeros relative to the real pixels (the ZPR measure of the speech-batching page)
+                "zpr": round((pinfo["computed_cells"] - Nw) / Nw, 4),
+                "computed_cells_padded": pinfo["computed_cells"],
+                "computed_cell_direction_updates_per_s_padded": 4 * pinfo["computed_cells"] / (pms * 1e-3),
+                "peak_device_bytes_packed": int(peak_packed), "peak_device_bytes_padded": int(peak_padded),
+                "padded_kernels_ms": {k: round(v, 5) for k, v in pk.items()},
+                "pages_context": "6.6x for IAM words: whole-model training epochs, 2x GTX 1080, batch 20 padded vs "
+                                 "200 packed (No Padding Please, Table IV)",
+            }
+            del padded
+            torch.cuda.empty_cache()
 
-    # the other image batch of the pages' comparison, timed the same way (packed), for context
-    other = {"word": "line", "line": "word"}.get(wl.name)
-    if other and not args.no_other:
-        wo = make_workload(other, args.seed)
-        No = int(np.sum(wo.heights.astype(np.int64) * wo.widths))
-        ro = Runner(wo, "packed", device, stream)
-        oms, _, _, ok = ro.time(max(5, args.steps // 2), 2)
-        oi = ro.dl.info
-        orects, _ = M.mdl_layout_rects(ro.dl.layout)
-        omodel = kernel_model(oi, orects, wo.C, wo.H, 2 if wo.x_dtype == "bf16" else 4, fwd_zero="zero_fill" not in ok)
-        out["other_workload"] = {
-            "workload": f"{wo.name}: {wo.n} images, C={wo.C}, H={wo.H}, seed {wo.seed}, canvas "
-                        f"{oi['canvas_h']}x{oi['canvas_w']}, x {wo.x_dtype}",
-            "value": 4 * No / (oms * 1e-3), "unit": "cell-direction updates/s", "ms_per_step": oms,
-            "max_depth": oi["max_depth"], "kernels_ms": {k: round(v, 5) for k, v in ok.items()},
-            "kernels_roofline": {k: {"bound": r["bound"], "frac": r["frac"]}
-                                 for k, r in ((k, roofline(k, v, omodel)) for k, v in ok.items() if k in omodel)},
-        }
-        del ro
+        # the pages' own layout for the same images: exact-height rows, whole canvas skewed for column-parallel
+        # steps; its canvas, skew padding and dependent-step count next to this schedule's, and this schedule
+        # timed on the exact-height canvas
+        if not args.no_literal:
+            print("bench: word on exact-height rows", file=sys.stderr, flush=True)
 
-    # the three-level stack of the pages' model (128 word-like images), timed the same way, for context
-    if wl.name == "word" and not args.no_stack:
+            def skewed(li):
+                Hc, Wc = li["canvas_h"], li["canvas_w"]
+                cells = Hc * (Wc + Hc - 1)
+                return {"canvas": f"{Hc}x{Wc}", "canvas_waste": round(1.0 - Nw / (Hc * Wc), 4),
+                        "skewed_cells": cells, "skewed_padding_fraction": round(1.0 - Nw / cells, 4),
+                        "global_depth": Hc + Wc - 1, "cells_per_column": Hc}
+            ex = Runner(ww, "exact", device, stream)
+            ems, _, _, ek = ex.time(max(5, args.steps // 2), 2)
+            ei = ex.dl.info
+            out["paper_literal_layout"] = {
+                "workload": "the word-like batch above",
+                "alg1_rows": skewed(wi), "exact_height_rows": skewed(ei),
+                "local_depth": wi["max_depth"], "widest_local_diagonal": wi["max_diag"],
+                "ms_per_step_alg1": wms, "ms_per_step_exact_height": ems,
+                "exact_height_kernels_ms": {k: round(v, 5) for k, v in ek.items()},
+            }
+            del ex
+            torch.cuda.empty_cache()
+
+    # the three-level stack of the pages' model (128 word-like images) and its head, timed the same way
+    if not args.no_stack and wl.name != "tiny":
+        print("bench: stack", file=sys.stderr, flush=True)
         ws_ = make_workload("stack", args.seed)
         sr = StackRunner(ws_, device, stream)
         sms, sk = sr.time(max(5, args.steps // 2), 2)
@@ -468,10 +592,7 @@ def main():
         }
         del sr
 
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
+    out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
     if args.copy_calib:
         copy_calibration(args.copy_calib)

@@ -49,6 +49,7 @@ _I32 = ctypes.c_int32
 _SZ = ctypes.c_size_t
 _SIGS = [
     ("mdl_pack", _I32, [_P, _P, _I32, _I32, _I32, _I32, ctypes.POINTER(_P)]),
+    ("mdl_pack_level", _I32, [_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_P)]),
     ("mdl_layout_free", None, [_P]),
     ("mdl_layout_info", _I32, [_P, _P]),
     ("mdl_layout_rects", _I32, [_P, _P, _P]),
@@ -159,6 +160,13 @@ def mdl_pack(heights, widths, canvas_w_min: int, sep: int = 1, mode: int = MDL_P
     w = np.ascontiguousarray(widths, dtype=np.int32)
     out = ctypes.c_void_p()
     _check(_lib.mdl_pack(h.ctypes.data, w.ctypes.data, len(h), canvas_w_min, sep, mode, ctypes.byref(out)))
+    return Layout(out.value)
+
+
+def mdl_pack_level(lk: Layout, kh: int, kw: int, canvas_w_min: int, sep: int = 1,
+                   mode: int = MDL_PACK_ALG1) -> Layout:
+    out = ctypes.c_void_p()
+    _check(_lib.mdl_pack_level(lk.handle, kh, kw, canvas_w_min, sep, mode, ctypes.byref(out)))
     return Layout(out.value)
 
 

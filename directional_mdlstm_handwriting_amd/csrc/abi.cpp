@@ -170,6 +170,25 @@ int mdl_pack(const int32_t* heights, const int32_t* widths, int32_t n, int32_t c
     GUARD_END
 }
 
+int mdl_pack_level(const mdl_layout* lk, int32_t kh, int32_t kw, int32_t canvas_w_min, int32_t sep, int32_t mode,
+                   mdl_layout** out) {
+    GUARD_BEGIN
+    if (!out) return fail(MDL_EINVAL, "mdl_pack_level: null output pointer");
+    *out = nullptr;
+    if (!lk) return fail(MDL_EINVAL, "mdl_pack_level: null layout");
+    if (kh < 1 || kw < 1) return fail(MDL_EINVAL, "mdl_pack_level: block sizes must be positive");
+    const mdl::Layout& A = L_of(lk);
+    // the block-strided convolution covers each example with ceil(h / kh) x ceil(w / kw) blocks, the last
+    // row and column of blocks padded with zeros
+    std::vector<int32_t> hs(A.n), ws(A.n);
+    for (int e = 0; e < A.n; ++e) {
+        hs[e] = (A.real[4 * e + 2] + kh - 1) / kh;
+        ws[e] = (A.real[4 * e + 3] + kw - 1) / kw;
+    }
+    return mdl_pack(hs.data(), ws.data(), A.n, canvas_w_min, sep, mode, out);
+    GUARD_END
+}
+
 void mdl_layout_free(mdl_layout* layout) { delete layout; }
 
 int mdl_layout_info(const mdl_layout* layout, int64_t* info) {

@@ -20,7 +20,7 @@ import torch
 
 from . import (MDL_BF16, MDL_F32, MDL_PACK_ALG1, MDL_PACK_EXACT, MDL_PACK_PADDED, Layout, mdl_backward,
                mdl_blockconv_backward, mdl_blockconv_forward, mdl_blockconv_workspace_size, mdl_dirsum_unpack, mdl_forward,
-               mdl_layout_device_size, mdl_layout_upload, mdl_pack, mdl_scatter, mdl_workspace_size,
+               mdl_layout_device_size, mdl_layout_rects, mdl_layout_upload, mdl_pack, mdl_pack_level, mdl_scatter, mdl_workspace_size,
                mdl_ctc_head, mdl_ctc_workspace_size)
 
 
@@ -50,16 +50,20 @@ class DeviceParams:
         return int(self.Ul.shape[1])
 
 
+PACK_MODES = {"packed": MDL_PACK_ALG1, "padded": MDL_PACK_PADDED, "exact": MDL_PACK_EXACT}
+
+
 class DeviceLayout:
     """A packed layout plus its uploaded device descriptor."""
 
     def __init__(self, heights, widths, canvas_w_min: int, sep: int = 1, mode: str = "packed",
-                 device: str = "cuda", stream=None):
-        modes = {"packed": MDL_PACK_ALG1, "padded": MDL_PACK_PADDED, "exact": MDL_PACK_EXACT}
-        if mode not in modes:
-            raise ValueError(f"unknown packing mode {mode!r}; one of {sorted(modes)}")
-        m = modes[mode]
-        self.layout: Layout = mdl_pack(heights, widths, canvas_w_min, sep, m)
+                 device: str = "cuda", stream=None, layout: Optional[Layout] = None):
+        """Packs (heights, widths), or takes an already built `layout` (heights and widths then unused)."""
+        if layout is None:
+            if mode not in PACK_MODES:
+                raise ValueError(f"unknown packing mode {mode!r}; one of {sorted(PACK_MODES)}")
+            layout = mdl_pack(heights, widths, canvas_w_min, sep, PACK_MODES[mode])
+        self.layout: Layout = layout
         self.device = device
         nbytes, self.eid_off, self.border_off = mdl_layout_device_size(self.layout)
         self.desc = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -69,6 +73,11 @@ class DeviceLayout:
     @property
     def info(self):
         return self.layout.info
+
+    def sizes(self):
+        """(heights, widths) of the examples, input order."""
+        _, real = mdl_layout_rects(self.layout)
+        return real[:, 2].copy(), real[:, 3].copy()
 
     def device_maps(self):
         Hc, Wc = self.layout.Hc, self.layout.Wc
@@ -137,15 +146,14 @@ class PackedStack:
                  sep: int = 1, kh: int = 2, kw: int = 4, device: str = "cuda"):
         self.kh, self.kw = kh, kw
         self.levels: List[PackedLayer] = []
-        hs = [int(v) for v in heights]
-        ws = [int(v) for v in widths]
         c_in = C
+        dl = DeviceLayout(heights, widths, canvas_w_min[0], sep, "packed", device)
         for lvl, H in enumerate(Hs):
-            dl = DeviceLayout(hs, ws, canvas_w_min[lvl], sep, "packed", device)
             self.levels.append(PackedLayer(dl, c_in, H))
             if lvl + 1 < len(Hs):
-                hs = [-(-h // kh) for h in hs]
-                ws = [-(-w // kw) for w in ws]
+                # the next level's examples: the block conv's output sizes, packed again (the library's rule)
+                nxt = mdl_pack_level(dl.layout, kh, kw, canvas_w_min[lvl + 1], sep, MDL_PACK_ALG1)
+                dl = DeviceLayout(None, None, 0, device=device, layout=nxt)
                 c_in = couts[lvl]
         self.couts = list(couts)
         self.conv_ws = []
@@ -157,6 +165,11 @@ class PackedStack:
             self.conv_ws.append((torch.empty(max(nb, 4), dtype=torch.uint8, device=device), nb))
             self.dx_canvas.append(torch.empty_like(lk1.x_canvas, dtype=torch.float32))
             self.dh_dirs.append(torch.empty_like(lk.h_dirs))
+
+    @property
+    def level_sizes(self):
+        """Per level, the (heights, widths) of its examples."""
+        return [lay.dl.sizes() for lay in self.levels]
 
     def forward(self, x_flat, params: Sequence[DeviceParams], convs, stream=None):
         L0 = self.levels[0]

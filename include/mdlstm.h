@@ -104,7 +104,21 @@ typedef struct mdl_layout mdl_layout; /* host object, immutable once built */
 int mdl_pack(const int32_t* heights, const int32_t* widths, int32_t n, int32_t canvas_w_min,
              int32_t sep, int32_t mode, mdl_layout** out);
 
-/* Frees a layout from mdl_pack (NULL is ignored). */
+/*
+ * mdl_pack_level — the layout of the next MDLSTM level of a stack ("No Padding
+ * Please" §V-B: a block-strided convolution of kh x kw blocks between two
+ * MDLSTM levels lowers each example's resolution, and the examples are packed
+ * again just before the next MDLSTM layer). Example e of the new layout has
+ * ceil(h_e / kh) x ceil(w_e / kw) cells, (h_e, w_e) its size in `lk` (the last
+ * row and column of blocks are zero-padded), examples in the same order; the
+ * sizes are then packed as by mdl_pack(..., canvas_w_min, sep, mode, out).
+ * Host-only; `lk` is only read. Errors: those of mdl_pack, and MDL_EINVAL for
+ * a null `lk` or `out` or kh, kw < 1.
+ */
+int mdl_pack_level(const mdl_layout* lk, int32_t kh, int32_t kw, int32_t canvas_w_min, int32_t sep,
+                   int32_t mode, mdl_layout** out);
+
+/* Frees a layout from mdl_pack or mdl_pack_level (NULL is ignored). */
 void mdl_layout_free(mdl_layout* layout);
 
 /* Fills info[MDL_INFO_COUNT] (host) with the layout's sizes. */
@@ -157,9 +171,13 @@ int mdl_layout_upload(const mdl_layout* layout, void* d_desc, size_t bytes, void
 int mdl_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes);
 
 /*
- * Scatter: x_flat (device, flat [h][w][C] per example, dtype MDL_F32 or
- * MDL_BF16) -> x_canvas (device, [Hc][Wc][C], same dtype), zero outside the real
- * pixels (separators, unused canvas, padding). Bit-exact copy.
+ * Scatter ("No Padding Please" §V-A, step 3: the examples are tiled onto the
+ * packed canvas at the positions the packer chose, separator and unused pixels
+ * zero): x_flat (device, flat [h][w][C] per example, input order, dtype MDL_F32
+ * or MDL_BF16) -> x_canvas (device, [Hc][Wc][C], same dtype), zero outside the
+ * real pixels (separators, unused canvas, padding). Bit-exact copy.
+ * Errors: MDL_EINVAL for null pointers, C < 1 or an unknown dtype; MDL_EHIP
+ * for a launch failure. Asynchronous on `stream`.
  */
 int mdl_scatter(const mdl_layout* layout, const void* d_desc, const void* x_flat, int32_t C,
                 int32_t dtype, void* x_canvas, void* stream);

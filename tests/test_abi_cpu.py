@@ -209,3 +209,23 @@ def test_ctc_head_error_codes():
                             None) == M.MDL_EINVAL
     assert lib.mdl_ctc_head(lay.handle, 1, 1, 4, 1, 1, 10, 1, 1, 4, 3, 1, None, None, None, 1, ws - 4,
                             None) == M.MDL_ESIZE
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_pack_level_matches_oracle_stack_sizes(seed):
+    """mdl_pack_level packs the next level of a stack: its example sizes are those of the oracle's chunked
+    block convolution (its output shapes), and its layout is the oracle packer's on those sizes."""
+    from oracle import blockconv as obc
+    h, w = make_sizes_only("word", seed, 40)
+    l1 = M.mdl_pack(h, w, 1024, 1)
+    hd = [np.zeros((4, int(a), int(b), 1)) for a, b in zip(h, w)]
+    outs = obc.conv_chunked(hd, np.zeros((1, 4, 1, 2, 4)), np.zeros(1), 2, 4)
+    h2 = [o.shape[0] for o in outs]
+    w2 = [o.shape[1] for o in outs]
+    l2 = M.mdl_pack_level(l1, 2, 4, 256, 1)
+    ref = opack.pack(h2, w2, 256, 1, "packed")
+    rects, real = M.mdl_layout_rects(l2)
+    assert (l2.Hc, l2.Wc) == (ref.Hc, ref.Wc)
+    assert np.array_equal(rects, ref.rects) and np.array_equal(real, ref.real)
+    with pytest.raises(M.MdlError):
+        M.mdl_pack_level(l1, 0, 4, 256, 1)
