@@ -67,6 +67,7 @@ _SIGS = [
     ("mdl_blockconv_workspace_size", _I32, [_P, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     ("mdl_blockconv_backward", _I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ,
                                       _P]),
+    ("mdl_blockconv_backward_noalloc", _I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P]),
     ("mdl_ctc_workspace_size", _I32, [_P, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     ("mdl_ctc_head", _I32, [_P, _P, _P, _I32, _P, _P, _I32, _P, _P, ctypes.c_int64, _I32, _P, _P, _P, _P, _P,
                             _SZ, _P]),
@@ -269,6 +270,13 @@ def mdl_blockconv_backward(lk: Layout, d_desc_k, lk1: Layout, d_desc_k1, h_dirs_
     _check(_lib.mdl_blockconv_backward(lk.handle, _ptr(d_desc_k), lk1.handle, _ptr(d_desc_k1), _ptr(h_dirs_k), H, kh,
                                        kw, _ptr(Wc), Cout, _ptr(dx_canvas_k1), _ptr(dh_dirs_k), _ptr(dWc), _ptr(dbc),
                                        _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mdl_blockconv_backward_noalloc(lk: Layout, d_desc_k, lk1: Layout, d_desc_k1, h_dirs_k, H: int, kh: int, kw: int,
+                                   Wc, Cout: int, dx_canvas_k1, dh_dirs_k, dWc, dbc, stream=None):
+    _check(_lib.mdl_blockconv_backward_noalloc(lk.handle, _ptr(d_desc_k), lk1.handle, _ptr(d_desc_k1), _ptr(h_dirs_k),
+                                               H, kh, kw, _ptr(Wc), Cout, _ptr(dx_canvas_k1), _ptr(dh_dirs_k),
+                                               _ptr(dWc), _ptr(dbc), _stream(stream)))
 
 
 def mdl_timing(enable: bool):

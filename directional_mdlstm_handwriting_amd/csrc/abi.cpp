@@ -475,24 +475,28 @@ int mdl_blockconv_workspace_size(const mdl_layout* lk1, int32_t H, int32_t kh, i
     return MDL_OK;
 }
 
-int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1, const void* d_desc_k1,
-                           const float* h_dirs_k, int32_t H, int32_t kh, int32_t kw, const float* Wc, int32_t Cout,
-                           const float* dx_canvas_k1, float* dh_dirs_k, float* dWc, float* dbc, void* ws,
-                           size_t ws_bytes, void* stream) {
-    GUARD_BEGIN
-    int rc = check_conv("mdl_blockconv_backward", lk, d_desc_k, lk1, d_desc_k1, H, kh, kw, Cout);
+static int conv_bwd(const char* fn, const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1,
+                    const void* d_desc_k1, const float* h_dirs_k, int32_t H, int32_t kh, int32_t kw, const float* Wc,
+                    int32_t Cout, const float* dx_canvas_k1, float* dh_dirs_k, float* dWc, float* dbc, void* ws,
+                    size_t ws_bytes, bool fixed_scratch, void* stream) {
+    int rc = check_conv(fn, lk, d_desc_k, lk1, d_desc_k1, H, kh, kw, Cout);
     if (rc) return rc;
     if (!h_dirs_k || !Wc || !dx_canvas_k1 || !dh_dirs_k || !dWc || !dbc || !ws)
-        return fail(MDL_EINVAL, "mdl_blockconv_backward: null tensor");
+        return fail(MDL_EINVAL, std::string(fn) + ": null tensor");
+    const int64_t K = 4 * (int64_t)H * kh * kw;
+    if (Cout * (K + 1) > 16 * 512) return fail(MDL_EUNSUPPORTED, std::string(fn) + ": Cout*(4*H*kh*kw+1) above 8192");
     size_t need = 0;
     mdl_blockconv_workspace_size(lk1, H, kh, kw, Cout, &need);
-    if (ws_bytes < need) return fail(MDL_ESIZE, "mdl_blockconv_backward: workspace too small");
-    const int64_t K = 4 * (int64_t)H * kh * kw;
-    if (Cout * (K + 1) > 16 * 512) return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: Cout*(4*H*kh*kw+1) above 8192");
+    if (ws_bytes < need) {
+        if (fixed_scratch)
+            return fail(MDL_ESIZE, std::string(fn) + ": the weight-gradient partials need " + std::to_string(need) +
+                                       " bytes, above the library's fixed scratch of " + std::to_string(ws_bytes));
+        return fail(MDL_ESIZE, std::string(fn) + ": workspace too small");
+    }
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
     if (mdl::conv_wgrad_lds(H, kh, kw, Cout) > lmax || mdl::conv_data_lds(H, kh, kw, Cout) > lmax)
-        return fail(MDL_EUNSUPPORTED, "mdl_blockconv_backward: weight-gradient tile or weights exceed LDS");
+        return fail(MDL_EUNSUPPORTED, std::string(fn) + ": weight-gradient tile or weights exceed LDS");
     hipError_t e;
     {
         Timed t("conv_bwd");
@@ -500,8 +504,34 @@ int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl
                                  dx_canvas_k1, dh_dirs_k, dWc, dbc, static_cast<float*>(ws),
                                  static_cast<hipStream_t>(stream));
     }
-    if (e != hipSuccess) return hip_fail(e, "mdl_blockconv_backward");
+    if (e != hipSuccess) return hip_fail(e, fn);
     return MDL_OK;
+}
+
+int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1, const void* d_desc_k1,
+                           const float* h_dirs_k, int32_t H, int32_t kh, int32_t kw, const float* Wc, int32_t Cout,
+                           const float* dx_canvas_k1, float* dh_dirs_k, float* dWc, float* dbc, void* ws,
+                           size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    return conv_bwd("mdl_blockconv_backward", lk, d_desc_k, lk1, d_desc_k1, h_dirs_k, H, kh, kw, Wc, Cout,
+                    dx_canvas_k1, dh_dirs_k, dWc, dbc, ws, ws_bytes, false, stream);
+    GUARD_END
+}
+
+int mdl_blockconv_backward_noalloc(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1,
+                                   const void* d_desc_k1, const float* h_dirs_k, int32_t H, int32_t kh, int32_t kw,
+                                   const float* Wc, int32_t Cout, const float* dx_canvas_k1, float* dh_dirs_k,
+                                   float* dWc, float* dbc, void* stream) {
+    GUARD_BEGIN
+    const char* fn = "mdl_blockconv_backward_noalloc";
+    int rc = check_conv(fn, lk, d_desc_k, lk1, d_desc_k1, H, kh, kw, Cout);
+    if (rc) return rc;
+    void* ws = nullptr;
+    size_t cap = 0;
+    const hipError_t e = mdl::conv_scratch(&ws, &cap);
+    if (e != hipSuccess) return hip_fail(e, "mdl_blockconv_backward_noalloc: scratch address");
+    return conv_bwd(fn, lk, d_desc_k, lk1, d_desc_k1, h_dirs_k, H, kh, kw, Wc, Cout, dx_canvas_k1, dh_dirs_k, dWc,
+                    dbc, ws, cap, true, stream);
     GUARD_END
 }
 

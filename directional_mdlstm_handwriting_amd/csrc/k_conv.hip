@@ -18,6 +18,8 @@
 // (Wc staged in LDS).
 #include "kernels.h"
 
+#include <mutex>
+
 namespace mdl {
 
 namespace {
@@ -229,6 +231,33 @@ inline unsigned grid_for(int64_t n) {
 }
 
 }  // namespace
+
+// The weight-gradient partials of the entry point that allocates nothing: one fixed array per device, as large
+// as the partials of any accepted call (at most CW_GROUPS chunks of Cout (K + 1) <= CW_MAXE CW_THREADS floats),
+// resident for the life of the process. Its device address is looked up once per device, with that device
+// current; host code passes that address, never the symbol itself.
+constexpr size_t kConvScratchFloats = (size_t)CW_GROUPS * CW_MAXE * CW_THREADS;  // 16 MiB
+static __device__ __align__(256) float scratch[kConvScratchFloats];
+
+hipError_t conv_scratch(void** ptr, size_t* bytes) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    *bytes = kConvScratchFloats * sizeof(float);
+    return hipSuccess;
+}
 
 int64_t conv_nchunks(const Dev& Dk1) {
     const int64_t P1 = (int64_t)Dk1.Hc * Dk1.Wc;

@@ -174,6 +174,9 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
 hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st);
 int64_t conv_nchunks(const Dev& Dk1);
+// this device's fixed weight-gradient scratch of the block conv (address and size), for callers that cannot
+// allocate; every call on one device shares it
+hipError_t conv_scratch(void** ptr, size_t* bytes);
 size_t conv_fwd_lds(int H, int kh, int kw, int Cout);
 size_t conv_wgrad_lds(int H, int kh, int kw, int Cout);
 size_t conv_data_lds(int H, int kh, int kw, int Cout);

@@ -270,6 +270,28 @@ int mdl_blockconv_backward(const mdl_layout* lk, const void* d_desc_k, const mdl
                            void* stream);
 
 /*
+ * mdl_blockconv_backward without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * allocation): the same computation and results as mdl_blockconv_backward,
+ * with the weight-gradient partial sums in a fixed scratch array inside the
+ * library, one per device, 16 MiB (the partials of any call that
+ * mdl_blockconv_backward accepts: at most 512 chunks of Cout*(4*H*kh*kw+1) <=
+ * 8192 floats). The array is held for the life of the process; its device
+ * address is looked up on the first call on each device. Nothing is allocated
+ * (no hipMalloc, no allocating library call). Every call on one device shares
+ * that array: calls that overlap on one device (two streams, two threads)
+ * race and must be serialized by the caller. Every partial is overwritten by
+ * each call, so no clearing is needed between calls.
+ * Errors: those of mdl_blockconv_backward; MDL_ESIZE if the partials would
+ * exceed the scratch (no accepted call does); MDL_EHIP if the scratch's
+ * address cannot be obtained.
+ */
+int mdl_blockconv_backward_noalloc(const mdl_layout* lk, const void* d_desc_k, const mdl_layout* lk1,
+                                   const void* d_desc_k1, const float* h_dirs_k, int32_t H, int32_t kh,
+                                   int32_t kw, const float* Wc, int32_t Cout, const float* dx_canvas_k1,
+                                   float* dh_dirs_k, float* dWc, float* dbc, void* stream);
+
+/*
  * Model head after the last MDLSTM level ("No Padding Please" §II / Figure 1:
  * one fully-connected layer shared across the four directions, trained with
  * CTC, the pages' reference [13]). For each example e of the layout, with
