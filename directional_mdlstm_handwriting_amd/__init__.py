@@ -55,6 +55,7 @@ _SIGS = [
     ("mdl_layout_rects", _I32, [_P, _P, _P]),
     ("mdl_layout_rows", _I32, [_P, _P, _P]),
     ("mdl_layout_maps", _I32, [_P, _P, _P]),
+    ("mdl_layout_units", _I32, [_P, _P, ctypes.POINTER(_SZ)]),
     ("mdl_layout_device_size", _I32, [_P, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     ("mdl_layout_upload", _I32, [_P, _P, _SZ, _P]),
     ("mdl_workspace_size", _I32, [_P, _I32, _I32, ctypes.POINTER(_SZ)]),
@@ -194,6 +195,14 @@ def mdl_layout_rows(layout: Layout):
     ex = np.zeros(layout.n, np.int32)
     _check(_lib.mdl_layout_rows(layout.handle, starts.ctypes.data, ex.ctypes.data))
     return [ex[starts[r]:starts[r + 1]].tolist() for r in range(layout.info["rows"])]
+
+
+def mdl_layout_units(layout: Layout):
+    """(units int32 [4n], byte offset of that array in the device descriptor)."""
+    units = np.zeros(4 * layout.info["n"], dtype=np.int32)
+    off = _SZ()
+    _check(_lib.mdl_layout_units(layout.handle, units.ctypes.data, ctypes.byref(off)))
+    return units, int(off.value)
 
 
 def mdl_layout_maps(layout: Layout):

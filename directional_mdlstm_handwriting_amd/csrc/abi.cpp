@@ -226,6 +226,14 @@ int mdl_layout_rows(const mdl_layout* layout, int32_t* row_start, int32_t* row_e
     return MDL_OK;
 }
 
+int mdl_layout_units(const mdl_layout* layout, int32_t* units, size_t* desc_offset) {
+    if (!layout || !units || !desc_offset) return fail(MDL_EINVAL, "mdl_layout_units: null argument");
+    const mdl::Layout& L = L_of(layout);
+    std::copy(L.units.begin(), L.units.end(), units);
+    *desc_offset = L.off.units;
+    return MDL_OK;
+}
+
 int mdl_layout_maps(const mdl_layout* layout, int32_t* eid, uint8_t* border) {
     if (!layout) return fail(MDL_EINVAL, "mdl_layout_maps: null layout");
     const mdl::Layout& L = L_of(layout);
@@ -299,6 +307,13 @@ static int check_extent(const char* fn, const mdl::Layout& L, int C, int H, int 
         return fail(MDL_EUNSUPPORTED, std::string(fn) + ": one direction's h plane or the canvas input above 1 GiB");
     if (backward && dabytes >= lim)
         return fail(MDL_EUNSUPPORTED, std::string(fn) + ": one direction's gate gradients above 2 GiB");
+    // The wavefront kernels address one example's stash and gate gradients (at most 16 H bytes per cell) through
+    // a per-example buffer range and park the accesses of idle lanes at byte offset 2^30, which must lie past
+    // that range.
+    int64_t cells = 0;
+    for (int e = 0; e < L.n; ++e) cells = std::max<int64_t>(cells, (int64_t)L.rect[4 * e + 2] * L.rect[4 * e + 3]);
+    if (cells * 16 * H > (int64_t(1) << 30))
+        return fail(MDL_EUNSUPPORTED, std::string(fn) + ": one example's cells x 16 H bytes above 1 GiB");
     return MDL_OK;
 }
 

@@ -2,10 +2,10 @@
 // and the padded-stack baseline (§VII-C), as integer host code.
 //
 // Shelf packing: examples are bucketed by height and the buckets visited from
-// the tallest; a row is filled by repeatedly taking the widest example of the
-// current bucket that still fits after a separator (equal widths: lowest
-// index); only when nothing of the current bucket fits is the row closed, so a
-// row may run on into the next, shorter bucket. Rows are then stacked with
+// the tallest; a row takes, each time, the widest example of the current
+// bucket that still fits after a separator (equal widths: lowest index); only
+// when nothing of the current bucket fits is the row closed, so a row may run
+// on into the next, shorter bucket. Rows are then stacked with
 // separator rows in between, examples top-aligned, and the row still open at
 // the end is kept. Canvas width = max(canvas_w_min, widest example).
 // The exact-height mode (§V: one height per packed row, which the input-skewing
@@ -174,31 +174,37 @@ int build_layout(const int32_t* heights, const int32_t* widths, int32_t n, int32
     }
 
     const int32_t Wc = std::max(canvas_w_min, wmax);
-    // distinct heights, tallest first; each bucket lists its examples in input order
-    std::vector<int32_t> hs(heights, heights + n);
-    std::sort(hs.begin(), hs.end(), std::greater<int32_t>());
-    hs.erase(std::unique(hs.begin(), hs.end()), hs.end());
-    std::vector<int32_t> x0(n, 0), row_of(n, -1);
-    std::vector<char> used(n, 0);
-    std::vector<int32_t> row;
+    // Step 1 of §V-A: buckets of equal height, filled tallest first. Step 2: rows take the widest example of
+    // the bucket that still fits. With each bucket ordered widest first (equal widths in input order), that
+    // example is the first one in this order that fits, and since a row only grows, whatever a scan passes
+    // over cannot fit later in the same row: one scan over what is left of the bucket fills the current row,
+    // and the row closes if the scan leaves anything. A scan that takes the whole bucket leaves the row open
+    // for the next, shorter bucket.
+    std::vector<int32_t> order(n);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        return heights[a] != heights[b] ? heights[a] > heights[b] : widths[a] > widths[b];
+    });
+    std::vector<int32_t> x0(n, 0), row, queue, rest;
     int64_t x_end = 0;
-    for (int32_t hb : hs) {
-        int64_t left = 0;
-        for (int e = 0; e < n; ++e) left += heights[e] == hb;
-        while (left > 0) {
-            const int64_t off = row.empty() ? 0 : x_end + sep;
-            int best = -1;
-            for (int e = 0; e < n; ++e) {
-                if (used[e] || heights[e] != hb || off + widths[e] > Wc) continue;
-                if (best < 0 || widths[e] > widths[best]) best = e;  // ascending scan keeps the lowest index on ties
+    for (int i = 0; i < n;) {
+        int j = i;
+        while (j < n && heights[order[j]] == heights[order[i]]) ++j;
+        queue.assign(order.begin() + i, order.begin() + j);
+        while (!queue.empty()) {
+            rest.clear();
+            for (int32_t e : queue) {
+                const int64_t off = row.empty() ? 0 : x_end + sep;
+                if (off + widths[e] <= Wc) {
+                    x0[e] = (int32_t)off;
+                    row.push_back(e);
+                    x_end = off + widths[e];
+                } else {
+                    rest.push_back(e);
+                }
             }
-            if (best >= 0) {
-                used[best] = 1;
-                --left;
-                x0[best] = (int32_t)off;
-                row.push_back(best);
-                x_end = off + widths[best];
-            } else {
+            queue.swap(rest);
+            if (!queue.empty()) {  // nothing left in the bucket fits: the row is full
                 L.rows.push_back(row);
                 row.clear();
                 x_end = 0;
@@ -209,6 +215,7 @@ int build_layout(const int32_t* heights, const int32_t* widths, int32_t n, int32
             row.clear();
             x_end = 0;
         }
+        i = j;
     }
     if (!row.empty()) L.rows.push_back(row);
 

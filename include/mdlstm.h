@@ -132,6 +132,18 @@ int mdl_layout_info(const mdl_layout* layout, int64_t* info);
 int mdl_layout_rects(const mdl_layout* layout, int32_t* rects, int32_t* real);
 
 /*
+ * The unit schedule: the wavefront kernels run one workgroup per (example,
+ * direction) unit, u = 4*e + d, and workgroup i takes units[i] (host array of
+ * 4n entries; the units with the most cells first, so the longest chains start
+ * first). *desc_offset receives the byte offset of this int32 array in the
+ * device descriptor that mdl_layout_upload writes. Results do not depend on
+ * the order (each unit's arithmetic is fixed and every reduction runs in a
+ * fixed order); a caller may permute the array in an uploaded descriptor, which
+ * only changes the dispatch order. Errors: MDL_EINVAL for a null argument.
+ */
+int mdl_layout_units(const mdl_layout* layout, int32_t* units, size_t* desc_offset);
+
+/*
  * Original example indices per packed row (Algorithm 1's result): row r holds
  * row_examples[row_start[r] .. row_start[r+1]-1], left to right.
  * row_start has info[MDL_INFO_ROWS]+1 entries, row_examples n.

@@ -102,29 +102,30 @@ def _shelf(heights, widths, canvas_w_min: int, sep: int, exact: bool) -> Layout:
     n = len(heights)
     Wc = max(int(canvas_w_min), max(widths))
 
-    # step 1 of §V-A: bucket the examples by height (tallest bucket first)
-    buckets = {}
-    for e in range(n):
-        buckets.setdefault(heights[e], []).append(e)
-
+    # §V-A step 1: buckets of equal height, filled tallest first.
+    # §V-A step 2: a row takes the widest example of the bucket that still fits (lowest index among equal
+    # widths). Ordered widest first, that is the first example of the bucket, in this order, that fits; a row
+    # only grows, so an example the scan passes over cannot fit later in the same row. One scan over the rest
+    # of the bucket therefore fills the current row, and the row is full if the scan leaves anything. A scan
+    # that empties the bucket leaves the row open for the next, shorter bucket (the loop as the pages print it).
     rows: List[List[int]] = []
     row: List[int] = []
     x_of = [0] * n
     x_end = 0
-    for hgt in sorted(buckets, reverse=True):
-        bucket = list(buckets[hgt])
-        while bucket:
-            off = 0 if not row else x_end + sep
-            fitting = [e for e in bucket if off + widths[e] <= Wc]
-            if fitting:
-                # step 2: the widest still-fitting example (lowest index on ties)
-                best = max(fitting, key=lambda e: (widths[e], -e))
-                bucket.remove(best)
-                row.append(best)
-                x_of[best] = off
-                x_end = off + widths[best]
-            else:
-                # current row is full: start a new one
+    for hgt in sorted(set(heights), reverse=True):
+        queue = sorted((e for e in range(n) if heights[e] == hgt), key=lambda e: (-widths[e], e))
+        while queue:
+            passed = []
+            for e in queue:
+                off = x_end + sep if row else 0
+                if off + widths[e] <= Wc:
+                    row.append(e)
+                    x_of[e] = off
+                    x_end = off + widths[e]
+                else:
+                    passed.append(e)
+            queue = passed
+            if queue:
                 rows.append(row)
                 row = []
                 x_end = 0

@@ -229,3 +229,18 @@ def test_pack_level_matches_oracle_stack_sizes(seed):
     assert np.array_equal(rects, ref.rects) and np.array_equal(real, ref.real)
     with pytest.raises(M.MdlError):
         M.mdl_pack_level(l1, 0, 4, 256, 1)
+
+
+def test_refuses_an_example_past_the_masked_lane_offset():
+    """One 64 x 70000 example at H = 16 fits the h-plane and input limits, but its stash range (cells x 16 H
+    bytes) would reach the byte offset where idle lanes park their accesses: refused before any launch (the
+    argument checks return first, so the placeholder device addresses are never used)."""
+    lay = M.mdl_pack([64], [70000], 70000, 1)
+    fake = 1 << 20
+    rc = M.library().mdl_forward(lay.handle, fake, fake, M.MDL_F32, 4, 16, fake, fake, fake, fake, fake, fake,
+                                 1 << 62, None)
+    assert rc == M.MDL_EUNSUPPORTED
+    assert "16 H" in M.mdl_last_error()
+    rc = M.library().mdl_backward(lay.handle, fake, fake, M.MDL_F32, 4, 16, fake, fake, fake, fake, fake, None, fake,
+                                  None, fake, fake, fake, fake, fake, 1 << 62, None)
+    assert rc == M.MDL_EUNSUPPORTED

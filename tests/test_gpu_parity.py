@@ -423,3 +423,50 @@ def test_stack_small():
     for j in range(2):
         for k, nm in enumerate(("dW", "db")):
             assert_close(f"conv{j} {nm}", _np(cg[j][k]), o["cg"][j][k], F32_TOL, sens=lambda j=j, k=k: sn()["cg"][j][k])
+
+
+def _fwd_bwd(dl, P, xs, dys, x_dtype="f32"):
+    lay = PackedLayer(dl, P.C, P.H, x_dtype)
+    poison(lay)
+    Pd = DeviceParams.from_host(P, DEV)
+    lay.scatter(flat_input(xs, x_dtype, DEV))
+    lay.forward(Pd)
+    lay.dirsum()
+    dy = torch.as_tensor(np.concatenate([d.reshape(-1) for d in dys]).astype(np.float32), device=DEV)
+    g = LayerGrads(*(torch.full_like(t, float("nan")) for t in (Pd.Wx, Pd.Ul, Pd.Uu, Pd.b)))
+    dx = torch.full((int(sum(np.asarray(x).size for x in xs)),), float("nan"), device=DEV)
+    lay.backward(Pd, g, dy_flat=dy, dx_flat=dx)
+    torch.cuda.synchronize()
+    return [lay.h_dirs.clone(), lay.y.clone(), dx, g.dWx, g.dUl, g.dUu, g.db]
+
+
+SCHEDULE_CASES = [
+    # (heights, widths, C, H): the f16 matrix-core kernels, the small-hidden-size vector-ALU kernels, the general
+    # fp32 kernels (no instantiation for H = 8), and H = 50
+    ([12, 30, 17, 40, 25, 8, 33], [50, 90, 17, 120, 40, 100, 60], 4, 16),
+    ([9, 14, 6, 12, 20], [30, 17, 40, 9, 51], 4, 2),
+    ([5, 9, 13, 7], [11, 6, 2, 30], 3, 8),
+    ([5, 3, 4, 2, 6], [9, 7, 3, 6, 12], 20, 50),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SCHEDULE_CASES)))
+def test_schedule_permutation_bit_identical(case):
+    """The same layout with its (example, direction) units dispatched in another order (a seeded permutation
+    written into the uploaded descriptor): every output and gradient is bit-identical, since each unit's
+    arithmetic is fixed and every reduction runs in a fixed order, whatever the order the units run in."""
+    h, w, C, H = SCHEDULE_CASES[case]
+    print(f"[gpu] schedule permutation: n={len(h)} C={C} H={H}", flush=True)
+    P = random_layer(400 + case, C, H)
+    xs = random_images(500 + case, h, w, C)
+    dys = cotangent(600 + case, h, w, H)
+    ref = _fwd_bwd(DeviceLayout(h, w, 128, 1, "packed", DEV), P, xs, dys)
+    dl = DeviceLayout(h, w, 128, 1, "packed", DEV)
+    units, off = M.mdl_layout_units(dl.layout)
+    perm = np.random.default_rng(700 + case).permutation(units).astype(np.int32)
+    assert not np.array_equal(perm, units)
+    dl.desc[off:off + 4 * len(units)].copy_(torch.as_tensor(perm.view(np.uint8), device=DEV))
+    torch.cuda.synchronize()
+    got = _fwd_bwd(dl, P, xs, dys)
+    for name, a, b in zip(("h_dirs", "y", "dx", "dWx", "dUl", "dUu", "db"), got, ref):
+        assert torch.equal(a, b), name
