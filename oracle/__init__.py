@@ -12,6 +12,7 @@ Modules:
   pack       example packing (§IX-B (packing algorithm details, Algorithm 1)) and the padded stack
   canvas     scatter onto the canvas, direction sum and un-packing (§V-A)
   mdlstm     the cell, forward and 2D BPTT, per-cell and per-diagonal forms
+  leaky      the Leaky-LP cell (lambda gate, two output gates), forward and 2D BPTT (§III, Fig. 4(b), §IX-A)
   blockconv  block-strided convolution with tensor-list chunking (§V-B)
   stack      three MDLSTM levels with block convs, re-packed per level (§II, §V)
 
@@ -20,4 +21,4 @@ against something other than itself (brute force, closed forms, a library
 routine, finite differences, invariants the pages state).
 """
 
-from . import pack, canvas, mdlstm, blockconv, stack  # noqa: F401
+from . import pack, canvas, mdlstm, leaky, blockconv, stack  # noqa: F401

@@ -62,6 +62,31 @@ class LayerParams:
 
 
 @dataclasses.dataclass
+class LeakyLayerParams:
+    """Parameters of one 4-direction Leaky-LP layer (float32).
+
+    Wx[d][C][5H], Ul[d][H][5H], Uu[d][H][5H], b[d][5H] with the gate blocks ordered (f, lambda, o1, o2, g),
+    each H wide; Vl[d][H][3H], Vu[d][H][3H] project the left and upper predecessors' memory states onto the
+    gates (lambda, o1, o2).
+    """
+
+    Wx: np.ndarray
+    Ul: np.ndarray
+    Uu: np.ndarray
+    b: np.ndarray
+    Vl: np.ndarray
+    Vu: np.ndarray
+
+    @property
+    def C(self) -> int:
+        return int(self.Wx.shape[1])
+
+    @property
+    def H(self) -> int:
+        return int(self.Ul.shape[1])
+
+
+@dataclasses.dataclass
 class ConvParams:
     """Block-strided conv between MDLSTM levels: W[Cout][4][H][kh][kw], b[Cout]."""
 
@@ -148,8 +173,45 @@ def _pixels(rng: np.random.Generator, heights, widths, C: int) -> List[np.ndarra
     return [rng.random((int(h), int(w), C), dtype=np.float32) for h, w in zip(heights, widths)]
 
 
-def make_workload(name: str, seed: int = 0) -> Workload:
-    """Build one of the five named workloads for ``seed``."""
+def _leaky(rng: np.random.Generator, C: int, H: int) -> LeakyLayerParams:
+    """Wx, Ul, Uu, b drawn as for the plain cell, then the memory-state projections Vl, Vu."""
+    P = _layer(rng, C, H)
+    Vl = rng.normal(0.0, 0.1, (DIRECTIONS, H, 3 * H)).astype(np.float32)
+    Vu = rng.normal(0.0, 0.1, (DIRECTIONS, H, 3 * H)).astype(np.float32)
+    return LeakyLayerParams(P.Wx, P.Ul, P.Uu, P.b, Vl, Vu)
+
+
+def random_leaky_layer(seed: int, C: int, H: int, scale: float = 0.1) -> LeakyLayerParams:
+    """Stand-alone random Leaky-LP layer parameters."""
+    rng = np.random.default_rng(seed)
+    p = _leaky(rng, C, H)
+    if scale != 0.1:
+        p = LeakyLayerParams(*(a * np.float32(scale / 0.1) for a in (p.Wx, p.Ul, p.Uu, p.b, p.Vl, p.Vu)))
+    return p
+
+
+def make_workload(name: str, seed: int = 0, cell: str = "mdlstm") -> Workload:
+    """Build one of the five named workloads for ``seed``. cell = "leaky": the single-layer workloads (tiny,
+    word, word_padded, line) with a Leaky-LP layer, drawn from the same stream (the same sizes, pixels and
+    Wx, Ul, Uu, b, then Vl, Vu)."""
+    if cell == "leaky":
+        if name == "stack":
+            raise ValueError("the Leaky-LP cell is offered for the single-layer workloads")
+        wl = make_workload(name, seed)
+        rng = np.random.default_rng(seed)
+        # replay the draws up to the layer, then draw the layer as a Leaky-LP one
+        if name == "tiny":
+            rng.integers(4, 9, 4); rng.integers(4, 13, 4)
+        elif name in ("word", "word_padded"):
+            _word_sizes(rng, 64)
+        else:
+            rng.integers(256, 1025, 32)
+        _pixels(rng, wl.heights, wl.widths, wl.C)
+        wl.layers = [_leaky(rng, wl.C, wl.H)]
+        wl.name = name
+        return wl
+    if cell != "mdlstm":
+        raise ValueError(f"unknown cell {cell!r}")
     rng = np.random.default_rng(seed)
     if name == "tiny":
         h = rng.integers(4, 9, 4).astype(np.int32)
