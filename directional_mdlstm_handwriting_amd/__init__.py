@@ -40,6 +40,8 @@ MDL_PACK_PADDED = 1
 MDL_PACK_EXACT = 2
 MDL_F32 = 0
 MDL_BF16 = 1
+MDL_CELL_MDLSTM = 0
+MDL_CELL_LEAKY_LP = 1
 
 INFO_KEYS = ("n", "canvas_h", "canvas_w", "rows", "real_pixels", "computed_cells", "max_depth", "max_diag", "mode")
 
@@ -60,10 +62,10 @@ _SIGS = [
     ("mdl_layout_upload", _I32, [_P, _P, _SZ, _P]),
     ("mdl_workspace_size", _I32, [_P, _I32, _I32, ctypes.POINTER(_SZ)]),
     ("mdl_scatter", _I32, [_P, _P, _P, _I32, _I32, _P, _P]),
-    ("mdl_forward", _I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("mdl_forward", _I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("mdl_dirsum_unpack", _I32, [_P, _P, _P, _I32, _P, _P]),
-    ("mdl_backward", _I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                            _P, _SZ, _P]),
+    ("mdl_backward", _I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                            _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("mdl_blockconv_forward", _I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _P, _P]),
     ("mdl_blockconv_workspace_size", _I32, [_P, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     ("mdl_blockconv_backward", _I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ,
@@ -232,21 +234,24 @@ def mdl_scatter(layout: Layout, d_desc, x_flat, C: int, dtype: int, x_canvas, st
     _check(_lib.mdl_scatter(layout.handle, _ptr(d_desc), _ptr(x_flat), C, dtype, _ptr(x_canvas), _stream(stream)))
 
 
-def mdl_forward(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, Wx, Ul, Uu, b, h_dirs, ws,
-                ws_bytes: int, stream=None):
-    _check(_lib.mdl_forward(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, _ptr(Wx), _ptr(Ul),
-                            _ptr(Uu), _ptr(b), _ptr(h_dirs), _ptr(ws), ws_bytes, _stream(stream)))
+def mdl_forward(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, cell: int, Wx, Ul, Uu, b, Vl, Vu,
+                h_dirs, ws, ws_bytes: int, stream=None):
+    _check(_lib.mdl_forward(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, cell, _ptr(Wx), _ptr(Ul),
+                            _ptr(Uu), _ptr(b), _ptr(Vl), _ptr(Vu), _ptr(h_dirs), _ptr(ws), ws_bytes,
+                            _stream(stream)))
 
 
 def mdl_dirsum_unpack(layout: Layout, d_desc, h_dirs, H: int, y_flat, stream=None):
     _check(_lib.mdl_dirsum_unpack(layout.handle, _ptr(d_desc), _ptr(h_dirs), H, _ptr(y_flat), _stream(stream)))
 
 
-def mdl_backward(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, Wx, Ul, Uu, h_dirs, dy_flat,
-                 dh_dirs, dx_flat, dx_canvas, dWx, dUl, dUu, db, ws, ws_bytes: int, stream=None):
-    _check(_lib.mdl_backward(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, _ptr(Wx), _ptr(Ul),
-                             _ptr(Uu), _ptr(h_dirs), _ptr(dy_flat), _ptr(dh_dirs), _ptr(dx_flat), _ptr(dx_canvas),
-                             _ptr(dWx), _ptr(dUl), _ptr(dUu), _ptr(db), _ptr(ws), ws_bytes, _stream(stream)))
+def mdl_backward(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, cell: int, Wx, Ul, Uu, Vl, Vu,
+                 h_dirs, dy_flat, dh_dirs, dx_flat, dx_canvas, dWx, dUl, dUu, db, dVl, dVu, ws, ws_bytes: int,
+                 stream=None):
+    _check(_lib.mdl_backward(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, cell, _ptr(Wx), _ptr(Ul),
+                             _ptr(Uu), _ptr(Vl), _ptr(Vu), _ptr(h_dirs), _ptr(dy_flat), _ptr(dh_dirs),
+                             _ptr(dx_flat), _ptr(dx_canvas), _ptr(dWx), _ptr(dUl), _ptr(dUu), _ptr(db), _ptr(dVl),
+                             _ptr(dVu), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def mdl_blockconv_forward(lk: Layout, d_desc_k, lk1: Layout, d_desc_k1, h_dirs_k, H: int, kh: int, kw: int, Wc, bc,

@@ -317,17 +317,54 @@ static int check_extent(const char* fn, const mdl::Layout& L, int C, int H, int 
     return MDL_OK;
 }
 
+static int check_cell(const char* fn, int32_t cell, const void* Vl, const void* Vu) {
+    if (cell == MDL_CELL_MDLSTM) {
+        if (Vl || Vu) return fail(MDL_EINVAL, std::string(fn) + ": memory-state projections given with the MDLSTM cell");
+        return MDL_OK;
+    }
+    if (cell == MDL_CELL_LEAKY_LP) {
+        if (!Vl || !Vu) return fail(MDL_EINVAL, std::string(fn) + ": the Leaky LP cell needs its memory-state projections");
+        return MDL_OK;
+    }
+    return fail(MDL_EINVAL, std::string(fn) + ": unknown cell");
+}
+
 int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype, int32_t C,
-                int32_t H, const float* Wx, const float* Ul, const float* Uu, const float* b, float* h_dirs, void* ws,
-                size_t ws_bytes, void* stream) {
+                int32_t H, int32_t cell, const float* Wx, const float* Ul, const float* Uu, const float* b,
+                const float* Vl, const float* Vu, float* h_dirs, void* ws, size_t ws_bytes, void* stream) {
     GUARD_BEGIN
     int rc = check_layer("mdl_forward", layout, d_desc, C, H, x_dtype);
     if (rc) return rc;
+    if ((rc = check_cell("mdl_forward", cell, Vl, Vu))) return rc;
     if (!x_canvas || !Wx || !Ul || !Uu || !b || !h_dirs || !ws) return fail(MDL_EINVAL, "mdl_forward: null tensor");
     const mdl::Layout& L = L_of(layout);
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
     if ((rc = check_extent("mdl_forward", L, C, H, x_dtype, false))) return rc;
+    if (cell == MDL_CELL_LEAKY_LP) {
+        if (!mdl::leaky_supported(H, C, L.max_diag))
+            return fail(MDL_EUNSUPPORTED, "mdl_forward: the Leaky LP cell runs for H in {4, 8, 16, 32}, C <= 16 and "
+                                          "a widest diagonal of at most 64 cells (32 at H = 32)");
+        size_t lmax = 0;
+        if ((rc = max_lds(lmax))) return rc;
+        if (mdl::leaky_fwd_lds(H, L.max_diag) > lmax)
+            return fail(MDL_EUNSUPPORTED, "mdl_forward: diagonal state exceeds LDS");
+        const mdl::Dev D = make_dev(layout, d_desc);
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        float* stash = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + W.stash);
+        hipError_t e;
+        {
+            Timed t("zero_fill");
+            e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, "mdl_forward: zero fill");
+        {
+            Timed t("fwd_wavefront");
+            e = mdl::launch_fwd_leaky(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, Vl, Vu, stash, h_dirs, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, "mdl_forward: wavefront");
+        return MDL_OK;
+    }
     // small hidden sizes: vector-ALU wavefront; instantiated matrix-core shapes: f16 wavefront; both with
     // the projection fused. Otherwise the projection as its own GEMM and the general fp32 wavefront.
     const bool small = mdl::small_fwd_supported(H, C, x_dtype, L.max_diag);
@@ -387,12 +424,17 @@ int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float*
 }
 
 int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype, int32_t C,
-                 int32_t H, const float* Wx, const float* Ul, const float* Uu, const float* h_dirs,
-                 const float* dy_flat, const float* dh_dirs, float* dx_flat, float* dx_canvas, float* dWx, float* dUl,
-                 float* dUu, float* db, void* ws, size_t ws_bytes, void* stream) {
+                 int32_t H, int32_t cell, const float* Wx, const float* Ul, const float* Uu, const float* Vl,
+                 const float* Vu, const float* h_dirs, const float* dy_flat, const float* dh_dirs, float* dx_flat,
+                 float* dx_canvas, float* dWx, float* dUl, float* dUu, float* db, float* dVl, float* dVu, void* ws,
+                 size_t ws_bytes, void* stream) {
     GUARD_BEGIN
     int rc = check_layer("mdl_backward", layout, d_desc, C, H, x_dtype);
     if (rc) return rc;
+    if ((rc = check_cell("mdl_backward", cell, Vl, Vu))) return rc;
+    const bool lk = cell == MDL_CELL_LEAKY_LP;
+    if (lk != (dVl != nullptr) || lk != (dVu != nullptr))
+        return fail(MDL_EINVAL, "mdl_backward: dVl and dVu go with the Leaky LP cell, and only with it");
     if (!x_canvas || !Wx || !Ul || !Uu || !h_dirs || !ws) return fail(MDL_EINVAL, "mdl_backward: null tensor");
     if (!dWx || !dUl || !dUu || !db) return fail(MDL_EINVAL, "mdl_backward: null weight-gradient output");
     if ((dy_flat == nullptr) == (dh_dirs == nullptr))
@@ -400,7 +442,10 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     const mdl::Layout& L = L_of(layout);
     const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_backward: workspace smaller than mdl_workspace_size");
-    if (!mdl::small_bwd_supported(H, L.max_diag) && !mdl::bwd16_supported(H, L.max_diag) &&
+    if (lk && !mdl::leaky_supported(H, C, L.max_diag))
+        return fail(MDL_EUNSUPPORTED, "mdl_backward: the Leaky LP cell runs for H in {4, 8, 16, 32}, C <= 16 and a "
+                                      "widest diagonal of at most 64 cells (32 at H = 32)");
+    if (!lk && !mdl::small_bwd_supported(H, L.max_diag) && !mdl::bwd16_supported(H, L.max_diag) &&
         !mdl::chain_uses_mfma(H, L.max_diag) &&
         (int64_t)L.max_diag * H > mdl::chain_max_items())
         return fail(MDL_EUNSUPPORTED, "mdl_backward: widest diagonal x H exceeds the wavefront kernel's items");
@@ -408,7 +453,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     if ((rc = check_extent("mdl_backward", L, C, H, x_dtype, true))) return rc;
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
-    if (mdl::bwd_chain_lds(H, L.max_diag) > lmax)
+    if ((lk ? mdl::leaky_bwd_lds(H, L.max_diag) : mdl::bwd_chain_lds(H, L.max_diag)) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward: recurrent weights and diagonal state exceed LDS");
     if ((wg2 ? mdl::wgrad2_lds_bytes(C, H, x_dtype) : mdl::wgrad_lds_bytes(C, H)) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward: weight-gradient tile exceeds LDS");
@@ -421,7 +466,8 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     hipError_t e;
     {
         Timed t("bwd_wavefront");
-        e = mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
+        e = lk ? mdl::launch_bwd_leaky(D, H, Ul, Uu, Vl, Vu, stash, dy_flat, dh_dirs, dA, st)
+               : mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward: reverse wavefront");
     if (dx_canvas) {
@@ -435,6 +481,13 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
                               st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight and input gradients");
+    if (lk) {
+        // the memory-state projections' gradients, their partials in the partial-sum buffer the weight gradients
+        // above are done with ([ngroups][4][2H][3H] fits in its [nparts][4][C+1+2H][5H])
+        Timed t("wgrad_mem");
+        e = mdl::launch_dv_leaky(D, H, stash, dA, part, dVl, dVu, st);
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward: memory-state projection gradients");
+    }
     return MDL_OK;
     GUARD_END
 }

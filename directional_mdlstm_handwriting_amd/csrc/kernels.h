@@ -174,6 +174,19 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
 hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st);
 int64_t conv_nchunks(const Dev& Dk1);
+// the Leaky LP cell (k_leaky.hip): forward and reverse wavefronts on the fp32 matrix cores, and the weight
+// gradients of its memory-state projections (partials in `part`, added in workgroup order)
+bool leaky_supported(int H, int C, int Lmax);
+size_t leaky_fwd_lds(int H, int Lmax);
+size_t leaky_bwd_lds(int H, int Lmax);
+hipError_t launch_fwd_leaky(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
+                            const float* b, const float* Ul, const float* Uu, const float* Vl, const float* Vu,
+                            float* stash, float* h_dirs, hipStream_t st);
+hipError_t launch_bwd_leaky(const Dev& D, int H, const float* Ul, const float* Uu, const float* Vl, const float* Vu,
+                            const float* stash, const float* dy_flat, const float* dh_dirs, float* dA,
+                            hipStream_t st);
+hipError_t launch_dv_leaky(const Dev& D, int H, const float* stash, const float* dA, float* part, float* dVl,
+                           float* dVu, hipStream_t st);
 // this device's fixed weight-gradient scratch of the block conv (address and size), for callers that cannot
 // allocate; every call on one device shares it
 hipError_t conv_scratch(void** ptr, size_t* bytes);

@@ -18,7 +18,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (MDL_BF16, MDL_F32, MDL_PACK_ALG1, MDL_PACK_EXACT, MDL_PACK_PADDED, Layout, mdl_backward,
+from . import (MDL_BF16, MDL_CELL_LEAKY_LP, MDL_CELL_MDLSTM, MDL_F32, MDL_PACK_ALG1, MDL_PACK_EXACT, MDL_PACK_PADDED, Layout, mdl_backward,
                mdl_blockconv_backward, mdl_blockconv_forward, mdl_blockconv_workspace_size, mdl_dirsum_unpack, mdl_forward,
                mdl_layout_device_size, mdl_layout_rects, mdl_layout_upload, mdl_pack, mdl_pack_level, mdl_scatter, mdl_workspace_size,
                mdl_ctc_head, mdl_ctc_workspace_size)
@@ -32,14 +32,22 @@ def _dev(a, device, dtype=torch.float32):
 
 @dataclasses.dataclass
 class DeviceParams:
+    """A layer's weights on the device; Vl, Vu (the memory-state projections) only for the Leaky LP cell."""
     Wx: torch.Tensor
     Ul: torch.Tensor
     Uu: torch.Tensor
     b: torch.Tensor
+    Vl: Optional[torch.Tensor] = None
+    Vu: Optional[torch.Tensor] = None
 
     @staticmethod
     def from_host(P, device) -> "DeviceParams":
-        return DeviceParams(_dev(P.Wx, device), _dev(P.Ul, device), _dev(P.Uu, device), _dev(P.b, device))
+        V = [_dev(getattr(P, n), device) if getattr(P, n, None) is not None else None for n in ("Vl", "Vu")]
+        return DeviceParams(_dev(P.Wx, device), _dev(P.Ul, device), _dev(P.Uu, device), _dev(P.b, device), *V)
+
+    @property
+    def cell(self):
+        return MDL_CELL_MDLSTM if self.Vl is None else MDL_CELL_LEAKY_LP
 
     @property
     def C(self):
@@ -106,30 +114,35 @@ class PackedLayer:
         mdl_scatter(self.dl.layout, self.dl.desc, x_flat, self.C, self.x_dtype, self.x_canvas, stream)
 
     def forward(self, P: DeviceParams, stream=None):
-        mdl_forward(self.dl.layout, self.dl.desc, self.x_canvas, self.x_dtype, self.C, self.H, P.Wx, P.Ul, P.Uu,
-                    P.b, self.h_dirs, self.ws, self.ws_bytes, stream)
+        """The cell follows the parameters: the Leaky LP cell when they carry Vl, Vu."""
+        mdl_forward(self.dl.layout, self.dl.desc, self.x_canvas, self.x_dtype, self.C, self.H, P.cell, P.Wx, P.Ul,
+                    P.Uu, P.b, P.Vl, P.Vu, self.h_dirs, self.ws, self.ws_bytes, stream)
 
     def dirsum(self, stream=None):
         mdl_dirsum_unpack(self.dl.layout, self.dl.desc, self.h_dirs, self.H, self.y, stream)
 
     def backward(self, P: DeviceParams, grads: "LayerGrads", dy_flat=None, dh_dirs=None, dx_flat=None,
                  dx_canvas=None, stream=None):
-        mdl_backward(self.dl.layout, self.dl.desc, self.x_canvas, self.x_dtype, self.C, self.H, P.Wx, P.Ul, P.Uu,
-                     self.h_dirs, dy_flat, dh_dirs, dx_flat, dx_canvas, grads.dWx, grads.dUl, grads.dUu, grads.db,
-                     self.ws, self.ws_bytes, stream)
+        mdl_backward(self.dl.layout, self.dl.desc, self.x_canvas, self.x_dtype, self.C, self.H, P.cell, P.Wx, P.Ul,
+                     P.Uu, P.Vl, P.Vu, self.h_dirs, dy_flat, dh_dirs, dx_flat, dx_canvas, grads.dWx, grads.dUl,
+                     grads.dUu, grads.db, grads.dVl, grads.dVu, self.ws, self.ws_bytes, stream)
 
 
 @dataclasses.dataclass
 class LayerGrads:
+    """Weight gradients; dVl, dVu for the Leaky LP cell only."""
     dWx: torch.Tensor
     dUl: torch.Tensor
     dUu: torch.Tensor
     db: torch.Tensor
+    dVl: Optional[torch.Tensor] = None
+    dVu: Optional[torch.Tensor] = None
 
     @staticmethod
     def like(P: DeviceParams) -> "LayerGrads":
+        V = [torch.empty_like(t) if t is not None else None for t in (P.Vl, P.Vu)]
         return LayerGrads(torch.empty_like(P.Wx), torch.empty_like(P.Ul), torch.empty_like(P.Uu),
-                          torch.empty_like(P.b))
+                          torch.empty_like(P.b), *V)
 
 
 def flat_input(xs: Sequence[np.ndarray], x_dtype: str, device) -> torch.Tensor:

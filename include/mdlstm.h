@@ -63,6 +63,10 @@ extern "C" {
 #define MDL_F32  0
 #define MDL_BF16 1
 
+/* cells ("No Padding Please" §III) */
+#define MDL_CELL_MDLSTM   0 /* the 2D MDLSTM cell: input gate, two forget gates, output gate */
+#define MDL_CELL_LEAKY_LP 1 /* the stable Leaky LP cell: lambda gate, leaky update, two output gates */
+
 /* indices into the int64 array filled by mdl_layout_info */
 #define MDL_INFO_N              0 /* examples */
 #define MDL_INFO_CANVAS_H       1
@@ -202,20 +206,30 @@ int mdl_scatter(const mdl_layout* layout, const void* d_desc, const void* x_flat
  * for the hidden sizes and channel counts the library instantiates and as one
  * GEMM before it otherwise, and the recurrence as an anti-diagonal wavefront
  * (§I; RETURNN §4.2: all positions of a diagonal at once, four directions at
- * once), each example on its own local diagonals:
- *   a = x.Wx[d] + b[d] + h_left.Ul[d] + h_up.Uu[d]
- *   i, f_l, f_u, o = sigmoid(.), g = tanh(.)
- *   c = f_l*c_left + f_u*c_up + i*g,  h = o*tanh(c)
- * with predecessors outside the example read as zero (§V mask).
+ * once), each example on its own local diagonals. `cell`:
+ *   MDL_CELL_MDLSTM (§III, Figure 4(a)): Vl and Vu must be NULL;
+ *     a = x.Wx[d] + b[d] + h_left.Ul[d] + h_up.Uu[d]      (gates i, f_l, f_u, o, g)
+ *     i, f_l, f_u, o = sigmoid(.), g = tanh(.)
+ *     c = f_l*c_left + f_u*c_up + i*g,  h = o*tanh(c)
+ *   MDL_CELL_LEAKY_LP (§III, Figure 4(b), §IX-A): Vl, Vu [4][H][3H] project the
+ *   predecessors' memory states onto the gates lam, o1, o2;
+ *     a = x.Wx[d] + b[d] + h_left.Ul[d] + h_up.Uu[d]      (gates f, lam, o1, o2, g)
+ *     a[lam, o1, o2] += s_left.Vl[d] + s_up.Vu[d]
+ *     sbar = lam*s_left + (1-lam)*s_up,  s = f*sbar + (1-f)*g,  h = o1*tanh(s) + o2*s
+ *   (supported for H in {4, 8, 16, 32}, C <= 16, and a widest diagonal of at
+ *   most 64 cells, 32 at H = 32; MDL_EUNSUPPORTED otherwise).
+ * Predecessors outside the example read as zero (§V mask).
  * x_canvas [Hc][Wc][C] (x_dtype), h_dirs out [4][Hc][Wc][H] float32 (zero
  * outside the computed region). ws: >= mdl_workspace_size bytes.
- * MDL_EUNSUPPORTED when H or the widest diagonal exceed the kernel's LDS budget,
- * or when one direction's h plane (Hc*Wc*H floats) or the canvas input
- * exceeds 1 GiB (buffer ranges are 32-bit).
+ * MDL_EINVAL for an unknown cell, or Vl/Vu given with the plain cell or missing
+ * with the Leaky LP one. MDL_EUNSUPPORTED when H or the widest diagonal exceed
+ * the kernel's LDS budget, or when one direction's h plane (Hc*Wc*H floats) or
+ * the canvas input exceeds 1 GiB (buffer ranges are 32-bit).
  */
 int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
-                int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu,
-                const float* b, float* h_dirs, void* ws, size_t ws_bytes, void* stream);
+                int32_t C, int32_t H, int32_t cell, const float* Wx, const float* Ul, const float* Uu,
+                const float* b, const float* Vl, const float* Vu, float* h_dirs, void* ws,
+                size_t ws_bytes, void* stream);
 
 /*
  * Direction sum and un-packing (§III four directions combined; §V-A
@@ -229,23 +243,25 @@ int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float*
 /*
  * 2D BPTT backward of the mdl_forward that filled `ws` (RETURNN §4.2: the
  * recurrent part back-propagated over the diagonals in reverse, then the
- * weight and input gradients as matrix products).
+ * weight and input gradients as matrix products), for the same `cell`.
  * Upstream gradient: exactly one of
  *   dy_flat  (flat [h][w][H], gradient of the direction-summed output; every
  *            direction receives it), or
  *   dh_dirs  ([4][Hc][Wc][H], gradient of each direction's output).
  * Outputs (each may be NULL except the weight gradients):
  *   dx_flat [h][w][C] float32 per example, dx_canvas [Hc][Wc][C] float32 (zero
- *   outside the real pixels); dWx, dUl, dUu, db shaped like Wx, Ul, Uu, b.
+ *   outside the real pixels); dWx, dUl, dUu, db shaped like Wx, Ul, Uu, b; for
+ *   MDL_CELL_LEAKY_LP also dVl, dVu shaped like Vl, Vu (NULL, with Vl and Vu,
+ *   for the plain cell).
  * Weight gradients are fixed-order blocked sums over all computed cells.
  * MDL_EUNSUPPORTED under the same size limits as mdl_forward and when one
  * direction's gate gradients (T*5H floats, T = computed cells) reach 2 GiB.
  */
 int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
-                 int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu,
-                 const float* h_dirs, const float* dy_flat, const float* dh_dirs, float* dx_flat,
-                 float* dx_canvas, float* dWx, float* dUl, float* dUu, float* db, void* ws,
-                 size_t ws_bytes, void* stream);
+                 int32_t C, int32_t H, int32_t cell, const float* Wx, const float* Ul, const float* Uu,
+                 const float* Vl, const float* Vu, const float* h_dirs, const float* dy_flat,
+                 const float* dh_dirs, float* dx_flat, float* dx_canvas, float* dWx, float* dUl,
+                 float* dUu, float* db, float* dVl, float* dVu, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Block-strided convolution between MDLSTM levels (§V-B), kernel kh x kw with

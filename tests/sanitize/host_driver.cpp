@@ -87,16 +87,26 @@ int main() {
     // device entry points: the checks that run before any launch
     void* fake = reinterpret_cast<void*>(uintptr_t(1) << 20);
     float* ff = static_cast<float*>(fake);
-    EXPECT(mdl_forward(L, fake, fake, MDL_F32, 0, 16, ff, ff, ff, ff, ff, fake, 1 << 20, nullptr) == MDL_EINVAL);
-    EXPECT(mdl_forward(L, fake, fake, 7, 4, 16, ff, ff, ff, ff, ff, fake, 1 << 20, nullptr) == MDL_EINVAL);
-    EXPECT(mdl_forward(L, fake, fake, MDL_F32, 4, 16, ff, ff, ff, ff, ff, fake, 16, nullptr) == MDL_ESIZE);
-    EXPECT(mdl_backward(L, fake, fake, MDL_F32, 4, 16, ff, ff, ff, ff, ff, ff, ff, nullptr, ff, ff, ff, ff, fake,
-                        1 << 20, nullptr) == MDL_EINVAL);  // dy_flat and dh_dirs both given
+    const int M0 = MDL_CELL_MDLSTM, M1 = MDL_CELL_LEAKY_LP;
+    EXPECT(mdl_forward(L, fake, fake, MDL_F32, 0, 16, M0, ff, ff, ff, ff, nullptr, nullptr, ff, fake, 1 << 20, nullptr) ==
+           MDL_EINVAL);
+    EXPECT(mdl_forward(L, fake, fake, 7, 4, 16, M0, ff, ff, ff, ff, nullptr, nullptr, ff, fake, 1 << 20, nullptr) ==
+           MDL_EINVAL);
+    EXPECT(mdl_forward(L, fake, fake, MDL_F32, 4, 16, M0, ff, ff, ff, ff, nullptr, nullptr, ff, fake, 16, nullptr) ==
+           MDL_ESIZE);
+    EXPECT(mdl_forward(L, fake, fake, MDL_F32, 4, 16, M1, ff, ff, ff, ff, nullptr, nullptr, ff, fake, 1 << 20, nullptr) ==
+           MDL_EINVAL);  // Leaky LP without its projections
+    EXPECT(mdl_forward(L, fake, fake, MDL_F32, 4, 16, 9, ff, ff, ff, ff, nullptr, nullptr, ff, fake, 1 << 20, nullptr) ==
+           MDL_EINVAL);  // unknown cell
+    EXPECT(mdl_backward(L, fake, fake, MDL_F32, 4, 16, M0, ff, ff, ff, nullptr, nullptr, ff, ff, ff, ff, nullptr, ff, ff,
+                        ff, ff, nullptr, nullptr, fake, 1 << 20, nullptr) == MDL_EINVAL);  // dy_flat and dh_dirs both
+    EXPECT(mdl_backward(L, fake, fake, MDL_F32, 4, 16, M1, ff, ff, ff, ff, ff, ff, ff, nullptr, ff, nullptr, ff, ff,
+                        ff, ff, nullptr, nullptr, fake, 1 << 20, nullptr) == MDL_EINVAL);  // Leaky LP without dV
     mdl_layout_free(L);
     int32_t hl = 64, wl = 70000;
     EXPECT(mdl_pack(&hl, &wl, 1, 70000, 1, MDL_PACK_ALG1, &L) == MDL_OK);
-    EXPECT(mdl_forward(L, fake, fake, MDL_F32, 4, 16, ff, ff, ff, ff, ff, fake, size_t(1) << 62, nullptr) ==
-           MDL_EUNSUPPORTED);
+    EXPECT(mdl_forward(L, fake, fake, MDL_F32, 4, 16, MDL_CELL_MDLSTM, ff, ff, ff, ff, nullptr, nullptr, ff, fake,
+                       size_t(1) << 62, nullptr) == MDL_EUNSUPPORTED);
     mdl_layout_free(L);
     mdl_layout_free(nullptr);
     // the timing hooks with nothing recorded

@@ -150,30 +150,41 @@ def test_error_codes():
     b = ctypes.c_size_t()
     assert lib.mdl_workspace_size(lay.handle, 0, 4, ctypes.byref(b)) == M.MDL_EINVAL
     # device entry points validate before touching the device
-    assert lib.mdl_forward(lay.handle, None, None, 0, 1, 4, None, None, None, None, None, None, 0, None) == M.MDL_EINVAL
-    assert lib.mdl_backward(lay.handle, 1, 1, 0, 1, 4, 1, 1, 1, 1, 1, 1, None, None, 1, 1, 1, 1, 1, 1, None) \
-        == M.MDL_EINVAL   # both dy_flat and dh_dirs given
+    assert lib.mdl_forward(lay.handle, None, None, 0, 1, 4, 0, None, None, None, None, None, None, None, None, 0,
+                           None) == M.MDL_EINVAL
+    assert lib.mdl_backward(lay.handle, 1, 1, 0, 1, 4, 0, 1, 1, 1, None, None, 1, 1, 1, 1, None, 1, 1, 1, 1, None, None,
+                            1, 1, None) == M.MDL_EINVAL   # both dy_flat and dh_dirs given
     assert "exactly one" in M.mdl_last_error()
     assert lib.mdl_scatter(lay.handle, 1, 1, 1, 5, 1, None) == M.MDL_EINVAL
     ws = M.mdl_workspace_size(lay, 4, 16)
-    assert lib.mdl_forward(lay.handle, 1, 1, 0, 4, 16, 1, 1, 1, 1, 1, 1, ws - 1, None) == M.MDL_ESIZE
+    assert lib.mdl_forward(lay.handle, 1, 1, 0, 4, 16, 0, 1, 1, 1, 1, None, None, 1, 1, ws - 1, None) == M.MDL_ESIZE
+    # the cell and its memory-state projections go together
+    assert lib.mdl_forward(lay.handle, 1, 1, 0, 4, 16, 0, 1, 1, 1, 1, 1, 1, 1, 1, ws, None) == M.MDL_EINVAL
+    assert lib.mdl_forward(lay.handle, 1, 1, 0, 4, 16, 1, 1, 1, 1, 1, None, None, 1, 1, ws, None) == M.MDL_EINVAL
+    assert lib.mdl_forward(lay.handle, 1, 1, 0, 4, 16, 7, 1, 1, 1, 1, None, None, 1, 1, ws, None) == M.MDL_EINVAL
+    assert lib.mdl_forward(lay.handle, 1, 1, 0, 4, 12, 1, 1, 1, 1, 1, 1, 1, 1, 1, M.mdl_workspace_size(lay, 4, 12),
+                           None) == M.MDL_EUNSUPPORTED   # no Leaky LP instantiation for H = 12
+    assert lib.mdl_backward(lay.handle, 1, 1, 0, 4, 16, 1, 1, 1, 1, 1, 1, 1, 1, None, None, None, 1, 1, 1, 1, None,
+                            None, 1, ws, None) == M.MDL_EINVAL   # Leaky LP without dVl, dVu
     # buffer ranges are 32-bit: one h plane of 3000 x 3000 x 32 floats (1.07 GiB) is refused before any launch
     big = M.mdl_pack([3000], [3000], 8, 1)
     wsb = M.mdl_workspace_size(big, 4, 32)
-    assert lib.mdl_forward(big.handle, 1, 1, 0, 4, 32, 1, 1, 1, 1, 1, 1, ctypes.c_size_t(wsb), None) \
+    assert lib.mdl_forward(big.handle, 1, 1, 0, 4, 32, 0, 1, 1, 1, 1, None, None, 1, 1, ctypes.c_size_t(wsb), None) \
         == M.MDL_EUNSUPPORTED
     assert "1 GiB" in M.mdl_last_error()
-    assert lib.mdl_backward(big.handle, 1, 1, 0, 4, 32, 1, 1, 1, 1, 1, None, None, None, 1, 1, 1, 1, 1,
-                            ctypes.c_size_t(wsb), None) == M.MDL_EUNSUPPORTED
+    assert lib.mdl_backward(big.handle, 1, 1, 0, 4, 32, 0, 1, 1, 1, None, None, 1, 1, None, None, None, 1, 1, 1, 1,
+                            None, None, 1, ctypes.c_size_t(wsb), None) == M.MDL_EUNSUPPORTED
     # the line workload's layer (stash above 2 GiB, each descriptor range below it) passes the size checks
     from workloads import make_workload
     wl = make_workload("line", 0)
     ll = M.mdl_pack(wl.heights, wl.widths, wl.canvas_w_min[0], wl.sep)
     wsl = M.mdl_workspace_size(ll, 4, 32)
     assert wsl > 2 ** 31
-    rc = lib.mdl_forward(ll.handle, 1, 1, 1, 4, 32, 1, 1, 1, 1, 1, 1, ctypes.c_size_t(wsl), None)
-    # with no GPU here the first device query fails (MDL_EHIP); with one the call would go on to launch
-    assert rc not in (M.MDL_EUNSUPPORTED, M.MDL_ESIZE, M.MDL_EINVAL), M.mdl_last_error()
+    import torch
+    if not torch.cuda.is_available():  # past the checks, the call would launch on a visible GPU
+        rc = lib.mdl_forward(ll.handle, 1, 1, 1, 4, 32, 0, 1, 1, 1, 1, None, None, 1, 1, ctypes.c_size_t(wsl), None)
+        # with no GPU the first device query fails (MDL_EHIP)
+        assert rc not in (M.MDL_EUNSUPPORTED, M.MDL_ESIZE, M.MDL_EINVAL), M.mdl_last_error()
 
 
 def test_workspace_grows_with_size():
@@ -237,10 +248,10 @@ def test_refuses_an_example_past_the_masked_lane_offset():
     argument checks return first, so the placeholder device addresses are never used)."""
     lay = M.mdl_pack([64], [70000], 70000, 1)
     fake = 1 << 20
-    rc = M.library().mdl_forward(lay.handle, fake, fake, M.MDL_F32, 4, 16, fake, fake, fake, fake, fake, fake,
-                                 1 << 62, None)
+    rc = M.library().mdl_forward(lay.handle, fake, fake, M.MDL_F32, 4, 16, 0, fake, fake, fake, fake, None, None,
+                                 fake, fake, 1 << 62, None)
     assert rc == M.MDL_EUNSUPPORTED
     assert "16 H" in M.mdl_last_error()
-    rc = M.library().mdl_backward(lay.handle, fake, fake, M.MDL_F32, 4, 16, fake, fake, fake, fake, fake, None, fake,
-                                  None, fake, fake, fake, fake, fake, 1 << 62, None)
+    rc = M.library().mdl_backward(lay.handle, fake, fake, M.MDL_F32, 4, 16, 0, fake, fake, fake, None, None, fake,
+                                  fake, None, fake, None, fake, fake, fake, fake, None, None, fake, 1 << 62, None)
     assert rc == M.MDL_EUNSUPPORTED
