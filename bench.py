@@ -61,6 +61,7 @@ def parse():
     ap.add_argument("--no-other", action="store_true",
                     help="skip the word-like companion runs (packed, as a padded stack, on exact-height rows)")
     ap.add_argument("--no-stack", action="store_true", help="skip the three-level stack companion run")
+    ap.add_argument("--no-leaky", action="store_true", help="skip the Leaky LP cell runs (word and line batches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the CPU oracle baseline")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB on the device (counter calibration under rocprofv3 --pmc)")
@@ -72,7 +73,7 @@ def link_count(rects):
     return sum(4 * (int(h) * (int(w) - 1) + (int(h) - 1) * int(w)) for (_, _, h, w) in rects)
 
 
-def kernel_model(info, rects, C, H, x_bytes, nchunks=None, fwd_zero=False):
+def kernel_model(info, rects, C, H, x_bytes, nchunks=None, fwd_zero=False, leaky=False):
     """Design bytes and algorithmic flops of one launch of each kernel group (one layer, one step).
 
     T = computed cells per direction, N = real pixels; every tensor of this
@@ -87,9 +88,15 @@ def kernel_model(info, rects, C, H, x_bytes, nchunks=None, fwd_zero=False):
     P = info["canvas_h"] * info["canvas_w"]
     G = 5 * H
     R = C + 1 + 2 * H
-    rec = 10 * H * H * link_count(rects)
+    # per predecessor link: 10 H^2 for the hidden state into five gates; the Leaky LP cell adds 6 H^2 for the
+    # memory state into three (its Vl, Vu products)
+    rec = (16 if leaky else 10) * H * H * link_count(rects)
     f = 4  # bytes per float
-    return {
+    extra = {}
+    if leaky:
+        # dVl, dVu: [s_l | s_u]^T da3 over the computed cells of each direction; s_l, s_u and da3 in, partials out
+        extra["wgrad_mem"] = (4 * T * (2 * H + 3 * H) * f, 4 * T * 2 * (2 * H) * (3 * H))
+    return {**extra,
         # x (canvas pixels) in for each direction; gate stash (i, f_l, f_u, o, g, c) and h out; the input
         # projection x Wx + b is computed in the same kernel
         "fwd_wavefront": (4 * T * (C * x_bytes + 7 * H * f) + (4 * (P - T) * H * f if fwd_zero else 0),
@@ -156,7 +163,7 @@ _COMMON = ("devmath.h", "kernels.h")
 KERNEL_SOURCES = {
     "projection": ("k_proj.hip",), "fwd_wavefront": ("k_fwd16.hip", "k_small.hip", "k_chain.hip") + _COMMON,
     "bwd_wavefront": ("k_bwd16.hip", "k_small.hip", "k_chain.hip") + _COMMON,
-    "wgrad": ("k_wgrad2.hip", "k_wgrad.hip") + _COMMON,
+    "wgrad": ("k_wgrad2.hip", "k_wgrad.hip") + _COMMON, "wgrad_mem": ("k_leaky.hip",) + _COMMON,
     "dirsum": ("k_layout.hip",), "scatter": ("k_layout.hip",), "zero_fill": ("k_layout.hip",),
     "conv_fwd": ("k_conv.hip",), "conv_bwd_data": ("k_conv.hip",), "conv_wgrad": ("k_conv.hip",),
 }
@@ -257,6 +264,54 @@ class Runner:
         dom = max(kern, key=kern.get)
         ms, kd = self.run(steps, dom)
         return ms, dom, kd[dom], kern
+
+
+class SkewRunner:
+    """The same layer step with the pages' schedule (mdl_forward_skewed / mdl_backward_skewed: one launch per
+    column of the input-skewed canvas), timed with events around the steps only."""
+
+    def __init__(self, wl, mode, device, stream):
+        import torch
+        import directional_mdlstm_handwriting_amd as M
+        from directional_mdlstm_handwriting_amd.layer import (DeviceLayout, DeviceParams, LayerGrads, PackedLayer,
+                                                              flat_input)
+        from workloads import cotangent
+        self.M = M
+        self.dl = DeviceLayout(wl.heights, wl.widths, wl.canvas_w_min[0], wl.sep, mode, device, stream)
+        self.layer = PackedLayer(self.dl, wl.C, wl.H, wl.x_dtype)
+        self.nb = M.mdl_skewed_workspace_size(self.dl.layout, wl.C, wl.H)
+        self.ws = torch.empty(self.nb, dtype=torch.uint8, device=device)
+        self.P = DeviceParams.from_host(wl.layers[0], device)
+        self.g = LayerGrads.like(self.P)
+        self.x = flat_input(wl.xs, wl.x_dtype, device)
+        dys = cotangent(wl.seed, wl.heights, wl.widths, wl.H)
+        self.dy = torch.as_tensor(np.concatenate([d.reshape(-1) for d in dys]), device=device)
+        self.dx = torch.empty(int(sum(x.size for x in wl.xs)), device=device)
+        self.stream = stream
+        self.C, self.H = wl.C, wl.H
+
+    def step(self):
+        L, s, P, M = self.layer, self.stream, self.P, self.M
+        L.scatter(self.x, s)
+        M.mdl_forward_skewed(L.dl.layout, L.dl.desc, L.x_canvas, L.x_dtype, self.C, self.H, P.Wx, P.Ul, P.Uu, P.b,
+                             L.h_dirs, self.ws, self.nb, s)
+        L.dirsum(s)
+        M.mdl_backward_skewed(L.dl.layout, L.dl.desc, L.x_canvas, L.x_dtype, self.C, self.H, P.Wx, P.Ul, P.Uu,
+                              L.h_dirs, self.dy, None, self.dx, None, self.g.dWx, self.g.dUl, self.g.dUu, self.g.db,
+                              self.ws, self.nb, s)
+
+    def time(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        stop.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
 
 
 class StackRunner:
@@ -407,7 +462,8 @@ def layer_report(runner, wl, ms, kern):
     info = runner.dl.info
     rects, _ = M.mdl_layout_rects(runner.dl.layout)
     xb = 2 if wl.x_dtype == "bf16" else 4
-    model = kernel_model(info, rects, wl.C, wl.H, xb, fwd_zero="zero_fill" not in kern)
+    model = kernel_model(info, rects, wl.C, wl.H, xb, fwd_zero="zero_fill" not in kern,
+                         leaky=hasattr(wl.layers[0], "Vl"))
     bmin = min_bytes(info["real_pixels"], wl.C, wl.H, xb)
     per = {k: roofline(k, v, model, bmin, wl.H) for k, v in kern.items() if k in model}
     return model, bmin, per
@@ -558,15 +614,26 @@ def main():
             ex = Runner(ww, "exact", device, stream)
             ems, _, _, ek = ex.time(max(5, args.steps // 2), 2)
             ei = ex.dl.info
+            del ex
+            torch.cuda.empty_cache()
+            print("bench: word, the skewed column schedule", file=sys.stderr, flush=True)
+            sk = SkewRunner(ww, "exact", device, stream)
+            sms = sk.time(3, 1)
+            del sk
+            torch.cuda.empty_cache()
             out["paper_literal_layout"] = {
                 "workload": "the word-like batch above",
                 "alg1_rows": skewed(wi), "exact_height_rows": skewed(ei),
                 "local_depth": wi["max_depth"], "widest_local_diagonal": wi["max_diag"],
                 "ms_per_step_alg1": wms, "ms_per_step_exact_height": ems,
+                "ms_per_step_skewed_columns_exact_height": sms,
+                "skewed_column_steps_per_pass": ei["canvas_h"] + ei["canvas_w"] - 1,
+                "skewed_note": "the pages' schedule on the exact-height canvas: one launch per skewed column, "
+                               "every skewed cell computed and masked, fp32 (mdl_forward_skewed / "
+                               "mdl_backward_skewed); the local-diagonal schedule on the same canvas is "
+                               "ms_per_step_exact_height",
                 "exact_height_kernels_ms": {k: round(v, 5) for k, v in ek.items()},
             }
-            del ex
-            torch.cuda.empty_cache()
 
     # the three-level stack of the pages' model (128 word-like images) and its head, timed the same way
     if not args.no_stack and wl.name != "tiny":
@@ -591,6 +658,31 @@ def main():
             "kernels_ms_per_step": {k: round(v, 5) for k, v in sk.items()},
         }
         del sr
+
+    # the Leaky LP cell (the pages' stable cell) on the same word and line batches, timed the same way
+    if not args.no_leaky and wl.name != "tiny":
+        out["leaky_cell"] = {}
+        for nm in ("line", "word"):
+            print(f"bench: {nm} with the Leaky LP cell", file=sys.stderr, flush=True)
+            wk_ = make_workload(nm, args.seed, cell="leaky")
+            Nk = int(np.sum(wk_.heights.astype(np.int64) * wk_.widths))
+            rk = Runner(wk_, "packed", device, stream)
+            kms, kdom, kdom_ms, kk = rk.time(max(5, args.steps // 2), 2)
+            kmodel, kbmin, kper = layer_report(rk, wk_, kms, kk)
+            kroof = roofline(kdom, kdom_ms, kmodel, kbmin, wk_.H)
+            kroof["dependent_steps"] = rk.dl.info["max_depth"]
+            kroof["us_per_dependent_step"] = round(kdom_ms * 1e3 / rk.dl.info["max_depth"], 4)
+            out["leaky_cell"][nm] = {
+                "workload": f"{nm}: {wk_.n} images, C={wk_.C}, H={wk_.H}, seed {wk_.seed}, Leaky LP cell",
+                "value": 4 * Nk / (kms * 1e-3), "unit": "cell-direction updates/s", "ms_per_step": kms,
+                "dtype": "f32 (fp32 matrix cores)" + (", bf16 input" if wk_.x_dtype == "bf16" else ""),
+                "roofline": kroof, "step_roofline": step_roofline(kmodel, kbmin, kms),
+                "kernels_ms": {k: round(v, 5) for k, v in kk.items()},
+                "kernels_roofline": {k: {kk2: r[kk2] for kk2 in ("bound", "frac", "fp32_frac", "min_bytes_hbm_frac")}
+                                     for k, r in kper.items()},
+            }
+            del rk
+            torch.cuda.empty_cache()
 
     out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

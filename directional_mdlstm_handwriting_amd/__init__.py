@@ -64,6 +64,10 @@ _SIGS = [
     ("mdl_scatter", _I32, [_P, _P, _P, _I32, _I32, _P, _P]),
     ("mdl_forward", _I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("mdl_dirsum_unpack", _I32, [_P, _P, _P, _I32, _P, _P]),
+    ("mdl_skewed_workspace_size", _I32, [_P, _I32, _I32, ctypes.POINTER(_SZ)]),
+    ("mdl_forward_skewed", _I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("mdl_backward_skewed", _I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _P, _SZ, _P]),
     ("mdl_backward", _I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                             _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("mdl_blockconv_forward", _I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _I32, _P, _P]),
@@ -239,6 +243,26 @@ def mdl_forward(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, 
     _check(_lib.mdl_forward(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, cell, _ptr(Wx), _ptr(Ul),
                             _ptr(Uu), _ptr(b), _ptr(Vl), _ptr(Vu), _ptr(h_dirs), _ptr(ws), ws_bytes,
                             _stream(stream)))
+
+
+def mdl_skewed_workspace_size(layout: Layout, C: int, H: int) -> int:
+    b = _SZ()
+    _check(_lib.mdl_skewed_workspace_size(layout.handle, C, H, ctypes.byref(b)))
+    return int(b.value)
+
+
+def mdl_forward_skewed(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, Wx, Ul, Uu, b, h_dirs, ws,
+                       ws_bytes: int, stream=None):
+    _check(_lib.mdl_forward_skewed(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, _ptr(Wx), _ptr(Ul),
+                                   _ptr(Uu), _ptr(b), _ptr(h_dirs), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def mdl_backward_skewed(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, Wx, Ul, Uu, h_dirs, dy_flat,
+                        dh_dirs, dx_flat, dx_canvas, dWx, dUl, dUu, db, ws, ws_bytes: int, stream=None):
+    _check(_lib.mdl_backward_skewed(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, _ptr(Wx), _ptr(Ul),
+                                    _ptr(Uu), _ptr(h_dirs), _ptr(dy_flat), _ptr(dh_dirs), _ptr(dx_flat),
+                                    _ptr(dx_canvas), _ptr(dWx), _ptr(dUl), _ptr(dUu), _ptr(db), _ptr(ws), ws_bytes,
+                                    _stream(stream)))
 
 
 def mdl_dirsum_unpack(layout: Layout, d_desc, h_dirs, H: int, y_flat, stream=None):

@@ -407,6 +407,109 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     GUARD_END
 }
 
+static size_t skew_dcb_offset(const mdl::WsLayout& W) { return (W.total + 255) & ~size_t(255); }
+
+int mdl_skewed_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes) {
+    if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_skewed_workspace_size: null argument");
+    if (C < 1 || H < 1) return fail(MDL_EINVAL, "mdl_skewed_workspace_size: need C >= 1 and H >= 1");
+    const mdl::Layout& L = L_of(layout);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
+    *bytes = skew_dcb_offset(W) + sizeof(float) * 4 * (size_t)L.computed_cells * 2 * H;
+    return MDL_OK;
+}
+
+int mdl_forward_skewed(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
+                       int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu, const float* b,
+                       float* h_dirs, void* ws, size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    int rc = check_layer("mdl_forward_skewed", layout, d_desc, C, H, x_dtype);
+    if (rc) return rc;
+    if (!x_canvas || !Wx || !Ul || !Uu || !b || !h_dirs || !ws)
+        return fail(MDL_EINVAL, "mdl_forward_skewed: null tensor");
+    if (!mdl::skew_supported(H)) return fail(MDL_EUNSUPPORTED, "mdl_forward_skewed: runs for H in {4, 16}");
+    const mdl::Layout& L = L_of(layout);
+    size_t need = 0;
+    mdl_skewed_workspace_size(layout, C, H, &need);
+    if (ws_bytes < need) return fail(MDL_ESIZE, "mdl_forward_skewed: workspace smaller than mdl_skewed_workspace_size");
+    if ((rc = check_extent("mdl_forward_skewed", L, C, H, x_dtype, true))) return rc;
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
+    const mdl::Dev D = make_dev(layout, d_desc);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    float* Z = reinterpret_cast<float*>(wsb + W.zda);
+    float* stash = reinterpret_cast<float*>(wsb + W.stash);
+    hipError_t e;
+    {
+        Timed t("zero_fill");
+        e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_forward_skewed: zero fill");
+    {
+        Timed t("projection");
+        e = mdl::launch_projection(D, x_canvas, x_dtype, C, H, Wx, b, Z, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_forward_skewed: projection");
+    {
+        Timed t("fwd_skewed_columns");
+        e = mdl::launch_skew_fwd(D, H, Ul, Uu, Z, stash, h_dirs, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_forward_skewed: column steps");
+    return MDL_OK;
+    GUARD_END
+}
+
+int mdl_backward_skewed(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
+                        int32_t C, int32_t H, const float* Wx, const float* Ul, const float* Uu, const float* h_dirs,
+                        const float* dy_flat, const float* dh_dirs, float* dx_flat, float* dx_canvas, float* dWx,
+                        float* dUl, float* dUu, float* db, void* ws, size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    int rc = check_layer("mdl_backward_skewed", layout, d_desc, C, H, x_dtype);
+    if (rc) return rc;
+    if (!x_canvas || !Wx || !Ul || !Uu || !h_dirs || !ws || !dWx || !dUl || !dUu || !db)
+        return fail(MDL_EINVAL, "mdl_backward_skewed: null tensor");
+    if ((dy_flat == nullptr) == (dh_dirs == nullptr))
+        return fail(MDL_EINVAL, "mdl_backward_skewed: pass exactly one of dy_flat and dh_dirs");
+    if (!mdl::skew_supported(H)) return fail(MDL_EUNSUPPORTED, "mdl_backward_skewed: runs for H in {4, 16}");
+    const mdl::Layout& L = L_of(layout);
+    size_t need = 0;
+    mdl_skewed_workspace_size(layout, C, H, &need);
+    if (ws_bytes < need)
+        return fail(MDL_ESIZE, "mdl_backward_skewed: workspace smaller than mdl_skewed_workspace_size");
+    if ((rc = check_extent("mdl_backward_skewed", L, C, H, x_dtype, true))) return rc;
+    const bool wg2 = mdl::wgrad2_supported(C, H, x_dtype);
+    size_t lmax = 0;
+    if ((rc = max_lds(lmax))) return rc;
+    if ((wg2 ? mdl::wgrad2_lds_bytes(C, H, x_dtype) : mdl::wgrad_lds_bytes(C, H)) > lmax)
+        return fail(MDL_EUNSUPPORTED, "mdl_backward_skewed: weight-gradient tile exceeds LDS");
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
+    const mdl::Dev D = make_dev(layout, d_desc);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    float* dA = reinterpret_cast<float*>(wsb + W.zda);
+    const float* stash = reinterpret_cast<const float*>(wsb + W.stash);
+    float* part = reinterpret_cast<float*>(wsb + W.part);
+    float* dcb = reinterpret_cast<float*>(wsb + skew_dcb_offset(W));
+    hipError_t e;
+    {
+        Timed t("bwd_skewed_columns");
+        e = mdl::launch_skew_bwd(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, dcb, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_backward_skewed: column steps");
+    if (dx_canvas) {
+        Timed t("zero_fill");
+        e = mdl::launch_zero_outside(D, dx_canvas, C, 1, st);
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward_skewed: zero fill");
+    }
+    {
+        Timed t("wgrad");
+        e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dWx, dUl, dUu, db, dx_flat, dx_canvas,
+                              st);
+    }
+    if (e != hipSuccess) return hip_fail(e, "mdl_backward_skewed: weight and input gradients");
+    return MDL_OK;
+    GUARD_END
+}
+
 int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float* h_dirs, int32_t H, float* y_flat,
                       void* stream) {
     GUARD_BEGIN

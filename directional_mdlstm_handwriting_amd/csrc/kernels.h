@@ -187,6 +187,13 @@ hipError_t launch_bwd_leaky(const Dev& D, int H, const float* Ul, const float* U
                             hipStream_t st);
 hipError_t launch_dv_leaky(const Dev& D, int H, const float* stash, const float* dA, float* part, float* dVl,
                            float* dVu, hipStream_t st);
+// the pages' schedule (k_skew.hip): one launch per column of the input-skewed canvas, Hc + Wc - 1 per pass
+bool skew_supported(int H);
+int skew_columns(const Dev& D);
+hipError_t launch_skew_fwd(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z, float* stash,
+                           float* h_dirs, hipStream_t st);
+hipError_t launch_skew_bwd(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
+                           const float* dy_flat, const float* dh_dirs, float* dA, float* dcb, hipStream_t st);
 // this device's fixed weight-gradient scratch of the block conv (address and size), for callers that cannot
 // allocate; every call on one device shares it
 hipError_t conv_scratch(void** ptr, size_t* bytes);

@@ -232,6 +232,36 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
                 size_t ws_bytes, void* stream);
 
 /*
+ * The pages' own schedule of the recurrence, for comparison with the local
+ * diagonals of mdl_forward / mdl_backward ("No Padding Please" §IV-A, Figure 3:
+ * the whole packed canvas skewed, row i shifted right by i, and computed one
+ * skewed column after another; RETURNN §4.2: one kernel launch per diagonal).
+ * A pass takes Hc + Wc - 1 dependent column steps, one launch each (all four
+ * directions in it), and every cell of the skewed grid is computed, padding
+ * and separators included, with only the example cells kept (§V mask). The
+ * results are the same cells as mdl_forward / mdl_backward's with
+ * MDL_CELL_MDLSTM (fp32 arithmetic, not the same rounding), in the same
+ * layouts: h_dirs, and the workspace's stash and gate gradients, so the
+ * weight gradients come from the same kernels. Arguments as mdl_forward /
+ * mdl_backward with the plain cell; the workspace is at least
+ * mdl_skewed_workspace_size bytes (mdl_workspace_size plus the dc f_l, dc f_u
+ * products every cell sends to its predecessors, 8H bytes per cell and
+ * direction), carried from mdl_forward_skewed to mdl_backward_skewed.
+ * MDL_EUNSUPPORTED for H outside {4, 16}; other errors as mdl_forward /
+ * mdl_backward.
+ */
+int mdl_skewed_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes);
+int mdl_forward_skewed(const mdl_layout* layout, const void* d_desc, const void* x_canvas,
+                       int32_t x_dtype, int32_t C, int32_t H, const float* Wx, const float* Ul,
+                       const float* Uu, const float* b, float* h_dirs, void* ws, size_t ws_bytes,
+                       void* stream);
+int mdl_backward_skewed(const mdl_layout* layout, const void* d_desc, const void* x_canvas,
+                        int32_t x_dtype, int32_t C, int32_t H, const float* Wx, const float* Ul,
+                        const float* Uu, const float* h_dirs, const float* dy_flat,
+                        const float* dh_dirs, float* dx_flat, float* dx_canvas, float* dWx,
+                        float* dUl, float* dUu, float* db, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Direction sum and un-packing (§III four directions combined; §V-A
  * un-packing by original index and size, separators dropped):
  * y_flat[e][r][c][k] = sum_{d=0..3} h_dirs[d][y0+r][x0+c][k] over each real pixel,

@@ -470,3 +470,37 @@ def test_schedule_permutation_bit_identical(case):
     got = _fwd_bwd(dl, P, xs, dys)
     for name, a, b in zip(("h_dirs", "y", "dx", "dWx", "dUl", "dUu", "db"), got, ref):
         assert torch.equal(a, b), name
+
+
+@pytest.mark.parametrize("mode", ["exact", "packed"])
+def test_skewed_schedule_subset(mode):
+    """The pages' schedule (mdl_forward_skewed / mdl_backward_skewed: one launch per column of the input-skewed
+    canvas, every skewed cell computed and masked) on word-like images at H = 16 and the tiny workload at H = 4:
+    the same cells as the oracle's, under the same criterion."""
+    wl = make_workload("word", 3)
+    idx = [1, 4, 8, 15, 22, 31, 47]
+    cases = [(wl.heights[idx], wl.widths[idx], [wl.xs[i] for i in idx], wl.layers[0], 256)]
+    tw = make_workload("tiny", 1)
+    cases.append((tw.heights, tw.widths, tw.xs, tw.layers[0], 8))
+    for h, w, xs, P, cw in cases:
+        print(f"[gpu] skewed schedule n={len(h)} H={P.H} mode={mode}", flush=True)
+        dl = DeviceLayout(h, w, cw, 1, mode, DEV)
+        lay = PackedLayer(dl, P.C, P.H)
+        nb = M.mdl_skewed_workspace_size(dl.layout, P.C, P.H)
+        ws = torch.full((nb // 4,), float("nan"), device=DEV)
+        lay.h_dirs.fill_(float("nan"))
+        lay.y.fill_(float("nan"))
+        Pd = DeviceParams.from_host(P, DEV)
+        lay.scatter(flat_input(xs, "f32", DEV))
+        M.mdl_forward_skewed(dl.layout, dl.desc, lay.x_canvas, M.MDL_F32, P.C, P.H, Pd.Wx, Pd.Ul, Pd.Uu, Pd.b,
+                             lay.h_dirs, ws, nb)
+        lay.dirsum()
+        dys = cotangent(17, h, w, P.H)
+        dy = torch.as_tensor(np.concatenate([d.reshape(-1) for d in dys]).astype(np.float32), device=DEV)
+        g = LayerGrads(*(torch.full_like(t, float("nan")) for t in (Pd.Wx, Pd.Ul, Pd.Uu, Pd.b)))
+        dx = torch.full((int(sum(np.asarray(x).size for x in xs)),), float("nan"), device=DEV)
+        M.mdl_backward_skewed(dl.layout, dl.desc, lay.x_canvas, M.MDL_F32, P.C, P.H, Pd.Wx, Pd.Ul, Pd.Uu, lay.h_dirs,
+                              dy, None, dx, None, g.dWx, g.dUl, g.dUu, g.db, ws, nb)
+        torch.cuda.synchronize()
+        o = oracle_layer(h, w, xs, P, mode=mode, canvas_w_min=cw, dys=dys)
+        check_layer({"layer": lay, "g": g, "dx": dx}, o)
