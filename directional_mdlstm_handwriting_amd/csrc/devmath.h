@@ -10,6 +10,7 @@ namespace mdl {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -57,6 +58,16 @@ __device__ inline float ftanh(float x) {
     p = __builtin_fmaf(x2, p, kTc0);
     const float small = __builtin_fmaf(x * x2, p, x);
     return ax < 0.55f ? small : __builtin_copysignf(big, x);
+}
+
+// The factors the reverse wavefront multiplies a cell's gradients by, formed by the forward from its own
+// values (gates i, f_l, f_u, o, cell input g, tc = tanh c) and its predecessors' memory states c_l, c_u:
+//   A = (g i(1-i), c_l f_l(1-f_l), c_u f_u(1-f_u), tc o(1-o)),  B = (i(1-g^2), o(1-tc^2), f_l, f_u)
+// so that dc = dh B[1] + dc_in and da = (dc A[0], dc A[1], dc A[2], dh A[3], dc B[0]).
+__device__ inline void bwd_factors(float ig, float fl, float fu, float og, float gg, float cl, float cu, float tc,
+                                   f32x4& A, f32x4& B) {
+    A = f32x4{gg * (ig * (1.f - ig)), cl * (fl * (1.f - fl)), cu * (fu * (1.f - fu)), tc * (og * (1.f - og))};
+    B = f32x4{ig * (1.f - gg * gg), og * (1.f - tc * tc), fl, fu};
 }
 
 // fp32 value -> f16 pair (hi, lo) with hi + lo equal to v to about 2^-22 relative,

@@ -10,30 +10,26 @@
 //     tc = tanh c;  dc = dc_in + dh o (1 - tc^2)
 //     da = [dc g i(1-i), dc c_l f_l(1-f_l), dc c_u f_u(1-f_u), dh tc o(1-o), dc i (1-g^2)]
 //
-// Each diagonal is done in two phases separated by a barrier.
-//  1. Four matrix waves (one per SIMD) take the gate gradients da of the later diagonal s + 1, already in
-//     LDS, and form for each of its cells m the products X(m) = da(m) Ul^T and Y(m) = da(m) Uu^T on
-//     v_mfma_f32_16x16x32_f16: the parts of dh that m sends to its left and upper predecessors. Then
-//     dh(a, b) = dy(a, b) + X(R) + Y(D), and each row of da is read once. Both operands are split
-//     into f16 hi + lo pairs (three partial products summed in fp32). Gate gradients have no bound, so
-//     each (cell, 16-wide block of hidden units) row of da was scaled by the power of two that brings its
-//     largest magnitude into [2^14, 2^15) before it was split; its exponent sits in LDS beside it and the
-//     product is scaled back exactly. The K dimension orders da by (hidden unit, gate), the five gates
-//     padded to eight.
-//  2. All waves do the elementwise part, each thread owning fixed
-//     (diagonal position, hidden unit) elements: dc, da, the scale of its
-//     row (a maximum over the 16 lanes of a DPP row), the split into the LDS
-//     A rows of the next phase 1, and the store of da for the weight
-//     gradients. A single wave issues a VALU instruction only every few
-//     cycles, so the workgroup is sized to give each thread of the widest
-//     diagonal one element (two where the registers do not allow it).
-// Rows of the LDS A operand are permuted so the 16 lanes gathering one K
-// block read 16 consecutive rows on distinct banks. The forward's gate stash
-// and the upstream gradient of each element are prefetched three diagonals
-// ahead; the memory states c of the predecessor diagonal come from its own
-// prefetch through LDS. The loop is unrolled by four so every step is
-// straight code and the compiler's vmcnt waits cover only the prefetch they
-// need (loads and stores retire in order on this hardware).
+// The workgroup of one (example, direction) unit has two roles, each in a loop of its own (so each has the
+// whole register file of its waves to itself); every step of diagonal s ends in two barriers.
+//  Matrix waves (the first four, one per SIMD) hold the recurrent weights, split, in registers. Before the
+//     first barrier they read the gate gradients da of the later diagonal s + 1 from LDS (all of the step's
+//     A operand at once) and form for each of its cells m the products X(m) = da(m) Ul^T and
+//     Y(m) = da(m) Uu^T on v_mfma_f32_16x16x32_f16: the parts of dh that m sends to its left and upper
+//     predecessors. Both operands are split into f16 hi + lo pairs (three partial products summed in
+//     fp32). Gate gradients have no bound, so each cell's row of da was scaled by the power of two that
+//     brings its largest magnitude into [2^14, 2^15) before it was split; its exponent sits in LDS beside
+//     it and the product is scaled back exactly. The K dimension orders da by (gate, hidden unit), the
+//     order of the columns of Ul and Uu, 5H entries padded to a multiple of 32.
+//  Element waves (the others) own fixed (diagonal position, hidden unit) elements. Every factor of dc and
+//     da that depends on the forward alone (o (1 - tc^2) and the five gate-derivative products) comes
+//     from the forward's stash; before the first barrier, while the products run, the element waves take
+//     it from the prefetch registers and work out the step's addresses. After it, dh = dy + X(R) + Y(D)
+//     and dc_in leave a few products, the cell's scale (a maximum over the lanes of its DPP rows), the split
+//     into the LDS A rows of the next step, dc f_l and dc f_u for the earlier diagonal, and the store of da
+//     for the weight gradients. Their stash and upstream-gradient reads are issued KPD diagonals ahead.
+// Rows of the LDS A operand are permuted so the 16 lanes gathering one K block read 16 consecutive rows
+// on distinct banks.
 #include "kernels.h"
 #include "devmath.h"
 
@@ -44,26 +40,29 @@ namespace mdl {
 namespace {
 
 constexpr int kOOB = 0x40000000;  // byte offset past every per-unit range used here (1 GiB)
-constexpr int kPD = 3;            // diagonals of prefetch ahead
-constexpr int kMatWaves = 4;      // phase 1 on the first four
+constexpr int kMatWaves = 4;      // the matrix role, one wave per SIMD
 
 template <int H>
 struct B16Shape {
-    static constexpr int NB = (H + 15) / 16;  // blocks of 16 hidden units
-    static constexpr int HE = 16 * NB;        // hidden units padded to whole DPP rows
-    static constexpr int CG = kMatWaves / NB; // cell groups of the matrix waves
-    static constexpr int KA = 128;            // K extent of one successor's da per block: 16 units x 8 slots
-    static constexpr int KT = KA / 32;        // K blocks of 32 per (successor, block)
+    static constexpr int NB = (H + 15) / 16;        // blocks of 16 hidden units
+    static constexpr int HE = 16 * NB;              // hidden units padded to whole DPP rows
+    static constexpr int CG = kMatWaves / NB;       // cell groups of the matrix waves
+    static constexpr int KP = (5 * H + 31) / 32 * 32;  // K extent of one cell's da: 5H, padded
+    static constexpr int KT = KP / 32;              // K blocks of 32
     static_assert(NB <= 2, "hidden size above 32");
 };
 
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-// exact power-of-two scale 2^E that brings m (> 0) into [2^14, 2^15); 0 for m = 0
+// LDS byte pointer (32-bit address); values of this type held across a barrier keep their fixed offsets
+// foldable into the LDS instructions
+typedef __attribute__((address_space(3))) unsigned char* lds_p;
+
+// exact power-of-two scale 2^E that brings m (> 0) into [2^14, 2^15), clamped to [-100, 100] (for m = 0
+// it is 100: a row of zeros stays zero under any scale)
 __device__ inline int scale_exp(uint32_t mbits) {
-    if (mbits == 0) return 0;
-    int E = 14 - ((int)((mbits >> 23) & 255) - 127);
+    const int E = 141 - (int)((mbits >> 23) & 255);
     return E < -100 ? -100 : (E > 100 ? 100 : E);
 }
 
@@ -76,106 +75,61 @@ __device__ inline uint32_t row16_max(uint32_t x) {
     x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, true));  // row_ror:8
     return x;
 }
+// ... over the 8 lanes of each half-row
+__device__ inline uint32_t row8_max(uint32_t x) {
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, true));  // row_half_mirror
+    return x;
+}
 
 // f16 pair of a scaled value v (|v| < 2^15): hi is v with its low 13 mantissa bits cleared, which f16
 // holds exactly (11 significant bits; below the f16 normal range the rounding is under 2^-25), and
 // lo = v - hi rounded to f16, so hi + lo is v to about 2^-21 of |v|
 __device__ inline float hi_part(float v) { return __uint_as_float(__float_as_uint(v) & 0xFFFFE000u); }
 
-// NE: elements per thread in phase 2, NT threads: NE NT covers the cells x padded units of the widest diagonal
-template <int H, int NE, int NT>
-__global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ Ul, const float* __restrict__ Uu,
-                                                    const float* __restrict__ stash,
-                                                    const float* __restrict__ dy_flat,
-                                                    const float* __restrict__ dh_dirs, float* __restrict__ dA) {
+// NE unit pairs per element-wave thread, EW element waves (NE 64 EW covers the cells x padded unit pairs of
+// the widest diagonal), KPD diagonals of prefetch ahead
+template <int H, int NE, int EW, int KPD>
+__global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const float* __restrict__ Ul,
+                                                                 const float* __restrict__ Uu,
+                                                                 const float* __restrict__ stash,
+                                                                 const float* __restrict__ dy_flat,
+                                                                 const float* __restrict__ dh_dirs,
+                                                                 float* __restrict__ dA) {
     using Sh = B16Shape<H>;
-    constexpr int NB = Sh::NB, HE = Sh::HE, CG = Sh::CG, KA = Sh::KA, KT = Sh::KT;
+    constexpr int NB = Sh::NB, HE = Sh::HE, CG = Sh::CG, KP = Sh::KP, KT = Sh::KT, HP2 = HE / 2;
     constexpr int G = 5 * H;
+    constexpr int NT = 64 * (kMatWaves + EW), ET = 64 * EW, NS = KPD + 1;
     const int u = D.units[blockIdx.x];
     const int e = u >> 2, d = u & 3;
     const int y0 = D.rect[4 * e], x0 = D.rect[4 * e + 1], h = D.rect[4 * e + 2], w = D.rect[4 * e + 3];
-    const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const bool mat = wave < kMatWaves;
-    // phase 1 role of a matrix wave: output block kb, cell group cg; lane (q, col)
-    const int kb = (wave % kMatWaves) / CG, cg = (wave % kMatWaves) % CG;
-    const int q = lane >> 4, col = lane & 15;
 
-    // Phase 1 forms, for every cell m of the later diagonal s + 1, X(m) = da(m) Ul^T and Y(m) = da(m) Uu^T:
-    // the parts of dh that cell m sends to its left and upper predecessors. A wave computes two output
-    // column blocks ("pairs") for its 16 cells: with one block of hidden units, X and Y of that block;
-    // with two, blocks 0 and 1 of X (kb = 0) or of Y (kb = 1).
-    // B operand of pair p: U^T rows in the (unit, gate) K order; for input block bi and K block t the lane
-    // holds K rows 32t + 8q + i = 8 (4t + q) + i: unit k' = 16 bi + 4t + q, gate i (zero for i >= 5).
-    // Scaled per output column by 2^E and split into f16 hi + lo.
-    auto pair_y = [&](int p) { return NB == 1 ? p : kb; };               // pair computes Y (uses Uu)
-    auto pair_col = [&](int p) { return 16 * (NB == 1 ? 0 : p) + col; };  // output hidden unit
-    f16x8 Bh[2][NB][KT], Bl[2][NB][KT];
-    int ec[2];  // the columns' scale exponents, negated
-#pragma unroll
-    for (int pp = 0; pp < 2; ++pp) {
-        float v[NB][KT][8];
-        float m = 0.f;
-        const float* U = pair_y(pp) ? Uu : Ul;
-        const int kc = pair_col(pp);
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-            for (int t = 0; t < KT; ++t)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int kp = 16 * bi + 4 * t + q;
-                    float x = 0.f;
-                    if (mat && kc < H && kp < H && i < 5) x = U[((int64_t)d * H + kc) * G + i * H + kp];
-                    v[bi][t][i] = x;
-                    m = fmaxf(m, fabsf(x));
-                }
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        const int E = scale_exp(__float_as_uint(m));
-        ec[pp] = -E;
-#pragma unroll
-        for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-            for (int t = 0; t < KT; ++t)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    _Float16 hi, lo;
-                    split16(ldexpf(v[bi][t][i], E), hi, lo);
-                    Bh[pp][bi][t][i] = hi;
-                    Bl[pp][bi][t][i] = lo;
-                }
-    }
-
-    // LDS, two buffers (later / current diagonal) of NRW rows: the split, scaled da as f16
-    // [hi | lo][block][unit][8] (row stride RA halves), the scale exponents [block] (ints), dc*f_l and
-    // dc*f_u (row stride CS floats); one buffer each of the phase-1 results X and Y of the later diagonal
-    // and of the memory states c of the predecessor diagonal (row stride CS). Diagonal position j lives
-    // in row P(j) (below); ZR is a zero row, XR absorbs the writes of idle threads.
-    constexpr int RA = 2 * NB * KA + 8, CS = HE + 4;
+    // LDS, two buffers (written on diagonals of even / odd distance from the last) of NRW rows: the scale
+    // exponent (ints, one copy per lane of the cell so that no two lanes write one word), dc*f_l and dc*f_u (row
+    // stride CS floats) and the split, scaled da as f16 [hi | lo][gate][unit] (each piece KP halves, row
+    // stride RA); one buffer each of the products X and Y of the later diagonal (row stride CS). The small
+    // buffers come first, where the 16-bit offsets of the LDS instructions reach them. Diagonal position j
+    // lives in row P(j) (below); ZR is a zero row, XR absorbs the writes of padding units. Each cell group's
+    // block of 16 rows is shifted by a further SK (A, exponents) or SKC (the float rows) bytes per group, so
+    // that the cells of different groups that one wave writes together fall on different banks.
+    constexpr int RA = 2 * KP + 8, CS = HE + 4;
     constexpr int NRW = 16 * CG + 2, ZR = 16 * CG, XR = 16 * CG + 1;
-    constexpr int ABUF = NRW * RA * 2, EBUF = NRW * NB * 4, CBUF = NRW * CS * 4;
-    constexpr int OFF_E = 2 * ABUF, OFF_CL = OFF_E + 2 * EBUF, OFF_CU = OFF_CL + 2 * CBUF;
-    constexpr int OFF_X = OFF_CU + 2 * CBUF, OFF_Y = OFF_X + CBUF;
-    constexpr int OFF_CP = OFF_Y + CBUF;
-    constexpr int LDS_BYTES = OFF_CP + CBUF;
+    constexpr int SK = 128 / CG, SKC = NB == 1 ? 64 : 0, NBLK = NRW / 16 + 1;
+    constexpr int ABUF = NRW * RA * 2 + NBLK * SK, EBUF = NRW * HP2 * 4 + NBLK * SK, CBUF = NRW * CS * 4 + NBLK * SKC;
+    auto rowA = [](int r) { return r * RA * 2 + (r >> 4) * SK; };    // byte offsets of row r in a buffer
+    auto rowE = [](int r) { return r * HP2 * 4 + (r >> 4) * SK; };
+    auto rowC = [](int r) { return r * CS * 4 + (r >> 4) * SKC; };
+    constexpr int OFF_E = 0, OFF_CL = OFF_E + 2 * EBUF, OFF_CU = OFF_CL + 2 * CBUF;
+    constexpr int OFF_X = OFF_CU + 2 * CBUF, OFF_Y = OFF_X + CBUF, OFF_A = (OFF_Y + CBUF + 15) / 16 * 16;
+    constexpr int LDS_BYTES = OFF_A + 2 * ABUF;
     extern __shared__ __align__(16) unsigned char smem[];
     {
         uint32_t* z32 = reinterpret_cast<uint32_t*>(smem);
         for (int i = tid; i < LDS_BYTES / 4; i += NT) z32[i] = 0u;
     }
-    const int64_t base = (int64_t)d * D.T + D.cell_off[e];
-    const int64_t cells = (int64_t)h * w;
-    const int64_t o1 = z1_offset(D.T, H);
-    const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 16 * H);
-    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 2 * H, cells * 8 * H);
-    const __amdgpu_buffer_rsrc_t rA4 = rsrc(dA + base * 4 * H, cells * 16 * H);
-    const __amdgpu_buffer_rsrc_t rA1 = rsrc(dA + o1 + base * H, cells * 4 * H);
-    const bool per_dir = dh_dirs != nullptr;
-    const __amdgpu_buffer_rsrc_t rU =
-        per_dir ? rsrc(dh_dirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4)
-                : rsrc(dy_flat + D.flat_off[e] * H, (int64_t)rh * rw * H * 4);
     const int S = h + w - 1;
 
     // Cell j of a diagonal belongs to cell group j % CG and is cell i = j / CG of that group's matrix wave,
@@ -186,15 +140,124 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
         const int i = j / CG;
         return 16 * (j % CG) + 4 * (i & 3) + (i >> 2);
     };
+    auto diag_len = [&](int s) {
+        if (s < 0 || s >= S) return 0;
+        const int lo = s > w - 1 ? s - (w - 1) : 0;
+        const int hi = s < h - 1 ? s : h - 1;
+        return hi - lo + 1;
+    };
+    auto diag_lo = [&](int s) { return s > w - 1 ? s - (w - 1) : 0; };
+    __syncthreads();
 
-    // ---- phase 1 constants (matrix waves) ----
-    // The lane's A row is its own cell ja = (4 (col & 3) + (col >> 2)) CG + cg of the later diagonal; its
-    // output rows r are the cells (4r + q) CG + cg, at LDS rows 16 cg + 4q + r, whose scale exponents the
-    // product carries.
-    const int oa1 = P((4 * (col & 3) + (col >> 2)) * CG + cg) * RA * 2;
-    const int orow = 16 * cg + 4 * q;  // LDS row of output row r: orow + r
+    if (wave < kMatWaves) {
+        // ================= matrix role =================
+        // output block kb, cell group cg; lane (q, col)
+        const int kb = wave / CG, cg = wave % CG;
+        const int q = lane >> 4, col = lane & 15;
+        // A wave computes two output column blocks ("pairs") for its 16 cells: with one block of hidden
+        // units, X and Y of that block; with two, blocks 0 and 1 of X (kb = 0) or of Y (kb = 1).
+        // B operand of pair p: U^T rows in the (gate, unit) K order, which is the order of U's columns: for
+        // K block t the lane holds K rows 32t + 8q + i, i < 8 (zero from 5H on). Scaled per output column
+        // by 2^E and split into f16 hi + lo.
+        auto pair_y = [&](int p) { return NB == 1 ? p : kb; };               // pair computes Y (uses Uu)
+        auto pair_col = [&](int p) { return 16 * (NB == 1 ? 0 : p) + col; };  // output hidden unit
+        f16x8 Bh[2][KT], Bl[2][KT];
+        int ec[2];  // the columns' scale exponents, negated
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+            float v[KT][8];
+            float m = 0.f;
+            const float* U = pair_y(pp) ? Uu : Ul;
+            const int kc = pair_col(pp);
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int kk = 32 * t + 8 * q + i;
+                    float x = 0.f;
+                    if (kc < H && kk < G) x = U[((int64_t)d * H + kc) * G + kk];
+                    v[t][i] = x;
+                    m = fmaxf(m, fabsf(x));
+                }
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            const int E = scale_exp(__float_as_uint(m));
+            ec[pp] = -E;
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    _Float16 hi, lo;
+                    split16(ldexpf(v[t][i], E), hi, lo);
+                    Bh[pp][t][i] = hi;
+                    Bl[pp][t][i] = lo;
+                }
+        }
+        // The lane's A row is its own cell ja = (4 (col & 3) + (col >> 2)) CG + cg of the later diagonal; its
+        // output rows r are the cells (4r + q) CG + cg, at LDS rows 16 cg + 4q + r, whose scale exponents the
+        // product carries.
+        const int oa1 = rowA(P((4 * (col & 3) + (col >> 2)) * CG + cg));
+        const int orow = 16 * cg + 4 * q;
+        for (int s = S - 1; s >= 0; --s) {
+            const int CB = (S - 1 - s) & 1;  // buffer this step's gate gradients go to; 1 - CB holds s + 1's
+            const unsigned char* ap = smem + OFF_A + (1 - CB) * ABUF + oa1;
+            const unsigned char* ep = smem + OFF_E + (1 - CB) * EBUF;
+            f16x8 ah[KT], al[KT];
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                const unsigned char* p = ap + (32 * t + 8 * q) * 2;
+                ah[t] = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p, 16));
+                al[t] = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p + KP * 2, 16));
+            }
+            int er[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) er[r] = *reinterpret_cast<const int*>(ep + rowE(orow + r));
+            f32x4 acc[2];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) acc[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    acc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[t], Bh[pp][t], acc[pp], 0, 0, 0);
+                    acc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[t], Bl[pp][t], acc[pp], 0, 0, 0);
+                    acc[pp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[t], Bh[pp][t], acc[pp], 0, 0, 0);
+                }
+            // every LDS read of the step ahead of the products: the reads then overlap one another, and the
+            // products wait only for the operands they take
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KT + 4, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 6 * KT, 0);      // the products
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    *reinterpret_cast<float*>(smem + (pair_y(pp) ? OFF_Y : OFF_X) + rowC(orow + r) + pair_col(pp) * 4) =
+                        ldexpf(acc[pp][r], ec[pp] - er[r]);
+            __syncthreads();  // X and Y of diagonal s + 1 are in LDS
+            __syncthreads();  // the element waves have written diagonal s's gate gradients
+        }
+        return;
+    }
 
-    // ---- phase 2 constants: element n of this thread is (position pj, unit pk) ----
+    // ================= element role =================
+    // Each thread owns NE pairs of adjacent hidden units (2m, 2m + 1) of one diagonal position: the HE / 2
+    // lanes of a cell sit in one DPP row (H = 32) or half-row (H = 16), and each gate's f16 pair goes to
+    // LDS as one 4-byte word.
+    const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
+    const int et = tid - 64 * kMatWaves;
+    const int64_t base = (int64_t)d * D.T + D.cell_off[e];
+    const int64_t cells = (int64_t)h * w;
+    const int64_t o1 = z1_offset(D.T, H);
+    const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 16 * H);
+    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 4 * H, cells * 16 * H);
+    const __amdgpu_buffer_rsrc_t rA4 = rsrc(dA + base * 4 * H, cells * 16 * H);
+    const __amdgpu_buffer_rsrc_t rA1 = rsrc(dA + o1 + base * H, cells * 4 * H);
+    const bool per_dir = dh_dirs != nullptr;
+    const __amdgpu_buffer_rsrc_t rU =
+        per_dir ? rsrc(dh_dirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4)
+                : rsrc(dy_flat + D.flat_off[e] * H, (int64_t)rh * rw * H * 4);
+
+    // pair n of this thread is (position pj, units 2 pm, 2 pm + 1).
     // Cell (a, b) sits at canvas (Y0 + SY a, X0 + SX b). The upstream gradient's byte offset is
     // UB + a UA + s US + 4 k (b = s - a): on the canvas plane for a per-direction gradient, else in
     // the example's flat real-pixel block, where the cell must also lie in the real region.
@@ -211,41 +274,32 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
     int pj[NE], vu[NE], ve[NE];
     bool pk_ok[NE];
     int wa[NE], we[NE], wc[NE];  // own LDS offsets (within a buffer)
-    int oc[NE][3];                         // c-row offsets at positions pj - 1, pj, pj + 1
+    int oc[NE][3];               // LDS row offsets (stride CS) of positions pj - 1, pj, pj + 1
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
-        const int el = tid + NT * n;
-        pj[n] = el / HE;
-        const int pk = el - pj[n] * HE, pb = pk / 16, pc = pk - 16 * pb;
-        pk_ok[n] = pk < H;
-        const int pkc = pk < H ? pk : 0;
-        vu[n] = pj[n] * UA + 4 * pkc;
-        ve[n] = pj[n] * H + pkc;
+        const int el = et + ET * n;
+        pj[n] = el / HP2;
+        const int pm = el - pj[n] * HP2, k0 = 2 * pm;
+        pk_ok[n] = k0 < H;
+        const int kc = k0 < H ? k0 : 0;
+        vu[n] = pj[n] * UA + 4 * kc;
+        ve[n] = pj[n] * H + kc;
         const int pr = P(pj[n]);
-        wa[n] = pr * RA * 2 + (pb * KA + 8 * pc) * 2;
-        we[n] = (pr * NB + pb) * 4;
-        wc[n] = pr * CS * 4 + 4 * pk;
+        wa[n] = rowA(pr) + 2 * k0;
+        we[n] = rowE(pr) + 4 * pm;
+        wc[n] = rowC(pr) + 4 * k0;
 #pragma unroll
-        for (int m = 0; m < 3; ++m) oc[n][m] = P(pj[n] + m - 1) * CS * 4 + 4 * pk;
+        for (int m = 0; m < 3; ++m) oc[n][m] = rowC(P(pj[n] + m - 1)) + 4 * k0;
     }
-    // writes of elements without a cell go to the discard row, reads of absent successors to the zero row
-    const int pk0 = tid % HE, pb0 = pk0 / 16, pc0 = pk0 - 16 * pb0;
-    const int xa = XR * RA * 2 + (pb0 * KA + 8 * pc0) * 2, xe = (XR * NB + pb0) * 4, xc = XR * CS * 4 + 4 * pk0;
-    const int zc = ZR * CS * 4 + 4 * pk0;
+    // writes of padding units (hidden sizes that are not a multiple of 16) go to the discard row
+    const int pm0 = et % HP2;
+    const int xa = rowA(XR), xe = rowE(XR) + 4 * pm0, xc = rowC(XR) + 8 * pm0;
 
-    auto diag_len = [&](int s) {
-        if (s < 0 || s >= S) return 0;
-        const int lo = s > w - 1 ? s - (w - 1) : 0;
-        const int hi = s < h - 1 ? s : h - 1;
-        return hi - lo + 1;
-    };
-    auto diag_lo = [&](int s) { return s > w - 1 ? s - (w - 1) : 0; };
-
-    // forward values of this thread's elements on one diagonal: i, f_l, f_u, o | g, c | dy
+    // the forward's factors of this thread's units on one diagonal (SA, SB; two units each) and their
+    // upstream gradient
     struct Fw {
-        f32x4 g4[NE];
-        f32x2 g2[NE];
-        float dy[NE];
+        f32x4 fa[NE][2], fb[NE][2];
+        f32x2 dy[NE];
     };
     // s1: diagonal, st1: stash index of its first cell
     auto load_f = [&](int s1, int st1, Fw& f) {
@@ -259,191 +313,197 @@ __global__ __launch_bounds__(NT) void k_bwd16(Dev D, const float* __restrict__ U
         for (int n = 0; n < NE; ++n) {
             // predicates combined without short-circuit evaluation: plain selects, no branches
             const bool ok = (pj[n] < L1) & pk_ok[n];
-            const int el = pe + ve[n];
-            f.g4[n] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, ok ? el * 16 : kOOB, 0, 0));
-            f.g2[n] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rS2, ok ? el * 8 : kOOB, 0, 0));
+            const int so = ok ? (pe + ve[n]) * 16 : kOOB;
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                f.fa[n][u2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, so + 16 * u2, 0, 0));
+                f.fb[n][u2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS2, so + 16 * u2, 0, 0));
+            }
             const bool vy = ok & (per_dir | ((pj[n] >= jr0) & (pj[n] < jr1)));
-            f.dy[n] = bld(rU, vy ? pu0 + vu[n] : kOOB);
+            f.dy[n] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rU, vy ? pu0 + vu[n] : kOOB, 0, 0));
         }
     };
 
-    Fw fs[4];
-    // stash index of the first cell of diagonal s and of the prefetch diagonal s - kPD
-    int st = (int)cells - 1;  // diagonal S - 1 is the single last cell
-    int stz = st;
+    Fw fs[NS];
+    // stash index of the first cell of the prefetch diagonal s - KPD
+    int stz = (int)cells - 1;  // diagonal S - 1 is the single last cell
 #pragma unroll
-    for (int i = 0; i < kPD; ++i) {
+    for (int i = 0; i < KPD; ++i) {
         load_f(S - 1 - i, stz, fs[i]);
         stz -= diag_len(S - 2 - i);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loop starts with nothing in flight
-    __syncthreads();
+    int st = (int)cells - 1;  // stash index of the first cell of diagonal s
 
-    // diagonal s at position POS of the unrolled loop (POS = (S - 1 - s) mod 4): buffer POS & 1 is
-    // written, 1 - (POS & 1) holds diagonal s + 1; prefetch set POS is consumed, (POS + kPD) & 3 refilled
+    // diagonal s at position POS = (S - 1 - s) mod NS of the unrolled loop: prefetch set POS is consumed,
+    // (POS + KPD) mod NS refilled; with NS even the LDS buffer parity (S - 1 - s) & 1 is POS & 1
+    static_assert(NS % 2 == 0, "the unrolled loop must keep the buffer parity");
+    typedef __attribute__((address_space(3))) f32x2 lds_f2;
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
     auto step = [&](int s, auto POSc) {
         constexpr int POS = decltype(POSc)::value;
         constexpr int CB = POS & 1;
-        const int L = diag_len(s), L1 = diag_len(s + 1);
-        // the prefetch: at the top of the step, except in the matrix waves, which issue it inside phase 1 so
-        // that its address arithmetic overlaps their LDS reads and products (every wave issues the same memory
-        // operations per step)
-        const int stz_now = stz;
-        stz -= diag_len(s - kPD - 1);
-        if (!mat) load_f(s - kPD, stz_now, fs[(POS + kPD) & 3]);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch at the top of the step
-        const int dn = s >= w - 1 ? 1 : 0;  // successors of position j: right j - dn, down j + 1 - dn
-        const unsigned char* ap = smem + (1 - CB) * ABUF;
-        const unsigned char* ep = smem + OFF_E + (1 - CB) * EBUF;
-        // ---- phase 1: X and Y of the later diagonal, matrix waves only (no global memory inside) ----
-        if (mat) {
-            // scale exponents of the output rows: read before the products where registers allow
-            int er[4][NB];
-            auto read_er = [&]() {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int bi = 0; bi < NB; ++bi)
-                        er[r][bi] = *reinterpret_cast<const int*>(ep + ((orow + r) * NB + bi) * 4);
-            };
-            if constexpr (NB == 1) read_er();
-            load_f(s - kPD, stz_now, fs[(POS + kPD) & 3]);
-            f32x4 acc[2][NB];
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-                for (int bi = 0; bi < NB; ++bi) acc[pp][bi] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int bi = 0; bi < NB; ++bi)
-#pragma unroll
-                for (int t = 0; t < KT; ++t) {
-                    const unsigned char* p = ap + oa1 + (bi * KA + 32 * t + 8 * q) * 2;
-                    const f16x8 ah = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p, 16));
-                    const f16x8 al = *reinterpret_cast<const f16x8*>(__builtin_assume_aligned(p + NB * KA * 2, 16));
-#pragma unroll
-                    for (int pp = 0; pp < 2; ++pp) {
-                        acc[pp][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[pp][bi][t], acc[pp][bi], 0, 0, 0);
-                        acc[pp][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[pp][bi][t], acc[pp][bi], 0, 0, 0);
-                        acc[pp][bi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[pp][bi][t], acc[pp][bi], 0, 0, 0);
-                    }
-                }
-            if constexpr (NB != 1) read_er();
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = 0.f;
-#pragma unroll
-                    for (int bi = 0; bi < NB; ++bi) v += ldexpf(acc[pp][bi][r], ec[pp] - er[r][bi]);
-                    *reinterpret_cast<float*>(smem + (pair_y(pp) ? OFF_Y : OFF_X) +
-                                              ((orow + r) * CS + pair_col(pp)) * 4) = v;
-                }
-        }
-        // memory states of diagonal s - 1 (prefetched with it) for this diagonal's predecessor terms
-#pragma unroll
-        for (int n = 0; n < NE; ++n) *reinterpret_cast<float*>(smem + OFF_CP + wc[n]) = fs[(POS + 1) & 3].g2[n][1];
-        __syncthreads();
-        // ---- phase 2: elementwise, all threads ----
+        load_f(s - KPD, stz, fs[(POS + KPD) % NS]);
+        stz -= diag_len(s - KPD - 1);
+        // ---- before the products are in: the factors into place, the step's addresses ----
         const Fw& f = fs[POS];
-        const unsigned char* clp = smem + OFF_CL + (1 - CB) * CBUF;
-        const unsigned char* cup = smem + OFF_CU + (1 - CB) * CBUF;
-        unsigned char* aw = smem + CB * ABUF;
-        unsigned char* ew = smem + OFF_E + CB * EBUF;
-        unsigned char* clw = smem + OFF_CL + CB * CBUF;
-        unsigned char* cuw = smem + OFF_CU + CB * CBUF;
+        const int L = diag_len(s);
+        const int dn = s >= w - 1 ? 1 : 0;  // successors of position j: right j - dn, down j + 1 - dn
         const int pe = st * H;
-        // predecessors of position j on diagonal s - 1: left j + dl iff j < Ml, up j + dl - 1 iff j >= 1 - dl
-        const int dl = s >= w ? 1 : 0;
-        const int lo = diag_lo(s);
-        const int Ml = L < s - lo ? L : s - lo;
+        float cB[NE][2], c0[NE][2], c1[NE][2], c2[NE][2], c3[NE][2], c4[NE][2], dyv[NE][2], flv[NE][2],
+            fuv[NE][2];
+        lds_p rr[NE], rd[NE], oa[NE], oe[NE], ocw[NE];
+        int og4[NE], og1[NE];
+        const lds_p L0 = (lds_p)smem;
 #pragma unroll
         for (int n = 0; n < NE; ++n) {
             const int j = pj[n];
+            // successors' rows: right j - dn, lower j + 1 - dn. A position outside the later diagonal has a row
+            // of zeros: the zero row below 0 and from 16 CG on, and in between the row its element wrote zeros to
+            // (an element outside its diagonal computes exact zeros, its stash loads being masked) or, never
+            // written, still holds the zeros of the start.
+            rr[n] = L0 + (dn ? oc[n][0] : oc[n][1]);
+            rd[n] = L0 + (dn ? oc[n][1] : oc[n][2]);
             const bool ok = (j < L) & pk_ok[n];
-            const bool hr = j >= dn, hd = j + 1 - dn < L1;
-            const float cl = *reinterpret_cast<const float*>(smem + OFF_CP + (j < Ml ? (dl ? oc[n][2] : oc[n][1]) : zc));
-            const float cu = *reinterpret_cast<const float*>(smem + OFF_CP + (j + dl >= 1 ? (dl ? oc[n][1] : oc[n][0]) : zc));
-            const int ocr = hr ? (dn ? oc[n][0] : oc[n][1]) : zc;  // right successor's c row, or zero row
-            const int ocd = hd ? (dn ? oc[n][1] : oc[n][2]) : zc;  // lower successor's
-            // dh: X of the right successor and Y of the lower one (zero rows when absent), plus dy
-            const float dh = (*reinterpret_cast<const float*>(smem + OFF_X + ocr) +
-                              *reinterpret_cast<const float*>(smem + OFF_Y + ocd)) + f.dy[n];
-            const float dcin = *reinterpret_cast<const float*>(clp + ocr) + *reinterpret_cast<const float*>(cup + ocd);
-            const float ig = f.g4[n][0], fl = f.g4[n][1], fu = f.g4[n][2], og = f.g4[n][3];
-            const float gg = f.g2[n][0], c = f.g2[n][1];
-            const float tc = ftanh(c);
-            const float dov = dh * tc;
-            const float dc = __builtin_fmaf(dh * og, 1.f - tc * tc, dcin);
-            const float d0 = dc * gg * ig * (1.f - ig);
-            const float d1 = dc * cl * fl * (1.f - fl);
-            const float d2 = dc * cu * fu * (1.f - fu);
-            const float d3 = dov * og * (1.f - og);
-            const float d4 = dc * ig * (1.f - gg * gg);
-            // scale of this (cell, block): the largest |da| over the 16 units of the block (non-negative
-            // floats order like their bit patterns)
-            const float am = fmaxf(fmaxf(fabsf(d0), fabsf(d1)), fmaxf(fmaxf(fabsf(d2), fabsf(d3)), fabsf(d4)));
-            const uint32_t mb = row16_max(ok ? __float_as_uint(am) : 0u);
-            const int E = scale_exp(mb);
-            const float s0 = ldexpf(d0, E), s1 = ldexpf(d1, E), s2 = ldexpf(d2, E), s3 = ldexpf(d3, E),
-                        s4 = ldexpf(d4, E);
-            const float t0 = hi_part(s0), t1 = hi_part(s1), t2 = hi_part(s2), t3 = hi_part(s3), t4 = hi_part(s4);
-            const f16x8 hv = {(_Float16)t0, (_Float16)t1, (_Float16)t2, (_Float16)t3, (_Float16)t4,
-                              (_Float16)0, (_Float16)0, (_Float16)0};
-            const f16x8 lv = {(_Float16)(s0 - t0), (_Float16)(s1 - t1), (_Float16)(s2 - t2), (_Float16)(s3 - t3),
-                              (_Float16)(s4 - t4), (_Float16)0, (_Float16)0, (_Float16)0};
-            unsigned char* pa = aw + (ok ? wa[n] : xa);
-            *reinterpret_cast<f16x8*>(__builtin_assume_aligned(pa, 16)) = hv;
-            *reinterpret_cast<f16x8*>(__builtin_assume_aligned(pa + NB * KA * 2, 16)) = lv;
-            *reinterpret_cast<int*>(ew + (ok ? we[n] : xe)) = E;
-            *reinterpret_cast<float*>(clw + (ok ? wc[n] : xc)) = dc * fl;
-            *reinterpret_cast<float*>(cuw + (ok ? wc[n] : xc)) = dc * fu;
+            // units beyond H (hidden sizes that are not a multiple of 16) write to the discard row
+            oa[n] = L0 + (H == HE ? wa[n] : (pk_ok[n] ? wa[n] : xa)) + CB * ABUF;
+            oe[n] = L0 + (H == HE ? we[n] : (pk_ok[n] ? we[n] : xe));
+            ocw[n] = L0 + (H == HE ? wc[n] : (pk_ok[n] ? wc[n] : xc));
             const int el = pe + ve[n];
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{d0, d1, d2, d3}), rA4,
-                                                   ok ? el * 16 : kOOB, 0, 0);
-            bst(d4, rA1, ok ? el * 4 : kOOB);
+            og4[n] = ok ? el * 16 : kOOB;
+            og1[n] = ok ? el * 4 : kOOB;
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                c0[n][u2] = f.fa[n][u2][0];
+                c1[n][u2] = f.fa[n][u2][1];
+                c2[n][u2] = f.fa[n][u2][2];
+                c3[n][u2] = f.fa[n][u2][3];
+                c4[n][u2] = f.fb[n][u2][0];
+                cB[n][u2] = f.fb[n][u2][1];
+                flv[n][u2] = f.fb[n][u2][2];
+                fuv[n][u2] = f.fb[n][u2][3];
+                dyv[n][u2] = f.dy[n][u2];
+            }
+        }
+        // keep all of it before the barrier (the compiler would otherwise sink it into the part after)
+#pragma unroll
+        for (int n = 0; n < NE; ++n) {
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                asm volatile("" : "+v"(cB[n][u2]), "+v"(c0[n][u2]), "+v"(c1[n][u2]), "+v"(c2[n][u2]),
+                             "+v"(c3[n][u2]), "+v"(c4[n][u2]));
+                asm volatile("" : "+v"(dyv[n][u2]), "+v"(flv[n][u2]), "+v"(fuv[n][u2]));
+            }
+            asm volatile("" : "+v"(rr[n]), "+v"(rd[n]), "+v"(oa[n]), "+v"(oe[n]), "+v"(ocw[n]), "+v"(og4[n]),
+                         "+v"(og1[n]));
+        }
+        __syncthreads();  // X and Y of diagonal s + 1 are in LDS
+        // ---- the rest of dc and da: all LDS reads first, then the arithmetic, then the writes ----
+        constexpr int RCL = OFF_CL + (1 - CB) * CBUF, RCU = OFF_CU + (1 - CB) * CBUF;  // the later diagonal's
+        constexpr int WE = OFF_E + CB * EBUF, WCL = OFF_CL + CB * CBUF, WCU = OFF_CU + CB * CBUF;  // this one's
+        f32x2 xv[NE], yv[NE], lv_[NE], uv[NE];
+#pragma unroll
+        for (int n = 0; n < NE; ++n) {
+            xv[n] = *reinterpret_cast<lds_f2*>(rr[n] + OFF_X);
+            yv[n] = *reinterpret_cast<lds_f2*>(rd[n] + OFF_Y);
+            lv_[n] = *reinterpret_cast<lds_f2*>(rr[n] + RCL);
+            uv[n] = *reinterpret_cast<lds_f2*>(rd[n] + RCU);
+        }
+        float dcv[NE][2], dd[NE][2][5];
+        uint32_t mb[NE];
+#pragma unroll
+        for (int n = 0; n < NE; ++n) {
+            float am = 0.f;
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2) {
+                // dh: X of the right successor and Y of the lower one (zero rows when absent), plus dy
+                const float dh = (xv[n][u2] + yv[n][u2]) + dyv[n][u2];
+                const float dc = __builtin_fmaf(dh, cB[n][u2], lv_[n][u2] + uv[n][u2]);
+                dcv[n][u2] = dc;
+                dd[n][u2][0] = dc * c0[n][u2];
+                dd[n][u2][1] = dc * c1[n][u2];
+                dd[n][u2][2] = dc * c2[n][u2];
+                dd[n][u2][3] = dh * c3[n][u2];
+                dd[n][u2][4] = dc * c4[n][u2];
+#pragma unroll
+                for (int g = 0; g < 5; ++g) am = fmaxf(am, fabsf(dd[n][u2][g]));
+            }
+            // scale of this cell: the largest |da| over its lanes (non-negative floats order like their bits)
+            mb[n] = __float_as_uint(am);
+            // dc f_l and dc f_u for the earlier diagonal: written now, while the scale is worked out
+            *reinterpret_cast<lds_f2*>(ocw[n] + WCL) = f32x2{dcv[n][0] * flv[n][0], dcv[n][1] * flv[n][1]};
+            *reinterpret_cast<lds_f2*>(ocw[n] + WCU) = f32x2{dcv[n][0] * fuv[n][0], dcv[n][1] * fuv[n][1]};
+        }
+#pragma unroll
+        for (int n = 0; n < NE; ++n) mb[n] = NB == 1 ? row8_max(mb[n]) : row16_max(mb[n]);
+#pragma unroll
+        for (int n = 0; n < NE; ++n) {
+            const int E = scale_exp(mb[n]);
+            float sv[2][5], tv[2][5];
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+                for (int g = 0; g < 5; ++g) {
+                    sv[u2][g] = ldexpf(dd[n][u2][g], E);
+                    tv[u2][g] = hi_part(sv[u2][g]);
+                }
+            // gate g of unit k goes to K = g H + k: the pair of units is one word per gate and piece
+#pragma unroll
+            for (int g = 0; g < 5; ++g) {
+                const f16x2 hp = __builtin_convertvector((f32x2){tv[0][g], tv[1][g]}, f16x2);
+                const f16x2 lp = __builtin_convertvector((f32x2){sv[0][g] - tv[0][g], sv[1][g] - tv[1][g]}, f16x2);
+                *reinterpret_cast<lds_u32*>(oa[n] + OFF_A + 2 * g * H) = __builtin_bit_cast(uint32_t, hp);
+                *reinterpret_cast<lds_u32*>(oa[n] + OFF_A + 2 * KP + 2 * g * H) = __builtin_bit_cast(uint32_t, lp);
+            }
+            *reinterpret_cast<lds_u32*>(oe[n] + WE) = (uint32_t)E;
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, f32x4{dd[n][u2][0], dd[n][u2][1], dd[n][u2][2], dd[n][u2][3]}), rA4,
+                    og4[n] + 16 * u2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{dd[n][0][4], dd[n][1][4]}), rA1,
+                                                  og1[n], 0, 0);
         }
         st -= diag_len(s - 1);
-        __syncthreads();
+        __syncthreads();  // diagonal s's gate gradients are written
     };
     int s = S - 1;
-    for (; s - 3 >= 0; s -= 4) {
+    for (; s - (NS - 1) >= 0; s -= NS) {
         step(s, IC<0>{});
         step(s - 1, IC<1>{});
         step(s - 2, IC<2>{});
-        step(s - 3, IC<3>{});
+        if constexpr (NS > 3) step(s - 3, IC<3>{});
     }
     if (s >= 0) step(s, IC<0>{});
     if (s - 1 >= 0) step(s - 1, IC<1>{});
-    if (s - 2 >= 0) step(s - 2, IC<2>{});
+    if constexpr (NS > 3)
+        if (s - 2 >= 0) step(s - 2, IC<2>{});
 }
 
 typedef void (*Bwd16Kernel)(Dev, const float*, const float*, const float*, const float*, const float*, float*);
 
-// hidden sizes of the workloads, each with its (elements per thread, threads) shapes in order of preference:
-// one element per thread while the widest diagonal fits the workgroup (shorter chains in phase 2), else two
+// hidden sizes of the workloads, each with its (unit pairs per thread, element waves) shapes in order of
+// preference: the smallest workgroup that covers the widest diagonal
 struct B16Shape2 {
-    int NE, NT;
+    int NE, EW;
     Bwd16Kernel k;
 };
 struct B16Entry {
     int H, NB, CG;
     B16Shape2 shapes[4];
 };
-#define MDL_B16S(h, ne, nt) {ne, nt, k_bwd16<h, ne, nt>}
-#define MDL_B16(h)                                                                                          \
-    {h, B16Shape<h>::NB, B16Shape<h>::CG,                                                                   \
-     {MDL_B16S(h, 1, 512), MDL_B16S(h, 1, 640), MDL_B16S(h, 1, 768), MDL_B16S(h, 2, 512)}}
-const B16Entry kB16[] = {MDL_B16(16),
-                         {32, B16Shape<32>::NB, B16Shape<32>::CG,
-                          {MDL_B16S(32, 1, 512), MDL_B16S(32, 2, 512), {0, 0, nullptr}, {0, 0, nullptr}}}};
-#undef MDL_B16
+#define MDL_B16S(h, ne, ew, pd) {ne, ew, k_bwd16<h, ne, ew, pd>}
+const B16Entry kB16[] = {
+    {16, B16Shape<16>::NB, B16Shape<16>::CG,
+     {MDL_B16S(16, 1, 4, 3), MDL_B16S(16, 1, 8, 3), {0, 0, nullptr}, {0, 0, nullptr}}},
+    {32, B16Shape<32>::NB, B16Shape<32>::CG,
+     {MDL_B16S(32, 1, 4, 3), MDL_B16S(32, 1, 8, 3), {0, 0, nullptr}, {0, 0, nullptr}}}};
 #undef MDL_B16S
 
-// the widest diagonal must fit the matrix waves' tiles (16 CG cells) and one of the phase-2 shapes
+// the widest diagonal must fit the matrix waves' tiles (16 CG cells) and one of the element shapes
 const B16Shape2* b16_shape(const B16Entry& m, int Lmax) {
-    const int elems = Lmax * 16 * m.NB;
+    const int elems = Lmax * 8 * m.NB;  // unit pairs
     for (const auto& sh : m.shapes)
-        if (sh.k && elems <= sh.NE * sh.NT) return &sh;
+        if (sh.k && elems <= sh.NE * 64 * sh.EW) return &sh;
     return nullptr;
 }
 const B16Entry* b16_entry(int H, int Lmax) {
@@ -453,9 +513,13 @@ const B16Entry* b16_entry(int H, int Lmax) {
 }
 
 size_t b16_lds(const B16Entry& m) {
-    const size_t nrw = 16 * (size_t)m.CG + 2, he = 16 * (size_t)m.NB;
-    const size_t ra = 2 * (size_t)m.NB * 128 + 8, cs = he + 4;
-    return 2 * nrw * ra * 2 + 2 * nrw * m.NB * 4 + 7 * nrw * cs * 4;
+    const size_t nrw = 16 * (size_t)m.CG + 2, he = 16 * (size_t)m.NB, nblk = nrw / 16 + 1;
+    const size_t kp = (5 * (size_t)m.H + 31) / 32 * 32, ra = 2 * kp + 8, cs = he + 4;
+    const size_t sk = 128 / m.CG, skc = m.NB == 1 ? 64 : 0;
+    const size_t ebuf = nrw * (he / 2) * 4 + nblk * sk, cbuf = nrw * cs * 4 + nblk * skc;
+    const size_t abuf = nrw * ra * 2 + nblk * sk;
+    const size_t small = 2 * ebuf + 6 * cbuf;  // exponents, dc f_l, dc f_u, X, Y
+    return (small + 15) / 16 * 16 + 2 * abuf;
 }
 
 }  // namespace
@@ -472,7 +536,8 @@ hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, c
     const B16Entry* m = b16_entry(H, D.max_diag);
     if (!m) return hipErrorInvalidValue;
     const B16Shape2* sh = b16_shape(*m, D.max_diag);
-    launch(sh->k, dim3(4 * D.n), dim3(sh->NT), b16_lds(*m), st, D, Ul, Uu, stash, dy_flat, dh_dirs, dA);
+    launch(sh->k, dim3(4 * D.n), dim3(64 * (kMatWaves + sh->EW)), b16_lds(*m), st, D, Ul, Uu, stash, dy_flat,
+           dh_dirs, dA);
     return hipGetLastError();
 }
 

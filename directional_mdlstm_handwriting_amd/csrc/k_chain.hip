@@ -25,7 +25,7 @@ namespace {
 constexpr int CHAIN_THREADS = 256;
 constexpr int MAXI = 8;  // (cell, hidden) items per thread and step
 
-// Forward. Z in (Z4, Z1), gate stash out (S4, S2), h_dirs out [4][Hc][Wc][H].
+// Forward. Z in (Z4, Z1), the reverse wavefront's factors out (SA, SB), h_dirs out [4][Hc][Wc][H].
 __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int Lmax, const float* __restrict__ Ul,
                                                              const float* __restrict__ Uu,
                                                              const float* __restrict__ Z, float* __restrict__ stash,
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
     const float* Z4d = Z + base * 4 * H;
     const float* Z1d = Z + z1_offset(D.T, H) + base * H;
     float* S4d = stash + base * 4 * H;
-    float* S2d = stash + z1_offset(D.T, H) + base * 2 * H;
+    float* SBd = stash + z1_offset(D.T, H) + base * 4 * H;
     float* Hd = hdirs + (int64_t)d * D.Hc * D.Wc * H;
     const int S = h + w - 1;
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -130,18 +130,15 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
                 const float ig = sigm(acc0), fl = sigm(acc1), fu = sigm(acc2), og = sigm(acc3);
                 const float gg = ftanh(acc4);
                 const float c = fl * cl + fu * cu + ig * gg;
-                const float hv = og * ftanh(c);
+                const float tc = ftanh(c);
+                const float hv = og * tc;
                 hn[j * H + k] = hv;
                 cn[j * H + k] = c;
                 Hd[((int64_t)F.y(a) * D.Wc + F.x(b)) * H + k] = hv;
-                float* r4 = S4d + ((st + j) * H + k) * 4;
-                r4[0] = ig;
-                r4[1] = fl;
-                r4[2] = fu;
-                r4[3] = og;
-                float* r2 = S2d + ((st + j) * H + k) * 2;
-                r2[0] = gg;
-                r2[1] = c;
+                f32x4 fa, fb;
+                bwd_factors(ig, fl, fu, og, gg, cl, cu, tc, fa, fb);
+                *reinterpret_cast<f32x4*>(S4d + ((st + j) * H + k) * 4) = fa;
+                *reinterpret_cast<f32x4*>(SBd + ((st + j) * H + k) * 4) = fb;
             }
         }
         __syncthreads();
@@ -181,8 +178,8 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
     }
     __syncthreads();
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
-    const float* S4d = stash + base * 4 * H;
-    const float* S2d = stash + z1_offset(D.T, H) + base * 2 * H;
+    const float* SAd = stash + base * 4 * H;
+    const float* SBd = stash + z1_offset(D.T, H) + base * 4 * H;
     float* dA4d = dA + base * 4 * H;
     float* dA1d = dA + z1_offset(D.T, H) + base * H;
     const float* dyb = dy_flat ? dy_flat + D.flat_off[e] * H : nullptr;
@@ -194,8 +191,6 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
         const int L = dg_len(h, w, s), lo = dg_lo(h, w, s);
         const int64_t st = dg_start(h, w, s);
         const int lon = dg_lo(h, w, s + 1);
-        const int lop = s > 0 ? dg_lo(h, w, s - 1) : 0;
-        const int64_t stp = s > 0 ? dg_start(h, w, s - 1) : 0;
         const float* dar = dab + ((s + 1) & 1) * Lmax * G;
         const float* dclr = dcl + ((s + 1) & 1) * Lmax * H;
         const float* dcur = dcu + ((s + 1) & 1) * Lmax * H;
@@ -209,12 +204,9 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
                 const int j = item / H, k = item - (item / H) * H;
                 const int a = lo + j, b = s - a;
                 const int y = F.y(a), x = F.x(b);
-                // forward values of this cell and its predecessors' memory states
-                const float* r4 = S4d + ((st + j) * H + k) * 4;
-                const float ig = r4[0], fl = r4[1], fu = r4[2], og = r4[3];
-                const float gg = S2d[((st + j) * H + k) * 2], c = S2d[((st + j) * H + k) * 2 + 1];
-                const float cl = b > 0 ? S2d[((stp + a - lop) * H + k) * 2 + 1] : 0.f;
-                const float cu = a > 0 ? S2d[((stp + a - 1 - lop) * H + k) * 2 + 1] : 0.f;
+                // the forward's factors of this cell
+                const f32x4 fa = *reinterpret_cast<const f32x4*>(SAd + ((st + j) * H + k) * 4);
+                const f32x4 fb = *reinterpret_cast<const f32x4*>(SBd + ((st + j) * H + k) * 4);
                 float dh = 0.f;
                 if (dhd) {
                     dh = dhd[((int64_t)y * D.Wc + x) * H + k];
@@ -237,18 +229,12 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
                     for (int n = 0; n < G; ++n) dh += dv[n] * ut[n * H2];
                     dcin += dcur[jd * H + k];
                 }
-                const float tc = ftanh(c);
-                const float dov = dh * tc;
-                const float dc = dcin + dh * og * (1.f - tc * tc);
-                const float d0 = dc * gg * ig * (1.f - ig);
-                const float d1 = dc * cl * fl * (1.f - fl);
-                const float d2 = dc * cu * fu * (1.f - fu);
-                const float d3 = dov * og * (1.f - og);
-                const float d4 = dc * ig * (1.f - gg * gg);
+                const float dc = __builtin_fmaf(dh, fb[1], dcin);
+                const float d0 = dc * fa[0], d1 = dc * fa[1], d2 = dc * fa[2], d3 = dh * fa[3], d4 = dc * fb[0];
                 float* dw = daw + j * G + k;
                 dw[0] = d0; dw[H] = d1; dw[2 * H] = d2; dw[3 * H] = d3; dw[4 * H] = d4;
-                dclw[j * H + k] = dc * fl;
-                dcuw[j * H + k] = dc * fu;
+                dclw[j * H + k] = dc * fb[2];
+                dcuw[j * H + k] = dc * fb[3];
                 float* dg = dA4d + ((st + j) * H + k) * 4;
                 dg[0] = d0; dg[1] = d1; dg[2] = d2; dg[3] = d3;
                 dA1d[(st + j) * H + k] = d4;
@@ -317,7 +303,7 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
     const int64_t cells = (int64_t)h * w;
     const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 4 * H * 4);
-    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + z1_offset(D.T, H) + base * 2 * H, cells * 2 * H * 4);
+    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + z1_offset(D.T, H) + base * 4 * H, cells * 4 * H * 4);
     const __amdgpu_buffer_rsrc_t rA4 = rsrc(dA + base * 4 * H, cells * 16 * H);
     const __amdgpu_buffer_rsrc_t rA1 = rsrc(dA + z1_offset(D.T, H) + base * H, cells * 4 * H);
     // upstream gradient: per-direction canvas tensor, or the flat gradient of the direction sum
@@ -327,26 +313,22 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
                 : rsrc(dy_flat + D.flat_off[e] * H, (int64_t)rh * rw * H * 4);
     const int S = h + w - 1;
 
-    // per output cell: i, f_l, f_u, o, g, c, c_left, c_up, upstream dh
+    // per output cell: the forward's factors (SA 0-3, SB 4-7), upstream dh
     auto load_v = [&](int s, float (&v)[9][4]) {
         const bool in = s >= 0;
         const int L = in ? dg_len(h, w, s) : 0, lo = in ? dg_lo(h, w, s) : 0;
         const int st = in ? (int)dg_start(h, w, s) : 0;
-        const int lop = s > 0 ? dg_lo(h, w, s - 1) : 0;
-        const int stp = s > 0 ? (int)dg_start(h, w, s - 1) : 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int jo = orow + r;
             const bool ok = jo < L && kok;
             const int a = lo + jo, b = s - a;
             const int ei = (st + jo) * H + kk;  // (cell, hidden unit) element of the stash
-            const int so4 = ok ? ei * 16 : kOOB, so2 = ok ? ei * 8 : kOOB;
+            const int so = ok ? ei * 16 : kOOB;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) v[g][r] = bld(rS4, so4 + g * 4);
-            v[4][r] = bld(rS2, so2);
-            v[5][r] = bld(rS2, so2 + 4);
-            v[6][r] = bld(rS2, (ok && b > 0) ? (((stp + a - lop) * H + kk) * 2 + 1) * 4 : kOOB);
-            v[7][r] = bld(rS2, (ok && a > 0) ? (((stp + a - 1 - lop) * H + kk) * 2 + 1) * 4 : kOOB);
+            for (int g = 0; g < 4; ++g) v[g][r] = bld(rS4, so + g * 4);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) v[4 + g][r] = bld(rS2, so + g * 4);
             const int y = F.y(a), x = F.x(b);
             const int ly = y - ry0, lx = x - rx0;
             int uo = kOOB;
@@ -398,21 +380,14 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
             const int kc = kok ? kk : 0;
             const float dcin = dclr[((ok && b + 1 < w) ? a - lon : ZR) * H + kc] +
                                dcur[((ok && a + 1 < h) ? a + 1 - lon : ZR) * H + kc];
-            const float ig = vc[0][r], fl = vc[1][r], fu = vc[2][r], og = vc[3][r];
-            const float gg = vc[4][r], c = vc[5][r], cl = vc[6][r], cu = vc[7][r];
-            const float tc = ftanh(c);
-            const float dov = dh * tc;
-            const float dc = dcin + dh * og * (1.f - tc * tc);
-            const float d0 = dc * gg * ig * (1.f - ig);
-            const float d1 = dc * cl * fl * (1.f - fl);
-            const float d2 = dc * cu * fu * (1.f - fu);
-            const float d3 = dov * og * (1.f - og);
-            const float d4 = dc * ig * (1.f - gg * gg);
+            const float dc = __builtin_fmaf(dh, vc[5][r], dcin);
+            const float d0 = dc * vc[0][r], d1 = dc * vc[1][r], d2 = dc * vc[2][r], d3 = dh * vc[3][r],
+                        d4 = dc * vc[4][r];
             if (ok) {
                 float* dw = daw + jo * G + kk;
                 dw[0] = d0; dw[H] = d1; dw[2 * H] = d2; dw[3 * H] = d3; dw[4 * H] = d4;
-                dclw[jo * H + kk] = dc * fl;
-                dcuw[jo * H + kk] = dc * fu;
+                dclw[jo * H + kk] = dc * vc[6][r];
+                dcuw[jo * H + kk] = dc * vc[7][r];
             }
             const int ea = (st + jo) * H + kk;
             const int a4 = ok ? ea * 16 : kOOB, a1 = ok ? ea * 4 : kOOB;

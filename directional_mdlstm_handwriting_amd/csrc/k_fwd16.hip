@@ -172,7 +172,7 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     constexpr int XB = BF16 ? 2 : 4;  // bytes per input value
     const __amdgpu_buffer_rsrc_t rX = rsrc(xc, (int64_t)D.Hc * D.Wc * C * XB);
     const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 16 * H);
-    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 2 * H, cells * 8 * H);
+    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 4 * H, cells * 16 * H);
     const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4);
     const int S = h + w - 1;
 
@@ -334,7 +334,8 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             const float og = sig_e2(__builtin_fmaf(acc[3][r], us[3], accx[3][r]));
             const float gg = ftanh(__builtin_fmaf(acc[4][r], us[4], accx[4][r]));
             const float c = __builtin_fmaf(fl, cl[r], __builtin_fmaf(fu, cu[r], ig * gg));
-            const float hv = og * ftanh(c);
+            const float tc = ftanh(c);
+            const float hv = og * tc;
             *reinterpret_cast<float*>(cw + owc[r]) = c;
             _Float16 hh, hl;
             split16(hv * kHScale, hh, hl);
@@ -343,10 +344,10 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             hp[HP] = hl;
             bst(hv, rH, ok ? ph + vh[r] : kOOB);
             const int el = pe + ve[r];
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{ig, fl, fu, og}), rS4,
-                                                   ok ? el * 16 : kOOB, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{gg, c}), rS2, ok ? el * 8 : kOOB,
-                                                  0, 0);
+            f32x4 fa, fb;
+            bwd_factors(ig, fl, fu, og, gg, cl[r], cu[r], tc, fa, fb);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fa), rS4, ok ? el * 16 : kOOB, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fb), rS2, ok ? el * 16 : kOOB, 0, 0);
         }
         project(xs[(POS + 1) & 3]);  // diagonal s + 1 (prefetched two steps ago)
         // refill the set just consumed with diagonal s + kZD; issued here, its address arithmetic stays off

@@ -8,11 +8,11 @@
 // unit k's weights (input projection x.Wx + b fused, recurrent product h_left.Ul + h_up.Uu), in fp32.
 //
 // Step structure shared with the matrix-core kernels: the loop is unrolled by four so every step is
-// straight code; the step's global inputs (canvas pixels forward; gate stash, memory states and upstream
+// straight code; the step's global inputs (canvas pixels forward; the forward's factors and the upstream
 // gradient backward) are prefetched three diagonals ahead into four register sets; loads and stores use
 // raw buffer instructions with an out-of-range offset for a masked lane; a zero row in LDS stands in for
 // a missing neighbour. One barrier per step: the forward double-buffers (h, c) of the diagonals, the
-// backward double-buffers the gate gradients, the dc * f terms and the predecessors' memory states.
+// backward double-buffers the gate gradients and the dc * f terms.
 #include "kernels.h"
 #include "devmath.h"
 
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(MAXT) void k_fwd_small(Dev D, const void* __restric
     const int64_t cells = (int64_t)h * w;
     const __amdgpu_buffer_rsrc_t rX = rsrc(xc, (int64_t)D.Hc * D.Wc * C * XB);
     const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 16 * H);
-    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + z1_offset(D.T, H) + base * 2 * H, cells * 8 * H);
+    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + z1_offset(D.T, H) + base * 4 * H, cells * 16 * H);
     const __amdgpu_buffer_rsrc_t rH = rsrc(hdirs + (int64_t)d * D.Hc * D.Wc * H, (int64_t)D.Hc * D.Wc * H * 4);
     const int S = h + w - 1;
     // cell (a, b) of the unit (b = s - a on diagonal s) sits at canvas (Y0 + SY a, X0 + SX b): its pixel is
@@ -160,17 +160,18 @@ __global__ __launch_bounds__(MAXT) void k_fwd_small(Dev D, const void* __restric
         const float ig = sigm(z[0]), fl = sigm(z[1]), fu = sigm(z[2]), og = sigm(z[3]);
         const float gg = ftanh(z[4]);
         const float c = __builtin_fmaf(fl, cl, __builtin_fmaf(fu, cu, ig * gg));
-        const float hv = og * ftanh(c);
+        const float tc = ftanh(c);
+        const float hv = og * tc;
         // positions past the diagonal write their own rows too: no later step reads them
         hb[(s & 1) * RB + j * HP + k] = hv;
         cb[(s & 1) * RB + j * HP + k] = c;
         const bool ok = j < L;
         const int el = (st + j) * H + k;
         bst(hv, rH, ok ? ((PB + (lo + j) * PA + s * PS) * H + k) * 4 : kOOBs);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{ig, fl, fu, og}), rS4,
-                                               ok ? el * 16 : kOOBs, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{gg, c}), rS2, ok ? el * 8 : kOOBs, 0,
-                                              0);
+        f32x4 fa, fb;
+        bwd_factors(ig, fl, fu, og, gg, cl, cu, tc, fa, fb);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fa), rS4, ok ? el * 16 : kOOBs, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fb), rS2, ok ? el * 16 : kOOBs, 0, 0);
         st += L;
         __syncthreads();
     };
@@ -191,6 +192,7 @@ __global__ __launch_bounds__(MAXT) void k_fwd_small(Dev D, const void* __restric
 //     dh = dy + da(R) . Ul[k][:] + da(D) . Uu[k][:],  dc_in = (dc f_l)(R) + (dc f_u)(D)
 //     tc = tanh c,  dc = dc_in + dh o (1 - tc^2)
 //     da = [dc g i(1-i), dc c_l f_l(1-f_l), dc c_u f_u(1-f_u), dh tc o(1-o), dc i (1-g^2)]
+// with every factor of dc and da that depends on the forward alone read from the forward's stash (SA, SB).
 template <int H, int MAXT>
 __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restrict__ Ul,
                                                              const float* __restrict__ Uu,
@@ -216,21 +218,19 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
         wl[n] = n < G ? Ul[((int64_t)d * H + k) * G + n] : 0.f;
         wu[n] = n < G ? Uu[((int64_t)d * H + k) * G + n] : 0.f;
     }
-    // LDS, each [2][NP + 1][.]: gate gradients (GP per row), dc f_l and dc f_u (H per row), memory states
-    // of the predecessor diagonal (H per row)
+    // LDS, each [2][NP + 1][.]: gate gradients (GP per row), dc f_l and dc f_u (H per row)
     extern __shared__ __align__(16) float sm[];
     const int RG = (NP + 1) * GP, RH = (NP + 1) * H;
     float* dab = sm;
     float* dcl = dab + 2 * RG;
     float* dcu = dcl + 2 * RH;
-    float* cpb = dcu + 2 * RH;
-    for (int i = tid; i < 2 * RG + 6 * RH; i += blockDim.x) sm[i] = 0.f;
+    for (int i = tid; i < 2 * RG + 4 * RH; i += blockDim.x) sm[i] = 0.f;
 
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
     const int64_t cells = (int64_t)h * w;
     const int64_t o1 = z1_offset(D.T, H);
     const __amdgpu_buffer_rsrc_t rS4 = rsrc(stash + base * 4 * H, cells * 16 * H);
-    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 2 * H, cells * 8 * H);
+    const __amdgpu_buffer_rsrc_t rS2 = rsrc(stash + o1 + base * 4 * H, cells * 16 * H);
     const __amdgpu_buffer_rsrc_t rA4 = rsrc(dA + base * 4 * H, cells * 16 * H);
     const __amdgpu_buffer_rsrc_t rA1 = rsrc(dA + o1 + base * H, cells * 4 * H);
     const bool per_dir = dh_dirs != nullptr;
@@ -253,8 +253,7 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
     const int br0 = (d & 1) ? w - (rx0 - x0) - rw : rx0 - x0, br1 = br0 + rw;
 
     struct Fw {
-        f32x4 g4;  // i, f_l, f_u, o
-        f32x2 g2;  // g, c
+        f32x4 fa, fb;  // the forward's factors (SA, SB)
         float dy;
     };
     // forward values of this thread's element on diagonal s1 (stash index st1 of its first cell)
@@ -263,8 +262,8 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
         const int lo1 = sd_lo(w, s1 < 0 ? 0 : s1);
         const bool ok = j < L1;
         const int el = st1 * H + j * H + k;
-        f.g4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, ok ? el * 16 : kOOBs, 0, 0));
-        f.g2 = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rS2, ok ? el * 8 : kOOBs, 0, 0));
+        f.fa = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, ok ? el * 16 : kOOBs, 0, 0));
+        f.fb = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS2, ok ? el * 16 : kOOBs, 0, 0));
         const int a = lo1 + j, b = s1 - a;
         const bool vy = ok & (per_dir | ((a >= ar0) & (a < ar1) & (b >= br0) & (b < br1)));
         f.dy = bld(rU, vy ? UB + a * UA + s1 * US : kOOBs);
@@ -281,26 +280,19 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
 
-    // diagonal s at position POS = (S - 1 - s) mod 4: prefetch set POS holds diagonal s, (POS + 1) & 3
-    // diagonal s - 1, and (POS + kPFs) & 3 is refilled for diagonal s - kPFs
+    // diagonal s at position POS = (S - 1 - s) mod 4: prefetch set POS holds diagonal s and (POS + kPFs) & 3
+    // is refilled for diagonal s - kPFs
     auto step = [&](int s, auto POSc) {
         constexpr int POS = decltype(POSc)::value;
         const int L = sd_len(h, w, s), L1 = sd_len(h, w, s + 1);
         load_f(s - kPFs, stz, fs[(POS + kPFs) & 3]);
         stz -= sd_len(h, w, s - kPFs - 1);
         __builtin_amdgcn_sched_barrier(0);
-        // memory states of diagonal s - 1 for this diagonal's predecessor terms
-        cpb[(s & 1) * RH + j * H + k] = fs[(POS + 1) & 3].g2[1];
         __syncthreads();
         const Fw& f = fs[POS];
         const int dn = s >= w - 1 ? 1 : 0;  // successors of position j: right j - dn, down j + 1 - dn
         const int rr = j >= dn ? j - dn : ZR;
         const int rd = j + 1 - dn < L1 ? j + 1 - dn : ZR;
-        const int dl = s >= w ? 1 : 0;
-        const int lo = sd_lo(w, s);
-        const int Ml = L < s - lo ? L : s - lo;
-        const int rl = j < Ml ? j + dl : ZR;                    // left predecessor on diagonal s - 1
-        const int ru = (j + dl >= 1 && j < L) ? j + dl - 1 : ZR;  // upper predecessor
         const float* dar = dab + ((s + 1) & 1) * RG;
         // dh as four partial sums over the two successors' gate gradients
         float p0 = f.dy, p1 = 0.f, p2 = 0.f, p3 = 0.f;
@@ -319,17 +311,8 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
         }
         const float dh = (p0 + p1) + (p2 + p3);
         const float dcin = dcl[((s + 1) & 1) * RH + rr * H + k] + dcu[((s + 1) & 1) * RH + rd * H + k];
-        const float cl = cpb[(s & 1) * RH + rl * H + k], cu = cpb[(s & 1) * RH + ru * H + k];
-        const float ig = f.g4[0], fl = f.g4[1], fu = f.g4[2], og = f.g4[3];
-        const float gg = f.g2[0], c = f.g2[1];
-        const float tc = ftanh(c);
-        const float dov = dh * tc;
-        const float dc = __builtin_fmaf(dh * og, 1.f - tc * tc, dcin);
-        const float d0 = dc * gg * ig * (1.f - ig);
-        const float d1 = dc * cl * fl * (1.f - fl);
-        const float d2 = dc * cu * fu * (1.f - fu);
-        const float d3 = dov * og * (1.f - og);
-        const float d4 = dc * ig * (1.f - gg * gg);
+        const float dc = __builtin_fmaf(dh, f.fb[1], dcin);
+        const float d0 = dc * f.fa[0], d1 = dc * f.fa[1], d2 = dc * f.fa[2], d3 = dh * f.fa[3], d4 = dc * f.fb[0];
         // positions past the diagonal write their own rows: no step reads them as successors
         float* daw = dab + (s & 1) * RG + j * GP + k;
         daw[0] = d0;
@@ -337,8 +320,8 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
         daw[2 * H] = d2;
         daw[3 * H] = d3;
         daw[4 * H] = d4;
-        dcl[(s & 1) * RH + j * H + k] = dc * fl;
-        dcu[(s & 1) * RH + j * H + k] = dc * fu;
+        dcl[(s & 1) * RH + j * H + k] = dc * f.fb[2];
+        dcu[(s & 1) * RH + j * H + k] = dc * f.fb[3];
         const bool ok = j < L;
         const int el = st * H + j * H + k;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{d0, d1, d2, d3}), rA4,
@@ -410,7 +393,7 @@ size_t small_fwd_lds(int H, int Lmax) {
 
 size_t small_bwd_lds(int H, int Lmax) {
     const size_t rows = small_positions(H, Lmax) + 1;
-    return sizeof(float) * (2 * rows * ((5 * H + 3) / 4 * 4) + 6 * rows * H);
+    return sizeof(float) * (2 * rows * ((5 * H + 3) / 4 * 4) + 4 * rows * H);
 }
 
 hipError_t launch_fwd_small(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,

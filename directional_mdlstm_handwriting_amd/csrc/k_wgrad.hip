@@ -30,7 +30,7 @@ WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H) {
     const int R = C + 1 + 2 * H;
     w.nparts = nparts;
     size_t p = 0;
-    w.stash = p; p = al(p + sizeof(float) * 4 * (size_t)T * 6 * H);
+    w.stash = p; p = al(p + sizeof(float) * 4 * (size_t)T * 8 * H);
     w.zda = p;   p = al(p + sizeof(float) * 4 * (size_t)T * G);
     w.part = p;  p = al(p + sizeof(float) * 4 * (size_t)nparts * R * G);
     w.total = p;

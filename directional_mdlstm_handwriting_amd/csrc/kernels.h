@@ -102,21 +102,24 @@ MDL_HD inline int find_example(const int64_t* off, int n, int64_t g) {
 }
 
 // Workspace carving for one MDLSTM layer (all offsets 256-byte aligned).
-// Projection and gate-stash layouts. For direction d, computed cell t (each
+// Projection and stash layouts. For direction d, computed cell t (each
 // example's cells in diagonal-major order, examples one after another) and
 // hidden unit k, with T computed cells per direction:
 //   Z4[((d*T + t)*H + k)*4 + g]  pre-activation x.Wx + b of gate g = i, f_l, f_u, o
 //   Z1[(d*T + t)*H + k]          pre-activation of the cell input g
-//   S4[((d*T + t)*H + k)*4 + g]  gate values i, f_l, f_u, o
-//   S2[((d*T + t)*H + k)*2 + m]  m = 0: g, m = 1: the memory state c
+//   SA[((d*T + t)*H + k)*4 + m]  the reverse wavefront's factors g i(1-i), c_l f_l(1-f_l), c_u f_u(1-f_u),
+//                                tanh(c) o(1-o)  (bwd_factors in devmath.h)
+//   SB[((d*T + t)*H + k)*4 + m]  i(1-g^2), o(1-tanh^2 c), f_l, f_u
 //   dA4, dA1: the gate pre-activation gradients in the layout of Z4 / Z1
-// A lane owning (cell, k) reads or writes its four sigmoid gates with one
-// 16-byte access. Z1 follows Z4 in the workspace's projection region, S2
-// follows S4 in its stash region.
+// A lane owning (cell, k) reads or writes each four-value group with one
+// 16-byte access. Z1 follows Z4 in the workspace's projection region, SB
+// follows SA in its stash region (at z1_offset). The skewed-schedule kernels
+// keep their own stash in the same region: gates i, f_l, f_u, o at SA's place
+// and (g, c) pairs, [(d*T + t)*H + k][2], at SB's.
 MDL_HD inline int64_t z1_offset(int64_t T, int H) { return 4 * T * 4 * (int64_t)H; }
 
 struct WsLayout {
-    size_t stash = 0;   // float [4][T][6H]: gates i, f_l, f_u, o, g and memory state c of every cell
+    size_t stash = 0;   // float [4][T][8H]: SA then SB, the reverse wavefront's factors of every cell
     size_t zda = 0;     // float [4][T][5H]: projection x.Wx+b (forward), gate gradients dA (backward)
     size_t part = 0;    // float [nparts][4][(C+1+2H)*5H]: weight-gradient partial sums
     size_t total = 0;
