@@ -60,14 +60,18 @@ __device__ inline float ftanh(float x) {
     return ax < 0.55f ? small : __builtin_copysignf(big, x);
 }
 
-// The factors the reverse wavefront multiplies a cell's gradients by, formed by the forward from its own
-// values (gates i, f_l, f_u, o, cell input g, tc = tanh c) and its predecessors' memory states c_l, c_u:
+// The factors the reverse wavefront multiplies a cell's gradients by, from the cell's forward values (gates
+// i, f_l, f_u, o, cell input g, tc = tanh c) and its predecessors' memory states c_l, c_u:
 //   A = (g i(1-i), c_l f_l(1-f_l), c_u f_u(1-f_u), tc o(1-o)),  B = (i(1-g^2), o(1-tc^2), f_l, f_u)
-// so that dc = dh B[1] + dc_in and da = (dc A[0], dc A[1], dc A[2], dh A[3], dc B[0]).
+// so that dc = dh B[1] + dc_in and da = (dc A[0], dc A[1], dc A[2], dh A[3], dc B[0]). The forward stashes
+// (i, f_l, f_u, o) and (g, tc, c_l, c_u); this forms the factors from the two vectors.
 __device__ inline void bwd_factors(float ig, float fl, float fu, float og, float gg, float cl, float cu, float tc,
                                    f32x4& A, f32x4& B) {
     A = f32x4{gg * (ig * (1.f - ig)), cl * (fl * (1.f - fl)), cu * (fu * (1.f - fu)), tc * (og * (1.f - og))};
     B = f32x4{ig * (1.f - gg * gg), og * (1.f - tc * tc), fl, fu};
+}
+__device__ inline void bwd_factors(f32x4 gates, f32x4 rest, f32x4& A, f32x4& B) {
+    bwd_factors(gates[0], gates[1], gates[2], gates[3], rest[0], rest[2], rest[3], rest[1], A, B);
 }
 
 // fp32 value -> f16 pair (hi, lo) with hi + lo equal to v to about 2^-22 relative,

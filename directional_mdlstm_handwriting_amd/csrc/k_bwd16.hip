@@ -21,10 +21,10 @@
 //     brings its largest magnitude into [2^14, 2^15) before it was split; its exponent sits in LDS beside
 //     it and the product is scaled back exactly. The K dimension orders da by (gate, hidden unit), the
 //     order of the columns of Ul and Uu, 5H entries padded to a multiple of 32.
-//  Element waves (the others) own fixed (diagonal position, hidden unit) elements. Every factor of dc and
-//     da that depends on the forward alone (o (1 - tc^2) and the five gate-derivative products) comes
-//     from the forward's stash; before the first barrier, while the products run, the element waves take
-//     it from the prefetch registers and work out the step's addresses. After it, dh = dy + X(R) + Y(D)
+//  Element waves (the others) own fixed (diagonal position, hidden unit) elements. Before the first
+//     barrier, while the products run, they form every factor of dc and da that depends on the forward
+//     alone (o (1 - tc^2) and the five gate-derivative products) from the forward's stash, which holds the
+//     gates, tc = tanh c and the predecessors' memory states c_l, c_u, and work out the step's addresses. After it, dh = dy + X(R) + Y(D)
 //     and dc_in leave a few products, the cell's scale (a maximum over the lanes of its DPP rows), the split
 //     into the LDS A rows of the next step, dc f_l and dc f_u for the earlier diagonal, and the store of da
 //     for the weight gradients. Their stash and upstream-gradient reads are issued KPD diagonals ahead.
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
     const int pm0 = et % HP2;
     const int xa = rowA(XR), xe = rowE(XR) + 4 * pm0, xc = rowC(XR) + 8 * pm0;
 
-    // the forward's factors of this thread's units on one diagonal (SA, SB; two units each) and their
+    // the forward's values of this thread's units on one diagonal (SA, SB; two units each) and their
     // upstream gradient
     struct Fw {
         f32x4 fa[NE][2], fb[NE][2];
@@ -373,14 +373,16 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
             og1[n] = ok ? el * 4 : kOOB;
 #pragma unroll
             for (int u2 = 0; u2 < 2; ++u2) {
-                c0[n][u2] = f.fa[n][u2][0];
-                c1[n][u2] = f.fa[n][u2][1];
-                c2[n][u2] = f.fa[n][u2][2];
-                c3[n][u2] = f.fa[n][u2][3];
-                c4[n][u2] = f.fb[n][u2][0];
-                cB[n][u2] = f.fb[n][u2][1];
-                flv[n][u2] = f.fb[n][u2][2];
-                fuv[n][u2] = f.fb[n][u2][3];
+                f32x4 ka, kb;
+                bwd_factors(f.fa[n][u2], f.fb[n][u2], ka, kb);
+                c0[n][u2] = ka[0];
+                c1[n][u2] = ka[1];
+                c2[n][u2] = ka[2];
+                c3[n][u2] = ka[3];
+                c4[n][u2] = kb[0];
+                cB[n][u2] = kb[1];
+                flv[n][u2] = kb[2];
+                fuv[n][u2] = kb[3];
                 dyv[n][u2] = f.dy[n][u2];
             }
         }

@@ -25,7 +25,7 @@ namespace {
 constexpr int CHAIN_THREADS = 256;
 constexpr int MAXI = 8;  // (cell, hidden) items per thread and step
 
-// Forward. Z in (Z4, Z1), the reverse wavefront's factors out (SA, SB), h_dirs out [4][Hc][Wc][H].
+// Forward. Z in (Z4, Z1), the forward values the reverse wavefront needs out (SA, SB), h_dirs out [4][Hc][Wc][H].
 __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int Lmax, const float* __restrict__ Ul,
                                                              const float* __restrict__ Uu,
                                                              const float* __restrict__ Z, float* __restrict__ stash,
@@ -135,10 +135,8 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_fwd_chain(Dev D, int H, int L
                 hn[j * H + k] = hv;
                 cn[j * H + k] = c;
                 Hd[((int64_t)F.y(a) * D.Wc + F.x(b)) * H + k] = hv;
-                f32x4 fa, fb;
-                bwd_factors(ig, fl, fu, og, gg, cl, cu, tc, fa, fb);
-                *reinterpret_cast<f32x4*>(S4d + ((st + j) * H + k) * 4) = fa;
-                *reinterpret_cast<f32x4*>(SBd + ((st + j) * H + k) * 4) = fb;
+                *reinterpret_cast<f32x4*>(S4d + ((st + j) * H + k) * 4) = f32x4{ig, fl, fu, og};
+                *reinterpret_cast<f32x4*>(SBd + ((st + j) * H + k) * 4) = f32x4{gg, tc, cl, cu};
             }
         }
         __syncthreads();
@@ -204,9 +202,10 @@ __global__ __launch_bounds__(CHAIN_THREADS) void k_bwd_chain(Dev D, int H, int L
                 const int j = item / H, k = item - (item / H) * H;
                 const int a = lo + j, b = s - a;
                 const int y = F.y(a), x = F.x(b);
-                // the forward's factors of this cell
-                const f32x4 fa = *reinterpret_cast<const f32x4*>(SAd + ((st + j) * H + k) * 4);
-                const f32x4 fb = *reinterpret_cast<const f32x4*>(SBd + ((st + j) * H + k) * 4);
+                // the forward's values of this cell, and the factors from them
+                f32x4 fa, fb;
+                bwd_factors(*reinterpret_cast<const f32x4*>(SAd + ((st + j) * H + k) * 4),
+                            *reinterpret_cast<const f32x4*>(SBd + ((st + j) * H + k) * 4), fa, fb);
                 float dh = 0.f;
                 if (dhd) {
                     dh = dhd[((int64_t)y * D.Wc + x) * H + k];
@@ -313,7 +312,7 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
                 : rsrc(dy_flat + D.flat_off[e] * H, (int64_t)rh * rw * H * 4);
     const int S = h + w - 1;
 
-    // per output cell: the forward's factors (SA 0-3, SB 4-7), upstream dh
+    // per output cell: the forward's values (SA 0-3, SB 4-7), upstream dh
     auto load_v = [&](int s, float (&v)[9][4]) {
         const bool in = s >= 0;
         const int L = in ? dg_len(h, w, s) : 0, lo = in ? dg_lo(h, w, s) : 0;
@@ -380,14 +379,16 @@ __global__ __launch_bounds__(256) void k_bwd_mfma(Dev D, int, int Lmax, const fl
             const int kc = kok ? kk : 0;
             const float dcin = dclr[((ok && b + 1 < w) ? a - lon : ZR) * H + kc] +
                                dcur[((ok && a + 1 < h) ? a + 1 - lon : ZR) * H + kc];
-            const float dc = __builtin_fmaf(dh, vc[5][r], dcin);
-            const float d0 = dc * vc[0][r], d1 = dc * vc[1][r], d2 = dc * vc[2][r], d3 = dh * vc[3][r],
-                        d4 = dc * vc[4][r];
+            f32x4 ka, kb;
+            bwd_factors(f32x4{vc[0][r], vc[1][r], vc[2][r], vc[3][r]}, f32x4{vc[4][r], vc[5][r], vc[6][r], vc[7][r]},
+                        ka, kb);
+            const float dc = __builtin_fmaf(dh, kb[1], dcin);
+            const float d0 = dc * ka[0], d1 = dc * ka[1], d2 = dc * ka[2], d3 = dh * ka[3], d4 = dc * kb[0];
             if (ok) {
                 float* dw = daw + jo * G + kk;
                 dw[0] = d0; dw[H] = d1; dw[2 * H] = d2; dw[3 * H] = d3; dw[4 * H] = d4;
-                dclw[jo * H + kk] = dc * vc[6][r];
-                dcuw[jo * H + kk] = dc * vc[7][r];
+                dclw[jo * H + kk] = dc * kb[2];
+                dcuw[jo * H + kk] = dc * kb[3];
             }
             const int ea = (st + jo) * H + kk;
             const int a4 = ok ? ea * 16 : kOOB, a1 = ok ? ea * 4 : kOOB;

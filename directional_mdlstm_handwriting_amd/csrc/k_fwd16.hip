@@ -344,10 +344,10 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
             hp[HP] = hl;
             bst(hv, rH, ok ? ph + vh[r] : kOOB);
             const int el = pe + ve[r];
-            f32x4 fa, fb;
-            bwd_factors(ig, fl, fu, og, gg, cl[r], cu[r], tc, fa, fb);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fa), rS4, ok ? el * 16 : kOOB, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fb), rS2, ok ? el * 16 : kOOB, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{ig, fl, fu, og}), rS4,
+                                                   ok ? el * 16 : kOOB, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{gg, tc, cl[r], cu[r]}), rS2,
+                                                   ok ? el * 16 : kOOB, 0, 0);
         }
         project(xs[(POS + 1) & 3]);  // diagonal s + 1 (prefetched two steps ago)
         // refill the set just consumed with diagonal s + kZD; issued here, its address arithmetic stays off

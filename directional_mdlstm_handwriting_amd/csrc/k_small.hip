@@ -168,10 +168,10 @@ __global__ __launch_bounds__(MAXT) void k_fwd_small(Dev D, const void* __restric
         const bool ok = j < L;
         const int el = (st + j) * H + k;
         bst(hv, rH, ok ? ((PB + (lo + j) * PA + s * PS) * H + k) * 4 : kOOBs);
-        f32x4 fa, fb;
-        bwd_factors(ig, fl, fu, og, gg, cl, cu, tc, fa, fb);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fa), rS4, ok ? el * 16 : kOOBs, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, fb), rS2, ok ? el * 16 : kOOBs, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{ig, fl, fu, og}), rS4,
+                                               ok ? el * 16 : kOOBs, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{gg, tc, cl, cu}), rS2,
+                                               ok ? el * 16 : kOOBs, 0, 0);
         st += L;
         __syncthreads();
     };
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(MAXT) void k_fwd_small(Dev D, const void* __restric
 //     dh = dy + da(R) . Ul[k][:] + da(D) . Uu[k][:],  dc_in = (dc f_l)(R) + (dc f_u)(D)
 //     tc = tanh c,  dc = dc_in + dh o (1 - tc^2)
 //     da = [dc g i(1-i), dc c_l f_l(1-f_l), dc c_u f_u(1-f_u), dh tc o(1-o), dc i (1-g^2)]
-// with every factor of dc and da that depends on the forward alone read from the forward's stash (SA, SB).
+// with c_l, c_u and tc = tanh c read from the forward's stash (SA, SB) with the gates.
 template <int H, int MAXT>
 __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restrict__ Ul,
                                                              const float* __restrict__ Uu,
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
     const int br0 = (d & 1) ? w - (rx0 - x0) - rw : rx0 - x0, br1 = br0 + rw;
 
     struct Fw {
-        f32x4 fa, fb;  // the forward's factors (SA, SB)
+        f32x4 fa, fb;  // the forward's values (SA, SB)
         float dy;
     };
     // forward values of this thread's element on diagonal s1 (stash index st1 of its first cell)
@@ -311,8 +311,10 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
         }
         const float dh = (p0 + p1) + (p2 + p3);
         const float dcin = dcl[((s + 1) & 1) * RH + rr * H + k] + dcu[((s + 1) & 1) * RH + rd * H + k];
-        const float dc = __builtin_fmaf(dh, f.fb[1], dcin);
-        const float d0 = dc * f.fa[0], d1 = dc * f.fa[1], d2 = dc * f.fa[2], d3 = dh * f.fa[3], d4 = dc * f.fb[0];
+        f32x4 ka, kb;
+        bwd_factors(f.fa, f.fb, ka, kb);
+        const float dc = __builtin_fmaf(dh, kb[1], dcin);
+        const float d0 = dc * ka[0], d1 = dc * ka[1], d2 = dc * ka[2], d3 = dh * ka[3], d4 = dc * kb[0];
         // positions past the diagonal write their own rows: no step reads them as successors
         float* daw = dab + (s & 1) * RG + j * GP + k;
         daw[0] = d0;
@@ -320,8 +322,8 @@ __global__ __launch_bounds__(MAXT) void k_bwd_small(Dev D, const float* __restri
         daw[2 * H] = d2;
         daw[3 * H] = d3;
         daw[4 * H] = d4;
-        dcl[(s & 1) * RH + j * H + k] = dc * f.fb[2];
-        dcu[(s & 1) * RH + j * H + k] = dc * f.fb[3];
+        dcl[(s & 1) * RH + j * H + k] = dc * kb[2];
+        dcu[(s & 1) * RH + j * H + k] = dc * kb[3];
         const bool ok = j < L;
         const int el = st * H + j * H + k;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{d0, d1, d2, d3}), rA4,

@@ -107,9 +107,9 @@ MDL_HD inline int find_example(const int64_t* off, int n, int64_t g) {
 // hidden unit k, with T computed cells per direction:
 //   Z4[((d*T + t)*H + k)*4 + g]  pre-activation x.Wx + b of gate g = i, f_l, f_u, o
 //   Z1[(d*T + t)*H + k]          pre-activation of the cell input g
-//   SA[((d*T + t)*H + k)*4 + m]  the reverse wavefront's factors g i(1-i), c_l f_l(1-f_l), c_u f_u(1-f_u),
-//                                tanh(c) o(1-o)  (bwd_factors in devmath.h)
-//   SB[((d*T + t)*H + k)*4 + m]  i(1-g^2), o(1-tanh^2 c), f_l, f_u
+//   SA[((d*T + t)*H + k)*4 + m]  gate values i, f_l, f_u, o
+//   SB[((d*T + t)*H + k)*4 + m]  the cell input g, tanh(c), and the predecessors' memory states c_l, c_u
+//                                (everything the reverse wavefront's factors need: bwd_factors in devmath.h)
 //   dA4, dA1: the gate pre-activation gradients in the layout of Z4 / Z1
 // A lane owning (cell, k) reads or writes each four-value group with one
 // 16-byte access. Z1 follows Z4 in the workspace's projection region, SB
@@ -119,7 +119,7 @@ MDL_HD inline int find_example(const int64_t* off, int n, int64_t g) {
 MDL_HD inline int64_t z1_offset(int64_t T, int H) { return 4 * T * 4 * (int64_t)H; }
 
 struct WsLayout {
-    size_t stash = 0;   // float [4][T][8H]: SA then SB, the reverse wavefront's factors of every cell
+    size_t stash = 0;   // float [4][T][8H]: SA then SB, the forward values of every cell the reverse wavefront needs
     size_t zda = 0;     // float [4][T][5H]: projection x.Wx+b (forward), gate gradients dA (backward)
     size_t part = 0;    // float [nparts][4][(C+1+2H)*5H]: weight-gradient partial sums
     size_t total = 0;
