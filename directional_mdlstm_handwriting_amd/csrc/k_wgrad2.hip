@@ -8,15 +8,23 @@
 // for shapes fixed at compile time. One workgroup takes one group of the
 // layout's weight-gradient split (a few cell ranges of about the same total
 // size for every workgroup, so all compute units finish together) for all
-// four directions, WPD waves per direction, and walks it in tiles of TP cells. The global loads of tile t+1 (16-byte loads of the
-// predecessors' h and of the gate gradients in their [cell][k][4] layout)
+// four directions, WPD waves per direction, and walks it in tiles of TP = 32 cells. The global loads of tile t+1 (16-byte
+// loads of the predecessors' h and of the gate gradients in their [cell][k][4] layout)
 // are issued before tile t is computed from LDS, so their latency hides
 // behind the matrix-core work. Each thread stages a fixed share of one cell
 // of each tile and works out that cell's pixel, predecessors and stash
-// position itself, so the loads wait on no shared table.
-// r^T da runs on v_mfma_f32_16x16x4_f32 (fp32 products and sums, K = 4
-// cells per instruction); each wave owns all M tiles of its direction and a
-// share of its N tiles. dx runs on v_mfma_f32_4x4x1f32, whose 16 independent
+// position itself, so the loads wait on no shared table. The tile sits in
+// LDS component-major: one row of TP cells for each component of r and each
+// gate column of da.
+// r^T da runs on v_mfma_f32_16x16x32_bf16 (K = the tile's 32 cells) where a
+// wave's tiles leave the registers for it: every fp32 operand is split exactly
+// into three bf16 pieces, v = v1 + v2 + v3 (each piece the leading 8
+// significant bits of what is left; bf16 keeps fp32's exponent range, so
+// nothing is scaled), and the product keeps the six terms v_i w_j with
+// i + j <= 4 (the dropped ones are below 2^-23 of v w), accumulated in fp32
+// smallest first. Otherwise it runs on v_mfma_f32_16x16x4_f32 (fp32 products
+// and sums, K = 4 cells per instruction). Each wave owns all M tiles of its
+// direction and a share of its N tiles. dx runs on v_mfma_f32_4x4x1f32, whose 16 independent
 // 4 x 4 blocks fit the few input channels without padding (the 16 x 16
 // instruction would waste three quarters of its columns at C = 4): every wave
 // takes a share of the gate-gradient columns of all four directions, the
@@ -35,12 +43,17 @@ constexpr int kOOBw = 0x7ffffff0;  // byte offset past every buffer range: loads
 template <int C, int H>
 struct WgShape {
     static constexpr int G = 5 * H, R = C + 1 + 2 * H;
-    static constexpr int TP = H >= 32 ? 16 : 32;          // cells per tile: the staged loads of the next tile fit
+    static constexpr int TP = 32;                         // cells per tile: the K extent of one product
     static constexpr int MT = (R + 15) / 16, NT = (G + 15) / 16;
     static constexpr int WPD = (MT * NT + 31) / 32;       // waves per direction: at most 32 tiles per wave
     static constexpr int NTW = (NT + WPD - 1) / WPD;      // N tiles per wave (bound)
-    static constexpr int RP = MT % 2 ? 16 * MT : 16 * MT + 16;  // r row stride: 16 (mod 32) floats
-    static constexpr int DS = G + 1 + ((4 - G % 4) % 4);  // da row stride: 1 (mod 4), > G (column G stays 0)
+    static constexpr int RR = 16 * MT, NR = 16 * NT;      // LDS rows of r components and of gate columns
+    // the product on bf16 pieces where a wave's split fragments fit its registers beside its accumulators
+    // (at most 16 tiles per wave), else on fp32 v_mfma_f32_16x16x4_f32
+    static constexpr bool BF = MT * NTW <= 16;
+    // LDS row stride: 16-byte rows (4 mod 32 floats) for the 8-cell fragment reads of the bf16 product,
+    // 2 (mod 32) for the single-cell reads of the fp32 one, so either read pattern hits distinct banks
+    static constexpr int TPD = BF ? TP + 4 : TP + 2;
     static constexpr int VH = H % 4 == 0 ? 4 : (H % 2 == 0 ? 2 : 1);    // h / dA1 load width
     static constexpr int NTH = 64 * WPD;                  // threads per direction
     static constexpr int TPC = NTH / TP;                  // threads per cell of a tile in the loads
@@ -52,9 +65,9 @@ struct WgShape {
     static constexpr int NWV = 4 * WPD;                   // waves of the workgroup
     static constexpr int NPW = (G + NWV - 1) / NWV;       // da columns of the dx product per wave
     static constexpr int NC4 = (C + 3) / 4;               // groups of 4 input channels
+    static constexpr int LATE = 0;                        // next tile's loads after the products (registers)
     static_assert(C <= 16, "dx product assumes at most 16 input channels");
-    static_assert(DS % 4 == 1 && DS > G, "da row stride");
-    static_assert(NWV * NPW <= DS, "dx column shares stay inside a da row");
+    static_assert(NWV * NPW <= NR, "dx column shares stay inside the gate-column rows");
     static_assert(NTH % TP == 0 && (TPC & (TPC - 1)) == 0, "whole power-of-two thread groups per cell");
 };
 
@@ -79,6 +92,31 @@ __device__ inline float vget(const typename VecOf<VB>::T& v, int i) {
     else return v[i];
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// the exact split v = v1 + v2 + v3 of eight fp32 values into three bf16 pieces, each piece the leading 8
+// significant bits (sign, exponent and 7 mantissa bits: the upper half of the fp32 pattern) of what the
+// pieces before it leave; the last remainder has at most 8 significant bits and is exact in bf16.
+// Pairs of values pack into one register as (low half: even value, high half: odd value).
+__device__ inline void split3(const f32x4& x0, const f32x4& x1, u32x4 (&p)[3]) {
+    uint32_t u[3][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float v = i < 4 ? x0[i] : x1[i - 4];
+        const uint32_t b0 = __float_as_uint(v);
+        const float e1 = v - __uint_as_float(b0 & 0xFFFF0000u);
+        const uint32_t b1 = __float_as_uint(e1);
+        const float e2 = e1 - __uint_as_float(b1 & 0xFFFF0000u);
+        u[0][i] = b0;
+        u[1][i] = b1;
+        u[2][i] = __float_as_uint(e2);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[k][i] = __builtin_amdgcn_perm(u[k][2 * i + 1], u[k][2 * i], 0x07060302u);
+}
+
 // position of region-local cell (ly, lx) of an h x w region in direction d's diagonal-major order
 __device__ inline int stash_pos(int h, int w, int ly, int lx, int d) {
     const int a = (d & 2) ? h - 1 - ly : ly;
@@ -97,8 +135,11 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
                                                                       float* __restrict__ dx_canvas) {
     using S = WgShape<C, H>;
     constexpr int G = S::G, R = S::R, MT = S::MT, NT = S::NT, WPD = S::WPD, NTW = S::NTW, TP = S::TP;
-    constexpr int RP = S::RP, DS = S::DS, VH = S::VH, NTH = S::NTH, NWV = S::NWV, NPW = S::NPW, NC4 = S::NC4;
+    constexpr int RR = S::RR, NR = S::NR, TPD = S::TPD, VH = S::VH, NTH = S::NTH, NWV = S::NWV, NPW = S::NPW,
+                  NC4 = S::NC4;
     constexpr int TPC = S::TPC, NVH = S::NVH, NV1 = S::NV1, NHL = S::NHL, ND4 = S::ND4, ND1 = S::ND1, NXL = S::NXL;
+    constexpr int LATE_LOADS = S::LATE;
+    constexpr bool BF = S::BF;
     constexpr int XB = BF16 ? 2 : 4;
     typedef typename VecOf<VH>::T HV;
     const int grp = blockIdx.x;
@@ -128,19 +169,19 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
         o[11] = D.segs[3 * sg + 2];
     }
 
-    // LDS: r rows [4][TP][RP], gate gradients [4][TP][DS] (units k: gates 0..3 at 4k + g, gate 4 at 4H + k),
-    // dx shares of the waves [NWV][TP][C], and two slots of the tile's cell table (pixel, flat index) for
-    // the dx store
+    // LDS: r [4][RR][TPD] (component m of r, then the tile's cells), gate gradients [4][NR][TPD] (gate
+    // column n = g H + k), dx shares of the waves [NWV][TP][C], and two slots of the tile's cell table
+    // (pixel, flat index) for the dx store; rows past R and G stay zero
     extern __shared__ __align__(16) unsigned char smem[];
     float* rs = reinterpret_cast<float*>(smem);
-    float* das = rs + 4 * TP * RP;
-    float* dxs = das + 4 * TP * DS;
+    float* das = rs + 4 * RR * TPD;
+    float* dxs = das + 4 * NR * TPD;
     int* tpix = reinterpret_cast<int*>(dxs + NWV * TP * C);  // [2][TP]
     int* tflat = tpix + 2 * TP;                              // [2][TP]
-    constexpr int NWORDS = 4 * TP * RP + 4 * TP * DS + NWV * TP * C + 4 * TP;
+    constexpr int NWORDS = 4 * RR * TPD + 4 * NR * TPD + NWV * TP * C + 4 * TP;
     for (int i = tid; i < NWORDS; i += blockDim.x) reinterpret_cast<uint32_t*>(smem)[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < 4 * TP; i += blockDim.x) rs[i * RP + C] = 1.f;  // the bias row of r
+    for (int i = tid; i < 4 * TP; i += blockDim.x) rs[((i / TP) * RR + C) * TPD + i % TP] = 1.f;  // the bias row
     int ntiles = 0;
     for (int sg = 0; sg < nsg; ++sg) ntiles += (sgt[sg][11] - sgt[sg][10] + TP - 1) / TP;
 
@@ -204,15 +245,15 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
         }
     };
     auto write_lds = [&]() {
-        float* rsd = rs + (d * TP + lc) * RP;
-        float* dad = das + (d * TP + lc) * DS;
+        float* rsd = rs + d * RR * TPD + lc;
+        float* dad = das + d * NR * TPD + lc;
 #pragma unroll
         for (int i = 0; i < NHL; ++i) {
             const int v = pt + i * TPC;
             if (v < NVH) {
                 const int up = v >= NV1 ? 1 : 0, kv = v - up * NV1;
 #pragma unroll
-                for (int j = 0; j < VH; ++j) rsd[C + 1 + up * H + kv * VH + j] = vget<VH>(vh[i], j);
+                for (int j = 0; j < VH; ++j) rsd[(C + 1 + up * H + kv * VH + j) * TPD] = vget<VH>(vh[i], j);
             }
         }
 #pragma unroll
@@ -220,7 +261,7 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
             const int k = pt + i * TPC;
             if (k < H) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) dad[4 * k + g] = vd4[i][g];
+                for (int g = 0; g < 4; ++g) dad[(g * H + k) * TPD] = vd4[i][g];
             }
         }
 #pragma unroll
@@ -228,29 +269,20 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
             const int kv = pt + i * TPC;
             if (kv < NV1) {
 #pragma unroll
-                for (int j = 0; j < VH; ++j) dad[4 * H + kv * VH + j] = vget<VH>(vd1[i], j);
+                for (int j = 0; j < VH; ++j) dad[(4 * H + kv * VH + j) * TPD] = vget<VH>(vd1[i], j);
             }
         }
 #pragma unroll
         for (int i = 0; i < NXL; ++i) {
             const int k = pt + i * TPC;
-            if (k < C) rsd[k] = vx[i];
+            if (k < C) rsd[k * TPD] = vx[i];
         }
     };
 
-    // B fragments of the r^T da product: LDS offset of gate-unit column n = 16 (nt0 + j) + i16 within a da row
-    int bo[NTW];
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        const int n = 16 * (nt0 + j) + i16;
-        const int g = n / H, k = n - g * H;
-        bo[j] = (nt0 + j < NT && n < G) ? (g < 4 ? 4 * k + g : 4 * H + k) : G;  // column G of a row is zero
-    }
     // dx = sum over d of da_d Wx_d^T on v_mfma_f32_4x4x1f32 (16 blocks of 4 x 4 x 1): block b = lane / 4
     // holds cell group b % 4 (4 cells) of direction b / 4 against 4 input channels, so every lane does
     // useful work with C <= 4 and the direction sum is two cross-lane additions. Each wave takes NPW
-    // consecutive columns of the da rows (same for all four directions); its Wx_d values, permuted to that
-    // column order (column 4k + g holds gate g < 4 of unit k, column 4H + k gate 4), stay in registers.
+    // consecutive gate columns (same for all four directions); its Wx_d values stay in registers.
     const int xd = lane >> 4, xi = lane & 3, xcell = lane & 15;  // block direction; row / channel in block; cell
     const int col0 = wave * NPW;
     float wxr[NC4][NPW];
@@ -259,8 +291,7 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
 #pragma unroll
         for (int sc = 0; sc < NPW; ++sc) {
             const int col = col0 + sc, ch = 4 * g4 + xi;
-            const int n = col < 4 * H ? (col & 3) * H + (col >> 2) : col;
-            wxr[g4][sc] = (col < G && ch < C) ? Wx[((int64_t)xd * C + ch) * G + n] : 0.f;
+            wxr[g4][sc] = (col < G && ch < C) ? Wx[((int64_t)xd * C + ch) * G + col] : 0.f;
         }
     const bool want_dx = dx_flat != nullptr || dx_canvas != nullptr;
 
@@ -281,34 +312,76 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
         }
         write_lds();
         __syncthreads();
-        if (t + 1 < ntiles) issue_loads(sgn, ltn, (t + 1) & 1);
-        const float* rsd = rs + d * TP * RP;
-        const float* dad = das + d * TP * DS;
-#pragma unroll
-        for (int ks = 0; ks < TP / 4; ++ks) {
-            const int c = 4 * ks + q;
-            float af[MT], bf[NTW];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) af[m] = rsd[c * RP + 16 * m + i16];
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) bf[j] = dad[c * DS + bo[j]];
+        // the next tile's loads go out once the products no longer need their registers; they are in flight
+        // through the dx part and the barrier (at hidden sizes whose product leaves room, right away)
+        if (LATE_LOADS == 0 && t + 1 < ntiles) issue_loads(sgn, ltn, (t + 1) & 1);
+        if constexpr (BF) {
+            // A fragment of M tile m: component 16 m + i16 of r over the cells 8q .. 8q + 7; B fragment of N tile
+            // j: gate column 16 (nt0 + j) + i16 over the same cells; both split into three bf16 pieces
+            const float* rsd = rs + (d * RR + i16) * TPD + 8 * q;
+            const float* dad = das + (d * NR + 16 * nt0 + i16) * TPD + 8 * q;
+            u32x4 ap[MT][3];
 #pragma unroll
             for (int m = 0; m < MT; ++m)
+                split3(*reinterpret_cast<const f32x4*>(rsd + 16 * m * TPD),
+                       *reinterpret_cast<const f32x4*>(rsd + 16 * m * TPD + 4), ap[m]);
 #pragma unroll
-                for (int j = 0; j < NTW; ++j)
-                    if (nt0 + j < NT) acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[m], bf[j], acc[m][j], 0, 0, 0);
+            for (int j = 0; j < NTW; ++j) {
+                if (nt0 + j < NT) {
+                    u32x4 bp[3];
+                    split3(*reinterpret_cast<const f32x4*>(dad + 16 * j * TPD),
+                           *reinterpret_cast<const f32x4*>(dad + 16 * j * TPD + 4), bp);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        f32x4 a = acc[m][j];
+                        // the six terms of order <= 2^-16, smallest first
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap[m][2]),
+                                                                    __builtin_bit_cast(bf16x8, bp[0]), a, 0, 0, 0);
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap[m][1]),
+                                                                    __builtin_bit_cast(bf16x8, bp[1]), a, 0, 0, 0);
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap[m][0]),
+                                                                    __builtin_bit_cast(bf16x8, bp[2]), a, 0, 0, 0);
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap[m][1]),
+                                                                    __builtin_bit_cast(bf16x8, bp[0]), a, 0, 0, 0);
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap[m][0]),
+                                                                    __builtin_bit_cast(bf16x8, bp[1]), a, 0, 0, 0);
+                        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ap[m][0]),
+                                                                    __builtin_bit_cast(bf16x8, bp[0]), a, 0, 0, 0);
+                        acc[m][j] = a;
+                    }
+                }
+            }
+        } else {
+            // K step ks: cell 4 ks + q of the tile; A component 16 m + i16, B gate column 16 (nt0 + j) + i16
+            const float* rsd = rs + (d * RR + i16) * TPD + q;
+            const float* dad = das + (d * NR + 16 * nt0 + i16) * TPD + q;
+#pragma unroll
+            for (int ks = 0; ks < TP / 4; ++ks) {
+                float af[MT], bf[NTW];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) af[m] = rsd[16 * m * TPD + 4 * ks];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) bf[j] = nt0 + j < NT ? dad[16 * j * TPD + 4 * ks] : 0.f;
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j)
+                        if (nt0 + j < NT)
+                            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[m], bf[j], acc[m][j], 0, 0, 0);
+            }
         }
+        if (LATE_LOADS != 0 && t + 1 < ntiles) issue_loads(sgn, ltn, (t + 1) & 1);
         // this wave's share of dx for the tile's cells, 16 cells at a time
         if (want_dx) {
 #pragma unroll
             for (int m2 = 0; m2 < TP / 16; ++m2) {
-                const float* arow = das + (xd * TP + 16 * m2 + xcell) * DS + col0;
+                const float* arow = das + (xd * NR + col0) * TPD + 16 * m2 + xcell;
                 f32x4 dacc[NC4];
 #pragma unroll
                 for (int g4 = 0; g4 < NC4; ++g4) dacc[g4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sc = 0; sc < NPW; ++sc) {
-                    const float av = arow[sc];  // columns G .. DS-1 of a row are zero
+                    const float av = arow[sc * TPD];  // gate columns from G on are zero rows
 #pragma unroll
                     for (int g4 = 0; g4 < NC4; ++g4)
                         dacc[g4] = __builtin_amdgcn_mfma_f32_4x4x1f32(av, wxr[g4][sc], dacc[g4], 0, 0, 0);
@@ -363,7 +436,7 @@ template <bool BF16, int C, int H>
 size_t wg2_lds() {
     using S = WgShape<C, H>;
     constexpr size_t TP = S::TP;
-    return 4 * (4 * TP * S::RP + 4 * TP * S::DS + (size_t)S::NWV * TP * C + 4 * TP);
+    return 4 * (4 * (size_t)S::RR * S::TPD + 4 * (size_t)S::NR * S::TPD + (size_t)S::NWV * TP * C + 4 * TP);
 }
 
 typedef void (*Wg2Kernel)(Dev, const void*, const float*, const float*, const float*, float*, float*, float*);
