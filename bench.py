@@ -93,18 +93,21 @@ def kernel_model(info, rects, C, H, x_bytes, nchunks=None, fwd_zero=False, leaky
     rec = (16 if leaky else 10) * H * H * link_count(rects)
     f = 4  # bytes per float
     extra = {}
+    # gate stash floats per cell and direction: (i, f_l, f_u, o) and (g, tanh c, c_l, c_u) per hidden unit; the
+    # Leaky LP cell keeps six values per unit
+    sw = 6 * H if leaky else 8 * H
     if leaky:
         # dVl, dVu: [s_l | s_u]^T da3 over the computed cells of each direction; s_l, s_u and da3 in, partials out
         extra["wgrad_mem"] = (4 * T * (2 * H + 3 * H) * f, 4 * T * 2 * (2 * H) * (3 * H))
     return {**extra,
-        # x (canvas pixels) in for each direction; gate stash (i, f_l, f_u, o, g, c) and h out; the input
-        # projection x Wx + b is computed in the same kernel
-        "fwd_wavefront": (4 * T * (C * x_bytes + 7 * H * f) + (4 * (P - T) * H * f if fwd_zero else 0),
+        # x (canvas pixels) in for each direction; gate stash and h out; the input projection x Wx + b is
+        # computed in the same kernel
+        "fwd_wavefront": (4 * T * (C * x_bytes + (sw + H) * f) + (4 * (P - T) * H * f if fwd_zero else 0),
                           rec + 4 * T * 2 * C * G),
         # four h planes in, y out
         "dirsum": (N * 5 * H * f, 3 * N * H),
         # gate stash and dy in (dy once per direction), dA (5H gate pre-activation gradients) out
-        "bwd_wavefront": (4 * T * (6 * H + G) * f + 4 * N * H * f, rec),
+        "bwd_wavefront": (4 * T * (sw + G) * f + 4 * N * H * f, rec),
         # dA and h in (each h once), x in, dx out, chunk partials out; r^T dA and dA Wx^T on the matrix cores
         "wgrad": (4 * T * (G + H) * f + 4 * T * C * x_bytes + N * C * f + 4 * R * G * f,
                   4 * T * 2 * R * G + 4 * T * 2 * G * C),
@@ -255,15 +258,24 @@ class Runner:
         return start.elapsed_time(stop) / steps, {k: v[0] / v[1] for k, v in per_kernel.items()}
 
     def time(self, steps, warmup):
-        """Untimed warmup, a breakdown pass with every kernel group timed (it names the dominant group), then
-        the timed region, where only the dominant group carries events.
-        Returns (ms per step of the timed region, dominant group, its ms per launch there, breakdown)."""
+        """Untimed warmup; a breakdown pass with every kernel group timed and the weight gradients' overlap
+        with the reverse wavefront switched off, so that each group's time is its own (it names the dominant
+        group); a second breakdown pass with the overlap on (the launch beside the wavefront, mostly waiting,
+        and the rest after it); then the timed region, overlap on, where only the dominant group carries events.
+        Returns (ms per step of the timed region, dominant group, its ms per launch there, breakdown without
+        the overlap, breakdown with it)."""
+        import directional_mdlstm_handwriting_amd as M
         for _ in range(warmup):
             self.step()
-        _, kern = self.run(steps, None)
+        M.mdl_set_wgrad_overlap(False)
+        try:
+            _, kern = self.run(steps, None)
+        finally:
+            M.mdl_set_wgrad_overlap(True)
+        _, kern_ov = self.run(steps, None)
         dom = max(kern, key=kern.get)
         ms, kd = self.run(steps, dom)
-        return ms, dom, kd[dom], kern
+        return ms, dom, kd[dom], kern, kern_ov
 
 
 class SkewRunner:
@@ -494,7 +506,7 @@ def main():
     print(f"bench: {wl.name} packed", file=sys.stderr, flush=True)
     torch.cuda.reset_peak_memory_stats()
     packed = Runner(wl, "packed", device, stream)
-    ms, dom, dom_ms, kern = packed.time(args.steps, args.warmup)
+    ms, dom, dom_ms, kern, kern_ov = packed.time(args.steps, args.warmup)
     info = packed.dl.info
     value = 4 * N / (ms * 1e-3)
 
@@ -535,7 +547,12 @@ def main():
         "roofline": roof,
         "step_roofline": step_roofline(model, bmin, ms),
         "kernels_ms": {k: round(v, 5) for k, v in kern.items()},
-        "kernels_ms_source": "breakdown pass before the timed region, events on every dispatch",
+        "kernels_ms_source": "breakdown pass before the timed region, events on every dispatch, the weight "
+                             "gradients run after the reverse wavefront",
+        "kernels_ms_overlap": {k: round(v, 5) for k, v in kern_ov.items()},
+        "kernels_ms_overlap_source": "second breakdown pass, the weight gradients' overlap on as in the timed "
+                                     "region: wgrad_overlap spans the launch beside the reverse wavefront "
+                                     "(mostly waiting for examples to finish), wgrad the groups left after it",
         "kernels_roofline": {k: {kk: r[kk] for kk in ("bound", "frac", "fp32_frac", "min_bytes_hbm_frac",
                                                        "design_bytes_hbm_frac")}
                              for k, r in per_kernel.items()},
@@ -558,7 +575,7 @@ def main():
         print("bench: word packed", file=sys.stderr, flush=True)
         torch.cuda.reset_peak_memory_stats()
         rw = Runner(ww, "packed", device, stream)
-        wms, _, _, wk = rw.time(args.steps, 2)
+        wms, _, _, wk, _ = rw.time(args.steps, 2)
         peak_packed = torch.cuda.max_memory_allocated()
         wi = rw.dl.info
         wmodel, wbmin, wper = layer_report(rw, ww, wms, wk)
@@ -580,7 +597,7 @@ def main():
             print("bench: word padded", file=sys.stderr, flush=True)
             torch.cuda.reset_peak_memory_stats()
             padded = Runner(ww, "padded", device, stream)
-            pms, _, _, pk = padded.time(max(5, args.steps // 2), 2)
+            pms, _, _, pk, _ = padded.time(max(5, args.steps // 2), 2)
             peak_padded = torch.cuda.max_memory_allocated()
             pinfo = padded.dl.info
             out["packed_vs_padded"] = {
@@ -612,7 +629,7 @@ def main():
                         "skewed_cells": cells, "skewed_padding_fraction": round(1.0 - Nw / cells, 4),
                         "global_depth": Hc + Wc - 1, "cells_per_column": Hc}
             ex = Runner(ww, "exact", device, stream)
-            ems, _, _, ek = ex.time(max(5, args.steps // 2), 2)
+            ems, _, _, ek, _ = ex.time(max(5, args.steps // 2), 2)
             ei = ex.dl.info
             del ex
             torch.cuda.empty_cache()
@@ -667,7 +684,7 @@ def main():
             wk_ = make_workload(nm, args.seed, cell="leaky")
             Nk = int(np.sum(wk_.heights.astype(np.int64) * wk_.widths))
             rk = Runner(wk_, "packed", device, stream)
-            kms, kdom, kdom_ms, kk = rk.time(max(5, args.steps // 2), 2)
+            kms, kdom, kdom_ms, kk, _ = rk.time(max(5, args.steps // 2), 2)
             kmodel, kbmin, kper = layer_report(rk, wk_, kms, kk)
             kroof = roofline(kdom, kdom_ms, kmodel, kbmin, wk_.H)
             kroof["dependent_steps"] = rk.dl.info["max_depth"]

@@ -79,6 +79,7 @@ _SIGS = [
     ("mdl_ctc_head", _I32, [_P, _P, _P, _I32, _P, _P, _I32, _P, _P, ctypes.c_int64, _I32, _P, _P, _P, _P, _P,
                             _SZ, _P]),
     ("mdl_timing", _I32, [_I32]),
+    ("mdl_set_wgrad_overlap", _I32, [_I32]),
     ("mdl_timing_only", _I32, [ctypes.c_char_p]),
     ("mdl_timing_report", _I32, [_I32, _P, _P, _P, ctypes.POINTER(_I32)]),
     ("mdl_last_error", ctypes.c_char_p, []),
@@ -315,6 +316,10 @@ def mdl_blockconv_backward_noalloc(lk: Layout, d_desc_k, lk1: Layout, d_desc_k1,
     _check(_lib.mdl_blockconv_backward_noalloc(lk.handle, _ptr(d_desc_k), lk1.handle, _ptr(d_desc_k1), _ptr(h_dirs_k),
                                                H, kh, kw, _ptr(Wc), Cout, _ptr(dx_canvas_k1), _ptr(dh_dirs_k),
                                                _ptr(dWc), _ptr(dbc), _stream(stream)))
+
+
+def mdl_set_wgrad_overlap(enable: bool):
+    _check(_lib.mdl_set_wgrad_overlap(1 if enable else 0))
 
 
 def mdl_timing(enable: bool):

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <new>
 #include <map>
@@ -34,6 +35,39 @@ int hip_fail(hipError_t e, const char* where) {
 
 const mdl::Layout& L_of(const mdl_layout* l) { return l->L; }
 
+// ints of the workspace's flags region: the overlap's per-example and per-group counters and its queue
+int64_t nflags_of(const mdl::Layout& L) { return (int64_t)L.n + L.ngroups + mdl::kFlagTail; }
+
+// the weight-gradient overlap: on by default; a stream (default priority) and fork / join events per device
+std::atomic<bool> g_overlap{true};
+struct Side {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    int ncu = 0;
+};
+constexpr int kMaxSideDevices = 64;
+int side_of(Side*& out) {
+    static std::mutex mu;
+    static Side sides[kMaxSideDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "mdl_backward: current device");
+    if (dev < 0 || dev >= kMaxSideDevices) return fail(MDL_EUNSUPPORTED, "mdl_backward: device index above 63");
+    std::lock_guard<std::mutex> lk(mu);
+    Side& sd = sides[dev];
+    if (sd.s == nullptr) {
+        Side n;
+        if ((e = hipDeviceGetAttribute(&n.ncu, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess ||
+            (e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess)
+            return hip_fail(e, "mdl_backward: weight-gradient stream");
+        sd = n;
+    }
+    out = &sd;
+    return MDL_OK;
+}
+
 mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     const mdl::Layout& L = L_of(lay);
     const uint8_t* b = static_cast<const uint8_t*>(d_desc);
@@ -45,6 +79,7 @@ mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     D.units = reinterpret_cast<const int32_t*>(b + L.off.units);
     D.segs = reinterpret_cast<const int32_t*>(b + L.off.segs);
     D.groups = reinterpret_cast<const int32_t*>(b + L.off.groups);
+    D.gorder = reinterpret_cast<const int32_t*>(b + L.off.gorder);
     D.eid = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(b + L.off.eid));
     D.border = const_cast<uint8_t*>(b + L.off.border);
     D.n = L.n;
@@ -274,7 +309,7 @@ int mdl_layout_upload(const mdl_layout* layout, void* d_desc, size_t bytes, void
 int mdl_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes) {
     if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_workspace_size: null argument");
     if (C < 1 || H < 1) return fail(MDL_EINVAL, "mdl_workspace_size: need C >= 1 and H >= 1");
-    *bytes = mdl::ws_layout(L_of(layout).computed_cells, L_of(layout).nparts(), C, H).total;
+    *bytes = mdl::ws_layout(L_of(layout).computed_cells, L_of(layout).nparts(), C, H, nflags_of(L_of(layout))).total;
     return MDL_OK;
 }
 
@@ -338,7 +373,7 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
     if ((rc = check_cell("mdl_forward", cell, Vl, Vu))) return rc;
     if (!x_canvas || !Wx || !Ul || !Uu || !b || !h_dirs || !ws) return fail(MDL_EINVAL, "mdl_forward: null tensor");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
     if ((rc = check_extent("mdl_forward", L, C, H, x_dtype, false))) return rc;
     if (cell == MDL_CELL_LEAKY_LP) {
@@ -413,7 +448,7 @@ int mdl_skewed_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, si
     if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_skewed_workspace_size: null argument");
     if (C < 1 || H < 1) return fail(MDL_EINVAL, "mdl_skewed_workspace_size: need C >= 1 and H >= 1");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
     *bytes = skew_dcb_offset(W) + sizeof(float) * 4 * (size_t)L.computed_cells * 2 * H;
     return MDL_OK;
 }
@@ -432,7 +467,7 @@ int mdl_forward_skewed(const mdl_layout* layout, const void* d_desc, const void*
     mdl_skewed_workspace_size(layout, C, H, &need);
     if (ws_bytes < need) return fail(MDL_ESIZE, "mdl_forward_skewed: workspace smaller than mdl_skewed_workspace_size");
     if ((rc = check_extent("mdl_forward_skewed", L, C, H, x_dtype, true))) return rc;
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -481,7 +516,7 @@ int mdl_backward_skewed(const mdl_layout* layout, const void* d_desc, const void
     if ((rc = max_lds(lmax))) return rc;
     if ((wg2 ? mdl::wgrad2_lds_bytes(C, H, x_dtype) : mdl::wgrad_lds_bytes(C, H)) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward_skewed: weight-gradient tile exceeds LDS");
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -503,7 +538,7 @@ int mdl_backward_skewed(const mdl_layout* layout, const void* d_desc, const void
     {
         Timed t("wgrad");
         e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dWx, dUl, dUu, db, dx_flat, dx_canvas,
-                              st);
+                              nullptr, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward_skewed: weight and input gradients");
     return MDL_OK;
@@ -543,7 +578,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     if ((dy_flat == nullptr) == (dh_dirs == nullptr))
         return fail(MDL_EINVAL, "mdl_backward: pass exactly one of dy_flat and dh_dirs");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H);
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_backward: workspace smaller than mdl_workspace_size");
     if (lk && !mdl::leaky_supported(H, C, L.max_diag))
         return fail(MDL_EUNSUPPORTED, "mdl_backward: the Leaky LP cell runs for H in {4, 8, 16, 32}, C <= 16 and a "
@@ -567,12 +602,49 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     const float* stash = reinterpret_cast<const float*>(wsb + W.stash);
     float* part = reinterpret_cast<float*>(wsb + W.part);
     hipError_t e;
+    // The weight gradient overlaps the reverse wavefront when the wavefront's units leave at least half of
+    // the compute units free: each unit counts itself on its example when done, and persistent workgroups
+    // on a second stream take the weight-gradient groups whose examples are done; the launch after the
+    // wavefront does the rest. Each group is computed by the same code either way.
+    Side* side = nullptr;
+    int ov_wg = 0;
+    if (!lk && g_overlap.load() && wg2 && mdl::bwd16_supported(H, L.max_diag)) {
+        if ((rc = side_of(side))) return rc;
+        const int free_cu = side->ncu - 4 * L.n;
+        if (2 * free_cu >= side->ncu) ov_wg = std::min(free_cu, (int)L.ngroups);
+    }
+    mdl::OverlapFlags F{};
+    if (ov_wg > 0) {
+        int32_t* fl = reinterpret_cast<int32_t*>(wsb + W.flags);
+        F.done = fl;
+        F.processed = fl + L.n;
+        F.queue = fl + L.n + L.ngroups;
+        F.stop = F.queue + 1;
+        if ((e = mdl::launch_fill_i32(fl, nflags_of(L), 0, st)) != hipSuccess)
+            return hip_fail(e, "mdl_backward: overlap counters");
+        if ((e = hipEventRecord(side->fork, st)) != hipSuccess || (e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess)
+            return hip_fail(e, "mdl_backward: fork to the weight-gradient stream");
+    }
     {
         Timed t("bwd_wavefront");
         e = lk ? mdl::launch_bwd_leaky(D, H, Ul, Uu, Vl, Vu, stash, dy_flat, dh_dirs, dA, st)
-               : mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
+           : ov_wg > 0 ? mdl::launch_bwd16(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, F.done, st)
+                       : mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward: reverse wavefront");
+    if (ov_wg > 0) {
+        // each wait at most ~2^15 clock cycles per dependent step of the layout (several times the reverse
+        // wavefront's own time per step), at least 2^26 cycles
+        const long long budget = std::max<long long>(1ll << 26, (long long)L.max_depth << 15);
+        {
+            Timed t("wgrad_overlap");
+            e = mdl::launch_wgrad2_overlap(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dx_flat, dx_canvas, F,
+                                           ov_wg, budget, side->s);
+        }
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward: overlapping weight gradients");
+        if ((e = hipEventRecord(side->join, side->s)) != hipSuccess || (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess)
+            return hip_fail(e, "mdl_backward: join from the weight-gradient stream");
+    }
     if (dx_canvas) {
         Timed t("zero_fill");
         e = mdl::launch_zero_outside(D, dx_canvas, C, 1, st);
@@ -581,7 +653,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     {
         Timed t("wgrad");
         e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dWx, dUl, dUu, db, dx_flat, dx_canvas,
-                              st);
+                              ov_wg > 0 ? F.processed : nullptr, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight and input gradients");
     if (lk) {
@@ -765,6 +837,11 @@ int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_fl
     if (e != hipSuccess) return hip_fail(e, "mdl_ctc_head");
     return MDL_OK;
     GUARD_END
+}
+
+int mdl_set_wgrad_overlap(int32_t enable) {
+    g_overlap.store(enable != 0);
+    return MDL_OK;
 }
 
 int mdl_timing(int32_t enable) {

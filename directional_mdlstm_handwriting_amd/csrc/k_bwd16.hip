@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
                                                                  const float* __restrict__ stash,
                                                                  const float* __restrict__ dy_flat,
                                                                  const float* __restrict__ dh_dirs,
-                                                                 float* __restrict__ dA) {
+                                                                 float* __restrict__ dA, int32_t* __restrict__ done) {
     using Sh = B16Shape<H>;
     constexpr int NB = Sh::NB, HE = Sh::HE, CG = Sh::CG, KP = Sh::KP, KT = Sh::KT, HP2 = HE / 2;
     constexpr int G = 5 * H;
@@ -236,9 +236,7 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
             __syncthreads();  // X and Y of diagonal s + 1 are in LDS
             __syncthreads();  // the element waves have written diagonal s's gate gradients
         }
-        return;
-    }
-
+    } else {
     // ================= element role =================
     // Each thread owns NE pairs of adjacent hidden units (2m, 2m + 1) of one diagonal position: the HE / 2
     // lanes of a cell sit in one DPP row (H = 32) or half-row (H = 16), and each gate's f16 pair goes to
@@ -479,9 +477,18 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
     if (s - 1 >= 0) step(s - 1, IC<1>{});
     if constexpr (NS > 3)
         if (s - 2 >= 0) step(s - 2, IC<2>{});
+    }
+    // The unit is done: once every wave's gate-gradient stores are visible device-wide, count it on its
+    // example (the weight gradient may then start on the example's cells while other units still run).
+    if (done != nullptr) {
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(done + e, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-typedef void (*Bwd16Kernel)(Dev, const float*, const float*, const float*, const float*, const float*, float*);
+typedef void (*Bwd16Kernel)(Dev, const float*, const float*, const float*, const float*, const float*, float*,
+                            int32_t*);
 
 // hidden sizes of the workloads, each with its (unit pairs per thread, element waves) shapes in order of
 // preference: the smallest workgroup that covers the widest diagonal
@@ -534,12 +541,12 @@ size_t bwd16_lds(int H, int Lmax) {
 }
 
 hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
-                        const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st) {
+                        const float* dy_flat, const float* dh_dirs, float* dA, int32_t* done, hipStream_t st) {
     const B16Entry* m = b16_entry(H, D.max_diag);
     if (!m) return hipErrorInvalidValue;
     const B16Shape2* sh = b16_shape(*m, D.max_diag);
     launch(sh->k, dim3(4 * D.n), dim3(64 * (kMatWaves + sh->EW)), b16_lds(*m), st, D, Ul, Uu, stash, dy_flat,
-           dh_dirs, dA);
+           dh_dirs, dA, done);
     return hipGetLastError();
 }
 

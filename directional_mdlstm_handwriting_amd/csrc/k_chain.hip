@@ -466,7 +466,7 @@ hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* U
                             const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st) {
     const int Lmax = D.max_diag;
     if (small_bwd_supported(H, Lmax)) return launch_bwd_small(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
-    if (bwd16_supported(H, Lmax)) return launch_bwd16(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
+    if (bwd16_supported(H, Lmax)) return launch_bwd16(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, nullptr, st);
     if (const MfmaEntry* m = mfma_entry(H, Lmax)) {
         launch(m->bwd, dim3(4 * D.n), dim3(256), bwd_mfma_lds(H, Lmax), st, D, H, Lmax, Ul, Uu, stash,
                dy_flat, dh_dirs, dA);

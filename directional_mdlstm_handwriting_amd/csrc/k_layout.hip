@@ -25,6 +25,11 @@ __global__ void k_fill_eid(int32_t* __restrict__ eid, int64_t P) {
         eid[p] = -1;
 }
 
+__global__ void k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
 // blockIdx.y = example; paints its computed region
 __global__ void k_paint_eid(Dev D) {
     const int e = blockIdx.y;
@@ -170,6 +175,11 @@ hipError_t launch_zero_outside(const Dev& D, float* buf, int K, int planes, hipS
     } else {
         launch(k_zero_outside, dim3(grid_for(E)), dim3(TPB), 0, st, D, buf, K, planes);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+    launch(k_fill_i32, dim3(grid_for(n)), dim3(TPB), 0, st, p, n, v);
     return hipGetLastError();
 }
 

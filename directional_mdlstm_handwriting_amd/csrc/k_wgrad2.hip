@@ -125,14 +125,12 @@ __device__ inline int stash_pos(int h, int w, int ly, int lx, int d) {
     return (int)dg_start(h, w, s) + (a - dg_lo(h, w, s));
 }
 
+// One workgroup's group grp: its partial sums and the input gradient of its cells.
 template <bool BF16, int C, int H>
-__global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, const void* __restrict__ xc,
-                                                                      const float* __restrict__ hdirs,
-                                                                      const float* __restrict__ dA,
-                                                                      const float* __restrict__ Wx,
-                                                                      float* __restrict__ part,
-                                                                      float* __restrict__ dx_flat,
-                                                                      float* __restrict__ dx_canvas) {
+__device__ __forceinline__ void wgrad_group(const Dev& D, const void* __restrict__ xc, const float* __restrict__ hdirs,
+                                            const float* __restrict__ dA, const float* __restrict__ Wx,
+                                            float* __restrict__ part, float* __restrict__ dx_flat,
+                                            float* __restrict__ dx_canvas, const int grp) {
     using S = WgShape<C, H>;
     constexpr int G = S::G, R = S::R, MT = S::MT, NT = S::NT, WPD = S::WPD, NTW = S::NTW, TP = S::TP;
     constexpr int RR = S::RR, NR = S::NR, TPD = S::TPD, VH = S::VH, NTH = S::NTH, NWV = S::NWV, NPW = S::NPW,
@@ -142,7 +140,6 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
     constexpr bool BF = S::BF;
     constexpr int XB = BF16 ? 2 : 4;
     typedef typename VecOf<VH>::T HV;
-    const int grp = blockIdx.x;
     const int sg0 = D.groups[grp], nsg = D.groups[grp + 1] - sg0;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave descriptors
@@ -432,6 +429,80 @@ __global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, co
         }
 }
 
+// one workgroup per group; groups whose processed flag is set (done by the overlapping launch) are skipped
+template <bool BF16, int C, int H>
+__global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2(Dev D, const void* __restrict__ xc,
+                                                                      const float* __restrict__ hdirs,
+                                                                      const float* __restrict__ dA,
+                                                                      const float* __restrict__ Wx,
+                                                                      float* __restrict__ part,
+                                                                      float* __restrict__ dx_flat,
+                                                                      float* __restrict__ dx_canvas,
+                                                                      const int32_t* __restrict__ processed) {
+    const int grp = blockIdx.x;
+    if (processed != nullptr && processed[grp] != 0) return;
+    wgrad_group<BF16, C, H>(D, xc, hdirs, dA, Wx, part, dx_flat, dx_canvas, grp);
+}
+
+// Thread 0 of an overlapping workgroup claims the next group in readiness order and waits until every
+// reverse-wavefront unit of its examples has finished. The counters are polled without ordering (no cache
+// invalidation per poll); one acquire fence once they are all complete orders the group's reads after the
+// units' stores. Each wait is bounded by `budget` shader-clock cycles; a group not ready by then is left to
+// the launch that follows the reverse wavefront, and the stop flag ends all claiming. Returns the group, or -1.
+__device__ int claim_ready_group(const Dev& D, const OverlapFlags& F, long long budget) {
+    if (__hip_atomic_load(F.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return -1;
+    const int qi = __hip_atomic_fetch_add(F.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (qi >= D.ngroups) return -1;
+    const int g = D.gorder[qi];
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    for (int sg = D.groups[g]; sg < D.groups[g + 1]; ++sg) {
+        const int e = D.segs[3 * sg];
+        while (__hip_atomic_load(F.done + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < 4) {
+            if ((long long)(__builtin_amdgcn_s_memtime() - t0) > budget) {
+                __hip_atomic_store(F.stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return -1;
+            }
+            __builtin_amdgcn_s_sleep(16);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return g;
+}
+
+// The weight gradient beside the reverse wavefront: a few persistent workgroups (on the compute units the
+// wavefront leaves free) take the groups in the order their examples finish, each after that example's
+// four units have signalled; every group they complete is marked processed.
+template <bool BF16, int C, int H>
+__global__ __launch_bounds__((256 * WgShape<C, H>::WPD)) void k_wgrad2_overlap(Dev D, const void* __restrict__ xc,
+                                                                              const float* __restrict__ hdirs,
+                                                                              const float* __restrict__ dA,
+                                                                              const float* __restrict__ Wx,
+                                                                              float* __restrict__ part,
+                                                                              float* __restrict__ dx_flat,
+                                                                              float* __restrict__ dx_canvas,
+                                                                              OverlapFlags F, long long budget) {
+    __shared__ int s_grp;
+    // Thread 0's work of an iteration (mark the group finished last, claim the next) is one region between
+    // barriers. Two separate thread-0 regions, one at the end of an iteration and one at the start of the
+    // next, may be merged across the loop's back edge by the compiler into a path on which thread 0 leaves
+    // the loop body while the rest of its wave goes on to the next barrier without it.
+    int prev = -1;  // the group this workgroup finished last (the same in every thread)
+    for (;;) {
+        if (threadIdx.x == 0) {
+            if (prev >= 0) __hip_atomic_store(F.processed + prev, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            s_grp = claim_ready_group(D, F, budget);
+        }
+        __syncthreads();
+        const int g = s_grp;
+        __syncthreads();
+        if (g < 0) break;
+        wgrad_group<BF16, C, H>(D, xc, hdirs, dA, Wx, part, dx_flat, dx_canvas, g);
+        __threadfence();  // the group's partial sums and dx before its processed flag
+        __syncthreads();
+        prev = g;
+    }
+}
+
 template <bool BF16, int C, int H>
 size_t wg2_lds() {
     using S = WgShape<C, H>;
@@ -439,15 +510,20 @@ size_t wg2_lds() {
     return 4 * (4 * (size_t)S::RR * S::TPD + 4 * (size_t)S::NR * S::TPD + (size_t)S::NWV * TP * C + 4 * TP);
 }
 
-typedef void (*Wg2Kernel)(Dev, const void*, const float*, const float*, const float*, float*, float*, float*);
+typedef void (*Wg2Kernel)(Dev, const void*, const float*, const float*, const float*, float*, float*, float*,
+                          const int32_t*);
+typedef void (*Wg2OverlapKernel)(Dev, const void*, const float*, const float*, const float*, float*, float*, float*,
+                                 OverlapFlags, long long);
 
 struct Wg2Entry {
     bool bf16;
     int C, H, threads;
     size_t lds;
     Wg2Kernel k;
+    Wg2OverlapKernel ko;
 };
-#define MDL_WG2(bf, c, h) {bf, c, h, 256 * WgShape<c, h>::WPD, wg2_lds<bf, c, h>(), k_wgrad2<bf, c, h>}
+#define MDL_WG2(bf, c, h) \
+    {bf, c, h, 256 * WgShape<c, h>::WPD, wg2_lds<bf, c, h>(), k_wgrad2<bf, c, h>, k_wgrad2_overlap<bf, c, h>}
 const Wg2Entry* wg2_entry(int C, int H, bool bf16) {
     static const Wg2Entry table[] = {MDL_WG2(false, 4, 16), MDL_WG2(true, 4, 16), MDL_WG2(false, 4, 32),
                                      MDL_WG2(true, 4, 32),  MDL_WG2(false, 4, 2), MDL_WG2(false, 6, 10),
@@ -469,11 +545,21 @@ size_t wgrad2_lds_bytes(int C, int H, int dtype) {
 
 hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
                          const float* dA, const float* Wx, float* part, float* dx_flat, float* dx_canvas,
-                         hipStream_t st) {
+                         const int32_t* processed, hipStream_t st) {
     const Wg2Entry* m = wg2_entry(C, H, dtype != 0);
     if (!m) return hipErrorInvalidValue;
     launch(m->k, dim3((unsigned)D.ngroups), dim3(m->threads), m->lds, st, D, x_canvas, h_dirs, dA, Wx,
-           part, dx_flat, dx_canvas);
+           part, dx_flat, dx_canvas, processed);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad2_overlap(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
+                                 const float* dA, const float* Wx, float* part, float* dx_flat, float* dx_canvas,
+                                 const OverlapFlags& F, int workgroups, long long budget, hipStream_t st) {
+    const Wg2Entry* m = wg2_entry(C, H, dtype != 0);
+    if (!m || workgroups < 1) return hipErrorInvalidValue;
+    launch(m->ko, dim3((unsigned)workgroups), dim3(m->threads), m->lds, st, D, x_canvas, h_dirs, dA, Wx, part,
+           dx_flat, dx_canvas, F, budget);
     return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@ struct Dev {
     const int32_t* units;     // [4n]
     const int32_t* segs;      // [nsegs][3] (example, first cell, end cell)
     const int32_t* groups;    // [ngroups+1] first segment of each weight-gradient workgroup
+    const int32_t* gorder;    // [ngroups] the groups in the order their examples finish the reverse wavefront
     int32_t* eid;             // [Hc*Wc]
     uint8_t* border;          // [Hc*Wc]
     int n, Hc, Wc;
@@ -122,13 +123,24 @@ struct WsLayout {
     size_t stash = 0;   // float [4][T][8H]: SA then SB, the forward values of every cell the reverse wavefront needs
     size_t zda = 0;     // float [4][T][5H]: projection x.Wx+b (forward), gate gradients dA (backward)
     size_t part = 0;    // float [nparts][4][(C+1+2H)*5H]: weight-gradient partial sums
+    size_t flags = 0;   // int32 [n + ngroups + kFlagTail]: the weight-gradient overlap's counters (OverlapFlags)
     size_t total = 0;
     int64_t nparts = 0;
 };
-WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H);
+constexpr int kFlagTail = 16;
+WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H, int64_t nflags);
+// the counters of the weight gradient's overlap with the reverse wavefront, in the workspace's flags region
+struct OverlapFlags {
+    int32_t* done;       // [n] reverse-wavefront units of each example that have finished (0..4)
+    int32_t* processed;  // [ngroups] 1 once the overlapping launch has written the group's partial sums
+    int32_t* queue;      // the next position of gorder to claim
+    int32_t* stop;       // set once a group was not ready in time: the overlapping launch claims no more
+};
 
 // launchers: return hipSuccess or the launch error
 hipError_t launch_build_maps(const Dev& D, hipStream_t st);
+// n ints set to v by a kernel (no memset node, so a captured graph replays it as a kernel)
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 hipError_t launch_zero_outside(const Dev& D, float* buf, int K, int planes, hipStream_t st);
 hipError_t launch_scatter(const Dev& D, const void* x_flat, int C, int dtype, void* x_canvas, hipStream_t st);
 hipError_t launch_projection(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
@@ -147,8 +159,9 @@ hipError_t launch_fwd16(const Dev& D, const void* x_canvas, int dtype, int C, in
 // reverse wavefront on the f16 matrix cores (split, power-of-two scaled operands)
 bool bwd16_supported(int H, int Lmax);
 size_t bwd16_lds(int H, int Lmax);
+// done (may be null): per-example counters, each unit adds 1 to its example's when its stores are visible
 hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
-                        const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
+                        const float* dy_flat, const float* dh_dirs, float* dA, int32_t* done, hipStream_t st);
 // wavefront kernels for small hidden sizes (H <= 10) on the vector ALUs, fp32, input projection fused
 bool small_fwd_supported(int H, int C, int dtype, int Lmax);
 bool small_bwd_supported(int H, int Lmax);
@@ -167,13 +180,21 @@ hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* U
 // software-pipelined weight-gradient kernel for the instantiated (C, H, dtype) shapes
 bool wgrad2_supported(int C, int H, int dtype);
 size_t wgrad2_lds_bytes(int C, int H, int dtype);
+// processed (may be null): groups whose flag is set were done by launch_wgrad2_overlap and are skipped
 hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
                          const float* dA, const float* Wx, float* part, float* dx_flat, float* dx_canvas,
-                         hipStream_t st);
+                         const int32_t* processed, hipStream_t st);
+// the same groups beside the reverse wavefront: `workgroups` persistent workgroups claim groups in the
+// layout's readiness order once the examples' units have counted themselves in F.done (each wait bounded
+// by `budget` shader-clock cycles) and mark the groups they complete in F.processed
+hipError_t launch_wgrad2_overlap(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
+                                 const float* dA, const float* Wx, float* part, float* dx_flat, float* dx_canvas,
+                                 const OverlapFlags& F, int workgroups, long long budget, hipStream_t st);
 size_t wgrad_lds_bytes(int C, int H);
+// processed: as for launch_wgrad2 (only with a shape launch_wgrad2 supports)
 hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
                         const float* dA, const float* Wx, float* part, float* dWx, float* dUl, float* dUu, float* db,
-                        float* dx_flat, float* dx_canvas, hipStream_t st);
+                        float* dx_flat, float* dx_canvas, const int32_t* processed, hipStream_t st);
 hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st);
 int64_t conv_nchunks(const Dev& Dk1);

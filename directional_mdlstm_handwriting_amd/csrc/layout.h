@@ -53,6 +53,7 @@ struct DescOffsets {
     size_t units = 0;     // int32 [4n] (example*4 + direction), most cells first
     size_t segs = 0;      // int32 [nsegs][3] (example, first cell, end cell) of the weight-gradient split
     size_t groups = 0;    // int32 [ngroups+1] first segment of each weight-gradient workgroup
+    size_t gorder = 0;    // int32 [ngroups] the groups in the order their examples finish the reverse wavefront
     size_t eid = 0;       // int32 [Hc*Wc]
     size_t border = 0;    // uint8 [Hc*Wc]
     size_t total = 0;
@@ -76,6 +77,9 @@ struct Layout {
     // take one segment per workgroup), so nparts() = max(nsegs, ngroups) partial blocks.
     std::vector<int32_t> segs;
     std::vector<int32_t> groups;
+    // the groups ordered by the largest dependent-step count (h + w - 1) of their examples, ties by index:
+    // the order in which they become ready while the reverse wavefront runs (its units all start together)
+    std::vector<int32_t> gorder;
     int32_t nsegs = 0, ngroups = 0;
     int64_t nparts() const { return nsegs > ngroups ? nsegs : ngroups; }
     DescOffsets off;

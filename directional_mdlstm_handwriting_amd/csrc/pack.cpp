@@ -78,6 +78,15 @@ void split_wgrad(Layout& L) {
     }
     L.nsegs = (int32_t)(L.segs.size() / 3);
     L.ngroups = (int32_t)L.groups.size() - 1;
+    std::vector<int32_t> key(L.ngroups, 0);
+    for (int g = 0; g < L.ngroups; ++g)
+        for (int sg = L.groups[g]; sg < L.groups[g + 1]; ++sg) {
+            const int32_t* r = &L.rect[4 * L.segs[3 * sg]];
+            key[g] = std::max(key[g], r[2] + r[3] - 1);
+        }
+    L.gorder.resize(L.ngroups);
+    std::iota(L.gorder.begin(), L.gorder.end(), 0);
+    std::stable_sort(L.gorder.begin(), L.gorder.end(), [&](int32_t a, int32_t b) { return key[a] < key[b]; });
 }
 
 void finish(Layout& L) {
@@ -117,6 +126,7 @@ void finish(Layout& L) {
     o.units = p;    p = align256(p + sizeof(int32_t) * 4 * n);
     o.segs = p;     p = align256(p + sizeof(int32_t) * L.segs.size());
     o.groups = p;   p = align256(p + sizeof(int32_t) * L.groups.size());
+    o.gorder = p;   p = align256(p + sizeof(int32_t) * L.gorder.size());
     o.eid = p;      p = align256(p + sizeof(int32_t) * (size_t)L.Hc * L.Wc);
     o.border = p;   p = align256(p + (size_t)L.Hc * L.Wc);
     o.total = p;
@@ -128,6 +138,7 @@ void finish(Layout& L) {
     std::memcpy(&L.host_desc[o.units], L.units.data(), sizeof(int32_t) * 4 * n);
     std::memcpy(&L.host_desc[o.segs], L.segs.data(), sizeof(int32_t) * L.segs.size());
     std::memcpy(&L.host_desc[o.groups], L.groups.data(), sizeof(int32_t) * L.groups.size());
+    std::memcpy(&L.host_desc[o.gorder], L.gorder.data(), sizeof(int32_t) * L.gorder.size());
 }
 
 }  // namespace

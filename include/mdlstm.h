@@ -284,6 +284,17 @@ int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float*
  *   MDL_CELL_LEAKY_LP also dVl, dVu shaped like Vl, Vu (NULL, with Vl and Vu,
  *   for the plain cell).
  * Weight gradients are fixed-order blocked sums over all computed cells.
+ * When the reverse wavefront's (example, direction) units leave at least half
+ * of the device's compute units free (and the f16 wavefront and the
+ * weight-gradient kernel cover H, C and the input type), the weight gradient
+ * overlaps the wavefront: every unit counts itself on its example when its
+ * gate gradients are stored, and persistent workgroups on a stream of the
+ * library's own (one per device, forked from and joined back into `stream`
+ * with events) compute the weight-gradient blocks whose examples are done;
+ * the blocks left over are computed after the wavefront. Each block is
+ * computed by the same code either way, so the results are the same bit for
+ * bit; every wait is bounded. Overlapping calls on one device share that
+ * stream (and a workspace must not be shared by calls that may overlap).
  * MDL_EUNSUPPORTED under the same size limits as mdl_forward and when one
  * direction's gate gradients (T*5H floats, T = computed cells) reach 2 GiB.
  */
@@ -385,7 +396,8 @@ int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_fl
 /*
  * Kernel timing (measurement support). mdl_timing(1) makes every later launch
  * of a kernel group (names: "build_maps", "scatter", "zero_fill", "projection",
- * "fwd_wavefront", "dirsum", "bwd_wavefront", "wgrad", "conv_fwd", "conv_bwd",
+ * "fwd_wavefront", "dirsum", "bwd_wavefront", "wgrad_overlap" (on the library's
+ * own stream, concurrent with "bwd_wavefront"), "wgrad", "conv_fwd", "conv_bwd",
  * "ctc_head")
  * hand each of its dispatches a HIP event pair that the dispatch itself
  * records (hipExtLaunchKernel): the group's time runs from its first
@@ -402,6 +414,10 @@ int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_fl
  */
 int mdl_timing(int32_t enable);
 int mdl_timing_only(const char* group);
+
+/* Turns the weight gradient's overlap with the reverse wavefront (mdl_backward) on (default) or off,
+ * process-wide; the results do not depend on it. Always MDL_OK. */
+int mdl_set_wgrad_overlap(int32_t enable);
 int mdl_timing_report(int32_t max, char* names, double* total_ms, int64_t* launches, int32_t* count);
 
 /* Message of the last failed call on this thread ("" if none). */

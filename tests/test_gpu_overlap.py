@@ -1,0 +1,69 @@
+"""The weight gradient's overlap with the reverse wavefront changes no result.
+
+mdl_backward lets persistent weight-gradient workgroups run beside the reverse wavefront (on the compute
+units its units leave free) and computes the blocks they did not get to after it; every block goes through
+the same code, so the gradients must equal, bit for bit, those of a call with the overlap switched off.
+Checked on the line batch (32 examples, 128 units: the overlap runs) and on a small batch, with the flat and
+the canvas input gradient; a second backward with the overlap on repeats the first exactly (the counters and
+the claim queue start from zero on every call).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from test_gpu_parity import DEV, run_layer
+from workloads import cotangent, make_workload, random_layer
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import directional_mdlstm_handwriting_amd as M
+    from directional_mdlstm_handwriting_amd.layer import DeviceParams, LayerGrads
+
+
+def _backward(out, P, dys, overlap):
+    M.mdl_set_wgrad_overlap(overlap)
+    try:
+        lay, dl = out["layer"], out["dl"]
+        Pd = DeviceParams.from_host(P, DEV)
+        dy = torch.as_tensor(np.concatenate([d.reshape(-1) for d in dys]).astype(np.float32), device=DEV)
+        g = LayerGrads(*(torch.full_like(t, float("nan")) for t in (Pd.Wx, Pd.Ul, Pd.Uu, Pd.b)))
+        n_in = int(out["dx"].numel())
+        dx = torch.full((n_in,), float("nan"), device=DEV)
+        dxc = torch.full((dl.info["canvas_h"], dl.info["canvas_w"], P.C), float("nan"), device=DEV)
+        lay.backward(Pd, g, dy_flat=dy, dx_flat=dx, dx_canvas=dxc)
+        torch.cuda.synchronize()
+        return [t.cpu().numpy() for t in (g.dWx, g.dUl, g.dUu, g.db, dx, dxc)]
+    finally:
+        M.mdl_set_wgrad_overlap(True)
+
+
+def _check(name, heights, widths, xs, P, x_dtype="f32", sep=1, canvas_w_min=None):
+    dys = cotangent(5, heights, widths, P.H)
+    out = run_layer(heights, widths, xs, P, x_dtype=x_dtype, sep=sep, canvas_w_min=canvas_w_min, dys=dys)
+    print(f"[gpu] overlap on / off: {name}", flush=True)
+    a = _backward(out, P, dys, True)
+    b = _backward(out, P, dys, False)
+    c = _backward(out, P, dys, True)
+    for nm, x, y, z in zip(("dWx", "dUl", "dUu", "db", "dx", "dx_canvas"), a, b, c):
+        assert np.all(np.isfinite(x)), f"{name} {nm}: non-finite values"
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"{name} {nm}: overlap changed the result"
+        assert np.array_equal(x.view(np.uint32), z.view(np.uint32)), f"{name} {nm}: repeated call differs"
+
+
+def test_overlap_line_batch():
+    wl = make_workload("line", 0)
+    _check("line", wl.heights, wl.widths, wl.xs, wl.layers[0], x_dtype=wl.x_dtype, sep=wl.sep,
+           canvas_w_min=wl.canvas_w_min[0])
+
+
+@pytest.mark.parametrize("H", [16, 32])
+def test_overlap_small_batch(H):
+    rng = np.random.default_rng(40 + H)
+    heights = rng.integers(3, 19, size=9)
+    widths = rng.integers(3, 41, size=9)
+    C = 4
+    xs = [rng.standard_normal((int(h), int(w), C)).astype(np.float32) for h, w in zip(heights, widths)]
+    P = random_layer(H, C, H)
+    _check(f"9 examples, H={H}", heights, widths, xs, P)
