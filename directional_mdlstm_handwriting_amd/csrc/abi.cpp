@@ -35,8 +35,8 @@ int hip_fail(hipError_t e, const char* where) {
 
 const mdl::Layout& L_of(const mdl_layout* l) { return l->L; }
 
-// ints of the workspace's flags region: the overlap's per-example and per-group counters and its queue
-int64_t nflags_of(const mdl::Layout& L) { return (int64_t)L.n + L.ngroups + mdl::kFlagTail; }
+// ints of the workspace's flags region: the overlap's per-unit and per-task flags and its counters
+int64_t nflags_of(const mdl::Layout& L) { return 4 * (int64_t)L.n + 8 * (int64_t)L.ngroups + mdl::kFlagTail; }
 
 // the weight-gradient overlap: on by default; a stream (default priority) and fork / join events per device
 std::atomic<bool> g_overlap{true};
@@ -523,6 +523,7 @@ int mdl_backward_skewed(const mdl_layout* layout, const void* d_desc, const void
     float* dA = reinterpret_cast<float*>(wsb + W.zda);
     const float* stash = reinterpret_cast<const float*>(wsb + W.stash);
     float* part = reinterpret_cast<float*>(wsb + W.part);
+    float* dxp = reinterpret_cast<float*>(wsb + W.dxp);
     float* dcb = reinterpret_cast<float*>(wsb + skew_dcb_offset(W));
     hipError_t e;
     {
@@ -537,8 +538,8 @@ int mdl_backward_skewed(const mdl_layout* layout, const void* d_desc, const void
     }
     {
         Timed t("wgrad");
-        e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dWx, dUl, dUu, db, dx_flat, dx_canvas,
-                              nullptr, st);
+        e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dxp, dWx, dUl, dUu, db, dx_flat,
+                              dx_canvas, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward_skewed: weight and input gradients");
     return MDL_OK;
@@ -601,25 +602,33 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     float* dA = reinterpret_cast<float*>(wsb + W.zda);
     const float* stash = reinterpret_cast<const float*>(wsb + W.stash);
     float* part = reinterpret_cast<float*>(wsb + W.part);
+    float* dxp = reinterpret_cast<float*>(wsb + W.dxp);
+    const bool want_dx = dx_flat != nullptr || dx_canvas != nullptr;
     hipError_t e;
     // The weight gradient overlaps the reverse wavefront when the wavefront's units leave at least half of
-    // the compute units free: each unit counts itself on its example when done, and persistent workgroups
-    // on a second stream take the weight-gradient groups whose examples are done; the launch after the
-    // wavefront does the rest. Each group is computed by the same code either way.
+    // the compute units free: each unit flags itself when done, and persistent workgroups on a second
+    // stream (one per free compute unit, so the wavefront's units always find room) take the weight-gradient
+    // tasks (one direction of one group) from a claim queue, in the order their units finish, once those
+    // units are done. The launch after the wavefront takes the rest of the queue on every compute unit while
+    // they finish their last tasks; a third launch, after both, does any task given up beside the wavefront
+    // for want of time. Each task is computed by the same code either way.
     Side* side = nullptr;
     int ov_wg = 0;
     if (!lk && g_overlap.load() && wg2 && mdl::bwd16_supported(H, L.max_diag)) {
         if ((rc = side_of(side))) return rc;
         const int free_cu = side->ncu - 4 * L.n;
-        if (2 * free_cu >= side->ncu) ov_wg = std::min(free_cu, (int)L.ngroups);
+        if (2 * free_cu >= side->ncu) ov_wg = std::min(free_cu, 4 * (int)L.ngroups);
     }
     mdl::OverlapFlags F{};
     if (ov_wg > 0) {
         int32_t* fl = reinterpret_cast<int32_t*>(wsb + W.flags);
         F.done = fl;
-        F.processed = fl + L.n;
-        F.queue = fl + L.n + L.ngroups;
+        F.taken = fl + 4 * L.n;
+        F.abandoned = F.taken + 4 * L.ngroups;
+        F.queue = F.abandoned + 4 * L.ngroups;
         F.stop = F.queue + 1;
+        F.nab = F.queue + 2;
+        F.abq = F.queue + 3;
         if ((e = mdl::launch_fill_i32(fl, nflags_of(L), 0, st)) != hipSuccess)
             return hip_fail(e, "mdl_backward: overlap counters");
         if ((e = hipEventRecord(side->fork, st)) != hipSuccess || (e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess)
@@ -632,30 +641,40 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
                        : mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     }
     if (e != hipSuccess) return hip_fail(e, "mdl_backward: reverse wavefront");
+    if (dx_canvas) {
+        Timed t("zero_fill");
+        e = mdl::launch_zero_outside(D, dx_canvas, C, 1, st);
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward: zero fill");
+    }
     if (ov_wg > 0) {
         // each wait at most ~2^15 clock cycles per dependent step of the layout (several times the reverse
         // wavefront's own time per step), at least 2^26 cycles
         const long long budget = std::max<long long>(1ll << 26, (long long)L.max_depth << 15);
         {
             Timed t("wgrad_overlap");
-            e = mdl::launch_wgrad2_overlap(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dx_flat, dx_canvas, F,
-                                           ov_wg, budget, side->s);
+            e = mdl::launch_wgrad2_claim(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, want_dx ? dxp : nullptr,
+                                         F, mdl::kClaimBeside, ov_wg, budget, side->s);
         }
-        if (e != hipSuccess) return hip_fail(e, "mdl_backward: overlapping weight gradients");
-        if ((e = hipEventRecord(side->join, side->s)) != hipSuccess || (e = hipStreamWaitEvent(st, side->join, 0)) != hipSuccess)
-            return hip_fail(e, "mdl_backward: join from the weight-gradient stream");
-    }
-    if (dx_canvas) {
-        Timed t("zero_fill");
-        e = mdl::launch_zero_outside(D, dx_canvas, C, 1, st);
-        if (e != hipSuccess) return hip_fail(e, "mdl_backward: zero fill");
-    }
-    {
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight gradients beside the reverse wavefront");
+        if ((e = hipEventRecord(side->join, side->s)) != hipSuccess)
+            return hip_fail(e, "mdl_backward: weight-gradient stream");
+        {
+            Timed t("wgrad");
+            e = mdl::launch_wgrad2_claim(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, want_dx ? dxp : nullptr,
+                                         F, mdl::kClaimDrain, 0, 0, st);
+            if (e == hipSuccess && (e = hipStreamWaitEvent(st, side->join, 0)) == hipSuccess)
+                e = mdl::launch_wgrad2_claim(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part,
+                                             want_dx ? dxp : nullptr, F, mdl::kClaimAbandoned, 16, 0, st);
+            if (e == hipSuccess) e = mdl::launch_dx_sum(D, C, dxp, dx_flat, dx_canvas, st);
+            if (e == hipSuccess) e = mdl::launch_wgrad_reduce(L.ngroups, C, H, part, dWx, dUl, dUu, db, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight and input gradients");
+    } else {
         Timed t("wgrad");
-        e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dWx, dUl, dUu, db, dx_flat, dx_canvas,
-                              ov_wg > 0 ? F.processed : nullptr, st);
+        e = mdl::launch_wgrad(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, dxp, dWx, dUl, dUu, db, dx_flat,
+                              dx_canvas, st);
+        if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight and input gradients");
     }
-    if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight and input gradients");
     if (lk) {
         // the memory-state projections' gradients, their partials in the partial-sum buffer the weight gradients
         // above are done with ([ngroups][4][2H][3H] fits in its [nparts][4][C+1+2H][5H])

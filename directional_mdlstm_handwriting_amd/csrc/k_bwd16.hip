@@ -478,12 +478,12 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
     if constexpr (NS > 3)
         if (s - 2 >= 0) step(s - 2, IC<2>{});
     }
-    // The unit is done: once every wave's gate-gradient stores are visible device-wide, count it on its
-    // example (the weight gradient may then start on the example's cells while other units still run).
+    // The unit is done: once every wave's gate-gradient stores are visible device-wide, flag it (the weight
+    // gradient may then start on this direction of the example's cells while other units still run).
     if (done != nullptr) {
         __threadfence();
         __syncthreads();
-        if (tid == 0) __hip_atomic_fetch_add(done + e, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(done + u, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -33,6 +33,7 @@ WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H, int64_t nflags) {
     w.stash = p; p = al(p + sizeof(float) * 4 * (size_t)T * 8 * H);
     w.zda = p;   p = al(p + sizeof(float) * 4 * (size_t)T * G);
     w.part = p;  p = al(p + sizeof(float) * 4 * (size_t)nparts * R * G);
+    w.dxp = p;   p = al(p + sizeof(float) * 4 * (size_t)T * C);
     w.flags = p; p = al(p + sizeof(int32_t) * (size_t)nflags);
     w.total = p;
     return w;
@@ -256,18 +257,29 @@ __global__ __launch_bounds__(RED_X* RY) void k_wgrad_reduce(const float* __restr
 
 size_t wgrad_lds_bytes(int, int) { return 2 * sizeof(float) * TW_K * TW_S; }
 
-hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
-                        const float* dA, const float* Wx, float* part, float* dWx, float* dUl, float* dUu, float* db,
-                        float* dx_flat, float* dx_canvas, const int32_t* processed, hipStream_t st) {
+hipError_t launch_wgrad_reduce(int64_t nparts, int C, int H, const float* part, float* dWx, float* dUl, float* dUu,
+                               float* db, hipStream_t st) {
     const int G = 5 * H, R = C + 1 + 2 * H;
     const int64_t tot = 4 * (int64_t)R * G;
+    const dim3 rgrid((unsigned)((tot + RED_X - 1) / RED_X));
+    if (nparts > 64)
+        launch(k_wgrad_reduce<16>, rgrid, dim3(RED_X * 16), 0, st, part, (int)nparts, C, H, dWx, dUl, dUu, db);
+    else
+        launch(k_wgrad_reduce<4>, rgrid, dim3(RED_X * 4), 0, st, part, (int)nparts, C, H, dWx, dUl, dUu, db);
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
+                        const float* dA, const float* Wx, float* part, float* dxp, float* dWx, float* dUl, float* dUu,
+                        float* db, float* dx_flat, float* dx_canvas, hipStream_t st) {
+    const int G = 5 * H, R = C + 1 + 2 * H;
     int64_t nparts = D.ngroups;
     if (wgrad2_supported(C, H, dtype)) {
-        hipError_t err =
-            launch_wgrad2(D, x_canvas, dtype, C, H, h_dirs, dA, Wx, part, dx_flat, dx_canvas, processed, st);
+        const bool want_dx = dx_flat != nullptr || dx_canvas != nullptr;
+        hipError_t err = launch_wgrad2(D, x_canvas, dtype, C, H, h_dirs, dA, Wx, part, want_dx ? dxp : nullptr, st);
+        if (err == hipSuccess) err = launch_dx_sum(D, C, dxp, dx_flat, dx_canvas, st);
         if (err != hipSuccess) return err;
     } else {
-        if (processed != nullptr) return hipErrorInvalidValue;
         const int MB = (R + TW_M - 1) / TW_M, NB = (G + TW_N - 1) / TW_N;
         const dim3 grid((unsigned)D.nsegs, (unsigned)(4 * MB * NB));
         if (dtype != 0) launch(k_wgrad_tile<true>, grid, dim3(256), 0, st, D, x_canvas, C, H, h_dirs, dA, part);
@@ -283,12 +295,7 @@ hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, in
         }
         nparts = D.nsegs;
     }
-    const dim3 rgrid((unsigned)((tot + RED_X - 1) / RED_X));
-    if (nparts > 64)
-        launch(k_wgrad_reduce<16>, rgrid, dim3(RED_X * 16), 0, st, part, (int)nparts, C, H, dWx, dUl, dUu, db);
-    else
-        launch(k_wgrad_reduce<4>, rgrid, dim3(RED_X * 4), 0, st, part, (int)nparts, C, H, dWx, dUl, dUu, db);
-    return hipGetLastError();
+    return launch_wgrad_reduce(nparts, C, H, part, dWx, dUl, dUu, db, st);
 }
 
 }  // namespace mdl

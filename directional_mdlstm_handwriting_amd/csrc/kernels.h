@@ -49,7 +49,7 @@ struct Dev {
     const int32_t* units;     // [4n]
     const int32_t* segs;      // [nsegs][3] (example, first cell, end cell)
     const int32_t* groups;    // [ngroups+1] first segment of each weight-gradient workgroup
-    const int32_t* gorder;    // [ngroups] the groups in the order their examples finish the reverse wavefront
+    const int32_t* gorder;    // [4 ngroups] the weight-gradient tasks (4 group + direction) in readiness order
     int32_t* eid;             // [Hc*Wc]
     uint8_t* border;          // [Hc*Wc]
     int n, Hc, Wc;
@@ -123,18 +123,30 @@ struct WsLayout {
     size_t stash = 0;   // float [4][T][8H]: SA then SB, the forward values of every cell the reverse wavefront needs
     size_t zda = 0;     // float [4][T][5H]: projection x.Wx+b (forward), gate gradients dA (backward)
     size_t part = 0;    // float [nparts][4][(C+1+2H)*5H]: weight-gradient partial sums
-    size_t flags = 0;   // int32 [n + ngroups + kFlagTail]: the weight-gradient overlap's counters (OverlapFlags)
+    size_t dxp = 0;     // float [4][T][C]: each direction's share of the input gradient
+    size_t flags = 0;   // int32 [4n + 8 ngroups + kFlagTail]: the weight-gradient overlap's flags (OverlapFlags)
     size_t total = 0;
     int64_t nparts = 0;
 };
 constexpr int kFlagTail = 16;
 WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H, int64_t nflags);
-// the counters of the weight gradient's overlap with the reverse wavefront, in the workspace's flags region
+// the flags and counters of the weight gradient's overlap with the reverse wavefront, in the workspace's
+// flags region ([4n] done, [4 ngroups] taken, [4 ngroups] abandoned, then the four single counters), all zero
+// before the reverse wavefront
 struct OverlapFlags {
-    int32_t* done;       // [n] reverse-wavefront units of each example that have finished (0..4)
-    int32_t* processed;  // [ngroups] 1 once the overlapping launch has written the group's partial sums
+    int32_t* done;       // [4n] set when reverse-wavefront unit (example, direction) has stored its gate gradients
+    int32_t* taken;      // [4 ngroups] set by the workgroup that takes queue position i (beside or after)
+    int32_t* abandoned;  // [4 ngroups] tasks claimed beside the wavefront but not ready in time, to do afterwards
     int32_t* queue;      // the next position of gorder to claim
-    int32_t* stop;       // set once a group was not ready in time: the overlapping launch claims no more
+    int32_t* stop;       // set once a group was not ready in time: the launch beside the wavefront claims no more
+    int32_t* nab;        // entries of `abandoned`
+    int32_t* abq;        // the next entry of `abandoned` to claim
+};
+// how a launch of the claiming weight-gradient kernel takes its groups
+enum WgClaim : int {
+    kClaimBeside = 0,     // beside the reverse wavefront: wait (bounded) for each task's units to finish
+    kClaimDrain = 1,      // after the reverse wavefront on its stream: one workgroup per queue position not taken
+    kClaimAbandoned = 2,  // after both: the tasks given up beside the wavefront
 };
 
 // launchers: return hipSuccess or the launch error
@@ -159,7 +171,7 @@ hipError_t launch_fwd16(const Dev& D, const void* x_canvas, int dtype, int C, in
 // reverse wavefront on the f16 matrix cores (split, power-of-two scaled operands)
 bool bwd16_supported(int H, int Lmax);
 size_t bwd16_lds(int H, int Lmax);
-// done (may be null): per-example counters, each unit adds 1 to its example's when its stores are visible
+// done (may be null): [4n] flags, unit (example e, direction d) sets done[4e + d] once its stores are visible
 hipError_t launch_bwd16(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                         const float* dy_flat, const float* dh_dirs, float* dA, int32_t* done, hipStream_t st);
 // wavefront kernels for small hidden sizes (H <= 10) on the vector ALUs, fp32, input projection fused
@@ -180,21 +192,28 @@ hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* U
 // software-pipelined weight-gradient kernel for the instantiated (C, H, dtype) shapes
 bool wgrad2_supported(int C, int H, int dtype);
 size_t wgrad2_lds_bytes(int C, int H, int dtype);
-// processed (may be null): groups whose flag is set were done by launch_wgrad2_overlap and are skipped
+// tasks (group, direction) into part[group][d] and, when dxp is not null, each direction's share of dx into
+// dxp [4][T][C] (cells numbered as in the layout's cell offsets, row-major inside each region)
 hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
-                         const float* dA, const float* Wx, float* part, float* dx_flat, float* dx_canvas,
-                         const int32_t* processed, hipStream_t st);
-// the same groups beside the reverse wavefront: `workgroups` persistent workgroups claim groups in the
-// layout's readiness order once the examples' units have counted themselves in F.done (each wait bounded
-// by `budget` shader-clock cycles) and mark the groups they complete in F.processed
-hipError_t launch_wgrad2_overlap(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
-                                 const float* dA, const float* Wx, float* part, float* dx_flat, float* dx_canvas,
-                                 const OverlapFlags& F, int workgroups, long long budget, hipStream_t st);
+                         const float* dA, const float* Wx, float* part, float* dxp, hipStream_t st);
+// the same tasks taken from the claim queue in F (in the layout's readiness order): beside the wavefront and
+// from the abandoned list by `workgroups` workgroups that loop until there is none left (beside, each wait for
+// a task's units, flagged in F.done, is bounded by `budget` shader-clock cycles); after the wavefront by one
+// workgroup per queue position whose taken flag is still clear (`workgroups` and `budget` unused)
+hipError_t launch_wgrad2_claim(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
+                               const float* dA, const float* Wx, float* part, float* dxp, const OverlapFlags& F,
+                               WgClaim mode, int workgroups, long long budget, hipStream_t st);
+// dx from the four directions' shares in dxp (added in direction order): dx_flat at the real pixels,
+// dx_canvas at the computed cells (zero outside the real pixels); nothing when both are null
+hipError_t launch_dx_sum(const Dev& D, int C, const float* dxp, float* dx_flat, float* dx_canvas, hipStream_t st);
 size_t wgrad_lds_bytes(int C, int H);
-// processed: as for launch_wgrad2 (only with a shape launch_wgrad2 supports)
+// dxp: the workspace's dx-share region (used by the shapes launch_wgrad2 supports)
 hipError_t launch_wgrad(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
-                        const float* dA, const float* Wx, float* part, float* dWx, float* dUl, float* dUu, float* db,
-                        float* dx_flat, float* dx_canvas, const int32_t* processed, hipStream_t st);
+                        const float* dA, const float* Wx, float* part, float* dxp, float* dWx, float* dUl, float* dUu,
+                        float* db, float* dx_flat, float* dx_canvas, hipStream_t st);
+// the sum of nparts partial blocks [nparts][4][C+1+2H][5H] into dWx, dUl, dUu, db
+hipError_t launch_wgrad_reduce(int64_t nparts, int C, int H, const float* part, float* dWx, float* dUl, float* dUu,
+                               float* db, hipStream_t st);
 hipError_t launch_conv_fwd(const Dev& Dk, const Dev& Dk1, const float* h_dirs_k, int H, int kh, int kw,
                            const float* Wc, const float* bc, int Cout, float* x_k1, hipStream_t st);
 int64_t conv_nchunks(const Dev& Dk1);

@@ -39,10 +39,12 @@ MDL_HD inline int64_t dg_start(int h, int w, int s) {
     return (int64_t)h * w - t * (t + 1) / 2;
 }
 
-// Weight-gradient work split (see Layout::segs): at most kGroups workgroups (two per compute unit of a
-// 256-CU device), at least about kGroupMinCells cells each, at most kGroupSegs segments each.
+// Weight-gradient work split (see Layout::segs): at most kGroups groups (each one task per direction), at
+// least about kGroupMinCells cells each, at most kGroupSegs segments each; from kGroupRound groups on, a
+// multiple of kGroupRound (whole rounds of tasks on a 256-CU device at two workgroups per unit).
 constexpr int kGroups = 512;
-constexpr int kGroupMinCells = 256;
+constexpr int kGroupMinCells = 512;
+constexpr int kGroupRound = 128;
 constexpr int kGroupSegs = 16;
 
 struct DescOffsets {
@@ -53,7 +55,7 @@ struct DescOffsets {
     size_t units = 0;     // int32 [4n] (example*4 + direction), most cells first
     size_t segs = 0;      // int32 [nsegs][3] (example, first cell, end cell) of the weight-gradient split
     size_t groups = 0;    // int32 [ngroups+1] first segment of each weight-gradient workgroup
-    size_t gorder = 0;    // int32 [ngroups] the groups in the order their examples finish the reverse wavefront
+    size_t gorder = 0;    // int32 [4 ngroups] the weight-gradient tasks (4 group + direction) in readiness order
     size_t eid = 0;       // int32 [Hc*Wc]
     size_t border = 0;    // uint8 [Hc*Wc]
     size_t total = 0;
@@ -77,8 +79,9 @@ struct Layout {
     // take one segment per workgroup), so nparts() = max(nsegs, ngroups) partial blocks.
     std::vector<int32_t> segs;
     std::vector<int32_t> groups;
-    // the groups ordered by the largest dependent-step count (h + w - 1) of their examples, ties by index:
-    // the order in which they become ready while the reverse wavefront runs (its units all start together)
+    // the weight-gradient tasks (task 4 g + d: direction d of group g) ordered by the largest dependent-step
+    // count (h + w - 1) of the group's examples, ties by task index: the order in which they become ready
+    // while the reverse wavefront runs (its units all start together)
     std::vector<int32_t> gorder;
     int32_t nsegs = 0, ngroups = 0;
     int64_t nparts() const { return nsegs > ngroups ? nsegs : ngroups; }

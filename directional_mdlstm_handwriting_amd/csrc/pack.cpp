@@ -46,16 +46,17 @@ void paint_maps(Layout& L) {
         }
 }
 
-// Cuts the computed cells of all examples (example order, row-major inside each region) into at most
-// kGroups ranges of nearly equal size, with boundaries on multiples of 32 cells of the sequence; each
-// range's pieces inside one example are its segments. A range that would hold more than kGroupSegs
+// Cuts the computed cells of all examples (example order, row-major inside each region) into G ranges of
+// nearly equal size (G as the constants in layout.h set it), with boundaries on multiples of 32 cells of
+// the sequence; each range's pieces inside one example are its segments. A range that would hold more than kGroupSegs
 // segments is closed early and its rest goes on in a new group. Depends only on the layout, so the
 // weight-gradient sums are blocked the same way on every run.
 void split_wgrad(Layout& L) {
     L.segs.clear();
     L.groups.assign(1, 0);
     const int64_t T = L.computed_cells;
-    const int64_t G = std::max<int64_t>(1, std::min<int64_t>(kGroups, (T + kGroupMinCells - 1) / kGroupMinCells));
+    int64_t G = std::max<int64_t>(1, std::min<int64_t>(kGroups, (T + kGroupMinCells - 1) / kGroupMinCells));
+    if (G >= kGroupRound) G = G / kGroupRound * kGroupRound;
     int e = 0;
     int64_t pos = 0;
     for (int64_t g = 0; g < G; ++g) {
@@ -84,9 +85,10 @@ void split_wgrad(Layout& L) {
             const int32_t* r = &L.rect[4 * L.segs[3 * sg]];
             key[g] = std::max(key[g], r[2] + r[3] - 1);
         }
-    L.gorder.resize(L.ngroups);
+    L.gorder.resize(4 * (size_t)L.ngroups);
     std::iota(L.gorder.begin(), L.gorder.end(), 0);
-    std::stable_sort(L.gorder.begin(), L.gorder.end(), [&](int32_t a, int32_t b) { return key[a] < key[b]; });
+    std::stable_sort(L.gorder.begin(), L.gorder.end(),
+                     [&](int32_t a, int32_t b) { return key[a >> 2] < key[b >> 2]; });
 }
 
 void finish(Layout& L) {

@@ -290,11 +290,14 @@ int mdl_dirsum_unpack(const mdl_layout* layout, const void* d_desc, const float*
  * overlaps the wavefront: every unit counts itself on its example when its
  * gate gradients are stored, and persistent workgroups on a stream of the
  * library's own (one per device, forked from and joined back into `stream`
- * with events) compute the weight-gradient blocks whose examples are done;
- * the blocks left over are computed after the wavefront. Each block is
- * computed by the same code either way, so the results are the same bit for
- * bit; every wait is bounded. Overlapping calls on one device share that
- * stream (and a workspace must not be shared by calls that may overlap).
+ * with events) take weight-gradient blocks from a claim queue, in the order
+ * their examples finish, once those examples are done; after the wavefront a
+ * launch on `stream` takes the rest of the queue on every compute unit while
+ * they finish theirs, and a block given up beside the wavefront (each wait is
+ * bounded) is computed after both. Each block is computed by the same code
+ * whichever launch takes it, so the results are the same bit for bit.
+ * Overlapping calls on one device share that stream (and a workspace must not
+ * be shared by calls that may overlap).
  * MDL_EUNSUPPORTED under the same size limits as mdl_forward and when one
  * direction's gate gradients (T*5H floats, T = computed cells) reach 2 GiB.
  */
