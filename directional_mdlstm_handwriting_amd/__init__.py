@@ -318,8 +318,10 @@ def mdl_blockconv_backward_noalloc(lk: Layout, d_desc_k, lk1: Layout, d_desc_k1,
                                                _ptr(dWc), _ptr(dbc), _stream(stream)))
 
 
-def mdl_set_wgrad_overlap(enable: bool):
-    _check(_lib.mdl_set_wgrad_overlap(1 if enable else 0))
+def mdl_set_wgrad_overlap(mode):
+    """Weight-gradient overlap with the reverse wavefront: True / 1 on, False / 0 off, 2 on with every task
+    given up beside the wavefront (the path of a wait that runs out of time)."""
+    _check(_lib.mdl_set_wgrad_overlap(int(mode)))
 
 
 def mdl_timing(enable: bool):

@@ -38,8 +38,10 @@ const mdl::Layout& L_of(const mdl_layout* l) { return l->L; }
 // ints of the workspace's flags region: the overlap's per-unit and per-task flags and its counters
 int64_t nflags_of(const mdl::Layout& L) { return 4 * (int64_t)L.n + 8 * (int64_t)L.ngroups + mdl::kFlagTail; }
 
-// the weight-gradient overlap: on by default; a stream (default priority) and fork / join events per device
-std::atomic<bool> g_overlap{true};
+// the weight-gradient overlap: 1 on (default), 0 off, 2 on with no time to wait for any task (every task
+// claimed beside the wavefront is given up and done after it); a stream (default priority) and fork / join
+// events per device
+std::atomic<int> g_overlap{1};
 struct Side {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr;
@@ -614,7 +616,8 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     // for want of time. Each task is computed by the same code either way.
     Side* side = nullptr;
     int ov_wg = 0;
-    if (!lk && g_overlap.load() && wg2 && mdl::bwd16_supported(H, L.max_diag)) {
+    const int ov_mode = g_overlap.load();
+    if (!lk && ov_mode != 0 && wg2 && mdl::bwd16_supported(H, L.max_diag)) {
         if ((rc = side_of(side))) return rc;
         const int free_cu = side->ncu - 4 * L.n;
         if (2 * free_cu >= side->ncu) ov_wg = std::min(free_cu, 4 * (int)L.ngroups);
@@ -649,7 +652,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     if (ov_wg > 0) {
         // each wait at most ~2^15 clock cycles per dependent step of the layout (several times the reverse
         // wavefront's own time per step), at least 2^26 cycles
-        const long long budget = std::max<long long>(1ll << 26, (long long)L.max_depth << 15);
+        const long long budget = ov_mode == 2 ? 0 : std::max<long long>(1ll << 26, (long long)L.max_depth << 15);
         {
             Timed t("wgrad_overlap");
             e = mdl::launch_wgrad2_claim(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, want_dx ? dxp : nullptr,
@@ -858,8 +861,9 @@ int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_fl
     GUARD_END
 }
 
-int mdl_set_wgrad_overlap(int32_t enable) {
-    g_overlap.store(enable != 0);
+int mdl_set_wgrad_overlap(int32_t mode) {
+    if (mode < 0 || mode > 2) return fail(MDL_EINVAL, "mdl_set_wgrad_overlap: mode must be 0, 1 or 2");
+    g_overlap.store(mode);
     return MDL_OK;
 }
 

@@ -418,9 +418,11 @@ int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_fl
 int mdl_timing(int32_t enable);
 int mdl_timing_only(const char* group);
 
-/* Turns the weight gradient's overlap with the reverse wavefront (mdl_backward) on (default) or off,
- * process-wide; the results do not depend on it. Always MDL_OK. */
-int mdl_set_wgrad_overlap(int32_t enable);
+/* Sets the weight gradient's overlap with the reverse wavefront (mdl_backward), process-wide: 1 on
+ * (default), 0 off, 2 on with no time allowed for any wait (every task claimed beside the wavefront is
+ * given up there and computed after it: the path a wait that runs out of time takes, for tests). The
+ * results do not depend on it. MDL_EINVAL for any other mode. */
+int mdl_set_wgrad_overlap(int32_t mode);
 int mdl_timing_report(int32_t max, char* names, double* total_ms, int64_t* launches, int32_t* count);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -187,6 +187,15 @@ def test_error_codes():
         assert rc not in (M.MDL_EUNSUPPORTED, M.MDL_ESIZE, M.MDL_EINVAL), M.mdl_last_error()
 
 
+def test_wgrad_overlap_modes():
+    for bad in (-1, 3):
+        with pytest.raises(M.MdlError) as e:
+            M.mdl_set_wgrad_overlap(bad)
+        assert e.value.code == M.MDL_EINVAL and "mode" in M.mdl_last_error()
+    for mode in (0, 2, 1):
+        M.mdl_set_wgrad_overlap(mode)
+
+
 def test_workspace_grows_with_size():
     lay = M.mdl_pack([10, 12], [30, 20], 64, 1)
     a = M.mdl_workspace_size(lay, 4, 16)

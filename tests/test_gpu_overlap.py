@@ -2,7 +2,9 @@
 
 mdl_backward lets persistent weight-gradient workgroups run beside the reverse wavefront (on the compute
 units its units leave free) and computes the blocks they did not get to after it; every block goes through
-the same code, so the gradients must equal, bit for bit, those of a call with the overlap switched off.
+the same code, so the gradients must equal, bit for bit, those of a call with the overlap switched off, and
+those of a call in which every task claimed beside the wavefront is given up there (no time allowed for its
+wait) and computed after it.
 Checked on the line batch (32 examples, 128 units: the overlap runs) and on a small batch, with the flat and
 the canvas input gradient; a second backward with the overlap on repeats the first exactly (the counters and
 the claim queue start from zero on every call).
@@ -36,20 +38,22 @@ def _backward(out, P, dys, overlap):
         torch.cuda.synchronize()
         return [t.cpu().numpy() for t in (g.dWx, g.dUl, g.dUu, g.db, dx, dxc)]
     finally:
-        M.mdl_set_wgrad_overlap(True)
+        M.mdl_set_wgrad_overlap(1)
 
 
 def _check(name, heights, widths, xs, P, x_dtype="f32", sep=1, canvas_w_min=None):
     dys = cotangent(5, heights, widths, P.H)
     out = run_layer(heights, widths, xs, P, x_dtype=x_dtype, sep=sep, canvas_w_min=canvas_w_min, dys=dys)
-    print(f"[gpu] overlap on / off: {name}", flush=True)
-    a = _backward(out, P, dys, True)
-    b = _backward(out, P, dys, False)
-    c = _backward(out, P, dys, True)
-    for nm, x, y, z in zip(("dWx", "dUl", "dUu", "db", "dx", "dx_canvas"), a, b, c):
+    print(f"[gpu] overlap on / off / given up: {name}", flush=True)
+    a = _backward(out, P, dys, 1)
+    b = _backward(out, P, dys, 0)
+    c = _backward(out, P, dys, 1)
+    g = _backward(out, P, dys, 2)  # every task claimed beside the wavefront given up, done after it
+    for nm, x, y, z, w in zip(("dWx", "dUl", "dUu", "db", "dx", "dx_canvas"), a, b, c, g):
         assert np.all(np.isfinite(x)), f"{name} {nm}: non-finite values"
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32)), f"{name} {nm}: overlap changed the result"
         assert np.array_equal(x.view(np.uint32), z.view(np.uint32)), f"{name} {nm}: repeated call differs"
+        assert np.array_equal(x.view(np.uint32), w.view(np.uint32)), f"{name} {nm}: given-up tasks differ"
 
 
 def test_overlap_line_batch():
