@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--no-stack", action="store_true", help="skip the three-level stack companion run")
     ap.add_argument("--no-leaky", action="store_true", help="skip the Leaky LP cell runs (word and line batches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum wall time of the CPU oracle baseline")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="weight gradients after the reverse wavefront only (one kernel at a time, for counter runs)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="after the run, copy MIB MiB on the device (counter calibration under rocprofv3 --pmc)")
     return ap.parse_args()
@@ -267,11 +269,11 @@ class Runner:
         import directional_mdlstm_handwriting_amd as M
         for _ in range(warmup):
             self.step()
-        M.mdl_set_wgrad_overlap(False)
+        M.mdl_set_wgrad_overlap(0)
         try:
             _, kern = self.run(steps, None)
         finally:
-            M.mdl_set_wgrad_overlap(True)
+            M.mdl_set_wgrad_overlap(OVERLAP)
         _, kern_ov = self.run(steps, None)
         dom = max(kern, key=kern.get)
         ms, kd = self.run(steps, dom)
@@ -481,7 +483,13 @@ def layer_report(runner, wl, ms, kern):
     return model, bmin, per
 
 
+# the weight gradients' overlap with the reverse wavefront in the warmup, the second breakdown pass and the
+# timed region (mdl_set_wgrad_overlap mode: 1 on, 0 off)
+OVERLAP = 1
+
+
 def main():
+    global OVERLAP
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -501,6 +509,8 @@ def main():
     import directional_mdlstm_handwriting_amd as M
     device = "cuda:0"
     torch.cuda.set_device(0)
+    OVERLAP = 0 if args.no_overlap else 1
+    M.mdl_set_wgrad_overlap(OVERLAP)
     stream = torch.cuda.current_stream()
 
     print(f"bench: {wl.name} packed", file=sys.stderr, flush=True)
@@ -550,9 +560,10 @@ def main():
         "kernels_ms_source": "breakdown pass before the timed region, events on every dispatch, the weight "
                              "gradients run after the reverse wavefront",
         "kernels_ms_overlap": {k: round(v, 5) for k, v in kern_ov.items()},
-        "kernels_ms_overlap_source": "second breakdown pass, the weight gradients' overlap on as in the timed "
-                                     "region: wgrad_overlap spans the launch beside the reverse wavefront "
-                                     "(mostly waiting for examples to finish), wgrad the groups left after it",
+        "kernels_ms_overlap_source": ("second breakdown pass, the weight gradients' overlap on as in the timed "
+                                      "region: wgrad_overlap spans the launch beside the reverse wavefront "
+                                      "(mostly waiting for its units to finish), wgrad the tasks left after it"
+                                      if OVERLAP else "the weight gradients' overlap is off in this run"),
         "kernels_roofline": {k: {kk: r[kk] for kk in ("bound", "frac", "fp32_frac", "min_bytes_hbm_frac",
                                                        "design_bytes_hbm_frac")}
                              for k, r in per_kernel.items()},
