@@ -110,8 +110,11 @@ def kernel_model(info, rects, C, H, x_bytes, nchunks=None, fwd_zero=False, leaky
         "dirsum": (N * 5 * H * f, 3 * N * H),
         # gate stash and dy in (dy once per direction), dA (5H gate pre-activation gradients) out
         "bwd_wavefront": (4 * T * (sw + G) * f + 4 * N * H * f, rec),
-        # dA and h in (each h once), x in, dx out, chunk partials out; r^T dA and dA Wx^T on the matrix cores
-        "wgrad": (4 * T * (G + H) * f + 4 * T * C * x_bytes + N * C * f + 4 * R * G * f,
+        # dA and h in (each h once), x in (once per direction), dx out; the design's own intermediates: each
+        # direction's dx share written and read back (4 T C floats), the task partial sums written and read by
+        # the reduction (4 groups x R x G floats), the weight gradients out; r^T dA and dA Wx^T on the matrix cores
+        "wgrad": (4 * T * (G + H) * f + 4 * T * C * x_bytes + N * C * f + 2 * 4 * T * C * f
+                  + 2 * 4 * info.get("wg_groups", 0) * R * G * f + 4 * R * G * f,
                   4 * T * 2 * R * G + 4 * T * 2 * G * C),
         # flat x in, canvas x out
         "scatter": (N * C * x_bytes + P * C * x_bytes, 0),

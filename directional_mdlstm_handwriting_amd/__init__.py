@@ -43,7 +43,8 @@ MDL_BF16 = 1
 MDL_CELL_MDLSTM = 0
 MDL_CELL_LEAKY_LP = 1
 
-INFO_KEYS = ("n", "canvas_h", "canvas_w", "rows", "real_pixels", "computed_cells", "max_depth", "max_diag", "mode")
+INFO_KEYS = ("n", "canvas_h", "canvas_w", "rows", "real_pixels", "computed_cells", "max_depth", "max_diag", "mode",
+             "wg_groups")
 
 # every exported entry point: (name, restype, argtypes)
 _P = ctypes.c_void_p

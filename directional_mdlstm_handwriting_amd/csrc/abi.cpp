@@ -240,6 +240,7 @@ int mdl_layout_info(const mdl_layout* layout, int64_t* info) {
     info[MDL_INFO_MAX_DEPTH] = L.max_depth;
     info[MDL_INFO_MAX_DIAG] = L.max_diag;
     info[MDL_INFO_MODE] = L.mode;
+    info[MDL_INFO_WG_GROUPS] = L.ngroups;
     return MDL_OK;
 }
 

@@ -77,7 +77,8 @@ extern "C" {
 #define MDL_INFO_MAX_DEPTH      6 /* max over examples of h+w-1: dependent steps per pass */
 #define MDL_INFO_MAX_DIAG       7 /* max over examples of min(h,w): widest anti-diagonal */
 #define MDL_INFO_MODE           8
-#define MDL_INFO_COUNT          9
+#define MDL_INFO_WG_GROUPS      9 /* groups of the weight-gradient split (one task per group and direction) */
+#define MDL_INFO_COUNT         10
 
 typedef struct mdl_layout mdl_layout; /* host object, immutable once built */
 
