@@ -236,8 +236,7 @@ class Runner:
     def step(self):
         L, s = self.layer, self.stream
         L.scatter(self.x, s)
-        L.forward(self.P, s)
-        L.dirsum(s)
+        L.forward_dirsum(self.P, s)  # the forward wavefront and the direction sum (beside it where it can)
         L.backward(self.P, self.g, dy_flat=self.dy, dx_flat=self.dx, stream=s)
 
     def run(self, steps, only):
@@ -565,7 +564,9 @@ def main():
         "kernels_ms_overlap": {k: round(v, 5) for k, v in kern_ov.items()},
         "kernels_ms_overlap_source": ("second breakdown pass, the weight gradients' overlap on as in the timed "
                                       "region: wgrad_overlap spans the launch beside the reverse wavefront "
-                                      "(mostly waiting for its units to finish), wgrad the tasks left after it"
+                                      "(mostly waiting for its units to finish), wgrad the tasks left after it; "
+                                      "dirsum_overlap and dirsum likewise for the direction sum beside the "
+                                      "forward wavefront"
                                       if OVERLAP else "the weight gradients' overlap is off in this run"),
         "kernels_roofline": {k: {kk: r[kk] for kk in ("bound", "frac", "fp32_frac", "min_bytes_hbm_frac",
                                                        "design_bytes_hbm_frac")}

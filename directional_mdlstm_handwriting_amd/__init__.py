@@ -64,6 +64,7 @@ _SIGS = [
     ("mdl_workspace_size", _I32, [_P, _I32, _I32, ctypes.POINTER(_SZ)]),
     ("mdl_scatter", _I32, [_P, _P, _P, _I32, _I32, _P, _P]),
     ("mdl_forward", _I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    ("mdl_forward_dirsum", _I32, [_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     ("mdl_dirsum_unpack", _I32, [_P, _P, _P, _I32, _P, _P]),
     ("mdl_skewed_workspace_size", _I32, [_P, _I32, _I32, ctypes.POINTER(_SZ)]),
     ("mdl_forward_skewed", _I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -245,6 +246,13 @@ def mdl_forward(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, 
     _check(_lib.mdl_forward(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, cell, _ptr(Wx), _ptr(Ul),
                             _ptr(Uu), _ptr(b), _ptr(Vl), _ptr(Vu), _ptr(h_dirs), _ptr(ws), ws_bytes,
                             _stream(stream)))
+
+
+def mdl_forward_dirsum(layout: Layout, d_desc, x_canvas, x_dtype: int, C: int, H: int, cell: int, Wx, Ul, Uu, b, Vl,
+                       Vu, h_dirs, y_flat, ws, ws_bytes: int, stream=None):
+    _check(_lib.mdl_forward_dirsum(layout.handle, _ptr(d_desc), _ptr(x_canvas), x_dtype, C, H, cell, _ptr(Wx),
+                                   _ptr(Ul), _ptr(Uu), _ptr(b), _ptr(Vl), _ptr(Vu), _ptr(h_dirs), _ptr(y_flat),
+                                   _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def mdl_skewed_workspace_size(layout: Layout, C: int, H: int) -> int:

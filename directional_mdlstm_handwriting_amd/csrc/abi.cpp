@@ -32,11 +32,14 @@ int fail(int code, const std::string& msg) {
 int hip_fail(hipError_t e, const char* where) {
     return fail(MDL_EHIP, std::string(where) + ": " + hipGetErrorString(e));
 }
+int hip_fail(hipError_t e, const std::string& where) { return hip_fail(e, where.c_str()); }
 
 const mdl::Layout& L_of(const mdl_layout* l) { return l->L; }
 
 // ints of the workspace's flags region: the overlap's per-unit and per-task flags and its counters
 int64_t nflags_of(const mdl::Layout& L) { return 4 * (int64_t)L.n + 8 * (int64_t)L.ngroups + mdl::kFlagTail; }
+// ints of the workspace's forward flags region: the direction sum's overlap with the forward
+int64_t nfflags_of(const mdl::Layout& L) { return 4 * (int64_t)L.n + 2 * (int64_t)L.nsum + mdl::kFlagTail; }
 
 // the weight-gradient overlap: 1 on (default), 0 off, 2 on with no time to wait for any task (every task
 // claimed beside the wavefront is given up and done after it); a stream (default priority) and fork / join
@@ -82,6 +85,7 @@ mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     D.segs = reinterpret_cast<const int32_t*>(b + L.off.segs);
     D.groups = reinterpret_cast<const int32_t*>(b + L.off.groups);
     D.gorder = reinterpret_cast<const int32_t*>(b + L.off.gorder);
+    D.dsum = reinterpret_cast<const int32_t*>(b + L.off.dsum);
     D.eid = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(b + L.off.eid));
     D.border = const_cast<uint8_t*>(b + L.off.border);
     D.n = L.n;
@@ -93,6 +97,7 @@ mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     D.max_diag = L.max_diag;
     D.nsegs = L.nsegs;
     D.ngroups = L.ngroups;
+    D.nsum = L.nsum;
     return D;
 }
 
@@ -312,7 +317,7 @@ int mdl_layout_upload(const mdl_layout* layout, void* d_desc, size_t bytes, void
 int mdl_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, size_t* bytes) {
     if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_workspace_size: null argument");
     if (C < 1 || H < 1) return fail(MDL_EINVAL, "mdl_workspace_size: need C >= 1 and H >= 1");
-    *bytes = mdl::ws_layout(L_of(layout).computed_cells, L_of(layout).nparts(), C, H, nflags_of(L_of(layout))).total;
+    *bytes = mdl::ws_layout(L_of(layout).computed_cells, L_of(layout).nparts(), C, H, nflags_of(L_of(layout)), nfflags_of(L_of(layout))).total;
     return MDL_OK;
 }
 
@@ -367,81 +372,148 @@ static int check_cell(const char* fn, int32_t cell, const void* Vl, const void* 
     return fail(MDL_EINVAL, std::string(fn) + ": unknown cell");
 }
 
-int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype, int32_t C,
-                int32_t H, int32_t cell, const float* Wx, const float* Ul, const float* Uu, const float* b,
-                const float* Vl, const float* Vu, float* h_dirs, void* ws, size_t ws_bytes, void* stream) {
-    GUARD_BEGIN
-    int rc = check_layer("mdl_forward", layout, d_desc, C, H, x_dtype);
+// The forward wavefront of mdl_forward and, when y_flat is given, the direction sum of mdl_dirsum_unpack.
+// The sum overlaps the wavefront when its units leave at least half of the compute units free (f16 path,
+// chunked sum supported): each unit flags itself when its h plane is stored, persistent workgroups on the
+// library's second stream take the sum's chunks (in the order their examples finish) once all four of an
+// example's units are done, and the launch after the wavefront takes the rest; every chunk runs the same code.
+static int forward_impl(const char* fn, const mdl_layout* layout, const void* d_desc, const void* x_canvas,
+                        int32_t x_dtype, int32_t C, int32_t H, int32_t cell, const float* Wx, const float* Ul,
+                        const float* Uu, const float* b, const float* Vl, const float* Vu, float* h_dirs,
+                        float* y_flat, void* ws, size_t ws_bytes, void* stream) {
+    const std::string F(fn);
+    int rc = check_layer(fn, layout, d_desc, C, H, x_dtype);
     if (rc) return rc;
-    if ((rc = check_cell("mdl_forward", cell, Vl, Vu))) return rc;
-    if (!x_canvas || !Wx || !Ul || !Uu || !b || !h_dirs || !ws) return fail(MDL_EINVAL, "mdl_forward: null tensor");
+    if ((rc = check_cell(fn, cell, Vl, Vu))) return rc;
+    if (!x_canvas || !Wx || !Ul || !Uu || !b || !h_dirs || !ws) return fail(MDL_EINVAL, F + ": null tensor");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
-    if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_forward: workspace smaller than mdl_workspace_size");
-    if ((rc = check_extent("mdl_forward", L, C, H, x_dtype, false))) return rc;
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L), nfflags_of(L));
+    if (ws_bytes < W.total) return fail(MDL_ESIZE, F + ": workspace smaller than mdl_workspace_size");
+    if ((rc = check_extent(fn, L, C, H, x_dtype, false))) return rc;
+    const mdl::Dev D = make_dev(layout, d_desc);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    float* stash = reinterpret_cast<float*>(wsb + W.stash);
+    hipError_t e = hipSuccess;
+    // the direction sum after the wavefront (when asked for and not overlapped)
+    auto dirsum_after = [&]() -> int {
+        if (!y_flat) return MDL_OK;
+        Timed t("dirsum");
+        const hipError_t e2 = mdl::launch_dirsum(D, h_dirs, H, y_flat, st);
+        return e2 == hipSuccess ? MDL_OK : hip_fail(e2, F + ": direction sum");
+    };
     if (cell == MDL_CELL_LEAKY_LP) {
         if (!mdl::leaky_supported(H, C, L.max_diag))
-            return fail(MDL_EUNSUPPORTED, "mdl_forward: the Leaky LP cell runs for H in {4, 8, 16, 32}, C <= 16 and "
-                                          "a widest diagonal of at most 64 cells (32 at H = 32)");
+            return fail(MDL_EUNSUPPORTED, F + ": the Leaky LP cell runs for H in {4, 8, 16, 32}, C <= 16 and "
+                                              "a widest diagonal of at most 64 cells (32 at H = 32)");
         size_t lmax = 0;
         if ((rc = max_lds(lmax))) return rc;
-        if (mdl::leaky_fwd_lds(H, L.max_diag) > lmax)
-            return fail(MDL_EUNSUPPORTED, "mdl_forward: diagonal state exceeds LDS");
-        const mdl::Dev D = make_dev(layout, d_desc);
-        hipStream_t st = static_cast<hipStream_t>(stream);
-        float* stash = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + W.stash);
-        hipError_t e;
+        if (mdl::leaky_fwd_lds(H, L.max_diag) > lmax) return fail(MDL_EUNSUPPORTED, F + ": diagonal state exceeds LDS");
         {
             Timed t("zero_fill");
             e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
         }
-        if (e != hipSuccess) return hip_fail(e, "mdl_forward: zero fill");
+        if (e != hipSuccess) return hip_fail(e, F + ": zero fill");
         {
             Timed t("fwd_wavefront");
             e = mdl::launch_fwd_leaky(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, Vl, Vu, stash, h_dirs, st);
         }
-        if (e != hipSuccess) return hip_fail(e, "mdl_forward: wavefront");
-        return MDL_OK;
+        if (e != hipSuccess) return hip_fail(e, F + ": wavefront");
+        return dirsum_after();
     }
     // small hidden sizes: vector-ALU wavefront; instantiated matrix-core shapes: f16 wavefront; both with
     // the projection fused. Otherwise the projection as its own GEMM and the general fp32 wavefront.
     const bool small = mdl::small_fwd_supported(H, C, x_dtype, L.max_diag);
     const bool fused = !small && mdl::fwd16_supported(H, C, x_dtype, L.max_diag);
     if (!small && !fused && (int64_t)L.max_diag * H > mdl::chain_max_items())
-        return fail(MDL_EUNSUPPORTED, "mdl_forward: widest diagonal x H exceeds the wavefront kernel's items");
+        return fail(MDL_EUNSUPPORTED, F + ": widest diagonal x H exceeds the wavefront kernel's items");
     size_t lmax = 0;
     if ((rc = max_lds(lmax))) return rc;
     const size_t need = small ? mdl::small_fwd_lds(H, L.max_diag)
                               : (fused ? mdl::fwd16_lds(H, C, x_dtype, L.max_diag) : mdl::fwd_chain_lds(H, L.max_diag));
-    if (need > lmax) return fail(MDL_EUNSUPPORTED, "mdl_forward: recurrent weights and diagonal state exceed LDS");
-    const mdl::Dev D = make_dev(layout, d_desc);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    if (need > lmax) return fail(MDL_EUNSUPPORTED, F + ": recurrent weights and diagonal state exceed LDS");
     float* Z = reinterpret_cast<float*>(wsb + W.zda);
-    float* stash = reinterpret_cast<float*>(wsb + W.stash);
-    hipError_t e = hipSuccess;
     if (!fused) {  // the f16 forward clears h outside the computed regions itself, in its smallest units' tail
         Timed t("zero_fill");
         e = mdl::launch_zero_outside(D, h_dirs, H, 4, st);
     }
-    if (e != hipSuccess) return hip_fail(e, "mdl_forward: zero fill");
+    if (e != hipSuccess) return hip_fail(e, F + ": zero fill");
+    Side* side = nullptr;
+    int ov_wg = 0;
+    const int ov_mode = g_overlap.load();
+    if (fused && y_flat && ov_mode != 0 && mdl::dirsum_chunked_supported(D, h_dirs, H, y_flat)) {
+        if ((rc = side_of(side))) return rc;
+        const int free_cu = side->ncu - 4 * L.n;
+        if (2 * free_cu >= side->ncu) ov_wg = std::min(free_cu, (int)L.nsum);
+    }
+    mdl::OverlapFlags Fl{};
+    if (ov_wg > 0) {
+        int32_t* fl = reinterpret_cast<int32_t*>(wsb + W.fflags);
+        Fl.done = fl;
+        Fl.taken = fl + 4 * L.n;
+        Fl.abandoned = Fl.taken + L.nsum;
+        Fl.queue = Fl.abandoned + L.nsum;
+        Fl.stop = Fl.queue + 1;
+        Fl.nab = Fl.queue + 2;
+        Fl.abq = Fl.queue + 3;
+        if ((e = mdl::launch_fill_i32(fl, nfflags_of(L), 0, st)) != hipSuccess)
+            return hip_fail(e, F + ": overlap flags");
+        if ((e = hipEventRecord(side->fork, st)) != hipSuccess || (e = hipStreamWaitEvent(side->s, side->fork, 0)) != hipSuccess)
+            return hip_fail(e, F + ": fork to the library's stream");
+    }
     if (small) {
         Timed t("fwd_wavefront");
         e = mdl::launch_fwd_small(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, stash, h_dirs, st);
     } else if (fused) {
         Timed t("fwd_wavefront");
-        e = mdl::launch_fwd16(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, stash, h_dirs, st);
+        e = mdl::launch_fwd16(D, x_canvas, x_dtype, C, H, Wx, b, Ul, Uu, stash, h_dirs, ov_wg > 0 ? Fl.done : nullptr,
+                              st);
     } else {
         {
             Timed t("projection");
             e = mdl::launch_projection(D, x_canvas, x_dtype, C, H, Wx, b, Z, st);
         }
-        if (e != hipSuccess) return hip_fail(e, "mdl_forward: projection");
+        if (e != hipSuccess) return hip_fail(e, F + ": projection");
         Timed t("fwd_wavefront");
         e = mdl::launch_fwd_chain(D, H, Ul, Uu, Z, stash, h_dirs, st);
     }
-    if (e != hipSuccess) return hip_fail(e, "mdl_forward: wavefront");
+    if (e != hipSuccess) return hip_fail(e, F + ": wavefront");
+    if (ov_wg == 0) return dirsum_after();
+    // each wait at most ~2^15 clock cycles per dependent step of the layout, at least 2^26 cycles
+    const long long budget = ov_mode == 2 ? 0 : std::max<long long>(1ll << 26, (long long)L.max_depth << 15);
+    {
+        Timed t("dirsum_overlap");
+        e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimBeside, ov_wg, budget, side->s);
+    }
+    if (e != hipSuccess) return hip_fail(e, F + ": direction sum beside the wavefront");
+    if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return hip_fail(e, F + ": library's stream");
+    {
+        Timed t("dirsum");
+        e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimDrain, 0, 0, st);
+        if (e == hipSuccess && (e = hipStreamWaitEvent(st, side->join, 0)) == hipSuccess)
+            e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimAbandoned, 16, 0, st);
+    }
+    if (e != hipSuccess) return hip_fail(e, F + ": direction sum");
     return MDL_OK;
+}
+
+int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype, int32_t C,
+                int32_t H, int32_t cell, const float* Wx, const float* Ul, const float* Uu, const float* b,
+                const float* Vl, const float* Vu, float* h_dirs, void* ws, size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    return forward_impl("mdl_forward", layout, d_desc, x_canvas, x_dtype, C, H, cell, Wx, Ul, Uu, b, Vl, Vu, h_dirs,
+                        nullptr, ws, ws_bytes, stream);
+    GUARD_END
+}
+
+int mdl_forward_dirsum(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
+                       int32_t C, int32_t H, int32_t cell, const float* Wx, const float* Ul, const float* Uu,
+                       const float* b, const float* Vl, const float* Vu, float* h_dirs, float* y_flat, void* ws,
+                       size_t ws_bytes, void* stream) {
+    GUARD_BEGIN
+    if (!y_flat) return fail(MDL_EINVAL, "mdl_forward_dirsum: null tensor");
+    return forward_impl("mdl_forward_dirsum", layout, d_desc, x_canvas, x_dtype, C, H, cell, Wx, Ul, Uu, b, Vl, Vu,
+                        h_dirs, y_flat, ws, ws_bytes, stream);
     GUARD_END
 }
 
@@ -451,7 +523,7 @@ int mdl_skewed_workspace_size(const mdl_layout* layout, int32_t C, int32_t H, si
     if (!layout || !bytes) return fail(MDL_EINVAL, "mdl_skewed_workspace_size: null argument");
     if (C < 1 || H < 1) return fail(MDL_EINVAL, "mdl_skewed_workspace_size: need C >= 1 and H >= 1");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L), nfflags_of(L));
     *bytes = skew_dcb_offset(W) + sizeof(float) * 4 * (size_t)L.computed_cells * 2 * H;
     return MDL_OK;
 }
@@ -470,7 +542,7 @@ int mdl_forward_skewed(const mdl_layout* layout, const void* d_desc, const void*
     mdl_skewed_workspace_size(layout, C, H, &need);
     if (ws_bytes < need) return fail(MDL_ESIZE, "mdl_forward_skewed: workspace smaller than mdl_skewed_workspace_size");
     if ((rc = check_extent("mdl_forward_skewed", L, C, H, x_dtype, true))) return rc;
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L), nfflags_of(L));
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -519,7 +591,7 @@ int mdl_backward_skewed(const mdl_layout* layout, const void* d_desc, const void
     if ((rc = max_lds(lmax))) return rc;
     if ((wg2 ? mdl::wgrad2_lds_bytes(C, H, x_dtype) : mdl::wgrad_lds_bytes(C, H)) > lmax)
         return fail(MDL_EUNSUPPORTED, "mdl_backward_skewed: weight-gradient tile exceeds LDS");
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L), nfflags_of(L));
     const mdl::Dev D = make_dev(layout, d_desc);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* wsb = static_cast<uint8_t*>(ws);
@@ -582,7 +654,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     if ((dy_flat == nullptr) == (dh_dirs == nullptr))
         return fail(MDL_EINVAL, "mdl_backward: pass exactly one of dy_flat and dh_dirs");
     const mdl::Layout& L = L_of(layout);
-    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L));
+    const mdl::WsLayout W = mdl::ws_layout(L.computed_cells, L.nparts(), C, H, nflags_of(L), nfflags_of(L));
     if (ws_bytes < W.total) return fail(MDL_ESIZE, "mdl_backward: workspace smaller than mdl_workspace_size");
     if (lk && !mdl::leaky_supported(H, C, L.max_diag))
         return fail(MDL_EUNSUPPORTED, "mdl_backward: the Leaky LP cell runs for H in {4, 8, 16, 32}, C <= 16 and a "

@@ -85,7 +85,8 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
                                                                      const float* __restrict__ Ul,
                                                                      const float* __restrict__ Uu,
                                                                      float* __restrict__ stash,
-                                                                     float* __restrict__ hdirs) {
+                                                                     float* __restrict__ hdirs,
+                                                                     int32_t* __restrict__ done) {
     using Sh = F16Shape<H>;
     constexpr int HP = Sh::HP, KB = Sh::KB;
     constexpr bool R3 = Sh::R3;
@@ -366,6 +367,13 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
     if (s < S) step(s, IC<0>{});
     if (s + 1 < S) step(s + 1, IC<1>{});
     if (s + 2 < S) step(s + 2, IC<2>{});
+    // the unit's h plane is complete: once every wave's stores are visible device-wide, flag it (the direction
+    // sum may then start on the example while other units still run)
+    if (done != nullptr) {
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(done + u, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // h outside every computed region reads zero: the second half of the launch order (the smallest units,
     // done first) clears it, one band of canvas rows per workgroup, while the larger units still run
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(64 * F16Shape<H>::NB * CG) void k_fwd16(Dev D, cons
 }
 
 typedef void (*Fwd16Kernel)(Dev, const void*, int, const float*, const float*, const float*, const float*, float*,
-                            float*);
+                            float*, int32_t*);
 
 // instantiated (hidden size, input K steps, bf16 input) combinations of the workloads, each with its
 // cell-group count CG (measured per shape: extra waves repeat the matrix-core work) and accumulator rows NR;
@@ -428,13 +436,13 @@ size_t fwd16_lds(int H, int C, int dtype, int Lmax) {
 
 hipError_t launch_fwd16(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
                         const float* b, const float* Ul, const float* Uu, float* stash, float* h_dirs,
-                        hipStream_t st) {
+                        int32_t* done, hipStream_t st) {
     const F16Entry* m = f16_entry(H, C, dtype, D.max_diag);
     if (!m) return hipErrorInvalidValue;
     const int cells = (D.max_diag + m->CG - 1) / m->CG;  // widest diagonal's cells per group, <= 16
     const int nr = (cells + 3) / 4;
     launch(m->fwd[nr - 1], dim3(4 * D.n), dim3(64 * m->NB * m->CG), f16_lds(*m), st, D, x_canvas, C, Wx,
-           b, Ul, Uu, stash, h_dirs);
+           b, Ul, Uu, stash, h_dirs, done);
     return hipGetLastError();
 }
 

@@ -13,6 +13,10 @@ namespace mdl {
 namespace {
 
 constexpr int TPB = 256;
+// the direction sums: threads per workgroup (k_dirsum4 is launched with TPB of them) and elements per thread
+// whose loads are in flight together
+constexpr int kSumThreads = TPB;
+constexpr int kSumBatch = 4;
 
 inline unsigned grid_for(int64_t n, int tpb = TPB, int64_t cap = 1 << 20) {
     int64_t g = (n + tpb - 1) / tpb;
@@ -117,16 +121,119 @@ __global__ void k_dirsum4(Dev D, const f32x4* __restrict__ hd, int H4, f32x4* __
     const int cnt = rh * rw * H4;
     const int64_t plane = (int64_t)D.Hc * D.Wc * H4;
     f32x4* out = y + D.flat_off[e] * H4;
-    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
-        const int pix = q / H4, k = q - pix * H4;
-        const int ly = pix / rw, lx = pix - ly * rw;
-        const int64_t src = ((int64_t)(y0 + ly) * D.Wc + x0 + lx) * H4 + k;
-        f32x4 s = hd[src];
-        s += hd[src + plane];
-        s += hd[src + 2 * plane];
-        s += hd[src + 3 * plane];
-        out[q] = s;
+    // kSumBatch elements per thread at a time, all their loads issued before the first sum
+    const int stride = (int)gridDim.x * kSumThreads;
+    for (int q0 = blockIdx.x * kSumThreads + threadIdx.x; q0 < cnt; q0 += kSumBatch * stride) {
+        f32x4 v[kSumBatch][4];
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j) {
+            const int q = q0 + j * stride;
+            const int pix = q / H4, k = q - pix * H4;
+            const int ly = pix / rw, lx = pix - ly * rw;
+            const int64_t src = ((int64_t)(y0 + ly) * D.Wc + x0 + lx) * H4 + k;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) v[j][d] = q < cnt ? hd[src + d * plane] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j)
+            if (q0 + j * stride < cnt) out[q0 + j * stride] = ((v[j][0] + v[j][1]) + v[j][2]) + v[j][3];
     }
+}
+
+// ---- the direction sum beside the forward wavefront ----
+
+
+// chunk i of the layout's direction-sum chunks (example e, real pixels [p0, p1) row-major): y of those pixels,
+// the directions added in order as in k_dirsum4
+__device__ __forceinline__ void dsum_chunk(const Dev& D, const f32x4* __restrict__ hd, int H4,
+                                           f32x4* __restrict__ y, int i) {
+    const int e = D.dsum[3 * i], p0 = D.dsum[3 * i + 1], p1 = D.dsum[3 * i + 2];
+    const int y0 = D.real[4 * e], x0 = D.real[4 * e + 1], rw = D.real[4 * e + 3];
+    const int64_t plane = (int64_t)D.Hc * D.Wc * H4;
+    f32x4* out = y + D.flat_off[e] * H4;
+    const int n = (p1 - p0) * H4;
+    // kSumBatch elements per thread at a time, all their loads issued before the first sum
+    for (int q0 = threadIdx.x; q0 < n; q0 += kSumBatch * kSumThreads) {
+        f32x4 v[kSumBatch][4];
+        int64_t dst[kSumBatch];
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j) {
+            const int q = q0 + j * kSumThreads;
+            const int pq = q / H4, k = q - pq * H4;
+            const int pix = p0 + pq;
+            const int ly = pix / rw, lx = pix - ly * rw;
+            const int64_t src = ((int64_t)(y0 + ly) * D.Wc + x0 + lx) * H4 + k;
+            dst[j] = q < n ? (int64_t)pix * H4 + k : -1;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) v[j][d] = q < n ? hd[src + d * plane] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int j = 0; j < kSumBatch; ++j)
+            if (dst[j] >= 0) out[dst[j]] = ((v[j][0] + v[j][1]) + v[j][2]) + v[j][3];
+    }
+}
+
+// Thread 0 of a workgroup beside the forward takes its next chunk: the next queue position (unless the stop
+// flag is set) whose taken flag it is first to set, then waits until the four forward units of the chunk's
+// example are flagged (polled without ordering, one acquire fence at the end; bounded by `budget` shader
+// clocks, past which the position goes on the abandoned list and the stop flag ends claiming). For the
+// abandoned list, the next entry. Returns the position, or -1 once there is none to take.
+__device__ int claim_chunk(const Dev& D, const OverlapFlags& F, int mode, long long budget) {
+    if (mode == kClaimAbandoned) {
+        const int i = __hip_atomic_fetch_add(F.abq, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return i < __hip_atomic_load(F.nab, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? F.abandoned[i] : -1;
+    }
+    int qi;
+    do {
+        if (__hip_atomic_load(F.stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return -1;
+        qi = __hip_atomic_fetch_add(F.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (qi >= D.nsum) return -1;
+    } while (__hip_atomic_exchange(F.taken + qi, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0);
+    const int e = D.dsum[3 * qi];
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+    for (int d = 0; d < 4; ++d) {
+        while (__hip_atomic_load(F.done + 4 * e + d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+            if ((long long)(__builtin_amdgcn_s_memtime() - t0) > budget) {
+                const int k = __hip_atomic_fetch_add(F.nab, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                F.abandoned[k] = qi;
+                __hip_atomic_store(F.stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return -1;
+            }
+            __builtin_amdgcn_s_sleep(16);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return qi;
+}
+
+// Chunks claimed one after another until none is left: persistent workgroups beside the forward, or the
+// abandoned list after the join.
+__global__ __launch_bounds__(kSumThreads) void k_dsum_claim(Dev D, const f32x4* __restrict__ hd, int H4,
+                                                            f32x4* __restrict__ y, OverlapFlags F, int mode,
+                                                            long long budget) {
+    __shared__ int s_pos;
+    // one thread-0 region per iteration, barriers closing every iteration (as in the weight gradients' claim)
+    for (;;) {
+        if (threadIdx.x == 0) s_pos = claim_chunk(D, F, mode, budget);
+        __syncthreads();
+        const int pos = s_pos;
+        __syncthreads();
+        if (pos < 0) break;
+        dsum_chunk(D, hd, H4, y, pos);
+        __syncthreads();
+    }
+}
+
+// After the forward on its stream: workgroup b takes queue position b unless a workgroup beside the forward
+// has taken it (every unit is complete, so nothing is waited for).
+__global__ __launch_bounds__(kSumThreads) void k_dsum_drain(Dev D, const f32x4* __restrict__ hd, int H4,
+                                                            f32x4* __restrict__ y, OverlapFlags F) {
+    __shared__ int s_taken;
+    if (threadIdx.x == 0)
+        s_taken = __hip_atomic_exchange(F.taken + blockIdx.x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_taken != 0) return;
+    dsum_chunk(D, hd, H4, y, blockIdx.x);
 }
 
 // blockIdx.y = example: y_flat[e][r][c][k] = sum_d h_dirs[d][y0+r][x0+c][k], d = 0..3 in order
@@ -209,6 +316,26 @@ hipError_t launch_scatter(const Dev& D, const void* x_flat, int C, int dtype, vo
     else
         launch(k_scatter<uint16_t>, dim3(grid_for(E)), dim3(TPB), 0, st, D,
                (const uint16_t*)x_flat, C, (uint16_t*)x_canvas);
+    return hipGetLastError();
+}
+
+bool dirsum_chunked_supported(const Dev& D, const float* h_dirs, int H, const float* y_flat) {
+    return H % 4 == 0 && aligned(h_dirs, 16) && aligned(y_flat, 16) && D.N * (H / 4) < (int64_t(1) << 31) &&
+           (int64_t)kSumChunk * (H / 4) < (int64_t(1) << 31) && D.nsum > 0;
+}
+
+hipError_t launch_dirsum_claim(const Dev& D, const float* h_dirs, int H, float* y_flat, const OverlapFlags& F,
+                               WgClaim mode, int workgroups, long long budget, hipStream_t st) {
+    if (!dirsum_chunked_supported(D, h_dirs, H, y_flat) || budget < 0) return hipErrorInvalidValue;
+    const f32x4* hd = reinterpret_cast<const f32x4*>(h_dirs);
+    f32x4* y = reinterpret_cast<f32x4*>(y_flat);
+    if (mode == kClaimDrain)
+        launch(k_dsum_drain, dim3((unsigned)D.nsum), dim3(kSumThreads), 0, st, D, hd, H / 4, y, F);
+    else if (workgroups < 1)
+        return hipErrorInvalidValue;
+    else
+        launch(k_dsum_claim, dim3((unsigned)workgroups), dim3(kSumThreads), 0, st, D, hd, H / 4, y, F, (int)mode,
+               budget);
     return hipGetLastError();
 }
 

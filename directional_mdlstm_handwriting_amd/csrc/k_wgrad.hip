@@ -23,7 +23,7 @@
 
 namespace mdl {
 
-WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H, int64_t nflags) {
+WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H, int64_t nflags, int64_t nfflags) {
     auto al = [](size_t v) { return (v + 255) & ~size_t(255); };
     WsLayout w;
     const int G = 5 * H;
@@ -35,6 +35,7 @@ WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H, int64_t nflags) {
     w.part = p;  p = al(p + sizeof(float) * 4 * (size_t)nparts * R * G);
     w.dxp = p;   p = al(p + sizeof(float) * 4 * (size_t)T * C);
     w.flags = p; p = al(p + sizeof(int32_t) * (size_t)nflags);
+    w.fflags = p; p = al(p + sizeof(int32_t) * (size_t)nfflags);
     w.total = p;
     return w;
 }

@@ -50,13 +50,14 @@ struct Dev {
     const int32_t* segs;      // [nsegs][3] (example, first cell, end cell)
     const int32_t* groups;    // [ngroups+1] first segment of each weight-gradient workgroup
     const int32_t* gorder;    // [4 ngroups] the weight-gradient tasks (4 group + direction) in readiness order
+    const int32_t* dsum;      // [nsum][3] direction-sum chunks (example, first pixel, end pixel) in readiness order
     int32_t* eid;             // [Hc*Wc]
     uint8_t* border;          // [Hc*Wc]
     int n, Hc, Wc;
     int64_t T;                // computed cells per direction
     int64_t N;                // real pixels
     int max_depth, max_diag;
-    int nsegs, ngroups;
+    int nsegs, ngroups, nsum;
 };
 
 // Canvas position of the direction-local cell (a, b) of an example whose
@@ -125,11 +126,12 @@ struct WsLayout {
     size_t part = 0;    // float [nparts][4][(C+1+2H)*5H]: weight-gradient partial sums
     size_t dxp = 0;     // float [4][T][C]: each direction's share of the input gradient
     size_t flags = 0;   // int32 [4n + 8 ngroups + kFlagTail]: the weight-gradient overlap's flags (OverlapFlags)
+    size_t fflags = 0;  // int32 [4n + 2 nsum + kFlagTail]: the direction sum's overlap with the forward (OverlapFlags)
     size_t total = 0;
     int64_t nparts = 0;
 };
 constexpr int kFlagTail = 16;
-WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H, int64_t nflags);
+WsLayout ws_layout(int64_t T, int64_t nparts, int C, int H, int64_t nflags, int64_t nfflags);
 // the flags and counters of the weight gradient's overlap with the reverse wavefront, in the workspace's
 // flags region ([4n] done, [4 ngroups] taken, [4 ngroups] abandoned, then the four single counters), all zero
 // before the reverse wavefront
@@ -165,9 +167,10 @@ bool chain_uses_mfma(int H, int Lmax);
 // (split operands, fp32-class accuracy); supported for the instantiated (H, C, dtype) combinations
 bool fwd16_supported(int H, int C, int dtype, int Lmax);
 size_t fwd16_lds(int H, int C, int dtype, int Lmax);
+// done (may be null): [4n] flags, unit (example e, direction d) sets done[4e + d] once its h stores are visible
 hipError_t launch_fwd16(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
                         const float* b, const float* Ul, const float* Uu, float* stash, float* h_dirs,
-                        hipStream_t st);
+                        int32_t* done, hipStream_t st);
 // reverse wavefront on the f16 matrix cores (split, power-of-two scaled operands)
 bool bwd16_supported(int H, int Lmax);
 size_t bwd16_lds(int H, int Lmax);
@@ -187,6 +190,13 @@ hipError_t launch_bwd_small(const Dev& D, int H, const float* Ul, const float* U
 hipError_t launch_fwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* Z,
                             float* stash, float* h_dirs, hipStream_t st);
 hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat, hipStream_t st);
+// the direction sum in the layout's chunks (D.dsum), for the overlap with the forward: whether the chunked
+// form runs for these buffers (4-wide vectors), and its launches, taking chunks from the claim queue in F as
+// launch_wgrad2_claim takes tasks (kClaimBeside: waits, bounded by `budget`, until the example's four forward
+// units are flagged in F.done; kClaimDrain: one workgroup per queue position not taken; kClaimAbandoned)
+bool dirsum_chunked_supported(const Dev& D, const float* h_dirs, int H, const float* y_flat);
+hipError_t launch_dirsum_claim(const Dev& D, const float* h_dirs, int H, float* y_flat, const OverlapFlags& F,
+                               WgClaim mode, int workgroups, long long budget, hipStream_t st);
 hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                             const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
 // software-pipelined weight-gradient kernel for the instantiated (C, H, dtype) shapes

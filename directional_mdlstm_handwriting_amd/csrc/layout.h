@@ -46,6 +46,8 @@ constexpr int kGroups = 512;
 constexpr int kGroupMinCells = 512;
 constexpr int kGroupRound = 128;
 constexpr int kGroupSegs = 16;
+// Direction-sum chunks (see Layout::dsum): runs of at most kSumChunk real pixels of one example.
+constexpr int kSumChunk = 256;
 
 struct DescOffsets {
     size_t rect = 0;      // int32 [n][4] computed region (y0, x0, h, w)
@@ -56,6 +58,7 @@ struct DescOffsets {
     size_t segs = 0;      // int32 [nsegs][3] (example, first cell, end cell) of the weight-gradient split
     size_t groups = 0;    // int32 [ngroups+1] first segment of each weight-gradient workgroup
     size_t gorder = 0;    // int32 [4 ngroups] the weight-gradient tasks (4 group + direction) in readiness order
+    size_t dsum = 0;      // int32 [nsum][3] direction-sum chunks (example, first pixel, end pixel) in readiness order
     size_t eid = 0;       // int32 [Hc*Wc]
     size_t border = 0;    // uint8 [Hc*Wc]
     size_t total = 0;
@@ -83,7 +86,11 @@ struct Layout {
     // count (h + w - 1) of the group's examples, ties by task index: the order in which they become ready
     // while the reverse wavefront runs (its units all start together)
     std::vector<int32_t> gorder;
-    int32_t nsegs = 0, ngroups = 0;
+    // the direction sum's chunks: runs of at most kSumChunk real pixels (row-major in the example's real
+    // region), the examples in the order their forward units finish (fewest dependent steps first, ties
+    // by index), each example's chunks in pixel order
+    std::vector<int32_t> dsum;
+    int32_t nsegs = 0, ngroups = 0, nsum = 0;
     int64_t nparts() const { return nsegs > ngroups ? nsegs : ngroups; }
     DescOffsets off;
     std::vector<uint8_t> host_desc;  // descriptor bytes up to off.eid (the maps are built on device)

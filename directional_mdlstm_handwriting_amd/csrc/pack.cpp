@@ -91,6 +91,24 @@ void split_wgrad(Layout& L) {
                      [&](int32_t a, int32_t b) { return key[a >> 2] < key[b >> 2]; });
 }
 
+// The direction sum's chunks in readiness order (Layout::dsum).
+void split_dsum(Layout& L) {
+    std::vector<int32_t> ord(L.n);
+    std::iota(ord.begin(), ord.end(), 0);
+    auto depth = [&](int32_t e) { return L.rect[4 * e + 2] + L.rect[4 * e + 3] - 1; };
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t a, int32_t b) { return depth(a) < depth(b); });
+    L.dsum.clear();
+    for (const int32_t e : ord) {
+        const int64_t np = (int64_t)L.real[4 * e + 2] * L.real[4 * e + 3];
+        for (int64_t p0 = 0; p0 < np; p0 += kSumChunk) {
+            L.dsum.push_back(e);
+            L.dsum.push_back((int32_t)p0);
+            L.dsum.push_back((int32_t)std::min<int64_t>(np, p0 + kSumChunk));
+        }
+    }
+    L.nsum = (int32_t)(L.dsum.size() / 3);
+}
+
 void finish(Layout& L) {
     const int n = L.n;
     L.flat_off.assign(n + 1, 0);
@@ -118,6 +136,7 @@ void finish(Layout& L) {
     });
     paint_maps(L);
     split_wgrad(L);
+    split_dsum(L);
 
     DescOffsets& o = L.off;
     size_t p = 0;
@@ -129,6 +148,7 @@ void finish(Layout& L) {
     o.segs = p;     p = align256(p + sizeof(int32_t) * L.segs.size());
     o.groups = p;   p = align256(p + sizeof(int32_t) * L.groups.size());
     o.gorder = p;   p = align256(p + sizeof(int32_t) * L.gorder.size());
+    o.dsum = p;     p = align256(p + sizeof(int32_t) * L.dsum.size());
     o.eid = p;      p = align256(p + sizeof(int32_t) * (size_t)L.Hc * L.Wc);
     o.border = p;   p = align256(p + (size_t)L.Hc * L.Wc);
     o.total = p;
@@ -141,6 +161,7 @@ void finish(Layout& L) {
     std::memcpy(&L.host_desc[o.segs], L.segs.data(), sizeof(int32_t) * L.segs.size());
     std::memcpy(&L.host_desc[o.groups], L.groups.data(), sizeof(int32_t) * L.groups.size());
     std::memcpy(&L.host_desc[o.gorder], L.gorder.data(), sizeof(int32_t) * L.gorder.size());
+    std::memcpy(&L.host_desc[o.dsum], L.dsum.data(), sizeof(int32_t) * L.dsum.size());
 }
 
 }  // namespace

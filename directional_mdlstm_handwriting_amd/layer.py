@@ -19,7 +19,7 @@ import numpy as np
 import torch
 
 from . import (MDL_BF16, MDL_CELL_LEAKY_LP, MDL_CELL_MDLSTM, MDL_F32, MDL_PACK_ALG1, MDL_PACK_EXACT, MDL_PACK_PADDED, Layout, mdl_backward,
-               mdl_blockconv_backward, mdl_blockconv_forward, mdl_blockconv_workspace_size, mdl_dirsum_unpack, mdl_forward,
+               mdl_blockconv_backward, mdl_blockconv_forward, mdl_blockconv_workspace_size, mdl_dirsum_unpack, mdl_forward, mdl_forward_dirsum,
                mdl_layout_device_size, mdl_layout_rects, mdl_layout_upload, mdl_pack, mdl_pack_level, mdl_scatter, mdl_workspace_size,
                mdl_ctc_head, mdl_ctc_workspace_size)
 
@@ -120,6 +120,11 @@ class PackedLayer:
 
     def dirsum(self, stream=None):
         mdl_dirsum_unpack(self.dl.layout, self.dl.desc, self.h_dirs, self.H, self.y, stream)
+
+    def forward_dirsum(self, P: DeviceParams, stream=None):
+        """forward() and dirsum() in one call, the direction sum overlapping the wavefront where it can."""
+        mdl_forward_dirsum(self.dl.layout, self.dl.desc, self.x_canvas, self.x_dtype, self.C, self.H, P.cell, P.Wx,
+                           P.Ul, P.Uu, P.b, P.Vl, P.Vu, self.h_dirs, self.y, self.ws, self.ws_bytes, stream)
 
     def backward(self, P: DeviceParams, grads: "LayerGrads", dy_flat=None, dh_dirs=None, dx_flat=None,
                  dx_canvas=None, stream=None):

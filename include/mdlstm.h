@@ -233,6 +233,28 @@ int mdl_forward(const mdl_layout* layout, const void* d_desc, const void* x_canv
                 size_t ws_bytes, void* stream);
 
 /*
+ * mdl_forward followed by mdl_dirsum_unpack (the layer output: the four
+ * directions' h added in direction order and un-packed to the flat per-example
+ * layout, "No Padding Please" §III, §V-A), in one call. y_flat [sum h*w][H]
+ * float32, flat per example in input order, must not be NULL. When the
+ * wavefront's (example, direction) units leave at least half of the device's
+ * compute units free (f16 wavefront, H a multiple of 4, 16-byte aligned h_dirs
+ * and y_flat), the direction sum overlaps the wavefront: each unit flags itself
+ * once its h plane is stored, workgroups on the library's own stream (as in
+ * mdl_backward) sum the output in runs of at most 256 pixels of one example,
+ * in the order the examples finish, once all four of an example's units are
+ * done, and a launch on `stream` after the wavefront takes the runs they did
+ * not get to. Every run is summed by the same code whichever launch takes it,
+ * so y equals mdl_dirsum_unpack's bit for bit. Every wait is bounded, and
+ * mdl_set_wgrad_overlap's mode applies to this overlap as well. Arguments and
+ * errors otherwise as mdl_forward; ws: >= mdl_workspace_size bytes.
+ */
+int mdl_forward_dirsum(const mdl_layout* layout, const void* d_desc, const void* x_canvas, int32_t x_dtype,
+                       int32_t C, int32_t H, int32_t cell, const float* Wx, const float* Ul, const float* Uu,
+                       const float* b, const float* Vl, const float* Vu, float* h_dirs, float* y_flat,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
  * The pages' own schedule of the recurrence, for comparison with the local
  * diagonals of mdl_forward / mdl_backward ("No Padding Please" §IV-A, Figure 3:
  * the whole packed canvas skewed, row i shifted right by i, and computed one
@@ -400,7 +422,8 @@ int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_fl
 /*
  * Kernel timing (measurement support). mdl_timing(1) makes every later launch
  * of a kernel group (names: "build_maps", "scatter", "zero_fill", "projection",
- * "fwd_wavefront", "dirsum", "bwd_wavefront", "wgrad_overlap" (on the library's
+ * "fwd_wavefront", "dirsum_overlap" (on the library's own stream, concurrent with
+ * "fwd_wavefront"), "dirsum", "bwd_wavefront", "wgrad_overlap" (on the library's
  * own stream, concurrent with "bwd_wavefront"), "wgrad", "conv_fwd", "conv_bwd",
  * "ctc_head")
  * hand each of its dispatches a HIP event pair that the dispatch itself
@@ -419,10 +442,11 @@ int mdl_ctc_head(const mdl_layout* layout, const void* d_desc, const float* y_fl
 int mdl_timing(int32_t enable);
 int mdl_timing_only(const char* group);
 
-/* Sets the weight gradient's overlap with the reverse wavefront (mdl_backward), process-wide: 1 on
- * (default), 0 off, 2 on with no time allowed for any wait (every task claimed beside the wavefront is
- * given up there and computed after it: the path a wait that runs out of time takes, for tests). The
- * results do not depend on it. MDL_EINVAL for any other mode. */
+/* Sets the overlaps with the wavefronts, process-wide: the weight gradients beside the reverse wavefront
+ * (mdl_backward) and the direction sum beside the forward one (mdl_forward_dirsum). 1 on (default), 0 off,
+ * 2 on with no time allowed for any wait (every task or run claimed beside a wavefront is given up there and
+ * computed after it: the path a wait that runs out of time takes, for tests). The results do not depend on
+ * it. MDL_EINVAL for any other mode. */
 int mdl_set_wgrad_overlap(int32_t mode);
 int mdl_timing_report(int32_t max, char* names, double* total_ms, int64_t* launches, int32_t* count);
 

@@ -187,6 +187,15 @@ def test_error_codes():
         assert rc not in (M.MDL_EUNSUPPORTED, M.MDL_ESIZE, M.MDL_EINVAL), M.mdl_last_error()
 
 
+def test_forward_dirsum_needs_its_output():
+    lay = M.mdl_pack([3, 4], [5, 6], 8, 1)
+    ws = M.mdl_workspace_size(lay, 4, 16)
+    lib = M._lib
+    assert lib.mdl_forward_dirsum(lay.handle, 1, 1, 0, 4, 16, 0, 1, 1, 1, 1, None, None, 1, None, 1,
+                                  ctypes.c_size_t(ws), None) == M.MDL_EINVAL
+    assert "mdl_forward_dirsum" in M.mdl_last_error()
+
+
 def test_wgrad_overlap_modes():
     for bad in (-1, 3):
         with pytest.raises(M.MdlError) as e:
