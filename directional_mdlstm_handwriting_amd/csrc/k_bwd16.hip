@@ -30,6 +30,10 @@
 //     for the weight gradients. Their stash and upstream-gradient reads are issued KPD diagonals ahead.
 // Rows of the LDS A operand are permuted so the 16 lanes gathering one K block read 16 consecutive rows
 // on distinct banks.
+// An element thread owns hidden units m and m + HE/2 of its cell, so that each of its global loads and stores
+// (one unit per instruction) covers one contiguous run of the cell's units across the lanes. In LDS the two
+// units sit side by side: the K order of the A operand and of the weight rows, and the column order of X, Y
+// and the dc rows, place unit k at 2 (k mod HE/2) + k div (HE/2) within each gate.
 #include "kernels.h"
 #include "devmath.h"
 
@@ -50,6 +54,7 @@ struct B16Shape {
     static constexpr int KP = (5 * H + 31) / 32 * 32;  // K extent of one cell's da: 5H, padded
     static constexpr int KT = KP / 32;              // K blocks of 32
     static_assert(NB <= 2, "hidden size above 32");
+    static_assert(H % 16 == 0, "hidden size not a multiple of 16");
 };
 
 template <int N>
@@ -112,11 +117,11 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
     // stride CS floats) and the split, scaled da as f16 [hi | lo][gate][unit] (each piece KP halves, row
     // stride RA); one buffer each of the products X and Y of the later diagonal (row stride CS). The small
     // buffers come first, where the 16-bit offsets of the LDS instructions reach them. Diagonal position j
-    // lives in row P(j) (below); ZR is a zero row, XR absorbs the writes of padding units. Each cell group's
+    // lives in row P(j) (below); ZR is a zero row. Each cell group's
     // block of 16 rows is shifted by a further SK (A, exponents) or SKC (the float rows) bytes per group, so
     // that the cells of different groups that one wave writes together fall on different banks.
     constexpr int RA = 2 * KP + 8, CS = HE + 4;
-    constexpr int NRW = 16 * CG + 2, ZR = 16 * CG, XR = 16 * CG + 1;
+    constexpr int NRW = 16 * CG + 1, ZR = 16 * CG;
     constexpr int SK = 128 / CG, SKC = NB == 1 ? 64 : 0, NBLK = NRW / 16 + 1;
     constexpr int ABUF = NRW * RA * 2 + NBLK * SK, EBUF = NRW * HP2 * 4 + NBLK * SK, CBUF = NRW * CS * 4 + NBLK * SKC;
     auto rowA = [](int r) { return r * RA * 2 + (r >> 4) * SK; };    // byte offsets of row r in a buffer
@@ -156,9 +161,9 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
         const int q = lane >> 4, col = lane & 15;
         // A wave computes two output column blocks ("pairs") for its 16 cells: with one block of hidden
         // units, X and Y of that block; with two, blocks 0 and 1 of X (kb = 0) or of Y (kb = 1).
-        // B operand of pair p: U^T rows in the (gate, unit) K order, which is the order of U's columns: for
-        // K block t the lane holds K rows 32t + 8q + i, i < 8 (zero from 5H on). Scaled per output column
-        // by 2^E and split into f16 hi + lo.
+        // B operand of pair p: U^T rows in the K order of the A operand (gate-major; within a gate, unit k at
+        // 2 (k mod HP2) + k div HP2): for K block t the lane holds K rows 32t + 8q + i, i < 8 (zero from 5H on).
+        // Scaled per output column by 2^E and split into f16 hi + lo.
         auto pair_y = [&](int p) { return NB == 1 ? p : kb; };               // pair computes Y (uses Uu)
         auto pair_col = [&](int p) { return 16 * (NB == 1 ? 0 : p) + col; };  // output hidden unit
         f16x8 Bh[2][KT], Bl[2][KT];
@@ -174,8 +179,10 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const int kk = 32 * t + 8 * q + i;
+                    const int pk = kk % H;  // position within the gate
+                    const int uk = kk - pk + (pk >> 1) + (pk & 1) * HP2;  // U column: (gate, unit)
                     float x = 0.f;
-                    if (kc < H && kk < G) x = U[((int64_t)d * H + kc) * G + kk];
+                    if (kk < G) x = U[((int64_t)d * H + kc) * G + uk];
                     v[t][i] = x;
                     m = fmaxf(m, fabsf(x));
                 }
@@ -227,20 +234,31 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
             // products wait only for the operands they take
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * KT + 4, 0);  // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, 6 * KT, 0);      // the products
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp)
+            // output unit k goes to column 2 (k mod HP2) + k div HP2: with two blocks of units (both pairs
+            // of one product) units col and 16 + col are one 8-byte word
+            if constexpr (NB == 2) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    *reinterpret_cast<float*>(smem + (pair_y(pp) ? OFF_Y : OFF_X) + rowC(orow + r) + pair_col(pp) * 4) =
-                        ldexpf(acc[pp][r], ec[pp] - er[r]);
+                    *reinterpret_cast<f32x2*>(smem + (kb ? OFF_Y : OFF_X) + rowC(orow + r) + col * 8) =
+                        f32x2{ldexpf(acc[0][r], ec[0] - er[r]), ldexpf(acc[1][r], ec[1] - er[r])};
+            } else {
+                const int oc = (2 * (col % HP2) + col / HP2) * 4;
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        *reinterpret_cast<float*>(smem + (pp ? OFF_Y : OFF_X) + rowC(orow + r) + oc) =
+                            ldexpf(acc[pp][r], ec[pp] - er[r]);
+            }
             __syncthreads();  // X and Y of diagonal s + 1 are in LDS
             __syncthreads();  // the element waves have written diagonal s's gate gradients
         }
     } else {
     // ================= element role =================
-    // Each thread owns NE pairs of adjacent hidden units (2m, 2m + 1) of one diagonal position: the HE / 2
-    // lanes of a cell sit in one DPP row (H = 32) or half-row (H = 16), and each gate's f16 pair goes to
-    // LDS as one 4-byte word.
+    // Each thread owns NE pairs of hidden units (m, m + HP2) of one diagonal position: the HP2 lanes of a
+    // cell sit in one DPP row (H = 32) or half-row (H = 16), each of its global accesses is one unit (the HP2
+    // lanes of a cell read or write one contiguous run), and in LDS the pair is adjacent, so each gate's f16
+    // pair goes to LDS as one 4-byte word.
     const int ry0 = D.real[4 * e], rx0 = D.real[4 * e + 1], rh = D.real[4 * e + 2], rw = D.real[4 * e + 3];
     const int et = tid - 64 * kMatWaves;
     const int64_t base = (int64_t)d * D.T + D.cell_off[e];
@@ -269,19 +287,17 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
     // real region in unit coordinates: a in [ar0, ar1), b in [br0, br1)
     const int ar0 = (d & 2) ? h - (ry0 - y0) - rh : ry0 - y0, ar1 = ar0 + rh;
     const int br0 = (d & 1) ? w - (rx0 - x0) - rw : rx0 - x0, br1 = br0 + rw;
-    int pj[NE], vu[NE], ve[NE];
-    bool pk_ok[NE];
+    int pj[NE], vu[NE], ve[NE];  // position; upstream-gradient and stash offsets of unit m (unit m + HP2 follows
+                                 // at + 4 HP2 bytes and + HP2 elements)
     int wa[NE], we[NE], wc[NE];  // own LDS offsets (within a buffer)
     int oc[NE][3];               // LDS row offsets (stride CS) of positions pj - 1, pj, pj + 1
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
         const int el = et + ET * n;
         pj[n] = el / HP2;
-        const int pm = el - pj[n] * HP2, k0 = 2 * pm;
-        pk_ok[n] = k0 < H;
-        const int kc = k0 < H ? k0 : 0;
-        vu[n] = pj[n] * UA + 4 * kc;
-        ve[n] = pj[n] * H + kc;
+        const int pm = el - pj[n] * HP2, k0 = 2 * pm;  // units pm, pm + HP2; LDS columns k0, k0 + 1
+        vu[n] = pj[n] * UA + 4 * pm;
+        ve[n] = pj[n] * H + pm;
         const int pr = P(pj[n]);
         wa[n] = rowA(pr) + 2 * k0;
         we[n] = rowE(pr) + 4 * pm;
@@ -289,11 +305,7 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
 #pragma unroll
         for (int m = 0; m < 3; ++m) oc[n][m] = rowC(P(pj[n] + m - 1)) + 4 * k0;
     }
-    // writes of padding units (hidden sizes that are not a multiple of 16) go to the discard row
-    const int pm0 = et % HP2;
-    const int xa = rowA(XR), xe = rowE(XR) + 4 * pm0, xc = rowC(XR) + 8 * pm0;
-
-    // the forward's values of this thread's units on one diagonal (SA, SB; two units each) and their
+    // the forward's values of this thread's units on one diagonal (SA, SB; one unit each) and their
     // upstream gradient
     struct Fw {
         f32x4 fa[NE][2], fb[NE][2];
@@ -310,15 +322,18 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
 #pragma unroll
         for (int n = 0; n < NE; ++n) {
             // predicates combined without short-circuit evaluation: plain selects, no branches
-            const bool ok = (pj[n] < L1) & pk_ok[n];
+            const bool ok = pj[n] < L1;
             const int so = ok ? (pe + ve[n]) * 16 : kOOB;
 #pragma unroll
             for (int u2 = 0; u2 < 2; ++u2) {
-                f.fa[n][u2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, so + 16 * u2, 0, 0));
-                f.fb[n][u2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS2, so + 16 * u2, 0, 0));
+                f.fa[n][u2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS4, so + 16 * HP2 * u2, 0, 0));
+                f.fb[n][u2] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rS2, so + 16 * HP2 * u2, 0, 0));
             }
             const bool vy = ok & (per_dir | ((pj[n] >= jr0) & (pj[n] < jr1)));
-            f.dy[n] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rU, vy ? pu0 + vu[n] : kOOB, 0, 0));
+            const int uo = vy ? pu0 + vu[n] : kOOB;
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2)
+                f.dy[n][u2] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rU, uo + 4 * HP2 * u2, 0, 0));
         }
     };
 
@@ -361,11 +376,10 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
             // written, still holds the zeros of the start.
             rr[n] = L0 + (dn ? oc[n][0] : oc[n][1]);
             rd[n] = L0 + (dn ? oc[n][1] : oc[n][2]);
-            const bool ok = (j < L) & pk_ok[n];
-            // units beyond H (hidden sizes that are not a multiple of 16) write to the discard row
-            oa[n] = L0 + (H == HE ? wa[n] : (pk_ok[n] ? wa[n] : xa)) + CB * ABUF;
-            oe[n] = L0 + (H == HE ? we[n] : (pk_ok[n] ? we[n] : xe));
-            ocw[n] = L0 + (H == HE ? wc[n] : (pk_ok[n] ? wc[n] : xc));
+            const bool ok = j < L;
+            oa[n] = L0 + wa[n] + CB * ABUF;
+            oe[n] = L0 + we[n];
+            ocw[n] = L0 + wc[n];
             const int el = pe + ve[n];
             og4[n] = ok ? el * 16 : kOOB;
             og1[n] = ok ? el * 4 : kOOB;
@@ -446,7 +460,7 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
                     sv[u2][g] = ldexpf(dd[n][u2][g], E);
                     tv[u2][g] = hi_part(sv[u2][g]);
                 }
-            // gate g of unit k goes to K = g H + k: the pair of units is one word per gate and piece
+            // gate g of the thread's units goes to K = g H + k0, k0 + 1: one word per gate and piece
 #pragma unroll
             for (int g = 0; g < 5; ++g) {
                 const f16x2 hp = __builtin_convertvector((f32x2){tv[0][g], tv[1][g]}, f16x2);
@@ -459,9 +473,11 @@ __global__ __launch_bounds__(64 * (kMatWaves + EW)) void k_bwd16(Dev D, const fl
             for (int u2 = 0; u2 < 2; ++u2)
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(u32x4, f32x4{dd[n][u2][0], dd[n][u2][1], dd[n][u2][2], dd[n][u2][3]}), rA4,
-                    og4[n] + 16 * u2, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, f32x2{dd[n][0][4], dd[n][1][4]}), rA1,
-                                                  og1[n], 0, 0);
+                    og4[n] + 16 * HP2 * u2, 0, 0);
+#pragma unroll
+            for (int u2 = 0; u2 < 2; ++u2)
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, dd[n][u2][4]), rA1,
+                                                      og1[n] + 4 * HP2 * u2, 0, 0);
         }
         st -= diag_len(s - 1);
         __syncthreads();  // diagonal s's gate gradients are written
@@ -522,7 +538,7 @@ const B16Entry* b16_entry(int H, int Lmax) {
 }
 
 size_t b16_lds(const B16Entry& m) {
-    const size_t nrw = 16 * (size_t)m.CG + 2, he = 16 * (size_t)m.NB, nblk = nrw / 16 + 1;
+    const size_t nrw = 16 * (size_t)m.CG + 1, he = 16 * (size_t)m.NB, nblk = nrw / 16 + 1;
     const size_t kp = (5 * (size_t)m.H + 31) / 32 * 32, ra = 2 * kp + 8, cs = he + 4;
     const size_t sk = 128 / m.CG, skc = m.NB == 1 ? 64 : 0;
     const size_t ebuf = nrw * (he / 2) * 4 + nblk * sk, cbuf = nrw * cs * 4 + nblk * skc;
