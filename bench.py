@@ -169,7 +169,8 @@ def roofline(kernel, avg_ms, model, bmin, H=None):
 # Every source file a kernel group is compiled from; a counter summary holds for the digest of all of them.
 _COMMON = ("devmath.h", "kernels.h")
 KERNEL_SOURCES = {
-    "projection": ("k_proj.hip",), "fwd_wavefront": ("k_fwd16.hip", "k_small.hip", "k_chain.hip") + _COMMON,
+    "projection": ("k_proj.hip",), "fwd_wavefront": ("k_fwd16.hip", "k_fwd16.h", "k_fwd16_h32.hip", "k_small.hip", "k_chain.hip")
+    + _COMMON,
     "bwd_wavefront": ("k_bwd16.hip", "k_small.hip", "k_chain.hip") + _COMMON,
     "wgrad": ("k_wgrad2.hip", "k_wgrad.hip") + _COMMON, "wgrad_mem": ("k_leaky.hip",) + _COMMON,
     "dirsum": ("k_layout.hip",), "scatter": ("k_layout.hip",), "zero_fill": ("k_layout.hip",),
