@@ -65,14 +65,17 @@ struct WgShape {
     static constexpr int ND4 = (H + TPC - 1) / TPC;       // dA4 loads per thread (16 bytes)
     static constexpr int ND1 = (NV1 + TPC - 1) / TPC;     // dA1 loads per thread
     static constexpr int NXL = (C + TPC - 1) / TPC;       // x loads per thread
-    static constexpr int NPW = (G + 4 * NWV - 1) / (4 * NWV) * 4;  // dx gate columns per wave (whole quarters)
-    static constexpr int NPQ = NPW / 4;                   // columns of each quarter
-    static constexpr int NC4 = (C + 3) / 4;               // groups of 4 input channels
+    static constexpr int NPW = (G + 4 * NWV - 1) / (4 * NWV) * 4;  // dx gate columns per wave
+    static constexpr int CP = (C + 3) / 4 * 4;            // dx weight row: channels padded to 16-byte vectors
+    static constexpr int NWX = NWV * NPW;                 // dx weight rows (gate columns, zero from G on)
+    // workgroups per compute unit the registers are held to (the LDS of two fits at every shape used)
+    static constexpr int OCC = 2;
     // tiles whose loads are in flight ahead of the one computed: two where a second set of staging registers
     // leaves the occupancy as it is (hidden sizes up to 16), else one
     static constexpr int PF = H <= 16 ? 2 : 1;
     static_assert(MT * NTW <= 16, "at most 16 product tiles per wave");
-    static_assert(C <= 16, "dx product assumes at most 16 input channels");
+    static_assert(C <= 16, "dx accumulators: at most 16 input channels");
+    static_assert(TP == 64, "dx: one cell of the tile per lane");
     static_assert(NWV * NPW <= NR, "dx column shares stay inside the gate-column rows");
     static_assert(NTH % TP == 0 && (TPC & (TPC - 1)) == 0, "whole power-of-two thread groups per cell");
 };
@@ -128,17 +131,6 @@ __device__ inline void split3(const f32x4& x0, const f32x4& x1, u32x4 (&p)[3]) {
         for (int i = 0; i < 4; ++i) p[k][i] = __builtin_amdgcn_perm(u[k][2 * i + 1], u[k][2 * i], 0x07060302u);
 }
 
-// (q0 + q1) + (q2 + q3) in every lane, q_i the value of lane l % 16 + 16 i: the lane-row swaps exchange
-// rows 0 <-> 1 and 2 <-> 3 (v_permlane16_swap), then the wave halves (v_permlane32_swap), in the VALU
-__device__ inline float quarter_sum(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // {rows 0,0,2,2 ; rows 1,1,3,3}
-    const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const uint32_t t = __float_as_uint(s);
-    const auto b = __builtin_amdgcn_permlane32_swap(t, t, false, false);  // {low half twice ; high half twice}
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // position of region-local cell (ly, lx) of an h x w region in direction d's diagonal-major order
 __device__ inline int stash_pos(int h, int w, int ly, int lx, int d) {
     const int a = (d & 2) ? h - 1 - ly : ly;
@@ -157,7 +149,7 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
     using S = WgShape<C, H>;
     constexpr int G = S::G, R = S::R, MT = S::MT, NT = S::NT, NTW = S::NTW, TP = S::TP;
     constexpr int NR = S::NR, TPD = S::TPD, TPD16 = S::TPD16, RPS = S::RPS, VH = S::VH, NWV = S::NWV,
-                  NPW = S::NPW, NPQ = S::NPQ, NC4 = S::NC4;
+                  NPW = S::NPW;
     constexpr int TPC = S::TPC, NVH = S::NVH, NV1 = S::NV1, NHL = S::NHL, ND4 = S::ND4, ND1 = S::ND1, NXL = S::NXL;
     // the launch's block size as a compile-time stride: the block size read at run time is a memory load, and
     // its wait would also wait for every tile load in flight
@@ -197,10 +189,15 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
     uint16_t* rp = reinterpret_cast<uint16_t*>(smem);
     float* das = reinterpret_cast<float*>(smem + S::RPB);
     float* dxs = das + NR * TPD;
-    constexpr int NWORDS = S::RPB / 4 + NR * TPD + NWV * TP * C;
+    float* wxs = dxs + NWV * TP * C;  // Wx_d^T [NWX][CP]: row = gate column, read by every lane at once
+    constexpr int NWORDS = S::RPB / 4 + NR * TPD + NWV * TP * C + S::NWX * S::CP;
     for (int i = tid; i < NWORDS; i += NTH) reinterpret_cast<uint32_t*>(smem)[i] = 0u;
     __syncthreads();
     for (int i = tid; i < TP; i += NTH) rp[C * TPD16 + i] = 0x3F80;  // the bias row: 1 = 1 + 0 + 0
+    for (int i = tid; i < G * C; i += NTH) {
+        const int col = i / C, c = i - col * C;
+        wxs[col * S::CP + c] = Wx[((int64_t)d * C + c) * G + col];
+    }
     int ntiles = 0;
     for (int sg = 0; sg < nsg; ++sg) ntiles += (sgt[sg][11] - sgt[sg][10] + TP - 1) / TP;
 
@@ -306,19 +303,10 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
         }
     };
 
-    // dx_d = da_d Wx_d^T on v_mfma_f32_4x4x1f32 (16 blocks of 4 x 4 x 1): block b = lane / 4 holds cell group
-    // b % 4 (4 cells) against 4 input channels, over quarter b / 4 of this wave's NPW consecutive gate columns
-    // (columns col0 + 4 sc + quarter); the quarters are added across lanes. Wx_d's values stay in registers.
-    const int xqt = lane >> 4, xi = lane & 3, xcell = lane & 15;  // quarter; row / channel in block; cell
+    // dx_d = da_d Wx_d^T: each wave takes NPW consecutive gate columns (col0 on), each lane one cell of the
+    // tile, with fp32 multiply-adds in column order; a column's weights are one LDS read that every lane
+    // shares (columns from G on are zeros, in both operands)
     const int col0 = wave * NPW;
-    float wxr[NC4][NPQ];
-#pragma unroll
-    for (int g4 = 0; g4 < NC4; ++g4)
-#pragma unroll
-        for (int sc = 0; sc < NPQ; ++sc) {
-            const int col = col0 + 4 * sc + xqt, ch = 4 * g4 + xi;
-            wxr[g4][sc] = (col < G && ch < C) ? Wx[((int64_t)d * C + ch) * G + col] : 0.f;
-        }
     const bool want_dx = dxp != nullptr;
 
     f32x4 acc[MT][NTW];
@@ -400,39 +388,26 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
                 term(0, 0);
             }
         }
-        // this wave's share of dx_d for the tile's cells: the four blocks of 16 cells advance together, so
-        // that consecutive products go to independent accumulators
+        // this wave's share of dx_d for the tile's cells
         if (want_dx) {
-            constexpr int NM2 = TP / 16;
-            const float* arow = das + (col0 + xqt) * TPD + xcell;
-            f32x4 dacc[NM2][NC4];
+            const float* arow = das + col0 * TPD + lane;
+            const float* wrow = wxs + col0 * S::CP;
+            float dv[C];
 #pragma unroll
-            for (int m2 = 0; m2 < NM2; ++m2)
+            for (int c = 0; c < C; ++c) dv[c] = 0.f;
 #pragma unroll
-                for (int g4 = 0; g4 < NC4; ++g4) dacc[m2][g4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < NPW; ++i) {
+                const float a = arow[i * TPD];
 #pragma unroll
-            for (int sc = 0; sc < NPQ; ++sc) {
-                float av[NM2];
+                for (int c4 = 0; c4 < S::CP / 4; ++c4) {
+                    const f32x4 wv = *reinterpret_cast<const f32x4*>(wrow + i * S::CP + 4 * c4);
 #pragma unroll
-                for (int m2 = 0; m2 < NM2; ++m2) av[m2] = arow[4 * sc * TPD + 16 * m2];  // rows from G on are zero
-#pragma unroll
-                for (int g4 = 0; g4 < NC4; ++g4)
-#pragma unroll
-                    for (int m2 = 0; m2 < NM2; ++m2)
-                        dacc[m2][g4] = __builtin_amdgcn_mfma_f32_4x4x1f32(av[m2], wxr[g4][sc], dacc[m2][g4], 0, 0, 0);
+                    for (int j = 0; j < 4; ++j)
+                        if (4 * c4 + j < C) dv[4 * c4 + j] = __builtin_fmaf(a, wv[j], dv[4 * c4 + j]);
+                }
             }
 #pragma unroll
-            for (int m2 = 0; m2 < NM2; ++m2)
-#pragma unroll
-                for (int g4 = 0; g4 < NC4; ++g4)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        // lanes l, l^16, l^32, l^48 hold the four quarters of one (cell, channel); every lane
-                        // ends with (q0 + q1) + (q2 + q3)
-                        const float v = quarter_sum(dacc[m2][g4][r]);
-                        const int ch = 4 * g4 + xi;
-                        if (lane < 16 && ch < C) dxs[(wave * TP + 16 * m2 + 4 * (xcell >> 2) + r) * C + ch] = v;
-                    }
+            for (int c = 0; c < C; ++c) dxs[(wave * TP + lane) * C + c] = dv[c];
         }
         __syncthreads();
         if (want_dx) {
@@ -472,7 +447,7 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
 
 // one workgroup per task (direction-minor: task = 4 group + direction)
 template <bool BF16, int C, int H>
-__global__ __launch_bounds__((64 * WgShape<C, H>::NWV)) void k_wgrad2(Dev D, const void* __restrict__ xc,
+__global__ __launch_bounds__((64 * WgShape<C, H>::NWV), (WgShape<C, H>::OCC)) void k_wgrad2(Dev D, const void* __restrict__ xc,
                                                                      const float* __restrict__ hdirs,
                                                                      const float* __restrict__ dA,
                                                                      const float* __restrict__ Wx,
@@ -523,7 +498,7 @@ __device__ int claim_task(const Dev& D, const OverlapFlags& F, int mode, long lo
 // workgroups on the compute units it leaves free, taking the tasks in the order their units finish) or,
 // after both launches, from the abandoned list.
 template <bool BF16, int C, int H>
-__global__ __launch_bounds__((64 * WgShape<C, H>::NWV)) void k_wgrad2_claim(Dev D, const void* __restrict__ xc,
+__global__ __launch_bounds__((64 * WgShape<C, H>::NWV), (WgShape<C, H>::OCC)) void k_wgrad2_claim(Dev D, const void* __restrict__ xc,
                                                                            const float* __restrict__ hdirs,
                                                                            const float* __restrict__ dA,
                                                                            const float* __restrict__ Wx,
@@ -549,7 +524,7 @@ __global__ __launch_bounds__((64 * WgShape<C, H>::NWV)) void k_wgrad2_claim(Dev 
 // After the reverse wavefront on its stream: workgroup b takes queue position b unless a workgroup beside
 // the wavefront has taken it (every unit is complete, so nothing is waited for).
 template <bool BF16, int C, int H>
-__global__ __launch_bounds__((64 * WgShape<C, H>::NWV)) void k_wgrad2_drain(Dev D, const void* __restrict__ xc,
+__global__ __launch_bounds__((64 * WgShape<C, H>::NWV), (WgShape<C, H>::OCC)) void k_wgrad2_drain(Dev D, const void* __restrict__ xc,
                                                                            const float* __restrict__ hdirs,
                                                                            const float* __restrict__ dA,
                                                                            const float* __restrict__ Wx,
@@ -590,7 +565,7 @@ __global__ __launch_bounds__(256) void k_dx_sum(Dev D, int C, const float* __res
 template <bool BF16, int C, int H>
 size_t wg2_lds() {
     using S = WgShape<C, H>;
-    return (size_t)S::RPB + 4 * ((size_t)S::NR * S::TPD + (size_t)S::NWV * S::TP * C);
+    return (size_t)S::RPB + 4 * ((size_t)S::NR * S::TPD + (size_t)S::NWV * S::TP * C + (size_t)S::NWX * S::CP);
 }
 
 typedef void (*Wg2Kernel)(Dev, const void*, const float*, const float*, const float*, float*, float*);
