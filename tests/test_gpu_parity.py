@@ -261,6 +261,8 @@ RAGGED = [
     ([1, 1, 3, 17, 2, 9], [1, 23, 1, 5, 40, 9], 4, 16),
     ([40, 12, 33, 25], [8, 200, 61, 25], 4, 16),
     ([32, 32, 32], [256, 300, 257], 4, 32),
+    # H = 32 with a diagonal of more than 32 cells: the four-group forward shape (the two-group one holds 32)
+    ([40, 12, 33], [50, 70, 36], 4, 32),
     ([7, 3, 11, 5, 6, 2, 9], [13, 27, 4, 16, 6, 31, 2], 6, 10),
     ([5, 3, 4, 2], [9, 7, 3, 6], 20, 50),
     ([6, 9, 4], [12, 7, 15], 4, 2),
