@@ -101,6 +101,11 @@ mdl::Dev make_dev(const mdl_layout* lay, const void* d_desc) {
     return D;
 }
 
+// LDS each workgroup of a launch beside a wavefront holds so that it cannot share a compute unit with one of the
+// wavefront's workgroups (whose LDS is wave_lds, out of lmax per compute unit): those would then take the compute
+// unit's issue slots from the wavefront's dependent chain, or, placed first, keep a wavefront workgroup waiting
+size_t beside_lds_hold(size_t lmax, size_t wave_lds) { return wave_lds < lmax ? lmax - wave_lds + 256 : 0; }
+
 int max_lds(size_t& out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -483,15 +488,16 @@ static int forward_impl(const char* fn, const mdl_layout* layout, const void* d_
     const long long budget = ov_mode == 2 ? 0 : std::max<long long>(1ll << 26, (long long)L.max_depth << 15);
     {
         Timed t("dirsum_overlap");
-        e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimBeside, ov_wg, budget, side->s);
+        e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimBeside, ov_wg, budget,
+                                     beside_lds_hold(lmax, need), side->s);
     }
     if (e != hipSuccess) return hip_fail(e, F + ": direction sum beside the wavefront");
     if ((e = hipEventRecord(side->join, side->s)) != hipSuccess) return hip_fail(e, F + ": library's stream");
     {
         Timed t("dirsum");
-        e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimDrain, 0, 0, st);
+        e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimDrain, 0, 0, 0, st);
         if (e == hipSuccess && (e = hipStreamWaitEvent(st, side->join, 0)) == hipSuccess)
-            e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimAbandoned, 16, 0, st);
+            e = mdl::launch_dirsum_claim(D, h_dirs, H, y_flat, Fl, mdl::kClaimAbandoned, 16, 0, 0, st);
     }
     if (e != hipSuccess) return hip_fail(e, F + ": direction sum");
     return MDL_OK;
@@ -729,7 +735,7 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
         {
             Timed t("wgrad_overlap");
             e = mdl::launch_wgrad2_claim(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, want_dx ? dxp : nullptr,
-                                         F, mdl::kClaimBeside, ov_wg, budget, side->s);
+                                         F, mdl::kClaimBeside, ov_wg, budget, 0, side->s);
         }
         if (e != hipSuccess) return hip_fail(e, "mdl_backward: weight gradients beside the reverse wavefront");
         if ((e = hipEventRecord(side->join, side->s)) != hipSuccess)
@@ -737,10 +743,10 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
         {
             Timed t("wgrad");
             e = mdl::launch_wgrad2_claim(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part, want_dx ? dxp : nullptr,
-                                         F, mdl::kClaimDrain, 0, 0, st);
+                                         F, mdl::kClaimDrain, 0, 0, 0, st);
             if (e == hipSuccess && (e = hipStreamWaitEvent(st, side->join, 0)) == hipSuccess)
                 e = mdl::launch_wgrad2_claim(D, x_canvas, x_dtype, C, H, h_dirs, dA, Wx, part,
-                                             want_dx ? dxp : nullptr, F, mdl::kClaimAbandoned, 16, 0, st);
+                                             want_dx ? dxp : nullptr, F, mdl::kClaimAbandoned, 16, 0, 0, st);
             if (e == hipSuccess) e = mdl::launch_dx_sum(D, C, dxp, dx_flat, dx_canvas, st);
             if (e == hipSuccess) e = mdl::launch_wgrad_reduce(L.ngroups, C, H, part, dWx, dUl, dUu, db, st);
         }

@@ -325,7 +325,7 @@ bool dirsum_chunked_supported(const Dev& D, const float* h_dirs, int H, const fl
 }
 
 hipError_t launch_dirsum_claim(const Dev& D, const float* h_dirs, int H, float* y_flat, const OverlapFlags& F,
-                               WgClaim mode, int workgroups, long long budget, hipStream_t st) {
+                               WgClaim mode, int workgroups, long long budget, size_t lds_hold, hipStream_t st) {
     if (!dirsum_chunked_supported(D, h_dirs, H, y_flat) || budget < 0) return hipErrorInvalidValue;
     const f32x4* hd = reinterpret_cast<const f32x4*>(h_dirs);
     f32x4* y = reinterpret_cast<f32x4*>(y_flat);
@@ -334,8 +334,8 @@ hipError_t launch_dirsum_claim(const Dev& D, const float* h_dirs, int H, float* 
     else if (workgroups < 1)
         return hipErrorInvalidValue;
     else
-        launch(k_dsum_claim, dim3((unsigned)workgroups), dim3(kSumThreads), 0, st, D, hd, H / 4, y, F, (int)mode,
-               budget);
+        launch(k_dsum_claim, dim3((unsigned)workgroups), dim3(kSumThreads), mode == kClaimBeside ? lds_hold : 0, st, D,
+               hd, H / 4, y, F, (int)mode, budget);
     return hipGetLastError();
 }
 

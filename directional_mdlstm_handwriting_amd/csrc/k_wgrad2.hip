@@ -615,7 +615,7 @@ hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, i
 
 hipError_t launch_wgrad2_claim(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
                                const float* dA, const float* Wx, float* part, float* dxp, const OverlapFlags& F,
-                               WgClaim mode, int workgroups, long long budget, hipStream_t st) {
+                               WgClaim mode, int workgroups, long long budget, size_t lds_hold, hipStream_t st) {
     const Wg2Entry* m = wg2_entry(C, H, dtype != 0);
     if (!m || budget < 0) return hipErrorInvalidValue;
     if (mode == kClaimDrain)
@@ -624,7 +624,8 @@ hipError_t launch_wgrad2_claim(const Dev& D, const void* x_canvas, int dtype, in
     else if (workgroups < 1)
         return hipErrorInvalidValue;
     else
-        launch(m->kc, dim3((unsigned)workgroups), dim3(m->threads), m->lds, st, D, x_canvas, h_dirs, dA, Wx, part,
+        launch(m->kc, dim3((unsigned)workgroups), dim3(m->threads),
+               mode == kClaimBeside ? std::max(m->lds, lds_hold) : m->lds, st, D, x_canvas, h_dirs, dA, Wx, part,
                dxp, F, (int)mode, budget);
     return hipGetLastError();
 }

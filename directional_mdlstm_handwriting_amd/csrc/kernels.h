@@ -193,10 +193,12 @@ hipError_t launch_dirsum(const Dev& D, const float* h_dirs, int H, float* y_flat
 // the direction sum in the layout's chunks (D.dsum), for the overlap with the forward: whether the chunked
 // form runs for these buffers (4-wide vectors), and its launches, taking chunks from the claim queue in F as
 // launch_wgrad2_claim takes tasks (kClaimBeside: waits, bounded by `budget`, until the example's four forward
-// units are flagged in F.done; kClaimDrain: one workgroup per queue position not taken; kClaimAbandoned)
+// units are flagged in F.done; kClaimDrain: one workgroup per queue position not taken; kClaimAbandoned).
+// lds_hold: LDS bytes each workgroup of the beside launch holds (at least its own): enough that it cannot share
+// a compute unit with a wavefront workgroup
 bool dirsum_chunked_supported(const Dev& D, const float* h_dirs, int H, const float* y_flat);
 hipError_t launch_dirsum_claim(const Dev& D, const float* h_dirs, int H, float* y_flat, const OverlapFlags& F,
-                               WgClaim mode, int workgroups, long long budget, hipStream_t st);
+                               WgClaim mode, int workgroups, long long budget, size_t lds_hold, hipStream_t st);
 hipError_t launch_bwd_chain(const Dev& D, int H, const float* Ul, const float* Uu, const float* stash,
                             const float* dy_flat, const float* dh_dirs, float* dA, hipStream_t st);
 // software-pipelined weight-gradient kernel for the instantiated (C, H, dtype) shapes
@@ -209,10 +211,11 @@ hipError_t launch_wgrad2(const Dev& D, const void* x_canvas, int dtype, int C, i
 // the same tasks taken from the claim queue in F (in the layout's readiness order): beside the wavefront and
 // from the abandoned list by `workgroups` workgroups that loop until there is none left (beside, each wait for
 // a task's units, flagged in F.done, is bounded by `budget` shader-clock cycles); after the wavefront by one
-// workgroup per queue position whose taken flag is still clear (`workgroups` and `budget` unused)
+// workgroup per queue position whose taken flag is still clear (`workgroups` and `budget` unused); lds_hold as
+// for launch_dirsum_claim
 hipError_t launch_wgrad2_claim(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* h_dirs,
                                const float* dA, const float* Wx, float* part, float* dxp, const OverlapFlags& F,
-                               WgClaim mode, int workgroups, long long budget, hipStream_t st);
+                               WgClaim mode, int workgroups, long long budget, size_t lds_hold, hipStream_t st);
 // dx from the four directions' shares in dxp (added in direction order): dx_flat at the real pixels,
 // dx_canvas at the computed cells (zero outside the real pixels); nothing when both are null
 hipError_t launch_dx_sum(const Dev& D, int C, const float* dxp, float* dx_flat, float* dx_canvas, hipStream_t st);
