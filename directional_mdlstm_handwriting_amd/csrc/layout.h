@@ -43,7 +43,7 @@ MDL_HD inline int64_t dg_start(int h, int w, int s) {
 // least about kGroupMinCells cells each, at most kGroupSegs segments each; from kGroupRound groups on, a
 // multiple of kGroupRound (whole rounds of tasks on a 256-CU device at two workgroups per unit).
 constexpr int kGroups = 512;
-constexpr int kGroupMinCells = 1024;
+constexpr int kGroupMinCells = 512;
 constexpr int kGroupRound = 128;
 constexpr int kGroupSegs = 16;
 // Direction-sum chunks (see Layout::dsum): runs of at most kSumChunk real pixels of one example.
