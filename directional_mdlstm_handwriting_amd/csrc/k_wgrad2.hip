@@ -131,6 +131,17 @@ __device__ inline void split3(const f32x4& x0, const f32x4& x1, u32x4 (&p)[3]) {
         for (int i = 0; i < 4; ++i) p[k][i] = __builtin_amdgcn_perm(u[k][2 * i + 1], u[k][2 * i], 0x07060302u);
 }
 
+// rows of a band in the weight-gradient walk (a power of two)
+constexpr int kBand = 8;
+
+// j / dv for 0 <= j < 2^22 and dv >= 1, from the hardware reciprocal of dv (within one ulp: the estimate is
+// off by at most one)
+__device__ inline int qdiv(int j, int dv) {
+    const int q = (int)((float)j * __builtin_amdgcn_rcpf((float)dv));
+    const int r = j - q * dv;
+    return q + (r >= dv ? 1 : 0) - (r < 0 ? 1 : 0);
+}
+
 // position of region-local cell (ly, lx) of an h x w region in direction d's diagonal-major order
 __device__ inline int stash_pos(int h, int w, int ly, int lx, int d) {
     const int a = (d & 2) ? h - 1 - ly : ly;
@@ -165,8 +176,16 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
     const int64_t plane = (int64_t)D.Hc * D.Wc * H;
 
     // this task's segments, read once into LDS (a global load inside the loop would wait on the
-    // stores): region y0, x0, h, w; real pixels y0, x0, h, w; stash and flat offsets; cell range
-    __shared__ int sgt[kGroupSegs][12];
+    // stores): region y0, x0, h, w; real pixels y0, x0, h, w; stash and flat offsets; cell range; its walk
+    // order. A segment (a row-major cell range of the region) is walked as its head (the rest of a row
+    // it starts inside, in row order), its body (the whole rows after it, in bands of kBand rows, each
+    // band column after column) and its tail (the start of the row it ends inside, in row order): inside
+    // a band a cell's upper predecessor is the cell before it and its left predecessor kBand cells back,
+    // so both are loaded while the cell that loaded them first is recent (still in the L2), and a load
+    // instruction still covers runs of kBand neighbouring pixels of a row. Fields 12..16: head cells, first
+    // body row, body rows, head row, head column. (Two workgroups of the largest shape fill the compute
+    // unit's LDS but for about 1.5 KB, which holds this table and the cell indices below.)
+    __shared__ int sgt[kGroupSegs][17];
     if (tid < nsg) {
         const int sg = sg0 + tid, e = D.segs[3 * sg];
         int* o = sgt[tid];
@@ -177,9 +196,19 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
         }
         o[8] = (int)D.cell_off[e];
         o[9] = (int)D.flat_off[e];
-        o[10] = D.segs[3 * sg + 1];
-        o[11] = D.segs[3 * sg + 2];
+        const int first = D.segs[3 * sg + 1], end = D.segs[3 * sg + 2], w = o[3];
+        const int ya = first / w, xa = first - ya * w, ye = end / w;
+        o[10] = first;
+        o[11] = end;
+        o[12] = ya == ye ? end - first : (xa > 0 ? w - xa : 0);
+        o[13] = ya + (xa > 0 ? 1 : 0);
+        o[14] = ya == ye ? 0 : ye - o[13];
+        o[15] = ya;
+        o[16] = xa;
     }
+    // region-local row-major index of each cell of the tile, for the dx store (written after the tile's
+    // first barrier, read after its second)
+    __shared__ int cids[TP];
 
     // LDS: r as its three bf16 pieces [3][R + 1][TPD16] (component m of r, then the tile's cells; row R stays
     // zero and stands for the rows of the last M tile past R), written split by the thread that loads the value,
@@ -215,6 +244,7 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
     f32x4 vd4[PF][ND4];
     HV vd1[PF][ND1];
     uint32_t vx[PF][NXL];
+    int vci[PF];  // region-local row-major index of the staged cell
     auto issue_loads = [&](auto Bc, int sg, int lt) {
         constexpr int B = decltype(Bc)::value;
         // this thread's cell (tile lt of segment sg): canvas pixel, predecessors in direction d, position
@@ -222,9 +252,31 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
         const int* Sg = sgt[sg];
         const int y0 = Sg[0], x0 = Sg[1], h = Sg[2], w = Sg[3];
         const int cell0 = Sg[8];
-        const int qc = Sg[10] + lt * TP + lc;
-        const bool ok = qc < Sg[11];
-        const int ly = qc / w, lx = qc - ly * w;
+        const int wi = lt * TP + lc;  // position in the segment's walk
+        const bool ok = wi < Sg[11] - Sg[10];
+        const int nhead = Sg[12], yb0 = Sg[13], nrows = Sg[14], nbody = nrows * w;
+        int ly, lx;
+        if (wi < nhead) {
+            ly = Sg[15];
+            lx = Sg[16] + wi;
+        } else if (wi < nhead + nbody) {
+            const int j = wi - nhead;
+            const int nfull = nrows / kBand, fullc = nfull * kBand * w;
+            if (j < fullc) {
+                const int b = qdiv(j, kBand * w);
+                const int jj = j - b * kBand * w;
+                lx = jj / kBand;
+                ly = yb0 + b * kBand + (jj - lx * kBand);
+            } else {
+                const int rbl = nrows - nfull * kBand, jj = j - fullc;
+                lx = qdiv(jj, rbl);
+                ly = yb0 + nfull * kBand + (jj - lx * rbl);
+            }
+        } else {
+            ly = yb0 + nrows;
+            lx = wi - nhead - nbody;
+        }
+        vci[B] = ly * w + lx;
         const int pix = ok ? (y0 + ly) * D.Wc + x0 + lx : -1;
         const bool lok = ok & ((d & 1) ? lx < w - 1 : lx > 0);  // left predecessor (y, x - sx)
         const bool uok = ok & ((d & 2) ? ly < h - 1 : ly > 0);  // upper predecessor (y - sy, x)
@@ -336,6 +388,8 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
     auto tile = [&](int t, auto Bc) {
         write_lds(Bc);
         __syncthreads();
+        // every wave has stored the tile before: its cells' indices, before the next loads reuse vci
+        if (want_dx && pt == 0) cids[lc] = vci[decltype(Bc)::value];
         // the loads of tile t + PF go out once tile t is in LDS, into the buffer it leaves; they are in flight
         // through the products, the dx part and the barrier (with PF = 2, also through all of tile t + 1)
         if (t + PF < ntiles) {
@@ -411,16 +465,17 @@ __device__ __forceinline__ void wgrad_task(const Dev& D, const void* __restrict_
         }
         __syncthreads();
         if (want_dx) {
-            // the tile's cells are consecutive in the cell numbering: one contiguous run of dxp
+            // each cell's C values at its place in the cell numbering (row-major inside the region)
             const int* Sg = sgt[sg];
-            const int q0 = Sg[10] + lt * TP;
-            const int nc = min(TP, Sg[11] - q0);
-            float* out = dxp + ((int64_t)d * D.T + Sg[8] + q0) * C;
+            const int nc = min(TP, Sg[11] - Sg[10] - lt * TP);
+            float* out = dxp + ((int64_t)d * D.T + Sg[8]) * C;
+            const int* ci = cids;
             for (int o = tid; o < nc * C; o += NTH) {
                 float v = dxs[o];
 #pragma unroll
                 for (int wv = 1; wv < NWV; ++wv) v += dxs[wv * TP * C + o];  // waves in order
-                out[o] = v;
+                const int c = o / C;
+                out[(int64_t)ci[c] * C + (o - c * C)] = v;
             }
         }
         advance(sg, lt);
