@@ -482,16 +482,20 @@ bool leaky_supported(int H, int C, int Lmax) {
 }
 
 size_t leaky_fwd_lds(int H, int Lmax) {
+    if (leaky16_used(H, Lmax)) return leaky16_fwd_lds(H, Lmax);
     return sizeof(float) * 2 * (size_t)(16 * leaky_tiles(Lmax) + 1) * (2 * H + 4);
 }
 
 size_t leaky_bwd_lds(int H, int Lmax) {
+    if (leaky16_used(H, Lmax)) return leaky16_bwd_lds(H, Lmax);
     return sizeof(float) * 2 * (size_t)(16 * leaky_tiles(Lmax) + 1) * ((5 * H + 4) + 2 * (H + 4));
 }
 
 hipError_t launch_fwd_leaky(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
                             const float* b, const float* Ul, const float* Uu, const float* Vl, const float* Vu,
                             float* stash, float* h_dirs, hipStream_t st) {
+    if (leaky16_used(H, D.max_diag))
+        return launch_fwd_leaky16(D, x_canvas, dtype, C, H, Wx, b, Ul, Uu, Vl, Vu, stash, h_dirs, st);
     const LeakyEntry* m = leaky_entry(H);
     if (!m) return hipErrorInvalidValue;
     const int NT = leaky_tiles(D.max_diag);
@@ -503,6 +507,8 @@ hipError_t launch_fwd_leaky(const Dev& D, const void* x_canvas, int dtype, int C
 hipError_t launch_bwd_leaky(const Dev& D, int H, const float* Ul, const float* Uu, const float* Vl, const float* Vu,
                             const float* stash, const float* dy_flat, const float* dh_dirs, float* dA,
                             hipStream_t st) {
+    if (leaky16_used(H, D.max_diag))
+        return launch_bwd_leaky16(D, H, Ul, Uu, Vl, Vu, stash, dy_flat, dh_dirs, dA, st);
     const LeakyEntry* m = leaky_entry(H);
     if (!m) return hipErrorInvalidValue;
     const int NT = leaky_tiles(D.max_diag);
