@@ -17,9 +17,9 @@
 //   added. The pieces of h and s are written to LDS once, by the lane that computes them.
 // - Reverse, dh += [da(R), da(D)].[Ul^T; Uu^T] and ds += [da3(R), da3(D)].[Vl^T; Vu^T], on
 //   v_mfma_f32_16x16x32_bf16. The gate gradients are unbounded, and bf16 keeps fp32's exponent range,
-//   so nothing is scaled: every fp32 operand is split exactly into three bf16 pieces (each the leading
-//   8 significant bits of what the ones before leave) and the six terms v_i w_j with i + j <= 2 are kept,
-//   smallest first (each dropped term is below 2^-23 of v w). The gate gradients' pieces are written to
+//   so nothing is scaled: every fp32 operand is split exactly into three bf16 pieces v1 + v2 + v3 (each
+//   the leading 8 significant bits of what the ones before leave) and the six terms v_i w_j with
+//   i + j <= 4 are kept, smallest first (each dropped term is below 2^-23 of v w). The gate gradients' pieces are written to
 //   LDS by the lane that computes them.
 #include "kernels.h"
 #include "devmath.h"
