@@ -20,6 +20,7 @@
 // dVl and dVu are computed here, from the stash's memory states and the lam, o1, o2 columns of dA.
 #include "kernels.h"
 #include "devmath.h"
+#include "leaky16.h"
 
 namespace mdl {
 

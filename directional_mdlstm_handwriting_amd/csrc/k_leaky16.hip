@@ -22,6 +22,7 @@
 //   i + j <= 4 are kept, smallest first (each dropped term is below 2^-23 of v w). The gate gradients' pieces are written to
 //   LDS by the lane that computes them.
 #include "kernels.h"
+#include "leaky16.h"
 #include "devmath.h"
 
 namespace mdl {

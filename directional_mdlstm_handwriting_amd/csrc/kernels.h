@@ -233,17 +233,6 @@ int64_t conv_nchunks(const Dev& Dk1);
 // the Leaky LP cell (k_leaky.hip): forward and reverse wavefronts on the fp32 matrix cores, and the weight
 // gradients of its memory-state projections (partials in `part`, added in workgroup order)
 bool leaky_supported(int H, int C, int Lmax);
-// the Leaky-LP wavefronts on the 16-bit matrix instructions (hidden sizes 16 and 32; k_leaky16.hip), which the
-// launchers below take whenever leaky16_used says they fit
-bool leaky16_used(int H, int Lmax);
-size_t leaky16_fwd_lds(int H, int Lmax);
-size_t leaky16_bwd_lds(int H, int Lmax);
-hipError_t launch_fwd_leaky16(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
-                              const float* b, const float* Ul, const float* Uu, const float* Vl, const float* Vu,
-                              float* stash, float* h_dirs, hipStream_t st);
-hipError_t launch_bwd_leaky16(const Dev& D, int H, const float* Ul, const float* Uu, const float* Vl,
-                              const float* Vu, const float* stash, const float* dy_flat, const float* dh_dirs,
-                              float* dA, hipStream_t st);
 size_t leaky_fwd_lds(int H, int Lmax);
 size_t leaky_bwd_lds(int H, int Lmax);
 hipError_t launch_fwd_leaky(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
