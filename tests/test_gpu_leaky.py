@@ -88,6 +88,8 @@ LEAKY_RAGGED = [
     ([7, 3, 11, 5, 6, 2, 9], [13, 27, 4, 16, 6, 31, 2], 6, 8),
     ([6, 9, 4, 1], [12, 7, 15, 3], 3, 4),
     ([5, 3, 4], [9, 7, 3], 13, 16),                # more than 4 input channels: several projection k-steps
+    ([100, 6], [104, 30], 4, 16),                  # 7 cell tiles: the 16-bit kernels at their LDS limit
+    ([120, 9], [126, 14], 4, 16),                  # 8 cell tiles: past that limit, the fp32 kernels
 ]
 
 
