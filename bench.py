@@ -708,7 +708,8 @@ def main():
             out["leaky_cell"][nm] = {
                 "workload": f"{nm}: {wk_.n} images, C={wk_.C}, H={wk_.H}, seed {wk_.seed}, Leaky LP cell",
                 "value": 4 * Nk / (kms * 1e-3), "unit": "cell-direction updates/s", "ms_per_step": kms,
-                "dtype": "f32 (fp32 matrix cores)" + (", bf16 input" if wk_.x_dtype == "bf16" else ""),
+                "dtype": ("f32 (recurrent products on 16-bit matrix cores, operands split into pieces: forward f16, "
+                          "reverse bf16; fp32 accumulation)" + (", bf16 input" if wk_.x_dtype == "bf16" else "")),
                 "roofline": kroof, "step_roofline": step_roofline(kmodel, kbmin, kms),
                 "kernels_ms": {k: round(v, 5) for k, v in kk.items()},
                 "kernels_roofline": {k: {kk2: r[kk2] for kk2 in ("bound", "frac", "fp32_frac", "min_bytes_hbm_frac")}
