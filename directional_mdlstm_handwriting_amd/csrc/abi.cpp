@@ -14,6 +14,7 @@
 
 #include "../../include/mdlstm.h"
 #include "kernels.h"
+#include "leaky16.h"
 #include "layout.h"
 
 namespace mdl {
@@ -696,7 +697,9 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     Side* side = nullptr;
     int ov_wg = 0;
     const int ov_mode = g_overlap.load();
-    if (!lk && ov_mode != 0 && wg2 && mdl::bwd16_supported(H, L.max_diag)) {
+    // (the Leaky-LP cell's gate gradients have the plain cell's layout: the same tasks, once its 16-bit reverse
+    // wavefront flags its units)
+    if (ov_mode != 0 && wg2 && (lk ? mdl::leaky16_used(H, L.max_diag) : mdl::bwd16_supported(H, L.max_diag))) {
         if ((rc = side_of(side))) return rc;
         const int free_cu = side->ncu - 4 * L.n;
         if (2 * free_cu >= side->ncu) ov_wg = std::min(free_cu, 4 * (int)L.ngroups);
@@ -718,7 +721,8 @@ int mdl_backward(const mdl_layout* layout, const void* d_desc, const void* x_can
     }
     {
         Timed t("bwd_wavefront");
-        e = lk ? mdl::launch_bwd_leaky(D, H, Ul, Uu, Vl, Vu, stash, dy_flat, dh_dirs, dA, st)
+        e = lk ? (ov_wg > 0 ? mdl::launch_bwd_leaky16(D, H, Ul, Uu, Vl, Vu, stash, dy_flat, dh_dirs, dA, F.done, st)
+                            : mdl::launch_bwd_leaky(D, H, Ul, Uu, Vl, Vu, stash, dy_flat, dh_dirs, dA, st))
            : ov_wg > 0 ? mdl::launch_bwd16(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, F.done, st)
                        : mdl::launch_bwd_chain(D, H, Ul, Uu, stash, dy_flat, dh_dirs, dA, st);
     }

@@ -509,7 +509,7 @@ hipError_t launch_bwd_leaky(const Dev& D, int H, const float* Ul, const float* U
                             const float* stash, const float* dy_flat, const float* dh_dirs, float* dA,
                             hipStream_t st) {
     if (leaky16_used(H, D.max_diag))
-        return launch_bwd_leaky16(D, H, Ul, Uu, Vl, Vu, stash, dy_flat, dh_dirs, dA, st);
+        return launch_bwd_leaky16(D, H, Ul, Uu, Vl, Vu, stash, dy_flat, dh_dirs, dA, nullptr, st);
     const LeakyEntry* m = leaky_entry(H);
     if (!m) return hipErrorInvalidValue;
     const int NT = leaky_tiles(D.max_diag);

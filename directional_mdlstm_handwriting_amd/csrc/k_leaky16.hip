@@ -338,7 +338,7 @@ __global__ __launch_bounds__(LK16<H>::MAXT) void k_bwd_leaky16(Dev D, int NT, co
                                                              const float* __restrict__ stash,
                                                              const float* __restrict__ dy_flat,
                                                              const float* __restrict__ dh_dirs,
-                                                             float* __restrict__ dA) {
+                                                             float* __restrict__ dA, int32_t* __restrict__ done) {
     using Sh = LK16<H>;
     constexpr int NB = Sh::NB, KU = Sh::KU, KV = Sh::KV, RGB = Sh::RGB, RD = Sh::RD, G = Sh::G, G3 = Sh::G3;
     const int u = D.units[blockIdx.x];
@@ -530,12 +530,19 @@ __global__ __launch_bounds__(LK16<H>::MAXT) void k_bwd_leaky16(Dev D, int NT, co
         step(s - 1, vB, vA);
     }
     if (s >= 0) step(s, vA, vB);
+    // The unit is done: once every wave's gate-gradient stores are visible device-wide, flag it (the weight
+    // gradient may then start on this direction of the example's cells while other units still run).
+    if (done != nullptr) {
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0) __hip_atomic_store(done + u, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 typedef void (*FwdL16K)(Dev, const void*, int, int, const float*, const float*, const float*, const float*,
                         const float*, const float*, float*, float*);
 typedef void (*BwdL16K)(Dev, int, const float*, const float*, const float*, const float*, const float*,
-                        const float*, const float*, float*);
+                        const float*, const float*, float*, int32_t*);
 
 struct L16Entry {
     int H;
@@ -594,12 +601,12 @@ hipError_t launch_fwd_leaky16(const Dev& D, const void* x_canvas, int dtype, int
 
 hipError_t launch_bwd_leaky16(const Dev& D, int H, const float* Ul, const float* Uu, const float* Vl,
                               const float* Vu, const float* stash, const float* dy_flat, const float* dh_dirs,
-                              float* dA, hipStream_t st) {
+                              float* dA, int32_t* done, hipStream_t st) {
     if (!leaky16_used(H, D.max_diag)) return hipErrorInvalidValue;
     const L16Entry* m = l16_entry(H);
     const int NT = l16_tiles(D.max_diag);
     launch(m->bwd, dim3(4 * D.n), dim3(64 * NT * m->NB), l16_bwd_bytes(*m, D.max_diag), st, D, NT, Ul, Uu, Vl, Vu,
-           stash, dy_flat, dh_dirs, dA);
+           stash, dy_flat, dh_dirs, dA, done);
     return hipGetLastError();
 }
 

@@ -12,8 +12,9 @@ size_t leaky16_bwd_lds(int H, int Lmax);
 hipError_t launch_fwd_leaky16(const Dev& D, const void* x_canvas, int dtype, int C, int H, const float* Wx,
                               const float* b, const float* Ul, const float* Uu, const float* Vl, const float* Vu,
                               float* stash, float* h_dirs, hipStream_t st);
+// done: NULL, or [4n] flags, each set (release, device scope) once that unit's gate gradients are stored
 hipError_t launch_bwd_leaky16(const Dev& D, int H, const float* Ul, const float* Uu, const float* Vl,
                               const float* Vu, const float* stash, const float* dy_flat, const float* dh_dirs,
-                              float* dA, hipStream_t st);
+                              float* dA, int32_t* done, hipStream_t st);
 
 }  // namespace mdl
